@@ -1,0 +1,310 @@
+"""Plain fp64 CPU oracle for the MoE layer forward pass.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module. It shares no code with the HIP
+library and never imports it.
+
+Every function follows one passage of the pages and is written to be read
+against it, not to be fast. Floating point is fp64 throughout; stored bf16
+values are widened exactly (a bf16 bit pattern is the top half of an fp32).
+Nothing is rounded in between, except the one place where floating point
+decides an integer (the top-k choice), which is taken on logits rounded to
+fp32, the precision the GPU kernel decides in.
+
+Sources, cited by short name:
+  [MoE Principles]   wrblog.cn, "MoE 模型原理：路由、专家负载、容量、通信与推理成本"
+                     (MoE principles: routing, expert load, capacity,
+                     communication and inference cost), sections 1-14.
+  [EP Token->Expert] 111qqz.com, "Expert Parallelism：为什么让 Token 去找 Expert，
+                     而不是搬运参数？", cited by section heading.
+  [Gate&Comm]        mianshidashi.cn, MiniMax interview answer on MoE gate
+                     outputs and distributed communication, "深入解析" items 01-06.
+
+Readings where the pages leave a step open (each one is also listed with its
+reason in the design notes):
+  R1  top-k selects on the logits s (softmax is strictly increasing, so the
+      chosen set equals TopK(p)); ids come in descending-score order and
+      equal scores go to the lower expert index.
+  R2  gate = renormalised top-k probability when `renormalize`, else the
+      plain softmax probability (the page's top-1 toy).
+  R3  gates are not renormalised again after capacity drops; a dropped
+      assignment contributes zero and a token with every assignment dropped
+      outputs exactly zero (the residual lies outside the layer).
+  R4  capacity C = ceil(c*T*k/E) of the exact value of c (a binary float), for
+      the whole call as one routing group.
+  R5  capacity is granted first-come in token order; a token's own k choices
+      never compete (they go to distinct experts).
+  R6  f_i counts assignments before capacity.
+  R7  dispatch layout: expert-major, token order within an expert, rows
+      packed from 0 (no padding to C).
+  R8  tanh-GELU is 0.5*u*(1 + tanh(sqrt(2/pi)*(u + 0.044715*u^3))) (Hendrycks &
+      Gimpel's published approximation; the pages do not define sigma). Its
+      constants are "parity unpinned" by the pages: they are pinned only
+      against an independent library implementation and the exact GELU.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+ORACLE_VERSION = 1
+
+NEAR_TIE_REL = 1e-6
+
+
+# ---------------------------------------------------------------- storage
+
+def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored values -> exact fp64. `a` is uint16 bit patterns for bf16,
+    float32 for f32."""
+    if dtype == "bf16":
+        a = np.ascontiguousarray(a, dtype=np.uint16)
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def round_f32(a: np.ndarray) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64).astype(np.float32)
+
+
+# ---------------------------------------------------------------- capacity
+
+def capacity(T: int, k: int, E: int, c: float) -> int:
+    """C = ceil(c * T * k / E)  [MoE Principles §4.1, capacity formula;
+    EP Token->Expert, "Expert Capacity 和 Token Dropping"].
+
+    Fraction(c) is the exact value of the float c (reading R4)."""
+    return math.ceil(Fraction(c) * T * k / E)
+
+
+# ---------------------------------------------------------------- routing
+
+def router_logits(x: np.ndarray, W_r: np.ndarray, b_r: np.ndarray) -> np.ndarray:
+    """s_t = W_r x_t + b_r for every token  [MoE Principles §2.1].
+
+    x [T, d], W_r [E, d], b_r [E], all fp64 -> s [T, E]."""
+    return x @ W_r.T + b_r[None, :]
+
+
+def softmax(s: np.ndarray) -> np.ndarray:
+    """p_{t,i} = exp(s_{t,i}) / sum_j exp(s_{t,j})  [MoE Principles §2.1].
+
+    The row maximum is subtracted first; the quotient is unchanged."""
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def topk_ids(s: np.ndarray, k: int) -> np.ndarray:
+    """S_t = TopK(p_t, k)  [MoE Principles §2.2], reading R1.
+
+    The decision is taken on the logits rounded to fp32. A stable sort of the
+    negated scores lists higher scores first and, among equal scores, lower
+    expert indices first. Returns int32 [T, k]."""
+    s32 = round_f32(s)
+    order = np.argsort(-s32, axis=1, kind="stable")
+    return order[:, :k].astype(np.int32)
+
+
+def gates(p: np.ndarray, ids: np.ndarray, renormalize: bool) -> np.ndarray:
+    """Combine weights of the chosen experts  [MoE Principles §2.2]:
+    p~_{t,i} = p_{t,i} / sum_{j in S_t} p_{t,j} when renormalising (reading R2),
+    else p_{t,i} as the page's top-1 example uses it  [MoE Principles §7]."""
+    chosen = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    if renormalize:
+        return chosen / chosen.sum(axis=1, keepdims=True)
+    return chosen
+
+
+def near_ties(s: np.ndarray, k: int, rel: float = NEAR_TIE_REL) -> np.ndarray:
+    """Tokens whose top-k decision is fragile: some gap between neighbouring
+    sorted logits at ranks (r, r+1), r < k, is below rel * max_i |s_{t,i}|.
+    Returns bool [T]."""
+    T, E = s.shape
+    srt = -np.sort(-s, axis=1)
+    scale = np.abs(s).max(axis=1)
+    fragile = np.zeros(T, dtype=bool)
+    for r in range(min(k, E - 1)):
+        fragile |= (srt[:, r] - srt[:, r + 1]) < rel * scale
+    return fragile
+
+
+def route(x, W_r, b_r, k: int, renormalize: bool) -> dict:
+    """Router, softmax, top-k and gates on fp64 inputs."""
+    s = router_logits(x, W_r, b_r)
+    p = softmax(s)
+    ids = topk_ids(s, k)
+    return {"logits": s, "probs": p, "topk_ids": ids,
+            "topk_gates": gates(p, ids, renormalize),
+            "prob_sum": p.sum(axis=0), "near_tie": near_ties(s, k)}
+
+
+# ---------------------------------------------------------------- dispatch
+
+def dispatch(ids: np.ndarray, E: int, C: int) -> dict:
+    """Capacity assignment and the expert-contiguous layout.
+
+    count_e   = |{t : e in S_t}|                       [MoE Principles §3.2, f_i]
+    slot(t,e) = |{t' < t : e in S_t'}|  (first come, token order)
+    kept      = slot < C        [MoE Principles §4.2 worked example; reading R5]
+    n_e       = min(count_e, C);  offset_e = sum_{e' < e} n_e'   (reading R7)
+    row_of    = offset_e + slot if kept else -1
+    row_token[offset_e + s] = the token holding slot s of expert e
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    T, k = ids.shape
+    member = np.zeros((T, E), dtype=np.int64)          # member[t, e] = [e in S_t]
+    np.put_along_axis(member, ids, 1, axis=1)
+    before = np.cumsum(member, axis=0) - member         # tokens t' < t holding e
+    counts = member.sum(axis=0)
+    slot = np.take_along_axis(before, ids, axis=1)
+    kept = slot < C
+    n = np.minimum(counts, C)
+    offsets = np.concatenate([[0], np.cumsum(n)])
+    row_of = np.where(kept, offsets[ids] + slot, -1)
+    rows = int(offsets[-1])
+    row_token = np.full(rows, -1, dtype=np.int64)
+    tt = np.broadcast_to(np.arange(T)[:, None], (T, k))
+    row_token[row_of[kept]] = tt[kept]
+    return {"expert_counts": counts.astype(np.int32), "n": n.astype(np.int32),
+            "expert_offsets": offsets.astype(np.int32), "slot": slot.astype(np.int32),
+            "kept": kept, "row_of": row_of.astype(np.int32),
+            "row_token": row_token.astype(np.int32), "rows": rows}
+
+
+def permute(x: np.ndarray, row_token: np.ndarray) -> np.ndarray:
+    """x_perm[r] = x[row_token[r]]: tokens gathered expert by expert
+    [MoE Principles §5; Gate&Comm 02, 06]. Works on stored values (a copy)."""
+    return x[np.asarray(row_token, dtype=np.int64)]
+
+
+# ---------------------------------------------------------------- experts
+
+def gelu_tanh(u: np.ndarray) -> np.ndarray:
+    """Reading R8 (parity unpinned by the pages)."""
+    return 0.5 * u * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (u + 0.044715 * u ** 3)))
+
+
+def relu(u: np.ndarray) -> np.ndarray:
+    return np.maximum(u, 0.0)
+
+
+ACTS = {"relu": relu, "gelu_tanh": gelu_tanh}
+
+
+def expert_ffn(x_rows, W1_e, b1_e, W2_e, b2_e, act: str):
+    """FFN(x) = W2 sigma(W1 x + b1) + b2  [MoE Principles §1], row by row.
+
+    x_rows [n, d]; W1_e [d_ff, d] maps d -> d_ff; W2_e [d, d_ff] maps back.
+    Returns (h [n, d_ff], Y [n, d])."""
+    h = ACTS[act](x_rows @ W1_e.T + b1_e[None, :])
+    return h, h @ W2_e.T + b2_e[None, :]
+
+
+def combine(Y_rows: np.ndarray, row_of: np.ndarray, g: np.ndarray) -> np.ndarray:
+    """y_t = sum_{i in S_t, kept} p~_{t,i} E_i(x_t)  [MoE Principles §2.2, §5];
+    dropped assignments add nothing (reading R3). Y_rows is indexed by row."""
+    T, k = row_of.shape
+    y = np.zeros((T, Y_rows.shape[1]), dtype=np.float64)
+    for j in range(k):
+        keep = row_of[:, j] >= 0
+        y[keep] += g[keep, j][:, None] * Y_rows[row_of[keep, j]]
+    return y
+
+
+# ---------------------------------------------------------------- whole layer
+
+def layer_forward(x, W_r, b_r, W1, b1, W2, b2, *, k: int, C: int, renormalize: bool,
+                  act: str, ids=None) -> dict:
+    """The whole hot path on fp64 inputs  [MoE Principles §5 flowchart]:
+    router -> probabilities -> top-k -> capacity assignment -> dispatch ->
+    expert FFNs -> combine.
+
+    W1 [E, d_ff, d], W2 [E, d, d_ff], b1 [E, d_ff], b2 [E, d]. When `ids` is
+    given, dispatch and everything after it use those expert ids instead of
+    the oracle's own choice (used when the GPU took the other side of a
+    near-tie)."""
+    E = W_r.shape[0]
+    r = route(x, W_r, b_r, k, renormalize)
+    use_ids = r["topk_ids"] if ids is None else np.asarray(ids, dtype=np.int32)
+    g = r["topk_gates"] if ids is None else gates(r["probs"], use_ids, renormalize)
+    dsp = dispatch(use_ids, E, C)
+    rows = dsp["rows"]
+    x_perm = permute(x, dsp["row_token"])
+    h = np.zeros((rows, W1.shape[1]), dtype=np.float64)
+    Y = np.zeros((rows, x.shape[1]), dtype=np.float64)
+    off = dsp["expert_offsets"]
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            h[a:b], Y[a:b] = expert_ffn(x_perm[a:b], W1[e], b1[e], W2[e], b2[e], act)
+    y = combine(Y, dsp["row_of"], g)
+    out = dict(r)
+    out.update(dsp)
+    out.update({"used_ids": use_ids, "used_gates": g, "x_perm": x_perm, "h": h,
+                "y_perm": Y, "y": y})
+    return out
+
+
+def sampled_outputs(tokens, x, ids, row_of, g, expert_weights, act: str) -> np.ndarray:
+    """y_t for a few tokens only, one token and one expert at a time, for the
+    full-size workloads where the oracle cannot afford every row: for each
+    kept assignment (t, j) the FFN of expert ids[t, j] on x_t, weighted by
+    g[t, j]  [MoE Principles §2.2 output formula].
+
+    `expert_weights(e)` returns (W1_e, b1_e, W2_e, b2_e) in fp64."""
+    out = np.zeros((len(tokens), x.shape[1]), dtype=np.float64)
+    cache = {}
+    for n, t in enumerate(tokens):
+        for j in range(ids.shape[1]):
+            if row_of[t, j] < 0:
+                continue
+            e = int(ids[t, j])
+            if e not in cache:
+                cache.clear()
+                cache[e] = expert_weights(e)
+            W1e, b1e, W2e, b2e = cache[e]
+            _, Y = expert_ffn(x[t:t + 1], W1e, b1e, W2e, b2e, act)
+            out[n] += g[t, j] * Y[0]
+    return out
+
+
+# ---------------------------------------------------------------- statistics
+
+def aux_loss(counts, prob_sum, T: int, E: int, alpha: float) -> float:
+    """L_aux = alpha * E * sum_i f_i * pbar_i with f_i = count_i / T and
+    pbar_i = (1/T) sum_t p_{t,i}  [MoE Principles §3.2; reading R6]."""
+    f = np.asarray(counts, dtype=np.float64) / T
+    pbar = np.asarray(prob_sum, dtype=np.float64) / T
+    return alpha * E * float(np.sum(f * pbar))
+
+
+def load_stats(counts, C: int, T: int, k: int) -> dict:
+    """What the pages ask to log per routing step  [MoE Principles §3.3, §13]:
+    tokens per expert, drops per expert, max/mean load, overflow ratio,
+    padding ratio of a padded [E, C] layout, entropy of the load."""
+    counts = np.asarray(counts, dtype=np.int64)
+    E = counts.size
+    kept = np.minimum(counts, C)
+    dropped = counts - kept
+    frac = counts / max(1, counts.sum())
+    nz = frac[frac > 0]
+    return {
+        "tokens_per_expert": counts.tolist(),
+        "kept_per_expert": kept.tolist(),
+        "dropped_per_expert": dropped.tolist(),
+        "dropped": int(dropped.sum()),
+        "overflow_ratio": float(dropped.sum() / max(1, T * k)),
+        "max_over_mean_load": float(counts.max() / max(1e-300, counts.mean())) if E else 0.0,
+        "padding_ratio": float(E * C / max(1, kept.sum())),
+        "load_entropy": float(-(nz * np.log(nz)).sum()),
+    }
+
+
+def ffn_flops(rows: int, d: int, d_ff: int) -> int:
+    """4 * d * d_ff per kept (token, expert) pair  [MoE Principles §8.3]."""
+    return 4 * d * d_ff * rows

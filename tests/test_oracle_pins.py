@@ -1,0 +1,532 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each check below ties one oracle function to something other than itself: a
+value the pages print for a worked example (tests/golden/, each with its
+citation), a closed form, an invariant, a special case that reduces to a
+library routine, or brute force on tiny inputs. The mutation tests at the end
+plant plausible mistakes in the oracle (on the CPU) and show that a pin fails
+for each.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as mo
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ------------------------------------------------------------------ capacity
+
+def check_capacity_pages():
+    for case in golden("capacity_examples.json")["cases"]:
+        assert mo.capacity(case["T"], case["k"], case["E"], case["c"]) == case["C"], case
+
+
+def check_capacity_closed_form():
+    # ceil of a non-integer quotient: 1.0*10*1/4 = 2.5 -> 3; 1.25*7*2/3 = 5.833 -> 6
+    assert mo.capacity(10, 1, 4, 1.0) == 3
+    assert mo.capacity(7, 2, 3, 1.25) == 6
+    # exact integer quotients stay put
+    assert mo.capacity(12, 2, 8, 1.0) == 3
+    # the five workloads
+    assert mo.capacity(8, 1, 2, 1.0) == 4
+    assert mo.capacity(4096, 2, 8, 1.25) == 1280
+    assert mo.capacity(16384, 2, 8, 1.25) == 5120
+    assert mo.capacity(8192, 4, 64, 1.0) == 512
+    assert mo.capacity(4096, 8, 256, 1.25) == 160
+
+
+def test_capacity_pages():
+    check_capacity_pages()
+
+
+def test_capacity_closed_form():
+    check_capacity_closed_form()
+
+
+# ------------------------------------------------------------------ dispatch
+
+def check_drop_rule():
+    g = golden("drop_rule_example.json")
+    ids = np.array(g["topk_ids"], dtype=np.int32)
+    for key in ("C4", "C6"):
+        exp = g[key]
+        out = mo.dispatch(ids, g["E"], exp["C"])
+        assert out["expert_counts"].tolist() == exp["expert_counts"]
+        assert out["n"].tolist() == exp["kept_per_expert"]
+        assert np.flatnonzero(~out["kept"][:, 0]).tolist() == exp["overflow_tokens"]
+        assert out["expert_offsets"].tolist() == exp["expert_offsets"]
+        assert out["row_token"].tolist() == exp["row_token"]
+        if "slot" in exp:
+            assert out["slot"].tolist() == exp["slot"]
+            assert out["row_of"].tolist() == exp["row_of"]
+
+
+def test_drop_rule_pages():
+    check_drop_rule()
+
+
+def overflow_routing(seed=3):
+    g = golden("overflow_example.json")
+    T, E, hot, n_hot = g["T"], g["E"], g["hot_expert"], g["hot_tokens"]
+    r = rng(seed)
+    hot_pos = np.sort(r.choice(T, size=n_hot, replace=False))
+    ids = np.empty((T, 1), dtype=np.int32)
+    others = [e for e in range(E) if e != hot]
+    ids[:, 0] = np.array(others)[np.arange(T) % len(others)]
+    ids[hot_pos, 0] = hot
+    return g, ids, hot_pos
+
+
+def test_overflow_pages():
+    g, ids, hot_pos = overflow_routing()
+    for case in g["cases"]:
+        C = mo.capacity(g["T"], g["k"], g["E"], case["c"])
+        assert C == case["C"]
+        out = mo.dispatch(ids, g["E"], C)
+        dropped = int((~out["kept"]).sum())
+        assert dropped == case["dropped"]
+        # the hot expert keeps its earliest C tokens, in token order
+        e = g["hot_expert"]
+        a, b = out["expert_offsets"][e], out["expert_offsets"][e + 1]
+        assert out["row_token"][a:b].tolist() == hot_pos[:C].tolist()
+        # every other expert stays within capacity
+        assert all(out["expert_counts"][i] <= C for i in range(g["E"]) if i != e)
+
+
+def brute_dispatch(ids, E, k):
+    """Token-by-token first-come assignment, pure Python."""
+    T = len(ids)
+    used = [0] * E
+    slot = [[0] * k for _ in range(T)]
+    for t in range(T):
+        for j in range(k):
+            e = ids[t][j]
+            slot[t][j] = used[e]
+            used[e] += 1
+    return used, slot
+
+
+def test_dispatch_bruteforce_and_invariants():
+    r = rng(11)
+    for trial in range(200):
+        E = int(r.integers(1, 9))
+        k = int(r.integers(1, E + 1))
+        T = int(r.integers(0, 40))
+        C = int(r.integers(1, max(2, T)))
+        ids = np.stack([r.permutation(E)[:k] for _ in range(T)]) if T else np.zeros((0, k), np.int32)
+        ids = ids.astype(np.int32).reshape(T, k)
+        out = mo.dispatch(ids, E, C)
+        used, slot = brute_dispatch(ids.tolist(), E, k)
+        assert out["expert_counts"].tolist() == used
+        assert out["slot"].tolist() == (slot if T else [])
+        n = np.minimum(np.array(used), C)
+        assert out["rows"] == int(n.sum()) == int(out["kept"].sum())
+        assert out["expert_offsets"].tolist() == [0] + np.cumsum(n).tolist()
+        for e in range(E):
+            seg = out["row_token"][out["expert_offsets"][e]:out["expert_offsets"][e + 1]]
+            assert np.all(np.diff(seg) > 0)              # token order inside an expert
+            assert all(e in ids[t] for t in seg)
+        for t in range(T):
+            for j in range(k):
+                row = out["row_of"][t, j]
+                if row >= 0:
+                    assert out["row_token"][row] == t
+        if C >= T:
+            assert out["rows"] == T * k
+
+
+# ------------------------------------------------------------------ routing
+
+def brute_topk(s32_row, k):
+    """rank_i = |{j : s_j > s_i}| + |{j < i : s_j = s_i}| by counting pairs."""
+    E = len(s32_row)
+    rank = [sum(1 for j in range(E) if s32_row[j] > s32_row[i]) +
+            sum(1 for j in range(i) if s32_row[j] == s32_row[i]) for i in range(E)]
+    return [rank.index(r) for r in range(k)]
+
+
+def check_topk_bruteforce():
+    r = rng(5)
+    for trial in range(300):
+        E = int(r.integers(1, 9))
+        k = int(r.integers(1, E + 1))
+        T = int(r.integers(1, 6))
+        d = int(r.integers(1, 5))
+        if trial % 2 == 0:
+            # integer-valued inputs: exact sums, frequent exact ties
+            x = r.integers(-2, 3, size=(T, d)).astype(np.float64)
+            W = r.integers(-2, 3, size=(E, d)).astype(np.float64)
+            b = r.integers(-1, 2, size=E).astype(np.float64)
+        else:
+            x = r.standard_normal((T, d))
+            W = r.standard_normal((E, d))
+            b = r.standard_normal(E)
+        s = mo.router_logits(x, W, b)
+        ids = mo.topk_ids(s, k)
+        s32 = mo.round_f32(s)
+        for t in range(T):
+            assert ids[t].tolist() == brute_topk(s32[t].tolist(), k), (s32[t], k)
+
+
+def test_topk_bruteforce():
+    check_topk_bruteforce()
+
+
+def test_router_logits_bruteforce():
+    r = rng(6)
+    x = r.standard_normal((3, 5))
+    W = r.standard_normal((4, 5))
+    b = r.standard_normal(4)
+    s = mo.router_logits(x, W, b)
+    for t in range(3):
+        for i in range(4):
+            assert s[t, i] == pytest.approx(b[i] + sum(W[i, m] * x[t, m] for m in range(5)), abs=1e-12)
+
+
+def check_gates():
+    r = rng(8)
+    s = r.standard_normal((50, 6)) * 3
+    p = mo.softmax(s)
+    # softmax against the library routine
+    np.testing.assert_allclose(p, torch.softmax(torch.from_numpy(s), dim=1).numpy(), rtol=1e-13)
+    for k in (1, 2, 6):
+        ids = mo.topk_ids(s, k)
+        g = mo.gates(p, ids, True)
+        np.testing.assert_allclose(g.sum(axis=1), 1.0, atol=1e-14)
+        chosen = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+        np.testing.assert_allclose(g, chosen / chosen.sum(axis=1, keepdims=True), rtol=1e-14)
+        raw = mo.gates(p, ids, False)
+        np.testing.assert_array_equal(raw, chosen)
+        if k == 1:
+            np.testing.assert_allclose(g, 1.0, atol=0)
+            np.testing.assert_array_equal(raw[:, 0], p.max(axis=1))
+        # descending order of the chosen probabilities
+        assert np.all(np.diff(raw, axis=1) <= 0)
+
+
+def test_gates():
+    check_gates()
+
+
+def test_near_ties():
+    s = np.array([[1.0, 1.0 + 1e-9, -3.0], [2.0, 1.0, 0.0], [5.0, 4.0, 4.0 + 1e-12]])
+    assert mo.near_ties(s, 1).tolist() == [True, False, False]
+    assert mo.near_ties(s, 2).tolist() == [True, False, True]
+
+
+# ------------------------------------------------------------------ aux loss
+
+def check_aux_loss():
+    g = golden("aux_loss_example.json")
+    w = g["worked"]
+    T, E = w["T"], w["E"]
+    counts = np.array(w["f"]) * T
+    prob_sum = np.array(w["pbar"]) * T
+    assert mo.aux_loss(counts, prob_sum, T, E, 1.0) == pytest.approx(w["loss_over_alpha"], abs=1e-12)
+    # realised by a real routing: rows with p = (0.6, 0.4) six times, (0.4, 0.6) twice
+    a = math.log(1.5) / 2
+    x = np.array([[1.0]] * 6 + [[-1.0]] * 2)
+    W = np.array([[a], [-a]])
+    r = mo.route(x, W, np.zeros(2), 1, False)
+    np.testing.assert_allclose(r["probs"][0], [0.6, 0.4], rtol=1e-14)
+    d = mo.dispatch(r["topk_ids"], E, 4)
+    assert d["expert_counts"].tolist() == [6, 2]
+    alpha = golden("aux_loss_example.json")["alpha_typical"]["alpha"]
+    assert mo.aux_loss(d["expert_counts"], r["prob_sum"], T, E, alpha) == pytest.approx(1.05 * alpha, rel=1e-12)
+    # uniform f (or uniform pbar) at k = 1 gives exactly alpha
+    for E in (2, 8, 64):
+        T = 4 * E
+        assert mo.aux_loss(np.full(E, T // E), r_sum(E, T), T, E, 0.01) == pytest.approx(0.01, rel=1e-12)
+        skew = rng(E).dirichlet(np.ones(E)) * T
+        assert mo.aux_loss(np.full(E, T // E), skew, T, E, 0.01) == pytest.approx(0.01, rel=1e-12)
+
+
+def r_sum(E, T):
+    return np.full(E, T / E)
+
+
+def test_aux_loss_pages():
+    check_aux_loss()
+
+
+# ------------------------------------------------------------------ experts
+
+def test_gelu_against_library_and_exact():
+    u = np.linspace(-8, 8, 4001)
+    ref = torch.nn.functional.gelu(torch.from_numpy(u), approximate="tanh").numpy()
+    np.testing.assert_allclose(mo.gelu_tanh(u), ref, rtol=1e-12, atol=1e-15)
+    exact = u * 0.5 * (1 + np.array([math.erf(v / math.sqrt(2)) for v in u]))
+    assert np.max(np.abs(mo.gelu_tanh(u) - exact)) < 1e-3
+    np.testing.assert_array_equal(mo.relu(np.array([-1.0, 0.0, 2.5])), [0.0, 0.0, 2.5])
+
+
+def dense_ffn_torch(x, W1, b1, W2, b2, act):
+    F = torch.nn.functional
+    u = F.linear(torch.from_numpy(x), torch.from_numpy(W1), torch.from_numpy(b1))
+    h = F.gelu(u, approximate="tanh") if act == "gelu_tanh" else F.relu(u)
+    return F.linear(h, torch.from_numpy(W2), torch.from_numpy(b2)).numpy()
+
+
+def random_layer(r, T, d, d_ff, E):
+    x = r.standard_normal((T, d))
+    W_r = r.standard_normal((E, d)) / math.sqrt(d)
+    b_r = r.standard_normal(E) * 0.1
+    W1 = r.standard_normal((E, d_ff, d)) / math.sqrt(d)
+    b1 = r.standard_normal((E, d_ff)) * 0.1
+    W2 = r.standard_normal((E, d, d_ff)) / math.sqrt(d_ff)
+    b2 = r.standard_normal((E, d)) * 0.1
+    return x, W_r, b_r, W1, b1, W2, b2
+
+
+def check_single_expert_is_dense_ffn():
+    r = rng(21)
+    x, W_r, b_r, W1, b1, W2, b2 = random_layer(r, 37, 12, 20, 1)
+    for act in ("relu", "gelu_tanh"):
+        out = mo.layer_forward(x, W_r, b_r, W1, b1, W2, b2, k=1, C=37, renormalize=True, act=act)
+        np.testing.assert_allclose(out["y"], dense_ffn_torch(x, W1[0], b1[0], W2[0], b2[0], act),
+                                   rtol=1e-12, atol=1e-12)
+
+
+def test_single_expert_is_dense_ffn():
+    check_single_expert_is_dense_ffn()
+
+
+def check_identical_experts():
+    r = rng(22)
+    x, W_r, b_r, W1, b1, W2, b2 = random_layer(r, 41, 10, 16, 5)
+    W1[:] = W1[0]
+    b1[:] = b1[0]
+    W2[:] = W2[0]
+    b2[:] = b2[0]
+    out = mo.layer_forward(x, W_r, b_r, W1, b1, W2, b2, k=3, C=41, renormalize=True, act="gelu_tanh")
+    np.testing.assert_allclose(out["y"], dense_ffn_torch(x, W1[0], b1[0], W2[0], b2[0], "gelu_tanh"),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_identical_experts_give_dense_ffn():
+    check_identical_experts()
+
+
+def check_dense_soft_mixture():
+    """k = E, renormalised, no drops: y = sum_i p_i E_i(x) over every expert."""
+    r = rng(23)
+    T, d, d_ff, E = 29, 9, 14, 4
+    x, W_r, b_r, W1, b1, W2, b2 = random_layer(r, T, d, d_ff, E)
+    out = mo.layer_forward(x, W_r, b_r, W1, b1, W2, b2, k=E, C=T, renormalize=True, act="relu")
+    p = torch.softmax(torch.from_numpy(x @ W_r.T + b_r), dim=1).numpy()
+    ref = sum(p[:, [i]] * dense_ffn_torch(x, W1[i], b1[i], W2[i], b2[i], "relu") for i in range(E))
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_dense_soft_mixture():
+    check_dense_soft_mixture()
+
+
+def test_layer_permutation_invariants():
+    r = rng(24)
+    T, d, d_ff, E, k = 53, 8, 12, 6, 2
+    x, W_r, b_r, W1, b1, W2, b2 = random_layer(r, T, d, d_ff, E)
+    b_r[2] += 3.0  # a hot expert so that drops happen
+    C = mo.capacity(T, k, E, 1.0)
+    out = mo.layer_forward(x, W_r, b_r, W1, b1, W2, b2, k=k, C=C, renormalize=True, act="gelu_tanh")
+    assert (~out["kept"]).sum() > 0
+    np.testing.assert_array_equal(out["x_perm"], x[out["row_token"]])
+    dropped_all = ~out["kept"].any(axis=1)
+    np.testing.assert_array_equal(out["y"][dropped_all], 0.0)
+    # a token's output: its kept assignments, computed one by one
+    for t in range(T):
+        ref = np.zeros(d)
+        for j in range(k):
+            if out["kept"][t, j]:
+                e = out["topk_ids"][t, j]
+                _, Y = mo.expert_ffn(x[t:t + 1], W1[e], b1[e], W2[e], b2[e], "gelu_tanh")
+                ref += out["topk_gates"][t, j] * Y[0]
+        np.testing.assert_allclose(out["y"][t], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_sampled_outputs_match_full_layer():
+    r = rng(25)
+    T, d, d_ff, E, k = 40, 8, 12, 5, 2
+    x, W_r, b_r, W1, b1, W2, b2 = random_layer(r, T, d, d_ff, E)
+    out = mo.layer_forward(x, W_r, b_r, W1, b1, W2, b2, k=k, C=10, renormalize=True, act="relu")
+    tok = [0, 7, 39]
+    ys = mo.sampled_outputs(tok, x, out["topk_ids"], out["row_of"], out["topk_gates"],
+                            lambda e: (W1[e], b1[e], W2[e], b2[e]), "relu")
+    np.testing.assert_allclose(ys, out["y"][tok], rtol=1e-12, atol=1e-13)
+
+
+def check_constructed_drop_layer():
+    """The page's [1,1,1,1,1,1,2,2] routing realised as a layer input."""
+    d, T = 16, 8
+    x = np.zeros((T, d))
+    x[:, 0] = [1, 1, 1, 1, 1, 1, -1, -1]
+    x[:, 1:] = rng(9).standard_normal((T, d - 1))
+    W_r = np.zeros((2, d))
+    W_r[:, 0] = [0.5, -0.5]
+    r = rng(10)
+    W1 = r.standard_normal((2, 64, d)) / 4
+    W2 = r.standard_normal((2, d, 64)) / 8
+    b1 = np.zeros((2, 64))
+    b2 = np.zeros((2, d))
+    out = mo.layer_forward(x, W_r, np.zeros(2), W1, b1, W2, b2, k=1,
+                           C=mo.capacity(T, 1, 2, 1.0), renormalize=False, act="relu")
+    assert out["topk_ids"][:, 0].tolist() == [0] * 6 + [1] * 2
+    assert out["n"].tolist() == [4, 2]
+    np.testing.assert_array_equal(out["y"][4:6], 0.0)
+    assert np.all(np.abs(out["y"][:4]).sum(axis=1) > 0)
+    out6 = mo.layer_forward(x, W_r, np.zeros(2), W1, b1, W2, b2, k=1,
+                            C=mo.capacity(T, 1, 2, 1.5), renormalize=False, act="relu")
+    assert out6["rows"] == 8
+
+
+def test_constructed_drop_layer():
+    check_constructed_drop_layer()
+
+
+def test_toy_top1_semantics():
+    """The page's top-1 example: kept per expert <= C, overflow tokens output
+    zero, the gate is the top softmax probability  [MoE Principles §7]."""
+    r = rng(12)
+    T, d, d_ff, E = 64, 4, 8, 2
+    x, W_r, b_r, W1, b1, W2, b2 = random_layer(r, T, d, d_ff, E)
+    b_r[:] = [0.8, 0.0]
+    C = mo.capacity(T, 1, E, 1.0)
+    out = mo.layer_forward(x, W_r, b_r, W1, b1, W2, b2, k=1, C=C, renormalize=False, act="relu")
+    assert np.all(out["n"] <= C)
+    overflow = ~out["kept"][:, 0]
+    assert overflow.sum() == max(0, out["expert_counts"].max() - C)
+    np.testing.assert_array_equal(out["y"][overflow], 0.0)
+    np.testing.assert_array_equal(out["topk_gates"][:, 0], out["probs"].max(axis=1))
+
+
+def test_flops_formula():
+    # 2 x (2 d d_ff) per (token, expert)  [MoE Principles §8.3]
+    assert mo.ffn_flops(1, 4096, 14336) == 2 * (2 * 4096 * 14336)
+
+
+def test_load_stats():
+    s = mo.load_stats([6, 2], 4, 8, 1)
+    assert s["dropped"] == 2 and s["dropped_per_expert"] == [2, 0]
+    assert s["padding_ratio"] == pytest.approx(2 * 4 / 6)
+
+
+def test_widen_bf16_exact():
+    vals = np.array([1.0, -2.5, 3.140625, 1e-3, 65504.0], dtype=np.float32)
+    bits = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    back = mo.widen(bits, "bf16")
+    ref = torch.from_numpy(vals).to(torch.bfloat16).to(torch.float64).numpy()
+    # truncation equals RNE for these values (their low halves are zero or tiny)
+    np.testing.assert_array_equal(back[:3], ref[:3])
+
+
+# ------------------------------------------------------------------ planted mistakes
+
+def _expect_fail(fn):
+    with pytest.raises(AssertionError):
+        fn()
+
+
+def test_planted_tie_break_is_caught(monkeypatch):
+    def highest_index_first(s, k):
+        s32 = mo.round_f32(s)
+        E = s32.shape[1]
+        order = np.argsort(-s32[:, ::-1], axis=1, kind="stable")
+        return (E - 1 - order[:, :k]).astype(np.int32)
+    monkeypatch.setattr(mo, "topk_ids", highest_index_first)
+    _expect_fail(check_topk_bruteforce)
+
+
+def test_planted_ascending_topk_is_caught(monkeypatch):
+    monkeypatch.setattr(mo, "topk_ids", lambda s, k: np.argsort(mo.round_f32(s), axis=1,
+                                                                kind="stable")[:, :k].astype(np.int32))
+    _expect_fail(check_topk_bruteforce)
+
+
+def test_planted_missing_renormalisation_is_caught(monkeypatch):
+    orig = mo.gates
+    monkeypatch.setattr(mo, "gates", lambda p, ids, renormalize: orig(p, ids, False))
+    _expect_fail(check_gates)
+    _expect_fail(check_identical_experts)
+
+
+def test_planted_last_come_slots_are_caught(monkeypatch):
+    orig = mo.dispatch
+
+    def last_come(ids, E, C):
+        ids = np.asarray(ids)
+        out = orig(ids[::-1], E, C)
+        for key in ("slot", "kept", "row_of"):
+            out[key] = out[key][::-1]
+        return out
+    monkeypatch.setattr(mo, "dispatch", last_come)
+    _expect_fail(check_drop_rule)
+
+
+def test_planted_floor_capacity_is_caught(monkeypatch):
+    monkeypatch.setattr(mo, "capacity", lambda T, k, E, c: int(c * T * k // E))
+    _expect_fail(check_capacity_closed_form)
+
+
+def test_planted_capacity_without_k_is_caught(monkeypatch):
+    monkeypatch.setattr(mo, "capacity", lambda T, k, E, c: math.ceil(c * T / E))
+    _expect_fail(check_capacity_closed_form)
+
+
+def test_planted_gelu_constant_is_caught(monkeypatch):
+    monkeypatch.setattr(mo, "gelu_tanh", lambda u: 0.5 * u * (1.0 + np.tanh(
+        math.sqrt(2.0 / math.pi) * (u + 0.44715 * u ** 3))))
+    monkeypatch.setitem(mo.ACTS, "gelu_tanh", mo.gelu_tanh)
+    _expect_fail(test_gelu_against_library_and_exact)
+    _expect_fail(check_identical_experts)
+
+
+def test_planted_transposed_w1_is_caught(monkeypatch):
+    def transposed(x_rows, W1_e, b1_e, W2_e, b2_e, act):
+        h = mo.ACTS[act](x_rows @ W1_e.reshape(W1_e.shape[1], W1_e.shape[0]) + b1_e[None, :])
+        return h, h @ W2_e.T + b2_e[None, :]
+    monkeypatch.setattr(mo, "expert_ffn", transposed)
+    _expect_fail(check_single_expert_is_dense_ffn)
+
+
+def test_planted_missing_bias_is_caught(monkeypatch):
+    def no_b2(x_rows, W1_e, b1_e, W2_e, b2_e, act):
+        h = mo.ACTS[act](x_rows @ W1_e.T + b1_e[None, :])
+        return h, h @ W2_e.T
+    monkeypatch.setattr(mo, "expert_ffn", no_b2)
+    _expect_fail(check_single_expert_is_dense_ffn)
+
+
+def test_planted_dropped_tokens_kept_is_caught(monkeypatch):
+    def combine_all(Y_rows, row_of, g):
+        return mo_combine_orig(Y_rows, np.where(row_of >= 0, row_of, 0), g)
+    mo_combine_orig = mo.combine
+    monkeypatch.setattr(mo, "combine", combine_all)
+    _expect_fail(check_constructed_drop_layer)
+
+
+def test_planted_aux_loss_without_E_is_caught(monkeypatch):
+    monkeypatch.setattr(mo, "aux_loss", lambda counts, prob_sum, T, E, alpha: alpha * float(
+        np.sum(np.asarray(counts) / T * np.asarray(prob_sum) / T)))
+    _expect_fail(check_aux_loss)
+
+
+def test_planted_softmax_sign_is_caught(monkeypatch):
+    monkeypatch.setattr(mo, "softmax", lambda s: np.exp(-s) / np.exp(-s).sum(axis=1, keepdims=True))
+    _expect_fail(check_gates)
+    _expect_fail(check_dense_soft_mixture)
