@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""MoE layer forward throughput on one MI355X (gfx950).
+
+One step = one moe_layer_forward call (route -> dispatch -> grouped expert
+FFN -> combine) over one batch of synthetic tokens already resident in HBM.
+Prints one JSON line: tokens/s, the roofline of the dominant kernel (live
+HIP-event timing), per-stage times and fractions, and the fp64 CPU oracle
+timed on the host as a baseline.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec at 1 GPU; grouped-GEMM % MFMA peak; dispatch/combine % HBM BW"
+
+# MI355X published peaks
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="small_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=30.0,
+                    help="upper bound on the oracle's CPU time for the baseline leg")
+    return ap.parse_args()
+
+
+def stage_bytes_flops(w, C, counts, offsets):
+    """Algorithmic bytes and flops per stage (one launch each)."""
+    import numpy as np
+    b = 2 if w.dtype == "bf16" else 4
+    rows = int(offsets[-1])
+    kept_e = np.minimum(counts, C)
+    T, d, d_ff, E, k = w.T, w.d, w.d_ff, w.E, w.k
+    touched = int((kept_e > 0).sum())
+    return {
+        # x read once, W_r once, ids+gates written
+        "route": {"bytes": T * d * b + E * d * b + T * k * 8, "flops": 2 * T * d * E},
+        # x rows read once per token with a kept assignment (<= T), x_perm written,
+        # ids read, slot/row_of written, row_token written
+        "dispatch": {"bytes": T * d * b + rows * d * b + T * k * 12 + rows * 4, "flops": 0},
+        # touched experts' W1 read, x_perm read, h written
+        "gemm1": {"bytes": touched * d_ff * d * b + rows * d * b + rows * d_ff * b,
+                  "flops": 2 * rows * d * d_ff},
+        # touched experts' W2 read, h read, y_perm (fp32) written
+        "gemm2": {"bytes": touched * d * d_ff * b + rows * d_ff * b + rows * d * 4,
+                  "flops": 2 * rows * d * d_ff},
+        # y_perm rows read (fp32), ids/gates read, y written
+        "combine": {"bytes": rows * d * 4 + T * k * 8 + T * d * b, "flops": 0},
+    }
+
+
+def cpu_baseline(w, inp, C, budget_s):
+    """The fp64 oracle, as it stands, on the host cores."""
+    import numpy as np
+    from oracle import moe_oracle as mo
+    from tests.parity import host64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    h = {k: host64(v, w.dtype) for k, v in inp.items()}
+    # estimate: FFN flops dominate; run the whole layer when it fits the budget,
+    # else a leading slice of the experts' rows (route + dispatch always whole)
+    t0 = time.perf_counter()
+    r = mo.route(h["x"], h["W_r"], h["b_r"], w.k, w.renormalize)
+    dsp = mo.dispatch(r["topk_ids"], w.E, C)
+    t_route = time.perf_counter() - t0
+    rows = dsp["rows"]
+    x_perm = mo.permute(h["x"], dsp["row_token"])
+    off = dsp["expert_offsets"]
+    Y = np.zeros((rows, w.d))
+    t1 = time.perf_counter()
+    done_rows = 0
+    for e in range(w.E):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            _, Y[a:b] = mo.expert_ffn(x_perm[a:b], h["W1"][e], h["b1"][e], h["W2"][e], h["b2"][e], w.act)
+            done_rows += b - a
+        if time.perf_counter() - t1 > budget_s:
+            break
+    t_ffn = time.perf_counter() - t1
+    t2 = time.perf_counter()
+    mo.combine(Y, dsp["row_of"], r["topk_gates"])
+    t_comb = time.perf_counter() - t2
+    frac = done_rows / max(1, rows)
+    est = t_route + t_comb + (t_ffn / frac if frac > 0 else float("inf"))
+    sample = ("whole layer" if frac >= 1.0 else
+              f"route+dispatch+combine on all {w.T} tokens, expert FFN on {done_rows}/{rows} rows "
+              f"(time scaled to all rows)")
+    return {"value": w.T / est, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{w.name}: {sample}; fp64 numpy; {est:.2f} s per layer"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the layer has no multi-GPU path in this library", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from top_routing_expert_02_amd import moe, synth
+    if not os.path.exists(moe.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    moe.lib()
+    w = synth.WORKLOADS[args.workload]
+    dev = "cuda"
+    log(f"[bench] {w.name}: generating inputs")
+    inp = synth.make_inputs(w, dev, seed=0)
+    C = moe.capacity(w.T, w.k, w.E, w.c)
+    cfg = moe.config(w.T, w.d, w.d_ff, w.E, w.k, C, w.renormalize, w.dtype, w.act)
+    R = moe.max_rows(cfg)
+    ws = moe.alloc_workspace(cfg, dev)
+    y = torch.empty((w.T, w.d), dtype=w.torch_dtype, device=dev)
+    info = {"expert_counts": torch.empty(w.E, dtype=torch.int32, device=dev),
+            "expert_offsets": torch.empty(w.E + 1, dtype=torch.int32, device=dev)}
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        moe.layer_forward(cfg, inp["x"], inp["W_r"], inp["b_r"], inp["W1"], inp["b1"], inp["W2"],
+                          inp["b2"], y, info=info, ws=ws, stage_events=events)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    counts = info["expert_counts"].cpu().numpy()
+    offsets = info["expert_offsets"].cpu().numpy()
+
+    # timed region: K whole-layer steps, stage events recorded inside it
+    K = args.steps
+    ev = [moe.HipEvents(moe.MOE_NUM_STAGES + 1) for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        step(ev[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms = total_ms / K
+    stage_ms = {n: float(np.mean([e.elapsed_ms(s, s + 1) for e in ev]))
+                for s, n in enumerate(moe.STAGE_NAMES)}
+    for e in ev:
+        e.close()
+    log(f"[bench] {K} steps: {ms:.4f} ms/step; stages {stage_ms}")
+
+    work = stage_bytes_flops(w, C, counts, offsets)
+    stages = {}
+    for n in moe.STAGE_NAMES:
+        t = stage_ms[n] * 1e-3
+        st = {"ms": round(stage_ms[n], 5), "bytes": work[n]["bytes"], "flops": work[n]["flops"],
+              "GB_s": work[n]["bytes"] / t / 1e9, "hbm_frac": work[n]["bytes"] / t / 1e9 / PEAK_HBM_GBS}
+        if work[n]["flops"] and n.startswith("gemm"):
+            peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+            st["TFLOP_s"] = work[n]["flops"] / t / 1e12
+            st["mfma_frac"] = st["TFLOP_s"] / peak
+        stages[n] = st
+    dom = max(("gemm1", "gemm2"), key=lambda n: stage_ms[n])
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    traffic = None
+    prof = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    if os.path.exists(prof):
+        try:
+            tr = json.load(open(prof))
+            traffic = tr.get(dom)
+        except Exception:
+            traffic = None
+    roofline = {"bound": "mfma", "kernel": f"grouped_gemm_bf16 ({dom})",
+                "achieved": stages[dom]["TFLOP_s"], "peak": peak, "unit": "TFLOP/s",
+                "frac": stages[dom]["TFLOP_s"] / peak, "traffic": traffic}
+
+    rows = int(offsets[-1])
+    out = {"metric": METRIC, "value": w.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+           "steps": K, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+           "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "E": w.E, "k": w.k,
+                      "c": w.c, "C": C, "act": w.act, "rows": rows,
+                      "dropped": int(np.maximum(counts - C, 0).sum()), "parallelism": "none"},
+           "roofline": roofline, "stages": stages}
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(w, inp, C, args.cpu_budget_s)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

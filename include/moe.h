@@ -1,0 +1,206 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the forward pass of one Mixture-of-Experts
+ * layer on one AMD MI355X (gfx950), as hand-written HIP kernels.
+ *
+ * The layer (page "MoE 模型原理：路由、专家负载、容量、通信与推理成本", wrblog.cn,
+ * cited below as [MoE Principles]):
+ *   router scores        s_t = W_r x_t + b_r                         (§2.1)
+ *   softmax              p_{t,i} = exp(s_{t,i}) / sum_j exp(s_{t,j}) (§2.1)
+ *   top-k                S_t = TopK(p_t, k)                          (§2.2)
+ *   gates                p~_{t,i} = p_{t,i} / sum_{j in S_t} p_{t,j} (§2.2)
+ *   capacity             C = ceil(c * T * k / E)                     (§4.1)
+ *   first-come dispatch  token order, per-expert limit C, overflow dropped (§4.2, §4.3)
+ *   expert FFN           FFN(x) = W2 sigma(W1 x + b1) + b2           (§1)
+ *   combine              y_t = sum_{i in S_t} p~_{t,i} E_i(x_t)      (§2.2, §5)
+ *
+ * Conventions shared by every entry point:
+ *  - Every pointer argument other than `cfg` (a host pointer) is a DEVICE
+ *    pointer owned by the caller. The library never allocates, frees,
+ *    synchronises or prints; all work is enqueued on `stream` in order.
+ *  - Row-major, last index contiguous. x [T,d]; W_r [E,d]; b_r [E];
+ *    W1 [E,d_ff,d]; b1 [E,d_ff]; W2 [E,d,d_ff]; b2 [E,d]. W1[e] maps d -> d_ff.
+ *  - x, W_r, W1, W2, x_perm, h and y have element type cfg->dtype (MOE_F32 or
+ *    MOE_BF16, bf16 = the top 16 bits of an IEEE fp32). Biases, logits,
+ *    probabilities, gates and y_perm are fp32 for both dtypes.
+ *  - Top-k returns expert ids in descending score order; equal scores go to
+ *    the lower expert index. The choice is made on fp32 logits.
+ *  - Capacity is granted first-come in token order (a token's own k choices
+ *    go to distinct experts, so they never compete). A dropped assignment
+ *    contributes nothing; gates are not renormalised after drops; a token
+ *    whose every assignment was dropped gets y_t = 0.
+ *  - Dispatch layout: rows are expert-major and, within an expert, in token
+ *    order, packed from row 0 without padding. rows = sum_e min(count_e, C)
+ *    is never read back to the host; buffers indexed by row are sized by
+ *    the bound max_rows = min(T*k, E*C) (see moe_max_rows). Entries at and
+ *    beyond `rows` are left untouched.
+ *  - Return value: MOE_OK (0) or a negative MOE_ERR_* code. On error nothing
+ *    has been enqueued. T == 0 is a valid no-op returning MOE_OK.
+ *  - Results are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null required pointer, bad sizes, misaligned pointer */
+  MOE_ERR_UNSUPPORTED = -2, /* valid but not implemented (shape/dtype combination) */
+  MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than moe_workspace_size */
+  MOE_ERR_HIP = -4          /* a HIP launch or event call failed */
+};
+
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+enum { MOE_ACT_RELU = 0, MOE_ACT_GELU_TANH = 1 };
+enum { MOE_MAX_EXPERTS = 1024, MOE_MAX_TOPK = 16 };
+
+/* Stage boundaries for moe_layer_forward's optional events. */
+enum {
+  MOE_STAGE_ROUTE = 0,    /* router GEMM, softmax, top-k, gates, per-tile counts */
+  MOE_STAGE_DISPATCH = 1, /* prefix sums, slots, capacity, token permutation */
+  MOE_STAGE_GEMM1 = 2,    /* h = sigma(x_perm W1_e^T + b1_e), grouped over experts */
+  MOE_STAGE_GEMM2 = 3,    /* y_perm = h W2_e^T + b2_e, grouped over experts */
+  MOE_STAGE_COMBINE = 4,  /* gate-weighted gather back to token order */
+  MOE_NUM_STAGES = 5
+};
+
+/*
+ * The layer's shape and behaviour, validated at every entry point
+ * ([MoE Principles] §12 lists what must be pinned: expert count and sizes,
+ * top-k, capacity, combine rule, overflow behaviour).
+ *   T            tokens in the call; the whole call is one routing group.
+ *   d, d_ff      hidden and expert-hidden sizes. MOE_BF16 needs both to be
+ *                multiples of 64 (else MOE_ERR_UNSUPPORTED).
+ *   E, k         experts and experts per token: 1 <= k <= E <= MOE_MAX_EXPERTS,
+ *                k <= MOE_MAX_TOPK.
+ *   capacity     C >= 1 (from moe_capacity, or any caller choice; C >= T
+ *                means nothing is ever dropped).
+ *   renormalize  1: gates are the top-k probabilities divided by their sum;
+ *                0: gates are the plain softmax probabilities.
+ *   dtype        MOE_F32 or MOE_BF16.
+ *   act          sigma: MOE_ACT_RELU or MOE_ACT_GELU_TANH
+ *                (0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3)))).
+ */
+typedef struct moe_config {
+  int64_t T;
+  int32_t d, d_ff, E, k, capacity, renormalize, dtype, act;
+} moe_config;
+
+/*
+ * Optional routing outputs of moe_layer_forward (device pointers; any may be
+ * NULL, in which case that result stays in the workspace).
+ *   topk_ids [T,k] int32, topk_gates [T,k] fp32, prob_sum [E] fp32
+ *   (sum over tokens of p_{t,i}, for the load-balance statistics of
+ *   [MoE Principles] §3.2), expert_counts [E] int32 (before capacity),
+ *   expert_offsets [E+1] int32 (after capacity), slot [T,k] int32,
+ *   row_of [T,k] int32 (-1 = dropped), row_token [max_rows] int32.
+ */
+typedef struct moe_route_info {
+  int32_t *topk_ids;
+  float *topk_gates;
+  float *prob_sum;
+  int32_t *expert_counts;
+  int32_t *expert_offsets;
+  int32_t *slot;
+  int32_t *row_of;
+  int32_t *row_token;
+} moe_route_info;
+
+/*
+ * C = ceil(c * T * k / E) ([MoE Principles] §4.1; page "Expert Parallelism：
+ * 为什么让 Token 去找 Expert，而不是搬运参数？", section "Expert Capacity 和 Token
+ * Dropping"), computed exactly from the binary value of c (host only, no GPU).
+ * Errors: MOE_ERR_INVALID_ARG if C_out is NULL, T < 0, k < 1, E < 1, c is not
+ * finite or c <= 0, or the result exceeds INT32_MAX. T == 0 gives C = 0.
+ */
+int32_t moe_capacity(int64_t T, int32_t k, int32_t E, double c, int32_t *C_out);
+
+/* max_rows = min(T*k, E*C): the size of every row-indexed buffer (host only). */
+int32_t moe_max_rows(const moe_config *cfg, int64_t *rows);
+
+/* Workspace bytes moe_layer_forward needs; the stage entry points need no
+ * more than this (host only). */
+int32_t moe_workspace_size(const moe_config *cfg, size_t *bytes);
+
+/*
+ * Route ([MoE Principles] §2.1-§2.2; page "MiniMax 面试: MoE gate 与分布式通信",
+ * mianshidashi.cn, 深入解析 01: the gate emits scores, top-k ids and weights).
+ *   x [T,d], W_r [E,d] (dtype); b_r [E] fp32 or NULL (zero bias).
+ *   out topk_ids [T,k] int32, topk_gates [T,k] fp32 (required);
+ *   out prob_sum [E] fp32 or NULL; out logits [T,E] fp32 or NULL.
+ *   ws: at least moe_workspace_size bytes, 256-byte aligned.
+ */
+int32_t moe_route(const moe_config *cfg, const void *x, const void *W_r, const float *b_r,
+                  int32_t *topk_ids, float *topk_gates, float *prob_sum, float *logits,
+                  void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Dispatch ([MoE Principles] §4.2 capacity assignment and §5 dispatch
+ * metadata; MiniMax gate/communication page, 深入解析 02 and 06: counting,
+ * prefix sum, permutation into a contiguous buffer). Recounts from topk_ids.
+ *   in  x [T,d] (dtype), topk_ids [T,k] int32 (each row k distinct ids in [0,E)).
+ *   out expert_counts [E] int32: count_e = |{t : e in S_t}| (before capacity).
+ *   out expert_offsets [E+1] int32: prefix sums of n_e = min(count_e, C).
+ *   out slot [T,k] int32: slot(t,e) = |{t' < t : e in S_t'}|.
+ *   out row_of [T,k] int32: offsets[e] + slot if slot < C, else -1.
+ *   out row_token [max_rows] int32: the token held by each row.
+ *   out x_perm [max_rows,d] (dtype): x_perm[r] = x[row_token[r]] (bit copy).
+ * Behaviour is undefined if an id is out of range or repeated within a row.
+ */
+int32_t moe_dispatch(const moe_config *cfg, const void *x, const int32_t *topk_ids,
+                     int32_t *expert_counts, int32_t *expert_offsets, int32_t *slot,
+                     int32_t *row_of, int32_t *row_token, void *x_perm, void *ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Expert FFN over the expert-contiguous rows as one grouped GEMM per layer
+ * ([MoE Principles] §1 FFN; MiniMax gate/communication page, 60-second answer:
+ * batched or grouped GEMM per expert).
+ *   in  x_perm [max_rows,d] (dtype), expert_offsets [E+1] int32 (device).
+ *   in  W1 [E,d_ff,d], W2 [E,d,d_ff] (dtype); b1 [E,d_ff], b2 [E,d] fp32 or NULL.
+ *   out h [max_rows,d_ff] (dtype): sigma(x_perm W1_e^T + b1_e), rounded once.
+ *   out y_perm [max_rows,d] fp32: h W2_e^T + b2_e.
+ */
+int32_t moe_expert_ffn(const moe_config *cfg, const void *x_perm, const int32_t *expert_offsets,
+                       const void *W1, const float *b1, const void *W2, const float *b2,
+                       void *h, float *y_perm, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Combine ([MoE Principles] §2.2 output formula and §5 "send outputs back in
+ * token order and weight them"):
+ *   y_t = sum_{j<k, row_of[t,j] >= 0} topk_gates[t,j] * y_perm[row_of[t,j]],
+ *   summed over j = 0..k-1 in fp32 and rounded once to dtype.
+ *   in y_perm [max_rows,d] fp32, row_of [T,k] int32, topk_gates [T,k] fp32;
+ *   out y [T,d] (dtype).
+ */
+int32_t moe_combine(const moe_config *cfg, const float *y_perm, const int32_t *row_of,
+                    const float *topk_gates, void *y, hipStream_t stream);
+
+/*
+ * The whole layer: route -> dispatch -> grouped FFN -> combine
+ * ([MoE Principles] §5 data-flow figure, without the all-to-all steps).
+ *   x, W_r, W1, W2 (dtype); b_r, b1, b2 fp32 or NULL; out y [T,d] (dtype).
+ *   info: optional routing outputs (NULL: none).
+ *   ws/ws_bytes: at least moe_workspace_size bytes, 256-byte aligned.
+ *   stage_events: NULL, or MOE_NUM_STAGES+1 caller-created hipEvents that
+ *   are recorded on `stream` before the first stage and after each stage.
+ */
+int32_t moe_layer_forward(const moe_config *cfg, const void *x, const void *W_r,
+                          const float *b_r, const void *W1, const float *b1, const void *W2,
+                          const float *b2, void *y, const moe_route_info *info, void *ws,
+                          size_t ws_bytes, hipEvent_t *stage_events, hipStream_t stream);
+
+/* A static string naming a status code. */
+const char *moe_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -256,18 +256,17 @@ def sampled_outputs(tokens, x, ids, row_of, g, expert_weights, act: str) -> np.n
     kept assignment (t, j) the FFN of expert ids[t, j] on x_t, weighted by
     g[t, j]  [MoE Principles §2.2 output formula].
 
-    `expert_weights(e)` returns (W1_e, b1_e, W2_e, b2_e) in fp64."""
+    `expert_weights(e)` returns (W1_e, b1_e, W2_e, b2_e) in fp64; each expert's
+    weights are fetched once (the pairs are visited expert by expert)."""
     out = np.zeros((len(tokens), x.shape[1]), dtype=np.float64)
-    cache = {}
+    pairs = {}
     for n, t in enumerate(tokens):
         for j in range(ids.shape[1]):
-            if row_of[t, j] < 0:
-                continue
-            e = int(ids[t, j])
-            if e not in cache:
-                cache.clear()
-                cache[e] = expert_weights(e)
-            W1e, b1e, W2e, b2e = cache[e]
+            if row_of[t, j] >= 0:
+                pairs.setdefault(int(ids[t, j]), []).append((n, t, j))
+    for e in sorted(pairs):
+        W1e, b1e, W2e, b2e = expert_weights(e)
+        for n, t, j in pairs[e]:
             _, Y = expert_ffn(x[t:t + 1], W1e, b1e, W2e, b2e, act)
             out[n] += g[t, j] * Y[0]
     return out

@@ -1,0 +1,131 @@
+"""Shared helpers of the parity tests: run the HIP library and the fp64 oracle
+on the same seeded inputs and compare them.
+
+Tolerances (fixed before any kernel was written):
+  routing, dispatch, slots, overflow mask, rows, x_perm: bit-exact
+  gates: |gpu - oracle| <= 1e-6 (fp32 softmax of fp32 logits)
+  fp32 layers: max |y_gpu - y_oracle| <= 1e-5
+  bf16 layers: ||y_gpu - y_oracle||_2 / ||y_oracle||_2 <= 1e-2 and max-abs <= 3e-2
+A top-k decision whose oracle logit gap is below 1e-6 * max|s_t| is a
+near-tie: the GPU may take the other side; such flips are counted, and
+everything after routing is then compared against the oracle run on the
+GPU's expert ids (dispatch is a pure function of the ids).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import moe_oracle as mo
+from top_routing_expert_02_amd import synth
+
+GATE_ATOL = 1e-6
+F32_MAX_ABS = 1e-5
+BF16_REL_L2 = 1e-2
+BF16_MAX_ABS = 3e-2
+
+
+def host64(t: torch.Tensor, dtype: str) -> np.ndarray:
+    """Exact fp64 copy of a tensor's stored values."""
+    if t.dtype == torch.bfloat16:
+        return mo.widen(synth.to_numpy_bits(t), "bf16")
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+def host_inputs(inp: dict, dtype: str) -> dict:
+    return {k: host64(v, dtype) for k, v in inp.items()}
+
+
+def moe_mod():
+    from top_routing_expert_02_amd import moe
+    return moe
+
+
+def make_cfg(w, C):
+    moe = moe_mod()
+    return moe.config(w.T, w.d, w.d_ff, w.E, w.k, C, w.renormalize, w.dtype, w.act)
+
+
+def info_tensors(w, R, device):
+    i32 = dict(dtype=torch.int32, device=device)
+    f32 = dict(dtype=torch.float32, device=device)
+    return {
+        "topk_ids": torch.full((w.T, w.k), -7, **i32),
+        "topk_gates": torch.full((w.T, w.k), -7.0, **f32),
+        "prob_sum": torch.full((w.E,), -7.0, **f32),
+        "expert_counts": torch.full((w.E,), -7, **i32),
+        "expert_offsets": torch.full((w.E + 1,), -7, **i32),
+        "slot": torch.full((w.T, w.k), -7, **i32),
+        "row_of": torch.full((w.T, w.k), -7, **i32),
+        "row_token": torch.full((max(R, 1),), -7, **i32),
+    }
+
+
+def gpu_layer(w, inp, C, ws=None):
+    moe = moe_mod()
+    cfg = make_cfg(w, C)
+    R = moe.max_rows(cfg)
+    dev = inp["x"].device
+    info = info_tensors(w, R, dev)
+    y = torch.full((w.T, w.d), float("nan"), dtype=w.torch_dtype, device=dev)
+    if ws is None:
+        ws = moe.alloc_workspace(cfg, dev)
+    moe.layer_forward(cfg, inp["x"], inp["W_r"], inp["b_r"], inp["W1"], inp["b1"], inp["W2"],
+                      inp["b2"], y, info=info, ws=ws)
+    torch.cuda.synchronize()
+    return y, {k: v.cpu().numpy() for k, v in info.items()}, cfg
+
+
+def check_routing(o_route: dict, g_ids: np.ndarray) -> dict:
+    """Ids must match except at near-ties; returns counts for the report."""
+    mism = (g_ids != o_route["topk_ids"]).any(axis=1)
+    bad = mism & ~o_route["near_tie"]
+    assert not bad.any(), (f"{int(bad.sum())} tokens route differently without a near-tie, "
+                           f"first at {np.flatnonzero(bad)[:5].tolist()}")
+    return {"near_ties": int(o_route["near_tie"].sum()), "flips": int(mism.sum())}
+
+
+def check_gates(o_route: dict, g_ids, g_gates, renormalize):
+    ref = mo.gates(o_route["probs"], g_ids, renormalize)
+    err = np.abs(g_gates.astype(np.float64) - ref).max() if ref.size else 0.0
+    assert err <= GATE_ATOL, f"gate max error {err:.3e}"
+    return err
+
+
+def check_dispatch(g: dict, o: dict, rows_only=True):
+    for key in ("expert_counts", "expert_offsets", "slot", "row_of"):
+        np.testing.assert_array_equal(g[key], o[key], err_msg=key)
+    rows = o["rows"]
+    np.testing.assert_array_equal(g["row_token"][:rows], o["row_token"], err_msg="row_token")
+
+
+def compare_outputs(y_gpu64: np.ndarray, y_ref: np.ndarray, dtype: str) -> dict:
+    diff = y_gpu64 - y_ref
+    max_abs = float(np.abs(diff).max()) if diff.size else 0.0
+    nref = float(np.linalg.norm(y_ref))
+    rel = float(np.linalg.norm(diff) / nref) if nref > 0 else float(np.linalg.norm(diff))
+    if dtype == "f32":
+        assert max_abs <= F32_MAX_ABS, f"max-abs {max_abs:.3e} > {F32_MAX_ABS}"
+    else:
+        assert rel <= BF16_REL_L2, f"rel-L2 {rel:.3e} > {BF16_REL_L2}"
+        assert max_abs <= BF16_MAX_ABS, f"max-abs {max_abs:.3e} > {BF16_MAX_ABS}"
+    return {"max_abs": max_abs, "rel_l2": rel}
+
+
+def full_parity(w, inp, C, report=None):
+    """Whole-layer parity at sizes the oracle finishes in seconds."""
+    y, g, cfg = gpu_layer(w, inp, C)
+    h = host_inputs(inp, w.dtype)
+    o_route = mo.route(h["x"], h["W_r"], h["b_r"], w.k, w.renormalize)
+    stats = check_routing(o_route, g["topk_ids"])
+    check_gates(o_route, g["topk_ids"], g["topk_gates"], w.renormalize)
+    o = mo.layer_forward(h["x"], h["W_r"], h["b_r"], h["W1"], h["b1"], h["W2"], h["b2"],
+                         k=w.k, C=C, renormalize=w.renormalize, act=w.act, ids=g["topk_ids"])
+    check_dispatch(g, o)
+    np.testing.assert_allclose(g["prob_sum"], o["prob_sum"], rtol=1e-5, atol=1e-4)
+    stats.update(compare_outputs(host64(y, w.dtype), o["y"], w.dtype))
+    stats["rows"] = o["rows"]
+    stats["dropped"] = int((~o["kept"]).sum())
+    if report is not None:
+        report(f"{w.name}: {stats}")
+    return y, g, o, stats

@@ -1,0 +1,192 @@
+// Capacity-limited dispatch: per-expert counts, prefix sums, first-come slots
+// and the permutation of token rows into expert-contiguous buffers.
+//
+// Page "MoE 模型原理：路由、专家负载、容量、通信与推理成本" (wrblog.cn) §4.2 fixes
+// the rule: each expert accepts tokens until its capacity C is used up, later
+// tokens overflow, and spare capacity of one expert is not handed to another.
+// §5 lists the metadata (expert ids, buffer positions, combine weights); the
+// MiniMax gate/communication interview page (mianshidashi.cn, 深入解析 02 and
+// 06) names the counting, packing and contiguous-buffer permutation.
+//
+// slot(t,e) = |{t' < t : e in S_t'}| makes the result unique and the layout
+// deterministic, with no atomics deciding an order:
+//   1. per 64-token tile, count each expert's tokens (histogram);
+//   2. an exclusive prefix over tiles gives each tile its first slot per
+//      expert; counts, n_e = min(count_e, C) and offsets follow;
+//   3. inside a tile, a 64-bit mask per expert marks the tokens that chose it;
+//      popcount of the mask below a token gives its rank in the tile.
+#include "moe_internal.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ ids, int64_t T,
+                                                   int k, int E, int32_t* __restrict__ hist) {
+  __shared__ int h[1024];
+  const int64_t tile = blockIdx.x;
+  const int64_t t0 = tile * kTileTokens;
+  const int nt = static_cast<int>(min<int64_t>(kTileTokens, T - t0));
+  for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
+  __syncthreads();
+  for (int p = threadIdx.x; p < nt * k; p += 256) atomicAdd(&h[ids[t0 * k + p]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) hist[tile * E + e] = h[e];
+}
+
+// One block of 1024 threads. Experts are processed in chunks of up to 1024;
+// each chunk's experts get 1024/pow2(chunk) segments of consecutive tiles.
+// Segment sums -> exclusive prefix over segments -> per-tile bases.
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ hist, int ntiles,
+                                                    int E, int C, int32_t* __restrict__ base,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets) {
+  __shared__ int part[1024];
+  __shared__ int cnt[1024];
+  const int tid = threadIdx.x;
+  for (int e0 = 0; e0 < E; e0 += 1024) {
+    const int ec = min(E - e0, 1024);
+    int ecp = 1;
+    while (ecp < ec) ecp <<= 1;
+    const int segs = 1024 / ecp;
+    const int el = tid & (ecp - 1);
+    const int seg = tid / ecp;
+    const int len = (ntiles + segs - 1) / segs;
+    const int tb = min(ntiles, seg * len);
+    const int te = min(ntiles, tb + len);
+    const int e = e0 + el;
+    const bool valid = el < ec;
+    int sum = 0;
+    if (valid)
+      for (int t = tb; t < te; ++t) sum += hist[static_cast<int64_t>(t) * E + e];
+    part[tid] = sum;
+    __syncthreads();
+    if (valid && seg == 0) {
+      int run = 0;
+      for (int s = 0; s < segs; ++s) {
+        const int v = part[s * ecp + el];
+        part[s * ecp + el] = run;
+        run += v;
+      }
+      cnt[e] = run;
+    }
+    __syncthreads();
+    if (valid) {
+      int run = part[tid];
+      for (int t = tb; t < te; ++t) {
+        const int64_t i = static_cast<int64_t>(t) * E + e;
+        const int v = hist[i];
+        base[i] = run;
+        run += v;
+      }
+    }
+    __syncthreads();
+  }
+  // offsets: exclusive prefix of n_e = min(count_e, C) (Hillis-Steele in LDS)
+  int v = (tid < E) ? min(cnt[tid], C) : 0;
+  part[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int add = (tid >= off) ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  if (tid < E) {
+    counts[tid] = cnt[tid];
+    offsets[tid + 1] = part[tid];
+  }
+  if (tid == 0) offsets[0] = 0;
+}
+
+// One block per 64-token tile.
+template <int VEC>
+__global__ __launch_bounds__(256) void permute_kernel(
+    const char* __restrict__ x, const int32_t* __restrict__ ids, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ offsets, int64_t T, int k, int E, int C, int row_bytes,
+    int32_t* __restrict__ slot, int32_t* __restrict__ row_of, int32_t* __restrict__ row_token,
+    char* __restrict__ x_perm) {
+  __shared__ unsigned long long mask[1024];
+  __shared__ int rows[kTileTokens * 16];
+  const int64_t tile = blockIdx.x;
+  const int64_t t0 = tile * kTileTokens;
+  const int nt = static_cast<int>(min<int64_t>(kTileTokens, T - t0));
+  const int np = nt * k;
+  for (int e = threadIdx.x; e < E; e += 256) mask[e] = 0ull;
+  __syncthreads();
+  for (int p = threadIdx.x; p < np; p += 256)
+    atomicOr(&mask[ids[t0 * k + p]], 1ull << (p / k));
+  __syncthreads();
+  for (int p = threadIdx.x; p < np; p += 256) {
+    const int t = p / k;
+    const int e = ids[t0 * k + p];
+    const int rank = __popcll(mask[e] & ((1ull << t) - 1ull));
+    const int s = base[tile * E + e] + rank;
+    const int row = (s < C) ? offsets[e] + s : -1;
+    slot[t0 * k + p] = s;
+    row_of[t0 * k + p] = row;
+    if (row >= 0) row_token[row] = static_cast<int32_t>(t0 + t);
+    rows[p] = row;
+  }
+  __syncthreads();
+  // copy: a wave per token; the row is read once and written to each kept slot
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int t = wave; t < nt; t += 4) {
+    const char* src = x + (t0 + t) * static_cast<int64_t>(row_bytes);
+    for (int c = lane * VEC; c < row_bytes; c += 64 * VEC * 4) {
+      // up to four chunks in flight per lane
+      uint4 v4[4];
+      uint32_t v1[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int cc = c + u * 64 * VEC;
+        if (cc < row_bytes) {
+          if constexpr (VEC == 16) v4[u] = *reinterpret_cast<const uint4*>(src + cc);
+          else v1[u] = *reinterpret_cast<const uint32_t*>(src + cc);
+        }
+      }
+      for (int j = 0; j < k; ++j) {
+        const int row = rows[t * k + j];
+        if (row < 0) continue;
+        char* dst = x_perm + static_cast<int64_t>(row) * row_bytes;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int cc = c + u * 64 * VEC;
+          if (cc < row_bytes) {
+            if constexpr (VEC == 16) *reinterpret_cast<uint4*>(dst + cc) = v4[u];
+            else *reinterpret_cast<uint32_t*>(dst + cc) = v1[u];
+          }
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_hist(const int32_t* ids, int64_t T, int k, int E, int32_t* hist,
+                       hipStream_t s) {
+  hist_kernel<<<static_cast<unsigned>((T + kTileTokens - 1) / kTileTokens), 256, 0, s>>>(ids, T, k, E, hist);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const int32_t* hist, int ntiles, int E, int C, int32_t* base,
+                       int32_t* counts, int32_t* offsets, hipStream_t s) {
+  scan_kernel<<<1, 1024, 0, s>>>(hist, ntiles, E, C, base, counts, offsets);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const void* x, const int32_t* ids, const int32_t* base,
+                          const int32_t* offsets, int64_t T, int k, int E, int C,
+                          int row_bytes, int32_t* slot, int32_t* row_of, int32_t* row_token,
+                          void* x_perm, hipStream_t s) {
+  const unsigned grid = static_cast<unsigned>((T + kTileTokens - 1) / kTileTokens);
+  if (row_bytes % 16 == 0)
+    permute_kernel<16><<<grid, 256, 0, s>>>(static_cast<const char*>(x), ids, base, offsets, T, k, E, C,
+                                            row_bytes, slot, row_of, row_token,
+                                            static_cast<char*>(x_perm));
+  else
+    permute_kernel<4><<<grid, 256, 0, s>>>(static_cast<const char*>(x), ids, base, offsets, T, k, E, C,
+                                           row_bytes, slot, row_of, row_token,
+                                           static_cast<char*>(x_perm));
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,337 @@
+// Host side of the C ABI declared in include/moe.h: validation, workspace
+// layout and the order of kernel launches for each entry point. No entry
+// point allocates, frees, synchronises or prints.
+#include "moe.h"
+
+#include <climits>
+#include <cmath>
+
+#include "moe_internal.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int64_t ntiles_of(int64_t T) { return (T + kTileTokens - 1) / kTileTokens; }
+
+int64_t max_rows_of(const moe_config& c) {
+  const int64_t a = c.T * c.k;
+  const int64_t b = static_cast<int64_t>(c.E) * c.capacity;
+  return a < b ? a : b;
+}
+
+int elem_size(const moe_config& c) { return c.dtype == MOE_BF16 ? 2 : 4; }
+
+int32_t check_cfg(const moe_config* c) {
+  if (c == nullptr) return MOE_ERR_INVALID_ARG;
+  if (c->T < 0 || c->E < 1 || c->E > MOE_MAX_EXPERTS || c->k < 1 || c->k > c->E ||
+      c->k > MOE_MAX_TOPK || c->d < 1 || c->d_ff < 1 || c->capacity < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (c->T > 0 && c->capacity < 1) return MOE_ERR_INVALID_ARG;
+  if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->act != MOE_ACT_RELU && c->act != MOE_ACT_GELU_TANH) return MOE_ERR_INVALID_ARG;
+  // rows, slots and per-token indices are int32; tiles index a 32-bit grid
+  if (c->T > (static_cast<int64_t>(INT32_MAX) / c->k)) return MOE_ERR_UNSUPPORTED;
+  if (c->dtype == MOE_BF16 && (c->d % 64 != 0 || c->d_ff % 64 != 0)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+struct Layout {
+  size_t logits, prob_part, hist, base, ids, gates, counts, offsets, prob_sum, slot, row_of,
+      row_token, x_perm, h, y_perm, total;
+};
+
+Layout layout_of(const moe_config& c) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const size_t o = off;
+    off += round_up(static_cast<size_t>(bytes > 0 ? bytes : 0));
+    return o;
+  };
+  const int64_t T = c.T, E = c.E, k = c.k, R = max_rows_of(c), nt = ntiles_of(c.T);
+  const int es = elem_size(c);
+  L.logits = take(T * E * 4);
+  L.prob_part = take(nt * E * 4);
+  L.hist = take(nt * E * 4);
+  L.base = take(nt * E * 4);
+  L.ids = take(T * k * 4);
+  L.gates = take(T * k * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.prob_sum = take(E * 4);
+  L.slot = take(T * k * 4);
+  L.row_of = take(T * k * 4);
+  L.row_token = take(R * 4);
+  L.x_perm = take(R * c.d * es);
+  L.h = take(R * c.d_ff * es);
+  L.y_perm = take(R * c.d * 4);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int32_t check_ws(const moe_config& c, void* ws, size_t ws_bytes) {
+  if (ws == nullptr || !aligned(ws, kAlign) || ws_bytes < layout_of(c).total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+#define MOE_HIP(call)                               \
+  do {                                              \
+    if ((call) != hipSuccess) return MOE_ERR_HIP;   \
+  } while (0)
+
+// ---- stages (arguments already validated)
+
+int32_t route_stage(const moe_config& c, const void* x, const void* Wr, const float* br,
+                    int32_t* ids, float* gates, float* prob_sum, float* logits, float* prob_part,
+                    int32_t* hist, hipStream_t s) {
+  if (c.dtype == MOE_BF16)
+    MOE_HIP(launch_logits_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(Wr), br,
+                               logits, c.T, c.d, c.E, s));
+  else
+    MOE_HIP(launch_logits_f32(static_cast<const float*>(x), static_cast<const float*>(Wr), br, logits,
+                              c.T, c.d, c.E, s));
+  MOE_HIP(launch_topk(logits, c.T, c.E, c.k, c.renormalize, ids, gates,
+                      prob_sum != nullptr ? prob_part : nullptr, hist, s));
+  if (prob_sum != nullptr)
+    MOE_HIP(launch_prob_reduce(prob_part, static_cast<int>(ntiles_of(c.T)), c.E, prob_sum, s));
+  return MOE_OK;
+}
+
+int32_t dispatch_stage(const moe_config& c, const void* x, const int32_t* ids, bool hist_ready,
+                       int32_t* hist, int32_t* base, int32_t* counts, int32_t* offsets,
+                       int32_t* slot, int32_t* row_of, int32_t* row_token, void* x_perm,
+                       hipStream_t s) {
+  if (!hist_ready) MOE_HIP(launch_hist(ids, c.T, c.k, c.E, hist, s));
+  MOE_HIP(launch_scan(hist, static_cast<int>(ntiles_of(c.T)), c.E, c.capacity, base, counts, offsets, s));
+  MOE_HIP(launch_permute(x, ids, base, offsets, c.T, c.k, c.E, c.capacity, c.d * elem_size(c), slot,
+                         row_of, row_token, x_perm, s));
+  return MOE_OK;
+}
+
+int32_t gemm1_stage(const moe_config& c, const void* x_perm, const int32_t* offsets,
+                    const void* W1, const float* b1, void* h, hipStream_t s) {
+  const int64_t R = max_rows_of(c);
+  const int per_expert = static_cast<int>(c.T < c.capacity ? c.T : c.capacity);
+  if (c.dtype == MOE_BF16)
+    MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(x_perm), static_cast<const uint16_t*>(W1), b1, h,
+                             false, c.act, offsets, c.E, c.d_ff, c.d, R, per_expert, s));
+  else
+    MOE_HIP(launch_gemm_f32(static_cast<const float*>(x_perm), static_cast<const float*>(W1), b1,
+                            static_cast<float*>(h), c.act, offsets, c.E, c.d_ff, c.d, per_expert, s));
+  return MOE_OK;
+}
+
+int32_t gemm2_stage(const moe_config& c, const void* h, const int32_t* offsets, const void* W2,
+                    const float* b2, float* y_perm, hipStream_t s) {
+  const int64_t R = max_rows_of(c);
+  const int per_expert = static_cast<int>(c.T < c.capacity ? c.T : c.capacity);
+  if (c.dtype == MOE_BF16)
+    MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W2), b2, y_perm,
+                             true, kActNone, offsets, c.E, c.d, c.d_ff, R, per_expert, s));
+  else
+    MOE_HIP(launch_gemm_f32(static_cast<const float*>(h), static_cast<const float*>(W2), b2, y_perm,
+                            kActNone, offsets, c.E, c.d, c.d_ff, per_expert, s));
+  return MOE_OK;
+}
+
+int32_t combine_stage(const moe_config& c, const float* y_perm, const int32_t* row_of,
+                      const float* gates, void* y, hipStream_t s) {
+  MOE_HIP(launch_combine(y_perm, row_of, gates, c.T, c.k, c.d, c.dtype == MOE_BF16, y, s));
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)              \
+  do {                             \
+    const int32_t st_ = (expr);    \
+    if (st_ != MOE_OK) return st_; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_capacity(int64_t T, int32_t k, int32_t E, double c, int32_t* C_out) {
+  if (C_out == nullptr || T < 0 || k < 1 || E < 1 || !std::isfinite(c) || !(c > 0.0))
+    return MOE_ERR_INVALID_ARG;
+  if (T == 0) {
+    *C_out = 0;
+    return MOE_OK;
+  }
+  // c = m * 2^-s exactly, m a 53-bit integer; C = ceil(m*T*k / (E * 2^s)).
+  int ex = 0;
+  const double f = std::frexp(c, &ex);  // c = f * 2^ex, f in [0.5, 1)
+  if (ex < -39 || ex > 41) return MOE_ERR_INVALID_ARG;  // c outside [2^-40, 2^40]
+  const int64_t m = static_cast<int64_t>(std::ldexp(f, 53));
+  const int s = 53 - ex;  // in [12, 92]
+  if (T > (static_cast<int64_t>(1) << 62) / k) return MOE_ERR_INVALID_ARG;
+  const __int128 num = static_cast<__int128>(m) * T * k;
+  const __int128 den = static_cast<__int128>(E) << s;
+  const __int128 q = (num + den - 1) / den;
+  if (q > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  *C_out = static_cast<int32_t>(q);
+  return MOE_OK;
+}
+
+int32_t moe_max_rows(const moe_config* cfg, int64_t* rows) {
+  MOE_TRY(check_cfg(cfg));
+  if (rows == nullptr) return MOE_ERR_INVALID_ARG;
+  *rows = max_rows_of(*cfg);
+  return MOE_OK;
+}
+
+int32_t moe_workspace_size(const moe_config* cfg, size_t* bytes) {
+  MOE_TRY(check_cfg(cfg));
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  *bytes = layout_of(*cfg).total;
+  return MOE_OK;
+}
+
+int32_t moe_route(const moe_config* cfg, const void* x, const void* W_r, const float* b_r,
+                  int32_t* topk_ids, float* topk_gates, float* prob_sum, float* logits, void* ws,
+                  size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_config& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  if (x == nullptr || W_r == nullptr || topk_ids == nullptr || topk_gates == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(W_r, 16) || !aligned(b_r, 4) || !aligned(topk_ids, 4) ||
+      !aligned(topk_gates, 4) || !aligned(prob_sum, 4) || !aligned(logits, 4))
+    return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_ws(c, ws, ws_bytes));
+  const Layout L = layout_of(c);
+  return route_stage(c, x, W_r, b_r, topk_ids, topk_gates, prob_sum,
+                     logits != nullptr ? logits : at<float>(ws, L.logits), at<float>(ws, L.prob_part),
+                     nullptr, stream);
+}
+
+int32_t moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_ids,
+                     int32_t* expert_counts, int32_t* expert_offsets, int32_t* slot,
+                     int32_t* row_of, int32_t* row_token, void* x_perm, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_config& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  if (x == nullptr || topk_ids == nullptr || expert_counts == nullptr ||
+      expert_offsets == nullptr || slot == nullptr || row_of == nullptr || row_token == nullptr ||
+      x_perm == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(x_perm, 16) || !aligned(topk_ids, 4) ||
+      !aligned(expert_counts, 4) || !aligned(expert_offsets, 4) || !aligned(slot, 4) ||
+      !aligned(row_of, 4) || !aligned(row_token, 4))
+    return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_ws(c, ws, ws_bytes));
+  const Layout L = layout_of(c);
+  return dispatch_stage(c, x, topk_ids, false, at<int32_t>(ws, L.hist), at<int32_t>(ws, L.base),
+                        expert_counts, expert_offsets, slot, row_of, row_token, x_perm, stream);
+}
+
+int32_t moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
+                       const void* W1, const float* b1, const void* W2, const float* b2, void* h,
+                       float* y_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_config& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  if (x_perm == nullptr || expert_offsets == nullptr || W1 == nullptr || W2 == nullptr ||
+      h == nullptr || y_perm == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x_perm, 16) || !aligned(W1, 16) || !aligned(W2, 16) || !aligned(b1, 16) ||
+      !aligned(b2, 16) || !aligned(h, 16) || !aligned(y_perm, 16) || !aligned(expert_offsets, 4))
+    return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_ws(c, ws, ws_bytes));
+  MOE_TRY(gemm1_stage(c, x_perm, expert_offsets, W1, b1, h, stream));
+  return gemm2_stage(c, h, expert_offsets, W2, b2, y_perm, stream);
+}
+
+int32_t moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* row_of,
+                    const float* topk_gates, void* y, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_config& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  if (y_perm == nullptr || row_of == nullptr || topk_gates == nullptr || y == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(y_perm, 16) || !aligned(y, 16) || !aligned(row_of, 4) || !aligned(topk_gates, 4))
+    return MOE_ERR_INVALID_ARG;
+  return combine_stage(c, y_perm, row_of, topk_gates, y, stream);
+}
+
+int32_t moe_layer_forward(const moe_config* cfg, const void* x, const void* W_r,
+                          const float* b_r, const void* W1, const float* b1, const void* W2,
+                          const float* b2, void* y, const moe_route_info* info, void* ws,
+                          size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_config& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  if (x == nullptr || W_r == nullptr || W1 == nullptr || W2 == nullptr || y == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(W_r, 16) || !aligned(W1, 16) || !aligned(W2, 16) ||
+      !aligned(y, 16) || !aligned(b_r, 4) || !aligned(b1, 16) || !aligned(b2, 16))
+    return MOE_ERR_INVALID_ARG;
+  moe_route_info in{};
+  if (info != nullptr) in = *info;
+  if (!aligned(in.topk_ids, 4) || !aligned(in.topk_gates, 4) || !aligned(in.prob_sum, 4) ||
+      !aligned(in.expert_counts, 4) || !aligned(in.expert_offsets, 4) || !aligned(in.slot, 4) ||
+      !aligned(in.row_of, 4) || !aligned(in.row_token, 4))
+    return MOE_ERR_INVALID_ARG;
+  if (stage_events != nullptr)
+    for (int i = 0; i <= MOE_NUM_STAGES; ++i)
+      if (stage_events[i] == nullptr) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_ws(c, ws, ws_bytes));
+
+  const Layout L = layout_of(c);
+  int32_t* ids = in.topk_ids != nullptr ? in.topk_ids : at<int32_t>(ws, L.ids);
+  float* gates = in.topk_gates != nullptr ? in.topk_gates : at<float>(ws, L.gates);
+  int32_t* counts = in.expert_counts != nullptr ? in.expert_counts : at<int32_t>(ws, L.counts);
+  int32_t* offsets = in.expert_offsets != nullptr ? in.expert_offsets : at<int32_t>(ws, L.offsets);
+  int32_t* slot = in.slot != nullptr ? in.slot : at<int32_t>(ws, L.slot);
+  int32_t* row_of = in.row_of != nullptr ? in.row_of : at<int32_t>(ws, L.row_of);
+  int32_t* row_token = in.row_token != nullptr ? in.row_token : at<int32_t>(ws, L.row_token);
+  void* x_perm = at<char>(ws, L.x_perm);
+  void* h = at<char>(ws, L.h);
+  float* y_perm = at<float>(ws, L.y_perm);
+  int32_t* hist = at<int32_t>(ws, L.hist);
+
+  auto mark = [&](int i) -> int32_t {
+    if (stage_events != nullptr && hipEventRecord(stage_events[i], stream) != hipSuccess)
+      return MOE_ERR_HIP;
+    return MOE_OK;
+  };
+  MOE_TRY(mark(0));
+  MOE_TRY(route_stage(c, x, W_r, b_r, ids, gates, in.prob_sum, at<float>(ws, L.logits),
+                      at<float>(ws, L.prob_part), hist, stream));
+  MOE_TRY(mark(1));
+  MOE_TRY(dispatch_stage(c, x, ids, true, hist, at<int32_t>(ws, L.base), counts, offsets, slot,
+                         row_of, row_token, x_perm, stream));
+  MOE_TRY(mark(2));
+  MOE_TRY(gemm1_stage(c, x_perm, offsets, W1, b1, h, stream));
+  MOE_TRY(mark(3));
+  MOE_TRY(gemm2_stage(c, h, offsets, W2, b2, y_perm, stream));
+  MOE_TRY(mark(4));
+  MOE_TRY(combine_stage(c, y_perm, row_of, gates, y, stream));
+  return mark(5);
+}
+
+const char* moe_status_string(int32_t status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_ERR_HIP: return "HIP launch or event error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Internal declarations shared by the host API and the kernel launchers of
+// libmoe.so. Not part of the public ABI (that is include/moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Tokens per dispatch tile: the unit of the per-tile expert histograms and of
+// the permutation kernel (one 64-bit lane mask per expert and tile).
+constexpr int kTileTokens = 64;
+
+// M tile of the bf16 grouped GEMM (tokens per tile).
+constexpr int kGemmBM = 256;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// sigma of the expert FFN. tanh-GELU written as u * sigmoid(2z) with
+// z = sqrt(2/pi) (u + 0.044715 u^3), which equals 0.5 u (1 + tanh z).
+__device__ __forceinline__ float act_relu(float u) { return u > 0.f ? u : 0.f; }
+__device__ __forceinline__ float act_gelu_tanh(float u) {
+  const float z = 0.7978845608028654f * (u + 0.044715f * u * u * u);
+  return u / (1.0f + __expf(-2.0f * z));
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns the first HIP error of its launches (hipSuccess if none).
+
+// logits[t,e] = b_r[e] + sum_m x[t,m] W_r[e,m]  (fp32 result)
+hipError_t launch_logits_bf16(const uint16_t* x, const uint16_t* Wr, const float* br,
+                              float* logits, int64_t T, int d, int E, hipStream_t s);
+hipError_t launch_logits_f32(const float* x, const float* Wr, const float* br, float* logits,
+                             int64_t T, int d, int E, hipStream_t s);
+
+// softmax, top-k, gates; optional per-tile prob sums [ntiles,E] and expert
+// histograms [ntiles,E] (tile = kTileTokens tokens).
+hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int renormalize,
+                       int32_t* ids, float* gates, float* prob_part, int32_t* hist,
+                       hipStream_t s);
+// out[e] = sum over tiles of part[tile,e], tiles in order.
+hipError_t launch_prob_reduce(const float* part, int ntiles, int E, float* out, hipStream_t s);
+
+// per-tile expert histograms from topk ids
+hipError_t launch_hist(const int32_t* ids, int64_t T, int k, int E, int32_t* hist,
+                       hipStream_t s);
+// column-wise exclusive prefix of hist over tiles (base), counts, offsets
+hipError_t launch_scan(const int32_t* hist, int ntiles, int E, int C, int32_t* base,
+                       int32_t* counts, int32_t* offsets, hipStream_t s);
+// slots, capacity, row_of, row_token and the row copy into x_perm
+hipError_t launch_permute(const void* x, const int32_t* ids, const int32_t* base,
+                          const int32_t* offsets, int64_t T, int k, int E, int C,
+                          int row_bytes, int32_t* slot, int32_t* row_of, int32_t* row_token,
+                          void* x_perm, hipStream_t s);
+
+// grouped expert GEMMs
+//   gemm1: h = act(A W1_e^T + b1_e)   A [rows,K=d], W1 [E,N=d_ff,K], h [rows,N]
+//   gemm2: y = A W2_e^T + b2_e        A [rows,K=d_ff], W2 [E,N=d,K], y fp32 [rows,N]
+hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, void* out,
+                            bool out_f32, int act, const int32_t* offsets, int E, int N, int K,
+                            int64_t max_rows, int max_rows_per_expert, hipStream_t s);
+hipError_t launch_gemm_f32(const float* A, const float* W, const float* bias, float* out,
+                           int act, const int32_t* offsets, int E, int N, int K,
+                           int max_rows_per_expert, hipStream_t s);
+
+// y[t] = sum_j gates[t,j] y_perm[row_of[t,j]] (kept j only), rounded once
+hipError_t launch_combine(const float* y_perm, const int32_t* row_of, const float* gates,
+                          int64_t T, int k, int d, bool out_bf16, void* y, hipStream_t s);
+
+// activation codes (same values as MOE_ACT_*)
+constexpr int kActRelu = 0;
+constexpr int kActGeluTanh = 1;
+constexpr int kActNone = -1;
+
+}  // namespace moe

@@ -1,0 +1,338 @@
+// Routing kernels: router scores, softmax, top-k and gates.
+//
+// Router scores s_t = W_r x_t + b_r, softmax over the E experts, top-k
+// selection and renormalised gates follow page "MoE 模型原理：路由、专家负载、
+// 容量、通信与推理成本" (wrblog.cn) §2.1 and §2.2. Top-k is taken on the fp32
+// logits (softmax is strictly increasing), ids in descending score order,
+// equal scores to the lower expert index.
+#include "moe_internal.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ logits (bf16, MFMA)
+//
+// A block computes a (16*MT tokens) x (16*NT experts) tile of the logits with
+// v_mfma_f32_16x16x32_bf16: x rows are the A operand, W_r rows the B operand.
+// The four waves split the d axis (wave w takes the 32-wide K steps w, w+4,
+// ...); their partial sums meet in LDS and are added in a fixed order.
+// Operands come straight from global memory: the kernel streams x once and
+// re-reads W_r (E*d*2 bytes) from L2 per token tile.
+template <int MT, int NT>
+__global__ __launch_bounds__(256) void logits_bf16_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ Wr,
+                                                          const float* __restrict__ br,
+                                                          float* __restrict__ logits, int64_t T,
+                                                          int d, int E) {
+  constexpr int NREG = MT * NT * 4;
+  __shared__ float red[3][NREG][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * (16 * MT);
+  const int e0 = blockIdx.y * (16 * NT);
+  const int kq = (lane >> 4) * 8;  // this lane's 8 consecutive k inside a 32-wide step
+
+  const uint16_t* xr[MT];
+  const uint16_t* wr[NT];
+  bool wvalid[NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    int64_t t = t0 + mt * 16 + (lane & 15);
+    if (t >= T) t = T - 1;  // clamp: rows past T are computed and discarded
+    xr[mt] = x + t * d + kq;
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    int e = e0 + nt * 16 + (lane & 15);
+    wvalid[nt] = e < E;
+    if (!wvalid[nt]) e = E - 1;
+    wr[nt] = Wr + static_cast<int64_t>(e) * d + kq;
+  }
+
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = wave * 32; k0 < d; k0 += 128) {
+    bf16x8_t a[MT], b[NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      a[mt] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xr[mt] + k0));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      uint4 v = *reinterpret_cast<const uint4*>(wr[nt] + k0);
+      if (!wvalid[nt]) v = make_uint4(0, 0, 0, 0);
+      b[nt] = __builtin_bit_cast(bf16x8_t, v);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
+  }
+
+  if (wave > 0) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave - 1][(mt * NT + nt) * 4 + i][lane] = acc[mt][nt][i];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int e = e0 + nt * 16 + (lane & 15);
+      const float bias = (br != nullptr && e < E) ? br[e] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = (mt * NT + nt) * 4 + i;
+        float v = acc[mt][nt][i];
+        v += red[0][r][lane];
+        v += red[1][r][lane];
+        v += red[2][r][lane];
+        // output layout of the 16x16 MFMA: lane holds rows 4*(lane/16)+i, column lane%16
+        const int64_t t = t0 + mt * 16 + (lane >> 4) * 4 + i;
+        if (t < T && e < E) logits[t * E + e] = v + bias;
+      }
+    }
+}
+
+// ------------------------------------------------------------------ logits (fp32)
+// One wave per token; lanes split d; one wave-wide sum per expert.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__global__ __launch_bounds__(256) void logits_f32_kernel(const float* __restrict__ x,
+                                                         const float* __restrict__ Wr,
+                                                         const float* __restrict__ br,
+                                                         float* __restrict__ logits, int64_t T,
+                                                         int d, int E) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* xt = x + t * d;
+  for (int e = 0; e < E; ++e) {
+    const float* we = Wr + static_cast<int64_t>(e) * d;
+    float s = 0.f;
+    for (int m = lane; m < d; m += 64) s = fmaf(xt[m], we[m], s);
+    s = wave_sum(s);
+    if (lane == 0) logits[t * E + e] = s + (br != nullptr ? br[e] : 0.f);
+  }
+}
+
+// ------------------------------------------------------------------ top-k, softmax, gates
+//
+// A block owns one tile of 64 tokens; each wave owns 16 of them. A token is
+// handled by a group of G lanes (G a power of two, 4 <= G <= 64); lane g of
+// the group holds the logits of experts g, g+G, ... (NV of them).
+//
+// Round r of k picks the group-wide best (largest logit, then lowest index)
+// among the experts not yet taken, by an xor butterfly over the group; the
+// comparison is a strict total order, so every lane ends with the same
+// winner. Lane r of the group keeps the winner of round r.
+//
+// p_{t,i} = exp(s_{t,i} - m) / sum_j exp(s_{t,j} - m) with m the top logit;
+// gates are exp(s - m) of the chosen experts divided by their sum
+// (renormalised) or by the full sum (plain softmax probability). Butterfly
+// sums add the same two operands on both partner lanes, so every lane holds
+// a bit-identical total and reruns are bit-exact.
+//
+// Side outputs per tile: the expert histogram (integer LDS atomics, order
+// free) and sum_t p_{t,i} (fixed-order sums: lanes, then groups, then waves).
+template <int G, int NV>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int64_t T,
+                                                   int E, int k, int renormalize,
+                                                   int32_t* __restrict__ ids,
+                                                   float* __restrict__ gates,
+                                                   float* __restrict__ prob_part,
+                                                   int32_t* __restrict__ hist) {
+  constexpr int TPW = 64 / G;      // tokens per wave pass
+  constexpr int PASSES = 16 / TPW;  // passes per wave (16 tokens per wave)
+  __shared__ float s_prob[4][1024];
+  __shared__ int s_hist[1024];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int gl = lane & (G - 1);   // lane inside the group
+  const int grp = lane / G;        // group inside the wave
+  const int64_t tile = blockIdx.x;
+  const bool want_prob = prob_part != nullptr;
+  const bool want_hist = hist != nullptr;
+
+  if (want_hist)
+    for (int e = threadIdx.x; e < E; e += 256) s_hist[e] = 0;
+  __syncthreads();
+
+  float psum[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) psum[j] = 0.f;
+
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int64_t t = tile * 64 + wave * 16 + pass * TPW + grp;
+    const bool tv = t < T;
+    const float* row = logits + (tv ? t : 0) * E;
+    float v[NV];
+    uint32_t taken = 0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int e = gl + j * G;
+      if (e < E && tv) {
+        v[j] = row[e];
+      } else {
+        v[j] = 0.f;
+        taken |= 1u << j;  // not an expert: never chosen, not summed
+      }
+    }
+    const uint32_t invalid = taken;
+
+    float my_v = 0.f, top = 0.f;
+    int my_id = -1;
+    for (int r = 0; r < k; ++r) {
+      float bv = -__builtin_inff();
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int e = gl + j * G;
+        if (!((taken >> j) & 1u) && (v[j] > bv || (v[j] == bv && e < bi))) {
+          bv = v[j];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int off = G / 2; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, 64);
+        const int oi = __shfl_xor(bi, off, 64);
+        if (ov > bv || (ov == bv && oi < bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if (r == 0) top = bv;
+      if ((bi & (G - 1)) == gl && bi < E) taken |= 1u << (bi / G);
+      if (gl == r) {
+        my_v = bv;
+        my_id = bi;
+      }
+    }
+
+    // softmax denominator
+    float ex[NV];
+    float se = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      ex[j] = ((invalid >> j) & 1u) ? 0.f : __expf(v[j] - top);
+      se += ex[j];
+    }
+#pragma unroll
+    for (int off = G / 2; off >= 1; off >>= 1) se += __shfl_xor(se, off, 64);
+
+    const float mine = (gl < k) ? __expf(my_v - top) : 0.f;
+    float den = se;
+    if (renormalize) {
+      den = mine;
+#pragma unroll
+      for (int off = G / 2; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
+    }
+    if (tv && gl < k) {
+      ids[t * k + gl] = my_id;
+      gates[t * k + gl] = mine / den;
+      if (want_hist) atomicAdd(&s_hist[my_id], 1);
+    }
+    if (want_prob && tv) {
+      const float inv = 1.0f / se;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) psum[j] += ex[j] * inv;
+    }
+  }
+
+  if (want_prob) {
+    // groups of the wave hold the same experts for different tokens
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int off = G; off < 64; off <<= 1) psum[j] += __shfl_xor(psum[j], off, 64);
+    if (grp == 0) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int e = gl + j * G;
+        if (e < E) s_prob[wave][e] = psum[j];
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) {
+    if (want_prob)
+      prob_part[tile * E + e] = ((s_prob[0][e] + s_prob[1][e]) + s_prob[2][e]) + s_prob[3][e];
+    if (want_hist) hist[tile * E + e] = s_hist[e];
+  }
+}
+
+__global__ __launch_bounds__(256) void prob_reduce_kernel(const float* __restrict__ part,
+                                                          int ntiles, int E,
+                                                          float* __restrict__ out) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  float s = 0.f;
+  for (int t = 0; t < ntiles; ++t) s += part[static_cast<int64_t>(t) * E + e];
+  out[e] = s;
+}
+
+// ------------------------------------------------------------------ launchers
+
+hipError_t launch_logits_bf16(const uint16_t* x, const uint16_t* Wr, const float* br,
+                              float* logits, int64_t T, int d, int E, hipStream_t s) {
+  if (E <= 16) {
+    dim3 grid(static_cast<unsigned>((T + 15) / 16), 1);
+    logits_bf16_kernel<1, 1><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E);
+  } else if (E <= 32) {
+    dim3 grid(static_cast<unsigned>((T + 15) / 16), 1);
+    logits_bf16_kernel<1, 2><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E);
+  } else if (E <= 64) {
+    dim3 grid(static_cast<unsigned>((T + 15) / 16), 1);
+    logits_bf16_kernel<1, 4><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E);
+  } else {
+    dim3 grid(static_cast<unsigned>((T + 63) / 64), static_cast<unsigned>((E + 63) / 64));
+    logits_bf16_kernel<4, 4><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_logits_f32(const float* x, const float* Wr, const float* br, float* logits,
+                             int64_t T, int d, int E, hipStream_t s) {
+  logits_f32_kernel<<<static_cast<unsigned>((T + 3) / 4), 256, 0, s>>>(x, Wr, br, logits, T, d, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int renormalize,
+                       int32_t* ids, float* gates, float* prob_part, int32_t* hist,
+                       hipStream_t s) {
+  const unsigned grid = static_cast<unsigned>((T + 63) / 64);
+#define MOE_TOPK(G, NV) \
+  topk_kernel<G, NV><<<grid, 256, 0, s>>>(logits, T, E, k, renormalize, ids, gates, prob_part, hist)
+  if (E <= 4) MOE_TOPK(4, 1);
+  else if (E <= 8) MOE_TOPK(8, 1);
+  else if (E <= 16) MOE_TOPK(16, 1);
+  else if (E <= 32) MOE_TOPK(32, 1);
+  else if (E <= 64) MOE_TOPK(64, 1);
+  else if (E <= 128) MOE_TOPK(64, 2);
+  else if (E <= 256) MOE_TOPK(64, 4);
+  else if (E <= 512) MOE_TOPK(64, 8);
+  else MOE_TOPK(64, 16);
+#undef MOE_TOPK
+  return hipGetLastError();
+}
+
+hipError_t launch_prob_reduce(const float* part, int ntiles, int E, float* out, hipStream_t s) {
+  prob_reduce_kernel<<<(E + 255) / 256, 256, 0, s>>>(part, ntiles, E, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe
