@@ -13,20 +13,20 @@
 // Both operands are K-contiguous (A row-major [rows, K]; W[e] row-major [N, K]).
 //
 // Design (gfx950, wave64, 160 KiB LDS per CU):
-//  * Block tile BM=256 tokens x BN features x BK=64, four waves in a 2x2 grid;
+//  * Block tile BM=256 tokens x BN features, K in steps of BK=32; four waves
+//    in a 2x2 grid;
 //    each wave owns 128 tokens x BN/2 features as 32x32 v_mfma_f32_32x32x16_bf16
 //    tiles. The weight tile is the MFMA A operand and the token tile the B
 //    operand, so a lane's accumulators hold 4 consecutive features of one
 //    token: the epilogue stores 8-byte (bf16) or 16-byte (fp32) vectors.
-//  * LDS holds two stages of both tiles (128 KiB at BN=256). Rows are 128 B
-//    (64 bf16); the eight 16-byte chunks of a row are XOR-swizzled with
-//    ((row + row/8) & 7) so that ds_read_b128 of 16 consecutive rows at one
-//    chunk touches every bank once.
+//  * LDS holds four stages of both tiles (128 KiB at BN=256): tiles kt+1..kt+3
+//    are in flight while kt computes. Rows are 64 B (32 bf16); the four
+//    16-byte chunks of a row are XOR-swizzled by the row's 256-byte block,
+//    which makes the fragment reads conflict-free.
 //  * Tiles move global -> LDS with gfx950's LDS-DMA loads (global_load_lds_
 //    dwordx4: no staging registers, no ds_write); each lane fetches the chunk
-//    the swizzle places at its LDS slot. Double buffered: the loads of K tile
-//    kt+1 are in flight while tile kt feeds the matrix cores; one barrier per
-//    K tile. Fragments of K16 step s+1 are read from LDS during step s.
+//    the swizzle places at its LDS slot; one barrier per stage. The next
+//    tile's first three stages load during the current tile's epilogue.
 //  * Persistent blocks, one per CU. The schedule is computed on the device
 //    from expert_offsets (no host read-back): expert-major tiles, M tiles of
 //    an expert innermost, so concurrent tiles share weight panels. Blocks are
@@ -40,23 +40,27 @@ namespace moe {
 
 namespace {
 
-constexpr int BM = kGemmBM;  // 256
-constexpr int BK = 64;
-constexpr int ROWB = BK * 2;  // bytes per LDS row
+constexpr int BM = kGemmBM;   // 256 token rows per tile
+constexpr int BK = 32;        // K per LDS stage
+constexpr int ROWB = BK * 2;  // bytes per LDS row (64)
+constexpr int NST = 4;        // LDS stages: up to four K tiles in flight
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return chunk ^ ((row + (row >> 3)) & 7);
-}
+// Row r of a stage holds its 16-byte chunk c at position c ^ swz_key(r): the
+// key is the row's 256-byte block (mod 4). With it the MFMA fragment reads
+// (32 consecutive rows at one chunk, per ds_read_b128) run at the LDS's full
+// 256 B/clk (4 cycles per instruction); measured with SQ_LDS_BANK_CONFLICT,
+// unswizzled rows take 16 cycles and keys r&3 or (r/2)&3 take 8.
+__device__ __forceinline__ int swz_key(int row) { return (row >> 2) & 3; }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Queue one K tile (BK columns) of the token and weight tiles into LDS stage
-// `sb` with LDS-DMA loads: instruction i of wave w fills the 1 KiB block
-// w*L+i, i.e. rows 8(w*L+i) .. 8(w*L+i)+7.
+// Queue one stage (BK columns of the token and weight tiles) with LDS-DMA
+// loads. One global_load_lds_dwordx4 fills 1 KiB = 16 rows of 64 B; wave w's
+// instruction i fills block w*L+i.
 template <int LA, int LB, int A_BYTES>
-__device__ __forceinline__ void issue_tile(const uint16_t* ak, const uint16_t* wk, char* sb,
-                                           const int (&aoffs)[LA], const int (&boffs)[LB],
-                                           int wave) {
+__device__ __forceinline__ void issue_stage(const char* ak, const char* wk, char* sb,
+                                            const uint32_t (&aoffs)[LA],
+                                            const uint32_t (&boffs)[LB], int wave) {
 #pragma unroll
   for (int i = 0; i < LA; ++i)
     __builtin_amdgcn_global_load_lds(ak + aoffs[i], (lds_void_t*)(sb + (wave * LA + i) * 1024), 16, 0, 0);
@@ -66,72 +70,248 @@ __device__ __forceinline__ void issue_tile(const uint16_t* ak, const uint16_t* w
                                      16, 0, 0);
 }
 
-// Fragments of K16 step s: tokens tile j (rows 32j..32j+31 of the wave's
-// token rows) and weights tile i.
-template <int TM, int TN>
-__device__ __forceinline__ void load_frags(const char* tb, const char* wb, const int (&fo)[4], int s,
-                                           bf16x8_t (&tf)[TM], bf16x8_t (&wf)[TN]) {
-#pragma unroll
-  for (int j = 0; j < TM; ++j)
-    tf[j] = *reinterpret_cast<const bf16x8_t*>(tb + j * 32 * ROWB + fo[s ^ ((j & 1) * 2)]);
-#pragma unroll
-  for (int i = 0; i < TN; ++i)
-    wf[i] = *reinterpret_cast<const bf16x8_t*>(wb + i * 32 * ROWB + fo[s ^ ((i & 1) * 2)]);
+// ---- hand-scheduled K16 steps
+//
+// A wave issues MFMAs one at a time (an MFMA waits for the matrix core), so
+// LDS latency is hidden only by reads issued between MFMAs. The compiler
+// cannot place them there: its wait insertion treats any LDS read as
+// dependent on every LDS-DMA load in flight and waits for all of them, which
+// would serialise the stage pipeline. Each block below therefore issues the
+// MFMAs of one K16 step interleaved with the reads of the next step's
+// fragments, and waits for those reads before it ends: no read is in flight
+// past a block. Stage order is explicit (wait_stage and a barrier before a
+// stage is read). Each block starts with two wait states (a VALU write of an
+// MFMA source register needs them).
+//   acc[i][j] += W_i * T_j: W = weight fragments (MFMA A operand),
+//   T = token fragments (B operand); next fragments from ta / wa, tiles
+//   2048 B apart.
+#define MOE_MFMA(D, A, B) "v_mfma_f32_32x32x16_bf16 " D ", " A ", " B ", " D "\n\t"
+#define MOE_RD(D, ADDR, OFF) "ds_read_b128 " D ", " ADDR " offset:" OFF "\n\t"
+
+__device__ __forceinline__ void step_4x4(f32x16_t (&acc)[4][4], const bf16x8_t (&w)[4],
+                                         const bf16x8_t (&t)[4], bf16x8_t (&nw)[4],
+                                         bf16x8_t (&nt)[4], uint32_t ta, uint32_t wa) {
+  asm volatile(
+      "s_nop 1\n\t"
+      MOE_MFMA("%0", "%24", "%28") MOE_RD("%16", "%32", "0")
+      MOE_MFMA("%1", "%24", "%29") MOE_RD("%17", "%32", "2048")
+      MOE_MFMA("%2", "%24", "%30") MOE_RD("%18", "%32", "4096")
+      MOE_MFMA("%3", "%24", "%31") MOE_RD("%19", "%32", "6144")
+      MOE_MFMA("%4", "%25", "%28") MOE_RD("%20", "%33", "0")
+      MOE_MFMA("%5", "%25", "%29") MOE_RD("%21", "%33", "2048")
+      MOE_MFMA("%6", "%25", "%30") MOE_RD("%22", "%33", "4096")
+      MOE_MFMA("%7", "%25", "%31") MOE_RD("%23", "%33", "6144")
+      MOE_MFMA("%8", "%26", "%28") MOE_MFMA("%9", "%26", "%29")
+      MOE_MFMA("%10", "%26", "%30") MOE_MFMA("%11", "%26", "%31")
+      MOE_MFMA("%12", "%27", "%28") MOE_MFMA("%13", "%27", "%29")
+      MOE_MFMA("%14", "%27", "%30") MOE_MFMA("%15", "%27", "%31")
+      "s_waitcnt lgkmcnt(0)"
+      : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]), "+a"(acc[1][0]),
+        "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]), "+a"(acc[2][0]), "+a"(acc[2][1]),
+        "+a"(acc[2][2]), "+a"(acc[2][3]), "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]),
+        "+a"(acc[3][3]), "=&v"(nt[0]), "=&v"(nt[1]), "=&v"(nt[2]), "=&v"(nt[3]), "=&v"(nw[0]),
+        "=&v"(nw[1]), "=&v"(nw[2]), "=&v"(nw[3])
+      : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3]),
+        "v"(ta), "v"(wa)
+      : "memory");
 }
 
-// One BK-wide K tile from LDS stage `st` into the accumulators; fragments of
-// step s+1 are read while step s runs on the matrix cores.
-template <int TM, int TN, int A_BYTES, int WM, int WN>
-__device__ __forceinline__ void compute_tile(const char* st, const int (&fo)[4], int wm, int wn,
-                                             f32x16_t (&acc)[TN][TM]) {
-  const char* tb = st + wm * WM * ROWB;
-  const char* wb = st + A_BYTES + wn * WN * ROWB;
-  bf16x8_t tf0[TM], wf0[TN], tf1[TM], wf1[TN];
-  load_frags<TM, TN>(tb, wb, fo, 0, tf0, wf0);
+__device__ __forceinline__ void last_4x4(f32x16_t (&acc)[4][4], const bf16x8_t (&w)[4],
+                                         const bf16x8_t (&t)[4]) {
+  asm volatile(
+      "s_nop 1\n\t"
+      MOE_MFMA("%0", "%16", "%20") MOE_MFMA("%1", "%16", "%21") MOE_MFMA("%2", "%16", "%22")
+      MOE_MFMA("%3", "%16", "%23") MOE_MFMA("%4", "%17", "%20") MOE_MFMA("%5", "%17", "%21")
+      MOE_MFMA("%6", "%17", "%22") MOE_MFMA("%7", "%17", "%23") MOE_MFMA("%8", "%18", "%20")
+      MOE_MFMA("%9", "%18", "%21") MOE_MFMA("%10", "%18", "%22") MOE_MFMA("%11", "%18", "%23")
+      MOE_MFMA("%12", "%19", "%20") MOE_MFMA("%13", "%19", "%21") MOE_MFMA("%14", "%19", "%22")
+      MOE_MFMA("%15", "%19", "%23")
+      // results are read by VALU next (accumulator moves): 24 wait states
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+      : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]), "+a"(acc[1][0]),
+        "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]), "+a"(acc[2][0]), "+a"(acc[2][1]),
+        "+a"(acc[2][2]), "+a"(acc[2][3]), "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]),
+        "+a"(acc[3][3])
+      : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3])
+      : "memory");
+}
+
+__device__ __forceinline__ void step_4x2(f32x16_t (&acc)[2][4], const bf16x8_t (&w)[2],
+                                         const bf16x8_t (&t)[4], bf16x8_t (&nw)[2],
+                                         bf16x8_t (&nt)[4], uint32_t ta, uint32_t wa) {
+  asm volatile(
+      "s_nop 1\n\t"
+      MOE_MFMA("%0", "%14", "%16") MOE_RD("%8", "%20", "0")
+      MOE_MFMA("%1", "%14", "%17") MOE_RD("%9", "%20", "2048")
+      MOE_MFMA("%2", "%14", "%18") MOE_RD("%10", "%20", "4096")
+      MOE_MFMA("%3", "%14", "%19") MOE_RD("%11", "%20", "6144")
+      MOE_MFMA("%4", "%15", "%16") MOE_RD("%12", "%21", "0")
+      MOE_MFMA("%5", "%15", "%17") MOE_RD("%13", "%21", "2048")
+      MOE_MFMA("%6", "%15", "%18") MOE_MFMA("%7", "%15", "%19")
+      "s_waitcnt lgkmcnt(0)"
+      : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]), "+a"(acc[1][0]),
+        "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]), "=&v"(nt[0]), "=&v"(nt[1]), "=&v"(nt[2]),
+        "=&v"(nt[3]), "=&v"(nw[0]), "=&v"(nw[1])
+      : "v"(w[0]), "v"(w[1]), "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3]), "v"(ta), "v"(wa)
+      : "memory");
+}
+
+__device__ __forceinline__ void last_4x2(f32x16_t (&acc)[2][4], const bf16x8_t (&w)[2],
+                                         const bf16x8_t (&t)[4]) {
+  asm volatile(
+      "s_nop 1\n\t"
+      MOE_MFMA("%0", "%8", "%10") MOE_MFMA("%1", "%8", "%11") MOE_MFMA("%2", "%8", "%12")
+      MOE_MFMA("%3", "%8", "%13") MOE_MFMA("%4", "%9", "%10") MOE_MFMA("%5", "%9", "%11")
+      MOE_MFMA("%6", "%9", "%12") MOE_MFMA("%7", "%9", "%13")
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+      : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]), "+a"(acc[1][0]),
+        "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3])
+      : "v"(w[0]), "v"(w[1]), "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3])
+      : "memory");
+}
+
+// Fragments only (the first K16 step of a tile).
+template <int TM, int TN>
+__device__ __forceinline__ void read_frags(bf16x8_t (&nw)[TN], bf16x8_t (&nt)[TM], uint32_t ta,
+                                           uint32_t wa) {
+  static_assert(TM == 4 && (TN == 4 || TN == 2), "wave tile is 128 tokens x 128 or 64 features");
+  if constexpr (TN == 4) {
+    asm volatile(
+        MOE_RD("%0", "%8", "0") MOE_RD("%1", "%8", "2048") MOE_RD("%2", "%8", "4096")
+        MOE_RD("%3", "%8", "6144") MOE_RD("%4", "%9", "0") MOE_RD("%5", "%9", "2048")
+        MOE_RD("%6", "%9", "4096") MOE_RD("%7", "%9", "6144")
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(nt[0]), "=v"(nt[1]), "=v"(nt[2]), "=v"(nt[3]), "=v"(nw[0]), "=v"(nw[1]), "=v"(nw[2]),
+          "=v"(nw[3])
+        : "v"(ta), "v"(wa)
+        : "memory");
+  } else {
+    asm volatile(
+        MOE_RD("%0", "%6", "0") MOE_RD("%1", "%6", "2048") MOE_RD("%2", "%6", "4096")
+        MOE_RD("%3", "%6", "6144") MOE_RD("%4", "%7", "0") MOE_RD("%5", "%7", "2048")
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(nt[0]), "=v"(nt[1]), "=v"(nt[2]), "=v"(nt[3]), "=v"(nw[0]), "=v"(nw[1])
+        : "v"(ta), "v"(wa)
+        : "memory");
+  }
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void step(f32x16_t (&acc)[TN][TM], const bf16x8_t (&w)[TN],
+                                     const bf16x8_t (&t)[TM], bf16x8_t (&nw)[TN], bf16x8_t (&nt)[TM],
+                                     uint32_t ta, uint32_t wa) {
+  if constexpr (TN == 4) step_4x4(acc, w, t, nw, nt, ta, wa);
+  else step_4x2(acc, w, t, nw, nt, ta, wa);
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void last_step(f32x16_t (&acc)[TN][TM], const bf16x8_t (&w)[TN],
+                                          const bf16x8_t (&t)[TM]) {
+  if constexpr (TN == 4) last_4x4(acc, w, t);
+  else last_4x2(acc, w, t);
+}
+#undef MOE_MFMA
+#undef MOE_RD
+
+// tanh-GELU as u * sigmoid(2z), z = sqrt(2/pi) (u + 0.044715 u^3), with the
+// hardware base-2 exponential and reciprocal (about 1 ulp each; the result is
+// rounded to bf16 afterwards).
+__device__ __forceinline__ float gelu_fast(float u) {
+  constexpr float kNeg2zLog2e = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+  const float p = fmaf(0.044715f, u * u, 1.0f);
+  const float x = (kNeg2zLog2e * u) * p;
+  return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
+}
+
+template <int ACT>
+__device__ __forceinline__ float activate(float v) {
+  if constexpr (ACT == kActRelu) return v > 0.f ? v : 0.f;
+  else if constexpr (ACT == kActGeluTanh) return gelu_fast(v);
+  else return v;
+}
+
+struct TileInfo {
+  int e, row0, rv, n0;
+};
+
+__device__ __forceinline__ TileInfo decode_tile(int tile, const int* s_tiles, const int32_t* offsets,
+                                                int E, int NT, int BN) {
+  // expert: the largest e with s_tiles[e] * NT <= tile (experts with no
+  // rows share their successor's prefix and are skipped)
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_tiles[mid] * NT <= tile) lo = mid;
+    else hi = mid - 1;
+  }
+  TileInfo t;
+  t.e = lo;
+  const int mte = s_tiles[lo + 1] - s_tiles[lo];
+  const int u = tile - s_tiles[lo] * NT;
+  const int nt = u / mte;  // M tiles of an expert are innermost
+  const int mt = u - nt * mte;
+  t.row0 = offsets[lo] + mt * BM;
+  t.rv = min(BM, offsets[lo + 1] - t.row0);
+  t.n0 = nt * BN;
+  return t;
+}
+
+// Wait until at most n later stages (G loads each) of this wave are in flight.
+template <int G>
+__device__ __forceinline__ void wait_loads(int n) {
+  if (n >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * G) : "memory");
+  else if (n == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Per-tile DMA sources: byte offsets (from the tile's token and weight bases)
+// of the chunk each lane loads for every 1 KiB block it fills. Token rows past
+// the expert's end read its last row; feature rows past N read row N-1.
+template <int LA, int LB>
+__device__ __forceinline__ void tile_sources(const TileInfo& t, const uint16_t* A, const uint16_t* W,
+                                             int N, int K, int wave, int drow, int dpos,
+                                             const char*& Abase, const char*& Wbase,
+                                             uint32_t (&aoffs)[LA], uint32_t (&boffs)[LB]) {
+  Abase = reinterpret_cast<const char*>(A + static_cast<int64_t>(t.row0) * K);
+  Wbase = reinterpret_cast<const char*>(W + (static_cast<int64_t>(t.e) * N + t.n0) * K);
 #pragma unroll
-  for (int s = 0; s < BK / 16; s += 2) {
-    load_frags<TM, TN>(tb, wb, fo, s + 1, tf1, wf1);
+  for (int i = 0; i < LA; ++i) {
+    const int r = (wave * LA + i) * 16 + drow;
+    aoffs[i] = static_cast<uint32_t>((min(r, t.rv - 1) * K + (dpos ^ swz_key(r)) * 8) * 2);
+  }
 #pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-      for (int j = 0; j < TM; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf0[i], tf0[j], acc[i][j], 0, 0, 0);
-    if (s + 2 < BK / 16) load_frags<TM, TN>(tb, wb, fo, s + 2, tf0, wf0);
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-      for (int j = 0; j < TM; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf1[i], tf1[j], acc[i][j], 0, 0, 0);
+  for (int i = 0; i < LB; ++i) {
+    const int r = (wave * LB + i) * 16 + drow;
+    boffs[i] = static_cast<uint32_t>(((min(t.n0 + r, N - 1) - t.n0) * K + (dpos ^ swz_key(r)) * 8) * 2);
   }
 }
 
 }  // namespace
 
-template <int BN, bool OUT_F32>
+template <int BN, bool OUT_F32, int ACT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                               const float* __restrict__ bias, void* __restrict__ out,
-                              const int32_t* __restrict__ offsets, int E, int N, int K,
-                              int act) {
-  constexpr int WM = BM / 2;   // tokens per wave
-  constexpr int WN = BN / 2;   // features per wave
-  constexpr int TM = WM / 32;  // 32-token MFMA tiles per wave
-  constexpr int TN = WN / 32;  // 32-feature MFMA tiles per wave
+                              const int32_t* __restrict__ offsets, int E, int N, int K) {
+  // the body uses gfx950 builtins only: the host pass needs just the signature
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int WM = BM / 2;         // tokens per wave
+  constexpr int WN = BN / 2;         // features per wave
+  constexpr int TM = WM / 32;        // 32-token MFMA tiles per wave
+  constexpr int TN = WN / 32;        // 32-feature MFMA tiles per wave
   constexpr int A_BYTES = BM * ROWB;
   constexpr int STAGE = (BM + BN) * ROWB;
-  constexpr int LA = BM / 32;  // 1 KiB LDS-DMA blocks of the token tile per wave
-  constexpr int LB = BN / 32;  // 1 KiB LDS-DMA blocks of the weight tile per wave
+  constexpr int LA = BM / 64;        // 1 KiB DMA blocks of the token tile per wave
+  constexpr int LB = BN / 64;        // 1 KiB DMA blocks of the weight tile per wave
+  constexpr int G = LA + LB;         // DMA loads per wave per stage
 
-  // two stages as distinct objects, so that the compiler can tell the stage
-  // being read from the stage the LDS-DMA loads are filling
-  __shared__ __attribute__((aligned(1024))) char lds0[STAGE];
-  __shared__ __attribute__((aligned(1024))) char lds1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[NST * STAGE];
   __shared__ int s_tiles[1025];  // exclusive prefix of M tiles per expert
   __shared__ int s_part[256];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1;
   const int wn = wave & 1;
 
@@ -140,10 +320,7 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __
     const int per = (E + 255) / 256;
     const int eb = tid * per;
     int local = 0;
-    for (int e = eb; e < min(E, eb + per); ++e) {
-      const int ne = offsets[e + 1] - offsets[e];
-      local += (ne + BM - 1) / BM;
-    }
+    for (int e = eb; e < min(E, eb + per); ++e) local += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
     s_part[tid] = local;
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {
@@ -155,67 +332,41 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __
     int run = s_part[tid] - local;
     for (int e = eb; e < min(E, eb + per); ++e) {
       s_tiles[e] = run;
-      const int ne = offsets[e + 1] - offsets[e];
-      run += (ne + BM - 1) / BM;
+      run += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
     }
     if (tid == 255) s_tiles[E] = s_part[255];
     __syncthreads();
   }
   const int NT = (N + BN - 1) / BN;
   const int total = s_tiles[E] * NT;
-
-  const int G = gridDim.x;
+  const int Gd = gridDim.x;
   const int b = blockIdx.x;
-  const int lb = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+  // blocks are dealt to the 8 XCDs round-robin: renumber so that consecutive
+  // tiles (which share weight and token panels) run on one XCD
+  int tile = (Gd % 8 == 0) ? (b % 8) * (Gd / 8) + b / 8 : b;
+  if (tile >= total) return;
 
-  // Fragment reads. Lane (l5 = lane%32, hi = lane/32) of a 32x32x16 MFMA reads
-  // row l5 of a 32-row tile at chunk 2s+hi (K16 step s). With f = (row +
-  // row/8) & 7, rows 32j+l5 have f = f0 for even j and f0^4 for odd j, and
-  // (2s+hi) ^ (f0^4) = (2(s^2)+hi) ^ f0: four per-lane offsets cover all reads.
+  // per-lane constants: fragment offsets (K16 step s of a stage) and the DMA
+  // source mapping (lane L lands at row L/4, position L%4 of its 1 KiB block,
+  // so it loads the chunk the swizzle places there)
   const int l5 = lane & 31, hi = lane >> 5;
-  const int f0 = (l5 + (l5 >> 3)) & 7;
-  int fo[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) fo[s] = l5 * ROWB + 16 * (((2 * s) ^ (f0 & 6)) | (hi ^ (f0 & 1)));
+  const uint32_t fo0 = l5 * ROWB + 16 * ((0 + hi) ^ swz_key(l5));
+  const uint32_t fo1 = l5 * ROWB + 16 * ((2 + hi) ^ swz_key(l5));
+  const int drow = lane >> 2, dpos = lane & 3;
+  const int nk = K / BK;
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  const uint32_t trow = wm * WM * ROWB;            // this wave's token rows in a stage
+  const uint32_t wrow = A_BYTES + wn * WN * ROWB;  // this wave's weight rows in a stage
 
-  // LDS-DMA: one global_load_lds_dwordx4 fills 1 KiB = 8 rows of 128 B; lane L
-  // lands at row L/8, position L%8, so it loads the chunk the swizzle puts
-  // there: chunk = position ^ f(row).
-  const int drow = lane >> 3, dpos = lane & 7;
+  uint32_t aoffs[LA], boffs[LB];
+  const char* Abase;
+  const char* Wbase;
+  TileInfo cur = decode_tile(tile, s_tiles, offsets, E, NT, BN);
+  tile_sources<LA, LB>(cur, A, W, N, K, wave, drow, dpos, Abase, Wbase, aoffs, boffs);
+  for (int p = 0; p < NST && p < nk; ++p)
+    issue_stage<LA, LB, A_BYTES>(Abase + p * ROWB, Wbase + p * ROWB, lds + p * STAGE, aoffs, boffs, wave);
 
-  for (int tile = lb; tile < total; tile += G) {
-    // expert of this tile: the largest e with s_tiles[e]*NT <= tile
-    int lo = 0, hi_e = E - 1;
-    while (lo < hi_e) {
-      const int mid = (lo + hi_e + 1) >> 1;
-      if (s_tiles[mid] * NT <= tile) lo = mid;
-      else hi_e = mid - 1;
-    }
-    const int e = lo;
-    const int mte = s_tiles[e + 1] - s_tiles[e];
-    const int u = tile - s_tiles[e] * NT;
-    const int nt = u / mte;
-    const int mt = u - nt * mte;
-    const int row0 = offsets[e] + mt * BM;
-    const int rv = min(BM, offsets[e + 1] - row0);  // valid rows in this tile
-    const int n0 = nt * BN;
-
-    const uint16_t* Abase = A + static_cast<int64_t>(row0) * K;
-    const uint16_t* Wbase = W + (static_cast<int64_t>(e) * N + n0) * K;
-    int aoffs[LA], boffs[LB];
-#pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int r = (wave * LA + i) * 8 + drow;
-      const int c = dpos ^ ((r + (r >> 3)) & 7);
-      aoffs[i] = min(r, rv - 1) * K + c * 8;
-    }
-#pragma unroll
-    for (int i = 0; i < LB; ++i) {
-      const int r = (wave * LB + i) * 8 + drow;
-      const int c = dpos ^ ((r + (r >> 3)) & 7);
-      boffs[i] = (min(n0 + r, N - 1) - n0) * K + c * 8;
-    }
-
+  for (;;) {
     f32x16_t acc[TN][TM];
 #pragma unroll
     for (int i = 0; i < TN; ++i)
@@ -224,66 +375,96 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-    const int nk = K / BK;
-    issue_tile<LA, LB, A_BYTES>(Abase, Wbase, lds0, aoffs, boffs, wave);
+    // the tile's first stage (and, after an epilogue, its stores)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    // tile kt sits in lds0 at the top of each pair
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-      issue_tile<LA, LB, A_BYTES>(Abase + (kt + 1) * BK, Wbase + (kt + 1) * BK, lds1, aoffs, boffs, wave);
-      compute_tile<TM, TN, A_BYTES, WM, WN>(lds0, fo, wm, wn, acc);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (kt + 2 < nk)
-        issue_tile<LA, LB, A_BYTES>(Abase + (kt + 2) * BK, Wbase + (kt + 2) * BK, lds0, aoffs, boffs, wave);
-      compute_tile<TM, TN, A_BYTES, WM, WN>(lds1, fo, wm, wn, acc);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-    }
-    if (kt < nk) {
-      compute_tile<TM, TN, A_BYTES, WM, WN>(lds0, fo, wm, wn, acc);
-      __syncthreads();
-    }
+    bf16x8_t w0[TN], t0[TM], w1[TN], t1[TM];
+    read_frags<TM, TN>(w0, t0, lds_base + trow + fo0, lds_base + wrow + fo0);
 
-    // ---- epilogue: lane holds token (lane%32) of each 32-token tile j and
-    // features 8q + 4*(lane/32) + {0..3} of each 32-feature tile i.
-    const float* be = bias != nullptr ? bias + static_cast<int64_t>(e) * N : nullptr;
+    TileInfo done = cur;
+    const int next = tile + Gd;
+    uint32_t sb = lds_base;  // stage of tile t
+    int t = 0;
+    // steady state: tile t+4 still to load
+    for (; t + NST < nk; ++t) {
+      const uint32_t sn = lds_base + ((t + 1) & (NST - 1)) * STAGE;
+      // K16 step 0 of stage t; read step 1 of stage t
+      step<TM, TN>(acc, w0, t0, w1, t1, sb + trow + fo1, sb + wrow + fo1);
+      // stage t+1 ready (tiles t+2, t+3 may still load); every wave is done
+      // with stage t, which then takes tile t+4
+      wait_loads<G>(2);
+      __syncthreads();
+      issue_stage<LA, LB, A_BYTES>(Abase + (t + NST) * ROWB, Wbase + (t + NST) * ROWB,
+                                   lds + (t & (NST - 1)) * STAGE, aoffs, boffs, wave);
+      // K16 step 1 of stage t; read step 0 of stage t+1
+      step<TM, TN>(acc, w1, t1, w0, t0, sn + trow + fo0, sn + wrow + fo0);
+      sb = sn;
+    }
+    // the last stages: nothing more to load
+    for (; t + 1 < nk; ++t) {
+      const uint32_t sn = lds_base + ((t + 1) & (NST - 1)) * STAGE;
+      step<TM, TN>(acc, w0, t0, w1, t1, sb + trow + fo1, sb + wrow + fo1);
+      wait_loads<G>(nk - 2 - t);
+      __syncthreads();
+      step<TM, TN>(acc, w1, t1, w0, t0, sn + trow + fo0, sn + wrow + fo0);
+      sb = sn;
+    }
+    // the last stage
+    step<TM, TN>(acc, w0, t0, w1, t1, sb + trow + fo1, sb + wrow + fo1);
+    __syncthreads();
+    if (next < total) {
+      // all stages are free: the next tile's first stages load during this
+      // tile's last MFMAs and epilogue
+      cur = decode_tile(next, s_tiles, offsets, E, NT, BN);
+      tile_sources<LA, LB>(cur, A, W, N, K, wave, drow, dpos, Abase, Wbase, aoffs, boffs);
+      for (int p = 0; p < NST && p < nk; ++p)
+        issue_stage<LA, LB, A_BYTES>(Abase + p * ROWB, Wbase + p * ROWB, lds + p * STAGE, aoffs, boffs,
+                                     wave);
+    }
+    last_step<TM, TN>(acc, w1, t1);
+
+    // ---- epilogue: lane holds token l5 of each 32-token tile j and
+    // features 8q + 4*hi + {0..3} of each 32-feature tile i
+    float4 bq[TN][4];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = done.n0 + wn * WN + i * 32 + q * 8 + hi * 4;
+        bq[i][q] = (bias != nullptr && n < N)
+                       ? *reinterpret_cast<const float4*>(bias + static_cast<int64_t>(done.e) * N + n)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
-      const int m = wm * WM + j * 32 + (lane & 31);
-      if (m >= rv) continue;
-      const int64_t orow = static_cast<int64_t>(row0 + m) * N;
+      const int m = wm * WM + j * 32 + l5;
+      if (m >= done.rv) continue;
+      const int64_t orow = static_cast<int64_t>(done.row0 + m) * N;
 #pragma unroll
       for (int i = 0; i < TN; ++i) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn * WN + i * 32 + q * 8 + (lane >> 5) * 4;
+          const int n = done.n0 + wn * WN + i * 32 + q * 8 + hi * 4;
           if (n >= N) continue;
-          float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
-          float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-          if (be != nullptr) {
-            const float4 bb = *reinterpret_cast<const float4*>(be + n);
-            v0 += bb.x; v1 += bb.y; v2 += bb.z; v3 += bb.w;
-          }
-          if (act == kActRelu) {
-            v0 = act_relu(v0); v1 = act_relu(v1); v2 = act_relu(v2); v3 = act_relu(v3);
-          } else if (act == kActGeluTanh) {
-            v0 = act_gelu_tanh(v0); v1 = act_gelu_tanh(v1);
-            v2 = act_gelu_tanh(v2); v3 = act_gelu_tanh(v3);
-          }
+          const float v0 = activate<ACT>(acc[i][j][4 * q + 0] + bq[i][q].x);
+          const float v1 = activate<ACT>(acc[i][j][4 * q + 1] + bq[i][q].y);
+          const float v2 = activate<ACT>(acc[i][j][4 * q + 2] + bq[i][q].z);
+          const float v3 = activate<ACT>(acc[i][j][4 * q + 3] + bq[i][q].w);
           if constexpr (OUT_F32) {
             *reinterpret_cast<float4*>(static_cast<float*>(out) + orow + n) = make_float4(v0, v1, v2, v3);
           } else {
-            uint2 o;
-            o.x = f32_to_bf16(v0) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16);
-            o.y = f32_to_bf16(v2) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + orow + n) = o;
+            typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+            const bf16x4_t o = {static_cast<__bf16>(v0), static_cast<__bf16>(v1),
+                                static_cast<__bf16>(v2), static_cast<__bf16>(v3)};
+            *reinterpret_cast<bf16x4_t*>(static_cast<uint16_t*>(out) + orow + n) = o;
           }
         }
       }
     }
+    if (next >= total) break;
+    tile = next;
   }
+#endif
 }
 
 namespace {
@@ -311,16 +492,21 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, const float* b
   // upper bound on tiles: sum_e ceil(n_e/BM) <= max_rows/BM + E
   const int64_t mt_bound = max_rows / BM + E;
   const int cus = cu_count();
+  auto grid_for = [&](int bn) {
+    const int64_t tiles = mt_bound * ((N + bn - 1) / bn);
+    return static_cast<unsigned>(tiles < cus ? tiles : cus);
+  };
   if (out_f32) {
     constexpr int BN = 128;
-    const int64_t tiles = mt_bound * ((N + BN - 1) / BN);
-    const unsigned grid = static_cast<unsigned>(tiles < cus ? tiles : cus);
-    grouped_gemm_bf16_kernel<BN, true><<<grid, 256, 0, s>>>(A, W, bias, out, offsets, E, N, K, act);
+    grouped_gemm_bf16_kernel<BN, true, kActNone><<<grid_for(BN), 256, 0, s>>>(A, W, bias, out, offsets, E, N, K);
   } else {
     constexpr int BN = 256;
-    const int64_t tiles = mt_bound * ((N + BN - 1) / BN);
-    const unsigned grid = static_cast<unsigned>(tiles < cus ? tiles : cus);
-    grouped_gemm_bf16_kernel<BN, false><<<grid, 256, 0, s>>>(A, W, bias, out, offsets, E, N, K, act);
+    if (act == kActRelu)
+      grouped_gemm_bf16_kernel<BN, false, kActRelu><<<grid_for(BN), 256, 0, s>>>(A, W, bias, out, offsets, E, N, K);
+    else if (act == kActGeluTanh)
+      grouped_gemm_bf16_kernel<BN, false, kActGeluTanh><<<grid_for(BN), 256, 0, s>>>(A, W, bias, out, offsets, E, N, K);
+    else
+      grouped_gemm_bf16_kernel<BN, false, kActNone><<<grid_for(BN), 256, 0, s>>>(A, W, bias, out, offsets, E, N, K);
   }
   return hipGetLastError();
 }
