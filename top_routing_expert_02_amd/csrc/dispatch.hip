@@ -97,15 +97,12 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   if (tid == 0) offsets[0] = 0;
 }
 
-// One block per 64-token tile.
-template <int VEC>
+// One block per 64-token tile: slots, capacity test, rows.
 __global__ __launch_bounds__(256) void permute_kernel(
-    const char* __restrict__ x, const int32_t* __restrict__ ids, const int32_t* __restrict__ base,
-    const int32_t* __restrict__ offsets, int64_t T, int k, int E, int C, int row_bytes,
-    int32_t* __restrict__ slot, int32_t* __restrict__ row_of, int32_t* __restrict__ row_token,
-    char* __restrict__ x_perm) {
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ offsets, int64_t T, int k, int E, int C,
+    int32_t* __restrict__ slot, int32_t* __restrict__ row_of, int32_t* __restrict__ row_token) {
   __shared__ unsigned long long mask[1024];
-  __shared__ int rows[kTileTokens * 16];
   const int64_t tile = blockIdx.x;
   const int64_t t0 = tile * kTileTokens;
   const int nt = static_cast<int>(min<int64_t>(kTileTokens, T - t0));
@@ -124,40 +121,27 @@ __global__ __launch_bounds__(256) void permute_kernel(
     slot[t0 * k + p] = s;
     row_of[t0 * k + p] = row;
     if (row >= 0) row_token[row] = static_cast<int32_t>(t0 + t);
-    rows[p] = row;
   }
-  __syncthreads();
-  // copy: a wave per token; the row is read once and written to each kept slot
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  for (int t = wave; t < nt; t += 4) {
-    const char* src = x + (t0 + t) * static_cast<int64_t>(row_bytes);
-    for (int c = lane * VEC; c < row_bytes; c += 64 * VEC * 4) {
-      // up to four chunks in flight per lane
-      uint4 v4[4];
-      uint32_t v1[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int cc = c + u * 64 * VEC;
-        if (cc < row_bytes) {
-          if constexpr (VEC == 16) v4[u] = *reinterpret_cast<const uint4*>(src + cc);
-          else v1[u] = *reinterpret_cast<const uint32_t*>(src + cc);
-        }
-      }
-      for (int j = 0; j < k; ++j) {
-        const int row = rows[t * k + j];
-        if (row < 0) continue;
-        char* dst = x_perm + static_cast<int64_t>(row) * row_bytes;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int cc = c + u * 64 * VEC;
-          if (cc < row_bytes) {
-            if constexpr (VEC == 16) *reinterpret_cast<uint4*>(dst + cc) = v4[u];
-            else *reinterpret_cast<uint32_t*>(dst + cc) = v1[u];
-          }
-        }
-      }
-    }
+}
+
+// x_perm[r] = x[row_token[r]] for every kept row, VEC bytes per thread, rows
+// read from offsets[E] on the device.
+template <int VEC>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict__ x,
+                                                          const int32_t* __restrict__ row_token,
+                                                          const int32_t* __restrict__ offsets, int E,
+                                                          int row_bytes, char* __restrict__ x_perm) {
+  const int64_t rows = offsets[E];
+  const int chunks = row_bytes / VEC;
+  const int64_t n = rows * chunks;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t r = i / chunks;
+    const int c = static_cast<int>(i - r * chunks) * VEC;
+    const char* src = x + static_cast<int64_t>(row_token[r]) * row_bytes + c;
+    char* dst = x_perm + r * row_bytes + c;
+    if constexpr (VEC == 16) *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+    else *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
   }
 }
 
@@ -178,14 +162,24 @@ hipError_t launch_permute(const void* x, const int32_t* ids, const int32_t* base
                           int row_bytes, int32_t* slot, int32_t* row_of, int32_t* row_token,
                           void* x_perm, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>((T + kTileTokens - 1) / kTileTokens);
-  if (row_bytes % 16 == 0)
-    permute_kernel<16><<<grid, 256, 0, s>>>(static_cast<const char*>(x), ids, base, offsets, T, k, E, C,
-                                            row_bytes, slot, row_of, row_token,
-                                            static_cast<char*>(x_perm));
+  permute_kernel<<<grid, 256, 0, s>>>(ids, base, offsets, T, k, E, C, slot, row_of, row_token);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || x_perm == nullptr) return err;
+  return launch_gather_rows(x, row_token, offsets, E, T * k, row_bytes, x_perm, s);
+}
+
+hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int32_t* offsets,
+                              int E, int64_t max_rows, int row_bytes, void* x_perm, hipStream_t s) {
+  if (max_rows <= 0) return hipSuccess;
+  const int vec = (row_bytes % 16 == 0) ? 16 : 4;
+  const int64_t n = max_rows * (row_bytes / vec);
+  const unsigned grid = static_cast<unsigned>(n / 256 + 1 < 8192 ? n / 256 + 1 : 8192);
+  if (vec == 16)
+    gather_rows_kernel<16><<<grid, 256, 0, s>>>(static_cast<const char*>(x), row_token, offsets, E,
+                                                row_bytes, static_cast<char*>(x_perm));
   else
-    permute_kernel<4><<<grid, 256, 0, s>>>(static_cast<const char*>(x), ids, base, offsets, T, k, E, C,
-                                           row_bytes, slot, row_of, row_token,
-                                           static_cast<char*>(x_perm));
+    gather_rows_kernel<4><<<grid, 256, 0, s>>>(static_cast<const char*>(x), row_token, offsets, E,
+                                               row_bytes, static_cast<char*>(x_perm));
   return hipGetLastError();
 }
 

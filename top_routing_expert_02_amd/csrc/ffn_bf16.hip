@@ -42,8 +42,8 @@ namespace {
 
 constexpr int BM = kGemmBM;   // 256 token rows per tile
 constexpr int BK = 32;        // K per LDS stage
-constexpr int ROWB = BK * 2;  // bytes per LDS row (64)
-constexpr int NST = 4;        // LDS stages: up to four K tiles in flight
+[[maybe_unused]] constexpr int ROWB = BK * 2;  // bytes per LDS row (64)
+[[maybe_unused]] constexpr int NST = 4;  // LDS stages: up to four K tiles in flight
 
 // Row r of a stage holds its 16-byte chunk c at position c ^ swz_key(r): the
 // key is the row's 256-byte block (mod 4). With it the MFMA fragment reads
@@ -217,9 +217,10 @@ __device__ __forceinline__ void last_step(f32x16_t (&acc)[TN][TM], const bf16x8_
 // hardware base-2 exponential and reciprocal (about 1 ulp each; the result is
 // rounded to bf16 afterwards).
 __device__ __forceinline__ float gelu_fast(float u) {
-  constexpr float kNeg2zLog2e = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
-  const float p = fmaf(0.044715f, u * u, 1.0f);
-  const float x = (kNeg2zLog2e * u) * p;
+  // exp(-2z) = 2^x with x = u * (c0 + c1 u^2)
+  constexpr float c0 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+  constexpr float c1 = c0 * 0.044715f;
+  const float x = u * fmaf(c1, u * u, c0);
   return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
 }
 
@@ -267,17 +268,30 @@ __device__ __forceinline__ void wait_loads(int n) {
 // Per-tile DMA sources: byte offsets (from the tile's token and weight bases)
 // of the chunk each lane loads for every 1 KiB block it fills. Token rows past
 // the expert's end read its last row; feature rows past N read row N-1.
+// With row_idx, tile row r is row row_idx[row0 + r] of A (the token rows are
+// gathered straight from x, so the permuted copy is never written).
 template <int LA, int LB>
-__device__ __forceinline__ void tile_sources(const TileInfo& t, const uint16_t* A, const uint16_t* W,
+__device__ __forceinline__ void tile_sources(const TileInfo& t, const uint16_t* A,
+                                             const int32_t* __restrict__ row_idx, const uint16_t* W,
                                              int N, int K, int wave, int drow, int dpos,
                                              const char*& Abase, const char*& Wbase,
                                              uint32_t (&aoffs)[LA], uint32_t (&boffs)[LB]) {
-  Abase = reinterpret_cast<const char*>(A + static_cast<int64_t>(t.row0) * K);
   Wbase = reinterpret_cast<const char*>(W + (static_cast<int64_t>(t.e) * N + t.n0) * K);
+  if (row_idx != nullptr) {
+    Abase = reinterpret_cast<const char*>(A);
 #pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    const int r = (wave * LA + i) * 16 + drow;
-    aoffs[i] = static_cast<uint32_t>((min(r, t.rv - 1) * K + (dpos ^ swz_key(r)) * 8) * 2);
+    for (int i = 0; i < LA; ++i) {
+      const int r = (wave * LA + i) * 16 + drow;
+      const uint32_t src = static_cast<uint32_t>(row_idx[t.row0 + min(r, t.rv - 1)]);
+      aoffs[i] = (src * static_cast<uint32_t>(K) + (dpos ^ swz_key(r)) * 8) * 2;
+    }
+  } else {
+    Abase = reinterpret_cast<const char*>(A + static_cast<int64_t>(t.row0) * K);
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      const int r = (wave * LA + i) * 16 + drow;
+      aoffs[i] = static_cast<uint32_t>((min(r, t.rv - 1) * K + (dpos ^ swz_key(r)) * 8) * 2);
+    }
   }
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
@@ -286,11 +300,58 @@ __device__ __forceinline__ void tile_sources(const TileInfo& t, const uint16_t* 
   }
 }
 
+
+// Bias, activation, conversion and stores of one wave's 128 x WN outputs.
+// FULL: every row and feature of the tile is in range (no per-lane checks).
+template <int TM, int TN, int WM, int WN, bool OUT_F32, int ACT, bool FULL>
+__device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], const float* __restrict__ bias,
+                                         void* __restrict__ out, const TileInfo& t, int N, int wm,
+                                         int wn, int l5, int hi) {
+  const int nb = t.n0 + wn * WN + hi * 4;  // this lane's first feature
+  float4 bq[TN][4];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = nb + i * 32 + q * 8;
+      bq[i][q] = (bias != nullptr && (FULL || n < N))
+                     ? *reinterpret_cast<const float4*>(bias + static_cast<int64_t>(t.e) * N + n)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int m = wm * WM + j * 32 + l5;
+    if (!FULL && m >= t.rv) continue;
+    const int64_t orow = static_cast<int64_t>(t.row0 + m) * N + nb;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (!FULL && nb + i * 32 + q * 8 >= N) continue;
+        const float v0 = activate<ACT>(acc[i][j][4 * q + 0] + bq[i][q].x);
+        const float v1 = activate<ACT>(acc[i][j][4 * q + 1] + bq[i][q].y);
+        const float v2 = activate<ACT>(acc[i][j][4 * q + 2] + bq[i][q].z);
+        const float v3 = activate<ACT>(acc[i][j][4 * q + 3] + bq[i][q].w);
+        const int64_t o = orow + i * 32 + q * 8;
+        if constexpr (OUT_F32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(out) + o) = make_float4(v0, v1, v2, v3);
+        } else {
+          typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+          const bf16x4_t h = {static_cast<__bf16>(v0), static_cast<__bf16>(v1), static_cast<__bf16>(v2),
+                              static_cast<__bf16>(v3)};
+          *reinterpret_cast<bf16x4_t*>(static_cast<uint16_t*>(out) + o) = h;
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 template <int BN, bool OUT_F32, int ACT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ row_idx,
+                              const uint16_t* __restrict__ W,
                               const float* __restrict__ bias, void* __restrict__ out,
                               const int32_t* __restrict__ offsets, int E, int N, int K) {
   // the body uses gfx950 builtins only: the host pass needs just the signature
@@ -362,7 +423,7 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __
   const char* Abase;
   const char* Wbase;
   TileInfo cur = decode_tile(tile, s_tiles, offsets, E, NT, BN);
-  tile_sources<LA, LB>(cur, A, W, N, K, wave, drow, dpos, Abase, Wbase, aoffs, boffs);
+  tile_sources<LA, LB>(cur, A, row_idx, W, N, K, wave, drow, dpos, Abase, Wbase, aoffs, boffs);
   for (int p = 0; p < NST && p < nk; ++p)
     issue_stage<LA, LB, A_BYTES>(Abase + p * ROWB, Wbase + p * ROWB, lds + p * STAGE, aoffs, boffs, wave);
 
@@ -416,7 +477,7 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __
       // all stages are free: the next tile's first stages load during this
       // tile's last MFMAs and epilogue
       cur = decode_tile(next, s_tiles, offsets, E, NT, BN);
-      tile_sources<LA, LB>(cur, A, W, N, K, wave, drow, dpos, Abase, Wbase, aoffs, boffs);
+      tile_sources<LA, LB>(cur, A, row_idx, W, N, K, wave, drow, dpos, Abase, Wbase, aoffs, boffs);
       for (int p = 0; p < NST && p < nk; ++p)
         issue_stage<LA, LB, A_BYTES>(Abase + p * ROWB, Wbase + p * ROWB, lds + p * STAGE, aoffs, boffs,
                                      wave);
@@ -425,42 +486,9 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __
 
     // ---- epilogue: lane holds token l5 of each 32-token tile j and
     // features 8q + 4*hi + {0..3} of each 32-feature tile i
-    float4 bq[TN][4];
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = done.n0 + wn * WN + i * 32 + q * 8 + hi * 4;
-        bq[i][q] = (bias != nullptr && n < N)
-                       ? *reinterpret_cast<const float4*>(bias + static_cast<int64_t>(done.e) * N + n)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      const int m = wm * WM + j * 32 + l5;
-      if (m >= done.rv) continue;
-      const int64_t orow = static_cast<int64_t>(done.row0 + m) * N;
-#pragma unroll
-      for (int i = 0; i < TN; ++i) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = done.n0 + wn * WN + i * 32 + q * 8 + hi * 4;
-          if (n >= N) continue;
-          const float v0 = activate<ACT>(acc[i][j][4 * q + 0] + bq[i][q].x);
-          const float v1 = activate<ACT>(acc[i][j][4 * q + 1] + bq[i][q].y);
-          const float v2 = activate<ACT>(acc[i][j][4 * q + 2] + bq[i][q].z);
-          const float v3 = activate<ACT>(acc[i][j][4 * q + 3] + bq[i][q].w);
-          if constexpr (OUT_F32) {
-            *reinterpret_cast<float4*>(static_cast<float*>(out) + orow + n) = make_float4(v0, v1, v2, v3);
-          } else {
-            typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-            const bf16x4_t o = {static_cast<__bf16>(v0), static_cast<__bf16>(v1),
-                                static_cast<__bf16>(v2), static_cast<__bf16>(v3)};
-            *reinterpret_cast<bf16x4_t*>(static_cast<uint16_t*>(out) + orow + n) = o;
-          }
-        }
-      }
-    }
+    const bool full_tile = done.rv == BM && done.n0 + BN <= N;
+    if (full_tile) epilogue<TM, TN, WM, WN, OUT_F32, ACT, true>(acc, bias, out, done, N, wm, wn, l5, hi);
+    else epilogue<TM, TN, WM, WN, OUT_F32, ACT, false>(acc, bias, out, done, N, wm, wn, l5, hi);
     if (next >= total) break;
     tile = next;
   }
@@ -484,7 +512,8 @@ int cu_count() {
 
 }  // namespace
 
-hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, void* out,
+hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uint16_t* W,
+                            const float* bias, void* out,
                             bool out_f32, int act, const int32_t* offsets, int E, int N, int K,
                             int64_t max_rows, int max_rows_per_expert, hipStream_t s) {
   (void)max_rows_per_expert;
@@ -498,15 +527,15 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, const float* b
   };
   if (out_f32) {
     constexpr int BN = 128;
-    grouped_gemm_bf16_kernel<BN, true, kActNone><<<grid_for(BN), 256, 0, s>>>(A, W, bias, out, offsets, E, N, K);
+    grouped_gemm_bf16_kernel<BN, true, kActNone><<<grid_for(BN), 256, 0, s>>>(A, row_idx, W, bias, out, offsets, E, N, K);
   } else {
-    constexpr int BN = 256;
+    constexpr int BN = 128;
     if (act == kActRelu)
-      grouped_gemm_bf16_kernel<BN, false, kActRelu><<<grid_for(BN), 256, 0, s>>>(A, W, bias, out, offsets, E, N, K);
+      grouped_gemm_bf16_kernel<BN, false, kActRelu><<<grid_for(BN), 256, 0, s>>>(A, row_idx, W, bias, out, offsets, E, N, K);
     else if (act == kActGeluTanh)
-      grouped_gemm_bf16_kernel<BN, false, kActGeluTanh><<<grid_for(BN), 256, 0, s>>>(A, W, bias, out, offsets, E, N, K);
+      grouped_gemm_bf16_kernel<BN, false, kActGeluTanh><<<grid_for(BN), 256, 0, s>>>(A, row_idx, W, bias, out, offsets, E, N, K);
     else
-      grouped_gemm_bf16_kernel<BN, false, kActNone><<<grid_for(BN), 256, 0, s>>>(A, W, bias, out, offsets, E, N, K);
+      grouped_gemm_bf16_kernel<BN, false, kActNone><<<grid_for(BN), 256, 0, s>>>(A, row_idx, W, bias, out, offsets, E, N, K);
   }
   return hipGetLastError();
 }

@@ -1,7 +1,8 @@
 // Grouped expert FFN GEMMs for fp32 layers (FFN(x) = W2 sigma(W1 x + b1) + b2,
 // page "MoE 模型原理：路由、专家负载、容量、通信与推理成本", wrblog.cn, §1).
 //
-// The fp32 path exists for small layers that need fp32 results; it uses
+// The fp32 path exists for small layers that need fp32 results (token rows
+// may be gathered through a row index, like the bf16 path); it uses
 // vector FMA with 64x64 LDS tiles (each thread 4x4 outputs, strided by 16 so
 // that LDS reads are conflict-free). The grid is (N tiles, M tiles of the
 // largest possible expert, experts); tiles past an expert's rows exit.
@@ -10,6 +11,7 @@
 namespace moe {
 
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A,
+                                                       const int32_t* __restrict__ row_idx,
                                                        const float* __restrict__ W,
                                                        const float* __restrict__ bias,
                                                        float* __restrict__ out,
@@ -39,7 +41,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
       const int m = idx >> 4;
       const int kk = idx & 15;
       const bool kv = k0 + kk < K;
-      As[kk][m] = (m0 + m < ne && kv) ? A[static_cast<int64_t>(r0 + m0 + m) * K + k0 + kk] : 0.f;
+      float a = 0.f;
+      if (m0 + m < ne && kv) {
+        const int64_t row = row_idx != nullptr ? row_idx[r0 + m0 + m] : r0 + m0 + m;
+        a = A[row * K + k0 + kk];
+      }
+      As[kk][m] = a;
       Bs[kk][m] = (n0 + m < N && kv) ? We[static_cast<int64_t>(n0 + m) * K + k0 + kk] : 0.f;
     }
     __syncthreads();
@@ -73,12 +80,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   }
 }
 
-hipError_t launch_gemm_f32(const float* A, const float* W, const float* bias, float* out,
+hipError_t launch_gemm_f32(const float* A, const int32_t* row_idx, const float* W, const float* bias,
+                           float* out,
                            int act, const int32_t* offsets, int E, int N, int K,
                            int max_rows_per_expert, hipStream_t s) {
   if (max_rows_per_expert <= 0) return hipSuccess;
   dim3 grid((N + 63) / 64, (max_rows_per_expert + 63) / 64, E);
-  gemm_f32_kernel<<<grid, 256, 0, s>>>(A, W, bias, out, offsets, N, K, act);
+  gemm_f32_kernel<<<grid, 256, 0, s>>>(A, row_idx, W, bias, out, offsets, N, K, act);
   return hipGetLastError();
 }
 

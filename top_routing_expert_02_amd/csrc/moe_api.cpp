@@ -28,6 +28,13 @@ int64_t max_rows_of(const moe_config& c) {
 
 int elem_size(const moe_config& c) { return c.dtype == MOE_BF16 ? 2 : 4; }
 
+// The layer's first expert GEMM reads token rows straight from x through
+// row_token (32-bit byte offsets into x); only a larger x needs the permuted
+// copy materialised in the workspace.
+bool layer_gathers(const moe_config& c) {
+  return c.T * static_cast<int64_t>(c.d) * elem_size(c) < (static_cast<int64_t>(1) << 32);
+}
+
 int32_t check_cfg(const moe_config* c) {
   if (c == nullptr) return MOE_ERR_INVALID_ARG;
   if (c->T < 0 || c->E < 1 || c->E > MOE_MAX_EXPERTS || c->k < 1 || c->k > c->E ||
@@ -70,7 +77,7 @@ Layout layout_of(const moe_config& c) {
   L.slot = take(T * k * 4);
   L.row_of = take(T * k * 4);
   L.row_token = take(R * 4);
-  L.x_perm = take(R * c.d * es);
+  L.x_perm = take(layer_gathers(c) ? 0 : R * c.d * es);
   L.h = take(R * c.d_ff * es);
   L.y_perm = take(R * c.d * 4);
   L.total = off;
@@ -110,6 +117,8 @@ int32_t route_stage(const moe_config& c, const void* x, const void* Wr, const fl
   return MOE_OK;
 }
 
+// x_perm may be null: the row copy is then skipped (the layer gathers rows in
+// its first GEMM instead).
 int32_t dispatch_stage(const moe_config& c, const void* x, const int32_t* ids, bool hist_ready,
                        int32_t* hist, int32_t* base, int32_t* counts, int32_t* offsets,
                        int32_t* slot, int32_t* row_of, int32_t* row_token, void* x_perm,
@@ -121,15 +130,17 @@ int32_t dispatch_stage(const moe_config& c, const void* x, const int32_t* ids, b
   return MOE_OK;
 }
 
-int32_t gemm1_stage(const moe_config& c, const void* x_perm, const int32_t* offsets,
-                    const void* W1, const float* b1, void* h, hipStream_t s) {
+// A is x_perm (row_idx null) or x with row r of the problem at row_idx[r].
+int32_t gemm1_stage(const moe_config& c, const void* A, const int32_t* row_idx,
+                    const int32_t* offsets, const void* W1, const float* b1, void* h,
+                    hipStream_t s) {
   const int64_t R = max_rows_of(c);
   const int per_expert = static_cast<int>(c.T < c.capacity ? c.T : c.capacity);
   if (c.dtype == MOE_BF16)
-    MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(x_perm), static_cast<const uint16_t*>(W1), b1, h,
-                             false, c.act, offsets, c.E, c.d_ff, c.d, R, per_expert, s));
+    MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(A), row_idx, static_cast<const uint16_t*>(W1), b1,
+                             h, false, c.act, offsets, c.E, c.d_ff, c.d, R, per_expert, s));
   else
-    MOE_HIP(launch_gemm_f32(static_cast<const float*>(x_perm), static_cast<const float*>(W1), b1,
+    MOE_HIP(launch_gemm_f32(static_cast<const float*>(A), row_idx, static_cast<const float*>(W1), b1,
                             static_cast<float*>(h), c.act, offsets, c.E, c.d_ff, c.d, per_expert, s));
   return MOE_OK;
 }
@@ -139,10 +150,10 @@ int32_t gemm2_stage(const moe_config& c, const void* h, const int32_t* offsets, 
   const int64_t R = max_rows_of(c);
   const int per_expert = static_cast<int>(c.T < c.capacity ? c.T : c.capacity);
   if (c.dtype == MOE_BF16)
-    MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W2), b2, y_perm,
-                             true, kActNone, offsets, c.E, c.d, c.d_ff, R, per_expert, s));
+    MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(h), nullptr, static_cast<const uint16_t*>(W2), b2,
+                             y_perm, true, kActNone, offsets, c.E, c.d, c.d_ff, R, per_expert, s));
   else
-    MOE_HIP(launch_gemm_f32(static_cast<const float*>(h), static_cast<const float*>(W2), b2, y_perm,
+    MOE_HIP(launch_gemm_f32(static_cast<const float*>(h), nullptr, static_cast<const float*>(W2), b2, y_perm,
                             kActNone, offsets, c.E, c.d, c.d_ff, per_expert, s));
   return MOE_OK;
 }
@@ -251,7 +262,7 @@ int32_t moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t*
       !aligned(b2, 16) || !aligned(h, 16) || !aligned(y_perm, 16) || !aligned(expert_offsets, 4))
     return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_ws(c, ws, ws_bytes));
-  MOE_TRY(gemm1_stage(c, x_perm, expert_offsets, W1, b1, h, stream));
+  MOE_TRY(gemm1_stage(c, x_perm, nullptr, expert_offsets, W1, b1, h, stream));
   return gemm2_stage(c, h, expert_offsets, W2, b2, y_perm, stream);
 }
 
@@ -298,7 +309,8 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* x, const void* W_r,
   int32_t* slot = in.slot != nullptr ? in.slot : at<int32_t>(ws, L.slot);
   int32_t* row_of = in.row_of != nullptr ? in.row_of : at<int32_t>(ws, L.row_of);
   int32_t* row_token = in.row_token != nullptr ? in.row_token : at<int32_t>(ws, L.row_token);
-  void* x_perm = at<char>(ws, L.x_perm);
+  const bool gather = layer_gathers(c);
+  void* x_perm = gather ? nullptr : at<char>(ws, L.x_perm);
   void* h = at<char>(ws, L.h);
   float* y_perm = at<float>(ws, L.y_perm);
   int32_t* hist = at<int32_t>(ws, L.hist);
@@ -315,7 +327,8 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* x, const void* W_r,
   MOE_TRY(dispatch_stage(c, x, ids, true, hist, at<int32_t>(ws, L.base), counts, offsets, slot,
                          row_of, row_token, x_perm, stream));
   MOE_TRY(mark(2));
-  MOE_TRY(gemm1_stage(c, x_perm, offsets, W1, b1, h, stream));
+  MOE_TRY(gemm1_stage(c, gather ? x : x_perm, gather ? row_token : nullptr, offsets, W1, b1, h,
+                      stream));
   MOE_TRY(mark(3));
   MOE_TRY(gemm2_stage(c, h, offsets, W2, b2, y_perm, stream));
   MOE_TRY(mark(4));

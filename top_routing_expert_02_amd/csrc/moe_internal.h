@@ -61,19 +61,27 @@ hipError_t launch_hist(const int32_t* ids, int64_t T, int k, int E, int32_t* his
 // column-wise exclusive prefix of hist over tiles (base), counts, offsets
 hipError_t launch_scan(const int32_t* hist, int ntiles, int E, int C, int32_t* base,
                        int32_t* counts, int32_t* offsets, hipStream_t s);
-// slots, capacity, row_of, row_token and the row copy into x_perm
+// slots, capacity, row_of, row_token and (when x_perm is not null) the row
+// copy into x_perm
 hipError_t launch_permute(const void* x, const int32_t* ids, const int32_t* base,
                           const int32_t* offsets, int64_t T, int k, int E, int C,
                           int row_bytes, int32_t* slot, int32_t* row_of, int32_t* row_token,
                           void* x_perm, hipStream_t s);
 
+// x_perm[r] = x[row_token[r]] for r < offsets[E] (rows bounded by max_rows)
+hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int32_t* offsets,
+                              int E, int64_t max_rows, int row_bytes, void* x_perm, hipStream_t s);
+
 // grouped expert GEMMs
 //   gemm1: h = act(A W1_e^T + b1_e)   A [rows,K=d], W1 [E,N=d_ff,K], h [rows,N]
 //   gemm2: y = A W2_e^T + b2_e        A [rows,K=d_ff], W2 [E,N=d,K], y fp32 [rows,N]
-hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, void* out,
+// row_idx (nullable): row r of the grouped problem is row row_idx[r] of A.
+hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uint16_t* W,
+                            const float* bias, void* out,
                             bool out_f32, int act, const int32_t* offsets, int E, int N, int K,
                             int64_t max_rows, int max_rows_per_expert, hipStream_t s);
-hipError_t launch_gemm_f32(const float* A, const float* W, const float* bias, float* out,
+hipError_t launch_gemm_f32(const float* A, const int32_t* row_idx, const float* W, const float* bias,
+                           float* out,
                            int act, const int32_t* offsets, int E, int N, int K,
                            int max_rows_per_expert, hipStream_t s);
 
