@@ -13,10 +13,9 @@
 // Both operands are K-contiguous (A row-major [rows, K]; W[e] row-major [N, K]).
 //
 // Design (gfx950, wave64, 160 KiB LDS per CU):
-//  * Block tile BM=256 tokens x BN features, K in steps of BK=32; four waves
-//    in a 2x2 grid;
-//    each wave owns 128 tokens x BN/2 features as 32x32 v_mfma_f32_32x32x16_bf16
-//    tiles. The weight tile is the MFMA A operand and the token tile the B
+//  * Block tile BM=256 tokens x BN=256 features, K in steps of BK=32; four
+//    waves in a 2x2 grid; each wave owns 128 tokens x 128 features as 32x32
+//    v_mfma_f32_32x32x16_bf16 tiles (fp32 accumulators in AGPRs). The weight tile is the MFMA A operand and the token tile the B
 //    operand, so a lane's accumulators hold 4 consecutive features of one
 //    token: the epilogue stores 8-byte (bf16) or 16-byte (fp32) vectors.
 //  * LDS holds four stages of both tiles (128 KiB at BN=256): tiles kt+1..kt+3
@@ -25,8 +24,10 @@
 //    which makes the fragment reads conflict-free.
 //  * Tiles move global -> LDS with gfx950's LDS-DMA loads (global_load_lds_
 //    dwordx4: no staging registers, no ds_write); each lane fetches the chunk
-//    the swizzle places at its LDS slot; one barrier per stage. The next
-//    tile's first three stages load during the current tile's epilogue.
+//    the swizzle places at its LDS slot; one barrier per stage. In the steady
+//    state a stage's loads are spread between the MFMAs of the K16 step that
+//    follows the barrier; the next tile's first stages load during the
+//    current tile's last MFMAs and epilogue.
 //  * Persistent blocks, one per CU. The schedule is computed on the device
 //    from expert_offsets (no host read-back): expert-major tiles, M tiles of
 //    an expert innermost, so concurrent tiles share weight panels. Blocks are
@@ -43,7 +44,6 @@ namespace {
 constexpr int BM = kGemmBM;   // 256 token rows per tile
 constexpr int BK = 32;        // K per LDS stage
 [[maybe_unused]] constexpr int ROWB = BK * 2;  // bytes per LDS row (64)
-[[maybe_unused]] constexpr int NST = 4;  // LDS stages: up to four K tiles in flight
 
 // Row r of a stage holds its 16-byte chunk c at position c ^ swz_key(r): the
 // key is the row's 256-byte block (mod 4). With it the MFMA fragment reads
@@ -92,15 +92,14 @@ __device__ __forceinline__ void step_4x4(f32x16_t (&acc)[4][4], const bf16x8_t (
                                          const bf16x8_t (&t)[4], bf16x8_t (&nw)[4],
                                          bf16x8_t (&nt)[4], uint32_t ta, uint32_t wa) {
   asm volatile(
-      "s_nop 1\n\t"
-      MOE_MFMA("%0", "%24", "%28") MOE_RD("%16", "%32", "0")
-      MOE_MFMA("%1", "%24", "%29") MOE_RD("%17", "%32", "2048")
-      MOE_MFMA("%2", "%24", "%30") MOE_RD("%18", "%32", "4096")
-      MOE_MFMA("%3", "%24", "%31") MOE_RD("%19", "%32", "6144")
-      MOE_MFMA("%4", "%25", "%28") MOE_RD("%20", "%33", "0")
-      MOE_MFMA("%5", "%25", "%29") MOE_RD("%21", "%33", "2048")
-      MOE_MFMA("%6", "%25", "%30") MOE_RD("%22", "%33", "4096")
-      MOE_MFMA("%7", "%25", "%31") MOE_RD("%23", "%33", "6144")
+      MOE_RD("%16", "%32", "0") MOE_RD("%17", "%32", "2048")
+      MOE_RD("%18", "%32", "4096") MOE_RD("%19", "%32", "6144")
+      MOE_RD("%20", "%33", "0") MOE_RD("%21", "%33", "2048")
+      MOE_RD("%22", "%33", "4096") MOE_RD("%23", "%33", "6144")
+      MOE_MFMA("%0", "%24", "%28") MOE_MFMA("%1", "%24", "%29")
+      MOE_MFMA("%2", "%24", "%30") MOE_MFMA("%3", "%24", "%31")
+      MOE_MFMA("%4", "%25", "%28") MOE_MFMA("%5", "%25", "%29")
+      MOE_MFMA("%6", "%25", "%30") MOE_MFMA("%7", "%25", "%31")
       MOE_MFMA("%8", "%26", "%28") MOE_MFMA("%9", "%26", "%29")
       MOE_MFMA("%10", "%26", "%30") MOE_MFMA("%11", "%26", "%31")
       MOE_MFMA("%12", "%27", "%28") MOE_MFMA("%13", "%27", "%29")
@@ -140,13 +139,12 @@ __device__ __forceinline__ void step_4x2(f32x16_t (&acc)[2][4], const bf16x8_t (
                                          const bf16x8_t (&t)[4], bf16x8_t (&nw)[2],
                                          bf16x8_t (&nt)[4], uint32_t ta, uint32_t wa) {
   asm volatile(
-      "s_nop 1\n\t"
-      MOE_MFMA("%0", "%14", "%16") MOE_RD("%8", "%20", "0")
-      MOE_MFMA("%1", "%14", "%17") MOE_RD("%9", "%20", "2048")
-      MOE_MFMA("%2", "%14", "%18") MOE_RD("%10", "%20", "4096")
-      MOE_MFMA("%3", "%14", "%19") MOE_RD("%11", "%20", "6144")
-      MOE_MFMA("%4", "%15", "%16") MOE_RD("%12", "%21", "0")
-      MOE_MFMA("%5", "%15", "%17") MOE_RD("%13", "%21", "2048")
+      MOE_RD("%8", "%20", "0") MOE_RD("%9", "%20", "2048")
+      MOE_RD("%10", "%20", "4096") MOE_RD("%11", "%20", "6144")
+      MOE_RD("%12", "%21", "0") MOE_RD("%13", "%21", "2048")
+      MOE_MFMA("%0", "%14", "%16") MOE_MFMA("%1", "%14", "%17")
+      MOE_MFMA("%2", "%14", "%18") MOE_MFMA("%3", "%14", "%19")
+      MOE_MFMA("%4", "%15", "%16") MOE_MFMA("%5", "%15", "%17")
       MOE_MFMA("%6", "%15", "%18") MOE_MFMA("%7", "%15", "%19")
       "s_waitcnt lgkmcnt(0)"
       : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]), "+a"(acc[1][0]),
@@ -169,6 +167,88 @@ __device__ __forceinline__ void last_4x2(f32x16_t (&acc)[2][4], const bf16x8_t (
       : "v"(w[0]), "v"(w[1]), "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3])
       : "memory");
 }
+
+// The same K16 steps with the next stage's LDS-DMA loads spread between the
+// MFMAs (one load per one or two MFMAs). Issued as a burst right after the
+// barrier, the four waves' loads queue at the address unit together and the
+// waves stall behind them; spread out, they issue in the MFMA shadow. M0
+// carries the LDS destination of each load (lane L writes bytes 16L..16L+15
+// of a 1 KiB block); la / lb are this wave's first token / weight block of the
+// stage being refilled, ga / gw the global bases of its K columns, vo the
+// per-lane byte offsets (token blocks first, then weight blocks).
+// M0 is reserved by the compiler, which sets it again before each LDS-DMA
+// load of its own; the clobber below orders those against these blocks.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+#define MOE_M0(BASE, OFF) "s_add_u32 m0, " BASE ", " OFF "\n\t"
+#define MOE_DMA(V, G) "global_load_lds_dwordx4 " V ", " G "\n\t"
+
+__device__ __forceinline__ void step_dma_4x4(f32x16_t (&acc)[4][4], const bf16x8_t (&w)[4],
+                                             const bf16x8_t (&t)[4], bf16x8_t (&nw)[4],
+                                             bf16x8_t (&nt)[4], uint32_t ta, uint32_t wa,
+                                             const uint32_t (&vo)[8], uint32_t la, uint32_t lb,
+                                             const char* ga, const char* gw) {
+  asm volatile(
+      MOE_RD("%16", "%32", "0") MOE_RD("%17", "%32", "2048")
+      MOE_RD("%18", "%32", "4096") MOE_RD("%19", "%32", "6144")
+      MOE_RD("%20", "%33", "0") MOE_RD("%21", "%33", "2048")
+      MOE_RD("%22", "%33", "4096") MOE_RD("%23", "%33", "6144")
+      MOE_M0("%42", "0") MOE_MFMA("%0", "%24", "%28") MOE_DMA("%34", "%44")
+      MOE_M0("%42", "0x400") MOE_MFMA("%1", "%24", "%29") MOE_MFMA("%2", "%24", "%30")
+      MOE_DMA("%35", "%44")
+      MOE_M0("%42", "0x800") MOE_MFMA("%3", "%24", "%31") MOE_MFMA("%4", "%25", "%28")
+      MOE_DMA("%36", "%44")
+      MOE_M0("%42", "0xc00") MOE_MFMA("%5", "%25", "%29") MOE_MFMA("%6", "%25", "%30")
+      MOE_DMA("%37", "%44")
+      MOE_M0("%43", "0") MOE_MFMA("%7", "%25", "%31") MOE_MFMA("%8", "%26", "%28")
+      MOE_DMA("%38", "%45")
+      MOE_M0("%43", "0x400") MOE_MFMA("%9", "%26", "%29") MOE_MFMA("%10", "%26", "%30")
+      MOE_DMA("%39", "%45")
+      MOE_M0("%43", "0x800") MOE_MFMA("%11", "%26", "%31") MOE_MFMA("%12", "%27", "%28")
+      MOE_DMA("%40", "%45")
+      MOE_M0("%43", "0xc00") MOE_MFMA("%13", "%27", "%29") MOE_MFMA("%14", "%27", "%30")
+      MOE_DMA("%41", "%45")
+      MOE_MFMA("%15", "%27", "%31")
+      "s_waitcnt lgkmcnt(0)"
+      : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]), "+a"(acc[1][0]),
+        "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]), "+a"(acc[2][0]), "+a"(acc[2][1]),
+        "+a"(acc[2][2]), "+a"(acc[2][3]), "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]),
+        "+a"(acc[3][3]), "=&v"(nt[0]), "=&v"(nt[1]), "=&v"(nt[2]), "=&v"(nt[3]), "=&v"(nw[0]),
+        "=&v"(nw[1]), "=&v"(nw[2]), "=&v"(nw[3])
+      : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3]),
+        "v"(ta), "v"(wa), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "v"(vo[4]), "v"(vo[5]),
+        "v"(vo[6]), "v"(vo[7]), "s"(la), "s"(lb), "s"(ga), "s"(gw)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ void step_dma_4x2(f32x16_t (&acc)[2][4], const bf16x8_t (&w)[2],
+                                             const bf16x8_t (&t)[4], bf16x8_t (&nw)[2],
+                                             bf16x8_t (&nt)[4], uint32_t ta, uint32_t wa,
+                                             const uint32_t (&vo)[6], uint32_t la, uint32_t lb,
+                                             const char* ga, const char* gw) {
+  asm volatile(
+      MOE_RD("%8", "%20", "0") MOE_RD("%9", "%20", "2048")
+      MOE_RD("%10", "%20", "4096") MOE_RD("%11", "%20", "6144")
+      MOE_RD("%12", "%21", "0") MOE_RD("%13", "%21", "2048")
+      MOE_M0("%28", "0") MOE_MFMA("%0", "%14", "%16") MOE_DMA("%22", "%30")
+      MOE_M0("%28", "0x400") MOE_MFMA("%1", "%14", "%17") MOE_DMA("%23", "%30")
+      MOE_M0("%28", "0x800") MOE_MFMA("%2", "%14", "%18") MOE_DMA("%24", "%30")
+      MOE_M0("%28", "0xc00") MOE_MFMA("%3", "%14", "%19") MOE_DMA("%25", "%30")
+      MOE_M0("%29", "0") MOE_MFMA("%4", "%15", "%16") MOE_DMA("%26", "%31")
+      MOE_M0("%29", "0x400") MOE_MFMA("%5", "%15", "%17") MOE_DMA("%27", "%31")
+      MOE_MFMA("%6", "%15", "%18") MOE_MFMA("%7", "%15", "%19")
+      "s_waitcnt lgkmcnt(0)"
+      : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]), "+a"(acc[1][0]),
+        "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]), "=&v"(nt[0]), "=&v"(nt[1]), "=&v"(nt[2]),
+        "=&v"(nt[3]), "=&v"(nw[0]), "=&v"(nw[1])
+      : "v"(w[0]), "v"(w[1]), "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3]), "v"(ta), "v"(wa),
+        "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "v"(vo[4]), "v"(vo[5]), "s"(la), "s"(lb),
+        "s"(ga), "s"(gw)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+#undef MOE_M0
+#undef MOE_DMA
 
 // Fragments only (the first K16 step of a tile).
 template <int TM, int TN>
@@ -202,6 +282,16 @@ __device__ __forceinline__ void step(f32x16_t (&acc)[TN][TM], const bf16x8_t (&w
                                      uint32_t ta, uint32_t wa) {
   if constexpr (TN == 4) step_4x4(acc, w, t, nw, nt, ta, wa);
   else step_4x2(acc, w, t, nw, nt, ta, wa);
+}
+
+template <int TM, int TN, int NV>
+__device__ __forceinline__ void step_dma(f32x16_t (&acc)[TN][TM], const bf16x8_t (&w)[TN],
+                                         const bf16x8_t (&t)[TM], bf16x8_t (&nw)[TN],
+                                         bf16x8_t (&nt)[TM], uint32_t ta, uint32_t wa,
+                                         const uint32_t (&vo)[NV], uint32_t la, uint32_t lb,
+                                         const char* ga, const char* gw) {
+  if constexpr (TN == 4) step_dma_4x4(acc, w, t, nw, nt, ta, wa, vo, la, lb, ga, gw);
+  else step_dma_4x2(acc, w, t, nw, nt, ta, wa, vo, la, lb, ga, gw);
 }
 
 template <int TM, int TN>
@@ -257,11 +347,12 @@ __device__ __forceinline__ TileInfo decode_tile(int tile, const int* s_tiles, co
   return t;
 }
 
-// Wait until at most n later stages (G loads each) of this wave are in flight.
-template <int G>
+// Wait until at most min(n, MAXN) later stages (G loads each) of this wave
+// are in flight.
+template <int G, int MAXN>
 __device__ __forceinline__ void wait_loads(int n) {
-  if (n >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * G) : "memory");
-  else if (n == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G) : "memory");
+  if (MAXN >= 2 && n >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * G) : "memory");
+  else if (MAXN >= 1 && n >= 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G) : "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
@@ -348,8 +439,8 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], const fl
 
 }  // namespace
 
-template <int BN, bool OUT_F32, int ACT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int BN, int NST, int OCC, bool OUT_F32, int ACT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ row_idx,
                               const uint16_t* __restrict__ W,
                               const float* __restrict__ bias, void* __restrict__ out,
@@ -419,7 +510,7 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
   const uint32_t trow = wm * WM * ROWB;            // this wave's token rows in a stage
   const uint32_t wrow = A_BYTES + wn * WN * ROWB;  // this wave's weight rows in a stage
 
-  uint32_t aoffs[LA], boffs[LB];
+  uint32_t aoffs[LA], boffs[LB], vo[G];
   const char* Abase;
   const char* Wbase;
   TileInfo cur = decode_tile(tile, s_tiles, offsets, E, NT, BN);
@@ -444,30 +535,43 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
 
     TileInfo done = cur;
     const int next = tile + Gd;
-    uint32_t sb = lds_base;  // stage of tile t
+#pragma unroll
+    for (int i = 0; i < LA; ++i) vo[i] = aoffs[i];
+#pragma unroll
+    for (int i = 0; i < LB; ++i) vo[LA + i] = boffs[i];
+    int sc = 0;              // stage holding K tile t
+    uint32_t sb = lds_base;  // its LDS address
     int t = 0;
-    // steady state: tile t+4 still to load
+    // steady state: K tile t+NST still to load
     for (; t + NST < nk; ++t) {
-      const uint32_t sn = lds_base + ((t + 1) & (NST - 1)) * STAGE;
+      const int sn_i = (sc + 1 == NST) ? 0 : sc + 1;
+      const uint32_t sn = lds_base + sn_i * STAGE;
       // K16 step 0 of stage t; read step 1 of stage t
       step<TM, TN>(acc, w0, t0, w1, t1, sb + trow + fo1, sb + wrow + fo1);
-      // stage t+1 ready (tiles t+2, t+3 may still load); every wave is done
-      // with stage t, which then takes tile t+4
-      wait_loads<G>(2);
+      // stage t+1 ready (t+2 .. t+NST-1 may still load); every wave is done
+      // with stage t, which then takes K tile t+NST
+      wait_loads<G, NST - 2>(NST - 2);
       __syncthreads();
-      issue_stage<LA, LB, A_BYTES>(Abase + (t + NST) * ROWB, Wbase + (t + NST) * ROWB,
-                                   lds + (t & (NST - 1)) * STAGE, aoffs, boffs, wave);
-      // K16 step 1 of stage t; read step 0 of stage t+1
-      step<TM, TN>(acc, w1, t1, w0, t0, sn + trow + fo0, sn + wrow + fo0);
+      // K16 step 1 of stage t; read step 0 of stage t+1; stage t (free after
+      // the barrier) takes K tile t+NST
+      {
+        const uint32_t sl = lds_base + sc * STAGE;
+        step_dma<TM, TN, G>(acc, w1, t1, w0, t0, sn + trow + fo0, sn + wrow + fo0, vo,
+                            sl + wave * LA * 1024, sl + A_BYTES + wave * LB * 1024,
+                            Abase + (t + NST) * ROWB, Wbase + (t + NST) * ROWB);
+      }
+      sc = sn_i;
       sb = sn;
     }
     // the last stages: nothing more to load
     for (; t + 1 < nk; ++t) {
-      const uint32_t sn = lds_base + ((t + 1) & (NST - 1)) * STAGE;
+      const int sn_i = (sc + 1 == NST) ? 0 : sc + 1;
+      const uint32_t sn = lds_base + sn_i * STAGE;
       step<TM, TN>(acc, w0, t0, w1, t1, sb + trow + fo1, sb + wrow + fo1);
-      wait_loads<G>(nk - 2 - t);
+      wait_loads<G, NST - 2>(nk - 2 - t);
       __syncthreads();
       step<TM, TN>(acc, w1, t1, w0, t0, sn + trow + fo0, sn + wrow + fo0);
+      sc = sn_i;
       sb = sn;
     }
     // the last stage
@@ -495,6 +599,13 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
 #endif
 }
 
+#ifndef MOE_GEMM_NST
+#define MOE_GEMM_NST 4
+#endif
+#ifndef MOE_GEMM_OCC
+#define MOE_GEMM_OCC 1
+#endif
+
 namespace {
 
 int cu_count() {
@@ -520,22 +631,19 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uin
   if (max_rows <= 0) return hipSuccess;
   // upper bound on tiles: sum_e ceil(n_e/BM) <= max_rows/BM + E
   const int64_t mt_bound = max_rows / BM + E;
-  const int cus = cu_count();
-  auto grid_for = [&](int bn) {
-    const int64_t tiles = mt_bound * ((N + bn - 1) / bn);
-    return static_cast<unsigned>(tiles < cus ? tiles : cus);
-  };
+  constexpr int BN = 256, NST = MOE_GEMM_NST, OCC = MOE_GEMM_OCC;
+  const int slots = cu_count() * OCC;
+  const int64_t tiles = mt_bound * ((N + BN - 1) / BN);
+  const unsigned grid = static_cast<unsigned>(tiles < slots ? tiles : slots);
   if (out_f32) {
-    constexpr int BN = 128;
-    grouped_gemm_bf16_kernel<BN, true, kActNone><<<grid_for(BN), 256, 0, s>>>(A, row_idx, W, bias, out, offsets, E, N, K);
+    grouped_gemm_bf16_kernel<BN, NST, OCC, true, kActNone><<<grid, 256, 0, s>>>(A, row_idx, W, bias, out, offsets, E, N, K);
   } else {
-    constexpr int BN = 128;
     if (act == kActRelu)
-      grouped_gemm_bf16_kernel<BN, false, kActRelu><<<grid_for(BN), 256, 0, s>>>(A, row_idx, W, bias, out, offsets, E, N, K);
+      grouped_gemm_bf16_kernel<BN, NST, OCC, false, kActRelu><<<grid, 256, 0, s>>>(A, row_idx, W, bias, out, offsets, E, N, K);
     else if (act == kActGeluTanh)
-      grouped_gemm_bf16_kernel<BN, false, kActGeluTanh><<<grid_for(BN), 256, 0, s>>>(A, row_idx, W, bias, out, offsets, E, N, K);
+      grouped_gemm_bf16_kernel<BN, NST, OCC, false, kActGeluTanh><<<grid, 256, 0, s>>>(A, row_idx, W, bias, out, offsets, E, N, K);
     else
-      grouped_gemm_bf16_kernel<BN, false, kActNone><<<grid_for(BN), 256, 0, s>>>(A, row_idx, W, bias, out, offsets, E, N, K);
+      grouped_gemm_bf16_kernel<BN, NST, OCC, false, kActNone><<<grid, 256, 0, s>>>(A, row_idx, W, bias, out, offsets, E, N, K);
   }
   return hipGetLastError();
 }
