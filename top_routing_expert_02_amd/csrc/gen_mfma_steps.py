@@ -1,0 +1,173 @@
+#!/usr/bin/env python3
+"""Writes mfma_steps.inc: the hand-scheduled inline-asm blocks of the bf16
+grouped GEMM (ffn_bf16.hip), one set per wave tile of (32*TM tokens) x
+(32*TN features).
+
+Each block is an unrolled list of v_mfma_f32_32x32x16_bf16 with the other
+instructions of the step placed one after each MFMA (see the kernel's notes
+on the matrix-core issue shadow). The blocks are generated rather than typed
+because every operand index depends on the tile shape.
+
+  python3 gen_mfma_steps.py        (rewrites mfma_steps.inc next to this file)
+"""
+import os
+
+SHAPES = [(4, 4), (3, 4)]  # (TM, TN): 256 x 256 and 192 x 256 block tiles
+
+
+def q(s):
+    return '      "' + s + '\\n\\t"'
+
+
+def acc_list(TM, TN):
+    return ", ".join(f'"+a"(acc[{i}][{j}])' for i in range(TN) for j in range(TM))
+
+
+def cur_list(TM, TN):
+    return ", ".join([f'"v"(w[{i}])' for i in range(TN)] + [f'"v"(t[{j}])' for j in range(TM)])
+
+
+def next_list(TM, TN):
+    return ", ".join([f'"=&v"(nt[{j}])' for j in range(TM)] + [f'"=&v"(nw[{i}])' for i in range(TN)])
+
+
+def mfmas(TM, TN, w0, t0):
+    return [f"v_mfma_f32_32x32x16_bf16 %{TM*i+j}, %{w0+i}, %{t0+j}, %{TM*i+j}"
+            for i in range(TN) for j in range(TM)]
+
+
+def step_body(TM, TN, dma):
+    nacc = TM * TN
+    nt0 = nacc
+    nw0 = nt0 + TM
+    w0 = nw0 + TN
+    t0 = w0 + TN
+    ta = t0 + TM
+    wa = ta + 1
+    LA, LB = 2 * TM, 2 * TN
+    vo0 = wa + 1
+    la = vo0 + LA + LB
+    lb, ga, gw = la + 1, la + 2, la + 3
+    reads = ([f"ds_read_b128 %{nt0+j}, %{ta} offset:{4096*j}" for j in range(TM)] +
+             [f"ds_read_b128 %{nw0+i}, %{wa} offset:{4096*i}" for i in range(TN)])
+    mf = mfmas(TM, TN, w0, t0)
+    loads = []
+    if dma:
+        loads = ([(f"s_add_u32 m0, %{la}, 0x{b*0x400:x}", f"global_load_lds_dwordx4 %{vo0+b}, %{ga}")
+                  for b in range(LA)] +
+                 [(f"s_add_u32 m0, %{lb}, 0x{b*0x400:x}", f"global_load_lds_dwordx4 %{vo0+LA+b}, %{gw}")
+                  for b in range(LB)])
+    per = [0] * len(mf)
+    for k in range(len(loads)):
+        per[k % len(mf)] += 1
+    out, di, ri = [], 0, 0
+    for m in range(len(mf)):
+        pend = loads[di:di + per[m]]
+        di += per[m]
+        if pend:
+            out.append(pend[0][0])  # M0 write; the MFMA gives the wait state
+        out.append(mf[m])
+        for k, (m0, ld) in enumerate(pend):
+            if k > 0:
+                out += [m0, "s_nop 0"]
+            out.append(ld)
+        if ri < len(reads):
+            out.append(reads[ri])
+            ri += 1
+    out += reads[ri:]
+    return "\n".join(q(s) for s in out) + '\n      "s_waitcnt lgkmcnt(0)"'
+
+
+def emit(TM, TN):
+    LA, LB = 2 * TM, 2 * TN
+    n = f"{TM}x{TN}"
+    vo = ", ".join(f'"v"(vo[{b}])' for b in range(LA + LB))
+    w0 = TM * TN
+    t0 = w0 + TN
+    last = "\n".join(q(s) for s in ["s_nop 1"] + mfmas(TM, TN, w0, t0) + ["s_nop 7", "s_nop 7"])
+    frag = ([f"ds_read_b128 %{j}, %{TM+TN} offset:{4096*j}" for j in range(TM)] +
+            [f"ds_read_b128 %{TM+i}, %{TM+TN+1} offset:{4096*i}" for i in range(TN)])
+    frag_outs = ", ".join([f'"=&v"(nt[{j}])' for j in range(TM)] + [f'"=&v"(nw[{i}])' for i in range(TN)])
+    stg = []
+    for b in range(LA):
+        stg += [f"s_add_u32 m0, %{LA+LB}, 0x{b*0x400:x}", "s_nop 0", f"global_load_lds_dwordx4 %{b}, %{LA+LB+2}"]
+    for b in range(LB):
+        stg += [f"s_add_u32 m0, %{LA+LB+1}, 0x{b*0x400:x}", "s_nop 0",
+                f"global_load_lds_dwordx4 %{LA+b}, %{LA+LB+3}"]
+    stg_ins = ", ".join([f'"v"(ao[{b}])' for b in range(LA)] + [f'"v"(bo[{b}])' for b in range(LB)])
+    sig_cur = f"const bf16x8_t (&w)[{TN}], const bf16x8_t (&t)[{TM}]"
+    sig_next = f"bf16x8_t (&nw)[{TN}], bf16x8_t (&nt)[{TM}]"
+    return f'''
+// ---- wave tile {32*TM} tokens x {32*TN} features ({TM}x{TN} MFMA tiles)
+__device__ __forceinline__ void step_{n}(f32x16_t (&acc)[{TN}][{TM}], {sig_cur},
+    {sig_next}, uint32_t ta, uint32_t wa) {{
+  asm volatile(
+{step_body(TM, TN, False)}
+      : {acc_list(TM, TN)},
+        {next_list(TM, TN)}
+      : {cur_list(TM, TN)}, "v"(ta), "v"(wa)
+      : "memory");
+}}
+
+__device__ __forceinline__ void step_dma_{n}(f32x16_t (&acc)[{TN}][{TM}], {sig_cur},
+    {sig_next}, uint32_t ta, uint32_t wa, const uint32_t (&vo)[{LA+LB}], uint32_t la, uint32_t lb,
+    const char* ga, const char* gw) {{
+  asm volatile(
+{step_body(TM, TN, True)}
+      : {acc_list(TM, TN)},
+        {next_list(TM, TN)}
+      : {cur_list(TM, TN)}, "v"(ta), "v"(wa),
+        {vo},
+        "s"(la), "s"(lb), "s"(ga), "s"(gw)
+      : "memory", "m0");
+}}
+
+// the last K16 step of a tile; its results are read by VALU next (24 wait states)
+__device__ __forceinline__ void last_{n}(f32x16_t (&acc)[{TN}][{TM}], {sig_cur}) {{
+  asm volatile(
+{last}
+      "s_nop 7"
+      : {acc_list(TM, TN)}
+      : {cur_list(TM, TN)}
+      : "memory");
+}}
+
+// the first fragments of a tile (early-clobber: a read may land before the
+// later reads are issued, so no destination may share an address register)
+__device__ __forceinline__ void frags_{n}({sig_next}, uint32_t ta, uint32_t wa) {{
+  asm volatile(
+{chr(10).join(q(s) for s in frag)}
+      "s_waitcnt lgkmcnt(0)"
+      : {frag_outs}
+      : "v"(ta), "v"(wa)
+      : "memory");
+}}
+
+// one stage's LDS-DMA loads: {LA} token blocks, then {LB} weight blocks
+__device__ __forceinline__ void stage_{n}(const uint32_t (&ao)[{LA}], const uint32_t (&bo)[{LB}],
+    uint32_t la, uint32_t lb, const char* ga, const char* gw) {{
+  asm volatile(
+{chr(10).join(q(s) for s in stg[:-1])}
+      "{stg[-1]}"
+      :
+      : {stg_ins},
+        "s"(la), "s"(lb), "s"(ga), "s"(gw)
+      : "memory", "m0");
+}}
+'''
+
+
+def main():
+    here = os.path.dirname(os.path.abspath(__file__))
+    parts = ["// Generated by gen_mfma_steps.py; do not edit by hand.\n"
+             "// Inline-asm K16 steps of the bf16 grouped GEMM (included by ffn_bf16.hip).\n"
+             "#pragma clang diagnostic push\n#pragma clang diagnostic ignored \"-Winline-asm\"\n"]
+    for TM, TN in SHAPES:
+        parts.append(emit(TM, TN))
+    parts.append("#pragma clang diagnostic pop\n")
+    with open(os.path.join(here, "mfma_steps.inc"), "w") as f:
+        f.write("".join(parts))
+
+
+if __name__ == "__main__":
+    main()
