@@ -53,7 +53,7 @@ def gemm_source_digest():
     count only while it is unchanged."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("ffn_bf16.hip", "moe_internal.h"):
+    for f in ("ffn_bf16.hip", "mfma_steps.inc", "moe_internal.h"):
         with open(os.path.join(ROOT, "top_routing_expert_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
