@@ -130,9 +130,12 @@ __global__ __launch_bounds__(256) void logits_f32_kernel(const float* __restrict
 
 // ------------------------------------------------------------------ top-k, softmax, gates
 //
-// A block owns one tile of 64 tokens; each wave owns 16 of them. A token is
-// handled by a group of G lanes (G a power of two, 4 <= G <= 64); lane g of
-// the group holds the logits of experts g, g+G, ... (NV of them).
+// A block owns one tile of 64 tokens. A token is handled by a group of G
+// lanes (G a power of two, 4 <= G <= 64); lane g of the group holds the
+// logits of experts g, g+G, ... (NV of them). A wave holds 64/G tokens at a
+// time, and the block has enough waves (up to 16) that the tile takes as few
+// passes as possible: the rounds below are chains of dependent cross-lane
+// shuffles, so the kernel is latency-bound and wants many waves in flight.
 //
 // Round r of k picks the group-wide best (largest logit, then lowest index)
 // among the experts not yet taken, by an xor butterfly over the group; the
@@ -147,16 +150,18 @@ __global__ __launch_bounds__(256) void logits_f32_kernel(const float* __restrict
 //
 // Side outputs per tile: the expert histogram (integer LDS atomics, order
 // free) and sum_t p_{t,i} (fixed-order sums: lanes, then groups, then waves).
-template <int G, int NV>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int64_t T,
+template <int G, int NV, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void topk_kernel(const float* __restrict__ logits, int64_t T,
                                                    int E, int k, int renormalize,
                                                    int32_t* __restrict__ ids,
                                                    float* __restrict__ gates,
                                                    float* __restrict__ prob_part,
                                                    int32_t* __restrict__ hist) {
-  constexpr int TPW = 64 / G;      // tokens per wave pass
-  constexpr int PASSES = 16 / TPW;  // passes per wave (16 tokens per wave)
-  __shared__ float s_prob[4][1024];
+  constexpr int TPW = 64 / G;                 // tokens per wave pass
+  constexpr int PASSES = 64 / (TPW * WAVES);  // passes per wave
+  static_assert(TPW * WAVES * PASSES == 64, "64 tokens per tile");
+  constexpr int NT = 64 * WAVES;              // threads
+  __shared__ float s_prob[WAVES][1024];
   __shared__ int s_hist[1024];
 
   const int lane = threadIdx.x & 63;
@@ -168,7 +173,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   const bool want_hist = hist != nullptr;
 
   if (want_hist)
-    for (int e = threadIdx.x; e < E; e += 256) s_hist[e] = 0;
+    for (int e = threadIdx.x; e < E; e += NT) s_hist[e] = 0;
   __syncthreads();
 
   float psum[NV];
@@ -176,7 +181,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   for (int j = 0; j < NV; ++j) psum[j] = 0.f;
 
   for (int pass = 0; pass < PASSES; ++pass) {
-    const int64_t t = tile * 64 + wave * 16 + pass * TPW + grp;
+    const int64_t t = tile * 64 + (wave * PASSES + pass) * TPW + grp;
     const bool tv = t < T;
     const float* row = logits + (tv ? t : 0) * E;
     float v[NV];
@@ -268,9 +273,13 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) {
-    if (want_prob)
-      prob_part[tile * E + e] = ((s_prob[0][e] + s_prob[1][e]) + s_prob[2][e]) + s_prob[3][e];
+  for (int e = threadIdx.x; e < E; e += NT) {
+    if (want_prob) {
+      float sum = s_prob[0][e];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) sum += s_prob[w][e];  // fixed order
+      prob_part[tile * E + e] = sum;
+    }
     if (want_hist) hist[tile * E + e] = s_hist[e];
   }
 }
@@ -315,16 +324,20 @@ hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int renorma
                        int32_t* ids, float* gates, float* prob_part, int32_t* hist,
                        hipStream_t s) {
   const unsigned grid = static_cast<unsigned>((T + 63) / 64);
-#define MOE_TOPK(G, NV) \
-  topk_kernel<G, NV><<<grid, 256, 0, s>>>(logits, T, E, k, renormalize, ids, gates, prob_part, hist)
+#define MOE_TOPK(G, NV)                                                                          \
+  topk_kernel<G, NV, (G >= 16 ? 16 : G)><<<grid, 64 * (G >= 16 ? 16 : G), 0, s>>>(                \
+      logits, T, E, k, renormalize, ids, gates, prob_part, hist)
+  // groups of at least 16 lanes (k <= 16 results per token) holding up to 16
+  // logits per lane: a wave runs 4 tokens' shuffle chains side by side, and
+  // each round's butterfly has at most 4 levels below 256 experts
   if (E <= 4) MOE_TOPK(4, 1);
   else if (E <= 8) MOE_TOPK(8, 1);
   else if (E <= 16) MOE_TOPK(16, 1);
-  else if (E <= 32) MOE_TOPK(32, 1);
-  else if (E <= 64) MOE_TOPK(64, 1);
-  else if (E <= 128) MOE_TOPK(64, 2);
-  else if (E <= 256) MOE_TOPK(64, 4);
-  else if (E <= 512) MOE_TOPK(64, 8);
+  else if (E <= 32) MOE_TOPK(16, 2);
+  else if (E <= 64) MOE_TOPK(16, 4);
+  else if (E <= 128) MOE_TOPK(16, 8);
+  else if (E <= 256) MOE_TOPK(16, 16);
+  else if (E <= 512) MOE_TOPK(32, 16);
   else MOE_TOPK(64, 16);
 #undef MOE_TOPK
   return hipGetLastError();
