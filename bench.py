@@ -100,9 +100,9 @@ def stage_bytes_flops(w, C, counts, offsets):
     return {
         # x read once, W_r once, ids+gates written
         "route": {"bytes": T * d * b + E * d * b + T * k * 8, "flops": 2 * T * d * E},
-        # x rows read once per token with a kept assignment (<= T), x_perm written,
-        # ids read, slot/row_of written, row_token written
-        "dispatch": {"bytes": T * d * b + rows * d * b + T * k * 12 + rows * 4, "flops": 0},
+        # ids read, slot/row_of written, row_token written (the layer path gathers
+        # token rows inside the first GEMM: no permuted copy of x is written)
+        "dispatch": {"bytes": T * k * 12 + rows * 4, "flops": 0},
         # touched experts' W1 read, x_perm read, h written
         "gemm1": {"bytes": touched * d_ff * d * b + rows * d * b + rows * d_ff * b,
                   "flops": 2 * rows * d * d_ff},

@@ -52,6 +52,13 @@ MINI = {
     "skewed_bf16_mini": WORKLOADS["skewed_bf16"].scaled(name="skewed_bf16_mini", T=1500, d=256, d_ff=256),
     "large_e_bf16_mini": WORKLOADS["large_e_bf16"].scaled(name="large_e_bf16_mini", T=600, d=256, d_ff=192),
     "max_e_k_bf16": WORKLOADS["large_e_bf16"].scaled(name="max_e_k_bf16", T=300, d=64, d_ff=64, E=1024, k=16),
+    # an expert count that does not divide 256 (the per-expert histogram sums
+    # take the strided path)
+    "e12_bf16": WORKLOADS["skewed_bf16"].scaled(name="e12_bf16", T=900, d=64, d_ff=128, E=12, k=3),
+    # 33 tiles x 1024 experts: above the single-launch scan limit, so the
+    # separate scan kernel runs
+    "scan_split_bf16": WORKLOADS["large_e_bf16"].scaled(name="scan_split_bf16", T=2100, d=64, d_ff=64,
+                                                        E=1024, k=4),
 }
 
 

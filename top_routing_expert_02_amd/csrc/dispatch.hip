@@ -15,6 +15,8 @@
 //      expert; counts, n_e = min(count_e, C) and offsets follow;
 //   3. inside a tile, a 64-bit mask per expert marks the tokens that chose it;
 //      popcount of the mask below a token gives its rank in the tile.
+// For small problems steps 2 and 3 run in one kernel (each tile block sums
+// the histograms it needs itself), which saves a launch.
 #include "moe_internal.h"
 
 namespace moe {
@@ -124,6 +126,112 @@ __global__ __launch_bounds__(256) void permute_kernel(
   }
 }
 
+// The same, for small problems (ntiles * E <= kFusedScanLimit) without the
+// separate scan: every block sums the per-tile histograms itself (the bases of
+// its own tile and the totals), then derives n_e = min(count_e, C) and the
+// exclusive prefix over experts. All blocks compute identical values; block 0
+// writes counts and offsets.
+constexpr int kFusedScanLimit = 32768;
+
+__global__ __launch_bounds__(256) void permute_scan_kernel(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ hist, int ntiles, int64_t T, int k,
+    int E, int C, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ slot, int32_t* __restrict__ row_of, int32_t* __restrict__ row_token) {
+  __shared__ unsigned long long mask[1024];
+  __shared__ int s_base[1024];
+  __shared__ int s_cnt[1024];
+  __shared__ int s_off[1025];
+  __shared__ int s_part[2][256];
+  const int tid = threadIdx.x;
+  const int64_t tile = blockIdx.x;
+  const int64_t t0 = tile * kTileTokens;
+  const int nt = static_cast<int>(min<int64_t>(kTileTokens, T - t0));
+  const int np = nt * k;
+  // s_base[e] = sum of hist[t2][e] over tiles t2 before this one, s_cnt[e] the
+  // sum over all tiles.
+  if (256 % E == 0) {
+    // E divides 256: read hist flat and coalesced; thread tid always meets
+    // expert tid % E, in tiles tid / E, tid / E + 256 / E, ...
+    const int P = 256 / E;
+    const int e = tid % E;
+    int b = 0, c = 0;
+    for (int t2 = tid / E; t2 < ntiles; t2 += P) {
+      const int h = hist[static_cast<int64_t>(t2) * E + e];
+      if (t2 < tile) b += h;
+      c += h;
+    }
+    s_part[0][tid] = b;
+    s_part[1][tid] = c;
+    __syncthreads();
+    if (tid < E) {
+      b = 0;
+      c = 0;
+      for (int j = 0; j < P; ++j) {
+        b += s_part[0][j * E + tid];
+        c += s_part[1][j * E + tid];
+      }
+      s_base[tid] = b;
+      s_cnt[tid] = c;
+    }
+  } else {
+    for (int e = tid; e < E; e += 256) {
+      int b = 0, c = 0;
+      for (int t2 = 0; t2 < ntiles; ++t2) {
+        const int h = hist[static_cast<int64_t>(t2) * E + e];
+        if (t2 < tile) b += h;
+        c += h;
+      }
+      s_base[e] = b;
+      s_cnt[e] = c;
+    }
+  }
+  for (int e = tid; e < E; e += 256) mask[e] = 0ull;
+  __syncthreads();
+  // kept rows n_e = min(count_e, C); thread tid sums experts 4 tid .. 4 tid + 3,
+  // then an exclusive prefix over the 256 partial sums gives the offsets.
+  int n_loc[4];
+  int part = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * tid + j;
+    n_loc[j] = (e < E) ? min(s_cnt[e], C) : 0;
+    part += n_loc[j];
+  }
+  s_part[0][tid] = part;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = (tid >= off) ? s_part[0][tid - off] : 0;
+    __syncthreads();
+    s_part[0][tid] += add;
+    __syncthreads();
+  }
+  int run = s_part[0][tid] - part;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * tid + j;
+    if (e < E) s_off[e] = run;
+    run += n_loc[j];
+  }
+  if (tid == 255) s_off[E] = run;  // the total: experts past E add nothing
+  __syncthreads();
+  if (tile == 0) {
+    for (int e = tid; e < E; e += 256) counts[e] = s_cnt[e];
+    for (int e = tid; e <= E; e += 256) offsets[e] = s_off[e];
+  }
+  for (int p = tid; p < np; p += 256) atomicOr(&mask[ids[t0 * k + p]], 1ull << (p / k));
+  __syncthreads();
+  for (int p = tid; p < np; p += 256) {
+    const int t = p / k;
+    const int e = ids[t0 * k + p];
+    const int rank = __popcll(mask[e] & ((1ull << t) - 1ull));
+    const int sl = s_base[e] + rank;
+    const int row = (sl < C) ? s_off[e] + sl : -1;
+    slot[t0 * k + p] = sl;
+    row_of[t0 * k + p] = row;
+    if (row >= 0) row_token[row] = static_cast<int32_t>(t0 + t);
+  }
+}
+
 // x_perm[r] = x[row_token[r]] for every kept row, VEC bytes per thread, rows
 // read from offsets[E] on the device.
 template <int VEC>
@@ -155,6 +263,22 @@ hipError_t launch_scan(const int32_t* hist, int ntiles, int E, int C, int32_t* b
                        int32_t* counts, int32_t* offsets, hipStream_t s) {
   scan_kernel<<<1, 1024, 0, s>>>(hist, ntiles, E, C, base, counts, offsets);
   return hipGetLastError();
+}
+
+bool fused_scan_fits(int ntiles, int E) {
+  return static_cast<int64_t>(ntiles) * E <= kFusedScanLimit;
+}
+
+hipError_t launch_permute_scan(const void* x, const int32_t* ids, const int32_t* hist, int64_t T,
+                               int k, int E, int C, int row_bytes, int32_t* counts,
+                               int32_t* offsets, int32_t* slot, int32_t* row_of,
+                               int32_t* row_token, void* x_perm, hipStream_t s) {
+  const int ntiles = static_cast<int>((T + kTileTokens - 1) / kTileTokens);
+  permute_scan_kernel<<<ntiles, 256, 0, s>>>(ids, hist, ntiles, T, k, E, C, counts, offsets, slot,
+                                             row_of, row_token);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || x_perm == nullptr) return err;
+  return launch_gather_rows(x, row_token, offsets, E, T * k, row_bytes, x_perm, s);
 }
 
 hipError_t launch_permute(const void* x, const int32_t* ids, const int32_t* base,

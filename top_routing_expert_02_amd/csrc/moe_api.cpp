@@ -124,7 +124,13 @@ int32_t dispatch_stage(const moe_config& c, const void* x, const int32_t* ids, b
                        int32_t* slot, int32_t* row_of, int32_t* row_token, void* x_perm,
                        hipStream_t s) {
   if (!hist_ready) MOE_HIP(launch_hist(ids, c.T, c.k, c.E, hist, s));
-  MOE_HIP(launch_scan(hist, static_cast<int>(ntiles_of(c.T)), c.E, c.capacity, base, counts, offsets, s));
+  const int nt = static_cast<int>(ntiles_of(c.T));
+  if (fused_scan_fits(nt, c.E)) {
+    MOE_HIP(launch_permute_scan(x, ids, hist, c.T, c.k, c.E, c.capacity, c.d * elem_size(c), counts,
+                                offsets, slot, row_of, row_token, x_perm, s));
+    return MOE_OK;
+  }
+  MOE_HIP(launch_scan(hist, nt, c.E, c.capacity, base, counts, offsets, s));
   MOE_HIP(launch_permute(x, ids, base, offsets, c.T, c.k, c.E, c.capacity, c.d * elem_size(c), slot,
                          row_of, row_token, x_perm, s));
   return MOE_OK;

@@ -68,6 +68,13 @@ hipError_t launch_permute(const void* x, const int32_t* ids, const int32_t* base
                           int row_bytes, int32_t* slot, int32_t* row_of, int32_t* row_token,
                           void* x_perm, hipStream_t s);
 
+// scan and permute in one launch; valid when fused_scan_fits(ntiles, E)
+bool fused_scan_fits(int ntiles, int E);
+hipError_t launch_permute_scan(const void* x, const int32_t* ids, const int32_t* hist, int64_t T,
+                               int k, int E, int C, int row_bytes, int32_t* counts,
+                               int32_t* offsets, int32_t* slot, int32_t* row_of,
+                               int32_t* row_token, void* x_perm, hipStream_t s);
+
 // x_perm[r] = x[row_token[r]] for r < offsets[E] (rows bounded by max_rows)
 hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int32_t* offsets,
                               int E, int64_t max_rows, int row_bytes, void* x_perm, hipStream_t s);
