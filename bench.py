@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=30.0,
                     help="upper bound on the oracle's CPU time for the baseline leg")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="after the timed steps, this many extra steps each preceded by a 1 GiB "
+                         "write that evicts L2 and the MALL (reported as 'cold', not as value)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run a plain device copy of this many MiB "
                          "three times (calibrates the HBM byte counters of a profiler run)")
@@ -174,7 +177,8 @@ def main():
     dev = "cuda"
     log(f"[bench] {w.name}: generating inputs")
     inp = synth.make_inputs(w, dev, seed=0)
-    C = moe.capacity(w.T, w.k, w.E, w.c)
+    # dropless: a token holds an expert at most once, so C = T never drops
+    C = w.T if w.dropless else moe.capacity(w.T, w.k, w.E, w.c)
     cfg = moe.config(w.T, w.d, w.d_ff, w.E, w.k, C, w.renormalize, w.dtype, w.act)
     R = moe.max_rows(cfg)
     ws = moe.alloc_workspace(cfg, dev)
@@ -231,6 +235,27 @@ def main():
                 "achieved": stages[dom]["TFLOP_s"], "peak": peak, "unit": "TFLOP/s",
                 "frac": stages[dom]["TFLOP_s"] / peak, "traffic": traffic}
 
+    cold = None
+    if args.cold_steps > 0:
+        # each step starts with nothing of the layer's inputs in L2 or the MALL
+        evict = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        t_cold = []
+        for i in range(args.cold_steps):
+            evict.fill_(i & 0xFF)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            t_cold.append(a.elapsed_time(b))
+        del evict
+        cold_ms = float(np.median(t_cold))
+        cold = {"ms_per_step_median": cold_ms, "ms_per_step_min": float(np.min(t_cold)),
+                "value": w.T / (cold_ms * 1e-3), "steps": args.cold_steps,
+                "note": "1 GiB written before each step; not part of value"}
+        log(f"[bench] cold: {cold_ms:.4f} ms/step (median of {args.cold_steps})")
+
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib)
     rows = int(offsets[-1])
@@ -238,9 +263,11 @@ def main():
            "steps": K, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
            "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "E": w.E, "k": w.k,
-                      "c": w.c, "C": C, "act": w.act, "rows": rows,
+                      "c": None if w.dropless else w.c, "C": C, "act": w.act, "rows": rows,
                       "dropped": int(np.maximum(counts - C, 0).sum()), "parallelism": "none"},
            "roofline": roofline, "stages": stages}
+    if cold is not None:
+        out["cold"] = cold
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(w, inp, C, args.cpu_budget_s)

@@ -36,6 +36,8 @@ def moe():
 
 
 def cap(w):
+    if w.dropless:
+        return w.T  # a token holds an expert at most once, so count_e <= T
     C = moe().capacity(w.T, w.k, w.E, w.c)
     assert C == mo.capacity(w.T, w.k, w.E, w.c)
     return C
@@ -68,6 +70,18 @@ def test_layer_parity_mini(name):
     say(f"[gpu] layer parity {name} T={w.T} d={w.d} d_ff={w.d_ff} E={w.E} k={w.k}")
     inp = synth.make_inputs(w, "cuda", seed=0)
     P.full_parity(w, inp, cap(w), report=say)
+
+
+@pytest.mark.parametrize("T", [1, 2, 17, 64, 65])
+@pytest.mark.parametrize("base", ["skewed_bf16", "mid_bf16"])
+def test_dropless_decode_sizes(base, T):
+    """Dropless (C = T) at decode batch sizes: every assignment is kept, the
+    hottest expert may take every token."""
+    w = WORKLOADS[base].scaled(name=f"dropless_{base}_T{T}", T=T, d=256, d_ff=512, dropless=True)
+    say(f"[gpu] dropless decode {w.name}")
+    inp = synth.make_inputs(w, "cuda", seed=1)
+    _, _, o, stats = P.full_parity(w, inp, cap(w), report=say)
+    assert stats["dropped"] == 0 and o["rows"] == T * w.k
 
 
 def test_layer_parity_uncapped_hot_expert():
@@ -249,7 +263,8 @@ def test_stages_separately(name):
 
 # ------------------------------------------------------------------ full sizes
 
-@pytest.mark.parametrize("name", ["small_bf16", "mid_bf16", "skewed_bf16", "large_e_bf16"])
+@pytest.mark.parametrize("name", ["small_bf16", "mid_bf16", "skewed_bf16", "large_e_bf16",
+                                  "skewed_dropless_bf16", "decode_bf16"])
 def test_full_size_workload(name):
     """Full-size workload in the launch configuration the benchmark times:
     routing and dispatch on every token, x_perm on every row, y on sampled
@@ -305,3 +320,5 @@ def test_full_size_workload(name):
     # fully dropped tokens output exact zeros
     if dropped_tok.size:
         assert torch.all(y[torch.from_numpy(dropped_tok).to(dev)] == 0)
+    if w.dropless:
+        assert o_disp["kept"].all() and o_disp["rows"] == w.T * w.k

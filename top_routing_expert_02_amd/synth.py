@@ -20,6 +20,12 @@ Workloads (all synthetic; no dataset or trained weights exist for them):
   large_e_bf16  T=4096,  d=4096, d_ff=2048,  E=256, k=8, c=1.25, bf16, tanh-GELU,
                 renormalised gates, router bias ~ N(0, 0.1), other biases zero
 
+Dropless variants (capacity C = T, so no assignment is ever dropped):
+
+  skewed_dropless_bf16  skewed_bf16's tensors with C = T: the hottest
+                expert takes most of the 8192 tokens
+  decode_bf16   mid_bf16's layer at decode size, T=64, C = T
+
 N(0, v) names the variance v. x ~ N(0, 1); W_r and W1 ~ N(0, 1/d); W2 ~ N(0, 1/d_ff).
 Values are drawn in fp32 and rounded to bf16 (round to nearest even) for the
 bf16 workloads; biases are always fp32.
@@ -57,6 +63,7 @@ class Workload:
     router_bias_var: float  # variance when router_bias == "normal"
     ffn_bias_var: float     # variance of b1 and b2 (0 means zero biases)
     seed_id: int
+    dropless: bool = False  # capacity C = T instead of ceil(c T k / E)
 
     def scaled(self, **changes) -> "Workload":
         """Same recipe at other sizes (used for parity tests the oracle can
@@ -82,6 +89,9 @@ WORKLOADS = {
     "large_e_bf16": Workload("large_e_bf16", "bf16", 4096, 4096, 2048, 256, 8, 1.25,
                              "gelu_tanh", True, "normal", 0.1, 0.0, 5),
 }
+WORKLOADS["skewed_dropless_bf16"] = WORKLOADS["skewed_bf16"].scaled(name="skewed_dropless_bf16",
+                                                                    dropless=True)
+WORKLOADS["decode_bf16"] = WORKLOADS["mid_bf16"].scaled(name="decode_bf16", T=64, dropless=True)
 
 
 def _seed(*ids) -> int:
