@@ -19,6 +19,8 @@ Sources, cited by short name:
                      而不是搬运参数？", cited by section heading.
   [Gate&Comm]        mianshidashi.cn, MiniMax interview answer on MoE gate
                      outputs and distributed communication, "深入解析" items 01-06.
+  [EP 001]           ai-master.cc, interview answer "moe-expert-parallelism-
+                     engineering-001", section 一 (load balance: capacity factor).
 
 Readings where the pages leave a step open (each one is also listed with its
 reason in the design notes):
@@ -41,6 +43,17 @@ reason in the design notes):
       Gimpel's published approximation; the pages do not define sigma). Its
       constants are "parity unpinned" by the pages: they are pinned only
       against an independent library implementation and the exact GELU.
+  R9  overflow re-routing ([MoE Principles §4.3], second option; [EP 001]
+      "overflow to the next-best expert"): an assignment that overflows moves
+      to the token's next candidate, the best-scoring expert the token has
+      not yet been offered; it is served with that expert's probability as
+      its weight (divided by the same top-k sum when renormalising).
+  R10 capacity is allocated candidate by candidate, in rounds: round 0
+      offers every top-k assignment and truncates each expert at C; round j
+      offers the assignments still unplaced to their next candidates, which
+      take what capacity round j-1 left. Inside a round, arrivals are served
+      in priority order: token order (t, then rank r) or, GShard-style, rank
+      order (every token's first choice before any second choice).
 """
 from __future__ import annotations
 
@@ -176,6 +189,113 @@ def dispatch(ids: np.ndarray, E: int, C: int) -> dict:
             "row_token": row_token.astype(np.int32), "rows": rows}
 
 
+def candidate_ids(s: np.ndarray, n: int) -> np.ndarray:
+    """Each token's n best experts in descending score order: the top-k list
+    followed by the next candidates an overflowing assignment may move to
+    [MoE Principles §4.3]; same decision rule as top-k (reading R1)."""
+    return topk_ids(s, n)
+
+
+def candidate_gates(p: np.ndarray, cand: np.ndarray, k: int, renormalize: bool) -> np.ndarray:
+    """Weight of every candidate column (reading R9): p_{t,c} divided by the
+    sum over the token's top-k when renormalising, else p_{t,c}. The first k
+    columns equal `gates`."""
+    chosen = np.take_along_axis(p, cand.astype(np.int64), axis=1)
+    if renormalize:
+        return chosen / chosen[:, :k].sum(axis=1, keepdims=True)
+    return chosen
+
+
+def dispatch_rerouted(cand: np.ndarray, k: int, E: int, C: int, priority: str = "token",
+                      rounds: int = 0) -> dict:
+    """Capacity assignment with a priority order and overflow re-routing,
+    readings R9 and R10, written as the sequential process it describes.
+
+    cand [T, n] holds each token's candidates (columns 0..k-1 = S_t). Round 0
+    offers assignment (t, r) to cand[t, r]. Before round j >= 1, each
+    still-unplaced assignment of token t, in rank order, takes the token's
+    next unused candidate column (columns k, k+1, ...; with none left the
+    assignment is dropped for good). In every round, arrivals at an expert
+    are served in priority order while its capacity lasts:
+      priority "token": (t, r) in token order, ranks inside a token;
+      priority "rank":  (r, t): all first choices, then all second choices...
+    An arrival's slot is its position in the expert's arrival order: the
+    expert's fill at the start of the round plus the arrivals before it in
+    this round; it is placed iff slot < C. Placed rows are laid out expert
+    by expert in slot order (round 0 arrivals first).
+
+    With rounds = 0 and priority "token" this is exactly `dispatch`.
+    Returns the fields of `dispatch` (slot = slot at the expert last tried)
+    plus served_col [T, k] (candidate column serving each assignment, -1 if
+    dropped) and served_ids [T, k] (its expert, -1 if dropped)."""
+    cand = np.asarray(cand, dtype=np.int64)
+    T, n = cand.shape
+    assert priority in ("token", "rank") and rounds >= 0 and n >= k
+    if priority == "token":
+        order = [(t, r) for t in range(T) for r in range(k)]
+    else:
+        order = [(t, r) for r in range(k) for t in range(T)]
+    col = [[r for r in range(k)] for _ in range(T)]   # column each assignment tries
+    next_col = [k] * T
+    served = [[-1] * k for _ in range(T)]
+    alive = [[True] * k for _ in range(T)]
+    slot = [[0] * k for _ in range(T)]
+    fill = [0] * E
+    counts = [0] * E
+    for rnd in range(rounds + 1):
+        if rnd > 0:
+            for t in range(T):
+                for r in range(k):
+                    if served[t][r] < 0 and alive[t][r]:
+                        if next_col[t] < n:
+                            col[t][r] = next_col[t]
+                            next_col[t] += 1
+                        else:
+                            alive[t][r] = False
+        arrived = list(fill)
+        for t, r in order:
+            if served[t][r] >= 0 or not alive[t][r]:
+                continue
+            e = int(cand[t, col[t][r]])
+            if rnd == 0:
+                counts[e] += 1
+            slot[t][r] = arrived[e]
+            arrived[e] += 1
+            if slot[t][r] < C:
+                served[t][r] = col[t][r]
+        fill = [min(a, C) for a in arrived]
+    offsets = [0]
+    for e in range(E):
+        offsets.append(offsets[-1] + fill[e])
+    rows = offsets[-1]
+    row_of = np.full((T, k), -1, dtype=np.int64)
+    served_ids = np.full((T, k), -1, dtype=np.int64)
+    row_token = np.full(rows, -1, dtype=np.int64)
+    for t in range(T):
+        for r in range(k):
+            if served[t][r] >= 0:
+                e = int(cand[t, served[t][r]])
+                served_ids[t, r] = e
+                row_of[t, r] = offsets[e] + slot[t][r]
+                row_token[row_of[t, r]] = t
+    served_col = np.array(served, dtype=np.int64).reshape(T, k)
+    return {"expert_counts": np.array(counts, dtype=np.int32),
+            "n": np.array(fill, dtype=np.int32),
+            "expert_offsets": np.array(offsets, dtype=np.int32),
+            "slot": np.array(slot, dtype=np.int32).reshape(T, k), "kept": served_col >= 0,
+            "row_of": row_of.astype(np.int32), "row_token": row_token.astype(np.int32),
+            "rows": rows, "served_col": served_col.astype(np.int32),
+            "served_ids": served_ids.astype(np.int32)}
+
+
+def served_gates(cand_gates: np.ndarray, served_col: np.ndarray) -> np.ndarray:
+    """Combine weight of each assignment: the weight of the candidate that
+    serves it (reading R9), 0 for a dropped one."""
+    col = np.maximum(served_col, 0).astype(np.int64)
+    g = np.take_along_axis(cand_gates, col, axis=1)
+    return np.where(served_col >= 0, g, 0.0)
+
+
 def permute(x: np.ndarray, row_token: np.ndarray) -> np.ndarray:
     """x_perm[r] = x[row_token[r]]: tokens gathered expert by expert
     [MoE Principles §5; Gate&Comm 02, 06]. Works on stored values (a copy)."""
@@ -219,20 +339,30 @@ def combine(Y_rows: np.ndarray, row_of: np.ndarray, g: np.ndarray) -> np.ndarray
 # ---------------------------------------------------------------- whole layer
 
 def layer_forward(x, W_r, b_r, W1, b1, W2, b2, *, k: int, C: int, renormalize: bool,
-                  act: str, ids=None) -> dict:
+                  act: str, ids=None, priority: str = "token", rounds: int = 0) -> dict:
     """The whole hot path on fp64 inputs  [MoE Principles §5 flowchart]:
     router -> probabilities -> top-k -> capacity assignment -> dispatch ->
     expert FFNs -> combine.
 
     W1 [E, d_ff, d], W2 [E, d, d_ff], b1 [E, d_ff], b2 [E, d]. When `ids` is
-    given, dispatch and everything after it use those expert ids instead of
-    the oracle's own choice (used when the GPU took the other side of a
-    near-tie)."""
+    given, dispatch and everything after it use those expert ids (with
+    re-routing: those candidate lists) instead of the oracle's own choice
+    (used when the GPU took the other side of a near-tie). `priority` and
+    `rounds` select the capacity rule of readings R9 and R10; the defaults
+    are the plain first-come, drop-on-overflow rule."""
     E = W_r.shape[0]
-    r = route(x, W_r, b_r, k, renormalize)
+    general = priority != "token" or rounds > 0
+    n_cand = min(E, k * (1 + rounds)) if rounds > 0 else k
+    r = route(x, W_r, b_r, n_cand, renormalize) if general else route(x, W_r, b_r, k, renormalize)
     use_ids = r["topk_ids"] if ids is None else np.asarray(ids, dtype=np.int32)
-    g = r["topk_gates"] if ids is None else gates(r["probs"], use_ids, renormalize)
-    dsp = dispatch(use_ids, E, C)
+    if general:
+        cg = candidate_gates(r["probs"], use_ids, k, renormalize)
+        dsp = dispatch_rerouted(use_ids, k, E, C, priority, rounds)
+        g = served_gates(cg, dsp["served_col"])
+        r["topk_gates"] = cg
+    else:
+        g = r["topk_gates"] if ids is None else gates(r["probs"], use_ids, renormalize)
+        dsp = dispatch(use_ids, E, C)
     rows = dsp["rows"]
     x_perm = permute(x, dsp["row_token"])
     h = np.zeros((rows, W1.shape[1]), dtype=np.float64)

@@ -530,3 +530,190 @@ def test_planted_softmax_sign_is_caught(monkeypatch):
     monkeypatch.setattr(mo, "softmax", lambda s: np.exp(-s) / np.exp(-s).sum(axis=1, keepdims=True))
     _expect_fail(check_gates)
     _expect_fail(check_dense_soft_mixture)
+
+
+# ------------------------------------------------------------------ re-routing and priority
+
+REROUTE_KEYS = ("expert_counts", "served_col", "served_ids", "slot", "expert_offsets", "row_of",
+                "row_token")
+
+
+def check_reroute_pages():
+    for c in golden("reroute_examples.json")["cases"]:
+        o = mo.dispatch_rerouted(np.array(c["cand"]), c["k"], c["E"], c["C"], c["priority"],
+                                 c["rounds"])
+        for key in REROUTE_KEYS:
+            assert o[key].tolist() == c[key], (c["name"], key, o[key].tolist())
+
+
+def test_reroute_pages():
+    check_reroute_pages()
+
+
+def random_candidates(r, T, E, n):
+    return (np.stack([r.permutation(E)[:n] for _ in range(T)]).astype(np.int32).reshape(T, n)
+            if T else np.zeros((0, n), np.int32))
+
+
+def counting_slots(cand, k, E, C, priority, rounds):
+    """The same rule as a count per round instead of a running simulation:
+    the slot of arrival (t, r) in round j is fill_j[e] plus the number of
+    arrivals at e before it in priority order in that round."""
+    T, n = cand.shape
+    pos = (lambda t, r: t * k + r) if priority == "token" else (lambda t, r: r * T + t)
+    col = np.tile(np.arange(k), (T, 1))
+    served = np.full((T, k), -1)
+    dead = np.zeros((T, k), bool)
+    slot = np.zeros((T, k), int)
+    fill = np.zeros(E, int)
+    used = np.full(T, k)
+    for rnd in range(rounds + 1):
+        if rnd:
+            for t in range(T):
+                for r in range(k):
+                    if served[t, r] < 0 and not dead[t, r]:
+                        if used[t] < n:
+                            col[t, r] = used[t]
+                            used[t] += 1
+                        else:
+                            dead[t, r] = True
+        live = [(t, r) for t in range(T) for r in range(k) if served[t, r] < 0 and not dead[t, r]]
+        exp = {(t, r): int(cand[t, col[t, r]]) for t, r in live}
+        arrivals = np.zeros(E, int)
+        for t, r in live:
+            e = exp[(t, r)]
+            before = sum(1 for (u, q) in live if exp[(u, q)] == e and pos(u, q) < pos(t, r))
+            slot[t, r] = fill[e] + before
+            arrivals[e] += 1
+        for t, r in live:
+            if slot[t, r] < C:
+                served[t, r] = col[t, r]
+        fill = np.minimum(fill + arrivals, C)
+    return served, slot, fill
+
+
+def check_reroute_properties(trials=150):
+    r = rng(21)
+    for trial in range(trials):
+        E = int(r.integers(1, 7))
+        k = int(r.integers(1, E + 1))
+        T = int(r.integers(0, 24))
+        C = int(r.integers(1, max(2, T)))
+        rounds = int(r.integers(0, 4))
+        n = min(E, k * (1 + rounds))
+        cand = random_candidates(r, T, E, n)
+        for priority in ("token", "rank"):
+            o = mo.dispatch_rerouted(cand, k, E, C, priority, rounds)
+            served, slot, fill = counting_slots(cand, k, E, C, priority, rounds)
+            assert o["served_col"].tolist() == served.tolist()
+            assert o["slot"].tolist() == slot.tolist()
+            assert o["n"].tolist() == fill.tolist()
+            # capacity and layout
+            assert np.all(o["n"] <= C)
+            assert o["rows"] == int(o["kept"].sum()) == int(o["n"].sum())
+            assert o["expert_offsets"].tolist() == [0] + np.cumsum(o["n"]).tolist()
+            for t in range(T):
+                ids_t = [e for e in o["served_ids"][t] if e >= 0]
+                assert len(ids_t) == len(set(ids_t))          # an expert serves a token once
+                for q in range(k):
+                    row = o["row_of"][t, q]
+                    if row >= 0:
+                        e = o["served_ids"][t, q]
+                        assert o["row_token"][row] == t
+                        assert o["expert_offsets"][e] <= row < o["expert_offsets"][e + 1]
+                        assert row - o["expert_offsets"][e] == o["slot"][t, q]
+            # the first round's demand is the top-k count
+            assert o["expert_counts"].tolist() == np.bincount(cand[:, :k].ravel(),
+                                                              minlength=E).tolist()
+            if rounds == 0 and priority == "token":
+                d = mo.dispatch(cand[:, :k], E, C)
+                for key in ("expert_counts", "expert_offsets", "slot", "row_of", "row_token"):
+                    assert o[key].tolist() == d[key].tolist(), key
+            if rounds > 0:
+                # more rounds never undo a placement
+                prev = mo.dispatch_rerouted(cand, k, E, C, priority, rounds - 1)
+                assert np.all(o["kept"][prev["kept"]])
+        if k == 1:
+            a = mo.dispatch_rerouted(cand, 1, E, C, "token", rounds)
+            b = mo.dispatch_rerouted(cand, 1, E, C, "rank", rounds)
+            for key in REROUTE_KEYS:
+                assert a[key].tolist() == b[key].tolist()
+
+
+def test_reroute_properties():
+    check_reroute_properties()
+
+
+def check_candidate_gates():
+    p = np.array([[0.5, 0.2, 0.2, 0.1], [0.1, 0.3, 0.4, 0.2]])
+    cand = mo.candidate_ids(np.log(p), 3)
+    assert cand.tolist() == [[0, 1, 2], [2, 1, 3]]     # equal scores: lower index first
+    g = mo.candidate_gates(p, cand, 2, True)
+    np.testing.assert_allclose(g, [[0.5 / 0.7, 0.2 / 0.7, 0.2 / 0.7],
+                                   [0.4 / 0.7, 0.3 / 0.7, 0.2 / 0.7]], rtol=1e-15)
+    np.testing.assert_allclose(mo.candidate_gates(p, cand, 2, False),
+                               [[0.5, 0.2, 0.2], [0.4, 0.3, 0.2]], rtol=1e-15)
+    # the first k columns are the top-k gates
+    np.testing.assert_allclose(g[:, :2], mo.gates(p, cand[:, :2], True), rtol=1e-15)
+    sg = mo.served_gates(g, np.array([[0, -1], [2, 1]]))
+    np.testing.assert_allclose(sg, [[0.5 / 0.7, 0.0], [0.2 / 0.7, 0.3 / 0.7]], rtol=1e-15)
+
+
+def test_candidate_gates():
+    check_candidate_gates()
+
+
+def test_rerouted_layer_reduces_to_plain_layer():
+    """rounds = 0 with token priority is the plain layer; with rounds > 0 an
+    assignment served by its next candidate adds that expert's FFN with the
+    candidate's weight (checked token by token)."""
+    r = rng(31)
+    T, d, d_ff, E, k, C = 40, 6, 10, 4, 2, 12
+    x = r.standard_normal((T, d))
+    W_r = r.standard_normal((E, d))
+    b_r = np.array([2.0, 0.0, 0.0, 0.0])      # expert 0 is hot: it overflows
+    W1 = r.standard_normal((E, d_ff, d))
+    b1 = r.standard_normal((E, d_ff))
+    W2 = r.standard_normal((E, d, d_ff))
+    b2 = r.standard_normal((E, d))
+    kw = dict(k=k, C=C, renormalize=True, act="relu")
+    plain = mo.layer_forward(x, W_r, b_r, W1, b1, W2, b2, **kw)
+    same = mo.layer_forward(x, W_r, b_r, W1, b1, W2, b2, priority="token", rounds=0, **kw)
+    np.testing.assert_array_equal(plain["y"], same["y"])
+    o = mo.layer_forward(x, W_r, b_r, W1, b1, W2, b2, rounds=1, **kw)
+    assert o["kept"].sum() > plain["kept"].sum()
+    p = mo.softmax(mo.router_logits(x, W_r, b_r))
+    for t in range(T):
+        top = np.sort(p[t])[::-1][:k].sum()
+        want = np.zeros(d)
+        for q in range(k):
+            e = o["served_ids"][t, q]
+            if e >= 0:
+                _, Y = mo.expert_ffn(x[t:t + 1], W1[e], b1[e], W2[e], b2[e], "relu")
+                want += p[t, e] / top * Y[0]
+        np.testing.assert_allclose(o["y"][t], want, rtol=1e-12, atol=1e-12)
+
+
+def test_planted_reroute_same_column_is_caught(monkeypatch):
+    """A re-route that offers the same expert again must fail the pins."""
+    orig = mo.dispatch_rerouted
+
+    def no_advance(cand, k, E, C, priority="token", rounds=0):
+        return orig(np.concatenate([cand[:, :k]] * (cand.shape[1] // k + 1), axis=1)[:, :cand.shape[1]],
+                    k, E, C, priority, rounds)
+    monkeypatch.setattr(mo, "dispatch_rerouted", no_advance)
+    _expect_fail(check_reroute_pages)
+
+
+def test_planted_priority_ignored_is_caught(monkeypatch):
+    orig = mo.dispatch_rerouted
+    monkeypatch.setattr(mo, "dispatch_rerouted",
+                        lambda cand, k, E, C, priority="token", rounds=0: orig(cand, k, E, C, "token", rounds))
+    _expect_fail(check_reroute_pages)
+
+
+def test_planted_candidate_gate_denominator_is_caught(monkeypatch):
+    orig = mo.candidate_gates
+    monkeypatch.setattr(mo, "candidate_gates",
+                        lambda p, cand, k, renormalize: orig(p, cand, cand.shape[1], renormalize))
+    _expect_fail(check_candidate_gates)
