@@ -100,12 +100,18 @@ def stage_bytes_flops(w, C, counts, offsets):
     kept_e = np.minimum(counts, C)
     T, d, d_ff, E, k = w.T, w.d, w.d_ff, w.E, w.k
     touched = int((kept_e > 0).sum())
+    if w.priority != "token" or w.reroute > 0:
+        n = min(E, k * (1 + w.reroute)) if w.reroute > 0 else k
+        # candidate ids and weights read; slot, row_of, serving id, weight written
+        disp = {"bytes": T * n * 8 + T * k * 16 + rows * 4, "flops": 0}
+    else:
+        # ids read, slot/row_of written, row_token written (the layer path gathers
+        # token rows inside the first GEMM: no permuted copy of x is written)
+        disp = {"bytes": T * k * 12 + rows * 4, "flops": 0}
     return {
         # x read once, W_r once, ids+gates written
         "route": {"bytes": T * d * b + E * d * b + T * k * 8, "flops": 2 * T * d * E},
-        # ids read, slot/row_of written, row_token written (the layer path gathers
-        # token rows inside the first GEMM: no permuted copy of x is written)
-        "dispatch": {"bytes": T * k * 12 + rows * 4, "flops": 0},
+        "dispatch": disp,
         # touched experts' W1 read, x_perm read, h written
         "gemm1": {"bytes": touched * d_ff * d * b + rows * d * b + rows * d_ff * b,
                   "flops": 2 * rows * d * d_ff},
@@ -179,7 +185,8 @@ def main():
     inp = synth.make_inputs(w, dev, seed=0)
     # dropless: a token holds an expert at most once, so C = T never drops
     C = w.T if w.dropless else moe.capacity(w.T, w.k, w.E, w.c)
-    cfg = moe.config(w.T, w.d, w.d_ff, w.E, w.k, C, w.renormalize, w.dtype, w.act)
+    cfg = moe.config(w.T, w.d, w.d_ff, w.E, w.k, C, w.renormalize, w.dtype, w.act,
+                     priority=w.priority, reroute=w.reroute)
     R = moe.max_rows(cfg)
     ws = moe.alloc_workspace(cfg, dev)
     y = torch.empty((w.T, w.d), dtype=w.torch_dtype, device=dev)
@@ -264,7 +271,8 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
            "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "E": w.E, "k": w.k,
                       "c": None if w.dropless else w.c, "C": C, "act": w.act, "rows": rows,
-                      "dropped": int(np.maximum(counts - C, 0).sum()), "parallelism": "none"},
+                      "dropped": w.T * w.k - rows, "priority": w.priority, "reroute_rounds": w.reroute,
+                      "parallelism": "none"},
            "roofline": roofline, "stages": stages}
     if cold is not None:
         out["cold"] = cold

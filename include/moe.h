@@ -27,7 +27,10 @@
  *  - Capacity is granted first-come in token order (a token's own k choices
  *    go to distinct experts, so they never compete). A dropped assignment
  *    contributes nothing; gates are not renormalised after drops; a token
- *    whose every assignment was dropped gets y_t = 0.
+ *    whose every assignment was dropped gets y_t = 0. Two optional rules
+ *    change this (cfg->priority, cfg->reroute; see moe_config):
+ *    rank-major priority, and moving an overflowing assignment to the
+ *    token's next candidate expert instead of dropping it.
  *  - Dispatch layout: rows are expert-major and, within an expert, in token
  *    order, packed from row 0 without padding. rows = sum_e min(count_e, C)
  *    is never read back to the host; buffers indexed by row are sized by
@@ -59,6 +62,8 @@ enum {
 enum { MOE_F32 = 0, MOE_BF16 = 1 };
 enum { MOE_ACT_RELU = 0, MOE_ACT_GELU_TANH = 1 };
 enum { MOE_MAX_EXPERTS = 1024, MOE_MAX_TOPK = 16 };
+/* Order in which arrivals at a full expert are served (moe_config.priority). */
+enum { MOE_PRIORITY_TOKEN = 0, MOE_PRIORITY_RANK = 1 };
 
 /* Stage boundaries for moe_layer_forward's optional events. */
 enum {
@@ -86,10 +91,30 @@ enum {
  *   dtype        MOE_F32 or MOE_BF16.
  *   act          sigma: MOE_ACT_RELU or MOE_ACT_GELU_TANH
  *                (0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3)))).
+ *   priority     MOE_PRIORITY_TOKEN: arrivals at an expert are served in
+ *                token order (t, then the token's rank r).
+ *                MOE_PRIORITY_RANK: in rank order (every token's first choice
+ *                before any token's second choice, then token order).
+ *   reroute      rounds of overflow re-routing R >= 0 ([MoE Principles] §4.3,
+ *                second option; ai-master.cc EP engineering answer 001, §一:
+ *                overflow goes to the next-best expert or is dropped).
+ *                0: an overflowing assignment is dropped. R > 0: capacity is
+ *                given out in rounds; round 0 offers the top-k assignments;
+ *                before round j every unplaced assignment of a token takes,
+ *                in rank order, the token's next candidate (the next expert
+ *                in descending score order that the token has not been
+ *                offered); arrivals are numbered from the expert's fill at
+ *                the round's start, in priority order, and placed while the
+ *                number is below C. An assignment served by a candidate is
+ *                weighted by that expert's probability (divided by the same
+ *                top-k sum when renormalising). The route then returns
+ *                n_cand = min(E, k (1 + R)) candidates per token (see
+ *                moe_candidates); n_cand must not exceed MOE_MAX_TOPK.
  */
 typedef struct moe_config {
   int64_t T;
   int32_t d, d_ff, E, k, capacity, renormalize, dtype, act;
+  int32_t priority, reroute;
 } moe_config;
 
 /*
@@ -100,6 +125,10 @@ typedef struct moe_config {
  *   [MoE Principles] §3.2), expert_counts [E] int32 (before capacity),
  *   expert_offsets [E+1] int32 (after capacity), slot [T,k] int32,
  *   row_of [T,k] int32 (-1 = dropped), row_token [max_rows] int32.
+ *   With priority or re-routing (see moe_dispatch_reroute): topk_ids and
+ *   topk_gates are [T,n_cand] candidate lists; served_ids [T,k] int32 and
+ *   combine_gates [T,k] fp32 are the serving expert (-1 = dropped) and the
+ *   combine weight (0 = dropped) of each assignment. Unused otherwise.
  */
 typedef struct moe_route_info {
   int32_t *topk_ids;
@@ -110,6 +139,8 @@ typedef struct moe_route_info {
   int32_t *slot;
   int32_t *row_of;
   int32_t *row_token;
+  int32_t *served_ids;
+  float *combine_gates;
 } moe_route_info;
 
 /*
@@ -120,6 +151,10 @@ typedef struct moe_route_info {
  * finite or c <= 0, or the result exceeds INT32_MAX. T == 0 gives C = 0.
  */
 int32_t moe_capacity(int64_t T, int32_t k, int32_t E, double c, int32_t *C_out);
+
+/* Candidates per token returned by moe_route: k, or min(E, k (1 + reroute))
+ * with re-routing (host only). */
+int32_t moe_candidates(const moe_config *cfg, int32_t *n_cand);
 
 /* max_rows = min(T*k, E*C): the size of every row-indexed buffer (host only). */
 int32_t moe_max_rows(const moe_config *cfg, int64_t *rows);
@@ -132,7 +167,10 @@ int32_t moe_workspace_size(const moe_config *cfg, size_t *bytes);
  * Route ([MoE Principles] §2.1-§2.2; page "MiniMax 面试: MoE gate 与分布式通信",
  * mianshidashi.cn, 深入解析 01: the gate emits scores, top-k ids and weights).
  *   x [T,d], W_r [E,d] (dtype); b_r [E] fp32 or NULL (zero bias).
- *   out topk_ids [T,k] int32, topk_gates [T,k] fp32 (required);
+ *   out topk_ids [T,k] int32, topk_gates [T,k] fp32 (required); with
+ *       re-routing [T,n_cand]: the top-k followed by the next candidates in
+ *       descending score order, every weight divided by the top-k sum when
+ *       renormalising;
  *   out prob_sum [E] fp32 or NULL; out logits [T,E] fp32 or NULL.
  *   ws: at least moe_workspace_size bytes, 256-byte aligned.
  */
@@ -151,12 +189,41 @@ int32_t moe_route(const moe_config *cfg, const void *x, const void *W_r, const f
  *   out row_of [T,k] int32: offsets[e] + slot if slot < C, else -1.
  *   out row_token [max_rows] int32: the token held by each row.
  *   out x_perm [max_rows,d] (dtype): x_perm[r] = x[row_token[r]] (bit copy).
+ * With cfg->priority == MOE_PRIORITY_RANK the slots follow rank order
+ * instead (slot = arrivals before it at that expert in rank order).
+ * cfg->reroute must be 0 (else MOE_ERR_INVALID_ARG): re-routing also changes
+ * the combine weights, which moe_dispatch_reroute returns.
  * Behaviour is undefined if an id is out of range or repeated within a row.
  */
 int32_t moe_dispatch(const moe_config *cfg, const void *x, const int32_t *topk_ids,
                      int32_t *expert_counts, int32_t *expert_offsets, int32_t *slot,
                      int32_t *row_of, int32_t *row_token, void *x_perm, void *ws,
                      size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Dispatch under any capacity rule of moe_config (priority, re-routing
+ * rounds; [MoE Principles] §4.3). For cfg->reroute == 0 and token priority
+ * it gives what moe_dispatch gives.
+ *   in  x [T,d] (dtype); cand_ids [T,n_cand] int32, each row n_cand distinct
+ *       ids in [0,E), best first; cand_gates [T,n_cand] fp32 (moe_route's
+ *       outputs).
+ *   out expert_counts [E] int32: top-k demand |{t : e in S_t}| (round 0).
+ *   out expert_offsets [E+1] int32: prefix sums of the rows each expert
+ *       finally holds (at most C).
+ *   out slot [T,k] int32: the assignment's arrival number at the expert it
+ *       was last offered to (its row within that expert when placed).
+ *   out row_of [T,k] int32 (-1 = dropped), row_token [max_rows] int32;
+ *       rows within an expert in slot order.
+ *   out served_ids [T,k] int32 or NULL: serving expert, -1 if dropped.
+ *   out combine_gates [T,k] fp32: cand_gates of the serving candidate, 0 if
+ *       dropped (the weights moe_combine takes).
+ *   out x_perm [max_rows,d] (dtype) or NULL: x_perm[r] = x[row_token[r]].
+ */
+int32_t moe_dispatch_reroute(const moe_config *cfg, const void *x, const int32_t *cand_ids,
+                             const float *cand_gates, int32_t *expert_counts,
+                             int32_t *expert_offsets, int32_t *slot, int32_t *row_of,
+                             int32_t *row_token, int32_t *served_ids, float *combine_gates,
+                             void *x_perm, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Expert FFN over the expert-contiguous rows as one grouped GEMM per layer
@@ -176,7 +243,8 @@ int32_t moe_expert_ffn(const moe_config *cfg, const void *x_perm, const int32_t 
  * token order and weight them"):
  *   y_t = sum_{j<k, row_of[t,j] >= 0} topk_gates[t,j] * y_perm[row_of[t,j]],
  *   summed over j = 0..k-1 in fp32 and rounded once to dtype.
- *   in y_perm [max_rows,d] fp32, row_of [T,k] int32, topk_gates [T,k] fp32;
+ *   in y_perm [max_rows,d] fp32, row_of [T,k] int32, topk_gates [T,k] fp32
+ *   (with re-routing: moe_dispatch_reroute's combine_gates);
  *   out y [T,d] (dtype).
  */
 int32_t moe_combine(const moe_config *cfg, const float *y_perm, const int32_t *row_of,

@@ -43,15 +43,30 @@ def moe_mod():
 
 def make_cfg(w, C):
     moe = moe_mod()
-    return moe.config(w.T, w.d, w.d_ff, w.E, w.k, C, w.renormalize, w.dtype, w.act)
+    return moe.config(w.T, w.d, w.d_ff, w.E, w.k, C, w.renormalize, w.dtype, w.act,
+                      priority=w.priority, reroute=w.reroute)
+
+
+def general_rule(w) -> bool:
+    return w.priority != "token" or w.reroute > 0
+
+
+def n_cand(w) -> int:
+    return min(w.E, w.k * (1 + w.reroute)) if w.reroute > 0 else w.k
 
 
 def info_tensors(w, R, device):
     i32 = dict(dtype=torch.int32, device=device)
     f32 = dict(dtype=torch.float32, device=device)
+    n = n_cand(w)
+    extra = {}
+    if general_rule(w):
+        extra = {"served_ids": torch.full((w.T, w.k), -7, **i32),
+                 "combine_gates": torch.full((w.T, w.k), -7.0, **f32)}
     return {
-        "topk_ids": torch.full((w.T, w.k), -7, **i32),
-        "topk_gates": torch.full((w.T, w.k), -7.0, **f32),
+        **extra,
+        "topk_ids": torch.full((w.T, n), -7, **i32),
+        "topk_gates": torch.full((w.T, n), -7.0, **f32),
         "prob_sum": torch.full((w.E,), -7.0, **f32),
         "expert_counts": torch.full((w.E,), -7, **i32),
         "expert_offsets": torch.full((w.E + 1,), -7, **i32),
@@ -85,8 +100,12 @@ def check_routing(o_route: dict, g_ids: np.ndarray) -> dict:
     return {"near_ties": int(o_route["near_tie"].sum()), "flips": int(mism.sum())}
 
 
-def check_gates(o_route: dict, g_ids, g_gates, renormalize):
-    ref = mo.gates(o_route["probs"], g_ids, renormalize)
+def check_gates(o_route: dict, g_ids, g_gates, renormalize, k=None):
+    """k: the top-k width when g_ids holds longer candidate lists."""
+    if k is None or k == g_ids.shape[1]:
+        ref = mo.gates(o_route["probs"], g_ids, renormalize)
+    else:
+        ref = mo.candidate_gates(o_route["probs"], g_ids, k, renormalize)
     err = np.abs(g_gates.astype(np.float64) - ref).max() if ref.size else 0.0
     assert err <= GATE_ATOL, f"gate max error {err:.3e}"
     return err
@@ -116,12 +135,17 @@ def full_parity(w, inp, C, report=None):
     """Whole-layer parity at sizes the oracle finishes in seconds."""
     y, g, cfg = gpu_layer(w, inp, C)
     h = host_inputs(inp, w.dtype)
-    o_route = mo.route(h["x"], h["W_r"], h["b_r"], w.k, w.renormalize)
+    o_route = mo.route(h["x"], h["W_r"], h["b_r"], n_cand(w), w.renormalize)
     stats = check_routing(o_route, g["topk_ids"])
-    check_gates(o_route, g["topk_ids"], g["topk_gates"], w.renormalize)
+    check_gates(o_route, g["topk_ids"], g["topk_gates"], w.renormalize, k=w.k)
     o = mo.layer_forward(h["x"], h["W_r"], h["b_r"], h["W1"], h["b1"], h["W2"], h["b2"],
-                         k=w.k, C=C, renormalize=w.renormalize, act=w.act, ids=g["topk_ids"])
+                         k=w.k, C=C, renormalize=w.renormalize, act=w.act, ids=g["topk_ids"],
+                         priority=w.priority, rounds=w.reroute)
     check_dispatch(g, o)
+    if general_rule(w):
+        np.testing.assert_array_equal(g["served_ids"], o["served_ids"], err_msg="served_ids")
+        err = float(np.abs(g["combine_gates"].astype(np.float64) - o["used_gates"]).max())
+        assert err <= GATE_ATOL, f"combine gate max error {err:.3e}"
     np.testing.assert_allclose(g["prob_sum"], o["prob_sum"], rtol=1e-5, atol=1e-4)
     stats.update(compare_outputs(host64(y, w.dtype), o["y"], w.dtype))
     stats["rows"] = o["rows"]

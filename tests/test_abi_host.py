@@ -121,6 +121,31 @@ def test_entry_points_reject_without_launching(m):
     assert L.moe_combine(ctypes.byref(empty), None, None, None, None, None) == 0
 
 
+def test_candidates_and_rule_validation(m):
+    """Candidate-list width for re-routing, and the checks of the two rule
+    fields (priority, reroute rounds)."""
+    assert m.candidates(good_cfg(m)) == 2
+    assert m.candidates(good_cfg(m, reroute=1)) == 4
+    assert m.candidates(good_cfg(m, reroute=3)) == 8           # min(E, k (1 + R))
+    assert m.candidates(good_cfg(m, reroute=9)) == 8
+    assert m.candidates(good_cfg(m, E=64, k=4, reroute=3)) == 16
+    n = ctypes.c_size_t(0)
+    L = m.lib()
+    for kw, status in [(dict(priority=2), -1), (dict(reroute=-1), -1), (dict(reroute=17), -1),
+                       (dict(E=64, k=4, reroute=4), -2), (dict(priority="rank", reroute=2), 0)]:
+        cfg = good_cfg(m, **kw)
+        assert L.moe_workspace_size(ctypes.byref(cfg), ctypes.byref(n)) == status, kw
+    # the plain dispatch entry point refuses re-routing (it returns no weights)
+    cfg = good_cfg(m, reroute=1)
+    fake = ctypes.c_void_p(0x100000)
+    ws = m.workspace_size(cfg)
+    assert L.moe_dispatch(ctypes.byref(cfg), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                          ws, None) == -1
+    # moe_dispatch_reroute: combine weights are required
+    assert L.moe_dispatch_reroute(ctypes.byref(cfg), fake, fake, fake, fake, fake, fake, fake, fake,
+                                  None, None, None, fake, ws, None) == -1
+
+
 def test_status_strings(m):
     L = m.lib()
     for s in (0, -1, -2, -3, -4, 99):

@@ -84,6 +84,100 @@ def test_dropless_decode_sizes(base, T):
     assert stats["dropped"] == 0 and o["rows"] == T * w.k
 
 
+# Priority order and overflow re-routing (the general capacity rule), on the
+# mini workloads: drops are frequent in the skewed and capped ones.
+REROUTE = {
+    "skewed_rank": MINI["skewed_bf16_mini"].scaled(name="skewed_rank", priority="rank"),
+    "skewed_reroute1": MINI["skewed_bf16_mini"].scaled(name="skewed_reroute1", reroute=1),
+    "skewed_rank_reroute2": MINI["skewed_bf16_mini"].scaled(name="skewed_rank_reroute2",
+                                                            priority="rank", reroute=2),
+    "skewed_reroute3": MINI["skewed_bf16_mini"].scaled(name="skewed_reroute3", reroute=3),
+    "small_capped_rank": MINI["small_bf16_mini"].scaled(name="small_capped_rank", c=0.8,
+                                                        priority="rank"),
+    "small_capped_reroute2": MINI["small_bf16_mini"].scaled(name="small_capped_reroute2", c=0.8,
+                                                            reroute=2),
+    "large_e_reroute1": MINI["large_e_bf16_mini"].scaled(name="large_e_reroute1", reroute=1),
+    "tiny_f32_reroute1": MINI["tiny_f32"].scaled(name="tiny_f32_reroute1", reroute=1),
+    "f32_mid_rank_reroute1": MINI["f32_mid"].scaled(name="f32_mid_rank_reroute1", c=0.7,
+                                                    priority="rank", reroute=1),
+    "e12_rank_reroute4": MINI["e12_bf16"].scaled(name="e12_rank_reroute4", priority="rank",
+                                                 reroute=4),
+}
+
+
+@pytest.mark.parametrize("name", list(REROUTE))
+def test_layer_parity_reroute(name):
+    w = REROUTE[name]
+    say(f"[gpu] reroute parity {name} priority={w.priority} rounds={w.reroute}")
+    inp = synth.make_inputs(w, "cuda", seed=0)
+    P.full_parity(w, inp, cap(w), report=say)
+
+
+def test_reroute_golden_on_gpu():
+    """The hand-worked re-routing and priority examples on the page's routing,
+    through moe_dispatch_reroute with the candidate lists given."""
+    import json
+    import os
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                        "reroute_examples.json")))["cases"]
+    m = moe()
+    dev = "cuda"
+    for c in cases:
+        cand = torch.tensor(c["cand"], dtype=torch.int32, device=dev)
+        T, n = cand.shape
+        k, E = c["k"], c["E"]
+        cg = (torch.arange(T * n, dtype=torch.float32, device=dev).reshape(T, n) + 1) / 64
+        cfg = m.config(T, 64, 64, E, k, c["C"], True, "f32", "relu", priority=c["priority"],
+                       reroute=c["rounds"])
+        assert m.candidates(cfg) == n
+        i32 = dict(dtype=torch.int32, device=dev)
+        counts = torch.full((E,), -7, **i32)
+        offs = torch.full((E + 1,), -7, **i32)
+        slot = torch.full((T, k), -7, **i32)
+        row_of = torch.full((T, k), -7, **i32)
+        row_token = torch.full((m.max_rows(cfg),), -7, **i32)
+        served = torch.full((T, k), -7, **i32)
+        gates = torch.full((T, k), -7.0, dtype=torch.float32, device=dev)
+        m.dispatch_reroute(cfg, None, cand, cg, counts, offs, slot, row_of, row_token, served, gates)
+        torch.cuda.synchronize()
+        rows = c["expert_offsets"][-1]
+        assert counts.tolist() == c["expert_counts"], c["name"]
+        assert offs.tolist() == c["expert_offsets"], c["name"]
+        assert slot.tolist() == c["slot"], c["name"]
+        assert row_of.tolist() == c["row_of"], c["name"]
+        assert row_token[:rows].tolist() == c["row_token"], c["name"]
+        assert served.tolist() == c["served_ids"], c["name"]
+        col = torch.tensor(c["served_col"], dtype=torch.int64, device=dev)
+        want = torch.where(col >= 0, torch.gather(cg, 1, col.clamp(min=0)), torch.zeros_like(gates))
+        assert torch.equal(gates, want), c["name"]
+
+
+def test_dispatch_entry_point_rank_priority():
+    """moe_dispatch under rank-major priority equals the oracle's rule."""
+    w = MINI["skewed_bf16_mini"].scaled(name="dispatch_rank", priority="rank")
+    inp = synth.make_inputs(w, "cuda", seed=3)
+    C = cap(w)
+    m = moe()
+    cfg = P.make_cfg(w, C)
+    dev = "cuda"
+    h = P.host_inputs(inp, w.dtype)
+    ids = torch.from_numpy(mo.route(h["x"], h["W_r"], h["b_r"], w.k, w.renormalize)["topk_ids"]).to(dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    R = m.max_rows(cfg)
+    out = {"expert_counts": torch.empty(w.E, **i32), "expert_offsets": torch.empty(w.E + 1, **i32),
+           "slot": torch.empty((w.T, w.k), **i32), "row_of": torch.empty((w.T, w.k), **i32),
+           "row_token": torch.full((R,), -1, **i32)}
+    x_perm = torch.empty((R, w.d), dtype=w.torch_dtype, device=dev)
+    m.dispatch(cfg, inp["x"], ids, out["expert_counts"], out["expert_offsets"], out["slot"],
+               out["row_of"], out["row_token"], x_perm)
+    torch.cuda.synchronize()
+    o = mo.dispatch_rerouted(ids.cpu().numpy(), w.k, w.E, C, "rank", 0)
+    P.check_dispatch({k: v.cpu().numpy() for k, v in out.items()}, o)
+    rows = o["rows"]
+    np.testing.assert_array_equal(synth.to_numpy_bits(x_perm[:rows]),
+                                  synth.to_numpy_bits(inp["x"])[o["row_token"]])
+
+
 def test_layer_parity_uncapped_hot_expert():
     """All tokens prefer one expert; with C >= T nothing drops and that
     expert's group spans several 256-row tiles."""
@@ -264,7 +358,7 @@ def test_stages_separately(name):
 # ------------------------------------------------------------------ full sizes
 
 @pytest.mark.parametrize("name", ["small_bf16", "mid_bf16", "skewed_bf16", "large_e_bf16",
-                                  "skewed_dropless_bf16", "decode_bf16"])
+                                  "skewed_dropless_bf16", "decode_bf16", "skewed_reroute_bf16"])
 def test_full_size_workload(name):
     """Full-size workload in the launch configuration the benchmark times:
     routing and dispatch on every token, x_perm on every row, y on sampled
@@ -278,11 +372,21 @@ def test_full_size_workload(name):
     say(f"[gpu] full size {name}: layer forward (C={C})")
     y, g, _ = P.gpu_layer(w, inp, C)
     x64 = P.host64(inp["x"], w.dtype)
-    o_route = mo.route(x64, P.host64(inp["W_r"], w.dtype), P.host64(inp["b_r"], "f32"), w.k,
-                       w.renormalize)
+    o_route = mo.route(x64, P.host64(inp["W_r"], w.dtype), P.host64(inp["b_r"], "f32"),
+                       P.n_cand(w), w.renormalize)
     stats = P.check_routing(o_route, g["topk_ids"])
-    P.check_gates(o_route, g["topk_ids"], g["topk_gates"], w.renormalize)
-    o_disp = mo.dispatch(g["topk_ids"], w.E, C)
+    P.check_gates(o_route, g["topk_ids"], g["topk_gates"], w.renormalize, k=w.k)
+    general = P.general_rule(w)
+    if general:
+        o_disp = mo.dispatch_rerouted(g["topk_ids"], w.k, w.E, C, w.priority, w.reroute)
+        np.testing.assert_array_equal(g["served_ids"], o_disp["served_ids"])
+        served = o_disp["served_ids"]
+        gates_ref = mo.served_gates(mo.candidate_gates(o_route["probs"], g["topk_ids"], w.k,
+                                                       w.renormalize), o_disp["served_col"])
+    else:
+        o_disp = mo.dispatch(g["topk_ids"], w.E, C)
+        served = g["topk_ids"]
+        gates_ref = mo.gates(o_route["probs"], g["topk_ids"], w.renormalize)
     P.check_dispatch(g, o_disp)
     # x_perm of the same call, through the dispatch entry point
     R = m.max_rows(cfg)
@@ -292,8 +396,15 @@ def test_full_size_workload(name):
          if k in ("expert_counts", "expert_offsets", "slot", "row_of")}
     row_token = torch.full((R,), -1, dtype=torch.int32, device=dev)
     x_perm = torch.empty((R, w.d), dtype=w.torch_dtype, device=dev)
-    m.dispatch(cfg, inp["x"], torch.from_numpy(g["topk_ids"]).to(dev), t["expert_counts"],
-               t["expert_offsets"], t["slot"], t["row_of"], row_token, x_perm, ws=ws)
+    if general:
+        m.dispatch_reroute(cfg, inp["x"], torch.from_numpy(g["topk_ids"]).to(dev),
+                           torch.from_numpy(g["topk_gates"]).to(dev), t["expert_counts"],
+                           t["expert_offsets"], t["slot"], t["row_of"], row_token,
+                           torch.empty((w.T, w.k), dtype=torch.int32, device=dev),
+                           torch.empty((w.T, w.k), dtype=torch.float32, device=dev), x_perm, ws=ws)
+    else:
+        m.dispatch(cfg, inp["x"], torch.from_numpy(g["topk_ids"]).to(dev), t["expert_counts"],
+                   t["expert_offsets"], t["slot"], t["row_of"], row_token, x_perm, ws=ws)
     torch.cuda.synchronize()
     rows = o_disp["rows"]
     xb = synth.to_numpy_bits(inp["x"])
@@ -305,14 +416,13 @@ def test_full_size_workload(name):
     part_tok = np.flatnonzero(~o_disp["kept"].all(axis=1) & o_disp["kept"].any(axis=1))
     tokens = sorted(set(rng.choice(w.T, size=24, replace=False).tolist()
                         + dropped_tok[:4].tolist() + part_tok[:4].tolist() + [0, w.T - 1]))
-    gates_ref = mo.gates(o_route["probs"], g["topk_ids"], w.renormalize)
 
     def expert_weights(e):
         return (P.host64(inp["W1"][e], w.dtype), P.host64(inp["b1"][e], "f32"),
                 P.host64(inp["W2"][e], w.dtype), P.host64(inp["b2"][e], "f32"))
 
     say(f"[gpu] full size {name}: oracle on {len(tokens)} sampled tokens")
-    y_ref = mo.sampled_outputs(tokens, x64, g["topk_ids"], o_disp["row_of"], gates_ref,
+    y_ref = mo.sampled_outputs(tokens, x64, served, o_disp["row_of"], gates_ref,
                                expert_weights, w.act)
     stats.update(P.compare_outputs(P.host64(y[tokens], w.dtype), y_ref, w.dtype))
     stats.update(rows=rows, dropped=int((~o_disp["kept"]).sum()), C=C)

@@ -28,6 +28,17 @@ int64_t max_rows_of(const moe_config& c) {
 
 int elem_size(const moe_config& c) { return c.dtype == MOE_BF16 ? 2 : 4; }
 
+// candidates per token the route keeps: the top-k, plus the next candidates
+// re-routing may need (each round uses at most k more per token)
+int n_cand_of(const moe_config& c) {
+  if (c.reroute <= 0) return c.k;
+  const int64_t n = static_cast<int64_t>(c.k) * (1 + static_cast<int64_t>(c.reroute));
+  return static_cast<int>(n < c.E ? n : c.E);
+}
+
+// priority order or re-routing: the general dispatch path
+bool general_rule(const moe_config& c) { return c.priority != MOE_PRIORITY_TOKEN || c.reroute > 0; }
+
 // The layer's first expert GEMM reads token rows straight from x through
 // row_token (32-bit byte offsets into x); only a larger x needs the permuted
 // copy materialised in the workspace.
@@ -44,6 +55,9 @@ int32_t check_cfg(const moe_config* c) {
   if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARG;
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (c->act != MOE_ACT_RELU && c->act != MOE_ACT_GELU_TANH) return MOE_ERR_INVALID_ARG;
+  if (c->priority != MOE_PRIORITY_TOKEN && c->priority != MOE_PRIORITY_RANK) return MOE_ERR_INVALID_ARG;
+  if (c->reroute < 0 || c->reroute > MOE_MAX_TOPK) return MOE_ERR_INVALID_ARG;
+  if (n_cand_of(*c) > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   // rows, slots and per-token indices are int32; tiles index a 32-bit grid
   if (c->T > (static_cast<int64_t>(INT32_MAX) / c->k)) return MOE_ERR_UNSUPPORTED;
   if (c->dtype == MOE_BF16 && (c->d % 64 != 0 || c->d_ff % 64 != 0)) return MOE_ERR_UNSUPPORTED;
@@ -52,7 +66,8 @@ int32_t check_cfg(const moe_config* c) {
 
 struct Layout {
   size_t logits, prob_part, hist, base, ids, gates, counts, offsets, prob_sum, slot, row_of,
-      row_token, x_perm, h, y_perm, total;
+      row_token, x_perm, h, y_perm, rr_col, rr_served, rr_next, rr_fill, rr_fill0, rr_hist,
+      rr_base, served_ids, cgates, total;
 };
 
 Layout layout_of(const moe_config& c) {
@@ -69,8 +84,8 @@ Layout layout_of(const moe_config& c) {
   L.prob_part = take(nt * E * 4);
   L.hist = take(nt * E * 4);
   L.base = take(nt * E * 4);
-  L.ids = take(T * k * 4);
-  L.gates = take(T * k * 4);
+  L.ids = take(T * n_cand_of(c) * 4);
+  L.gates = take(T * n_cand_of(c) * 4);
   L.counts = take(E * 4);
   L.offsets = take((E + 1) * 4);
   L.prob_sum = take(E * 4);
@@ -80,6 +95,19 @@ Layout layout_of(const moe_config& c) {
   L.x_perm = take(layer_gathers(c) ? 0 : R * c.d * es);
   L.h = take(R * c.d_ff * es);
   L.y_perm = take(R * c.d * 4);
+  // state of the general dispatch (priority order, re-routing rounds); small
+  // next to h, so every layout has it and moe_dispatch_reroute works for any
+  // config
+  const int64_t ntv = reroute_tiles(T, c.k);
+  L.rr_col = take(T * k * 4);
+  L.rr_served = take(T * k * 4);
+  L.rr_next = take(T * 4);
+  L.rr_fill = take(E * 4);
+  L.rr_fill0 = take(E * 4);
+  L.rr_hist = take(ntv * E * 4);
+  L.rr_base = take(ntv * E * 4);
+  L.served_ids = take(T * k * 4);
+  L.cgates = take(T * k * 4);
   L.total = off;
   return L;
 }
@@ -110,7 +138,7 @@ int32_t route_stage(const moe_config& c, const void* x, const void* Wr, const fl
   else
     MOE_HIP(launch_logits_f32(static_cast<const float*>(x), static_cast<const float*>(Wr), br, logits,
                               c.T, c.d, c.E, s));
-  MOE_HIP(launch_topk(logits, c.T, c.E, c.k, c.renormalize, ids, gates,
+  MOE_HIP(launch_topk(logits, c.T, c.E, c.k, n_cand_of(c), c.renormalize, ids, gates,
                       prob_sum != nullptr ? prob_part : nullptr, hist, s));
   if (prob_sum != nullptr)
     MOE_HIP(launch_prob_reduce(prob_part, static_cast<int>(ntiles_of(c.T)), c.E, prob_sum, s));
@@ -133,6 +161,24 @@ int32_t dispatch_stage(const moe_config& c, const void* x, const int32_t* ids, b
   MOE_HIP(launch_scan(hist, nt, c.E, c.capacity, base, counts, offsets, s));
   MOE_HIP(launch_permute(x, ids, base, offsets, c.T, c.k, c.E, c.capacity, c.d * elem_size(c), slot,
                          row_of, row_token, x_perm, s));
+  return MOE_OK;
+}
+
+// the general capacity rule (priority order, re-routing rounds); cand has
+// n_cand_of(c) columns; cand_gates, served_ids, cgates and x_perm may be null
+int32_t dispatch_general_stage(const moe_config& c, void* ws, const void* x, const int32_t* cand,
+                               const float* cand_gates, int32_t* counts, int32_t* offsets,
+                               int32_t* slot, int32_t* row_of, int32_t* row_token,
+                               int32_t* served_ids, float* cgates, void* x_perm, hipStream_t s) {
+  const Layout L = layout_of(c);
+  const ReroutePlan plan{at<int32_t>(ws, L.rr_col),  at<int32_t>(ws, L.rr_served),
+                         at<int32_t>(ws, L.rr_next), at<int32_t>(ws, L.rr_fill),
+                         at<int32_t>(ws, L.rr_fill0), at<int32_t>(ws, L.rr_hist),
+                         at<int32_t>(ws, L.rr_base)};
+  MOE_HIP(launch_dispatch_reroute(x, cand, cand_gates, c.T, c.k, n_cand_of(c), c.E, c.capacity,
+                                  c.priority == MOE_PRIORITY_RANK, c.reroute,
+                                  c.d * elem_size(c), plan, counts, offsets, slot, row_of,
+                                  row_token, served_ids, cgates, x_perm, s));
   return MOE_OK;
 }
 
@@ -202,6 +248,13 @@ int32_t moe_capacity(int64_t T, int32_t k, int32_t E, double c, int32_t* C_out) 
   return MOE_OK;
 }
 
+int32_t moe_candidates(const moe_config* cfg, int32_t* n_cand) {
+  MOE_TRY(check_cfg(cfg));
+  if (n_cand == nullptr) return MOE_ERR_INVALID_ARG;
+  *n_cand = n_cand_of(*cfg);
+  return MOE_OK;
+}
+
 int32_t moe_max_rows(const moe_config* cfg, int64_t* rows) {
   MOE_TRY(check_cfg(cfg));
   if (rows == nullptr) return MOE_ERR_INVALID_ARG;
@@ -249,10 +302,37 @@ int32_t moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_i
       !aligned(expert_counts, 4) || !aligned(expert_offsets, 4) || !aligned(slot, 4) ||
       !aligned(row_of, 4) || !aligned(row_token, 4))
     return MOE_ERR_INVALID_ARG;
+  if (c.reroute != 0) return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_ws(c, ws, ws_bytes));
   const Layout L = layout_of(c);
+  if (general_rule(c))
+    return dispatch_general_stage(c, ws, x, topk_ids, nullptr, expert_counts, expert_offsets, slot,
+                                  row_of, row_token, nullptr, nullptr, x_perm, stream);
   return dispatch_stage(c, x, topk_ids, false, at<int32_t>(ws, L.hist), at<int32_t>(ws, L.base),
                         expert_counts, expert_offsets, slot, row_of, row_token, x_perm, stream);
+}
+
+int32_t moe_dispatch_reroute(const moe_config* cfg, const void* x, const int32_t* cand_ids,
+                             const float* cand_gates, int32_t* expert_counts,
+                             int32_t* expert_offsets, int32_t* slot, int32_t* row_of,
+                             int32_t* row_token, int32_t* served_ids, float* combine_gates,
+                             void* x_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_config& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  if (cand_ids == nullptr || cand_gates == nullptr || expert_counts == nullptr ||
+      expert_offsets == nullptr || slot == nullptr || row_of == nullptr || row_token == nullptr ||
+      combine_gates == nullptr || (x_perm != nullptr && x == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(x_perm, 16) || !aligned(cand_ids, 4) || !aligned(cand_gates, 4) ||
+      !aligned(expert_counts, 4) || !aligned(expert_offsets, 4) || !aligned(slot, 4) ||
+      !aligned(row_of, 4) || !aligned(row_token, 4) || !aligned(served_ids, 4) ||
+      !aligned(combine_gates, 4))
+    return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_ws(c, ws, ws_bytes));
+  return dispatch_general_stage(c, ws, x, cand_ids, cand_gates, expert_counts, expert_offsets,
+                                slot, row_of, row_token, served_ids, combine_gates, x_perm,
+                                stream);
 }
 
 int32_t moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
@@ -300,7 +380,8 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* x, const void* W_r,
   if (info != nullptr) in = *info;
   if (!aligned(in.topk_ids, 4) || !aligned(in.topk_gates, 4) || !aligned(in.prob_sum, 4) ||
       !aligned(in.expert_counts, 4) || !aligned(in.expert_offsets, 4) || !aligned(in.slot, 4) ||
-      !aligned(in.row_of, 4) || !aligned(in.row_token, 4))
+      !aligned(in.row_of, 4) || !aligned(in.row_token, 4) || !aligned(in.served_ids, 4) ||
+      !aligned(in.combine_gates, 4))
     return MOE_ERR_INVALID_ARG;
   if (stage_events != nullptr)
     for (int i = 0; i <= MOE_NUM_STAGES; ++i)
@@ -320,6 +401,9 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* x, const void* W_r,
   void* h = at<char>(ws, L.h);
   float* y_perm = at<float>(ws, L.y_perm);
   int32_t* hist = at<int32_t>(ws, L.hist);
+  const bool gen = general_rule(c);
+  float* cgates = gates;  // combine weights
+  if (gen) cgates = in.combine_gates != nullptr ? in.combine_gates : at<float>(ws, L.cgates);
 
   auto mark = [&](int i) -> int32_t {
     if (stage_events != nullptr && hipEventRecord(stage_events[i], stream) != hipSuccess)
@@ -328,17 +412,21 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* x, const void* W_r,
   };
   MOE_TRY(mark(0));
   MOE_TRY(route_stage(c, x, W_r, b_r, ids, gates, in.prob_sum, at<float>(ws, L.logits),
-                      at<float>(ws, L.prob_part), hist, stream));
+                      at<float>(ws, L.prob_part), gen ? nullptr : hist, stream));
   MOE_TRY(mark(1));
-  MOE_TRY(dispatch_stage(c, x, ids, true, hist, at<int32_t>(ws, L.base), counts, offsets, slot,
-                         row_of, row_token, x_perm, stream));
+  if (gen)
+    MOE_TRY(dispatch_general_stage(c, ws, x, ids, gates, counts, offsets, slot, row_of, row_token,
+                                   in.served_ids, cgates, x_perm, stream));
+  else
+    MOE_TRY(dispatch_stage(c, x, ids, true, hist, at<int32_t>(ws, L.base), counts, offsets, slot,
+                           row_of, row_token, x_perm, stream));
   MOE_TRY(mark(2));
   MOE_TRY(gemm1_stage(c, gather ? x : x_perm, gather ? row_token : nullptr, offsets, W1, b1, h,
                       stream));
   MOE_TRY(mark(3));
   MOE_TRY(gemm2_stage(c, h, offsets, W2, b2, y_perm, stream));
   MOE_TRY(mark(4));
-  MOE_TRY(combine_stage(c, y_perm, row_of, gates, y, stream));
+  MOE_TRY(combine_stage(c, y_perm, row_of, cgates, y, stream));
   return mark(5);
 }
 

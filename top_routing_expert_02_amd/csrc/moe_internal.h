@@ -47,9 +47,11 @@ hipError_t launch_logits_bf16(const uint16_t* x, const uint16_t* Wr, const float
 hipError_t launch_logits_f32(const float* x, const float* Wr, const float* br, float* logits,
                              int64_t T, int d, int E, hipStream_t s);
 
-// softmax, top-k, gates; optional per-tile prob sums [ntiles,E] and expert
-// histograms [ntiles,E] (tile = kTileTokens tokens).
-hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int renormalize,
+// softmax, top-nsel, gates; optional per-tile prob sums [ntiles,E] and expert
+// histograms of the first k choices [ntiles,E] (tile = kTileTokens tokens).
+// ids/gates are [T,nsel] (nsel >= k): the top-k then the next candidates;
+// renormalised gates divide by the sum over the first k only.
+hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int nsel, int renormalize,
                        int32_t* ids, float* gates, float* prob_part, int32_t* hist,
                        hipStream_t s);
 // out[e] = sum over tiles of part[tile,e], tiles in order.
@@ -74,6 +76,26 @@ hipError_t launch_permute_scan(const void* x, const int32_t* ids, const int32_t*
                                int k, int E, int C, int row_bytes, int32_t* counts,
                                int32_t* offsets, int32_t* slot, int32_t* row_of,
                                int32_t* row_token, void* x_perm, hipStream_t s);
+
+// Dispatch with a priority order and overflow re-routing rounds. The plan's
+// buffers live in the workspace: col/served [T*k], next_col [T], fill/fill0
+// [E], hist/base [reroute_tiles(T,k) * E].
+struct ReroutePlan {
+  int32_t* col;
+  int32_t* served;
+  int32_t* next_col;
+  int32_t* fill;
+  int32_t* fill0;
+  int32_t* hist;
+  int32_t* base;
+};
+int64_t reroute_tiles(int64_t T, int k);
+hipError_t launch_dispatch_reroute(const void* x, const int32_t* cand, const float* cand_gates,
+                                   int64_t T, int k, int n, int E, int C, bool rank_priority,
+                                   int rounds, int row_bytes, const ReroutePlan& ws,
+                                   int32_t* counts, int32_t* offsets, int32_t* slot,
+                                   int32_t* row_of, int32_t* row_token, int32_t* served_ids,
+                                   float* combine_gates, void* x_perm, hipStream_t s);
 
 // x_perm[r] = x[row_token[r]] for r < offsets[E] (rows bounded by max_rows)
 hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int32_t* offsets,

@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void logits_f32_kernel(const float* __restrict
 // free) and sum_t p_{t,i} (fixed-order sums: lanes, then groups, then waves).
 template <int G, int NV, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void topk_kernel(const float* __restrict__ logits, int64_t T,
-                                                   int E, int k, int renormalize,
+                                                   int E, int k, int nsel, int renormalize,
                                                    int32_t* __restrict__ ids,
                                                    float* __restrict__ gates,
                                                    float* __restrict__ prob_part,
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(64 * WAVES) void topk_kernel(const float* __restric
 
     float my_v = 0.f, top = 0.f;
     int my_id = -1;
-    for (int r = 0; r < k; ++r) {
+    for (int r = 0; r < nsel; ++r) {
       float bv = -__builtin_inff();
       int bi = 0x7fffffff;
 #pragma unroll
@@ -239,17 +239,17 @@ __global__ __launch_bounds__(64 * WAVES) void topk_kernel(const float* __restric
 #pragma unroll
     for (int off = G / 2; off >= 1; off >>= 1) se += __shfl_xor(se, off, 64);
 
-    const float mine = (gl < k) ? __expf(my_v - top) : 0.f;
+    const float mine = (gl < nsel) ? __expf(my_v - top) : 0.f;
     float den = se;
     if (renormalize) {
-      den = mine;
+      den = (gl < k) ? mine : 0.f;  // the top-k sum, also for later candidates
 #pragma unroll
       for (int off = G / 2; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
     }
-    if (tv && gl < k) {
-      ids[t * k + gl] = my_id;
-      gates[t * k + gl] = mine / den;
-      if (want_hist) atomicAdd(&s_hist[my_id], 1);
+    if (tv && gl < nsel) {
+      ids[t * nsel + gl] = my_id;
+      gates[t * nsel + gl] = mine / den;
+      if (want_hist && gl < k) atomicAdd(&s_hist[my_id], 1);
     }
     if (want_prob && tv) {
       const float inv = 1.0f / se;
@@ -320,13 +320,13 @@ hipError_t launch_logits_f32(const float* x, const float* Wr, const float* br, f
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int renormalize,
+hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int nsel, int renormalize,
                        int32_t* ids, float* gates, float* prob_part, int32_t* hist,
                        hipStream_t s) {
   const unsigned grid = static_cast<unsigned>((T + 63) / 64);
 #define MOE_TOPK(G, NV)                                                                          \
   topk_kernel<G, NV, (G >= 16 ? 16 : G)><<<grid, 64 * (G >= 16 ? 16 : G), 0, s>>>(                \
-      logits, T, E, k, renormalize, ids, gates, prob_part, hist)
+      logits, T, E, k, nsel, renormalize, ids, gates, prob_part, hist)
   // groups of at least 16 lanes (k <= 16 results per token) holding up to 16
   // logits per lane: a wave runs 4 tokens' shuffle chains side by side, and
   // each round's butterfly has at most 4 levels below 256 experts

@@ -20,11 +20,13 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
           -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_RELU, MOE_ACT_GELU_TANH = 0, 1
+MOE_PRIORITY_TOKEN, MOE_PRIORITY_RANK = 0, 1
 MOE_NUM_STAGES = 5
 STAGE_NAMES = ["route", "dispatch", "gemm1", "gemm2", "combine"]
 
-EXPORTED = ["moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_route", "moe_dispatch",
-            "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_status_string"]
+EXPORTED = ["moe_capacity", "moe_candidates", "moe_max_rows", "moe_workspace_size", "moe_route",
+            "moe_dispatch", "moe_dispatch_reroute", "moe_expert_ffn", "moe_combine",
+            "moe_layer_forward", "moe_status_string"]
 
 
 class MoeError(RuntimeError):
@@ -37,13 +39,14 @@ class MoeError(RuntimeError):
 class MoeConfig(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("capacity", ctypes.c_int32),
-                ("renormalize", ctypes.c_int32), ("dtype", ctypes.c_int32), ("act", ctypes.c_int32)]
+                ("renormalize", ctypes.c_int32), ("dtype", ctypes.c_int32), ("act", ctypes.c_int32),
+                ("priority", ctypes.c_int32), ("reroute", ctypes.c_int32)]
 
 
 class MoeRouteInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("topk_ids", "topk_gates", "prob_sum", "expert_counts", "expert_offsets", "slot",
-                 "row_of", "row_token")]
+                 "row_of", "row_token", "served_ids", "combine_gates")]
 
 
 _lib = None
@@ -60,10 +63,12 @@ def lib():
         P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         CFG = ctypes.POINTER(MoeConfig)
         L.moe_capacity.argtypes = [I64, I32, I32, ctypes.c_double, ctypes.POINTER(I32)]
+        L.moe_candidates.argtypes = [CFG, ctypes.POINTER(I32)]
         L.moe_max_rows.argtypes = [CFG, ctypes.POINTER(I64)]
         L.moe_workspace_size.argtypes = [CFG, ctypes.POINTER(SZ)]
         L.moe_route.argtypes = [CFG, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_dispatch.argtypes = [CFG, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.moe_dispatch_reroute.argtypes = [CFG, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_expert_ffn.argtypes = [CFG, P, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_combine.argtypes = [CFG, P, P, P, P, P]
         L.moe_layer_forward.argtypes = [CFG, P, P, P, P, P, P, P, P, ctypes.POINTER(MoeRouteInfo),
@@ -96,11 +101,13 @@ def _stream(stream):
     return s.cuda_stream
 
 
-def config(T, d, d_ff, E, k, capacity, renormalize, dtype, act) -> MoeConfig:
+def config(T, d, d_ff, E, k, capacity, renormalize, dtype, act, priority="token",
+           reroute=0) -> MoeConfig:
     dt = {"f32": MOE_F32, "bf16": MOE_BF16}.get(dtype, dtype)
     ac = {"relu": MOE_ACT_RELU, "gelu_tanh": MOE_ACT_GELU_TANH}.get(act, act)
+    pr = {"token": MOE_PRIORITY_TOKEN, "rank": MOE_PRIORITY_RANK}.get(priority, priority)
     return MoeConfig(int(T), int(d), int(d_ff), int(E), int(k), int(capacity),
-                     int(bool(renormalize)), int(dt), int(ac))
+                     int(bool(renormalize)), int(dt), int(ac), int(pr), int(reroute))
 
 
 # ------------------------------------------------------------------ host-only calls
@@ -108,6 +115,12 @@ def config(T, d, d_ff, E, k, capacity, renormalize, dtype, act) -> MoeConfig:
 def capacity(T: int, k: int, E: int, c: float) -> int:
     out = ctypes.c_int32(0)
     _check("moe_capacity", lib().moe_capacity(int(T), int(k), int(E), float(c), ctypes.byref(out)))
+    return out.value
+
+
+def candidates(cfg: MoeConfig) -> int:
+    out = ctypes.c_int32(0)
+    _check("moe_candidates", lib().moe_candidates(ctypes.byref(cfg), ctypes.byref(out)))
     return out.value
 
 
@@ -145,6 +158,15 @@ def dispatch(cfg, x, topk_ids, expert_counts, expert_offsets, slot, row_of, row_
                                               _ptr(slot), _ptr(row_of), _ptr(row_token),
                                               _ptr(x_perm), _ptr(ws), ws.numel(),
                                               _stream(stream)))
+
+
+def dispatch_reroute(cfg, x, cand_ids, cand_gates, expert_counts, expert_offsets, slot, row_of,
+                     row_token, served_ids, combine_gates, x_perm=None, ws=None, stream=None):
+    ws = alloc_workspace(cfg, cand_ids.device) if ws is None else ws
+    _check("moe_dispatch_reroute", lib().moe_dispatch_reroute(
+        ctypes.byref(cfg), _ptr(x), _ptr(cand_ids), _ptr(cand_gates), _ptr(expert_counts),
+        _ptr(expert_offsets), _ptr(slot), _ptr(row_of), _ptr(row_token), _ptr(served_ids),
+        _ptr(combine_gates), _ptr(x_perm), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def expert_ffn(cfg, x_perm, expert_offsets, W1, b1, W2, b2, h, y_perm, ws=None, stream=None):

@@ -26,6 +26,11 @@ Dropless variants (capacity C = T, so no assignment is ever dropped):
                 expert takes most of the 8192 tokens
   decode_bf16   mid_bf16's layer at decode size, T=64, C = T
 
+Re-routing variant:
+
+  skewed_reroute_bf16  skewed_bf16 with rank-major priority and two rounds
+                of overflow re-routing to the next candidate experts
+
 N(0, v) names the variance v. x ~ N(0, 1); W_r and W1 ~ N(0, 1/d); W2 ~ N(0, 1/d_ff).
 Values are drawn in fp32 and rounded to bf16 (round to nearest even) for the
 bf16 workloads; biases are always fp32.
@@ -64,6 +69,8 @@ class Workload:
     ffn_bias_var: float     # variance of b1 and b2 (0 means zero biases)
     seed_id: int
     dropless: bool = False  # capacity C = T instead of ceil(c T k / E)
+    priority: str = "token"  # "token" or "rank": order arrivals at a full expert are served
+    reroute: int = 0        # rounds of overflow re-routing to the next candidate
 
     def scaled(self, **changes) -> "Workload":
         """Same recipe at other sizes (used for parity tests the oracle can
@@ -92,6 +99,8 @@ WORKLOADS = {
 WORKLOADS["skewed_dropless_bf16"] = WORKLOADS["skewed_bf16"].scaled(name="skewed_dropless_bf16",
                                                                     dropless=True)
 WORKLOADS["decode_bf16"] = WORKLOADS["mid_bf16"].scaled(name="decode_bf16", T=64, dropless=True)
+WORKLOADS["skewed_reroute_bf16"] = WORKLOADS["skewed_bf16"].scaled(name="skewed_reroute_bf16",
+                                                                   priority="rank", reroute=2)
 
 
 def _seed(*ids) -> int:
