@@ -44,7 +44,7 @@ reason in the design notes):
       constants are "parity unpinned" by the pages: they are pinned only
       against an independent library implementation and the exact GELU.
   R9  overflow re-routing ([MoE Principles §4.3], second option; [EP 001]
-      "overflow to the next-best expert"): an assignment that overflows moves
+      section 一, overflow may go to the next-best expert): an assignment that overflows moves
       to the token's next candidate, the best-scoring expert the token has
       not yet been offered; it is served with that expert's probability as
       its weight (divided by the same top-k sum when renormalising).
@@ -54,6 +54,12 @@ reason in the design notes):
       take what capacity round j-1 left. Inside a round, arrivals are served
       in priority order: token order (t, then rank r) or, GShard-style, rank
       order (every token's first choice before any second choice).
+  R11 backward: the top-k choice and the capacity decisions are held fixed
+      (a discrete choice has no gradient, [MoE Principles §2.4]); gradients
+      reach the router through the combine weights of the kept assignments
+      and, when alpha > 0, through pbar in L_aux (f_i is a count, constant)
+      [MoE Principles §3.2]. The scalar differentiated is
+      L = <dy, y> + L_aux.
 """
 from __future__ import annotations
 
@@ -400,6 +406,113 @@ def sampled_outputs(tokens, x, ids, row_of, g, expert_weights, act: str) -> np.n
             _, Y = expert_ffn(x[t:t + 1], W1e, b1e, W2e, b2e, act)
             out[n] += g[t, j] * Y[0]
     return out
+
+
+# ---------------------------------------------------------------- backward
+
+def gelu_tanh_grad(u: np.ndarray) -> np.ndarray:
+    """d/du of gelu_tanh: 0.5 (1 + tanh z) + 0.5 u (1 - tanh^2 z) dz/du with
+    z = a (u + b u^3), dz/du = a (1 + 3 b u^2)  (reading R8's function)."""
+    a = math.sqrt(2.0 / math.pi)
+    b = 0.044715
+    th = np.tanh(a * (u + b * u ** 3))
+    return 0.5 * (1.0 + th) + 0.5 * u * (1.0 - th * th) * a * (1.0 + 3.0 * b * u * u)
+
+
+def relu_grad(u: np.ndarray) -> np.ndarray:
+    return (u > 0).astype(np.float64)
+
+
+ACT_GRADS = {"relu": relu_grad, "gelu_tanh": gelu_tanh_grad}
+
+
+def layer_backward(x, W_r, b_r, W1, b1, W2, b2, dy, *, k: int, C: int, renormalize: bool,
+                   act: str, alpha: float = 0.0, ids=None, priority: str = "token") -> dict:
+    """Gradients of L = <dy, y> + L_aux with respect to x and every parameter,
+    by the chain rule through the forward's steps (reading R11):
+
+      dY_r   = g_{t,j} dy_t                    for each kept row r = row_of[t, j]
+      dg_tj  = <dy_t, Y_r>                     (0 for a dropped assignment)
+      dh     = dY W2_e;  du = dh * sigma'(u)   u = x_perm W1_e^T + b1_e
+      dW2_e  = dY_e^T h_e, db2_e = sum_r dY_r; dW1_e = du_e^T x_perm_e, db1_e = sum_r du_r
+      dx_t  += sum_j du_{row_of[t,j]} W1_e
+      router: gates g = p_i / P (renormalised, P = sum over S_t) or p_i, so
+        dp_i = (dg_i - sum_j dg_j g_j) / P  or  dg_i  for i in S_t;
+        L_aux adds alpha E f_i / T to dp_{t,i} for every t, i;
+        ds = p * (dp - sum_j p_j dp_j)  (softmax);
+        dW_r = ds^T x, db_r = sum_t ds_t, dx_t += ds_t W_r.
+
+    Works for the plain and rank-priority rules (both keep the top-k gates).
+    Returns fp64 arrays dx [T,d], dW_r, db_r, dW1, db1, dW2, db2 and the
+    forward dict under "fwd"."""
+    T, d = x.shape
+    E = W_r.shape[0]
+    fwd = layer_forward(x, W_r, b_r, W1, b1, W2, b2, k=k, C=C, renormalize=renormalize,
+                        act=act, ids=ids, priority=priority)
+    use_ids = np.asarray(fwd["used_ids"], dtype=np.int64)[:, :k]
+    g = fwd["used_gates"]
+    row_of = fwd["row_of"]
+    off = fwd["expert_offsets"]
+    x_perm, h, Y = fwd["x_perm"], fwd["h"], fwd["y_perm"]
+    rows = fwd["rows"]
+    dY = np.zeros((rows, d))
+    dg = np.zeros((T, k))
+    for t in range(T):
+        for j in range(k):
+            r = row_of[t, j]
+            if r >= 0:
+                dY[r] = g[t, j] * dy[t]
+                dg[t, j] = float(np.dot(dy[t], Y[r]))
+    dx = np.zeros((T, d))
+    dW1, db1 = np.zeros_like(W1), np.zeros_like(b1)
+    dW2, db2 = np.zeros_like(W2), np.zeros_like(b2)
+    dx_perm = np.zeros((rows, d))
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if b == a:
+            continue
+        u = x_perm[a:b] @ W1[e].T + b1[e][None, :]
+        dh = dY[a:b] @ W2[e]
+        du = dh * ACT_GRADS[act](u)
+        dW2[e] = dY[a:b].T @ h[a:b]
+        db2[e] = dY[a:b].sum(axis=0)
+        dW1[e] = du.T @ x_perm[a:b]
+        db1[e] = du.sum(axis=0)
+        dx_perm[a:b] = du @ W1[e]
+    for t in range(T):
+        for j in range(k):
+            r = row_of[t, j]
+            if r >= 0:
+                dx[t] += dx_perm[r]
+    # router
+    p = fwd["probs"]
+    dp = np.zeros((T, E))
+    chosen = np.take_along_axis(p, use_ids, axis=1)
+    if renormalize:
+        P = chosen.sum(axis=1, keepdims=True)
+        gg = chosen / P
+        inner = (dg * gg).sum(axis=1, keepdims=True)
+        np.put_along_axis(dp, use_ids, (dg - inner) / P, axis=1)
+    else:
+        np.put_along_axis(dp, use_ids, dg, axis=1)
+    if alpha != 0.0:
+        f = np.asarray(fwd["expert_counts"], dtype=np.float64) / T
+        dp += alpha * E * f[None, :] / T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    dW_r = ds.T @ x
+    db_r = ds.sum(axis=0)
+    dx += ds @ W_r
+    return {"dx": dx, "dW_r": dW_r, "db_r": db_r, "dW1": dW1, "db1": db1, "dW2": dW2,
+            "db2": db2, "dg": dg, "ds": ds, "fwd": fwd}
+
+
+def layer_loss(x, W_r, b_r, W1, b1, W2, b2, dy, *, k: int, C: int, renormalize: bool, act: str,
+               alpha: float = 0.0, ids=None, priority: str = "token") -> float:
+    """The scalar L = <dy, y> + L_aux that layer_backward differentiates."""
+    o = layer_forward(x, W_r, b_r, W1, b1, W2, b2, k=k, C=C, renormalize=renormalize, act=act,
+                      ids=ids, priority=priority)
+    T, E = x.shape[0], W_r.shape[0]
+    return float(np.sum(dy * o["y"])) + aux_loss(o["expert_counts"], o["prob_sum"], T, E, alpha)
 
 
 # ---------------------------------------------------------------- statistics

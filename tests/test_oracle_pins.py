@@ -717,3 +717,141 @@ def test_planted_candidate_gate_denominator_is_caught(monkeypatch):
     monkeypatch.setattr(mo, "candidate_gates",
                         lambda p, cand, k, renormalize: orig(p, cand, cand.shape[1], renormalize))
     _expect_fail(check_candidate_gates)
+
+
+# ------------------------------------------------------------------ backward
+
+def small_layer(seed, T=24, d=6, d_ff=10, E=4, k=2, hot=1.5):
+    r = rng(seed)
+    x = r.standard_normal((T, d))
+    W_r = r.standard_normal((E, d))
+    b_r = np.zeros(E)
+    b_r[0] = hot                      # expert 0 overflows at small C
+    W1 = r.standard_normal((E, d_ff, d)) / math.sqrt(d)
+    b1 = 0.1 * r.standard_normal((E, d_ff))
+    W2 = r.standard_normal((E, d, d_ff)) / math.sqrt(d_ff)
+    b2 = 0.1 * r.standard_normal((E, d))
+    dy = r.standard_normal((T, d))
+    return dict(x=x, W_r=W_r, b_r=b_r, W1=W1, b1=b1, W2=W2, b2=b2), dy
+
+
+def check_backward_finite_differences(act="gelu_tanh", renormalize=True, alpha=0.3, C=9,
+                                      priority="token", seed=41):
+    """<grad, v> against a central difference of the forward's scalar loss
+    along a random direction v, for every input and parameter tensor; the
+    routing and capacity decisions do not change within +-eps."""
+    P, dy = small_layer(seed)
+    kw = dict(k=2, C=C, renormalize=renormalize, act=act, alpha=alpha, priority=priority)
+    g = mo.layer_backward(P["x"], P["W_r"], P["b_r"], P["W1"], P["b1"], P["W2"], P["b2"], dy, **kw)
+    assert 0 < g["fwd"]["rows"] < 24 * 2          # some drops, some kept
+    names = {"x": "dx", "W_r": "dW_r", "b_r": "db_r", "W1": "dW1", "b1": "db1", "W2": "dW2",
+             "b2": "db2"}
+    r = rng(seed + 1)
+    eps = 1e-6
+    for name, gname in names.items():
+        v = r.standard_normal(P[name].shape)
+        plus, minus = dict(P), dict(P)
+        plus[name] = P[name] + eps * v
+        minus[name] = P[name] - eps * v
+        args_p = [plus[n] for n in ("x", "W_r", "b_r", "W1", "b1", "W2", "b2")]
+        args_m = [minus[n] for n in ("x", "W_r", "b_r", "W1", "b1", "W2", "b2")]
+        fp = mo.layer_forward(*args_p, k=2, C=C, renormalize=renormalize, act=act, priority=priority)
+        fm = mo.layer_forward(*args_m, k=2, C=C, renormalize=renormalize, act=act, priority=priority)
+        assert np.array_equal(fp["row_of"], g["fwd"]["row_of"]) and np.array_equal(fm["row_of"], g["fwd"]["row_of"])
+        fd = (mo.layer_loss(*args_p, dy, **kw) - mo.layer_loss(*args_m, dy, **kw)) / (2 * eps)
+        an = float(np.sum(g[gname] * v))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_backward_finite_differences():
+    check_backward_finite_differences()
+
+
+@pytest.mark.parametrize("act,renormalize,alpha,priority", [
+    ("relu", False, 0.0, "token"), ("gelu_tanh", True, 0.0, "rank"), ("relu", True, 1.0, "token")])
+def test_backward_finite_differences_variants(act, renormalize, alpha, priority):
+    check_backward_finite_differences(act=act, renormalize=renormalize, alpha=alpha,
+                                      priority=priority, seed=43)
+
+
+def torch_layer_loss(P, dy, ids, row_kept, k, renormalize, act, alpha, counts):
+    """The same scalar loss written with torch ops (fp64) from the layer's
+    definition, for autograd: the routing decisions are given."""
+    x, W_r, b_r = P["x"], P["W_r"], P["b_r"]
+    s = x @ W_r.T + b_r
+    p = torch.softmax(s, dim=1)
+    chosen = torch.gather(p, 1, ids)
+    g = chosen / chosen.sum(dim=1, keepdim=True) if renormalize else chosen
+    y = torch.zeros_like(x)
+    T = x.shape[0]
+    for j in range(k):
+        e_j = ids[:, j]
+        u = torch.einsum("tfd,td->tf", P["W1"][e_j], x) + P["b1"][e_j]
+        hh = torch.nn.functional.gelu(u, approximate="tanh") if act == "gelu_tanh" else torch.relu(u)
+        Y = torch.einsum("tdf,tf->td", P["W2"][e_j], hh) + P["b2"][e_j]
+        y = y + (g[:, j] * row_kept[:, j])[:, None] * Y
+    E = W_r.shape[0]
+    aux = alpha * E * torch.sum((counts / T) * (p.sum(dim=0) / T))
+    return torch.sum(dy * y) + aux
+
+
+def test_backward_against_autograd():
+    P, dy = small_layer(47, T=30, E=5)
+    for act, renorm, alpha in [("gelu_tanh", True, 0.5), ("relu", False, 0.0)]:
+        g = mo.layer_backward(P["x"], P["W_r"], P["b_r"], P["W1"], P["b1"], P["W2"], P["b2"], dy,
+                              k=2, C=8, renormalize=renorm, act=act, alpha=alpha)
+        f = g["fwd"]
+        tp = {n: torch.tensor(v, dtype=torch.float64, requires_grad=True) for n, v in P.items()}
+        ids = torch.tensor(f["used_ids"], dtype=torch.int64)
+        kept = torch.tensor(f["row_of"] >= 0, dtype=torch.float64)
+        counts = torch.tensor(f["expert_counts"], dtype=torch.float64)
+        L = torch_layer_loss(tp, torch.tensor(dy), ids, kept, 2, renorm, act, alpha, counts)
+        L.backward()
+        for n, gn in [("x", "dx"), ("W_r", "dW_r"), ("b_r", "db_r"), ("W1", "dW1"), ("b1", "db1"),
+                      ("W2", "dW2"), ("b2", "db2")]:
+            np.testing.assert_allclose(g[gn], tp[n].grad.numpy(), rtol=1e-10, atol=1e-12,
+                                       err_msg=f"{act} {n}")
+
+
+def test_backward_single_expert_is_dense_mlp():
+    """E = 1, k = 1, C >= T: the layer is a dense MLP; its router sees a
+    softmax over one expert (constant 1), so the router gradients vanish."""
+    P, dy = small_layer(53, T=12, E=1, k=1, hot=0.0)
+    g = mo.layer_backward(P["x"], P["W_r"], P["b_r"], P["W1"], P["b1"], P["W2"], P["b2"], dy,
+                          k=1, C=12, renormalize=True, act="gelu_tanh", alpha=0.7)
+    x = torch.tensor(P["x"], requires_grad=True)
+    W1 = torch.tensor(P["W1"][0], requires_grad=True)
+    b1 = torch.tensor(P["b1"][0], requires_grad=True)
+    W2 = torch.tensor(P["W2"][0], requires_grad=True)
+    b2 = torch.tensor(P["b2"][0], requires_grad=True)
+    F = torch.nn.functional
+    y = F.linear(F.gelu(F.linear(x, W1, b1), approximate="tanh"), W2, b2)
+    torch.sum(torch.tensor(dy) * y).backward()
+    np.testing.assert_allclose(g["dx"], x.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["dW1"][0], W1.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["db1"][0], b1.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["dW2"][0], W2.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["db2"][0], b2.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.abs(g["dW_r"]).max() < 1e-14 and np.abs(g["db_r"]).max() < 1e-14
+
+
+def test_planted_missing_activation_grad_is_caught(monkeypatch):
+    monkeypatch.setitem(mo.ACT_GRADS, "gelu_tanh", lambda u: np.ones_like(u))
+    _expect_fail(check_backward_finite_differences)
+
+
+def test_planted_renorm_grad_sign_is_caught(monkeypatch):
+    orig = mo.layer_backward
+
+    def flipped(*a, **kw):
+        out = orig(*a, **kw)
+        out["db_r"] = -out["db_r"]
+        return out
+    monkeypatch.setattr(mo, "layer_backward", flipped)
+    _expect_fail(check_backward_finite_differences)
+
+
+def test_planted_missing_aux_grad_is_caught(monkeypatch):
+    orig = mo.layer_backward
+    monkeypatch.setattr(mo, "layer_backward", lambda *a, **kw: orig(*a, **{**kw, "alpha": 0.0}))
+    _expect_fail(check_backward_finite_differences)
