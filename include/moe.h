@@ -264,6 +264,40 @@ int32_t moe_layer_forward(const moe_config *cfg, const void *x, const void *W_r,
                           const float *b2, void *y, const moe_route_info *info, void *ws,
                           size_t ws_bytes, hipEvent_t *stage_events, hipStream_t stream);
 
+/* Workspace bytes moe_layer_backward needs (host only). */
+int32_t moe_backward_workspace_size(const moe_config *cfg, size_t *bytes);
+
+/*
+ * Backward pass of the layer: gradients of L = <dy, y> + L_aux, L_aux =
+ * aux_alpha E sum_i f_i pbar_i ([MoE Principles] §3.2), with the forward's
+ * top-k choices and capacity decisions held fixed (a discrete choice has no
+ * gradient; a chosen expert receives its gradient through its combine
+ * weight, [MoE Principles] §2.4; §9.1 lists the expert and combine backward
+ * among the training steps):
+ *   dY_r = g_{t,j} dy_t for kept rows; dg_{t,j} = <dy_t, y_perm_r>;
+ *   dh = dY W2_e; du = dh * sigma'(u), u = x W1_e^T + b1_e;
+ *   dW2_e = dY^T h, db2_e = sum dY; dW1_e = du^T x, db1_e = sum du;
+ *   dx_t = sum_j du_r W1_e + ds_t W_r; the router: dp through the
+ *   (renormalised) gates plus aux_alpha E f_i / T, ds = softmax backward,
+ *   dW_r = ds^T x, db_r = sum_t ds_t.
+ * u, h and y_perm's contribution are recomputed from x (nothing of the
+ * forward is stored beyond its routing results). bf16 layers round the
+ * GEMM operands dY, du (and h, as the forward does) to bf16; all
+ * accumulation is fp32.
+ *   in  x, W_r, W1, W2, dy [T,d] (dtype); b_r, b1, b2 fp32 or NULL.
+ *   in  fwd: the forward's topk_ids, topk_gates, expert_counts,
+ *       expert_offsets, row_of and row_token (all required).
+ *   out dx [T,d], dW_r [E,d], dW1 [E,d_ff,d], dW2 [E,d,d_ff] fp32 (required);
+ *       db_r [E], db1 [E,d_ff], db2 [E,d] fp32 or NULL (not computed).
+ *   ws: at least moe_backward_workspace_size bytes, 256-byte aligned.
+ * Errors as the forward; cfg->reroute != 0 gives MOE_ERR_UNSUPPORTED.
+ */
+int32_t moe_layer_backward(const moe_config *cfg, const void *x, const void *W_r, const float *b_r,
+                           const void *W1, const float *b1, const void *W2, const float *b2,
+                           const moe_route_info *fwd, const void *dy, float aux_alpha, float *dx,
+                           float *dW_r, float *db_r, float *dW1, float *db1, float *dW2, float *db2,
+                           void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* A static string naming a status code. */
 const char *moe_status_string(int32_t status);
 

@@ -146,6 +146,38 @@ def test_candidates_and_rule_validation(m):
                                   None, None, None, fake, ws, None) == -1
 
 
+def test_backward_rejects_without_launching(m):
+    L = m.lib()
+    P = ctypes.c_void_p
+    fake = P(0x100000)
+    cfg = good_cfg(m)
+    n = m.backward_workspace_size(cfg)
+    assert n >= m.workspace_size(cfg) // 4 and n % 256 == 0
+    info = m.MoeRouteInfo(*([0x100000] * 10))
+    args = lambda c, ws_n: (ctypes.byref(c), fake, fake, None, fake, None, fake, None,
+                            ctypes.byref(info), fake, ctypes.c_float(0.0), fake, fake, None, fake,
+                            None, fake, None, fake, ws_n, None)
+    # re-routing has no backward
+    rr = good_cfg(m, reroute=1)
+    assert L.moe_layer_backward(*args(rr, m.backward_workspace_size(rr))) == -2
+    # short workspace
+    assert L.moe_layer_backward(*args(cfg, n - 256)) == -3
+    # missing forward state
+    bad_info = m.MoeRouteInfo(*([0x100000] * 5 + [0] * 5))
+    a = list(args(cfg, n))
+    a[8] = ctypes.byref(bad_info)
+    assert L.moe_layer_backward(*a) == -1
+    # non-finite aux coefficient
+    a = list(args(cfg, n))
+    a[10] = ctypes.c_float(float("nan"))
+    assert L.moe_layer_backward(*a) == -1
+    # T == 0: no-op
+    empty = good_cfg(m, T=0)
+    assert L.moe_layer_backward(ctypes.byref(empty), None, None, None, None, None, None, None, None,
+                                None, ctypes.c_float(0.0), None, None, None, None, None, None, None,
+                                None, 0, None) == 0
+
+
 def test_status_strings(m):
     L = m.lib()
     for s in (0, -1, -2, -3, -4, 99):

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
-SOURCES = ["moe_api.cpp", "route.hip", "dispatch.hip", "reroute.hip", "ffn_bf16.hip", "ffn_f32.hip",
+SOURCES = ["moe_api.cpp", "route.hip", "dispatch.hip", "reroute.hip", "backward.hip", "ffn_bf16.hip", "ffn_f32.hip",
            "combine.hip"]
 
 ARCH = "gfx950"

@@ -1,0 +1,396 @@
+// Backward pass of the MoE layer: gradients of L = <dy, y> + L_aux with the
+// routing and capacity decisions of the forward held fixed (page "MoE 模型原理：
+// 路由、专家负载、容量、通信与推理成本", wrblog.cn: §2.4, a chosen expert gets its
+// gradient through the combine weight; §3.2, L_aux = alpha E sum_i f_i pbar_i
+// with f_i a count; §9.1 lists expert backward and combine backward among the
+// training steps).
+//
+// Kernels here (the expert dgrad GEMMs reuse the forward's grouped GEMMs on
+// transposed weights):
+//   transpose        W[e] [R,C] -> Wt[e] [C,R]
+//   row_info         per kept row: its gate and expert
+//   bwd_rows         per kept row: h = sigma(u) (as the forward rounds it),
+//                    du = g Z sigma'(u), dY = g dy_t, and the combine-weight
+//                    gradient dg = <Z, h> + <dy_t, b2_e> (Z = dy_t W2_e)
+//   router_bwd       per token: softmax probabilities from the logits, dp
+//                    through the (renormalised) gates and L_aux, ds (softmax
+//                    backward), in [T,E] and [E,T] layouts
+//   dx_gather        dx_t = sum over kept j of dx_perm[row_of[t,j]]
+//   wgrad            C[g] (+)= A_g^T B_g over the rows of group g (fp32
+//                    accumulate, 64x64 tiles): dW1, dW2, dW_r and ds W_r
+//   colsum           per group, column sums over its rows: db1, db2, db_r
+// Every reduction runs in a fixed order: results are deterministic.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+template <typename TE>
+__device__ __forceinline__ float ld(const TE* p, int64_t i) {
+  if constexpr (sizeof(TE) == 2) return bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+  else return reinterpret_cast<const float*>(p)[i];
+}
+
+template <typename TE>
+__device__ __forceinline__ float round_to(float v) {
+  if constexpr (sizeof(TE) == 2) return static_cast<float>(static_cast<__bf16>(v));
+  else return v;
+}
+
+template <typename TE>
+__device__ __forceinline__ void st(TE* p, int64_t i, float v) {
+  if constexpr (sizeof(TE) == 2) {
+    const __bf16 b = static_cast<__bf16>(v);
+    reinterpret_cast<__bf16*>(p)[i] = b;
+  } else {
+    reinterpret_cast<float*>(p)[i] = v;
+  }
+}
+
+// dst[e][c][r] = src[e][r][c]; 64x64 tiles through LDS
+template <typename TE>
+__global__ __launch_bounds__(256) void transpose_kernel(const TE* __restrict__ src, TE* __restrict__ dst,
+                                                        int R, int Cc) {
+  __shared__ TE tile[64][65];
+  const int64_t e = blockIdx.z;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const TE* s = src + e * R * static_cast<int64_t>(Cc);
+  TE* d = dst + e * R * static_cast<int64_t>(Cc);
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    if (r < R && c < Cc) tile[i][tx] = s[static_cast<int64_t>(r) * Cc + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (r < R && c < Cc) d[static_cast<int64_t>(c) * R + r] = tile[tx][i];
+  }
+}
+
+__global__ __launch_bounds__(256) void row_info_kernel(const int32_t* __restrict__ ids,
+                                                       const float* __restrict__ gates,
+                                                       const int32_t* __restrict__ row_of,
+                                                       int64_t Tk, int32_t* __restrict__ row_expert,
+                                                       float* __restrict__ row_gate) {
+  const int64_t a = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (a >= Tk) return;
+  const int row = row_of[a];
+  if (row < 0) return;
+  row_expert[row] = ids[a];
+  row_gate[row] = gates[a];
+}
+
+__device__ __forceinline__ float gelu_tanh_grad(float u) {
+  // d/du 0.5 u (1 + tanh z), z = a (u + b u^3): 0.5 (1 + th) + 0.5 u (1 - th^2) a (1 + 3 b u^2)
+  constexpr float a = 0.7978845608028654f, b = 0.044715f;
+  const float z = a * fmaf(b * u * u, u, u);
+  const float th = 1.0f - 2.0f / (1.0f + __expf(2.0f * z));
+  return 0.5f * (1.0f + th) + 0.5f * u * (1.0f - th * th) * a * fmaf(3.0f * b, u * u, 1.0f);
+}
+
+template <typename TE, int ACT>
+__device__ __forceinline__ float act_fwd(float u) {
+  if constexpr (ACT == kActRelu) return act_relu(u);
+  else if constexpr (sizeof(TE) == 2) return act_gelu_tanh_fast(u);  // as the bf16 GEMM epilogue
+  else return act_gelu_tanh(u);                                     // as the fp32 GEMM
+}
+
+template <int ACT>
+__device__ __forceinline__ float act_grad(float u) {
+  if constexpr (ACT == kActRelu) return u > 0.f ? 1.f : 0.f;
+  else return gelu_tanh_grad(u);
+}
+
+// one block per kept row
+template <typename TE, int ACT>
+__global__ __launch_bounds__(256) void bwd_rows_kernel(
+    const float* __restrict__ u, const float* __restrict__ Z, const int32_t* __restrict__ row_token,
+    const float* __restrict__ row_gate, const int32_t* __restrict__ row_expert,
+    const int32_t* __restrict__ offsets, int E, const TE* __restrict__ dy, const float* __restrict__ b2,
+    int d, int d_ff, TE* __restrict__ h, TE* __restrict__ du, TE* __restrict__ dY,
+    float* __restrict__ dg_row) {
+  __shared__ float red[256];
+  const int64_t r = blockIdx.x;
+  if (r >= offsets[E]) return;
+  const int64_t t = row_token[r];
+  const float g = row_gate[r];
+  const int e = row_expert[r];
+  float dot = 0.f;
+  for (int c = threadIdx.x; c < d_ff; c += 256) {
+    const int64_t i = r * d_ff + c;
+    const float uv = u[i];
+    const float z = Z[i];
+    const float hv = round_to<TE>(act_fwd<TE, ACT>(uv));
+    st(h, i, hv);
+    dot = fmaf(z, hv, dot);
+    st(du, i, g * z * act_grad<ACT>(uv));
+  }
+  for (int c = threadIdx.x; c < d; c += 256) {
+    const float dv = ld(dy, t * d + c);
+    if (b2 != nullptr) dot = fmaf(dv, b2[static_cast<int64_t>(e) * d + c], dot);
+    st(dY, r * d + c, g * dv);
+  }
+  red[threadIdx.x] = dot;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dg_row[r] = red[0];
+}
+
+// one wave per token
+__global__ __launch_bounds__(256) void router_bwd_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ ids, const int32_t* __restrict__ row_of,
+    const float* __restrict__ dg_row, const int32_t* __restrict__ counts, int64_t T, int E, int k,
+    int renormalize, float aux_coef, float* __restrict__ ds, float* __restrict__ dsT) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* s = logits + t * E;
+  float mx = -__builtin_inff();
+  for (int i = lane; i < E; i += 64) mx = fmaxf(mx, s[i]);
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  float se = 0.f;
+  for (int i = lane; i < E; i += 64) se += __expf(s[i] - mx);
+  for (int off = 32; off >= 1; off >>= 1) se += __shfl_xor(se, off, 64);
+  const float inv = 1.0f / se;
+  // the token's chosen experts: probabilities, their sum, dg and sum dg g
+  float P = 0.f, dgg = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int i = ids[t * k + j];
+    P += __expf(s[i] - mx) * inv;
+  }
+  for (int j = 0; j < k; ++j) {
+    const int i = ids[t * k + j];
+    const int row = row_of[t * k + j];
+    const float dg = row >= 0 ? dg_row[row] : 0.f;
+    const float pj = __expf(s[i] - mx) * inv;
+    dgg += dg * (pj / P);
+  }
+  // dp_i and the softmax backward
+  float pdp = 0.f;
+  for (int i = lane; i < E; i += 64) {
+    const float p = __expf(s[i] - mx) * inv;
+    float dp = aux_coef * static_cast<float>(counts[i]);
+    for (int j = 0; j < k; ++j) {
+      if (ids[t * k + j] != i) continue;
+      const int row = row_of[t * k + j];
+      const float dg = row >= 0 ? dg_row[row] : 0.f;
+      dp += renormalize ? (dg - dgg) / P : dg;
+    }
+    pdp += p * dp;
+  }
+  for (int off = 32; off >= 1; off >>= 1) pdp += __shfl_xor(pdp, off, 64);
+  for (int i = lane; i < E; i += 64) {
+    const float p = __expf(s[i] - mx) * inv;
+    float dp = aux_coef * static_cast<float>(counts[i]);
+    for (int j = 0; j < k; ++j) {
+      if (ids[t * k + j] != i) continue;
+      const int row = row_of[t * k + j];
+      const float dg = row >= 0 ? dg_row[row] : 0.f;
+      dp += renormalize ? (dg - dgg) / P : dg;
+    }
+    const float v = p * (dp - pdp);
+    ds[t * E + i] = v;
+    dsT[static_cast<int64_t>(i) * T + t] = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void dx_gather_kernel(const float* __restrict__ dxp,
+                                                        const int32_t* __restrict__ row_of, int64_t T,
+                                                        int k, int d, float* __restrict__ dx) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= T * d) return;
+  const int64_t t = i / d;
+  const int c = static_cast<int>(i - t * d);
+  float acc = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int row = row_of[t * k + j];
+    if (row >= 0) acc += dxp[static_cast<int64_t>(row) * d + c];
+  }
+  dx[i] = acc;
+}
+
+// C[g][m][n] (+)= sum over rows r of group g of A[r][m] * B[src(r)][n]
+// (src(r) = b_rows[r] when given). Group g holds rows [offsets[g],
+// offsets[g+1]). 64x64 output tiles, 16 rows per step, 4x4 per thread.
+template <typename TA, typename TB>
+__global__ __launch_bounds__(256) void wgrad_kernel(const TA* __restrict__ A, const TB* __restrict__ B,
+                                                    const int32_t* __restrict__ b_rows,
+                                                    const int32_t* __restrict__ offsets, int M, int N,
+                                                    float* __restrict__ C, int accumulate) {
+  __shared__ float As[16][65];
+  __shared__ float Bs[16][65];
+  const int64_t g = blockIdx.z;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int r_begin = offsets[g], r_end = offsets[g + 1];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  for (int r0 = r_begin; r0 < r_end; r0 += 16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = threadIdx.x + q * 256;
+      const int rr = idx >> 6, cc = idx & 63;
+      const int r = r0 + rr;
+      const bool rv = r < r_end;
+      As[rr][cc] = (rv && m0 + cc < M) ? ld(A, static_cast<int64_t>(r) * M + m0 + cc) : 0.f;
+      const int64_t src = rv ? (b_rows != nullptr ? b_rows[r] : r) : 0;
+      Bs[rr][cc] = (rv && n0 + cc < N) ? ld(B, src * N + n0 + cc) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  float* Cg = C + g * static_cast<int64_t>(M) * N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty + 16 * i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx + 16 * j;
+      if (n >= N) continue;
+      const int64_t o = static_cast<int64_t>(m) * N + n;
+      Cg[o] = accumulate ? Cg[o] + acc[i][j] : acc[i][j];
+    }
+  }
+}
+
+// out[g][m] = sum over rows r of group g of A[r][m], rows in order
+template <typename TA>
+__global__ __launch_bounds__(256) void colsum_kernel(const TA* __restrict__ A,
+                                                     const int32_t* __restrict__ offsets, int M,
+                                                     float* __restrict__ out) {
+  const int64_t g = blockIdx.y;
+  const int m = blockIdx.x * 256 + threadIdx.x;
+  if (m >= M) return;
+  float acc = 0.f;
+  for (int r = offsets[g]; r < offsets[g + 1]; ++r) acc += ld(A, static_cast<int64_t>(r) * M + m);
+  out[g * M + m] = acc;
+}
+
+__global__ void range_kernel(int32_t* __restrict__ o, int32_t n) {
+  if (threadIdx.x == 0) {
+    o[0] = 0;
+    o[1] = n;
+  }
+}
+
+unsigned blocks(int64_t n, int per) { return static_cast<unsigned>((n + per - 1) / per); }
+
+}  // namespace
+
+hipError_t launch_transpose(const void* src, void* dst, int groups, int R, int Cc, bool bf16,
+                            hipStream_t s) {
+  dim3 grid(blocks(Cc, 64), blocks(R, 64), groups);
+  if (bf16)
+    transpose_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(src),
+                                                    static_cast<uint16_t*>(dst), R, Cc);
+  else
+    transpose_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(src),
+                                                 static_cast<float*>(dst), R, Cc);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_info(const int32_t* ids, const float* gates, const int32_t* row_of, int64_t T,
+                           int k, int32_t* row_expert, float* row_gate, hipStream_t s) {
+  row_info_kernel<<<blocks(T * k, 256), 256, 0, s>>>(ids, gates, row_of, T * k, row_expert,
+                                                      row_gate);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_rows(const float* u, const float* Z, const int32_t* row_token,
+                           const float* row_gate, const int32_t* row_expert, const int32_t* offsets,
+                           int E, const void* dy, const float* b2, int d, int d_ff, int64_t max_rows,
+                           bool bf16, int act, void* h, void* du, void* dY, float* dg_row,
+                           hipStream_t s) {
+  if (max_rows <= 0) return hipSuccess;
+  const unsigned grid = static_cast<unsigned>(max_rows);
+#define MOE_BWD_ROWS(TE, ACT)                                                                        \
+  bwd_rows_kernel<TE, ACT><<<grid, 256, 0, s>>>(u, Z, row_token, row_gate, row_expert, offsets, E, \
+                                                static_cast<const TE*>(dy), b2, d, d_ff,          \
+                                                static_cast<TE*>(h), static_cast<TE*>(du),        \
+                                                static_cast<TE*>(dY), dg_row)
+  if (bf16) {
+    if (act == kActRelu) MOE_BWD_ROWS(uint16_t, kActRelu);
+    else MOE_BWD_ROWS(uint16_t, kActGeluTanh);
+  } else {
+    if (act == kActRelu) MOE_BWD_ROWS(float, kActRelu);
+    else MOE_BWD_ROWS(float, kActGeluTanh);
+  }
+#undef MOE_BWD_ROWS
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const float* logits, const int32_t* ids, const int32_t* row_of,
+                             const float* dg_row, const int32_t* counts, int64_t T, int E, int k,
+                             int renormalize, float aux_coef, float* ds, float* dsT, hipStream_t s) {
+  router_bwd_kernel<<<blocks(T, 4), 256, 0, s>>>(logits, ids, row_of, dg_row, counts, T, E, k,
+                                                  renormalize, aux_coef, ds, dsT);
+  return hipGetLastError();
+}
+
+hipError_t launch_dx_gather(const float* dxp, const int32_t* row_of, int64_t T, int k, int d,
+                            float* dx, hipStream_t s) {
+  dx_gather_kernel<<<blocks(T * d, 256), 256, 0, s>>>(dxp, row_of, T, k, d, dx);
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad(const void* A, bool a_bf16, const void* B, bool b_bf16, const int32_t* b_rows,
+                        const int32_t* offsets, int groups, int M, int N, float* C, bool accumulate,
+                        hipStream_t s) {
+  dim3 grid(blocks(N, 64), blocks(M, 64), groups);
+  const int acc = accumulate ? 1 : 0;
+  if (a_bf16 && b_bf16)
+    wgrad_kernel<uint16_t, uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(A),
+                                                          static_cast<const uint16_t*>(B), b_rows,
+                                                          offsets, M, N, C, acc);
+  else if (!a_bf16 && b_bf16)
+    wgrad_kernel<float, uint16_t><<<grid, 256, 0, s>>>(static_cast<const float*>(A),
+                                                       static_cast<const uint16_t*>(B), b_rows,
+                                                       offsets, M, N, C, acc);
+  else if (a_bf16 && !b_bf16)
+    wgrad_kernel<uint16_t, float><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(A),
+                                                       static_cast<const float*>(B), b_rows,
+                                                       offsets, M, N, C, acc);
+  else
+    wgrad_kernel<float, float><<<grid, 256, 0, s>>>(static_cast<const float*>(A),
+                                                    static_cast<const float*>(B), b_rows, offsets,
+                                                    M, N, C, acc);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum(const void* A, bool bf16, const int32_t* offsets, int groups, int M,
+                         float* out, hipStream_t s) {
+  dim3 grid(blocks(M, 256), groups);
+  if (bf16)
+    colsum_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(A), offsets, M, out);
+  else
+    colsum_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(A), offsets, M, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_range(int32_t* o, int32_t n, hipStream_t s) {
+  range_kernel<<<1, 64, 0, s>>>(o, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -146,21 +146,10 @@ __device__ __forceinline__ void issue_bias(const float* gsrc, uint32_t lds_dst) 
 #pragma clang diagnostic pop
 }
 
-// tanh-GELU as u * sigmoid(2z), z = sqrt(2/pi) (u + 0.044715 u^3), with the
-// hardware base-2 exponential and reciprocal (about 1 ulp each; the result is
-// rounded to bf16 afterwards).
-__device__ __forceinline__ float gelu_fast(float u) {
-  // exp(-2z) = 2^x with x = u * (c0 + c1 u^2)
-  constexpr float c0 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
-  constexpr float c1 = c0 * 0.044715f;
-  const float x = u * fmaf(c1, u * u, c0);
-  return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
-}
-
 template <int ACT>
 __device__ __forceinline__ float activate(float v) {
   if constexpr (ACT == kActRelu) return v > 0.f ? v : 0.f;
-  else if constexpr (ACT == kActGeluTanh) return gelu_fast(v);
+  else if constexpr (ACT == kActGeluTanh) return act_gelu_tanh_fast(v);
   else return v;
 }
 

@@ -112,6 +112,45 @@ Layout layout_of(const moe_config& c) {
   return L;
 }
 
+// workspace of moe_layer_backward
+struct BwdLayout {
+  size_t logits, W1t, W2t, x_perm, dy_perm, u, Z, h, du, dY, dxp, row_expert, row_gate, dg_row, ds,
+      dsT, range_T, range_E, total;
+};
+
+BwdLayout bwd_layout_of(const moe_config& c) {
+  BwdLayout L{};
+  size_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const size_t o = off;
+    off += round_up(static_cast<size_t>(bytes > 0 ? bytes : 0));
+    return o;
+  };
+  const int64_t T = c.T, E = c.E, R = max_rows_of(c), d = c.d, f = c.d_ff;
+  const int es = elem_size(c);
+  const bool gather = layer_gathers(c);
+  L.logits = take(T * E * 4);
+  L.W1t = take(E * d * f * es);
+  L.W2t = take(E * d * f * es);
+  L.x_perm = take(gather ? 0 : R * d * es);
+  L.dy_perm = take(gather ? 0 : R * d * es);
+  L.u = take(R * f * 4);
+  L.Z = take(R * f * 4);
+  L.h = take(R * f * es);
+  L.du = take(R * f * es);
+  L.dY = take(R * d * es);
+  L.dxp = take(R * d * 4);
+  L.row_expert = take(R * 4);
+  L.row_gate = take(R * 4);
+  L.dg_row = take(R * 4);
+  L.ds = take(T * E * 4);
+  L.dsT = take(T * E * 4);
+  L.range_T = take(8);
+  L.range_E = take(8);
+  L.total = off;
+  return L;
+}
+
 template <typename T>
 T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
@@ -428,6 +467,127 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* x, const void* W_r,
   MOE_TRY(mark(4));
   MOE_TRY(combine_stage(c, y_perm, row_of, cgates, y, stream));
   return mark(5);
+}
+
+int32_t moe_backward_workspace_size(const moe_config* cfg, size_t* bytes) {
+  MOE_TRY(check_cfg(cfg));
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  *bytes = bwd_layout_of(*cfg).total;
+  return MOE_OK;
+}
+
+int32_t moe_layer_backward(const moe_config* cfg, const void* x, const void* W_r, const float* b_r,
+                           const void* W1, const float* b1, const void* W2, const float* b2,
+                           const moe_route_info* fwd, const void* dy, float aux_alpha, float* dx,
+                           float* dW_r, float* db_r, float* dW1, float* db1, float* dW2, float* db2,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_config& c = *cfg;
+  if (c.reroute != 0) return MOE_ERR_UNSUPPORTED;
+  if (c.T == 0) return MOE_OK;
+  if (x == nullptr || W_r == nullptr || W1 == nullptr || W2 == nullptr || fwd == nullptr ||
+      dy == nullptr || dx == nullptr || dW_r == nullptr || dW1 == nullptr || dW2 == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  const moe_route_info& f = *fwd;
+  if (f.topk_ids == nullptr || f.topk_gates == nullptr || f.expert_counts == nullptr ||
+      f.expert_offsets == nullptr || f.row_of == nullptr || f.row_token == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(aux_alpha)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(W_r, 16) || !aligned(W1, 16) || !aligned(W2, 16) ||
+      !aligned(dy, 16) || !aligned(b_r, 4) || !aligned(b1, 16) || !aligned(b2, 16) ||
+      !aligned(dx, 4) || !aligned(dW_r, 4) || !aligned(db_r, 4) || !aligned(dW1, 4) ||
+      !aligned(db1, 4) || !aligned(dW2, 4) || !aligned(db2, 4) || !aligned(f.topk_ids, 4) ||
+      !aligned(f.topk_gates, 4) || !aligned(f.expert_counts, 4) || !aligned(f.expert_offsets, 4) ||
+      !aligned(f.row_of, 4) || !aligned(f.row_token, 4))
+    return MOE_ERR_INVALID_ARG;
+  const BwdLayout L = bwd_layout_of(c);
+  if (ws == nullptr || !aligned(ws, kAlign) || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+
+  hipStream_t s = stream;
+  const bool bf = c.dtype == MOE_BF16;
+  const int es = elem_size(c);
+  const int64_t R = max_rows_of(c);
+  const int per_expert = static_cast<int>(c.T < c.capacity ? c.T : c.capacity);
+  const int32_t* offsets = f.expert_offsets;
+  const int32_t* row_token = f.row_token;
+  float* logits = at<float>(ws, L.logits);
+  void* W1t = at<char>(ws, L.W1t);
+  void* W2t = at<char>(ws, L.W2t);
+  float* u = at<float>(ws, L.u);
+  float* Z = at<float>(ws, L.Z);
+  void* h = at<char>(ws, L.h);
+  void* du = at<char>(ws, L.du);
+  void* dY = at<char>(ws, L.dY);
+  float* dxp = at<float>(ws, L.dxp);
+  int32_t* row_expert = at<int32_t>(ws, L.row_expert);
+  float* row_gate = at<float>(ws, L.row_gate);
+  float* dg_row = at<float>(ws, L.dg_row);
+  float* ds = at<float>(ws, L.ds);
+  float* dsT = at<float>(ws, L.dsT);
+  int32_t* range_T = at<int32_t>(ws, L.range_T);
+  int32_t* range_E = at<int32_t>(ws, L.range_E);
+
+  // router logits again (the probabilities of every expert are needed)
+  if (bf)
+    MOE_HIP(launch_logits_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W_r), b_r,
+                               logits, c.T, c.d, c.E, s));
+  else
+    MOE_HIP(launch_logits_f32(static_cast<const float*>(x), static_cast<const float*>(W_r), b_r,
+                              logits, c.T, c.d, c.E, s));
+  // transposed expert weights for the dgrad GEMMs: W1t[e] [d, d_ff], W2t[e] [d_ff, d]
+  MOE_HIP(launch_transpose(W1, W1t, c.E, c.d_ff, c.d, bf, s));
+  MOE_HIP(launch_transpose(W2, W2t, c.E, c.d, c.d_ff, bf, s));
+  // token rows of x and dy for the kept rows (read through row_token, or copied)
+  const bool gather = layer_gathers(c);
+  const void* xa = x;
+  const void* dya = dy;
+  const int32_t* ridx = row_token;
+  if (!gather) {
+    MOE_HIP(launch_gather_rows(x, row_token, offsets, c.E, R, c.d * es, at<char>(ws, L.x_perm), s));
+    MOE_HIP(launch_gather_rows(dy, row_token, offsets, c.E, R, c.d * es, at<char>(ws, L.dy_perm), s));
+    xa = at<char>(ws, L.x_perm);
+    dya = at<char>(ws, L.dy_perm);
+    ridx = nullptr;
+  }
+  // u = x W1_e^T + b1_e (pre-activation, fp32); Z = dy W2_e (fp32)
+  if (bf) {
+    MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(xa), ridx, static_cast<const uint16_t*>(W1), b1,
+                             u, true, kActNone, offsets, c.E, c.d_ff, c.d, R, per_expert, s));
+    MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(dya), ridx, static_cast<const uint16_t*>(W2t),
+                             nullptr, Z, true, kActNone, offsets, c.E, c.d_ff, c.d, R, per_expert, s));
+  } else {
+    MOE_HIP(launch_gemm_f32(static_cast<const float*>(xa), ridx, static_cast<const float*>(W1), b1, u,
+                            kActNone, offsets, c.E, c.d_ff, c.d, per_expert, s));
+    MOE_HIP(launch_gemm_f32(static_cast<const float*>(dya), ridx, static_cast<const float*>(W2t), nullptr,
+                            Z, kActNone, offsets, c.E, c.d_ff, c.d, per_expert, s));
+  }
+  // per row: h, du, dY and the combine-weight gradient
+  MOE_HIP(launch_row_info(f.topk_ids, f.topk_gates, f.row_of, c.T, c.k, row_expert, row_gate, s));
+  MOE_HIP(launch_bwd_rows(u, Z, row_token, row_gate, row_expert, offsets, c.E, dy, b2, c.d, c.d_ff, R,
+                          bf, c.act, h, du, dY, dg_row, s));
+  // dx_perm = du W1_e
+  if (bf)
+    MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(du), nullptr, static_cast<const uint16_t*>(W1t),
+                             nullptr, dxp, true, kActNone, offsets, c.E, c.d, c.d_ff, R, per_expert, s));
+  else
+    MOE_HIP(launch_gemm_f32(static_cast<const float*>(du), nullptr, static_cast<const float*>(W1t), nullptr,
+                            dxp, kActNone, offsets, c.E, c.d, c.d_ff, per_expert, s));
+  // expert weight and bias gradients
+  MOE_HIP(launch_wgrad(du, bf, x, bf, row_token, offsets, c.E, c.d_ff, c.d, dW1, false, s));
+  MOE_HIP(launch_wgrad(dY, bf, h, bf, nullptr, offsets, c.E, c.d, c.d_ff, dW2, false, s));
+  if (db1 != nullptr) MOE_HIP(launch_colsum(du, bf, offsets, c.E, c.d_ff, db1, s));
+  if (db2 != nullptr) MOE_HIP(launch_colsum(dY, bf, offsets, c.E, c.d, db2, s));
+  // router: ds, then dW_r = ds^T x, db_r, and dx = gathered dx_perm + ds W_r
+  const double aux = static_cast<double>(aux_alpha) * c.E / (static_cast<double>(c.T) * c.T);
+  MOE_HIP(launch_router_bwd(logits, f.topk_ids, f.row_of, dg_row, f.expert_counts, c.T, c.E, c.k,
+                            c.renormalize, static_cast<float>(aux), ds, dsT, s));
+  MOE_HIP(launch_range(range_T, static_cast<int32_t>(c.T), s));
+  MOE_HIP(launch_range(range_E, c.E, s));
+  MOE_HIP(launch_wgrad(ds, false, x, bf, nullptr, range_T, 1, c.E, c.d, dW_r, false, s));
+  if (db_r != nullptr) MOE_HIP(launch_colsum(ds, false, range_T, 1, c.E, db_r, s));
+  MOE_HIP(launch_dx_gather(dxp, f.row_of, c.T, c.k, c.d, dx, s));
+  MOE_HIP(launch_wgrad(dsT, false, W_r, bf, nullptr, range_E, 1, static_cast<int>(c.T), c.d, dx, true, s));
+  return MOE_OK;
 }
 
 const char* moe_status_string(int32_t status) {

@@ -38,6 +38,17 @@ __device__ __forceinline__ float act_gelu_tanh(float u) {
   return u / (1.0f + __expf(-2.0f * z));
 }
 
+// tanh-GELU of the bf16 expert GEMM epilogue: u * sigmoid(2z) with the
+// hardware base-2 exponential and reciprocal (about 1 ulp each; the result is
+// rounded to bf16 afterwards). The backward pass recomputes h with it.
+__device__ __forceinline__ float act_gelu_tanh_fast(float u) {
+  // exp(-2z) = 2^x with x = u * (c0 + c1 u^2)
+  constexpr float c0 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+  constexpr float c1 = c0 * 0.044715f;
+  const float x = u * fmaf(c1, u * u, c0);
+  return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
+}
+
 // ---------------------------------------------------------------- launchers
 // Each returns the first HIP error of its launches (hipSuccess if none).
 
@@ -96,6 +107,37 @@ hipError_t launch_dispatch_reroute(const void* x, const int32_t* cand, const flo
                                    int32_t* counts, int32_t* offsets, int32_t* slot,
                                    int32_t* row_of, int32_t* row_token, int32_t* served_ids,
                                    float* combine_gates, void* x_perm, hipStream_t s);
+
+// ---- backward (backward.hip)
+// dst[g] = src[g]^T for groups of [R, Cc] matrices (2- or 4-byte elements)
+hipError_t launch_transpose(const void* src, void* dst, int groups, int R, int Cc, bool bf16,
+                            hipStream_t s);
+// row_expert[row_of[a]] = ids[a], row_gate[row_of[a]] = gates[a] for kept a
+hipError_t launch_row_info(const int32_t* ids, const float* gates, const int32_t* row_of, int64_t T,
+                           int k, int32_t* row_expert, float* row_gate, hipStream_t s);
+// per kept row: h = sigma(u) rounded as the forward, du = g Z sigma'(u),
+// dY = g dy_t, dg_row = <Z, h> + <dy_t, b2_e>
+hipError_t launch_bwd_rows(const float* u, const float* Z, const int32_t* row_token,
+                           const float* row_gate, const int32_t* row_expert, const int32_t* offsets,
+                           int E, const void* dy, const float* b2, int d, int d_ff, int64_t max_rows,
+                           bool bf16, int act, void* h, void* du, void* dY, float* dg_row,
+                           hipStream_t s);
+// ds [T,E] and dsT [E,T]: softmax backward of dp (gates and L_aux terms)
+hipError_t launch_router_bwd(const float* logits, const int32_t* ids, const int32_t* row_of,
+                             const float* dg_row, const int32_t* counts, int64_t T, int E, int k,
+                             int renormalize, float aux_coef, float* ds, float* dsT, hipStream_t s);
+// dx[t] = sum over kept j of dxp[row_of[t,j]]
+hipError_t launch_dx_gather(const float* dxp, const int32_t* row_of, int64_t T, int k, int d,
+                            float* dx, hipStream_t s);
+// C[g] (+)= A_g^T B_g over the rows [offsets[g], offsets[g+1]); B rows through b_rows
+hipError_t launch_wgrad(const void* A, bool a_bf16, const void* B, bool b_bf16, const int32_t* b_rows,
+                        const int32_t* offsets, int groups, int M, int N, float* C, bool accumulate,
+                        hipStream_t s);
+// out[g][m] = sum over the rows of group g of A[r][m]
+hipError_t launch_colsum(const void* A, bool bf16, const int32_t* offsets, int groups, int M,
+                         float* out, hipStream_t s);
+// o = {0, n}
+hipError_t launch_range(int32_t* o, int32_t n, hipStream_t s);
 
 // x_perm[r] = x[row_token[r]] for r < offsets[E] (rows bounded by max_rows)
 hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int32_t* offsets,

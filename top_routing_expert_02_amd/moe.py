@@ -26,7 +26,8 @@ STAGE_NAMES = ["route", "dispatch", "gemm1", "gemm2", "combine"]
 
 EXPORTED = ["moe_capacity", "moe_candidates", "moe_max_rows", "moe_workspace_size", "moe_route",
             "moe_dispatch", "moe_dispatch_reroute", "moe_expert_ffn", "moe_combine",
-            "moe_layer_forward", "moe_status_string"]
+            "moe_layer_forward", "moe_backward_workspace_size", "moe_layer_backward",
+            "moe_status_string"]
 
 
 class MoeError(RuntimeError):
@@ -73,6 +74,9 @@ def lib():
         L.moe_combine.argtypes = [CFG, P, P, P, P, P]
         L.moe_layer_forward.argtypes = [CFG, P, P, P, P, P, P, P, P, ctypes.POINTER(MoeRouteInfo),
                                         P, SZ, P, P]
+        L.moe_backward_workspace_size.argtypes = [CFG, ctypes.POINTER(SZ)]
+        L.moe_layer_backward.argtypes = [CFG, P, P, P, P, P, P, P, ctypes.POINTER(MoeRouteInfo), P,
+                                         ctypes.c_float, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_status_string.argtypes = [I32]
         L.moe_status_string.restype = ctypes.c_char_p
         for n in EXPORTED[:-1]:
@@ -195,6 +199,28 @@ def layer_forward(cfg, x, W_r, b_r, W1, b1, W2, b2, y, info: dict | None = None,
         ctypes.byref(cfg), _ptr(x), _ptr(W_r), _ptr(b_r), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
         _ptr(y), ctypes.byref(ri) if ri is not None else None, _ptr(ws), ws.numel(), ev,
         _stream(stream)))
+
+
+def backward_workspace_size(cfg: MoeConfig) -> int:
+    out = ctypes.c_size_t(0)
+    _check("moe_backward_workspace_size",
+           lib().moe_backward_workspace_size(ctypes.byref(cfg), ctypes.byref(out)))
+    return out.value
+
+
+def layer_backward(cfg, x, W_r, b_r, W1, b1, W2, b2, fwd: dict, dy, aux_alpha, grads: dict,
+                   ws=None, stream=None):
+    """fwd: the forward's routing outputs (topk_ids, topk_gates, expert_counts,
+    expert_offsets, row_of, row_token). grads: output tensors dx, dW_r, dW1,
+    dW2 and optionally db_r, db1, db2."""
+    if ws is None:
+        ws = torch.empty(max(1, backward_workspace_size(cfg)), dtype=torch.uint8, device=x.device)
+    ri = MoeRouteInfo(**{k: _ptr(v) for k, v in fwd.items()})
+    gp = {k: _ptr(grads.get(k)) for k in ("dx", "dW_r", "db_r", "dW1", "db1", "dW2", "db2")}
+    _check("moe_layer_backward", lib().moe_layer_backward(
+        ctypes.byref(cfg), _ptr(x), _ptr(W_r), _ptr(b_r), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
+        ctypes.byref(ri), _ptr(dy), float(aux_alpha), gp["dx"], gp["dW_r"], gp["db_r"], gp["dW1"],
+        gp["db1"], gp["dW2"], gp["db2"], _ptr(ws), ws.numel(), _stream(stream)))
 
 
 # ------------------------------------------------------------------ HIP events (timing)

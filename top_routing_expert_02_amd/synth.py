@@ -49,7 +49,7 @@ import torch
 
 MAGIC = 0x4D6F45
 
-TENSOR_IDS = {"x": 1, "W_r": 2, "b_r": 3, "W1": 4, "b1": 5, "W2": 6, "b2": 7}
+TENSOR_IDS = {"x": 1, "W_r": 2, "b_r": 3, "W1": 4, "b1": 5, "W2": 6, "b2": 7, "dy": 8}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -123,6 +123,13 @@ def _normal(shape, var, device, gen, out_dtype):
 
 def make_x(w: Workload, device, seed: int = 0) -> torch.Tensor:
     g = _gen(device, w.seed_id, TENSOR_IDS["x"], 0, seed)
+    return _normal((w.T, w.d), 1.0, device, g, w.torch_dtype)
+
+
+def make_dy(w: Workload, device, seed: int = 0) -> torch.Tensor:
+    """Upstream gradient dL/dy [T, d] ~ N(0, 1) in the workload dtype, for the
+    backward pass."""
+    g = _gen(device, w.seed_id, TENSOR_IDS["dy"], 0, seed)
     return _normal((w.T, w.d), 1.0, device, g, w.torch_dtype)
 
 
