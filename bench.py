@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=30.0,
                     help="upper bound on the oracle's CPU time for the baseline leg")
+    ap.add_argument("--backward", action="store_true",
+                    help="time a training step instead: the layer forward, then its backward "
+                         "(gradients of x and every parameter, L_aux coefficient 0.01)")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="after the timed steps, this many extra steps each preceded by a 1 GiB "
                          "write that evicts L2 and the MALL (reported as 'cold', not as value)")
@@ -166,12 +169,105 @@ def cpu_baseline(w, inp, C, budget_s):
             "sample": f"{w.name}: {sample}; fp64 numpy; {est:.2f} s per layer"}
 
 
+def main_backward(args):
+    """A training step: moe_layer_forward, then moe_layer_backward with the
+    forward's routing outputs (gradients of x and every parameter)."""
+    import numpy as np
+    import torch
+    from top_routing_expert_02_amd import moe, synth
+    moe.lib()
+    w = synth.WORKLOADS[args.workload]
+    if w.reroute > 0:
+        print("the backward pass does not cover re-routing", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda"
+    log(f"[bench] {w.name}: generating inputs (training step)")
+    inp = synth.make_inputs(w, dev, seed=0)
+    dy = synth.make_dy(w, dev, seed=0)
+    C = w.T if w.dropless else moe.capacity(w.T, w.k, w.E, w.c)
+    cfg = moe.config(w.T, w.d, w.d_ff, w.E, w.k, C, w.renormalize, w.dtype, w.act,
+                     priority=w.priority, reroute=w.reroute)
+    R = moe.max_rows(cfg)
+    ws = moe.alloc_workspace(cfg, dev)
+    bws = torch.empty(moe.backward_workspace_size(cfg), dtype=torch.uint8, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    info = {"topk_ids": torch.empty((w.T, w.k), **i32), "topk_gates": torch.empty((w.T, w.k), **f32),
+            "expert_counts": torch.empty(w.E, **i32), "expert_offsets": torch.empty(w.E + 1, **i32),
+            "row_of": torch.empty((w.T, w.k), **i32), "row_token": torch.empty(max(R, 1), **i32)}
+    y = torch.empty((w.T, w.d), dtype=w.torch_dtype, device=dev)
+    grads = {"dx": torch.empty((w.T, w.d), **f32), "dW_r": torch.empty((w.E, w.d), **f32),
+             "db_r": torch.empty(w.E, **f32), "dW1": torch.empty((w.E, w.d_ff, w.d), **f32),
+             "db1": torch.empty((w.E, w.d_ff), **f32), "dW2": torch.empty((w.E, w.d, w.d_ff), **f32),
+             "db2": torch.empty((w.E, w.d), **f32)}
+    alpha = 0.01
+    stream = torch.cuda.current_stream()
+
+    def step(fev=None, bev=None):
+        moe.layer_forward(cfg, inp["x"], inp["W_r"], inp["b_r"], inp["W1"], inp["b1"], inp["W2"],
+                          inp["b2"], y, info=info, ws=ws, stage_events=fev)
+        moe.layer_backward(cfg, inp["x"], inp["W_r"], inp["b_r"], inp["W1"], inp["b1"], inp["W2"],
+                           inp["b2"], info, dy, alpha, grads, ws=bws, stage_events=bev)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    offsets = info["expert_offsets"].cpu().numpy()
+    rows = int(offsets[-1])
+    K = args.steps
+    fev = [moe.HipEvents(moe.MOE_NUM_STAGES + 1) for _ in range(K)]
+    bev = [moe.HipEvents(moe.MOE_BWD_NUM_STAGES + 1) for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        step(fev[i], bev[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / K
+    stage_ms = {n: float(np.mean([e.elapsed_ms(s, s + 1) for e in fev]))
+                for s, n in enumerate(moe.STAGE_NAMES)}
+    stage_ms.update({"bwd_" + n: float(np.mean([e.elapsed_ms(s, s + 1) for e in bev]))
+                     for s, n in enumerate(moe.BWD_STAGE_NAMES)})
+    fwd_ms = float(np.mean([e.elapsed_ms(0, moe.MOE_NUM_STAGES) for e in fev]))
+    bwd_ms = float(np.mean([e.elapsed_ms(0, moe.MOE_BWD_NUM_STAGES) for e in bev]))
+    for e in fev + bev:
+        e.close()
+    log(f"[bench] {K} training steps: {ms:.4f} ms/step (forward {fwd_ms:.4f}, backward "
+        f"{bwd_ms:.4f}); stages {stage_ms}")
+    rdf = 2 * rows * w.d * w.d_ff  # one grouped expert GEMM
+    flops = {"gemm1": rdf, "gemm2": rdf, "bwd_recompute": 2 * rdf + 2 * w.T * w.d * w.E,
+             "bwd_dgrad": rdf, "bwd_wgrad": 2 * rdf, "bwd_router": 4 * w.T * w.d * w.E}
+    stages = {}
+    for n, t in stage_ms.items():
+        st = {"ms": round(t, 5)}
+        if flops.get(n):
+            st["flops"] = flops[n]
+            st["TFLOP_s"] = flops[n] / (t * 1e-3) / 1e12
+        stages[n] = st
+    dom = "bwd_wgrad"
+    roofline = {"bound": "alu", "kernel": "wgrad_kernel (dW1 and dW2: fp32 FMA)",
+                "achieved": stages[dom]["TFLOP_s"], "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+                "frac": stages[dom]["TFLOP_s"] / PEAK_F32_TFLOPS, "traffic": None}
+    out = {"metric": "MoE-layer training step (forward + backward) tokens/sec", "value": w.T / (ms * 1e-3),
+           "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+           "data": "synthetic",
+           "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "E": w.E, "k": w.k,
+                      "C": C, "rows": rows, "aux_alpha": alpha, "parallelism": "none"},
+           "forward_ms": fwd_ms, "backward_ms": bwd_ms, "roofline": roofline, "stages": stages}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "the layer has no multi-GPU path in this library", file=sys.stderr)
         sys.exit(2)
+    if args.backward:
+        return main_backward(args)
     import numpy as np
     import torch
     from top_routing_expert_02_amd import moe, synth

@@ -264,6 +264,16 @@ int32_t moe_layer_forward(const moe_config *cfg, const void *x, const void *W_r,
                           const float *b2, void *y, const moe_route_info *info, void *ws,
                           size_t ws_bytes, hipEvent_t *stage_events, hipStream_t stream);
 
+/* Stage boundaries for moe_layer_backward's optional events. */
+enum {
+  MOE_BWD_STAGE_RECOMPUTE = 0, /* logits, transposed weights, u = x W1^T + b1, Z = dy W2 */
+  MOE_BWD_STAGE_ROWS = 1,      /* per-row h, du, dY and combine-weight gradients */
+  MOE_BWD_STAGE_DGRAD = 2,     /* dx_perm = du W1_e, grouped */
+  MOE_BWD_STAGE_WGRAD = 3,     /* dW1, dW2, db1, db2 */
+  MOE_BWD_STAGE_ROUTER = 4,    /* softmax/L_aux backward, dW_r, db_r, dx */
+  MOE_BWD_NUM_STAGES = 5
+};
+
 /* Workspace bytes moe_layer_backward needs (host only). */
 int32_t moe_backward_workspace_size(const moe_config *cfg, size_t *bytes);
 
@@ -290,13 +300,15 @@ int32_t moe_backward_workspace_size(const moe_config *cfg, size_t *bytes);
  *   out dx [T,d], dW_r [E,d], dW1 [E,d_ff,d], dW2 [E,d,d_ff] fp32 (required);
  *       db_r [E], db1 [E,d_ff], db2 [E,d] fp32 or NULL (not computed).
  *   ws: at least moe_backward_workspace_size bytes, 256-byte aligned.
+ *   stage_events: NULL, or MOE_BWD_NUM_STAGES+1 caller-created hipEvents
+ *   recorded on `stream` before the first stage and after each stage.
  * Errors as the forward; cfg->reroute != 0 gives MOE_ERR_UNSUPPORTED.
  */
 int32_t moe_layer_backward(const moe_config *cfg, const void *x, const void *W_r, const float *b_r,
                            const void *W1, const float *b1, const void *W2, const float *b2,
                            const moe_route_info *fwd, const void *dy, float aux_alpha, float *dx,
                            float *dW_r, float *db_r, float *dW1, float *db1, float *dW2, float *db2,
-                           void *ws, size_t ws_bytes, hipStream_t stream);
+                           void *ws, size_t ws_bytes, hipEvent_t *stage_events, hipStream_t stream);
 
 /* A static string naming a status code. */
 const char *moe_status_string(int32_t status);

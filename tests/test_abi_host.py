@@ -156,7 +156,7 @@ def test_backward_rejects_without_launching(m):
     info = m.MoeRouteInfo(*([0x100000] * 10))
     args = lambda c, ws_n: (ctypes.byref(c), fake, fake, None, fake, None, fake, None,
                             ctypes.byref(info), fake, ctypes.c_float(0.0), fake, fake, None, fake,
-                            None, fake, None, fake, ws_n, None)
+                            None, fake, None, fake, ws_n, None, None)
     # re-routing has no backward
     rr = good_cfg(m, reroute=1)
     assert L.moe_layer_backward(*args(rr, m.backward_workspace_size(rr))) == -2
@@ -175,7 +175,7 @@ def test_backward_rejects_without_launching(m):
     empty = good_cfg(m, T=0)
     assert L.moe_layer_backward(ctypes.byref(empty), None, None, None, None, None, None, None, None,
                                 None, ctypes.c_float(0.0), None, None, None, None, None, None, None,
-                                None, 0, None) == 0
+                                None, 0, None, None) == 0
 
 
 def test_status_strings(m):

@@ -17,8 +17,10 @@
 //                    backward), in [T,E] and [E,T] layouts
 //   dx_gather        dx_t = sum over kept j of dx_perm[row_of[t,j]]
 //   wgrad            C[g] (+)= A_g^T B_g over the rows of group g (fp32
-//                    accumulate, 64x64 tiles): dW1, dW2, dW_r and ds W_r
-//   colsum           per group, column sums over its rows: db1, db2, db_r
+//                    accumulate, 64x64 tiles, optional split over rows with
+//                    an in-order reduction), and the column sums of A_g as
+//                    one extra column of ones: dW1/db1, dW2/db2, dW_r/db_r,
+//                    and ds W_r
 // Every reduction runs in a fixed order: results are deterministic.
 #include "moe_internal.h"
 
@@ -217,16 +219,27 @@ __global__ __launch_bounds__(256) void dx_gather_kernel(const float* __restrict_
 // C[g][m][n] (+)= sum over rows r of group g of A[r][m] * B[src(r)][n]
 // (src(r) = b_rows[r] when given). Group g holds rows [offsets[g],
 // offsets[g+1]). 64x64 output tiles, 16 rows per step, 4x4 per thread.
+// With dbias, column N is a column of ones: dbias[g][m] = sum_r A[r][m].
+// With splits > 1, block z = g * splits + s takes the s-th slice of the
+// group's rows and writes its partial sums to part[z] ([M, N+1]); a second
+// kernel adds the slices in order.
 template <typename TA, typename TB>
 __global__ __launch_bounds__(256) void wgrad_kernel(const TA* __restrict__ A, const TB* __restrict__ B,
                                                     const int32_t* __restrict__ b_rows,
                                                     const int32_t* __restrict__ offsets, int M, int N,
-                                                    float* __restrict__ C, int accumulate) {
+                                                    int splits, float* __restrict__ C,
+                                                    float* __restrict__ dbias, int accumulate,
+                                                    float* __restrict__ part) {
   __shared__ float As[16][65];
   __shared__ float Bs[16][65];
-  const int64_t g = blockIdx.z;
+  const int64_t g = blockIdx.z / splits;
+  const int sp = blockIdx.z - static_cast<int>(g) * splits;
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
-  const int r_begin = offsets[g], r_end = offsets[g + 1];
+  const int g_begin = offsets[g], g_end = offsets[g + 1];
+  const int chunk = ((g_end - g_begin + splits - 1) / splits + 15) & ~15;
+  const int r_begin = min(g_end, g_begin + sp * chunk);
+  const int r_end = min(g_end, r_begin + chunk);
+  const int NB = dbias != nullptr ? N + 1 : N;  // columns incl. the ones column
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   float acc[4][4];
 #pragma unroll
@@ -241,8 +254,15 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const TA* __restrict__ A, co
       const int r = r0 + rr;
       const bool rv = r < r_end;
       As[rr][cc] = (rv && m0 + cc < M) ? ld(A, static_cast<int64_t>(r) * M + m0 + cc) : 0.f;
-      const int64_t src = rv ? (b_rows != nullptr ? b_rows[r] : r) : 0;
-      Bs[rr][cc] = (rv && n0 + cc < N) ? ld(B, src * N + n0 + cc) : 0.f;
+      const int n = n0 + cc;
+      float bv = 0.f;
+      if (rv && n < N) {
+        const int64_t src = b_rows != nullptr ? b_rows[r] : r;
+        bv = ld(B, src * N + n);
+      } else if (rv && n == N) {
+        bv = 1.f;  // the ones column (only reached when dbias is given: NB = N + 1)
+      }
+      Bs[rr][cc] = bv;
     }
     __syncthreads();
 #pragma unroll
@@ -259,7 +279,6 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const TA* __restrict__ A, co
     }
     __syncthreads();
   }
-  float* Cg = C + g * static_cast<int64_t>(M) * N;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + ty + 16 * i;
@@ -267,24 +286,40 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const TA* __restrict__ A, co
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = n0 + tx + 16 * j;
-      if (n >= N) continue;
-      const int64_t o = static_cast<int64_t>(m) * N + n;
-      Cg[o] = accumulate ? Cg[o] + acc[i][j] : acc[i][j];
+      if (n >= NB) continue;
+      if (splits > 1) {
+        part[(static_cast<int64_t>(blockIdx.z) * M + m) * NB + n] = acc[i][j];
+      } else if (n < N) {
+        const int64_t o = (g * M + m) * static_cast<int64_t>(N) + n;
+        C[o] = accumulate ? C[o] + acc[i][j] : acc[i][j];
+      } else {
+        dbias[g * M + m] = acc[i][j];
+      }
     }
   }
 }
 
-// out[g][m] = sum over rows r of group g of A[r][m], rows in order
-template <typename TA>
-__global__ __launch_bounds__(256) void colsum_kernel(const TA* __restrict__ A,
-                                                     const int32_t* __restrict__ offsets, int M,
-                                                     float* __restrict__ out) {
-  const int64_t g = blockIdx.y;
-  const int m = blockIdx.x * 256 + threadIdx.x;
-  if (m >= M) return;
+// C[g][m][n] (+)= sum over s of part[g*splits+s][m][n], s in order; column N
+// of the partials (when present) goes to dbias.
+__global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restrict__ part, int groups,
+                                                           int splits, int M, int N, int NB,
+                                                           float* __restrict__ C,
+                                                           float* __restrict__ dbias, int accumulate) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t per = static_cast<int64_t>(M) * NB;
+  if (i >= per * groups) return;
+  const int64_t g = i / per;
+  const int64_t mn = i - g * per;
+  const int m = static_cast<int>(mn / NB);
+  const int n = static_cast<int>(mn - static_cast<int64_t>(m) * NB);
   float acc = 0.f;
-  for (int r = offsets[g]; r < offsets[g + 1]; ++r) acc += ld(A, static_cast<int64_t>(r) * M + m);
-  out[g * M + m] = acc;
+  for (int sp = 0; sp < splits; ++sp) acc += part[(g * splits + sp) * per + mn];
+  if (n < N) {
+    const int64_t o = (g * M + m) * static_cast<int64_t>(N) + n;
+    C[o] = accumulate ? C[o] + acc : acc;
+  } else {
+    dbias[g * M + m] = acc;
+  }
 }
 
 __global__ void range_kernel(int32_t* __restrict__ o, int32_t n) {
@@ -355,36 +390,24 @@ hipError_t launch_dx_gather(const float* dxp, const int32_t* row_of, int64_t T, 
 }
 
 hipError_t launch_wgrad(const void* A, bool a_bf16, const void* B, bool b_bf16, const int32_t* b_rows,
-                        const int32_t* offsets, int groups, int M, int N, float* C, bool accumulate,
-                        hipStream_t s) {
-  dim3 grid(blocks(N, 64), blocks(M, 64), groups);
+                        const int32_t* offsets, int groups, int M, int N, float* C, float* dbias,
+                        bool accumulate, int splits, float* part, hipStream_t s) {
+  const int NB = dbias != nullptr ? N + 1 : N;
+  if (splits < 1 || (splits > 1 && part == nullptr)) return hipErrorInvalidValue;
+  dim3 grid(blocks(NB, 64), blocks(M, 64), groups * splits);
   const int acc = accumulate ? 1 : 0;
-  if (a_bf16 && b_bf16)
-    wgrad_kernel<uint16_t, uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(A),
-                                                          static_cast<const uint16_t*>(B), b_rows,
-                                                          offsets, M, N, C, acc);
-  else if (!a_bf16 && b_bf16)
-    wgrad_kernel<float, uint16_t><<<grid, 256, 0, s>>>(static_cast<const float*>(A),
-                                                       static_cast<const uint16_t*>(B), b_rows,
-                                                       offsets, M, N, C, acc);
-  else if (a_bf16 && !b_bf16)
-    wgrad_kernel<uint16_t, float><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(A),
-                                                       static_cast<const float*>(B), b_rows,
-                                                       offsets, M, N, C, acc);
-  else
-    wgrad_kernel<float, float><<<grid, 256, 0, s>>>(static_cast<const float*>(A),
-                                                    static_cast<const float*>(B), b_rows, offsets,
-                                                    M, N, C, acc);
-  return hipGetLastError();
-}
-
-hipError_t launch_colsum(const void* A, bool bf16, const int32_t* offsets, int groups, int M,
-                         float* out, hipStream_t s) {
-  dim3 grid(blocks(M, 256), groups);
-  if (bf16)
-    colsum_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(A), offsets, M, out);
-  else
-    colsum_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(A), offsets, M, out);
+#define MOE_WGRAD(TA, TB)                                                                        \
+  wgrad_kernel<TA, TB><<<grid, 256, 0, s>>>(static_cast<const TA*>(A), static_cast<const TB*>(B), \
+                                            b_rows, offsets, M, N, splits, C, dbias, acc, part)
+  if (a_bf16 && b_bf16) MOE_WGRAD(uint16_t, uint16_t);
+  else if (!a_bf16 && b_bf16) MOE_WGRAD(float, uint16_t);
+  else if (a_bf16 && !b_bf16) MOE_WGRAD(uint16_t, float);
+  else MOE_WGRAD(float, float);
+#undef MOE_WGRAD
+  if (splits > 1) {
+    const int64_t n = static_cast<int64_t>(groups) * M * NB;
+    wgrad_reduce_kernel<<<blocks(n, 256), 256, 0, s>>>(part, groups, splits, M, N, NB, C, dbias, acc);
+  }
   return hipGetLastError();
 }
 

@@ -115,8 +115,20 @@ Layout layout_of(const moe_config& c) {
 // workspace of moe_layer_backward
 struct BwdLayout {
   size_t logits, W1t, W2t, x_perm, dy_perm, u, Z, h, du, dY, dxp, row_expert, row_gate, dg_row, ds,
-      dsT, range_T, range_E, total;
+      dsT, range_T, range_E, part, total;
+  int router_splits;
 };
+
+// row slices of dW_r = ds^T x (one group, K = T rows): enough blocks to fill
+// the chip, slices of at least 256 rows
+int router_splits_of(const moe_config& c) {
+  const int64_t tiles = ((c.E + 63) / 64) * ((c.d + 1 + 63) / 64);
+  int64_t sp = (1024 + tiles - 1) / tiles;
+  const int64_t by_rows = c.T / 256;
+  if (sp > by_rows) sp = by_rows;
+  if (sp > 256) sp = 256;
+  return sp < 1 ? 1 : static_cast<int>(sp);
+}
 
 BwdLayout bwd_layout_of(const moe_config& c) {
   BwdLayout L{};
@@ -147,6 +159,8 @@ BwdLayout bwd_layout_of(const moe_config& c) {
   L.dsT = take(T * E * 4);
   L.range_T = take(8);
   L.range_E = take(8);
+  L.router_splits = router_splits_of(c);
+  L.part = take(L.router_splits > 1 ? static_cast<int64_t>(L.router_splits) * E * (d + 1) * 4 : 0);
   L.total = off;
   return L;
 }
@@ -480,7 +494,7 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* x, const void* W_r
                            const void* W1, const float* b1, const void* W2, const float* b2,
                            const moe_route_info* fwd, const void* dy, float aux_alpha, float* dx,
                            float* dW_r, float* db_r, float* dW1, float* db1, float* dW2, float* db2,
-                           void* ws, size_t ws_bytes, hipStream_t stream) {
+                           void* ws, size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
   MOE_TRY(check_cfg(cfg));
   const moe_config& c = *cfg;
   if (c.reroute != 0) return MOE_ERR_UNSUPPORTED;
@@ -500,8 +514,16 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* x, const void* W_r
       !aligned(f.topk_gates, 4) || !aligned(f.expert_counts, 4) || !aligned(f.expert_offsets, 4) ||
       !aligned(f.row_of, 4) || !aligned(f.row_token, 4))
     return MOE_ERR_INVALID_ARG;
+  if (stage_events != nullptr)
+    for (int i = 0; i <= MOE_BWD_NUM_STAGES; ++i)
+      if (stage_events[i] == nullptr) return MOE_ERR_INVALID_ARG;
   const BwdLayout L = bwd_layout_of(c);
   if (ws == nullptr || !aligned(ws, kAlign) || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  auto mark = [&](int i) -> int32_t {
+    if (stage_events != nullptr && hipEventRecord(stage_events[i], stream) != hipSuccess)
+      return MOE_ERR_HIP;
+    return MOE_OK;
+  };
 
   hipStream_t s = stream;
   const bool bf = c.dtype == MOE_BF16;
@@ -527,6 +549,7 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* x, const void* W_r
   int32_t* range_T = at<int32_t>(ws, L.range_T);
   int32_t* range_E = at<int32_t>(ws, L.range_E);
 
+  MOE_TRY(mark(MOE_BWD_STAGE_RECOMPUTE));
   // router logits again (the probabilities of every expert are needed)
   if (bf)
     MOE_HIP(launch_logits_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W_r), b_r,
@@ -562,10 +585,12 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* x, const void* W_r
                             Z, kActNone, offsets, c.E, c.d_ff, c.d, per_expert, s));
   }
   // per row: h, du, dY and the combine-weight gradient
+  MOE_TRY(mark(MOE_BWD_STAGE_ROWS));
   MOE_HIP(launch_row_info(f.topk_ids, f.topk_gates, f.row_of, c.T, c.k, row_expert, row_gate, s));
   MOE_HIP(launch_bwd_rows(u, Z, row_token, row_gate, row_expert, offsets, c.E, dy, b2, c.d, c.d_ff, R,
                           bf, c.act, h, du, dY, dg_row, s));
   // dx_perm = du W1_e
+  MOE_TRY(mark(MOE_BWD_STAGE_DGRAD));
   if (bf)
     MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(du), nullptr, static_cast<const uint16_t*>(W1t),
                              nullptr, dxp, true, kActNone, offsets, c.E, c.d, c.d_ff, R, per_expert, s));
@@ -573,21 +598,24 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* x, const void* W_r
     MOE_HIP(launch_gemm_f32(static_cast<const float*>(du), nullptr, static_cast<const float*>(W1t), nullptr,
                             dxp, kActNone, offsets, c.E, c.d, c.d_ff, per_expert, s));
   // expert weight and bias gradients
-  MOE_HIP(launch_wgrad(du, bf, x, bf, row_token, offsets, c.E, c.d_ff, c.d, dW1, false, s));
-  MOE_HIP(launch_wgrad(dY, bf, h, bf, nullptr, offsets, c.E, c.d, c.d_ff, dW2, false, s));
-  if (db1 != nullptr) MOE_HIP(launch_colsum(du, bf, offsets, c.E, c.d_ff, db1, s));
-  if (db2 != nullptr) MOE_HIP(launch_colsum(dY, bf, offsets, c.E, c.d, db2, s));
+  MOE_TRY(mark(MOE_BWD_STAGE_WGRAD));
+  MOE_HIP(launch_wgrad(du, bf, x, bf, row_token, offsets, c.E, c.d_ff, c.d, dW1, db1, false, 1,
+                       nullptr, s));
+  MOE_HIP(launch_wgrad(dY, bf, h, bf, nullptr, offsets, c.E, c.d, c.d_ff, dW2, db2, false, 1, nullptr,
+                       s));
   // router: ds, then dW_r = ds^T x, db_r, and dx = gathered dx_perm + ds W_r
+  MOE_TRY(mark(MOE_BWD_STAGE_ROUTER));
   const double aux = static_cast<double>(aux_alpha) * c.E / (static_cast<double>(c.T) * c.T);
   MOE_HIP(launch_router_bwd(logits, f.topk_ids, f.row_of, dg_row, f.expert_counts, c.T, c.E, c.k,
                             c.renormalize, static_cast<float>(aux), ds, dsT, s));
   MOE_HIP(launch_range(range_T, static_cast<int32_t>(c.T), s));
   MOE_HIP(launch_range(range_E, c.E, s));
-  MOE_HIP(launch_wgrad(ds, false, x, bf, nullptr, range_T, 1, c.E, c.d, dW_r, false, s));
-  if (db_r != nullptr) MOE_HIP(launch_colsum(ds, false, range_T, 1, c.E, db_r, s));
+  MOE_HIP(launch_wgrad(ds, false, x, bf, nullptr, range_T, 1, c.E, c.d, dW_r, db_r, false,
+                       L.router_splits, at<float>(ws, L.part), s));
   MOE_HIP(launch_dx_gather(dxp, f.row_of, c.T, c.k, c.d, dx, s));
-  MOE_HIP(launch_wgrad(dsT, false, W_r, bf, nullptr, range_E, 1, static_cast<int>(c.T), c.d, dx, true, s));
-  return MOE_OK;
+  MOE_HIP(launch_wgrad(dsT, false, W_r, bf, nullptr, range_E, 1, static_cast<int>(c.T), c.d, dx, nullptr,
+                       true, 1, nullptr, s));
+  return mark(MOE_BWD_NUM_STAGES);
 }
 
 const char* moe_status_string(int32_t status) {

@@ -129,13 +129,12 @@ hipError_t launch_router_bwd(const float* logits, const int32_t* ids, const int3
 // dx[t] = sum over kept j of dxp[row_of[t,j]]
 hipError_t launch_dx_gather(const float* dxp, const int32_t* row_of, int64_t T, int k, int d,
                             float* dx, hipStream_t s);
-// C[g] (+)= A_g^T B_g over the rows [offsets[g], offsets[g+1]); B rows through b_rows
+// C[g] (+)= A_g^T B_g over the rows [offsets[g], offsets[g+1]); B rows through
+// b_rows; dbias (nullable) gets the column sums of A_g. splits > 1 splits
+// each group's rows; part then holds groups*splits*M*(N+1) floats.
 hipError_t launch_wgrad(const void* A, bool a_bf16, const void* B, bool b_bf16, const int32_t* b_rows,
-                        const int32_t* offsets, int groups, int M, int N, float* C, bool accumulate,
-                        hipStream_t s);
-// out[g][m] = sum over the rows of group g of A[r][m]
-hipError_t launch_colsum(const void* A, bool bf16, const int32_t* offsets, int groups, int M,
-                         float* out, hipStream_t s);
+                        const int32_t* offsets, int groups, int M, int N, float* C, float* dbias,
+                        bool accumulate, int splits, float* part, hipStream_t s);
 // o = {0, n}
 hipError_t launch_range(int32_t* o, int32_t n, hipStream_t s);
 

@@ -76,7 +76,7 @@ def lib():
                                         P, SZ, P, P]
         L.moe_backward_workspace_size.argtypes = [CFG, ctypes.POINTER(SZ)]
         L.moe_layer_backward.argtypes = [CFG, P, P, P, P, P, P, P, ctypes.POINTER(MoeRouteInfo), P,
-                                         ctypes.c_float, P, P, P, P, P, P, P, P, SZ, P]
+                                         ctypes.c_float, P, P, P, P, P, P, P, P, SZ, P, P]
         L.moe_status_string.argtypes = [I32]
         L.moe_status_string.restype = ctypes.c_char_p
         for n in EXPORTED[:-1]:
@@ -208,11 +208,16 @@ def backward_workspace_size(cfg: MoeConfig) -> int:
     return out.value
 
 
+MOE_BWD_NUM_STAGES = 5
+BWD_STAGE_NAMES = ["recompute", "rows", "dgrad", "wgrad", "router"]
+
+
 def layer_backward(cfg, x, W_r, b_r, W1, b1, W2, b2, fwd: dict, dy, aux_alpha, grads: dict,
-                   ws=None, stream=None):
+                   ws=None, stage_events=None, stream=None):
     """fwd: the forward's routing outputs (topk_ids, topk_gates, expert_counts,
     expert_offsets, row_of, row_token). grads: output tensors dx, dW_r, dW1,
-    dW2 and optionally db_r, db1, db2."""
+    dW2 and optionally db_r, db1, db2. stage_events: optional HipEvents with
+    MOE_BWD_NUM_STAGES + 1 events."""
     if ws is None:
         ws = torch.empty(max(1, backward_workspace_size(cfg)), dtype=torch.uint8, device=x.device)
     ri = MoeRouteInfo(**{k: _ptr(v) for k, v in fwd.items()})
@@ -220,7 +225,8 @@ def layer_backward(cfg, x, W_r, b_r, W1, b1, W2, b2, fwd: dict, dy, aux_alpha, g
     _check("moe_layer_backward", lib().moe_layer_backward(
         ctypes.byref(cfg), _ptr(x), _ptr(W_r), _ptr(b_r), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
         ctypes.byref(ri), _ptr(dy), float(aux_alpha), gp["dx"], gp["dW_r"], gp["db_r"], gp["dW1"],
-        gp["db1"], gp["dW2"], gp["db2"], _ptr(ws), ws.numel(), _stream(stream)))
+        gp["db1"], gp["dW2"], gp["db2"], _ptr(ws), ws.numel(),
+        stage_events.array if stage_events is not None else None, _stream(stream)))
 
 
 # ------------------------------------------------------------------ HIP events (timing)
