@@ -322,6 +322,90 @@ __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restri
   }
 }
 
+// poff = exclusive prefix of the experts' row counts rounded up to 64
+// (one block, E <= 1024)
+__global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* __restrict__ offsets, int E,
+                                                           int32_t* __restrict__ poff) {
+  __shared__ int s[1024];
+  const int e = threadIdx.x;
+  const int v = (e < E) ? ((offsets[e + 1] - offsets[e] + 63) & ~63) : 0;
+  s[e] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int add = (e >= off) ? s[e - off] : 0;
+    __syncthreads();
+    s[e] += add;
+    __syncthreads();
+  }
+  if (e < E) poff[e] = s[e] - v;
+  if (e == E - 1) poff[E] = s[e];
+}
+
+// dst[c][poff[e] + i] = src[row(offsets[e] + i)][c] for i < n_e and 0 for
+// n_e <= i < padded n_e (row(r) = row_idx[r] when given); 64x64 tiles, a
+// tile never straddles experts (poff is a multiple of 64)
+template <typename TE>
+__global__ __launch_bounds__(256) void padded_transpose_kernel(const TE* __restrict__ src,
+                                                               const int32_t* __restrict__ row_idx,
+                                                               const int32_t* __restrict__ offsets,
+                                                               const int32_t* __restrict__ poff, int E,
+                                                               int Cc, int ldd, TE* __restrict__ dst) {
+  __shared__ TE tile[64][65];
+  const int p0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  if (p0 >= poff[E]) return;
+  int lo = 0, hi = E - 1;  // the expert e with poff[e] <= p0 < poff[e+1]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (poff[mid] <= p0) lo = mid;
+    else hi = mid - 1;
+  }
+  const int ne = offsets[lo + 1] - offsets[lo];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int local = p0 - poff[lo] + i;
+    const int c = c0 + tx;
+    TE v{};
+    if (local < ne && c < Cc) {
+      const int64_t r = offsets[lo] + local;
+      const int64_t row = row_idx != nullptr ? row_idx[r] : r;
+      v = src[row * Cc + c];
+    }
+    tile[i][tx] = v;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i;
+    if (c < Cc) dst[static_cast<int64_t>(c) * ldd + p0 + tx] = tile[tx][i];
+  }
+}
+
+// out[e][m] = sum of At[m][poff[e] .. poff[e+1]) (zero padding included);
+// one wave per (m, e), lanes in a fixed order
+template <typename TE>
+__global__ __launch_bounds__(256) void seg_rowsum_kernel(const TE* __restrict__ At,
+                                                         const int32_t* __restrict__ poff, int E, int M,
+                                                         int lda, float* __restrict__ out) {
+  const int64_t wv = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (wv >= static_cast<int64_t>(M) * E) return;
+  const int e = static_cast<int>(wv / M);
+  const int m = static_cast<int>(wv - static_cast<int64_t>(e) * M);
+  float acc = 0.f;
+  for (int p = poff[e] + lane; p < poff[e + 1]; p += 64) acc += ld(At, static_cast<int64_t>(m) * lda + p);
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (lane == 0) out[static_cast<int64_t>(e) * M + m] = acc;
+}
+
+// C[e] = 0 for the experts without rows (block y = expert)
+__global__ __launch_bounds__(256) void zero_empty_kernel(const int32_t* __restrict__ offsets, int64_t MN,
+                                                         float* __restrict__ C) {
+  const int64_t e = blockIdx.y;
+  if (offsets[e + 1] > offsets[e]) return;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < MN;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    C[e * MN + i] = 0.f;
+}
+
 __global__ void range_kernel(int32_t* __restrict__ o, int32_t n) {
   if (threadIdx.x == 0) {
     o[0] = 0;
@@ -408,6 +492,44 @@ hipError_t launch_wgrad(const void* A, bool a_bf16, const void* B, bool b_bf16, 
     const int64_t n = static_cast<int64_t>(groups) * M * NB;
     wgrad_reduce_kernel<<<blocks(n, 256), 256, 0, s>>>(part, groups, splits, M, N, NB, C, dbias, acc);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t s) {
+  pad_offsets_kernel<<<1, 1024, 0, s>>>(offsets, E, poff);
+  return hipGetLastError();
+}
+
+hipError_t launch_padded_transpose(const void* src, const int32_t* row_idx, const int32_t* offsets,
+                                   const int32_t* poff, int E, int Cc, int64_t max_padded, int ld,
+                                   bool bf16, void* dst, hipStream_t s) {
+  if (max_padded <= 0) return hipSuccess;
+  dim3 grid(blocks(Cc, 64), blocks(max_padded, 64));
+  if (bf16)
+    padded_transpose_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(src), row_idx,
+                                                           offsets, poff, E, Cc, ld,
+                                                           static_cast<uint16_t*>(dst));
+  else
+    padded_transpose_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(src), row_idx, offsets,
+                                                        poff, E, Cc, ld, static_cast<float*>(dst));
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_rowsum(const void* At, bool bf16, const int32_t* poff, int E, int M, int ld,
+                             float* out, hipStream_t s) {
+  const unsigned grid = blocks(static_cast<int64_t>(M) * E, 4);
+  if (bf16)
+    seg_rowsum_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(At), poff, E, M, ld, out);
+  else
+    seg_rowsum_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(At), poff, E, M, ld, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_empty(const int32_t* offsets, int E, int64_t MN, float* C, hipStream_t s) {
+  int64_t bx = (MN + 256 * 16 - 1) / (256 * 16);
+  if (bx > 4096) bx = 4096;
+  dim3 grid(static_cast<unsigned>(bx), E);
+  zero_empty_kernel<<<grid, 256, 0, s>>>(offsets, MN, C);
   return hipGetLastError();
 }
 

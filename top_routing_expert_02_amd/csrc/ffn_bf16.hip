@@ -153,13 +153,16 @@ __device__ __forceinline__ float activate(float v) {
   else return v;
 }
 
+// One output tile: expert e, output rows [row0, row0 + rv) (rv valid of the
+// tile's height), features from n0; operand A's first row arow and K range
+// [k0, k0 + 64 nk).
 struct TileInfo {
-  int e, row0, rv, n0;
+  int e, row0, rv, n0, arow, k0, nk;
 };
 
 // s_tiles[e]: exclusive prefix over experts of their M tiles of height BM.
 __device__ __forceinline__ TileInfo decode_tile(int tile, const int* s_tiles, const int32_t* offsets,
-                                                int E, int NT, int BM) {
+                                                int E, int NT, int BM, int nk) {
   // expert: the largest e with s_tiles[e] * NT <= tile (experts with no
   // rows share their successor's prefix and are skipped)
   int lo = 0, hi = E - 1;
@@ -177,6 +180,37 @@ __device__ __forceinline__ TileInfo decode_tile(int tile, const int* s_tiles, co
   t.row0 = offsets[lo] + mt * BM;
   t.rv = min(BM, offsets[lo + 1] - t.row0);
   t.n0 = nt * BN;
+  t.arow = t.row0;
+  t.k0 = 0;
+  t.nk = nk;
+  return t;
+}
+
+// Weight-gradient tiles: C[e] [M, N] = A_e^T B_e where the operands come
+// transposed (A^T [M, lda], B^T [N, lda]) with expert e's rows padded to a
+// multiple of 64 at columns [poff[e], poff[e+1]). s_tiles[e]: prefix of the
+// experts' M tiles (MT for an expert with rows, 0 without); M tiles inner.
+__device__ __forceinline__ TileInfo decode_tile_wg(int tile, const int* s_tiles,
+                                                   const int32_t* poff, int E, int NT, int BM,
+                                                   int M) {
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_tiles[mid] * NT <= tile) lo = mid;
+    else hi = mid - 1;
+  }
+  TileInfo t;
+  t.e = lo;
+  const int mte = s_tiles[lo + 1] - s_tiles[lo];
+  const int u = tile - s_tiles[lo] * NT;
+  const int nt = u / mte;
+  const int mt = u - nt * mte;
+  t.arow = mt * BM;
+  t.row0 = lo * M + t.arow;  // C viewed as [E*M, N]
+  t.rv = min(BM, M - t.arow);
+  t.n0 = nt * BN;
+  t.k0 = poff[lo];
+  t.nk = (poff[lo + 1] - poff[lo]) / BK;
   return t;
 }
 
@@ -194,33 +228,36 @@ __device__ __forceinline__ void wait_loads(int n) {
 // read its last row; feature rows past N read row N-1. With row_idx, tile row
 // r is row row_idx[row0 + r] of A (the token rows are gathered straight from
 // x, so the permuted copy is never written).
+// lda: elements between consecutive rows of A and of W (K for the expert
+// FFN); w_estride: elements between experts' weight matrices (0 when W is
+// one matrix).
 template <int LA, int LB>
 __device__ __forceinline__ void tile_sources(const TileInfo& t, const uint16_t* A,
                                              const int32_t* __restrict__ row_idx, const uint16_t* W,
-                                             int N, int K, int wave, int drow, int dpos,
-                                             const char*& Abase, const char*& Wbase,
+                                             int N, int lda, int64_t w_estride, int wave, int drow,
+                                             int dpos, const char*& Abase, const char*& Wbase,
                                              uint32_t (&aoffs)[LA], uint32_t (&boffs)[LB]) {
-  Wbase = reinterpret_cast<const char*>(W + (static_cast<int64_t>(t.e) * N + t.n0) * K);
+  Wbase = reinterpret_cast<const char*>(W + t.e * w_estride + static_cast<int64_t>(t.n0) * lda + t.k0);
   if (row_idx != nullptr) {
-    Abase = reinterpret_cast<const char*>(A);
+    Abase = reinterpret_cast<const char*>(A + t.k0);
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
       const int r = (wave * LA + i) * 8 + drow;
       const uint32_t src = static_cast<uint32_t>(row_idx[t.row0 + min(r, t.rv - 1)]);
-      aoffs[i] = (src * static_cast<uint32_t>(K) + (dpos ^ swz_key(r)) * 8) * 2;
+      aoffs[i] = (src * static_cast<uint32_t>(lda) + (dpos ^ swz_key(r)) * 8) * 2;
     }
   } else {
-    Abase = reinterpret_cast<const char*>(A + static_cast<int64_t>(t.row0) * K);
+    Abase = reinterpret_cast<const char*>(A + static_cast<int64_t>(t.arow) * lda + t.k0);
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
       const int r = (wave * LA + i) * 8 + drow;
-      aoffs[i] = static_cast<uint32_t>((min(r, t.rv - 1) * K + (dpos ^ swz_key(r)) * 8) * 2);
+      aoffs[i] = static_cast<uint32_t>((min(r, t.rv - 1) * lda + (dpos ^ swz_key(r)) * 8) * 2);
     }
   }
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
     const int r = (wave * LB + i) * 8 + drow;
-    boffs[i] = static_cast<uint32_t>(((min(t.n0 + r, N - 1) - t.n0) * K + (dpos ^ swz_key(r)) * 8) * 2);
+    boffs[i] = static_cast<uint32_t>(((min(t.n0 + r, N - 1) - t.n0) * lda + (dpos ^ swz_key(r)) * 8) * 2);
   }
 }
 
@@ -271,12 +308,16 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], const fl
 
 // The persistent tile loop for tiles of BM = 64 TM rows. lds: NST stage
 // buffers; s_tiles: the M-tile prefix for this height; s_bias: two slices.
-template <int TM, bool OUT_F32, int ACT>
+// WG: weight-gradient tiles (decode_tile_wg; offsets holds the padded K
+// offsets, M the rows of C per expert); else expert-FFN tiles with K/64
+// stages each.
+template <int TM, bool OUT_F32, int ACT, bool WG>
 __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const int32_t* __restrict__ row_idx,
                                           const uint16_t* __restrict__ W, const float* __restrict__ bias,
                                           void* __restrict__ out, const int32_t* __restrict__ offsets,
-                                          int E, int N, int K, char* lds, const int* s_tiles,
-                                          float (*s_bias)[BN], int tile, int total, int NT) {
+                                          int E, int N, int K, int lda, int64_t w_estride, int M,
+                                          char* lds, const int* s_tiles, float (*s_bias)[BN], int tile,
+                                          int total, int NT) {
   constexpr int BM = 64 * TM;
   constexpr int WM = BM / 2;         // tokens per wave
   constexpr int A_BYTES = BM * ROWB;
@@ -299,7 +340,10 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
 #pragma unroll
   for (int s = 0; s < 4; ++s) fo[s] = l5 * ROWB + 16 * ((2 * s + hi) ^ key);
   const int drow = lane >> 3, dpos = lane & 7;
-  const int nk = K / BK;
+  auto decode = [&](int tl) {
+    if constexpr (WG) return decode_tile_wg(tl, s_tiles, offsets, E, NT, BM, M);
+    else return decode_tile(tl, s_tiles, offsets, E, NT, BM, K / BK);
+  };
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
   const uint32_t trow = wm * WM * ROWB;            // this wave's token rows in a stage
   const uint32_t wrow = A_BYTES + wn * WN * ROWB;  // this wave's weight rows in a stage
@@ -309,7 +353,7 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
   const char* Wbase;
   // a tile's first stages and its bias slice (wave 0, one lane per 4 features)
   auto prologue = [&](const TileInfo& c, int par) {
-    for (int p = 0; p < NST && p < nk; ++p)
+    for (int p = 0; p < NST && p < c.nk; ++p)
       issue_stage<TM>(aoffs, boffs, lds_base + p * STAGE + wave * LA * 1024,
                       lds_base + p * STAGE + A_BYTES + wave * LB * 1024, Abase + p * ROWB,
                       Wbase + p * ROWB);
@@ -318,11 +362,13 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
                  static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&s_bias[par][0])));
   };
   int par = 0;  // bias slice of the current tile
-  TileInfo cur = decode_tile(tile, s_tiles, offsets, E, NT, BM);
-  tile_sources<LA, LB>(cur, A, row_idx, W, N, K, wave, drow, dpos, Abase, Wbase, aoffs, boffs);
+  TileInfo cur = decode(tile);
+  tile_sources<LA, LB>(cur, A, row_idx, W, N, lda, w_estride, wave, drow, dpos, Abase, Wbase, aoffs,
+                       boffs);
   prologue(cur, par);
 
   for (;;) {
+    const int nk = cur.nk;  // K stages of this tile (cur moves on before its epilogue)
     f32x16_t acc[TN][TM];
 #pragma unroll
     for (int i = 0; i < TN; ++i)
@@ -387,8 +433,9 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     // next tile's first stages load during this tile's last MFMAs and epilogue
     __syncthreads();
     if (next < total) {
-      cur = decode_tile(next, s_tiles, offsets, E, NT, BM);
-      tile_sources<LA, LB>(cur, A, row_idx, W, N, K, wave, drow, dpos, Abase, Wbase, aoffs, boffs);
+      cur = decode(next);
+      tile_sources<LA, LB>(cur, A, row_idx, W, N, lda, w_estride, wave, drow, dpos, Abase, Wbase, aoffs,
+                           boffs);
       prologue(cur, par ^ 1);
     }
     last_step<TM>(acc, wf1, tf1);
@@ -466,11 +513,62 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
   const int tile = (Gd % 8 == 0) ? (b % 8) * (Gd / 8) + b / 8 : b;
   if (tile >= total) return;
   if (tall)
-    tile_loop<4, OUT_F32, ACT>(A, row_idx, W, bias, out, offsets, E, N, K, lds, s_tiles, s_bias, tile,
+    tile_loop<4, OUT_F32, ACT, false>(A, row_idx, W, bias, out, offsets, E, N, K, K,
+                                      static_cast<int64_t>(N) * K, 0, lds, s_tiles, s_bias, tile,
                                total, NT);
   else
-    tile_loop<3, OUT_F32, ACT>(A, row_idx, W, bias, out, offsets, E, N, K, lds, s_tiles, s_bias, tile,
+    tile_loop<3, OUT_F32, ACT, false>(A, row_idx, W, bias, out, offsets, E, N, K, K,
+                                      static_cast<int64_t>(N) * K, 0, lds, s_tiles, s_bias, tile,
                                total, NT);
+#endif
+}
+
+// Weight gradients of the expert GEMMs on the same tile loop:
+//   C[e] [M, N] = sum over expert e's rows r of A[r, m] B[r, n]
+// with both operands given transposed and K-contiguous: At [M, lda],
+// Bt [N, lda], expert e's rows at columns [poff[e], poff[e+1]) (a multiple
+// of 64, zero-padded). Experts without rows get no tiles (their C is left
+// to the caller). 256-row tiles, fp32 out, no bias.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void grouped_wgrad_bf16_kernel(const uint16_t* __restrict__ At, const uint16_t* __restrict__ Bt,
+                               const int32_t* __restrict__ poff, int E, int M, int N, int lda,
+                               float* __restrict__ C) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ __attribute__((aligned(1024))) char lds[NST * (256 + BN) * ROWB];
+  __shared__ int s_tiles[1025];
+  __shared__ int s_part[256];
+  __shared__ __attribute__((aligned(16))) float s_bias[2][BN];
+  const int tid = threadIdx.x;
+  const int NT = (N + BN - 1) / BN;
+  const int MT = (M + 255) / 256;
+  const int per = (E + 255) / 256;
+  const int eb = tid * per;
+  int cnt = 0;
+  for (int e = eb; e < min(E, eb + per); ++e) cnt += (poff[e + 1] > poff[e]) ? MT : 0;
+  s_part[tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int a0 = (tid >= off) ? s_part[tid - off] : 0;
+    __syncthreads();
+    s_part[tid] += a0;
+    __syncthreads();
+  }
+  {
+    int run = s_part[tid] - cnt;
+    for (int e = eb; e < min(E, eb + per); ++e) {
+      s_tiles[e] = run;
+      run += (poff[e + 1] > poff[e]) ? MT : 0;
+    }
+    if (tid == 255) s_tiles[E] = s_part[255];
+  }
+  __syncthreads();
+  const int total = s_tiles[E] * NT;
+  const int Gd = gridDim.x;
+  const int b = blockIdx.x;
+  const int tile = (Gd % 8 == 0) ? (b % 8) * (Gd / 8) + b / 8 : b;
+  if (tile >= total) return;
+  tile_loop<4, true, kActNone, true>(At, nullptr, Bt, nullptr, C, poff, E, N, 0, lda, 0, M, lds,
+                                     s_tiles, s_bias, tile, total, NT);
 #endif
 }
 
@@ -511,6 +609,16 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uin
   } else {
     grouped_gemm_bf16_kernel<false, kActNone><<<grid, 256, 0, s>>>(A, row_idx, W, bias, out, offsets, E, N, K);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad_bf16(const uint16_t* At, const uint16_t* Bt, const int32_t* poff, int E,
+                             int M, int N, int lda, float* C, hipStream_t s) {
+  const int64_t tiles = static_cast<int64_t>(E) * ((M + 255) / 256) * ((N + BN - 1) / BN);
+  const int slots = cu_count();
+  const unsigned grid = static_cast<unsigned>(tiles < slots ? tiles : slots);
+  if (grid == 0) return hipSuccess;
+  grouped_wgrad_bf16_kernel<<<grid, 256, 0, s>>>(At, Bt, poff, E, M, N, lda, C);
   return hipGetLastError();
 }
 

@@ -115,9 +115,20 @@ Layout layout_of(const moe_config& c) {
 // workspace of moe_layer_backward
 struct BwdLayout {
   size_t logits, W1t, W2t, x_perm, dy_perm, u, Z, h, du, dY, dxp, row_expert, row_gate, dg_row, ds,
-      dsT, range_T, range_E, part, total;
+      dsT, range_T, range_E, part, poff, At, Bt, total;
   int router_splits;
+  int64_t ldp;     // columns of the transposed weight-gradient operands (0: not used)
 };
+
+// bf16 weight gradients run on the MFMA grouped GEMM with transposed operands
+// whose expert row ranges are padded to multiples of 64: at most R + 63 E
+// columns. Its DMA offsets are 32-bit (256 rows of ldp bf16 values).
+int64_t wgrad_ld_of(const moe_config& c) {
+  if (c.dtype != MOE_BF16) return 0;
+  const int64_t ldp = ((max_rows_of(c) + 64LL * c.E) + 63) / 64 * 64;
+  if (256 * ldp * 2 >= (static_cast<int64_t>(1) << 32)) return 0;
+  return ldp;
+}
 
 // row slices of dW_r = ds^T x (one group, K = T rows): enough blocks to fill
 // the chip, slices of at least 256 rows
@@ -161,6 +172,11 @@ BwdLayout bwd_layout_of(const moe_config& c) {
   L.range_E = take(8);
   L.router_splits = router_splits_of(c);
   L.part = take(L.router_splits > 1 ? static_cast<int64_t>(L.router_splits) * E * (d + 1) * 4 : 0);
+  L.ldp = wgrad_ld_of(c);
+  const int64_t wide = d > f ? d : f;
+  L.poff = take((E + 1) * 4);
+  L.At = take(L.ldp * wide * es);
+  L.Bt = take(L.ldp * wide * es);
   L.total = off;
   return L;
 }
@@ -599,10 +615,29 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* x, const void* W_r
                             dxp, kActNone, offsets, c.E, c.d, c.d_ff, per_expert, s));
   // expert weight and bias gradients
   MOE_TRY(mark(MOE_BWD_STAGE_WGRAD));
-  MOE_HIP(launch_wgrad(du, bf, x, bf, row_token, offsets, c.E, c.d_ff, c.d, dW1, db1, false, 1,
-                       nullptr, s));
-  MOE_HIP(launch_wgrad(dY, bf, h, bf, nullptr, offsets, c.E, c.d, c.d_ff, dW2, db2, false, 1, nullptr,
-                       s));
+  if (L.ldp > 0) {
+    // MFMA path: K-contiguous operands (expert rows as padded columns)
+    int32_t* poff = at<int32_t>(ws, L.poff);
+    auto* At = at<uint16_t>(ws, L.At);
+    auto* Bt = at<uint16_t>(ws, L.Bt);
+    const int ld = static_cast<int>(L.ldp);
+    MOE_HIP(launch_pad_offsets(offsets, c.E, poff, s));
+    MOE_HIP(launch_padded_transpose(du, nullptr, offsets, poff, c.E, c.d_ff, L.ldp, ld, true, At, s));
+    MOE_HIP(launch_padded_transpose(x, row_token, offsets, poff, c.E, c.d, L.ldp, ld, true, Bt, s));
+    MOE_HIP(launch_wgrad_bf16(At, Bt, poff, c.E, c.d_ff, c.d, ld, dW1, s));
+    if (db1 != nullptr) MOE_HIP(launch_seg_rowsum(At, true, poff, c.E, c.d_ff, ld, db1, s));
+    MOE_HIP(launch_padded_transpose(dY, nullptr, offsets, poff, c.E, c.d, L.ldp, ld, true, At, s));
+    MOE_HIP(launch_padded_transpose(h, nullptr, offsets, poff, c.E, c.d_ff, L.ldp, ld, true, Bt, s));
+    MOE_HIP(launch_wgrad_bf16(At, Bt, poff, c.E, c.d, c.d_ff, ld, dW2, s));
+    if (db2 != nullptr) MOE_HIP(launch_seg_rowsum(At, true, poff, c.E, c.d, ld, db2, s));
+    MOE_HIP(launch_zero_empty(offsets, c.E, static_cast<int64_t>(c.d) * c.d_ff, dW1, s));
+    MOE_HIP(launch_zero_empty(offsets, c.E, static_cast<int64_t>(c.d) * c.d_ff, dW2, s));
+  } else {
+    MOE_HIP(launch_wgrad(du, bf, x, bf, row_token, offsets, c.E, c.d_ff, c.d, dW1, db1, false, 1,
+                         nullptr, s));
+    MOE_HIP(launch_wgrad(dY, bf, h, bf, nullptr, offsets, c.E, c.d, c.d_ff, dW2, db2, false, 1,
+                         nullptr, s));
+  }
   // router: ds, then dW_r = ds^T x, db_r, and dx = gathered dx_perm + ds W_r
   MOE_TRY(mark(MOE_BWD_STAGE_ROUTER));
   const double aux = static_cast<double>(aux_alpha) * c.E / (static_cast<double>(c.T) * c.T);

@@ -135,6 +135,22 @@ hipError_t launch_dx_gather(const float* dxp, const int32_t* row_of, int64_t T, 
 hipError_t launch_wgrad(const void* A, bool a_bf16, const void* B, bool b_bf16, const int32_t* b_rows,
                         const int32_t* offsets, int groups, int M, int N, float* C, float* dbias,
                         bool accumulate, int splits, float* part, hipStream_t s);
+// poff = exclusive prefix of the experts' row counts rounded up to 64
+hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t s);
+// dst [Cc, ld]: expert e's rows of src [*, Cc] (through row_idx when given)
+// as columns [poff[e], poff[e] + n_e), zeros up to poff[e+1]
+hipError_t launch_padded_transpose(const void* src, const int32_t* row_idx, const int32_t* offsets,
+                                   const int32_t* poff, int E, int Cc, int64_t max_padded, int ld,
+                                   bool bf16, void* dst, hipStream_t s);
+// out[e][m] = sum over columns [poff[e], poff[e+1]) of At[m][.]
+hipError_t launch_seg_rowsum(const void* At, bool bf16, const int32_t* poff, int E, int M, int ld,
+                             float* out, hipStream_t s);
+// C[e] (MN floats each) = 0 for the experts without rows
+hipError_t launch_zero_empty(const int32_t* offsets, int E, int64_t MN, float* C, hipStream_t s);
+// C[e] = At_e Bt_e^T over expert e's padded K range (bf16 MFMA, fp32 out);
+// experts without rows are skipped
+hipError_t launch_wgrad_bf16(const uint16_t* At, const uint16_t* Bt, const int32_t* poff, int E,
+                             int M, int N, int lda, float* C, hipStream_t s);
 // o = {0, n}
 hipError_t launch_range(int32_t* o, int32_t n, hipStream_t s);
 
