@@ -353,7 +353,7 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
   const char* Wbase;
   // a tile's first stages and its bias slice (wave 0, one lane per 4 features)
   auto prologue = [&](const TileInfo& c, int par) {
-    for (int p = 0; p < NST && p < c.nk; ++p)
+    for (int p = 0; p < NST && p < (WG ? c.nk : K / BK); ++p)
       issue_stage<TM>(aoffs, boffs, lds_base + p * STAGE + wave * LA * 1024,
                       lds_base + p * STAGE + A_BYTES + wave * LB * 1024, Abase + p * ROWB,
                       Wbase + p * ROWB);
@@ -368,7 +368,9 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
   prologue(cur, par);
 
   for (;;) {
-    const int nk = cur.nk;  // K stages of this tile (cur moves on before its epilogue)
+    // K stages of this tile (cur moves on before its epilogue); the same for
+    // every expert-FFN tile
+    const int nk = WG ? cur.nk : K / BK;
     f32x16_t acc[TN][TM];
 #pragma unroll
     for (int i = 0; i < TN; ++i)
