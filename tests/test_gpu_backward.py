@@ -130,3 +130,15 @@ def test_backward_deterministic():
         outs.append({k: v.cpu() for k, v in grads.items()})
     for k in outs[0]:
         assert torch.equal(outs[0][k], outs[1][k]), k
+
+
+@pytest.mark.parametrize("name", ["small_bf16"])
+def test_backward_full_size(name):
+    """The backward pass at the full workload size, in the configuration the
+    training-step benchmark times (L_aux coefficient 0.01), against the
+    whole fp64 oracle backward."""
+    w = WORKLOADS[name]
+    C = mo.capacity(w.T, w.k, w.E, w.c)
+    say(f"[gpu] backward full size {name}")
+    stats = backward_parity(w, C, 0.01)
+    say(f"[gpu] backward full size {name}: {stats}")
