@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="time a training step instead: the layer forward, then its backward "
                          "(gradients of x and every parameter, L_aux coefficient 0.01)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time replays of the layer captured once in a HIP graph (on this "
+                         "stack they were slower than eager launches; value takes the faster)")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="after the timed steps, this many extra steps each preceded by a 1 GiB "
                          "write that evicts L2 and the MALL (reported as 'cold', not as value)")
@@ -301,24 +304,52 @@ def main():
     counts = info["expert_counts"].cpu().numpy()
     offsets = info["expert_offsets"].cpu().numpy()
 
-    # timed region: K whole-layer steps, stage events recorded inside it
     K = args.steps
+
+    def timed(run):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(K):
+            run()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / K
+
+    # eager launches, no instrumentation
+    eager_ms = timed(step)
+    graph_ms = None
+    if args.graph:
+        # the same layer call captured once and replayed (launches without
+        # host overhead between kernels)
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            g.replay()
+        graph_ms = timed(g.replay)
+    ms = eager_ms if graph_ms is None else min(eager_ms, graph_ms)
+    # stage breakdown: K more eager steps with a HIP event between stages
+    # (not part of the timed region)
     ev = [moe.HipEvents(moe.MOE_NUM_STAGES + 1) for _ in range(K)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record(stream)
     for i in range(K):
         step(ev[i])
-    end.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms = total_ms / K
     stage_ms = {n: float(np.mean([e.elapsed_ms(s, s + 1) for e in ev]))
                 for s, n in enumerate(moe.STAGE_NAMES)}
     for e in ev:
         e.close()
-    log(f"[bench] {K} steps: {ms:.4f} ms/step; stages {stage_ms}")
+    log(f"[bench] {K} steps: {ms:.4f} ms/step (eager {eager_ms:.4f}, graph "
+        f"{graph_ms if graph_ms is None else round(graph_ms, 4)}); stages {stage_ms}")
 
     work = stage_bytes_flops(w, C, counts, offsets)
     stages = {}
@@ -369,7 +400,11 @@ def main():
                       "c": None if w.dropless else w.c, "C": C, "act": w.act, "rows": rows,
                       "dropped": w.T * w.k - rows, "priority": w.priority, "reroute_rounds": w.reroute,
                       "parallelism": "none"},
-           "roofline": roofline, "stages": stages}
+           "roofline": roofline, "stages": stages,
+           "timing": {"launch": "hip graph replay" if graph_ms is not None and graph_ms < eager_ms
+                      else "eager",
+                      "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
+                      "stages_from": "HIP events between stages of separate eager steps"}}
     if cold is not None:
         out["cold"] = cold
     if not args.no_cpu_baseline:

@@ -432,3 +432,53 @@ def test_full_size_workload(name):
         assert torch.all(y[torch.from_numpy(dropped_tok).to(dev)] == 0)
     if w.dropless:
         assert o_disp["kept"].all() and o_disp["rows"] == w.T * w.k
+
+
+def test_graph_replay_matches_eager():
+    """The layer captured once in a HIP graph and replayed gives the eager
+    result bit for bit, on every replay, with eager work and synchronisation
+    between replays (the benchmark times such replays)."""
+    w = WORKLOADS["small_bf16"].scaled(name="graph_replay", T=1000, d=256, d_ff=512)
+    dev = "cuda"
+    inp = synth.make_inputs(w, dev, seed=5)
+    other = synth.make_inputs(w, dev, seed=6)
+    C = cap(w)
+    m = moe()
+    cfg = P.make_cfg(w, C)
+    ws = m.alloc_workspace(cfg, dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    info = {"topk_ids": torch.empty((w.T, w.k), **i32),
+            "expert_offsets": torch.empty(w.E + 1, **i32),
+            "row_of": torch.empty((w.T, w.k), **i32)}
+    y = torch.empty((w.T, w.d), dtype=w.torch_dtype, device=dev)
+
+    def call(src, out, inf):
+        m.layer_forward(cfg, src["x"], src["W_r"], src["b_r"], src["W1"], src["b1"], src["W2"],
+                        src["b2"], out, info=inf, ws=ws)
+
+    y_ref = torch.empty_like(y)
+    info_ref = {k: torch.empty_like(v) for k, v in info.items()}
+    call(inp, y_ref, info_ref)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(inp, y, info)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(inp, y, info)
+    y_other = torch.empty_like(y)
+    for rep in range(3):
+        y.fill_(0)
+        for v in info.values():
+            v.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), f"replay {rep}: y differs"
+        for k in info:
+            assert torch.equal(info[k], info_ref[k]), f"replay {rep}: {k} differs"
+        # eager work on the same workspace between replays
+        call(other, y_other, {k: torch.empty_like(v) for k, v in info.items()})
+        torch.cuda.synchronize()
