@@ -54,9 +54,6 @@ __global__ __launch_bounds__(256) void logits_bf16_kernel(const uint16_t* __rest
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // unrolled so that the loads of several K steps are in flight together
-  // (the loop is bound by L2 latency, not by the MFMAs)
-#pragma unroll 4
   for (int k0 = wave * 32; k0 < d; k0 += 128) {
     bf16x8_t a[MT], b[NT];
 #pragma unroll
