@@ -249,10 +249,15 @@ def main_backward(args):
             st["flops"] = flops[n]
             st["TFLOP_s"] = flops[n] / (t * 1e-3) / 1e12
         stages[n] = st
-    dom = "bwd_wgrad"
-    roofline = {"bound": "alu", "kernel": "wgrad_kernel (dW1 and dW2: fp32 FMA)",
-                "achieved": stages[dom]["TFLOP_s"], "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
-                "frac": stages[dom]["TFLOP_s"] / PEAK_F32_TFLOPS, "traffic": None}
+    # the grouped GEMM is the dominant kernel of the step (GEMM2, u, Z and
+    # dx_perm use it); the dgrad stage is exactly one launch of it
+    dom = "bwd_dgrad"
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    roofline = {"bound": "mfma" if w.dtype == "bf16" else "alu",
+                "kernel": "grouped_gemm_bf16 (dx_perm = du W1_e)" if w.dtype == "bf16"
+                else "gemm_f32 (dx_perm = du W1_e)",
+                "achieved": stages[dom]["TFLOP_s"], "peak": peak, "unit": "TFLOP/s",
+                "frac": stages[dom]["TFLOP_s"] / peak, "traffic": None}
     out = {"metric": "MoE-layer training step (forward + backward) tokens/sec", "value": w.T / (ms * 1e-3),
            "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
