@@ -13,17 +13,18 @@
 // Both operands are K-contiguous (A row-major [rows, K]; W[e] row-major [N, K]).
 //
 // Design (gfx950, wave64, 160 KiB LDS per CU):
-//  * Block tile BM tokens x BN=256 features with BM = 256 or 192; four waves
-//    in a 2x2 grid; each wave owns BM/2 tokens x 128 features as 32x32
+//  * Block tile BM tokens x BN=256 features with BM = 256, 192, 128 or 64;
+//    four waves in a 2x2 grid; each wave owns BM/2 tokens x 128 features as 32x32
 //    v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulators in AGPRs. The
 //    weight tile is the MFMA A operand and the token tile the B operand, so a
 //    lane's accumulators hold 4 consecutive features of one token: the
 //    epilogue stores 8-byte (bf16) or 16-byte (fp32) vectors.
 //  * The tile height is chosen on the device, per launch, from the actual
-//    expert row counts: the schedule takes the height whose tile count needs
-//    the fewer rounds of the persistent blocks (rounds x height), so a group
+//    expert row counts (the cost model is at the schedule below): a group
 //    count that leaves a mostly idle last round of 256-row tiles runs as
-//    192-row tiles instead. The host never learns the row counts.
+//    192-row tiles, and experts with a few dozen rows (decode batches) run
+//    64-row tiles, which stream the same weights with a quarter of the
+//    MFMAs. The host never learns the row counts.
 //  * K advances in stages of BK=64: every LDS row is 128 bytes, one full
 //    cache line of the source row, so each L1->L2 request moves a whole line.
 //    The 16-byte chunks of a row are XOR-swizzled by (row/2)&7, which keeps
@@ -32,7 +33,7 @@
 //    (global_load_lds_dwordx4: no staging registers, no ds_write); one
 //    instruction fills 8 rows (1 KiB); each lane fetches the chunk that the
 //    swizzle places at its LDS slot.
-//  * Two stage buffers. A stage is four K16 steps; each step's MFMAs run with
+//  * Two stage buffers (three for tiles of 128 or 64 rows). A stage is four K16 steps; each step's MFMAs run with
 //    the next step's fragment reads in flight, and the buffer a stage occupied
 //    is refilled (with the stage after next) between the MFMAs of that
 //    stage's last step, right after the barrier that shows every wave has
@@ -54,7 +55,11 @@ namespace {
 constexpr int BN = 256;       // features per tile
 constexpr int BK = 64;        // K per LDS stage
 constexpr int ROWB = BK * 2;  // bytes per LDS row (128)
-constexpr int NST = 2;        // stage buffers
+// stage buffers: two for the 256- and 192-row tiles, three for the shorter
+// ones (a tile of few rows streams weights, so more bytes in flight pay)
+template <int TM>
+constexpr int stages_for() { return TM <= 2 ? 3 : 2; }  // wait_loads allows at most 3
+constexpr int kLdsBytes = 3 * (128 + BN) * ROWB;  // the largest of NST (BM + BN) rows
 constexpr int TN = 4;         // 32-feature MFMA tiles per wave
 constexpr int WN = BN / 2;    // features per wave
 static_assert(kGemmBM == 256, "the taller of the two tile heights");
@@ -96,7 +101,9 @@ __device__ __forceinline__ void step(f32x16_t (&acc)[TN][TM], const bf16x8_t (&w
                                      const bf16x8_t (&t)[TM], bf16x8_t (&nw)[TN], bf16x8_t (&nt)[TM],
                                      uint32_t ta, uint32_t wa) {
   if constexpr (TM == 4) step_4x4(acc, w, t, nw, nt, ta, wa);
-  else step_3x4(acc, w, t, nw, nt, ta, wa);
+  else if constexpr (TM == 3) step_3x4(acc, w, t, nw, nt, ta, wa);
+  else if constexpr (TM == 2) step_2x4(acc, w, t, nw, nt, ta, wa);
+  else step_1x4(acc, w, t, nw, nt, ta, wa);
 }
 
 template <int TM>
@@ -106,28 +113,36 @@ __device__ __forceinline__ void step_dma(f32x16_t (&acc)[TN][TM], const bf16x8_t
                                          const uint32_t (&vo)[2 * TM + 2 * TN], uint32_t la, uint32_t lb,
                                          const char* ga, const char* gw) {
   if constexpr (TM == 4) step_dma_4x4(acc, w, t, nw, nt, ta, wa, vo, la, lb, ga, gw);
-  else step_dma_3x4(acc, w, t, nw, nt, ta, wa, vo, la, lb, ga, gw);
+  else if constexpr (TM == 3) step_dma_3x4(acc, w, t, nw, nt, ta, wa, vo, la, lb, ga, gw);
+  else if constexpr (TM == 2) step_dma_2x4(acc, w, t, nw, nt, ta, wa, vo, la, lb, ga, gw);
+  else step_dma_1x4(acc, w, t, nw, nt, ta, wa, vo, la, lb, ga, gw);
 }
 
 template <int TM>
 __device__ __forceinline__ void last_step(f32x16_t (&acc)[TN][TM], const bf16x8_t (&w)[TN],
                                           const bf16x8_t (&t)[TM]) {
   if constexpr (TM == 4) last_4x4(acc, w, t);
-  else last_3x4(acc, w, t);
+  else if constexpr (TM == 3) last_3x4(acc, w, t);
+  else if constexpr (TM == 2) last_2x4(acc, w, t);
+  else last_1x4(acc, w, t);
 }
 
 template <int TM>
 __device__ __forceinline__ void read_frags(bf16x8_t (&nw)[TN], bf16x8_t (&nt)[TM], uint32_t ta,
                                            uint32_t wa) {
   if constexpr (TM == 4) frags_4x4(nw, nt, ta, wa);
-  else frags_3x4(nw, nt, ta, wa);
+  else if constexpr (TM == 3) frags_3x4(nw, nt, ta, wa);
+  else if constexpr (TM == 2) frags_2x4(nw, nt, ta, wa);
+  else frags_1x4(nw, nt, ta, wa);
 }
 
 template <int TM>
 __device__ __forceinline__ void issue_stage(const uint32_t (&ao)[2 * TM], const uint32_t (&bo)[2 * TN],
                                             uint32_t la, uint32_t lb, const char* ga, const char* gw) {
   if constexpr (TM == 4) stage_4x4(ao, bo, la, lb, ga, gw);
-  else stage_3x4(ao, bo, la, lb, ga, gw);
+  else if constexpr (TM == 3) stage_3x4(ao, bo, la, lb, ga, gw);
+  else if constexpr (TM == 2) stage_2x4(ao, bo, la, lb, ga, gw);
+  else stage_1x4(ao, bo, la, lb, ga, gw);
 }
 
 // The tile's bias slice (BN fp32 values, 1 KiB) goes to LDS with the tile's
@@ -215,7 +230,7 @@ __device__ __forceinline__ TileInfo decode_tile_wg(int tile, const int* s_tiles,
 }
 
 // Wait until the stage awaited has landed, with n (0 or 1) later stages of
-// G loads each still allowed in flight.
+// G loads each still allowed in flight (at most three stage buffers).
 template <int G>
 __device__ __forceinline__ void wait_loads(int n) {
   if (n >= 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G) : "memory");
@@ -325,6 +340,8 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
   constexpr int LA = BM / 32;        // 1 KiB (8-row) DMA blocks of the token tile per wave
   constexpr int LB = BN / 32;        // 1 KiB DMA blocks of the weight tile per wave
   constexpr int G = LA + LB;         // DMA loads per wave per stage
+  constexpr int NST = stages_for<TM>();
+  static_assert(NST * STAGE <= kLdsBytes, "stage buffers exceed the LDS array");
   const int Gd = gridDim.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -456,7 +473,11 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
 
 }  // namespace
 
-template <bool OUT_F32, int ACT>
+// SHORT selects the tile heights: 256 or 192 rows (experts that can fill
+// tall tiles), or 192, 128 or 64 rows (every expert holds fewer than 256
+// rows: decode batches, many experts). Two instantiations rather than one
+// kernel with all four: each keeps its own register allocation.
+template <bool OUT_F32, int ACT, bool SHORT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ row_idx,
                               const uint16_t* __restrict__ W,
@@ -464,64 +485,121 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
                               const int32_t* __restrict__ offsets, int E, int N, int K) {
   // the body uses gfx950 builtins only: the host pass needs just the signature
 #if defined(__HIP_DEVICE_COMPILE__)
-  __shared__ __attribute__((aligned(1024))) char lds[NST * (256 + BN) * ROWB];
+  __shared__ __attribute__((aligned(1024))) char lds[SHORT ? kLdsBytes : 2 * (256 + BN) * ROWB];
   __shared__ int s_tiles[1025];  // exclusive prefix of M tiles per expert
-  __shared__ int s_part[2][256];
+  __shared__ int s_part[SHORT ? 3 : 2][256];
   __shared__ __attribute__((aligned(16))) float s_bias[2][BN];  // bias slices of this and the next tile
 
   const int tid = threadIdx.x;
-  // ---- device-side schedule. Both tile heights are counted; the one whose
-  // tiles need fewer rounds of the persistent blocks (rounds x height: the
-  // work of a block) runs, the taller one on a tie.
   const int NT = (N + BN - 1) / BN;
   const int Gd = gridDim.x;
   const int per = (E + 255) / 256;
   const int eb = tid * per;
-  int c256 = 0, c192 = 0;
-  for (int e = eb; e < min(E, eb + per); ++e) {
-    const int n = offsets[e + 1] - offsets[e];
-    c256 += (n + 255) / 256;
-    c192 += (n + 191) / 192;
-  }
-  s_part[0][tid] = c256;
-  s_part[1][tid] = c192;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int a0 = (tid >= off) ? s_part[0][tid - off] : 0;
-    const int a1 = (tid >= off) ? s_part[1][tid - off] : 0;
-    __syncthreads();
-    s_part[0][tid] += a0;
-    s_part[1][tid] += a1;
-    __syncthreads();
-  }
-  const int64_t r256 = (static_cast<int64_t>(s_part[0][255]) * NT + Gd - 1) / Gd;
-  const int64_t r192 = (static_cast<int64_t>(s_part[1][255]) * NT + Gd - 1) / Gd;
-  const bool tall = r256 * 256 <= r192 * 192;
-  const int BMs = tall ? 256 : 192;
-  {
-    const int sel = tall ? 0 : 1;
-    int run = s_part[sel][tid] - (tall ? c256 : c192);
-    for (int e = eb; e < min(E, eb + per); ++e) {
-      s_tiles[e] = run;
-      run += (offsets[e + 1] - offsets[e] + BMs - 1) / BMs;
-    }
-    if (tid == 255) s_tiles[E] = s_part[sel][255];
-  }
-  __syncthreads();
-  const int total = s_tiles[E] * NT;
   const int b = blockIdx.x;
   // blocks are dealt to the 8 XCDs round-robin: renumber so that consecutive
   // tiles (which share weight and token panels) run on one XCD
   const int tile = (Gd % 8 == 0) ? (b % 8) * (Gd / 8) + b / 8 : b;
-  if (tile >= total) return;
-  if (tall)
-    tile_loop<4, OUT_F32, ACT, false>(A, row_idx, W, bias, out, offsets, E, N, K, K,
-                                      static_cast<int64_t>(N) * K, 0, lds, s_tiles, s_bias, tile,
-                               total, NT);
-  else
-    tile_loop<3, OUT_F32, ACT, false>(A, row_idx, W, bias, out, offsets, E, N, K, K,
-                                      static_cast<int64_t>(N) * K, 0, lds, s_tiles, s_bias, tile,
-                               total, NT);
+  const int64_t wes = static_cast<int64_t>(N) * K;
+  if constexpr (!SHORT) {
+    // ---- device-side schedule. Both tile heights are counted; the one
+    // whose tiles need fewer rounds of the persistent blocks (rounds x
+    // height: the work of a block) runs, the taller one on a tie.
+    int c256 = 0, c192 = 0;
+    for (int e = eb; e < min(E, eb + per); ++e) {
+      const int n = offsets[e + 1] - offsets[e];
+      c256 += (n + 255) / 256;
+      c192 += (n + 191) / 192;
+    }
+    s_part[0][tid] = c256;
+    s_part[1][tid] = c192;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int a0 = (tid >= off) ? s_part[0][tid - off] : 0;
+      const int a1 = (tid >= off) ? s_part[1][tid - off] : 0;
+      __syncthreads();
+      s_part[0][tid] += a0;
+      s_part[1][tid] += a1;
+      __syncthreads();
+    }
+    const int64_t r256 = (static_cast<int64_t>(s_part[0][255]) * NT + Gd - 1) / Gd;
+    const int64_t r192 = (static_cast<int64_t>(s_part[1][255]) * NT + Gd - 1) / Gd;
+    const bool tall = r256 * 256 <= r192 * 192;
+    const int BMs = tall ? 256 : 192;
+    {
+      const int sel = tall ? 0 : 1;
+      int run = s_part[sel][tid] - (tall ? c256 : c192);
+      for (int e = eb; e < min(E, eb + per); ++e) {
+        s_tiles[e] = run;
+        run += (offsets[e + 1] - offsets[e] + BMs - 1) / BMs;
+      }
+      if (tid == 255) s_tiles[E] = s_part[sel][255];
+    }
+    __syncthreads();
+    const int total = s_tiles[E] * NT;
+    if (tile >= total) return;
+    if (tall)
+      tile_loop<4, OUT_F32, ACT, false>(A, row_idx, W, bias, out, offsets, E, N, K, K, wes, 0, lds,
+                                        s_tiles, s_bias, tile, total, NT);
+    else
+      tile_loop<3, OUT_F32, ACT, false>(A, row_idx, W, bias, out, offsets, E, N, K, K, wes, 0, lds,
+                                        s_tiles, s_bias, tile, total, NT);
+  } else {
+    // ---- the same with heights 192, 128 and 64: the one with the least
+    // rounds(h) * (h + 64) (a tile's MFMA rows plus a fixed share for its
+    // weight panel, which short tiles stream with fewer MFMAs), the taller
+    // one on a tie
+    constexpr int kH[3] = {192, 128, 64};
+    int c[3] = {0, 0, 0};
+    for (int e = eb; e < min(E, eb + per); ++e) {
+      const int n = offsets[e + 1] - offsets[e];
+#pragma unroll
+      for (int q = 0; q < 3; ++q) c[q] += (n + kH[q] - 1) / kH[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) s_part[q][tid] = c[q];
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      int a[3];
+#pragma unroll
+      for (int q = 0; q < 3; ++q) a[q] = (tid >= off) ? s_part[q][tid - off] : 0;
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 3; ++q) s_part[q][tid] += a[q];
+      __syncthreads();
+    }
+    int sel = 0;
+    int64_t best = -1;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int64_t rounds = (static_cast<int64_t>(s_part[q][255]) * NT + Gd - 1) / Gd;
+      const int64_t cost = rounds * (kH[q] + 64);
+      if (best < 0 || cost < best) {
+        best = cost;
+        sel = q;
+      }
+    }
+    const int BMs = sel == 0 ? 192 : (sel == 1 ? 128 : 64);
+    {
+      int run = s_part[sel][tid] - c[sel];
+      for (int e = eb; e < min(E, eb + per); ++e) {
+        s_tiles[e] = run;
+        run += (offsets[e + 1] - offsets[e] + BMs - 1) / BMs;
+      }
+      if (tid == 255) s_tiles[E] = s_part[sel][255];
+    }
+    __syncthreads();
+    const int total = s_tiles[E] * NT;
+    if (tile >= total) return;
+    if (sel == 0)
+      tile_loop<3, OUT_F32, ACT, false>(A, row_idx, W, bias, out, offsets, E, N, K, K, wes, 0, lds,
+                                        s_tiles, s_bias, tile, total, NT);
+    else if (sel == 1)
+      tile_loop<2, OUT_F32, ACT, false>(A, row_idx, W, bias, out, offsets, E, N, K, K, wes, 0, lds,
+                                        s_tiles, s_bias, tile, total, NT);
+    else
+      tile_loop<1, OUT_F32, ACT, false>(A, row_idx, W, bias, out, offsets, E, N, K, K, wes, 0, lds,
+                                        s_tiles, s_bias, tile, total, NT);
+  }
 #endif
 }
 
@@ -536,7 +614,7 @@ void grouped_wgrad_bf16_kernel(const uint16_t* __restrict__ At, const uint16_t* 
                                const int32_t* __restrict__ poff, int E, int M, int N, int lda,
                                float* __restrict__ C) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __shared__ __attribute__((aligned(1024))) char lds[NST * (256 + BN) * ROWB];
+  __shared__ __attribute__((aligned(1024))) char lds[2 * (256 + BN) * ROWB];
   __shared__ int s_tiles[1025];
   __shared__ int s_part[256];
   __shared__ __attribute__((aligned(16))) float s_bias[2][BN];
@@ -595,22 +673,28 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uin
                             const float* bias, void* out,
                             bool out_f32, int act, const int32_t* offsets, int E, int N, int K,
                             int64_t max_rows, int max_rows_per_expert, hipStream_t s) {
-  (void)max_rows_per_expert;
   if (max_rows <= 0) return hipSuccess;
-  // upper bound on tiles of the shorter height: sum_e ceil(n_e/192) <= max_rows/192 + E
-  const int64_t mt_bound = max_rows / 192 + E;
+  // short tiles when no expert can fill a 256-row tile
+  const bool shorter = max_rows_per_expert < 256;
+  // upper bound on tiles: sum_e ceil(n_e/h) <= max_rows/h + E for the shortest h
+  const int64_t mt_bound = max_rows / (shorter ? 64 : 192) + E;
   const int slots = cu_count();
   const int64_t tiles = mt_bound * ((N + BN - 1) / BN);
   const unsigned grid = static_cast<unsigned>(tiles < slots ? tiles : slots);
-  if (out_f32) {
-    grouped_gemm_bf16_kernel<true, kActNone><<<grid, 256, 0, s>>>(A, row_idx, W, bias, out, offsets, E, N, K);
-  } else if (act == kActRelu) {
-    grouped_gemm_bf16_kernel<false, kActRelu><<<grid, 256, 0, s>>>(A, row_idx, W, bias, out, offsets, E, N, K);
-  } else if (act == kActGeluTanh) {
-    grouped_gemm_bf16_kernel<false, kActGeluTanh><<<grid, 256, 0, s>>>(A, row_idx, W, bias, out, offsets, E, N, K);
-  } else {
-    grouped_gemm_bf16_kernel<false, kActNone><<<grid, 256, 0, s>>>(A, row_idx, W, bias, out, offsets, E, N, K);
-  }
+#define MOE_GEMM(OF, AC)                                                                          \
+  do {                                                                                            \
+    if (shorter)                                                                                  \
+      grouped_gemm_bf16_kernel<OF, AC, true><<<grid, 256, 0, s>>>(A, row_idx, W, bias, out,       \
+                                                                  offsets, E, N, K);              \
+    else                                                                                          \
+      grouped_gemm_bf16_kernel<OF, AC, false><<<grid, 256, 0, s>>>(A, row_idx, W, bias, out,      \
+                                                                   offsets, E, N, K);             \
+  } while (0)
+  if (out_f32) MOE_GEMM(true, kActNone);
+  else if (act == kActRelu) MOE_GEMM(false, kActRelu);
+  else if (act == kActGeluTanh) MOE_GEMM(false, kActGeluTanh);
+  else MOE_GEMM(false, kActNone);
+#undef MOE_GEMM
   return hipGetLastError();
 }
 

@@ -12,7 +12,7 @@ because every operand index depends on the tile shape.
 """
 import os
 
-SHAPES = [(4, 4), (3, 4)]  # (TM, TN): 256 x 256 and 192 x 256 block tiles
+SHAPES = [(4, 4), (3, 4), (2, 4), (1, 4)]  # (TM, TN): 256, 192, 128 and 64 x 256 block tiles
 
 
 def q(s):
