@@ -13,10 +13,14 @@ namespace moe {
 //
 // A block computes a (16*MT tokens) x (16*NT experts) tile of the logits with
 // v_mfma_f32_16x16x32_bf16: x rows are the A operand, W_r rows the B operand.
-// The four waves split the d axis (wave w takes the 32-wide K steps w, w+4,
+// The four waves split the d axis (wave w takes the 64-wide K steps w, w+4,
 // ...); their partial sums meet in LDS and are added in a fixed order.
 // Operands come straight from global memory: the kernel streams x once and
-// re-reads W_r (E*d*2 bytes) from L2 per token tile.
+// re-reads W_r (E*d*2 bytes) from L2 per token tile. In a 64-wide step lane
+// group g holds k = 16g .. 16g+15 of its row (32 contiguous bytes, so the
+// 4 groups of a row cover a whole 128-byte line) and feeds them to two
+// MFMAs, k = 16g .. 16g+7 and 16g+8 .. 16g+15; x and W_r use the same
+// split, so every product is formed once.
 template <int MT, int NT>
 __global__ __launch_bounds__(256) void logits_bf16_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ Wr,
@@ -29,7 +33,7 @@ __global__ __launch_bounds__(256) void logits_bf16_kernel(const uint16_t* __rest
   const int wave = threadIdx.x >> 6;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * (16 * MT);
   const int e0 = blockIdx.y * (16 * NT);
-  const int kq = (lane >> 4) * 8;  // this lane's 8 consecutive k inside a 32-wide step
+  const int kq = (lane >> 4) * 16;  // this lane's 16 consecutive k inside a 64-wide step
 
   const uint16_t* xr[MT];
   const uint16_t* wr[NT];
@@ -54,22 +58,28 @@ __global__ __launch_bounds__(256) void logits_bf16_kernel(const uint16_t* __rest
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = wave * 32; k0 < d; k0 += 128) {
-    bf16x8_t a[MT], b[NT];
+  for (int k0 = wave * 64; k0 < d; k0 += 256) {
+    bf16x8_t a[2][MT], b[2][NT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      a[mt] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xr[mt] + k0));
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      uint4 v = *reinterpret_cast<const uint4*>(wr[nt] + k0);
-      if (!wvalid[nt]) v = make_uint4(0, 0, 0, 0);
-      b[nt] = __builtin_bit_cast(bf16x8_t, v);
-    }
+      for (int mt = 0; mt < MT; ++mt)
+        a[h][mt] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xr[mt] + k0 + 8 * h));
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
+      for (int nt = 0; nt < NT; ++nt) {
+        uint4 v = *reinterpret_cast<const uint4*>(wr[nt] + k0 + 8 * h);
+        if (!wvalid[nt]) v = make_uint4(0, 0, 0, 0);
+        b[h][nt] = __builtin_bit_cast(bf16x8_t, v);
+      }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[h][mt], b[h][nt], acc[mt][nt], 0, 0, 0);
   }
 
   if (wave > 0) {
