@@ -148,18 +148,34 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(
   const int nt = static_cast<int>(min<int64_t>(kTileTokens, T - t0));
   const int np = nt * k;
   // s_base[e] = sum of hist[t2][e] over tiles t2 before this one, s_cnt[e] the
-  // sum over all tiles.
+  // sum over all tiles. Tiles first, first + stride, ...: eight loads are
+  // issued before their sums (the loop is bound by load latency; integer
+  // sums do not depend on the order).
+  auto tile_sums = [&](int e, int first, int stride, int& b, int& c) {
+    int t2 = first;
+    for (; t2 + 7 * stride < ntiles; t2 += 8 * stride) {
+      int h[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) h[u] = hist[static_cast<int64_t>(t2 + u * stride) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (t2 + u * stride < tile) b += h[u];
+        c += h[u];
+      }
+    }
+    for (; t2 < ntiles; t2 += stride) {
+      const int h = hist[static_cast<int64_t>(t2) * E + e];
+      if (t2 < tile) b += h;
+      c += h;
+    }
+  };
   if (256 % E == 0) {
     // E divides 256: read hist flat and coalesced; thread tid always meets
     // expert tid % E, in tiles tid / E, tid / E + 256 / E, ...
     const int P = 256 / E;
     const int e = tid % E;
     int b = 0, c = 0;
-    for (int t2 = tid / E; t2 < ntiles; t2 += P) {
-      const int h = hist[static_cast<int64_t>(t2) * E + e];
-      if (t2 < tile) b += h;
-      c += h;
-    }
+    tile_sums(e, tid / E, P, b, c);
     s_part[0][tid] = b;
     s_part[1][tid] = c;
     __syncthreads();
@@ -176,11 +192,7 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(
   } else {
     for (int e = tid; e < E; e += 256) {
       int b = 0, c = 0;
-      for (int t2 = 0; t2 < ntiles; ++t2) {
-        const int h = hist[static_cast<int64_t>(t2) * E + e];
-        if (t2 < tile) b += h;
-        c += h;
-      }
+      tile_sums(e, 0, 1, b, c);
       s_base[e] = b;
       s_cnt[e] = c;
     }
