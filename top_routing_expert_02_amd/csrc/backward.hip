@@ -71,6 +71,51 @@ __global__ __launch_bounds__(256) void transpose_kernel(const TE* __restrict__ s
   }
 }
 
+// bf16 transposes move 4-byte pairs: a thread reads the same two columns of
+// two consecutive rows, repacks them into two (row, row+1) pairs of the
+// transposed matrix and the tile goes through LDS in 32-bit words (pitch 33:
+// conflict-free). row_ptr(i) gives source row i of the 64-row tile, or null
+// for a row of zeros; the tile lands at dst[c][dcol0 + i].
+template <typename RowPtr>
+__device__ __forceinline__ void transpose_tile_bf16(RowPtr row_ptr, int c0, int Cc, uint16_t* dst,
+                                                    int64_t ldd, int64_t dcol0) {
+  __shared__ uint32_t t32[64][33];
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rp = ty + 8 * i;  // row pair
+    const uint16_t* ra = row_ptr(2 * rp);
+    const uint16_t* rb = row_ptr(2 * rp + 1);
+    const int c = c0 + 2 * tx;
+    uint32_t a = 0, b = 0;
+    if (c < Cc) {
+      if (ra != nullptr) a = *reinterpret_cast<const uint32_t*>(ra + c);
+      if (rb != nullptr) b = *reinterpret_cast<const uint32_t*>(rb + c);
+    }
+    t32[2 * tx][rp] = (a & 0xFFFFu) | (b << 16);
+    t32[2 * tx + 1][rp] = (a >> 16) | (b & 0xFFFF0000u);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int cl = ty + 8 * i;
+    if (c0 + cl < Cc)
+      *reinterpret_cast<uint32_t*>(dst + static_cast<int64_t>(c0 + cl) * ldd + dcol0 + 2 * tx) = t32[cl][tx];
+  }
+}
+
+// dst[e][c][r] = src[e][r][c] for bf16, R and Cc even
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src,
+                                                             uint16_t* __restrict__ dst, int R, int Cc) {
+  const int64_t e = blockIdx.z;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const uint16_t* s = src + e * R * static_cast<int64_t>(Cc);
+  uint16_t* d = dst + e * R * static_cast<int64_t>(Cc);
+  transpose_tile_bf16([&](int i) -> const uint16_t* {
+    return (r0 + i < R) ? s + static_cast<int64_t>(r0 + i) * Cc : nullptr;
+  }, c0, Cc, d, R, r0);
+}
+
 __global__ __launch_bounds__(256) void row_info_kernel(const int32_t* __restrict__ ids,
                                                        const float* __restrict__ gates,
                                                        const int32_t* __restrict__ row_of,
@@ -379,6 +424,33 @@ __global__ __launch_bounds__(256) void padded_transpose_kernel(const TE* __restr
   }
 }
 
+// the same for bf16 through 4-byte pairs (see transpose_tile_bf16)
+__global__ __launch_bounds__(256) void padded_transpose_bf16_kernel(const uint16_t* __restrict__ src,
+                                                                    const int32_t* __restrict__ row_idx,
+                                                                    const int32_t* __restrict__ offsets,
+                                                                    const int32_t* __restrict__ poff, int E,
+                                                                    int Cc, int ldd,
+                                                                    uint16_t* __restrict__ dst) {
+  const int p0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  if (p0 >= poff[E]) return;
+  int lo = 0, hi = E - 1;  // the expert e with poff[e] <= p0 < poff[e+1]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (poff[mid] <= p0) lo = mid;
+    else hi = mid - 1;
+  }
+  const int ne = offsets[lo + 1] - offsets[lo];
+  const int first = p0 - poff[lo];
+  const int64_t rbase = offsets[lo];
+  transpose_tile_bf16([&](int i) -> const uint16_t* {
+    const int local = first + i;
+    if (local >= ne) return nullptr;
+    const int64_t r = rbase + local;
+    const int64_t row = row_idx != nullptr ? row_idx[r] : r;
+    return src + row * Cc;
+  }, c0, Cc, dst, ldd, p0);
+}
+
 // out[e][m] = sum of At[m][poff[e] .. poff[e+1]) (zero padding included);
 // one wave per (m, e), lanes in a fixed order
 template <typename TE>
@@ -421,8 +493,8 @@ hipError_t launch_transpose(const void* src, void* dst, int groups, int R, int C
                             hipStream_t s) {
   dim3 grid(blocks(Cc, 64), blocks(R, 64), groups);
   if (bf16)
-    transpose_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(src),
-                                                    static_cast<uint16_t*>(dst), R, Cc);
+    transpose_bf16_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(src),
+                                               static_cast<uint16_t*>(dst), R, Cc);
   else
     transpose_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(src),
                                                  static_cast<float*>(dst), R, Cc);
@@ -506,9 +578,8 @@ hipError_t launch_padded_transpose(const void* src, const int32_t* row_idx, cons
   if (max_padded <= 0) return hipSuccess;
   dim3 grid(blocks(Cc, 64), blocks(max_padded, 64));
   if (bf16)
-    padded_transpose_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(src), row_idx,
-                                                           offsets, poff, E, Cc, ld,
-                                                           static_cast<uint16_t*>(dst));
+    padded_transpose_bf16_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(src), row_idx, offsets,
+                                                      poff, E, Cc, ld, static_cast<uint16_t*>(dst));
   else
     padded_transpose_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(src), row_idx, offsets,
                                                         poff, E, Cc, ld, static_cast<float*>(dst));

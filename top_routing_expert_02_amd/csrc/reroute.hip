@@ -100,24 +100,65 @@ __global__ __launch_bounds__(kRrTile) void rr_hist_kernel(Order o, int64_t Q, co
   for (int i = threadIdx.x; i < E; i += kRrTile) h[i] = s_hist[i];
 }
 
-// one block; thread e walks the tiles of expert e
+// one block: P = 1024 / E (rounded down to a power of two) threads per
+// expert, each owning a contiguous run of tiles; a first pass sums each run,
+// an exclusive prefix over the runs (in LDS) gives each its starting base,
+// a second pass writes the bases. Loads go out eight at a time (the passes
+// are bound by load latency).
 __global__ __launch_bounds__(1024) void rr_scan_kernel(const int32_t* __restrict__ hist, int ntiles, int E,
                                                        int C, int round, int32_t* __restrict__ base,
                                                        int32_t* __restrict__ fill,
                                                        int32_t* __restrict__ fill0,
                                                        int32_t* __restrict__ counts) {
-  const int e = threadIdx.x;
-  if (e >= E) return;
+  __shared__ int part[1024];
+  int P = 1;
+  while (P * 2 * E <= 1024) P *= 2;
+  const int tid = threadIdx.x;
+  const bool active = tid < P * E;
+  const int e = tid % E;
+  const int p = tid / E;
+  const int chunk = (ntiles + P - 1) / P;
+  const int t_begin = min(ntiles, p * chunk);
+  const int t_end = min(ntiles, t_begin + chunk);
+  int sum = 0;
+  if (active) {
+    int t = t_begin;
+    for (; t + 8 <= t_end; t += 8) {
+      int h[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) h[u] = hist[static_cast<int64_t>(t + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum += h[u];
+    }
+    for (; t < t_end; ++t) sum += hist[static_cast<int64_t>(t) * E + e];
+    part[p * E + e] = sum;
+  }
+  __syncthreads();
+  if (!active) return;
   int run = 0;
-  for (int t = 0; t < ntiles; ++t) {
+  for (int q = 0; q < p; ++q) run += part[q * E + e];
+  int t = t_begin;
+  for (; t + 8 <= t_end; t += 8) {
+    int h[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) h[u] = hist[static_cast<int64_t>(t + u) * E + e];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      base[static_cast<int64_t>(t + u) * E + e] = run;
+      run += h[u];
+    }
+  }
+  for (; t < t_end; ++t) {
     const int64_t i = static_cast<int64_t>(t) * E + e;
     base[i] = run;
     run += hist[i];
   }
-  const int f = fill[e];
-  fill0[e] = f;
-  fill[e] = min(C, f + run);
-  if (round == 0 && counts != nullptr) counts[e] = run;
+  if (p == P - 1) {  // run is now the expert's total over all tiles
+    const int f = fill[e];
+    fill0[e] = f;
+    fill[e] = min(C, f + run);
+    if (round == 0 && counts != nullptr) counts[e] = run;
+  }
 }
 
 __global__ __launch_bounds__(kRrTile) void rr_place_kernel(Order o, int64_t Q, const int32_t* __restrict__ cand,
