@@ -276,23 +276,15 @@ __device__ __forceinline__ void tile_sources(const TileInfo& t, const uint16_t* 
   }
 }
 
-// Bias, activation, conversion and stores of one wave's (32 TM) x 128
-// outputs. s_bias: the tile's bias slice in LDS (null: no bias). FULL: every
-// row and feature of the tile is in range (no per-lane checks).
+// Activation, conversion and stores of one wave's (32 TM) x 128 outputs (the
+// accumulators started at the bias). FULL: every row and feature of the tile
+// is in range (no per-lane checks).
 template <int TM, bool OUT_F32, int ACT, bool FULL>
-__device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], const float* s_bias,
-                                         void* __restrict__ out, const TileInfo& t, int N, int wm,
-                                         int wn, int l5, int hi) {
+__device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], void* __restrict__ out,
+                                         const TileInfo& t, int N, int wm, int wn, int l5, int hi) {
   constexpr int WM = 32 * TM;
   const int fb = wn * WN + hi * 4;  // this lane's first feature in the tile
   const int nb = t.n0 + fb;
-  float4 bq[TN][4];
-#pragma unroll
-  for (int i = 0; i < TN; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      bq[i][q] = (s_bias != nullptr) ? *reinterpret_cast<const float4*>(s_bias + fb + i * 32 + q * 8)
-                                     : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
     const int m = wm * WM + j * 32 + l5;
@@ -303,10 +295,10 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], const fl
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (!FULL && nb + i * 32 + q * 8 >= N) continue;
-        const float v0 = activate<ACT>(acc[i][j][4 * q + 0] + bq[i][q].x);
-        const float v1 = activate<ACT>(acc[i][j][4 * q + 1] + bq[i][q].y);
-        const float v2 = activate<ACT>(acc[i][j][4 * q + 2] + bq[i][q].z);
-        const float v3 = activate<ACT>(acc[i][j][4 * q + 3] + bq[i][q].w);
+        const float v0 = activate<ACT>(acc[i][j][4 * q + 0]);
+        const float v1 = activate<ACT>(acc[i][j][4 * q + 1]);
+        const float v2 = activate<ACT>(acc[i][j][4 * q + 2]);
+        const float v3 = activate<ACT>(acc[i][j][4 * q + 3]);
         const int64_t o = orow + i * 32 + q * 8;
         if constexpr (OUT_F32) {
           *reinterpret_cast<float4*>(static_cast<float*>(out) + o) = make_float4(v0, v1, v2, v3);
@@ -388,17 +380,32 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     // K stages of this tile (cur moves on before its epilogue); the same for
     // every expert-FFN tile
     const int nk = WG ? cur.nk : K / BK;
-    f32x16_t acc[TN][TM];
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-      for (int j = 0; j < TM; ++j)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-    // the tile's first stages (and, after an epilogue, its stores)
+    // the tile's first stages and bias slice (and, after an epilogue, its
+    // stores)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    // accumulators start at the bias: lane (l5, hi) holds features
+    // fb + 32 i + 8 q + {0..3} of tile i (the same for every token tile j)
+    f32x16_t acc[TN][TM];
+    {
+      const int fb = wn * WN + hi * 4;
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 b = (bias != nullptr)
+                               ? *reinterpret_cast<const float4*>(&s_bias[par][fb + i * 32 + q * 8])
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+          for (int j = 0; j < TM; ++j) {
+            acc[i][j][4 * q + 0] = b.x;
+            acc[i][j][4 * q + 1] = b.y;
+            acc[i][j][4 * q + 2] = b.z;
+            acc[i][j][4 * q + 3] = b.w;
+          }
+        }
+    }
     bf16x8_t wf0[TN], tf0[TM], wf1[TN], tf1[TM];
     read_frags<TM>(wf0, tf0, lds_base + trow + fo[0], lds_base + wrow + fo[0]);
 
@@ -461,10 +468,9 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
 
     // ---- epilogue: lane holds token l5 of each 32-token tile j and
     // features 8q + 4*hi + {0..3} of each 32-feature tile i
-    const float* sbias = (bias != nullptr) ? &s_bias[par][0] : nullptr;
     const bool full_tile = done.rv == BM && done.n0 + BN <= N;
-    if (full_tile) epilogue<TM, OUT_F32, ACT, true>(acc, sbias, out, done, N, wm, wn, l5, hi);
-    else epilogue<TM, OUT_F32, ACT, false>(acc, sbias, out, done, N, wm, wn, l5, hi);
+    if (full_tile) epilogue<TM, OUT_F32, ACT, true>(acc, out, done, N, wm, wn, l5, hi);
+    else epilogue<TM, OUT_F32, ACT, false>(acc, out, done, N, wm, wn, l5, hi);
     if (next >= total) break;
     tile = next;
     par ^= 1;
