@@ -35,10 +35,13 @@
 //    swizzle places at its LDS slot.
 //  * Two stage buffers (three for tiles of 128 or 64 rows). A stage is four K16 steps; each step's MFMAs run with
 //    the next step's fragment reads in flight, and the buffer a stage occupied
-//    is refilled (with the stage after next) between the MFMAs of that
-//    stage's last step, right after the barrier that shows every wave has
-//    read it. The next tile's first stages, and its bias slice, load during
-//    the current tile's last step and epilogue.
+//    is refilled (with the stage after next) right after the barrier that
+//    shows every wave has read it: half of the loads between the MFMAs of
+//    that stage's last step, the other half between those of the next
+//    stage's first step (a whole stage's loads at once back up the load
+//    queue, and the wave stalls at an MFMA issue slot). The next tile's first
+//    stages, and its bias slice, load during the current tile's last step and
+//    epilogue.
 //  * Persistent blocks, one per CU. The schedule is computed on the device
 //    from expert_offsets (no host read-back): expert-major tiles, M tiles of
 //    an expert innermost, so concurrent tiles share weight panels. Blocks are
@@ -47,6 +50,8 @@
 //  * Ragged M: rows past an expert's end read that expert's last row and are
 //    never stored, so no tile reads outside [0, rows).
 #include "moe_internal.h"
+
+#include <type_traits>
 
 namespace moe {
 
@@ -90,7 +95,9 @@ __device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
 // LDS-DMA loads take their LDS destination from M0 (lane L writes bytes
 // 16L..16L+15 of a 1 KiB block); an instruction sits between each M0 write
 // and the load that uses it. M0 is reserved by the compiler; the clobber
-// orders its own uses against these blocks. Every LDS-DMA load of this kernel
+// orders its own uses against these blocks. The M0 sums also write SCC, which
+// the compiler may hold a comparison in across a block: it is clobbered
+// too. Every LDS-DMA load of this kernel
 // is issued from asm, so the compiler tracks none of them: it would otherwise
 // wait for all of them before reusing an address register or reading any
 // LDS, which would stall each epilogue on the next tile's prefetch.
@@ -106,16 +113,24 @@ __device__ __forceinline__ void step(f32x16_t (&acc)[TN][TM], const bf16x8_t (&w
   else step_1x4(acc, w, t, nw, nt, ta, wa);
 }
 
-template <int TM>
+// HALF 0: the first half of a stage's LDS-DMA loads, 1: the rest
+template <int TM, int HALF>
 __device__ __forceinline__ void step_dma(f32x16_t (&acc)[TN][TM], const bf16x8_t (&w)[TN],
                                          const bf16x8_t (&t)[TM], bf16x8_t (&nw)[TN],
                                          bf16x8_t (&nt)[TM], uint32_t ta, uint32_t wa,
                                          const uint32_t (&vo)[2 * TM + 2 * TN], uint32_t la, uint32_t lb,
                                          const char* ga, const char* gw) {
-  if constexpr (TM == 4) step_dma_4x4(acc, w, t, nw, nt, ta, wa, vo, la, lb, ga, gw);
-  else if constexpr (TM == 3) step_dma_3x4(acc, w, t, nw, nt, ta, wa, vo, la, lb, ga, gw);
-  else if constexpr (TM == 2) step_dma_2x4(acc, w, t, nw, nt, ta, wa, vo, la, lb, ga, gw);
-  else step_dma_1x4(acc, w, t, nw, nt, ta, wa, vo, la, lb, ga, gw);
+  if constexpr (HALF == 0) {
+    if constexpr (TM == 4) step_dma0_4x4(acc, w, t, nw, nt, ta, wa, vo, la, lb, ga, gw);
+    else if constexpr (TM == 3) step_dma0_3x4(acc, w, t, nw, nt, ta, wa, vo, la, lb, ga, gw);
+    else if constexpr (TM == 2) step_dma0_2x4(acc, w, t, nw, nt, ta, wa, vo, la, lb, ga, gw);
+    else step_dma0_1x4(acc, w, t, nw, nt, ta, wa, vo, la, lb, ga, gw);
+  } else {
+    if constexpr (TM == 4) step_dma1_4x4(acc, w, t, nw, nt, ta, wa, vo, la, lb, ga, gw);
+    else if constexpr (TM == 3) step_dma1_3x4(acc, w, t, nw, nt, ta, wa, vo, la, lb, ga, gw);
+    else if constexpr (TM == 2) step_dma1_2x4(acc, w, t, nw, nt, ta, wa, vo, la, lb, ga, gw);
+    else step_dma1_1x4(acc, w, t, nw, nt, ta, wa, vo, la, lb, ga, gw);
+  }
 }
 
 template <int TM>
@@ -170,14 +185,24 @@ __device__ __forceinline__ float activate(float v) {
 
 // One output tile: expert e, output rows [row0, row0 + rv) (rv valid of the
 // tile's height), features from n0; operand A's first row arow and K range
-// [k0, k0 + 64 nk).
+// [k0, k0 + 64 nk); part: which K half (split launches write the second half's
+// partial sums to their own buffer).
 struct TileInfo {
-  int e, row0, rv, n0, arow, k0, nk;
+  int e, row0, rv, n0, arow, k0, nk, part;
 };
 
-// s_tiles[e]: exclusive prefix over experts of their M tiles of height BM.
-__device__ __forceinline__ TileInfo decode_tile(int tile, const int* s_tiles, const int32_t* offsets,
-                                                int E, int NT, int BM, int nk) {
+// Epilogue cost of an fp32 output tile in K-equivalents (its stores take
+// about as long as 512 more K per row of MFMA work); weighs a K split, which
+// doubles the stores, against the rounds it saves.
+constexpr int kEpiK = 512;
+
+// s_tiles[e]: exclusive prefix over experts of their M tiles of height BM;
+// ntiles output tiles, each in K parts of nk stages (unit u covers tile
+// u mod ntiles, part u / ntiles; at most two parts).
+__device__ __forceinline__ TileInfo decode_tile(int u, const int* s_tiles, const int32_t* offsets,
+                                                int E, int NT, int BM, int nk, int ntiles) {
+  const int part = u >= ntiles ? 1 : 0;
+  const int tile = u - part * ntiles;
   // expert: the largest e with s_tiles[e] * NT <= tile (experts with no
   // rows share their successor's prefix and are skipped)
   int lo = 0, hi = E - 1;
@@ -189,15 +214,16 @@ __device__ __forceinline__ TileInfo decode_tile(int tile, const int* s_tiles, co
   TileInfo t;
   t.e = lo;
   const int mte = s_tiles[lo + 1] - s_tiles[lo];
-  const int u = tile - s_tiles[lo] * NT;
-  const int nt = u / mte;  // M tiles of an expert are innermost
-  const int mt = u - nt * mte;
+  const int v = tile - s_tiles[lo] * NT;
+  const int nt = v / mte;  // M tiles of an expert are innermost
+  const int mt = v - nt * mte;
   t.row0 = offsets[lo] + mt * BM;
   t.rv = min(BM, offsets[lo + 1] - t.row0);
   t.n0 = nt * BN;
   t.arow = t.row0;
-  t.k0 = 0;
+  t.k0 = part * nk * BK;
   t.nk = nk;
+  t.part = part;
   return t;
 }
 
@@ -226,6 +252,7 @@ __device__ __forceinline__ TileInfo decode_tile_wg(int tile, const int* s_tiles,
   t.n0 = nt * BN;
   t.k0 = poff[lo];
   t.nk = (poff[lo + 1] - poff[lo]) / BK;
+  t.part = 0;
   return t;
 }
 
@@ -309,6 +336,10 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], void* __
           *reinterpret_cast<bf16x4_t*>(static_cast<uint16_t*>(out) + o) = h;
         }
       }
+      // one 32x32 tile at a time: the scheduler may not hoist the next
+      // tile's accumulator reads above these stores (that needs more VGPRs
+      // than the next tile's prefetch state leaves free)
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -316,15 +347,17 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], void* __
 // The persistent tile loop for tiles of BM = 64 TM rows. lds: NST stage
 // buffers; s_tiles: the M-tile prefix for this height; s_bias: two slices.
 // WG: weight-gradient tiles (decode_tile_wg; offsets holds the padded K
-// offsets, M the rows of C per expert); else expert-FFN tiles with K/64
-// stages each.
+// offsets, M the rows of C per expert); else expert-FFN tiles of nkl stages
+// each: ntiles output tiles, and total = ntiles (whole K) or 2 ntiles (two K
+// halves; the second half's partial sums go to out2, without bias).
 template <int TM, bool OUT_F32, int ACT, bool WG>
 __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const int32_t* __restrict__ row_idx,
                                           const uint16_t* __restrict__ W, const float* __restrict__ bias,
-                                          void* __restrict__ out, const int32_t* __restrict__ offsets,
-                                          int E, int N, int K, int lda, int64_t w_estride, int M,
+                                          void* __restrict__ out, void* __restrict__ out2,
+                                          const int32_t* __restrict__ offsets,
+                                          int E, int N, int nkl, int lda, int64_t w_estride, int M,
                                           char* lds, const int* s_tiles, float (*s_bias)[BN], int tile,
-                                          int total, int NT) {
+                                          int total, int ntiles, int NT) {
   constexpr int BM = 64 * TM;
   constexpr int WM = BM / 2;         // tokens per wave
   constexpr int A_BYTES = BM * ROWB;
@@ -351,7 +384,7 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
   const int drow = lane >> 3, dpos = lane & 7;
   auto decode = [&](int tl) {
     if constexpr (WG) return decode_tile_wg(tl, s_tiles, offsets, E, NT, BM, M);
-    else return decode_tile(tl, s_tiles, offsets, E, NT, BM, K / BK);
+    else return decode_tile(tl, s_tiles, offsets, E, NT, BM, nkl, ntiles);
   };
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
   const uint32_t trow = wm * WM * ROWB;            // this wave's token rows in a stage
@@ -362,11 +395,11 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
   const char* Wbase;
   // a tile's first stages and its bias slice (wave 0, one lane per 4 features)
   auto prologue = [&](const TileInfo& c, int par) {
-    for (int p = 0; p < NST && p < (WG ? c.nk : K / BK); ++p)
+    for (int p = 0; p < NST && p < (WG ? c.nk : nkl); ++p)
       issue_stage<TM>(aoffs, boffs, lds_base + p * STAGE + wave * LA * 1024,
                       lds_base + p * STAGE + A_BYTES + wave * LB * 1024, Abase + p * ROWB,
                       Wbase + p * ROWB);
-    if (bias != nullptr && wave == 0)
+    if (bias != nullptr && c.part == 0 && wave == 0)
       issue_bias(bias + static_cast<int64_t>(c.e) * N + min(c.n0 + 4 * lane, N - 4),
                  static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&s_bias[par][0])));
   };
@@ -379,7 +412,7 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
   for (;;) {
     // K stages of this tile (cur moves on before its epilogue); the same for
     // every expert-FFN tile
-    const int nk = WG ? cur.nk : K / BK;
+    const int nk = WG ? cur.nk : nkl;
 
     // the tile's first stages and bias slice (and, after an epilogue, its
     // stores)
@@ -389,12 +422,13 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     // fb + 32 i + 8 q + {0..3} of tile i (the same for every token tile j)
     f32x16_t acc[TN][TM];
     {
+      const bool with_bias = bias != nullptr && cur.part == 0;
       const int fb = wn * WN + hi * 4;
 #pragma unroll
       for (int i = 0; i < TN; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float4 b = (bias != nullptr)
+          const float4 b = with_bias
                                ? *reinterpret_cast<const float4*>(&s_bias[par][fb + i * 32 + q * 8])
                                : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -418,39 +452,58 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     int sc = 0;              // buffer holding K stage t
     uint32_t sb = lds_base;  // its LDS address
     int t = 0;
-    // steady state: stage t+NST still to load
-    for (; t + NST < nk; ++t) {
-      // K16 steps 0..2 of stage t, each reading the next step's fragments
-      step<TM>(acc, wf0, tf0, wf1, tf1, sb + trow + fo[1], sb + wrow + fo[1]);
+    // the second half of the last refill, issued with the next stage's first
+    // K16 step: its LDS and global bases
+    uint32_t pla = 0, plb = 0;
+    const char* pga = nullptr;
+    const char* pgw = nullptr;
+    // One K stage. D1: step 0 issues the second half of the previous stage's
+    // refill; RF: stage t+NST is still to load (this stage's buffer takes it
+    // once every wave has read the stage).
+    auto stage = [&](auto d1, auto rf) {
+      // K16 steps 0..2, each reading the next step's fragments
+      if constexpr (decltype(d1)::value)
+        step_dma<TM, 1>(acc, wf0, tf0, wf1, tf1, sb + trow + fo[1], sb + wrow + fo[1], vo, pla, plb, pga,
+                        pgw);
+      else
+        step<TM>(acc, wf0, tf0, wf1, tf1, sb + trow + fo[1], sb + wrow + fo[1]);
       step<TM>(acc, wf1, tf1, wf0, tf0, sb + trow + fo[2], sb + wrow + fo[2]);
       step<TM>(acc, wf0, tf0, wf1, tf1, sb + trow + fo[3], sb + wrow + fo[3]);
       // stage t+1 has landed and every wave has read its last fragments of
       // stage t
-      wait_loads<G>(NST - 2);
+      if constexpr (decltype(rf)::value) wait_loads<G>(NST - 2);
+      else wait_loads<G>(nk - 2 - t);
       __syncthreads();
       const int sn_i = (sc + 1 == NST) ? 0 : sc + 1;
       const uint32_t sn = lds_base + sn_i * STAGE;
-      // K16 step 3 of stage t; read step 0 of stage t+1; the buffer of stage
-      // t takes stage t+NST
-      step_dma<TM>(acc, wf1, tf1, wf0, tf0, sn + trow + fo[0], sn + wrow + fo[0], vo,
-                   sb + wave * LA * 1024, sb + A_BYTES + wave * LB * 1024,
-                   Abase + (t + NST) * ROWB, Wbase + (t + NST) * ROWB);
+      // K16 step 3; read step 0 of stage t+1
+      if constexpr (decltype(rf)::value) {
+        // the buffer of stage t takes stage t+NST: half of its loads now,
+        // the rest with step 0 of stage t+1
+        pla = sb + wave * LA * 1024;
+        plb = sb + A_BYTES + wave * LB * 1024;
+        pga = Abase + (t + NST) * ROWB;
+        pgw = Wbase + (t + NST) * ROWB;
+        step_dma<TM, 0>(acc, wf1, tf1, wf0, tf0, sn + trow + fo[0], sn + wrow + fo[0], vo, pla, plb, pga,
+                        pgw);
+      } else {
+        step<TM>(acc, wf1, tf1, wf0, tf0, sn + trow + fo[0], sn + wrow + fo[0]);
+      }
       sc = sn_i;
       sb = sn;
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+    if (t + NST < nk) {
+      // steady state; the first tail stage (there is one, as NST >= 2)
+      // issues the last refill's second half
+      stage(no{}, yes{});
+      for (++t; t + NST < nk; ++t) stage(yes{}, yes{});
+      stage(yes{}, no{});
+      ++t;
     }
     // the last stages: nothing more to load
-    for (; t + 1 < nk; ++t) {
-      step<TM>(acc, wf0, tf0, wf1, tf1, sb + trow + fo[1], sb + wrow + fo[1]);
-      step<TM>(acc, wf1, tf1, wf0, tf0, sb + trow + fo[2], sb + wrow + fo[2]);
-      step<TM>(acc, wf0, tf0, wf1, tf1, sb + trow + fo[3], sb + wrow + fo[3]);
-      wait_loads<G>(nk - 2 - t);
-      __syncthreads();
-      const int sn_i = (sc + 1 == NST) ? 0 : sc + 1;
-      const uint32_t sn = lds_base + sn_i * STAGE;
-      step<TM>(acc, wf1, tf1, wf0, tf0, sn + trow + fo[0], sn + wrow + fo[0]);
-      sc = sn_i;
-      sb = sn;
-    }
+    for (; t + 1 < nk; ++t) stage(no{}, no{});
     // the last stage
     step<TM>(acc, wf0, tf0, wf1, tf1, sb + trow + fo[1], sb + wrow + fo[1]);
     step<TM>(acc, wf1, tf1, wf0, tf0, sb + trow + fo[2], sb + wrow + fo[2]);
@@ -469,8 +522,9 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     // ---- epilogue: lane holds token l5 of each 32-token tile j and
     // features 8q + 4*hi + {0..3} of each 32-feature tile i
     const bool full_tile = done.rv == BM && done.n0 + BN <= N;
-    if (full_tile) epilogue<TM, OUT_F32, ACT, true>(acc, out, done, N, wm, wn, l5, hi);
-    else epilogue<TM, OUT_F32, ACT, false>(acc, out, done, N, wm, wn, l5, hi);
+    void* dst = done.part ? out2 : out;
+    if (full_tile) epilogue<TM, OUT_F32, ACT, true>(acc, dst, done, N, wm, wn, l5, hi);
+    else epilogue<TM, OUT_F32, ACT, false>(acc, dst, done, N, wm, wn, l5, hi);
     if (next >= total) break;
     tile = next;
     par ^= 1;
@@ -483,11 +537,17 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
 // tall tiles), or 192, 128 or 64 rows (every expert holds fewer than 256
 // rows: decode batches, many experts). Two instantiations rather than one
 // kernel with all four: each keeps its own register allocation.
+// out2 (fp32 output without activation only, else null): with it, the
+// schedule may split K in two halves when that fills more of the chip (few
+// output tiles, long K); the first half (with bias) goes to out, the second
+// to out2, and the number of parts (1 or 2) to *nsplit (when not null), so
+// out = out + out2 holds the product only when *nsplit is 2.
 template <bool OUT_F32, int ACT, bool SHORT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ row_idx,
                               const uint16_t* __restrict__ W,
                               const float* __restrict__ bias, void* __restrict__ out,
+                              void* __restrict__ out2, int32_t* __restrict__ nsplit,
                               const int32_t* __restrict__ offsets, int E, int N, int K) {
   // the body uses gfx950 builtins only: the host pass needs just the signature
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -506,10 +566,18 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
   // tiles (which share weight and token panels) run on one XCD
   const int tile = (Gd % 8 == 0) ? (b % 8) * (Gd / 8) + b / 8 : b;
   const int64_t wes = static_cast<int64_t>(N) * K;
+  // K parts allowed: two when out2 is given and K splits into whole stages
+  const int smax = (out2 != nullptr && (K / BK) % 2 == 0) ? 2 : 1;
+  // work of one block: rounds of units x (rows x (K per part + epilogue))
+  auto cost = [&](int64_t tiles, int rows, int S) {
+    const int64_t rounds = (tiles * S + Gd - 1) / Gd;
+    return rounds * rows * static_cast<int64_t>(K / S + kEpiK);
+  };
   if constexpr (!SHORT) {
-    // ---- device-side schedule. Both tile heights are counted; the one
-    // whose tiles need fewer rounds of the persistent blocks (rounds x
-    // height: the work of a block) runs, the taller one on a tie.
+    // ---- device-side schedule. Both tile heights are counted, each whole
+    // and (when allowed) split in K; the choice whose units need the least
+    // block work (cost above) runs: the taller height, then the unsplit one,
+    // on a tie.
     int c256 = 0, c192 = 0;
     for (int e = eb; e < min(E, eb + per); ++e) {
       const int n = offsets[e + 1] - offsets[e];
@@ -527,9 +595,18 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
       s_part[1][tid] += a1;
       __syncthreads();
     }
-    const int64_t r256 = (static_cast<int64_t>(s_part[0][255]) * NT + Gd - 1) / Gd;
-    const int64_t r192 = (static_cast<int64_t>(s_part[1][255]) * NT + Gd - 1) / Gd;
-    const bool tall = r256 * 256 <= r192 * 192;
+    bool tall = true;
+    int S = 1;
+    int64_t best = -1;
+    for (int sp = 1; sp <= smax; ++sp)
+      for (int q = 0; q < 2; ++q) {
+        const int64_t c = cost(static_cast<int64_t>(s_part[q][255]) * NT, q == 0 ? 256 : 192, sp);
+        if (best < 0 || c < best) {
+          best = c;
+          tall = q == 0;
+          S = sp;
+        }
+      }
     const int BMs = tall ? 256 : 192;
     {
       const int sel = tall ? 0 : 1;
@@ -541,19 +618,22 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
       if (tid == 255) s_tiles[E] = s_part[sel][255];
     }
     __syncthreads();
-    const int total = s_tiles[E] * NT;
+    if (nsplit != nullptr && b == 0 && tid == 0) *nsplit = S;
+    const int ntiles = s_tiles[E] * NT;
+    const int total = ntiles * S;
+    const int nkl = K / BK / S;
     if (tile >= total) return;
     if (tall)
-      tile_loop<4, OUT_F32, ACT, false>(A, row_idx, W, bias, out, offsets, E, N, K, K, wes, 0, lds,
-                                        s_tiles, s_bias, tile, total, NT);
+      tile_loop<4, OUT_F32, ACT, false>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
+                                        lds, s_tiles, s_bias, tile, total, ntiles, NT);
     else
-      tile_loop<3, OUT_F32, ACT, false>(A, row_idx, W, bias, out, offsets, E, N, K, K, wes, 0, lds,
-                                        s_tiles, s_bias, tile, total, NT);
+      tile_loop<3, OUT_F32, ACT, false>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
+                                        lds, s_tiles, s_bias, tile, total, ntiles, NT);
   } else {
-    // ---- the same with heights 192, 128 and 64: the one with the least
-    // rounds(h) * (h + 64) (a tile's MFMA rows plus a fixed share for its
-    // weight panel, which short tiles stream with fewer MFMAs), the taller
-    // one on a tie
+    // ---- the same with heights 192, 128 and 64, whole or split in K: the
+    // least cost with h + 64 rows per tile of height h (its MFMA rows plus a
+    // fixed share for its weight panel, which short tiles stream with fewer
+    // MFMAs); the taller height, then the unsplit one, on a tie
     constexpr int kH[3] = {192, 128, 64};
     int c[3] = {0, 0, 0};
     for (int e = eb; e < min(E, eb + per); ++e) {
@@ -573,17 +653,18 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
       for (int q = 0; q < 3; ++q) s_part[q][tid] += a[q];
       __syncthreads();
     }
-    int sel = 0;
+    int sel = 0, S = 1;
     int64_t best = -1;
+    for (int sp = 1; sp <= smax; ++sp)
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const int64_t rounds = (static_cast<int64_t>(s_part[q][255]) * NT + Gd - 1) / Gd;
-      const int64_t cost = rounds * (kH[q] + 64);
-      if (best < 0 || cost < best) {
-        best = cost;
-        sel = q;
+      for (int q = 0; q < 3; ++q) {
+        const int64_t c = cost(static_cast<int64_t>(s_part[q][255]) * NT, kH[q] + 64, sp);
+        if (best < 0 || c < best) {
+          best = c;
+          sel = q;
+          S = sp;
+        }
       }
-    }
     const int BMs = sel == 0 ? 192 : (sel == 1 ? 128 : 64);
     {
       int run = s_part[sel][tid] - c[sel];
@@ -594,17 +675,20 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
       if (tid == 255) s_tiles[E] = s_part[sel][255];
     }
     __syncthreads();
-    const int total = s_tiles[E] * NT;
+    if (nsplit != nullptr && b == 0 && tid == 0) *nsplit = S;
+    const int ntiles = s_tiles[E] * NT;
+    const int total = ntiles * S;
+    const int nkl = K / BK / S;
     if (tile >= total) return;
     if (sel == 0)
-      tile_loop<3, OUT_F32, ACT, false>(A, row_idx, W, bias, out, offsets, E, N, K, K, wes, 0, lds,
-                                        s_tiles, s_bias, tile, total, NT);
+      tile_loop<3, OUT_F32, ACT, false>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
+                                        lds, s_tiles, s_bias, tile, total, ntiles, NT);
     else if (sel == 1)
-      tile_loop<2, OUT_F32, ACT, false>(A, row_idx, W, bias, out, offsets, E, N, K, K, wes, 0, lds,
-                                        s_tiles, s_bias, tile, total, NT);
+      tile_loop<2, OUT_F32, ACT, false>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
+                                        lds, s_tiles, s_bias, tile, total, ntiles, NT);
     else
-      tile_loop<1, OUT_F32, ACT, false>(A, row_idx, W, bias, out, offsets, E, N, K, K, wes, 0, lds,
-                                        s_tiles, s_bias, tile, total, NT);
+      tile_loop<1, OUT_F32, ACT, false>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
+                                        lds, s_tiles, s_bias, tile, total, ntiles, NT);
   }
 #endif
 }
@@ -653,8 +737,8 @@ void grouped_wgrad_bf16_kernel(const uint16_t* __restrict__ At, const uint16_t* 
   const int b = blockIdx.x;
   const int tile = (Gd % 8 == 0) ? (b % 8) * (Gd / 8) + b / 8 : b;
   if (tile >= total) return;
-  tile_loop<4, true, kActNone, true>(At, nullptr, Bt, nullptr, C, poff, E, N, 0, lda, 0, M, lds,
-                                     s_tiles, s_bias, tile, total, NT);
+  tile_loop<4, true, kActNone, true>(At, nullptr, Bt, nullptr, C, nullptr, poff, E, N, 0, lda, 0, M,
+                                     lds, s_tiles, s_bias, tile, total, total, NT);
 #endif
 }
 
@@ -676,25 +760,27 @@ int cu_count() {
 }  // namespace
 
 hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uint16_t* W,
-                            const float* bias, void* out,
+                            const float* bias, void* out, float* out2, int32_t* nsplit,
                             bool out_f32, int act, const int32_t* offsets, int E, int N, int K,
                             int64_t max_rows, int max_rows_per_expert, hipStream_t s) {
   if (max_rows <= 0) return hipSuccess;
+  if (!out_f32 || act != kActNone) out2 = nullptr;  // a split needs a linear fp32 output
+  const int smax = (out2 != nullptr && (K / BK) % 2 == 0) ? 2 : 1;
   // short tiles when no expert can fill a 256-row tile
   const bool shorter = max_rows_per_expert < 256;
   // upper bound on tiles: sum_e ceil(n_e/h) <= max_rows/h + E for the shortest h
   const int64_t mt_bound = max_rows / (shorter ? 64 : 192) + E;
   const int slots = cu_count();
-  const int64_t tiles = mt_bound * ((N + BN - 1) / BN);
+  const int64_t tiles = mt_bound * ((N + BN - 1) / BN) * smax;
   const unsigned grid = static_cast<unsigned>(tiles < slots ? tiles : slots);
 #define MOE_GEMM(OF, AC)                                                                          \
   do {                                                                                            \
     if (shorter)                                                                                  \
-      grouped_gemm_bf16_kernel<OF, AC, true><<<grid, 256, 0, s>>>(A, row_idx, W, bias, out,       \
-                                                                  offsets, E, N, K);              \
+      grouped_gemm_bf16_kernel<OF, AC, true><<<grid, 256, 0, s>>>(A, row_idx, W, bias, out, out2, \
+                                                                  nsplit, offsets, E, N, K);      \
     else                                                                                          \
-      grouped_gemm_bf16_kernel<OF, AC, false><<<grid, 256, 0, s>>>(A, row_idx, W, bias, out,      \
-                                                                   offsets, E, N, K);             \
+      grouped_gemm_bf16_kernel<OF, AC, false><<<grid, 256, 0, s>>>(A, row_idx, W, bias, out, out2, \
+                                                                   nsplit, offsets, E, N, K);      \
   } while (0)
   if (out_f32) MOE_GEMM(true, kActNone);
   else if (act == kActRelu) MOE_GEMM(false, kActRelu);

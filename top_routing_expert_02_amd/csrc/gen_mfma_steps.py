@@ -4,9 +4,11 @@ grouped GEMM (ffn_bf16.hip), one set per wave tile of (32*TM tokens) x
 (32*TN features).
 
 Each block is an unrolled list of v_mfma_f32_32x32x16_bf16 with the other
-instructions of the step placed one after each MFMA (see the kernel's notes
-on the matrix-core issue shadow). The blocks are generated rather than typed
-because every operand index depends on the tile shape.
+instructions of the step spread between the MFMAs (see the kernel's notes on
+the matrix-core issue shadow). A stage's LDS-DMA loads go out in two halves,
+with the last K16 step of one stage and the first of the next, so that the
+load queue is never handed a whole stage at once. The blocks are generated
+rather than typed because every operand index depends on the tile shape.
 
   python3 gen_mfma_steps.py        (rewrites mfma_steps.inc next to this file)
 """
@@ -36,7 +38,7 @@ def mfmas(TM, TN, w0, t0):
             for i in range(TN) for j in range(TM)]
 
 
-def step_body(TM, TN, dma):
+def step_body(TM, TN, dma, half=None):
     nacc = TM * TN
     nt0 = nacc
     nw0 = nt0 + TM
@@ -57,9 +59,13 @@ def step_body(TM, TN, dma):
                   for b in range(LA)] +
                  [(f"s_add_u32 m0, %{lb}, 0x{b*0x400:x}", f"global_load_lds_dwordx4 %{vo0+LA+b}, %{gw}")
                   for b in range(LB)])
+    if half is not None:
+        n1 = (len(loads) + 1) // 2
+        loads = loads[:n1] if half == 0 else loads[n1:]
+    # loads evenly over the step's MFMAs
     per = [0] * len(mf)
     for k in range(len(loads)):
-        per[k % len(mf)] += 1
+        per[(k * len(mf)) // len(loads)] += 1
     out, di, ri = [], 0, 0
     for m in range(len(mf)):
         pend = loads[di:di + per[m]]
@@ -76,6 +82,28 @@ def step_body(TM, TN, dma):
             ri += 1
     out += reads[ri:]
     return "\n".join(q(s) for s in out) + '\n      "s_waitcnt lgkmcnt(0)"'
+
+
+def dma_half(TM, TN, half):
+    LA, LB = 2 * TM, 2 * TN
+    n = f"{TM}x{TN}"
+    vo = ", ".join(f'"v"(vo[{b}])' for b in range(LA + LB))
+    sig_cur = f"const bf16x8_t (&w)[{TN}], const bf16x8_t (&t)[{TM}]"
+    sig_next = f"bf16x8_t (&nw)[{TN}], bf16x8_t (&nt)[{TM}]"
+    which = "first" if half == 0 else "second"
+    return f'''// a K16 step that also issues the {which} half of a stage's LDS-DMA loads
+__device__ __forceinline__ void step_dma{half}_{n}(f32x16_t (&acc)[{TN}][{TM}], {sig_cur},
+    {sig_next}, uint32_t ta, uint32_t wa, const uint32_t (&vo)[{LA+LB}], uint32_t la, uint32_t lb,
+    const char* ga, const char* gw) {{
+  asm volatile(
+{step_body(TM, TN, True, half)}
+      : {acc_list(TM, TN)},
+        {next_list(TM, TN)}
+      : {cur_list(TM, TN)}, "v"(ta), "v"(wa),
+        {vo},
+        "s"(la), "s"(lb), "s"(ga), "s"(gw)
+      : "memory", "m0", "scc");
+}}'''
 
 
 def emit(TM, TN):
@@ -109,19 +137,8 @@ __device__ __forceinline__ void step_{n}(f32x16_t (&acc)[{TN}][{TM}], {sig_cur},
       : "memory");
 }}
 
-__device__ __forceinline__ void step_dma_{n}(f32x16_t (&acc)[{TN}][{TM}], {sig_cur},
-    {sig_next}, uint32_t ta, uint32_t wa, const uint32_t (&vo)[{LA+LB}], uint32_t la, uint32_t lb,
-    const char* ga, const char* gw) {{
-  asm volatile(
-{step_body(TM, TN, True)}
-      : {acc_list(TM, TN)},
-        {next_list(TM, TN)}
-      : {cur_list(TM, TN)}, "v"(ta), "v"(wa),
-        {vo},
-        "s"(la), "s"(lb), "s"(ga), "s"(gw)
-      : "memory", "m0");
-}}
-
+{dma_half(TM, TN, 0)}
+{dma_half(TM, TN, 1)}
 // the last K16 step of a tile; its results are read by VALU next (24 wait states)
 __device__ __forceinline__ void last_{n}(f32x16_t (&acc)[{TN}][{TM}], {sig_cur}) {{
   asm volatile(
@@ -152,7 +169,7 @@ __device__ __forceinline__ void stage_{n}(const uint32_t (&ao)[{LA}], const uint
       :
       : {stg_ins},
         "s"(la), "s"(lb), "s"(ga), "s"(gw)
-      : "memory", "m0");
+      : "memory", "m0", "scc");
 }}
 '''
 

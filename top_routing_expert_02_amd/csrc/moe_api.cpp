@@ -66,7 +66,7 @@ int32_t check_cfg(const moe_config* c) {
 
 struct Layout {
   size_t logits, prob_part, hist, base, ids, gates, counts, offsets, prob_sum, slot, row_of,
-      row_token, x_perm, h, y_perm, rr_col, rr_served, rr_next, rr_fill, rr_fill0, rr_hist,
+      row_token, x_perm, h, y_perm, y_perm2, nsplit, rr_col, rr_served, rr_next, rr_fill, rr_fill0, rr_hist,
       rr_base, served_ids, cgates, total;
 };
 
@@ -95,6 +95,9 @@ Layout layout_of(const moe_config& c) {
   L.x_perm = take(layer_gathers(c) ? 0 : R * c.d * es);
   L.h = take(R * c.d_ff * es);
   L.y_perm = take(R * c.d * 4);
+  // the second K half's partial sums of a split second GEMM (bf16 layers)
+  L.y_perm2 = take(c.dtype == MOE_BF16 ? R * c.d * 4 : 0);
+  L.nsplit = take(4);
   // state of the general dispatch (priority order, re-routing rounds); small
   // next to h, so every layout has it and moe_dispatch_reroute works for any
   // config
@@ -259,29 +262,33 @@ int32_t gemm1_stage(const moe_config& c, const void* A, const int32_t* row_idx,
   const int per_expert = static_cast<int>(c.T < c.capacity ? c.T : c.capacity);
   if (c.dtype == MOE_BF16)
     MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(A), row_idx, static_cast<const uint16_t*>(W1), b1,
-                             h, false, c.act, offsets, c.E, c.d_ff, c.d, R, per_expert, s));
+                             h, nullptr, nullptr, false, c.act, offsets, c.E, c.d_ff, c.d, R, per_expert, s));
   else
     MOE_HIP(launch_gemm_f32(static_cast<const float*>(A), row_idx, static_cast<const float*>(W1), b1,
                             static_cast<float*>(h), c.act, offsets, c.E, c.d_ff, c.d, per_expert, s));
   return MOE_OK;
 }
 
+// y_perm2/nsplit (nullable): let a bf16 GEMM split K (see launch_gemm_bf16)
 int32_t gemm2_stage(const moe_config& c, const void* h, const int32_t* offsets, const void* W2,
-                    const float* b2, float* y_perm, hipStream_t s) {
+                    const float* b2, float* y_perm, float* y_perm2, int32_t* nsplit,
+                    hipStream_t s) {
   const int64_t R = max_rows_of(c);
   const int per_expert = static_cast<int>(c.T < c.capacity ? c.T : c.capacity);
   if (c.dtype == MOE_BF16)
     MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(h), nullptr, static_cast<const uint16_t*>(W2), b2,
-                             y_perm, true, kActNone, offsets, c.E, c.d, c.d_ff, R, per_expert, s));
+                             y_perm, y_perm2, nsplit, true, kActNone, offsets, c.E, c.d, c.d_ff, R, per_expert, s));
   else
     MOE_HIP(launch_gemm_f32(static_cast<const float*>(h), nullptr, static_cast<const float*>(W2), b2, y_perm,
                             kActNone, offsets, c.E, c.d, c.d_ff, per_expert, s));
   return MOE_OK;
 }
 
-int32_t combine_stage(const moe_config& c, const float* y_perm, const int32_t* row_of,
-                      const float* gates, void* y, hipStream_t s) {
-  MOE_HIP(launch_combine(y_perm, row_of, gates, c.T, c.k, c.d, c.dtype == MOE_BF16, y, s));
+int32_t combine_stage(const moe_config& c, const float* y_perm, const float* y_perm2,
+                      const int32_t* nsplit, const int32_t* row_of, const float* gates, void* y,
+                      hipStream_t s) {
+  MOE_HIP(launch_combine(y_perm, y_perm2, nsplit, row_of, gates, c.T, c.k, c.d, c.dtype == MOE_BF16,
+                         y, s));
   return MOE_OK;
 }
 
@@ -418,7 +425,7 @@ int32_t moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t*
     return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_ws(c, ws, ws_bytes));
   MOE_TRY(gemm1_stage(c, x_perm, nullptr, expert_offsets, W1, b1, h, stream));
-  return gemm2_stage(c, h, expert_offsets, W2, b2, y_perm, stream);
+  return gemm2_stage(c, h, expert_offsets, W2, b2, y_perm, nullptr, nullptr, stream);
 }
 
 int32_t moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* row_of,
@@ -430,7 +437,7 @@ int32_t moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* r
     return MOE_ERR_INVALID_ARG;
   if (!aligned(y_perm, 16) || !aligned(y, 16) || !aligned(row_of, 4) || !aligned(topk_gates, 4))
     return MOE_ERR_INVALID_ARG;
-  return combine_stage(c, y_perm, row_of, topk_gates, y, stream);
+  return combine_stage(c, y_perm, nullptr, nullptr, row_of, topk_gates, y, stream);
 }
 
 int32_t moe_layer_forward(const moe_config* cfg, const void* x, const void* W_r,
@@ -493,9 +500,11 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* x, const void* W_r,
   MOE_TRY(gemm1_stage(c, gather ? x : x_perm, gather ? row_token : nullptr, offsets, W1, b1, h,
                       stream));
   MOE_TRY(mark(3));
-  MOE_TRY(gemm2_stage(c, h, offsets, W2, b2, y_perm, stream));
+  float* y_perm2 = at<float>(ws, L.y_perm2);
+  int32_t* nsplit = at<int32_t>(ws, L.nsplit);
+  MOE_TRY(gemm2_stage(c, h, offsets, W2, b2, y_perm, y_perm2, nsplit, stream));
   MOE_TRY(mark(4));
-  MOE_TRY(combine_stage(c, y_perm, row_of, cgates, y, stream));
+  MOE_TRY(combine_stage(c, y_perm, y_perm2, nsplit, row_of, cgates, y, stream));
   return mark(5);
 }
 
@@ -591,9 +600,9 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* x, const void* W_r
   // u = x W1_e^T + b1_e (pre-activation, fp32); Z = dy W2_e (fp32)
   if (bf) {
     MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(xa), ridx, static_cast<const uint16_t*>(W1), b1,
-                             u, true, kActNone, offsets, c.E, c.d_ff, c.d, R, per_expert, s));
+                             u, nullptr, nullptr, true, kActNone, offsets, c.E, c.d_ff, c.d, R, per_expert, s));
     MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(dya), ridx, static_cast<const uint16_t*>(W2t),
-                             nullptr, Z, true, kActNone, offsets, c.E, c.d_ff, c.d, R, per_expert, s));
+                             nullptr, Z, nullptr, nullptr, true, kActNone, offsets, c.E, c.d_ff, c.d, R, per_expert, s));
   } else {
     MOE_HIP(launch_gemm_f32(static_cast<const float*>(xa), ridx, static_cast<const float*>(W1), b1, u,
                             kActNone, offsets, c.E, c.d_ff, c.d, per_expert, s));
@@ -609,7 +618,7 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* x, const void* W_r
   MOE_TRY(mark(MOE_BWD_STAGE_DGRAD));
   if (bf)
     MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(du), nullptr, static_cast<const uint16_t*>(W1t),
-                             nullptr, dxp, true, kActNone, offsets, c.E, c.d, c.d_ff, R, per_expert, s));
+                             nullptr, dxp, nullptr, nullptr, true, kActNone, offsets, c.E, c.d, c.d_ff, R, per_expert, s));
   else
     MOE_HIP(launch_gemm_f32(static_cast<const float*>(du), nullptr, static_cast<const float*>(W1t), nullptr,
                             dxp, kActNone, offsets, c.E, c.d, c.d_ff, per_expert, s));

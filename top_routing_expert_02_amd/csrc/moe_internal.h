@@ -162,8 +162,12 @@ hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int
 //   gemm1: h = act(A W1_e^T + b1_e)   A [rows,K=d], W1 [E,N=d_ff,K], h [rows,N]
 //   gemm2: y = A W2_e^T + b2_e        A [rows,K=d_ff], W2 [E,N=d,K], y fp32 [rows,N]
 // row_idx (nullable): row r of the grouped problem is row row_idx[r] of A.
+// out2 (nullable; used for a linear fp32 output only): a second [rows,N]
+// buffer that lets the kernel split K in two; it then writes the partial sum
+// of the second half there and 2 to *nsplit (1 when it did not split), so the
+// result is out + out2 when *nsplit == 2.
 hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uint16_t* W,
-                            const float* bias, void* out,
+                            const float* bias, void* out, float* out2, int32_t* nsplit,
                             bool out_f32, int act, const int32_t* offsets, int E, int N, int K,
                             int64_t max_rows, int max_rows_per_expert, hipStream_t s);
 hipError_t launch_gemm_f32(const float* A, const int32_t* row_idx, const float* W, const float* bias,
@@ -171,9 +175,12 @@ hipError_t launch_gemm_f32(const float* A, const int32_t* row_idx, const float* 
                            int act, const int32_t* offsets, int E, int N, int K,
                            int max_rows_per_expert, hipStream_t s);
 
-// y[t] = sum_j gates[t,j] y_perm[row_of[t,j]] (kept j only), rounded once
-hipError_t launch_combine(const float* y_perm, const int32_t* row_of, const float* gates,
-                          int64_t T, int k, int d, bool out_bf16, void* y, hipStream_t s);
+// y[t] = sum_j gates[t,j] y_perm[row_of[t,j]] (kept j only), rounded once;
+// with y_perm2 (nullable) and *nsplit == 2 the rows are y_perm + y_perm2
+// (a K-split second GEMM's two partial sums, added first)
+hipError_t launch_combine(const float* y_perm, const float* y_perm2, const int32_t* nsplit,
+                          const int32_t* row_of, const float* gates, int64_t T, int k, int d,
+                          bool out_bf16, void* y, hipStream_t s);
 
 // activation codes (same values as MOE_ACT_*)
 constexpr int kActRelu = 0;
