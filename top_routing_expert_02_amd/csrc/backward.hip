@@ -246,19 +246,164 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
   }
 }
 
-__global__ __launch_bounds__(256) void dx_gather_kernel(const float* __restrict__ dxp,
-                                                        const int32_t* __restrict__ row_of, int64_t T,
-                                                        int k, int d, float* __restrict__ dx) {
+// VEC consecutive values as floats (one 16- or 8-byte load for VEC = 4)
+template <int VEC>
+__device__ __forceinline__ void load_vec(const float* p, float (&o)[VEC]) {
+  if constexpr (VEC == 4) {
+    const float4 q = *reinterpret_cast<const float4*>(p);
+    o[0] = q.x;
+    o[1] = q.y;
+    o[2] = q.z;
+    o[3] = q.w;
+  } else {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) o[v] = p[v];
+  }
+}
+template <int VEC>
+__device__ __forceinline__ void load_vec(const uint16_t* p, float (&o)[VEC]) {
+  if constexpr (VEC == 4) {
+    const uint2 q = *reinterpret_cast<const uint2*>(p);
+    o[0] = __uint_as_float(q.x << 16);
+    o[1] = __uint_as_float(q.x & 0xffff0000u);
+    o[2] = __uint_as_float(q.y << 16);
+    o[3] = __uint_as_float(q.y & 0xffff0000u);
+  } else {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) o[v] = ld(p, v);
+  }
+}
+
+// dx[t] = sum over kept j of dxp[row_of[t,j]], plus (W_r given) the router
+// term sum_e ds[t,e] W_r[e], formed separately in expert order and added
+// last; VEC consecutive columns per thread.
+template <typename TW, int VEC>
+__global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict__ dxp,
+                                                        const int32_t* __restrict__ row_of,
+                                                        const float* __restrict__ ds,
+                                                        const TW* __restrict__ W_r, int64_t T, int k,
+                                                        int E, int d, float* __restrict__ dx) {
+  const int chunks = d / VEC;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= T * d) return;
-  const int64_t t = i / d;
-  const int c = static_cast<int>(i - t * d);
-  float acc = 0.f;
+  if (i >= T * chunks) return;
+  const int64_t t = i / chunks;
+  const int c = static_cast<int>(i - t * chunks) * VEC;
+  float acc[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
   for (int j = 0; j < k; ++j) {
     const int row = row_of[t * k + j];
-    if (row >= 0) acc += dxp[static_cast<int64_t>(row) * d + c];
+    if (row < 0) continue;
+    const float* src = dxp + static_cast<int64_t>(row) * d + c;
+    if constexpr (VEC == 4) {
+      const float4 q = *reinterpret_cast<const float4*>(src);
+      acc[0] += q.x;
+      acc[1] += q.y;
+      acc[2] += q.z;
+      acc[3] += q.w;
+    } else {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[v] += src[v];
+    }
   }
-  dx[i] = acc;
+  if (W_r != nullptr) {
+    float r[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) r[v] = 0.f;
+    for (int e = 0; e < E; ++e) {
+      const float g = ds[t * E + e];
+      float w[VEC];
+      load_vec<VEC>(W_r + static_cast<int64_t>(e) * d + c, w);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) r[v] = fmaf(g, w[v], r[v]);
+    }
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] += r[v];
+  }
+  float* dst = dx + t * d + c;
+  if constexpr (VEC == 4) {
+    *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  } else {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) dst[v] = acc[v];
+  }
+}
+
+// Router weight gradient for a few experts (E <= EMAX <= kRouterDirectMaxE):
+//   dW_r[e][n] = sum_t ds[t,e] x[t,n],  db_r[e] = sum_t ds[t,e].
+// Block (bx, sl) takes columns [256 VEC bx, 256 VEC (bx + 1)) (VEC per
+// thread, all E sums in registers) and the sl-th of S token slices, in chunks
+// of 64 tokens whose ds rows wait in LDS (zero-padded to EMAX); x is read 8
+// tokens at a time, the loads of a batch in flight together. S == 1 writes
+// dW and db; else part[sl] [E, d+1] (column d: the bias sums) for
+// wgrad_reduce_kernel, which adds the slices in order.
+template <typename TX, int EMAX, int VEC>
+__global__ __launch_bounds__(256) void router_wgrad_kernel(const float* __restrict__ ds,
+                                                           const TX* __restrict__ x, int64_t T, int E,
+                                                           int d, int S, float* __restrict__ part,
+                                                           float* __restrict__ dW,
+                                                           float* __restrict__ db) {
+  constexpr int kChunk = 64, kBatch = 8;
+  __shared__ __attribute__((aligned(16))) float s_ds[kChunk * EMAX];
+  const int c = (blockIdx.x * 256 + threadIdx.x) * VEC;
+  const int sl = blockIdx.y;
+  const int64_t t0 = T * sl / S, t1 = T * (sl + 1) / S;
+  const bool bias_thread = blockIdx.x == 0 && static_cast<int>(threadIdx.x) < E;
+  float acc[EMAX][VEC];
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e)
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[e][v] = 0.f;
+  float bacc = 0.f;
+  auto token = [&](const float (&xv)[VEC], const float* g) {
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[e][v] = fmaf(g[e], xv[v], acc[e][v]);
+  };
+  for (int64_t tb = t0; tb < t1; tb += kChunk) {
+    const int nt = static_cast<int>(min(static_cast<int64_t>(kChunk), t1 - tb));
+    __syncthreads();
+    for (int q = threadIdx.x; q < nt * EMAX; q += 256) {
+      const int tt = q / EMAX, e = q - tt * EMAX;
+      s_ds[q] = e < E ? ds[(tb + tt) * E + e] : 0.f;
+    }
+    __syncthreads();
+    if (c < d) {
+      const TX* xc = x + tb * d + c;
+      int b0 = 0;
+      for (; b0 + kBatch <= nt; b0 += kBatch) {
+        float xv[kBatch][VEC];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) load_vec<VEC>(xc + static_cast<int64_t>(b0 + u) * d, xv[u]);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) token(xv[u], s_ds + (b0 + u) * EMAX);
+      }
+      for (; b0 < nt; ++b0) {
+        float xv[VEC];
+        load_vec<VEC>(xc + static_cast<int64_t>(b0) * d, xv);
+        token(xv, s_ds + b0 * EMAX);
+      }
+    }
+    if (bias_thread)
+      for (int tt = 0; tt < nt; ++tt) bacc += s_ds[tt * EMAX + threadIdx.x];
+  }
+  float* out = dW;
+  int64_t ld_out = d;
+  if (S > 1) {
+    out = part + static_cast<int64_t>(sl) * E * (d + 1);
+    ld_out = d + 1;
+  }
+  if (c < d)
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+      if (e < E)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) out[e * ld_out + c + v] = acc[e][v];
+  if (bias_thread) {
+    if (S > 1) out[threadIdx.x * ld_out + d] = bacc;
+    else if (db != nullptr) db[threadIdx.x] = bacc;
+  }
 }
 
 // C[g][m][n] (+)= sum over rows r of group g of A[r][m] * B[src(r)][n]
@@ -357,12 +502,21 @@ __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restri
   const int64_t mn = i - g * per;
   const int m = static_cast<int>(mn / NB);
   const int n = static_cast<int>(mn - static_cast<int64_t>(m) * NB);
+  // the slices in order, their loads eight at a time
   float acc = 0.f;
-  for (int sp = 0; sp < splits; ++sp) acc += part[(g * splits + sp) * per + mn];
+  int sp = 0;
+  for (; sp + 8 <= splits; sp += 8) {
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = part[(g * splits + sp + q) * per + mn];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc += v[q];
+  }
+  for (; sp < splits; ++sp) acc += part[(g * splits + sp) * per + mn];
   if (n < N) {
     const int64_t o = (g * M + m) * static_cast<int64_t>(N) + n;
     C[o] = accumulate ? C[o] + acc : acc;
-  } else {
+  } else if (dbias != nullptr) {
     dbias[g * M + m] = acc;
   }
 }
@@ -539,9 +693,52 @@ hipError_t launch_router_bwd(const float* logits, const int32_t* ids, const int3
   return hipGetLastError();
 }
 
-hipError_t launch_dx_gather(const float* dxp, const int32_t* row_of, int64_t T, int k, int d,
-                            float* dx, hipStream_t s) {
-  dx_gather_kernel<<<blocks(T * d, 256), 256, 0, s>>>(dxp, row_of, T, k, d, dx);
+hipError_t launch_router_dx(const float* dxp, const int32_t* row_of, const float* ds, const void* W_r,
+                            bool w_bf16, int64_t T, int k, int E, int d, float* dx, hipStream_t s) {
+#define MOE_RDX(TW, V)                                                                          \
+  router_dx_kernel<TW, V><<<blocks(T * (d / V), 256), 256, 0, s>>>(dxp, row_of, ds,             \
+                                                                  static_cast<const TW*>(W_r), \
+                                                                  T, k, E, d, dx)
+  if (d % 4 == 0) {
+    if (w_bf16) MOE_RDX(uint16_t, 4);
+    else MOE_RDX(float, 4);
+  } else {
+    if (w_bf16) MOE_RDX(uint16_t, 1);
+    else MOE_RDX(float, 1);
+  }
+#undef MOE_RDX
+  return hipGetLastError();
+}
+
+hipError_t launch_router_wgrad(const float* ds, const void* x, bool x_bf16, int64_t T, int E, int d,
+                               int splits, float* part, float* dW, float* db, hipStream_t s) {
+  if (E > kRouterDirectMaxE || splits < 1 || (splits > 1 && part == nullptr)) return hipErrorInvalidValue;
+  const int vec = d % 4 == 0 ? 4 : 1;
+  dim3 grid(blocks(d, 256 * vec), splits);
+#define MOE_RWG(TX, EM, V)                                                                              \
+  router_wgrad_kernel<TX, EM, V><<<grid, 256, 0, s>>>(ds, static_cast<const TX*>(x), T, E, d, splits, \
+                                                      part, dW, db)
+#define MOE_RWG_V(TX, EM)           \
+  if (vec == 4) MOE_RWG(TX, EM, 4); \
+  else MOE_RWG(TX, EM, 1)
+#define MOE_RWG_E(TX)             \
+  if (E <= 8) {                   \
+    MOE_RWG_V(TX, 8);             \
+  } else {                        \
+    MOE_RWG_V(TX, 16);            \
+  }
+  if (x_bf16) {
+    MOE_RWG_E(uint16_t);
+  } else {
+    MOE_RWG_E(float);
+  }
+#undef MOE_RWG_E
+#undef MOE_RWG_V
+#undef MOE_RWG
+  if (splits > 1) {
+    const int64_t n = static_cast<int64_t>(E) * (d + 1);
+    wgrad_reduce_kernel<<<blocks(n, 256), 256, 0, s>>>(part, 1, splits, E, d, d + 1, dW, db, 0);
+  }
   return hipGetLastError();
 }
 

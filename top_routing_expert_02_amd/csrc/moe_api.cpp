@@ -119,7 +119,7 @@ Layout layout_of(const moe_config& c) {
 struct BwdLayout {
   size_t logits, W1t, W2t, x_perm, dy_perm, u, Z, h, du, dY, dxp, row_expert, row_gate, dg_row, ds,
       dsT, range_T, range_E, part, poff, At, Bt, total;
-  int router_splits;
+  int router_splits, router_dsplits;
   int64_t ldp;     // columns of the transposed weight-gradient operands (0: not used)
 };
 
@@ -135,6 +135,16 @@ int64_t wgrad_ld_of(const moe_config& c) {
 
 // row slices of dW_r = ds^T x (one group, K = T rows): enough blocks to fill
 // the chip, slices of at least 256 rows
+// token slices of the direct router weight gradient (few experts): 64 tokens
+// or more per slice, about 1024 blocks of 256 columns at most
+int router_direct_splits_of(const moe_config& c) {
+  const int64_t col_blocks = (c.d + 255) / 256;
+  int64_t sp = c.T / 64;
+  const int64_t cap = 1024 / col_blocks;
+  if (sp > cap) sp = cap;
+  return sp < 1 ? 1 : static_cast<int>(sp);
+}
+
 int router_splits_of(const moe_config& c) {
   const int64_t tiles = ((c.E + 63) / 64) * ((c.d + 1 + 63) / 64);
   int64_t sp = (1024 + tiles - 1) / tiles;
@@ -174,7 +184,11 @@ BwdLayout bwd_layout_of(const moe_config& c) {
   L.range_T = take(8);
   L.range_E = take(8);
   L.router_splits = router_splits_of(c);
-  L.part = take(L.router_splits > 1 ? static_cast<int64_t>(L.router_splits) * E * (d + 1) * 4 : 0);
+  L.router_dsplits = router_direct_splits_of(c);
+  {
+    const int64_t sp = E <= kRouterDirectMaxE ? L.router_dsplits : L.router_splits;
+    L.part = take(sp > 1 ? sp * E * (d + 1) * 4 : 0);
+  }
   L.ldp = wgrad_ld_of(c);
   const int64_t wide = d > f ? d : f;
   L.poff = take((E + 1) * 4);
@@ -652,13 +666,21 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* x, const void* W_r
   const double aux = static_cast<double>(aux_alpha) * c.E / (static_cast<double>(c.T) * c.T);
   MOE_HIP(launch_router_bwd(logits, f.topk_ids, f.row_of, dg_row, f.expert_counts, c.T, c.E, c.k,
                             c.renormalize, static_cast<float>(aux), ds, dsT, s));
-  MOE_HIP(launch_range(range_T, static_cast<int32_t>(c.T), s));
-  MOE_HIP(launch_range(range_E, c.E, s));
-  MOE_HIP(launch_wgrad(ds, false, x, bf, nullptr, range_T, 1, c.E, c.d, dW_r, db_r, false,
-                       L.router_splits, at<float>(ws, L.part), s));
-  MOE_HIP(launch_dx_gather(dxp, f.row_of, c.T, c.k, c.d, dx, s));
-  MOE_HIP(launch_wgrad(dsT, false, W_r, bf, nullptr, range_E, 1, static_cast<int>(c.T), c.d, dx, nullptr,
-                       true, 1, nullptr, s));
+  if (c.E <= kRouterDirectMaxE) {
+    // few experts: one pass over x for all E sums per column, and the router
+    // term of dx (E products per element) inside the dx gather
+    MOE_HIP(launch_router_wgrad(ds, x, bf, c.T, c.E, c.d, L.router_dsplits, at<float>(ws, L.part), dW_r,
+                                db_r, s));
+    MOE_HIP(launch_router_dx(dxp, f.row_of, ds, W_r, bf, c.T, c.k, c.E, c.d, dx, s));
+  } else {
+    MOE_HIP(launch_range(range_T, static_cast<int32_t>(c.T), s));
+    MOE_HIP(launch_range(range_E, c.E, s));
+    MOE_HIP(launch_wgrad(ds, false, x, bf, nullptr, range_T, 1, c.E, c.d, dW_r, db_r, false,
+                         L.router_splits, at<float>(ws, L.part), s));
+    MOE_HIP(launch_router_dx(dxp, f.row_of, nullptr, nullptr, bf, c.T, c.k, c.E, c.d, dx, s));
+    MOE_HIP(launch_wgrad(dsT, false, W_r, bf, nullptr, range_E, 1, static_cast<int>(c.T), c.d, dx,
+                         nullptr, true, 1, nullptr, s));
+  }
   return mark(MOE_BWD_NUM_STAGES);
 }
 

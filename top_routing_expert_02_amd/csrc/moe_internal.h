@@ -126,9 +126,16 @@ hipError_t launch_bwd_rows(const float* u, const float* Z, const int32_t* row_to
 hipError_t launch_router_bwd(const float* logits, const int32_t* ids, const int32_t* row_of,
                              const float* dg_row, const int32_t* counts, int64_t T, int E, int k,
                              int renormalize, float aux_coef, float* ds, float* dsT, hipStream_t s);
-// dx[t] = sum over kept j of dxp[row_of[t,j]]
-hipError_t launch_dx_gather(const float* dxp, const int32_t* row_of, int64_t T, int k, int d,
-                            float* dx, hipStream_t s);
+// router terms for a few experts (E <= kRouterDirectMaxE):
+// dx[t] = sum over kept j of dxp[row_of[t,j]] + sum_e ds[t,e] W_r[e] (W_r
+// nullable: the gather only)
+constexpr int kRouterDirectMaxE = 16;
+hipError_t launch_router_dx(const float* dxp, const int32_t* row_of, const float* ds, const void* W_r,
+                            bool w_bf16, int64_t T, int k, int E, int d, float* dx, hipStream_t s);
+// dW_r = ds^T x [E,d], db_r (nullable) = column sums of ds; splits > 1 token
+// slices through part (splits*E*(d+1) floats), added in slice order
+hipError_t launch_router_wgrad(const float* ds, const void* x, bool x_bf16, int64_t T, int E, int d,
+                               int splits, float* part, float* dW, float* db, hipStream_t s);
 // C[g] (+)= A_g^T B_g over the rows [offsets[g], offsets[g+1]); B rows through
 // b_rows; dbias (nullable) gets the column sums of A_g. splits > 1 splits
 // each group's rows; part then holds groups*splits*M*(N+1) floats.
