@@ -196,6 +196,8 @@ struct TileInfo {
 // doubles the stores, against the rounds it saves.
 constexpr int kEpiK = 512;
 
+constexpr int kGroupM = 4;  // M tiles per group of the tile order
+
 // s_tiles[e]: exclusive prefix over experts of their M tiles of height BM;
 // ntiles output tiles, each in K parts of nk stages (unit u covers tile
 // u mod ntiles, part u / ntiles; at most two parts).
@@ -215,8 +217,14 @@ __device__ __forceinline__ TileInfo decode_tile(int u, const int* s_tiles, const
   t.e = lo;
   const int mte = s_tiles[lo + 1] - s_tiles[lo];
   const int v = tile - s_tiles[lo] * NT;
-  const int nt = v / mte;  // M tiles of an expert are innermost
-  const int mt = v - nt * mte;
+  // grouped order inside an expert: groups of kGroupM M tiles, each swept
+  // over all N tiles with its M tiles innermost, so the 32 consecutive tiles
+  // one XCD runs at a time share 4 token panels and 8 weight panels
+  const int g = v / (kGroupM * NT);
+  const int r = v - g * kGroupM * NT;
+  const int gm = min(kGroupM, mte - g * kGroupM);
+  const int nt = r / gm;
+  const int mt = g * kGroupM + (r - nt * gm);
   t.row0 = offsets[lo] + mt * BM;
   t.rv = min(BM, offsets[lo + 1] - t.row0);
   t.n0 = nt * BN;
