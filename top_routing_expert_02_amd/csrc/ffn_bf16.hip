@@ -217,12 +217,15 @@ __device__ __forceinline__ TileInfo decode_tile(int u, const int* s_tiles, const
   t.e = lo;
   const int mte = s_tiles[lo + 1] - s_tiles[lo];
   const int v = tile - s_tiles[lo] * NT;
-  // grouped order inside an expert: groups of kGroupM M tiles, each swept
-  // over all N tiles with its M tiles innermost, so the 32 consecutive tiles
-  // one XCD runs at a time share 4 token panels and 8 weight panels
-  const int g = v / (kGroupM * NT);
-  const int r = v - g * kGroupM * NT;
-  const int gm = min(kGroupM, mte - g * kGroupM);
+  // grouped order inside an expert with many M tiles: groups of kGroupM M
+  // tiles, each swept over all N tiles with its M tiles innermost, so the 32
+  // consecutive tiles one XCD runs at a time share 4 token panels and 8
+  // weight panels; up to 8 M tiles form one group (every weight panel is
+  // then read once per expert)
+  const int GM = mte <= 2 * kGroupM ? mte : kGroupM;
+  const int g = v / (GM * NT);
+  const int r = v - g * GM * NT;
+  const int gm = min(GM, mte - g * GM);
   const int nt = r / gm;
   const int mt = g * kGroupM + (r - nt * gm);
   t.row0 = offsets[lo] + mt * BM;
