@@ -255,8 +255,13 @@ __device__ __forceinline__ TileInfo decode_tile_wg(int tile, const int* s_tiles,
   t.e = lo;
   const int mte = s_tiles[lo + 1] - s_tiles[lo];
   const int u = tile - s_tiles[lo] * NT;
-  const int nt = u / mte;
-  const int mt = u - nt * mte;
+  // the grouped order of decode_tile
+  const int GM = mte <= 2 * kGroupM ? mte : kGroupM;
+  const int g = u / (GM * NT);
+  const int r = u - g * GM * NT;
+  const int gm = min(GM, mte - g * GM);
+  const int nt = r / gm;
+  const int mt = g * GM + (r - nt * gm);
   t.arow = mt * BM;
   t.row0 = lo * M + t.arow;  // C viewed as [E*M, N]
   t.rv = min(BM, M - t.arow);
