@@ -150,8 +150,69 @@ __device__ __forceinline__ float act_grad(float u) {
   else return gelu_tanh_grad(u);
 }
 
-// one block per kept row
+// bf16 layers: h and dh/du of the tanh-GELU from one exp2 and one rcp.
+// With E = exp2(u (c1 u^2 + c0)) = exp(-2z) (the forward epilogue's form) and
+// s = 1 / (1 + E): h = u s (bit-identical to the forward), tanh z = 2 s - 1,
+// 1 - tanh^2 z = 4 s (1 - s), so dh/du = s + 2 a u s (1 - s) (1 + 3 b u^2).
+__device__ __forceinline__ void gelu_tanh_fwd_grad_fast(float u, float& h, float& dh) {
+  constexpr float a = 0.7978845608028654f, b3 = 3.0f * 0.044715f;
+  const float uu = u * u;
+  const float x = u * fmaf(kGeluExpC1, uu, kGeluExpC0);
+  const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
+  h = u * sg;
+  dh = fmaf(2.0f * a * u * sg * (1.0f - sg), fmaf(b3, uu, 1.0f), sg);
+}
+
+// the activation (rounded as the layer stores it) and its derivative
 template <typename TE, int ACT>
+__device__ __forceinline__ void act_fwd_grad(float u, float& h, float& dh) {
+  if constexpr (ACT == kActGeluTanh && sizeof(TE) == 2) {
+    gelu_tanh_fwd_grad_fast(u, h, dh);
+    h = round_to<TE>(h);
+  } else {
+    h = round_to<TE>(act_fwd<TE, ACT>(u));
+    dh = act_grad<ACT>(u);
+  }
+}
+
+// VEC consecutive elements i .. i + VEC - 1 of an fp32 or bf16 array
+template <int VEC, typename TE>
+__device__ __forceinline__ void st_vec(TE* p, int64_t i, const float (&v)[VEC]) {
+  if constexpr (VEC == 4 && sizeof(TE) == 2) {
+    uint2 o;
+    o.x = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+    o.y = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p) + i) = o;
+  } else if constexpr (VEC == 4) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p) + i) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) st(p, i + q, v[q]);
+  }
+}
+template <int VEC, typename TE>
+__device__ __forceinline__ void ld_vec(const TE* p, int64_t i, float (&v)[VEC]) {
+  if constexpr (VEC == 4 && sizeof(TE) == 2) {
+    const uint2 q = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p) + i);
+    v[0] = __uint_as_float(q.x << 16);
+    v[1] = __uint_as_float(q.x & 0xffff0000u);
+    v[2] = __uint_as_float(q.y << 16);
+    v[3] = __uint_as_float(q.y & 0xffff0000u);
+  } else if constexpr (VEC == 4) {
+    const float4 q = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i);
+    v[0] = q.x;
+    v[1] = q.y;
+    v[2] = q.z;
+    v[3] = q.w;
+  } else {
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) v[q] = ld(p, i + q);
+  }
+}
+
+// one block per kept row; VEC consecutive elements per thread (d and d_ff
+// multiples of VEC)
+template <typename TE, int ACT, int VEC>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(
     const float* __restrict__ u, const float* __restrict__ Z, const int32_t* __restrict__ row_token,
     const float* __restrict__ row_gate, const int32_t* __restrict__ row_expert,
@@ -165,19 +226,30 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
   const float g = row_gate[r];
   const int e = row_expert[r];
   float dot = 0.f;
-  for (int c = threadIdx.x; c < d_ff; c += 256) {
+  for (int c = threadIdx.x * VEC; c < d_ff; c += 256 * VEC) {
     const int64_t i = r * d_ff + c;
-    const float uv = u[i];
-    const float z = Z[i];
-    const float hv = round_to<TE>(act_fwd<TE, ACT>(uv));
-    st(h, i, hv);
-    dot = fmaf(z, hv, dot);
-    st(du, i, g * z * act_grad<ACT>(uv));
+    float uv[VEC], z[VEC], hv[VEC], dv[VEC];
+    ld_vec<VEC>(u, i, uv);
+    ld_vec<VEC>(Z, i, z);
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) {
+      float dh;
+      act_fwd_grad<TE, ACT>(uv[q], hv[q], dh);
+      dot = fmaf(z[q], hv[q], dot);
+      dv[q] = g * z[q] * dh;
+    }
+    st_vec<VEC>(h, i, hv);
+    st_vec<VEC>(du, i, dv);
   }
-  for (int c = threadIdx.x; c < d; c += 256) {
-    const float dv = ld(dy, t * d + c);
-    if (b2 != nullptr) dot = fmaf(dv, b2[static_cast<int64_t>(e) * d + c], dot);
-    st(dY, r * d + c, g * dv);
+  for (int c = threadIdx.x * VEC; c < d; c += 256 * VEC) {
+    float yv[VEC], o[VEC];
+    ld_vec<VEC>(dy, t * d + c, yv);
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) {
+      if (b2 != nullptr) dot = fmaf(yv[q], b2[static_cast<int64_t>(e) * d + c + q], dot);
+      o[q] = g * yv[q];
+    }
+    st_vec<VEC>(dY, r * d + c, o);
   }
   red[threadIdx.x] = dot;
   __syncthreads();
@@ -669,17 +741,22 @@ hipError_t launch_bwd_rows(const float* u, const float* Z, const int32_t* row_to
                            hipStream_t s) {
   if (max_rows <= 0) return hipSuccess;
   const unsigned grid = static_cast<unsigned>(max_rows);
-#define MOE_BWD_ROWS(TE, ACT)                                                                        \
-  bwd_rows_kernel<TE, ACT><<<grid, 256, 0, s>>>(u, Z, row_token, row_gate, row_expert, offsets, E, \
-                                                static_cast<const TE*>(dy), b2, d, d_ff,          \
-                                                static_cast<TE*>(h), static_cast<TE*>(du),        \
-                                                static_cast<TE*>(dY), dg_row)
+#define MOE_BWD_ROWS(TE, ACT, V)                                                                        \
+  bwd_rows_kernel<TE, ACT, V><<<grid, 256, 0, s>>>(u, Z, row_token, row_gate, row_expert, offsets, E, \
+                                                   static_cast<const TE*>(dy), b2, d, d_ff,          \
+                                                   static_cast<TE*>(h), static_cast<TE*>(du),        \
+                                                   static_cast<TE*>(dY), dg_row)
+  // bf16 layers have d and d_ff multiples of 64; fp32 layers take 4-wide
+  // vectors when both are multiples of 4
   if (bf16) {
-    if (act == kActRelu) MOE_BWD_ROWS(uint16_t, kActRelu);
-    else MOE_BWD_ROWS(uint16_t, kActGeluTanh);
+    if (act == kActRelu) MOE_BWD_ROWS(uint16_t, kActRelu, 4);
+    else MOE_BWD_ROWS(uint16_t, kActGeluTanh, 4);
+  } else if (d % 4 == 0 && d_ff % 4 == 0) {
+    if (act == kActRelu) MOE_BWD_ROWS(float, kActRelu, 4);
+    else MOE_BWD_ROWS(float, kActGeluTanh, 4);
   } else {
-    if (act == kActRelu) MOE_BWD_ROWS(float, kActRelu);
-    else MOE_BWD_ROWS(float, kActGeluTanh);
+    if (act == kActRelu) MOE_BWD_ROWS(float, kActRelu, 1);
+    else MOE_BWD_ROWS(float, kActGeluTanh, 1);
   }
 #undef MOE_BWD_ROWS
   return hipGetLastError();

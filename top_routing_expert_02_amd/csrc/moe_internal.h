@@ -41,11 +41,11 @@ __device__ __forceinline__ float act_gelu_tanh(float u) {
 // tanh-GELU of the bf16 expert GEMM epilogue: u * sigmoid(2z) with the
 // hardware base-2 exponential and reciprocal (about 1 ulp each; the result is
 // rounded to bf16 afterwards). The backward pass recomputes h with it.
+// exp(-2z) = 2^x with x = u * (c0 + c1 u^2)
+constexpr float kGeluExpC0 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+constexpr float kGeluExpC1 = kGeluExpC0 * 0.044715f;
 __device__ __forceinline__ float act_gelu_tanh_fast(float u) {
-  // exp(-2z) = 2^x with x = u * (c0 + c1 u^2)
-  constexpr float c0 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
-  constexpr float c1 = c0 * 0.044715f;
-  const float x = u * fmaf(c1, u * u, c0);
+  const float x = u * fmaf(kGeluExpC1, u * u, kGeluExpC0);
   return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
 }
 
