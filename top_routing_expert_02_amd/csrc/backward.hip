@@ -76,9 +76,13 @@ __global__ __launch_bounds__(256) void transpose_kernel(const TE* __restrict__ s
 // transposed matrix and the tile goes through LDS in 32-bit words (pitch 33:
 // conflict-free). row_ptr(i) gives source row i of the 64-row tile, or null
 // for a row of zeros; the tile lands at dst[c][dcol0 + i].
+// colsum (nullable): colsum[c0 + c] = the sum over the tile's 64 rows of
+// column c0 + c (fp32, rows in ascending order within each thread's four
+// pairs, then the four threads of a column in lane order)
 template <typename RowPtr>
 __device__ __forceinline__ void transpose_tile_bf16(RowPtr row_ptr, int c0, int Cc, uint16_t* dst,
-                                                    int64_t ldd, int64_t dcol0) {
+                                                    int64_t ldd, int64_t dcol0,
+                                                    float* colsum = nullptr) {
   __shared__ uint32_t t32[64][33];
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
 #pragma unroll
@@ -101,6 +105,20 @@ __device__ __forceinline__ void transpose_tile_bf16(RowPtr row_ptr, int c0, int 
     const int cl = ty + 8 * i;
     if (c0 + cl < Cc)
       *reinterpret_cast<uint32_t*>(dst + static_cast<int64_t>(c0 + cl) * ldd + dcol0 + 2 * tx) = t32[cl][tx];
+  }
+  if (colsum != nullptr) {
+    // column cl = thread / 4; its 32 row pairs in four runs of 8
+    const int cl = threadIdx.x >> 2, part = threadIdx.x & 3;
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t v = t32[cl][part * 8 + k];
+      sum += __uint_as_float(v << 16);
+      sum += __uint_as_float(v & 0xFFFF0000u);
+    }
+    sum += __shfl_xor(sum, 1, 64);
+    sum += __shfl_xor(sum, 2, 64);
+    if (part == 0 && c0 + cl < Cc) colsum[c0 + cl] = sum;
   }
 }
 
@@ -651,12 +669,15 @@ __global__ __launch_bounds__(256) void padded_transpose_kernel(const TE* __restr
 }
 
 // the same for bf16 through 4-byte pairs (see transpose_tile_bf16)
+// colsum_part (nullable): per 64-row tile of the padded rows, the column
+// sums of that tile ([padded rows / 64, Cc])
 __global__ __launch_bounds__(256) void padded_transpose_bf16_kernel(const uint16_t* __restrict__ src,
                                                                     const int32_t* __restrict__ row_idx,
                                                                     const int32_t* __restrict__ offsets,
                                                                     const int32_t* __restrict__ poff, int E,
                                                                     int Cc, int ldd,
-                                                                    uint16_t* __restrict__ dst) {
+                                                                    uint16_t* __restrict__ dst,
+                                                                    float* __restrict__ colsum_part) {
   const int p0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   if (p0 >= poff[E]) return;
   int lo = 0, hi = E - 1;  // the expert e with poff[e] <= p0 < poff[e+1]
@@ -674,24 +695,31 @@ __global__ __launch_bounds__(256) void padded_transpose_bf16_kernel(const uint16
     const int64_t r = rbase + local;
     const int64_t row = row_idx != nullptr ? row_idx[r] : r;
     return src + row * Cc;
-  }, c0, Cc, dst, ldd, p0);
+  }, c0, Cc, dst, ldd, p0,
+     colsum_part != nullptr ? colsum_part + static_cast<int64_t>(blockIdx.y) * Cc : nullptr);
 }
 
-// out[e][m] = sum of At[m][poff[e] .. poff[e+1]) (zero padding included);
-// one wave per (m, e), lanes in a fixed order
-template <typename TE>
-__global__ __launch_bounds__(256) void seg_rowsum_kernel(const TE* __restrict__ At,
-                                                         const int32_t* __restrict__ poff, int E, int M,
-                                                         int lda, float* __restrict__ out) {
-  const int64_t wv = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (wv >= static_cast<int64_t>(M) * E) return;
-  const int e = static_cast<int>(wv / M);
-  const int m = static_cast<int>(wv - static_cast<int64_t>(e) * M);
+// out[e][c] = sum over expert e's 64-row tiles pt (ascending) of
+// part[pt][c]: the column sums of the expert's rows (zero without rows)
+__global__ __launch_bounds__(256) void seg_colsum_kernel(const float* __restrict__ part,
+                                                         const int32_t* __restrict__ poff, int E, int Cc,
+                                                         float* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(E) * Cc) return;
+  const int e = static_cast<int>(i / Cc);
+  const int c = static_cast<int>(i - static_cast<int64_t>(e) * Cc);
+  const int t0 = poff[e] / 64, t1 = poff[e + 1] / 64;
   float acc = 0.f;
-  for (int p = poff[e] + lane; p < poff[e + 1]; p += 64) acc += ld(At, static_cast<int64_t>(m) * lda + p);
-  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (lane == 0) out[static_cast<int64_t>(e) * M + m] = acc;
+  int pt = t0;
+  for (; pt + 8 <= t1; pt += 8) {
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = part[static_cast<int64_t>(pt + q) * Cc + c];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc += v[q];
+  }
+  for (; pt < t1; ++pt) acc += part[static_cast<int64_t>(pt) * Cc + c];
+  out[i] = acc;
 }
 
 // C[e] = 0 for the experts without rows (block y = expert)
@@ -848,27 +876,26 @@ hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* poff, hipS
 
 hipError_t launch_padded_transpose(const void* src, const int32_t* row_idx, const int32_t* offsets,
                                    const int32_t* poff, int E, int Cc, int64_t max_padded, int ld,
-                                   bool bf16, void* dst, hipStream_t s) {
+                                   bool bf16, void* dst, float* colsum_part, hipStream_t s) {
   if (max_padded <= 0) return hipSuccess;
+  if (colsum_part != nullptr && !bf16) return hipErrorInvalidValue;
   dim3 grid(blocks(Cc, 64), blocks(max_padded, 64));
   if (bf16)
     padded_transpose_bf16_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(src), row_idx, offsets,
-                                                      poff, E, Cc, ld, static_cast<uint16_t*>(dst));
+                                                      poff, E, Cc, ld, static_cast<uint16_t*>(dst),
+                                                      colsum_part);
   else
     padded_transpose_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(src), row_idx, offsets,
                                                         poff, E, Cc, ld, static_cast<float*>(dst));
   return hipGetLastError();
 }
 
-hipError_t launch_seg_rowsum(const void* At, bool bf16, const int32_t* poff, int E, int M, int ld,
-                             float* out, hipStream_t s) {
-  const unsigned grid = blocks(static_cast<int64_t>(M) * E, 4);
-  if (bf16)
-    seg_rowsum_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(At), poff, E, M, ld, out);
-  else
-    seg_rowsum_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(At), poff, E, M, ld, out);
+hipError_t launch_seg_colsum(const float* part, const int32_t* poff, int E, int Cc, float* out,
+                             hipStream_t s) {
+  seg_colsum_kernel<<<blocks(static_cast<int64_t>(E) * Cc, 256), 256, 0, s>>>(part, poff, E, Cc, out);
   return hipGetLastError();
 }
+
 
 hipError_t launch_zero_empty(const int32_t* offsets, int E, int64_t MN, float* C, hipStream_t s) {
   int64_t bx = (MN + 256 * 16 - 1) / (256 * 16);

@@ -118,7 +118,7 @@ Layout layout_of(const moe_config& c) {
 // workspace of moe_layer_backward
 struct BwdLayout {
   size_t logits, W1t, W2t, x_perm, dy_perm, u, Z, h, du, dY, dxp, row_expert, row_gate, dg_row, ds,
-      dsT, range_T, range_E, part, poff, At, Bt, total;
+      dsT, range_T, range_E, part, poff, At, Bt, colsum, total;
   int router_splits, router_dsplits;
   int64_t ldp;     // columns of the transposed weight-gradient operands (0: not used)
 };
@@ -194,6 +194,8 @@ BwdLayout bwd_layout_of(const moe_config& c) {
   L.poff = take((E + 1) * 4);
   L.At = take(L.ldp * wide * es);
   L.Bt = take(L.ldp * wide * es);
+  // per 64-row tile column sums of the transposed du and dY (bias gradients)
+  L.colsum = take(L.ldp / 64 * wide * 4);
   L.total = off;
   return L;
 }
@@ -645,14 +647,19 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* x, const void* W_r
     auto* Bt = at<uint16_t>(ws, L.Bt);
     const int ld = static_cast<int>(L.ldp);
     MOE_HIP(launch_pad_offsets(offsets, c.E, poff, s));
-    MOE_HIP(launch_padded_transpose(du, nullptr, offsets, poff, c.E, c.d_ff, L.ldp, ld, true, At, s));
-    MOE_HIP(launch_padded_transpose(x, row_token, offsets, poff, c.E, c.d, L.ldp, ld, true, Bt, s));
+    float* colsum = at<float>(ws, L.colsum);
+    MOE_HIP(launch_padded_transpose(du, nullptr, offsets, poff, c.E, c.d_ff, L.ldp, ld, true, At,
+                                    db1 != nullptr ? colsum : nullptr, s));
+    if (db1 != nullptr) MOE_HIP(launch_seg_colsum(colsum, poff, c.E, c.d_ff, db1, s));
+    MOE_HIP(launch_padded_transpose(x, row_token, offsets, poff, c.E, c.d, L.ldp, ld, true, Bt, nullptr,
+                                    s));
     MOE_HIP(launch_wgrad_bf16(At, Bt, poff, c.E, c.d_ff, c.d, ld, dW1, s));
-    if (db1 != nullptr) MOE_HIP(launch_seg_rowsum(At, true, poff, c.E, c.d_ff, ld, db1, s));
-    MOE_HIP(launch_padded_transpose(dY, nullptr, offsets, poff, c.E, c.d, L.ldp, ld, true, At, s));
-    MOE_HIP(launch_padded_transpose(h, nullptr, offsets, poff, c.E, c.d_ff, L.ldp, ld, true, Bt, s));
+    MOE_HIP(launch_padded_transpose(dY, nullptr, offsets, poff, c.E, c.d, L.ldp, ld, true, At,
+                                    db2 != nullptr ? colsum : nullptr, s));
+    if (db2 != nullptr) MOE_HIP(launch_seg_colsum(colsum, poff, c.E, c.d, db2, s));
+    MOE_HIP(launch_padded_transpose(h, nullptr, offsets, poff, c.E, c.d_ff, L.ldp, ld, true, Bt, nullptr,
+                                    s));
     MOE_HIP(launch_wgrad_bf16(At, Bt, poff, c.E, c.d, c.d_ff, ld, dW2, s));
-    if (db2 != nullptr) MOE_HIP(launch_seg_rowsum(At, true, poff, c.E, c.d, ld, db2, s));
     MOE_HIP(launch_zero_empty(offsets, c.E, static_cast<int64_t>(c.d) * c.d_ff, dW1, s));
     MOE_HIP(launch_zero_empty(offsets, c.E, static_cast<int64_t>(c.d) * c.d_ff, dW2, s));
   } else {

@@ -145,13 +145,17 @@ hipError_t launch_wgrad(const void* A, bool a_bf16, const void* B, bool b_bf16, 
 // poff = exclusive prefix of the experts' row counts rounded up to 64
 hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t s);
 // dst [Cc, ld]: expert e's rows of src [*, Cc] (through row_idx when given)
-// as columns [poff[e], poff[e] + n_e), zeros up to poff[e+1]
+// as columns [poff[e], poff[e] + n_e), zeros up to poff[e+1]; colsum_part
+// (nullable, bf16 only): the column sums of each 64-row tile of the padded
+// rows, [max_padded / 64, Cc]
 hipError_t launch_padded_transpose(const void* src, const int32_t* row_idx, const int32_t* offsets,
                                    const int32_t* poff, int E, int Cc, int64_t max_padded, int ld,
-                                   bool bf16, void* dst, hipStream_t s);
-// out[e][m] = sum over columns [poff[e], poff[e+1]) of At[m][.]
-hipError_t launch_seg_rowsum(const void* At, bool bf16, const int32_t* poff, int E, int M, int ld,
-                             float* out, hipStream_t s);
+                                   bool bf16, void* dst, float* colsum_part,
+                                   hipStream_t s);
+// out[e][c] = the column sums of expert e's rows from padded_transpose's
+// per-tile sums (ascending tiles)
+hipError_t launch_seg_colsum(const float* part, const int32_t* poff, int E, int Cc, float* out,
+                             hipStream_t s);
 // C[e] (MN floats each) = 0 for the experts without rows
 hipError_t launch_zero_empty(const int32_t* offsets, int E, int64_t MN, float* C, hipStream_t s);
 // C[e] = At_e Bt_e^T over expert e's padded K range (bf16 MFMA, fp32 out);
