@@ -84,6 +84,11 @@ CASES = {
     "f32_mid_gelu": (WORKLOADS["tiny_f32"].scaled(name="f32_mid_gelu", T=301, d=48, d_ff=80, E=4,
                                                   k=2, act="gelu_tanh", renormalize=True, c=1.1),
                      0.3),
+    # d and d_ff not multiples of 4: the one-element-per-thread paths of the
+    # rows, router-dx and router-weight kernels
+    "f32_odd_dims": (WORKLOADS["tiny_f32"].scaled(name="f32_odd_dims", T=257, d=18, d_ff=30, E=3,
+                                                  k=2, act="gelu_tanh", renormalize=True, c=1.2),
+                     0.2),
     "small_bf16_mini": (WORKLOADS["small_bf16"].scaled(name="small_bf16_mini", T=700, d=256,
                                                        d_ff=512), 0.01),
     "skewed_bf16_mini": (WORKLOADS["skewed_bf16"].scaled(name="skewed_bf16_mini", T=900, d=256,
