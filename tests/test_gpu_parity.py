@@ -482,3 +482,38 @@ def test_graph_replay_matches_eager():
         # eager work on the same workspace between replays
         call(other, y_other, {k: torch.empty_like(v) for k, v in info.items()})
         torch.cuda.synchronize()
+
+
+# Router logits kernel shapes: every tile instantiation (E <= 16, <= 32,
+# <= 64 with few and with many tokens, > 64) and K step counts that leave
+# some of the four waves with no step (d = 64, 192) or with step counts that
+# are not a multiple of the operand ring's depth (d = 704, 1344).
+LOGIT_CASES = [
+    ("e8_d64", dict(T=37, d=64, E=8, k=2)),
+    ("e24_d192", dict(T=130, d=192, E=24, k=3)),
+    ("e64_d1344_few", dict(T=300, d=1344, E=64, k=4)),
+    ("e64_d1344_many", dict(T=8199, d=1344, E=64, k=4)),
+    ("e200_d704", dict(T=130, d=704, E=200, k=8)),
+]
+
+
+@pytest.mark.parametrize("name,shape", LOGIT_CASES, ids=[c[0] for c in LOGIT_CASES])
+def test_router_logits_shapes(name, shape):
+    w = WORKLOADS["skewed_bf16"].scaled(name=name, d_ff=64, **shape)
+    m = moe()
+    inp = synth.make_inputs(w, "cuda", seed=5)
+    C = cap(w)
+    cfg = P.make_cfg(w, C)
+    ws = m.alloc_workspace(cfg, "cuda")
+    h = P.host_inputs(inp, w.dtype)
+    say(f"[gpu] router logits {name} T={w.T} d={w.d} E={w.E}")
+    ids = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((w.T, w.k), dtype=torch.float32, device="cuda")
+    psum = torch.empty(w.E, dtype=torch.float32, device="cuda")
+    logits = torch.empty((w.T, w.E), dtype=torch.float32, device="cuda")
+    m.route(cfg, inp["x"], inp["W_r"], inp["b_r"], ids, gates, psum, logits, ws=ws)
+    torch.cuda.synchronize()
+    s = mo.router_logits(h["x"], h["W_r"], h["b_r"])
+    np.testing.assert_allclose(logits.cpu().numpy(), s, rtol=1e-5, atol=1e-5)
+    o = mo.route(h["x"], h["W_r"], h["b_r"], w.k, w.renormalize)
+    P.check_routing(o, ids.cpu().numpy())

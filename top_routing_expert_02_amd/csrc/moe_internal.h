@@ -16,6 +16,7 @@ constexpr int kGemmBM = 256;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

@@ -15,42 +15,59 @@ namespace moe {
 // v_mfma_f32_16x16x32_bf16: x rows are the A operand, W_r rows the B operand.
 // The four waves split the d axis (wave w takes the 64-wide K steps w, w+4,
 // ...); their partial sums meet in LDS and are added in a fixed order.
-// Operands come straight from global memory: the kernel streams x once and
-// re-reads W_r (E*d*2 bytes) from L2 per token tile. In a 64-wide step lane
-// group g holds k = 16g .. 16g+15 of its row (32 contiguous bytes, so the
-// 4 groups of a row cover a whole 128-byte line) and feeds them to two
-// MFMAs, k = 16g .. 16g+7 and 16g+8 .. 16g+15; x and W_r use the same
-// split, so every product is formed once.
-template <int MT, int NT>
+// The kernel streams x once and re-reads W_r (E*d*2 bytes) from L2 per token
+// tile.
+//
+// Operands pass through a per-wave LDS tile. The MFMA layout gives every
+// lane of a quad a different row, and 16-byte loads in that layout touch 16
+// cache lines per instruction, half of each: they ran at about a fifth of
+// the per-CU load rate. So a wave loads whole lines instead (one instruction
+// = 8 rows x 128 bytes, 8 lanes per row), writes them to its own tile of
+// 128-byte rows with 16-byte chunks XOR-swizzled by (row / 2) & 7, and
+// reads the fragments back conflict-free: in a 64-wide step, MFMA h takes
+// k = 32h + 8g .. 32h + 8g + 7 for lane group g. A wave only reads what it
+// wrote itself, and one wave's LDS operations run in order, so the tile
+// needs no barrier.
+//
+// A wave keeps P K steps of loads in flight: a ring of P register slots,
+// each refilled with the step P further on as soon as it is written to LDS.
+// Refills past the wave's last step (when its step count is not a multiple
+// of P) re-read that step and are never used. Each wave adds its steps in
+// order, so neither P nor the pipelining changes the result. Rows past T
+// and experts past E are clamped on load; their outputs are computed and
+// never stored.
+template <int MT, int NT, int P>
 __global__ __launch_bounds__(256) void logits_bf16_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ Wr,
                                                           const float* __restrict__ br,
                                                           float* __restrict__ logits, int64_t T,
                                                           int d, int E) {
   constexpr int NREG = MT * NT * 4;
-  __shared__ float red[3][NREG][64];
+  constexpr int ROWS = 16 * (MT + NT);  // staged rows per wave and step: x rows, then W_r rows
+  constexpr int NLD = ROWS / 8;         // load instructions per step
+  static_assert(4 * ROWS * 8 * 16 >= 3 * NREG * 64 * 4, "the partial sums reuse the tiles");
+  __shared__ u32x4_t tile[4][ROWS][8];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * (16 * MT);
   const int e0 = blockIdx.y * (16 * NT);
-  const int kq = (lane >> 4) * 16;  // this lane's 16 consecutive k inside a 64-wide step
 
-  const uint16_t* xr[MT];
-  const uint16_t* wr[NT];
-  bool wvalid[NT];
+  // whole-line loads: instruction j, lane l -> staged row 8j + l/8, chunk l%8
+  const uint16_t* src[NLD];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    int64_t t = t0 + mt * 16 + (lane & 15);
-    if (t >= T) t = T - 1;  // clamp: rows past T are computed and discarded
-    xr[mt] = x + t * d + kq;
+  for (int j = 0; j < NLD; ++j) {
+    const int r = 8 * j + (lane >> 3);
+    if (r < 16 * MT) {
+      int64_t t = t0 + r;
+      if (t >= T) t = T - 1;
+      src[j] = x + t * d + 8 * (lane & 7);
+    } else {
+      int e = e0 + r - 16 * MT;
+      if (e >= E) e = E - 1;
+      src[j] = Wr + static_cast<int64_t>(e) * d + 8 * (lane & 7);
+    }
   }
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    int e = e0 + nt * 16 + (lane & 15);
-    wvalid[nt] = e < E;
-    if (!wvalid[nt]) e = E - 1;
-    wr[nt] = Wr + static_cast<int64_t>(e) * d + kq;
-  }
+  u32x4_t(&my)[ROWS][8] = tile[wave];
 
   f32x4_t acc[MT][NT];
 #pragma unroll
@@ -58,30 +75,87 @@ __global__ __launch_bounds__(256) void logits_bf16_kernel(const uint16_t* __rest
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = wave * 64; k0 < d; k0 += 256) {
-    bf16x8_t a[2][MT], b[2][NT];
+  const int nsteps = d >> 6;  // d is a multiple of 64
+  const int nw = nsteps > wave ? (nsteps - wave + 3) >> 2 : 0;  // this wave's K steps
+  if (nw > 0) {
+    const int klast = wave * 64 + (nw - 1) * 256;
+    u32x4_t slot[P][NLD];
+    auto load = [&](u32x4_t (&v)[NLD], int i) {
+      const int k0 = min(wave * 64 + i * 256, klast);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int j = 0; j < NLD; ++j) v[j] = *reinterpret_cast<const u32x4_t*>(src[j] + k0);
+    };
+    auto put = [&](const u32x4_t (&v)[NLD]) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        a[h][mt] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xr[mt] + k0 + 8 * h));
+      for (int j = 0; j < NLD; ++j) {
+        const int r = 8 * j + (lane >> 3);
+        my[r][(lane & 7) ^ ((r >> 1) & 7)] = v[j];
+      }
+    };
+    // fragments of one half step (32 of the 64 k), double-buffered
+    bf16x8_t fa[2][MT], fb[2][NT];
+    auto read = [&](bf16x8_t (&a)[MT], bf16x8_t (&b)[NT], int h) {
+      const int c = 4 * h + (lane >> 4);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        uint4 v = *reinterpret_cast<const uint4*>(wr[nt] + k0 + 8 * h);
-        if (!wvalid[nt]) v = make_uint4(0, 0, 0, 0);
-        b[h][nt] = __builtin_bit_cast(bf16x8_t, v);
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = 16 * mt + (lane & 15);
+        a[mt] = __builtin_bit_cast(bf16x8_t, my[r][c ^ ((r >> 1) & 7)]);
       }
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int nt = 0; nt < NT; ++nt) {
+        const int r = 16 * (MT + nt) + (lane & 15);
+        b[nt] = __builtin_bit_cast(bf16x8_t, my[r][c ^ ((r >> 1) & 7)]);
+      }
+    };
+    auto mma = [&](const bf16x8_t (&a)[MT], const bf16x8_t (&b)[NT]) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[h][mt], b[h][nt], acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
+    };
+    // Step s sits in ring slot s % P. While the MFMAs of one half step run,
+    // the wave reads the next half step's fragments; step s + 1 goes into
+    // the tile right behind the last fragment reads of step s. The main
+    // loop has no branches (the compiler then counts the ring's loads in
+    // flight exactly); the last P steps, whose data is already loaded, run
+    // in the tail.
+#pragma unroll
+    for (int p = 0; p < P; ++p) load(slot[p], p);
+    __builtin_amdgcn_sched_barrier(0);
+    put(slot[0]);
+    load(slot[0], P);
+    __builtin_amdgcn_sched_barrier(0);
+    read(fa[0], fb[0], 0);
+    int s0 = 0;
+    for (; s0 + P < nw; s0 += P) {
+#pragma unroll
+      for (int q = 0; q < P; ++q) {
+        read(fa[1], fb[1], 1);  // step s0 + q, k 32..63
+        mma(fa[0], fb[0]);      // step s0 + q, k 0..31
+        put(slot[(q + 1) % P]);  // step s0 + q + 1 replaces step s0 + q in the tile
+        load(slot[(q + 1) % P], s0 + q + 1 + P);
+        __builtin_amdgcn_sched_barrier(0);
+        read(fa[0], fb[0], 0);  // step s0 + q + 1, k 0..31
+        mma(fa[1], fb[1]);      // step s0 + q, k 32..63
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      if (s0 + q < nw) {
+        read(fa[1], fb[1], 1);
+        mma(fa[0], fb[0]);
+        if (s0 + q + 1 < nw) {
+          put(slot[(q + 1) % P]);
+          read(fa[0], fb[0], 0);
+        }
+        mma(fa[1], fb[1]);
+      }
+    }
   }
 
+  __syncthreads();  // every wave is done with its tile: the partial sums reuse them
+  float(&red)[3][NREG][64] = *reinterpret_cast<float(*)[3][NREG][64]>(&tile[0][0][0]);
   if (wave > 0) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -308,18 +382,24 @@ __global__ __launch_bounds__(256) void prob_reduce_kernel(const float* __restric
 
 hipError_t launch_logits_bf16(const uint16_t* x, const uint16_t* Wr, const float* br,
                               float* logits, int64_t T, int d, int E, hipStream_t s) {
+  // tiles: 16 tokens x all of E up to 64 experts (32 tokens once that still
+  // gives 256 blocks), 64 x 64 beyond; the ring depth P keeps 32-48 KiB of
+  // loads in flight per wave
   if (E <= 16) {
     dim3 grid(static_cast<unsigned>((T + 15) / 16), 1);
-    logits_bf16_kernel<1, 1><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E);
+    logits_bf16_kernel<1, 1, 4><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E);
   } else if (E <= 32) {
     dim3 grid(static_cast<unsigned>((T + 15) / 16), 1);
-    logits_bf16_kernel<1, 2><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E);
+    logits_bf16_kernel<1, 2, 4><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E);
+  } else if (E <= 64 && T >= 32 * 256) {
+    dim3 grid(static_cast<unsigned>((T + 31) / 32), 1);
+    logits_bf16_kernel<2, 4, 3><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E);
   } else if (E <= 64) {
     dim3 grid(static_cast<unsigned>((T + 15) / 16), 1);
-    logits_bf16_kernel<1, 4><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E);
+    logits_bf16_kernel<1, 4, 4><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E);
   } else {
     dim3 grid(static_cast<unsigned>((T + 63) / 64), static_cast<unsigned>((E + 63) / 64));
-    logits_bf16_kernel<4, 4><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E);
+    logits_bf16_kernel<4, 4, 3><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E);
   }
   return hipGetLastError();
 }
