@@ -60,6 +60,7 @@ namespace {
 constexpr int BN = 256;       // features per tile
 constexpr int BK = 64;        // K per LDS stage
 constexpr int ROWB = BK * 2;  // bytes per LDS row (128)
+constexpr int kWtRowB = BN * 2;  // bytes per row of a K-major weight stage (512)
 // stage buffers: two for the 256- and 192-row tiles, three for the shorter
 // ones (a tile of few rows streams weights, so more bytes in flight pay)
 template <int TM>
@@ -101,6 +102,7 @@ __device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
 // is issued from asm, so the compiler tracks none of them: it would otherwise
 // wait for all of them before reusing an address register or reading any
 // LDS, which would stall each epilogue on the next tile's prefetch.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 #include "mfma_steps.inc"
 
 template <int TM>
@@ -149,6 +151,59 @@ __device__ __forceinline__ void read_frags(bf16x8_t (&nw)[TN], bf16x8_t (&nt)[TM
   else if constexpr (TM == 3) frags_3x4(nw, nt, ta, wa);
   else if constexpr (TM == 2) frags_2x4(nw, nt, ta, wa);
   else frags_1x4(nw, nt, ta, wa);
+}
+
+// The same steps for a K-major weight stage (WT): the next weight fragments
+// arrive as 64-bit halves (k 0..3 and 4..7 of each lane's 8), joined here.
+__device__ __forceinline__ void join_halves(bf16x8_t (&nw)[TN], const v4i16 (&lo)[TN],
+                                            const v4i16 (&hi)[TN]) {
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+    nw[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo[i], hi[i], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int TM>
+__device__ __forceinline__ void step_t(f32x16_t (&acc)[TN][TM], const bf16x8_t (&w)[TN],
+                                       const bf16x8_t (&t)[TM], bf16x8_t (&nw)[TN], bf16x8_t (&nt)[TM],
+                                       uint32_t ta, const uint32_t (&wa)[TN]) {
+  v4i16 lo[TN], hi[TN];
+  if constexpr (TM == 4) step_t_4x4(acc, w, t, nt, lo, hi, ta, wa);
+  else if constexpr (TM == 3) step_t_3x4(acc, w, t, nt, lo, hi, ta, wa);
+  else if constexpr (TM == 2) step_t_2x4(acc, w, t, nt, lo, hi, ta, wa);
+  else step_t_1x4(acc, w, t, nt, lo, hi, ta, wa);
+  join_halves(nw, lo, hi);
+}
+
+template <int TM, int HALF>
+__device__ __forceinline__ void step_dma_t(f32x16_t (&acc)[TN][TM], const bf16x8_t (&w)[TN],
+                                           const bf16x8_t (&t)[TM], bf16x8_t (&nw)[TN],
+                                           bf16x8_t (&nt)[TM], uint32_t ta, const uint32_t (&wa)[TN],
+                                           const uint32_t (&vo)[2 * TM + 2 * TN], uint32_t la,
+                                           uint32_t lb, const char* ga, const char* gw) {
+  v4i16 lo[TN], hi[TN];
+  if constexpr (HALF == 0) {
+    if constexpr (TM == 4) step_dma0_t_4x4(acc, w, t, nt, lo, hi, ta, wa, vo, la, lb, ga, gw);
+    else if constexpr (TM == 3) step_dma0_t_3x4(acc, w, t, nt, lo, hi, ta, wa, vo, la, lb, ga, gw);
+    else if constexpr (TM == 2) step_dma0_t_2x4(acc, w, t, nt, lo, hi, ta, wa, vo, la, lb, ga, gw);
+    else step_dma0_t_1x4(acc, w, t, nt, lo, hi, ta, wa, vo, la, lb, ga, gw);
+  } else {
+    if constexpr (TM == 4) step_dma1_t_4x4(acc, w, t, nt, lo, hi, ta, wa, vo, la, lb, ga, gw);
+    else if constexpr (TM == 3) step_dma1_t_3x4(acc, w, t, nt, lo, hi, ta, wa, vo, la, lb, ga, gw);
+    else if constexpr (TM == 2) step_dma1_t_2x4(acc, w, t, nt, lo, hi, ta, wa, vo, la, lb, ga, gw);
+    else step_dma1_t_1x4(acc, w, t, nt, lo, hi, ta, wa, vo, la, lb, ga, gw);
+  }
+  join_halves(nw, lo, hi);
+}
+
+template <int TM>
+__device__ __forceinline__ void read_frags_t(bf16x8_t (&nw)[TN], bf16x8_t (&nt)[TM], uint32_t ta,
+                                             const uint32_t (&wa)[TN]) {
+  v4i16 lo[TN], hi[TN];
+  if constexpr (TM == 4) frags_t_4x4(nt, lo, hi, ta, wa);
+  else if constexpr (TM == 3) frags_t_3x4(nt, lo, hi, ta, wa);
+  else if constexpr (TM == 2) frags_t_2x4(nt, lo, hi, ta, wa);
+  else frags_t_1x4(nt, lo, hi, ta, wa);
+  join_halves(nw, lo, hi);
 }
 
 template <int TM>
@@ -289,13 +344,16 @@ __device__ __forceinline__ void wait_loads(int n) {
 // lda: elements between consecutive rows of A and of W (K for the expert
 // FFN); w_estride: elements between experts' weight matrices (0 when W is
 // one matrix).
-template <int LA, int LB>
+template <int LA, int LB, bool WT>
 __device__ __forceinline__ void tile_sources(const TileInfo& t, const uint16_t* A,
                                              const int32_t* __restrict__ row_idx, const uint16_t* W,
                                              int N, int lda, int64_t w_estride, int wave, int drow,
                                              int dpos, const char*& Abase, const char*& Wbase,
                                              uint32_t (&aoffs)[LA], uint32_t (&boffs)[LB]) {
-  Wbase = reinterpret_cast<const char*>(W + t.e * w_estride + static_cast<int64_t>(t.n0) * lda + t.k0);
+  if constexpr (WT)  // W_e stored [K, N]: the tile's columns from its first K row
+    Wbase = reinterpret_cast<const char*>(W + t.e * w_estride + static_cast<int64_t>(t.k0) * N + t.n0);
+  else
+    Wbase = reinterpret_cast<const char*>(W + t.e * w_estride + static_cast<int64_t>(t.n0) * lda + t.k0);
   if (row_idx != nullptr) {
     Abase = reinterpret_cast<const char*>(A + t.k0);
 #pragma unroll
@@ -312,10 +370,25 @@ __device__ __forceinline__ void tile_sources(const TileInfo& t, const uint16_t* 
       aoffs[i] = static_cast<uint32_t>((min(r, t.rv - 1) * lda + (dpos ^ swz_key(r)) * 8) * 2);
     }
   }
+  if constexpr (WT) {
+    // K-major stage: block i of this wave is K rows kr, kr + 1 (512 bytes
+    // each); lane L lands at byte 16 (L % 32) of row kr + L / 32, in 64-byte
+    // segment p = (L % 32) / 4, which holds the row's segment p ^ (kr & 3).
+    // Columns past N read column N - 8 onward (never stored).
+    const int lane = drow * 8 + dpos;
 #pragma unroll
-  for (int i = 0; i < LB; ++i) {
-    const int r = (wave * LB + i) * 8 + drow;
-    boffs[i] = static_cast<uint32_t>(((min(t.n0 + r, N - 1) - t.n0) * lda + (dpos ^ swz_key(r)) * 8) * 2);
+    for (int i = 0; i < LB; ++i) {
+      const int kr = (wave * LB + i) * 2 + (lane >> 5);
+      const int p = (lane & 31) >> 2;
+      const int col = min(t.n0 + 32 * (p ^ (kr & 3)) + 8 * (lane & 3), N - 8) - t.n0;
+      boffs[i] = static_cast<uint32_t>((static_cast<int64_t>(kr) * N + col) * 2);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int r = (wave * LB + i) * 8 + drow;
+      boffs[i] = static_cast<uint32_t>(((min(t.n0 + r, N - 1) - t.n0) * lda + (dpos ^ swz_key(r)) * 8) * 2);
+    }
   }
 }
 
@@ -366,7 +439,7 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], void* __
 // offsets, M the rows of C per expert); else expert-FFN tiles of nkl stages
 // each: ntiles output tiles, and total = ntiles (whole K) or 2 ntiles (two K
 // halves; the second half's partial sums go to out2, without bias).
-template <int TM, bool OUT_F32, int ACT, bool WG>
+template <int TM, bool OUT_F32, int ACT, bool WG, bool WT = false>
 __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const int32_t* __restrict__ row_idx,
                                           const uint16_t* __restrict__ W, const float* __restrict__ bias,
                                           void* __restrict__ out, void* __restrict__ out2,
@@ -405,6 +478,26 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
   const uint32_t trow = wm * WM * ROWB;            // this wave's token rows in a stage
   const uint32_t wrow = A_BYTES + wn * WN * ROWB;  // this wave's weight rows in a stage
+  // WT: the weight stage is K-major, BK rows of BN features (kWtRowB bytes,
+  // 64-byte segments at position seg ^ (row & 3)). Weight fragment tile i
+  // of lane (l5, hi) in K16 step s: feature 32 i + l5 of this wave's 128,
+  // k = 16 s + 8 hi .. + 7, as two transposing reads of 4 rows: a 16-lane
+  // group g reads rows 8 (g / 2) + (lane % 16) / 4 at features
+  // 16 (g % 2) + 4 (lane % 4) of the tile, and lane o of the group gets
+  // feature 16 (g % 2) + o for those 4 rows.
+  uint32_t wo[TN];
+  if constexpr (WT) {
+    const int key4 = (lane >> 2) & 3;
+    const uint32_t rb = (8 * hi + ((lane & 15) >> 2)) * kWtRowB + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+#pragma unroll
+    for (int i = 0; i < TN; ++i) wo[i] = A_BYTES + rb + 64 * ((4 * wn + i) ^ key4);
+  }
+  // bytes from one K stage of W to the next
+  const int64_t wst = WT ? static_cast<int64_t>(BK) * N * 2 : ROWB;
+  auto wadr = [&](uint32_t sbase, int s, uint32_t (&wa)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i) wa[i] = sbase + wo[i] + s * 16 * kWtRowB;
+  };
 
   uint32_t aoffs[LA], boffs[LB], vo[G];
   const char* Abase;
@@ -414,15 +507,15 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     for (int p = 0; p < NST && p < (WG ? c.nk : nkl); ++p)
       issue_stage<TM>(aoffs, boffs, lds_base + p * STAGE + wave * LA * 1024,
                       lds_base + p * STAGE + A_BYTES + wave * LB * 1024, Abase + p * ROWB,
-                      Wbase + p * ROWB);
+                      Wbase + p * wst);
     if (bias != nullptr && c.part == 0 && wave == 0)
       issue_bias(bias + static_cast<int64_t>(c.e) * N + min(c.n0 + 4 * lane, N - 4),
                  static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&s_bias[par][0])));
   };
   int par = 0;  // bias slice of the current tile
   TileInfo cur = decode(tile);
-  tile_sources<LA, LB>(cur, A, row_idx, W, N, lda, w_estride, wave, drow, dpos, Abase, Wbase, aoffs,
-                       boffs);
+  tile_sources<LA, LB, WT>(cur, A, row_idx, W, N, lda, w_estride, wave, drow, dpos, Abase, Wbase, aoffs,
+                           boffs);
   prologue(cur, par);
 
   for (;;) {
@@ -457,7 +550,13 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
         }
     }
     bf16x8_t wf0[TN], tf0[TM], wf1[TN], tf1[TM];
-    read_frags<TM>(wf0, tf0, lds_base + trow + fo[0], lds_base + wrow + fo[0]);
+    if constexpr (WT) {
+      uint32_t wa[TN];
+      wadr(lds_base, 0, wa);
+      read_frags_t<TM>(wf0, tf0, lds_base + trow + fo[0], wa);
+    } else {
+      read_frags<TM>(wf0, tf0, lds_base + trow + fo[0], lds_base + wrow + fo[0]);
+    }
 
     TileInfo done = cur;
     const int next = tile + Gd;
@@ -473,18 +572,41 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     uint32_t pla = 0, plb = 0;
     const char* pga = nullptr;
     const char* pgw = nullptr;
+    // one K16 step reading the fragments of step s of the stage at sbase
+    auto kstep = [&](const bf16x8_t (&w)[TN], const bf16x8_t (&tk)[TM], bf16x8_t (&nw)[TN],
+                     bf16x8_t (&nt)[TM], uint32_t sbase, int s) {
+      if constexpr (WT) {
+        uint32_t wa[TN];
+        wadr(sbase, s, wa);
+        step_t<TM>(acc, w, tk, nw, nt, sbase + trow + fo[s], wa);
+      } else {
+        step<TM>(acc, w, tk, nw, nt, sbase + trow + fo[s], sbase + wrow + fo[s]);
+      }
+    };
+    // the same with half of a stage's LDS-DMA loads
+    auto kstep_dma = [&](auto half, const bf16x8_t (&w)[TN], const bf16x8_t (&tk)[TM], bf16x8_t (&nw)[TN],
+                         bf16x8_t (&nt)[TM], uint32_t sbase, int s) {
+      constexpr int H = decltype(half)::value;
+      if constexpr (WT) {
+        uint32_t wa[TN];
+        wadr(sbase, s, wa);
+        step_dma_t<TM, H>(acc, w, tk, nw, nt, sbase + trow + fo[s], wa, vo, pla, plb, pga, pgw);
+      } else {
+        step_dma<TM, H>(acc, w, tk, nw, nt, sbase + trow + fo[s], sbase + wrow + fo[s], vo, pla, plb, pga,
+                        pgw);
+      }
+    };
     // One K stage. D1: step 0 issues the second half of the previous stage's
     // refill; RF: stage t+NST is still to load (this stage's buffer takes it
     // once every wave has read the stage).
     auto stage = [&](auto d1, auto rf) {
       // K16 steps 0..2, each reading the next step's fragments
       if constexpr (decltype(d1)::value)
-        step_dma<TM, 1>(acc, wf0, tf0, wf1, tf1, sb + trow + fo[1], sb + wrow + fo[1], vo, pla, plb, pga,
-                        pgw);
+        kstep_dma(std::integral_constant<int, 1>{}, wf0, tf0, wf1, tf1, sb, 1);
       else
-        step<TM>(acc, wf0, tf0, wf1, tf1, sb + trow + fo[1], sb + wrow + fo[1]);
-      step<TM>(acc, wf1, tf1, wf0, tf0, sb + trow + fo[2], sb + wrow + fo[2]);
-      step<TM>(acc, wf0, tf0, wf1, tf1, sb + trow + fo[3], sb + wrow + fo[3]);
+        kstep(wf0, tf0, wf1, tf1, sb, 1);
+      kstep(wf1, tf1, wf0, tf0, sb, 2);
+      kstep(wf0, tf0, wf1, tf1, sb, 3);
       // stage t+1 has landed and every wave has read its last fragments of
       // stage t
       if constexpr (decltype(rf)::value) wait_loads<G>(NST - 2);
@@ -499,11 +621,10 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
         pla = sb + wave * LA * 1024;
         plb = sb + A_BYTES + wave * LB * 1024;
         pga = Abase + (t + NST) * ROWB;
-        pgw = Wbase + (t + NST) * ROWB;
-        step_dma<TM, 0>(acc, wf1, tf1, wf0, tf0, sn + trow + fo[0], sn + wrow + fo[0], vo, pla, plb, pga,
-                        pgw);
+        pgw = Wbase + (t + NST) * wst;
+        kstep_dma(std::integral_constant<int, 0>{}, wf1, tf1, wf0, tf0, sn, 0);
       } else {
-        step<TM>(acc, wf1, tf1, wf0, tf0, sn + trow + fo[0], sn + wrow + fo[0]);
+        kstep(wf1, tf1, wf0, tf0, sn, 0);
       }
       sc = sn_i;
       sb = sn;
@@ -521,16 +642,16 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     // the last stages: nothing more to load
     for (; t + 1 < nk; ++t) stage(no{}, no{});
     // the last stage
-    step<TM>(acc, wf0, tf0, wf1, tf1, sb + trow + fo[1], sb + wrow + fo[1]);
-    step<TM>(acc, wf1, tf1, wf0, tf0, sb + trow + fo[2], sb + wrow + fo[2]);
-    step<TM>(acc, wf0, tf0, wf1, tf1, sb + trow + fo[3], sb + wrow + fo[3]);
+    kstep(wf0, tf0, wf1, tf1, sb, 1);
+    kstep(wf1, tf1, wf0, tf0, sb, 2);
+    kstep(wf0, tf0, wf1, tf1, sb, 3);
     // every wave has read all of its fragments: all buffers are free, and the
     // next tile's first stages load during this tile's last MFMAs and epilogue
     __syncthreads();
     if (next < total) {
       cur = decode(next);
-      tile_sources<LA, LB>(cur, A, row_idx, W, N, lda, w_estride, wave, drow, dpos, Abase, Wbase, aoffs,
-                           boffs);
+      tile_sources<LA, LB, WT>(cur, A, row_idx, W, N, lda, w_estride, wave, drow, dpos, Abase, Wbase,
+                               aoffs, boffs);
       prologue(cur, par ^ 1);
     }
     last_step<TM>(acc, wf1, tf1);
@@ -558,7 +679,10 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
 // output tiles, long K); the first half (with bias) goes to out, the second
 // to out2, and the number of parts (1 or 2) to *nsplit (when not null), so
 // out = out + out2 holds the product only when *nsplit is 2.
-template <bool OUT_F32, int ACT, bool SHORT>
+// WT: each W_e is stored [K, N] (K-major, as W^T of the usual [N, K]); the
+// weight stages are loaded row by row of K and read with transposing LDS
+// reads.
+template <bool OUT_F32, int ACT, bool SHORT, bool WT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ row_idx,
                               const uint16_t* __restrict__ W,
@@ -640,10 +764,10 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
     const int nkl = K / BK / S;
     if (tile >= total) return;
     if (tall)
-      tile_loop<4, OUT_F32, ACT, false>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
+      tile_loop<4, OUT_F32, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
                                         lds, s_tiles, s_bias, tile, total, ntiles, NT);
     else
-      tile_loop<3, OUT_F32, ACT, false>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
+      tile_loop<3, OUT_F32, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
                                         lds, s_tiles, s_bias, tile, total, ntiles, NT);
   } else {
     // ---- the same with heights 192, 128 and 64, whole or split in K: the
@@ -697,13 +821,13 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
     const int nkl = K / BK / S;
     if (tile >= total) return;
     if (sel == 0)
-      tile_loop<3, OUT_F32, ACT, false>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
+      tile_loop<3, OUT_F32, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
                                         lds, s_tiles, s_bias, tile, total, ntiles, NT);
     else if (sel == 1)
-      tile_loop<2, OUT_F32, ACT, false>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
+      tile_loop<2, OUT_F32, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
                                         lds, s_tiles, s_bias, tile, total, ntiles, NT);
     else
-      tile_loop<1, OUT_F32, ACT, false>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
+      tile_loop<1, OUT_F32, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
                                         lds, s_tiles, s_bias, tile, total, ntiles, NT);
   }
 #endif
@@ -803,6 +927,24 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uin
   else if (act == kActGeluTanh) MOE_GEMM(false, kActGeluTanh);
   else MOE_GEMM(false, kActNone);
 #undef MOE_GEMM
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_wt(const uint16_t* A, const int32_t* row_idx, const uint16_t* W,
+                               const float* bias, float* out, const int32_t* offsets, int E, int N,
+                               int K, int64_t max_rows, int max_rows_per_expert, hipStream_t s) {
+  if (max_rows <= 0) return hipSuccess;
+  const bool shorter = max_rows_per_expert < 256;
+  const int64_t mt_bound = max_rows / (shorter ? 64 : 192) + E;
+  const int slots = cu_count();
+  const int64_t tiles = mt_bound * ((N + BN - 1) / BN);
+  const unsigned grid = static_cast<unsigned>(tiles < slots ? tiles : slots);
+  if (shorter)
+    grouped_gemm_bf16_kernel<true, kActNone, true, true><<<grid, 256, 0, s>>>(
+        A, row_idx, W, bias, out, nullptr, nullptr, offsets, E, N, K);
+  else
+    grouped_gemm_bf16_kernel<true, kActNone, false, true><<<grid, 256, 0, s>>>(
+        A, row_idx, W, bias, out, nullptr, nullptr, offsets, E, N, K);
   return hipGetLastError();
 }
 

@@ -33,25 +33,42 @@ def next_list(TM, TN):
     return ", ".join([f'"=&v"(nt[{j}])' for j in range(TM)] + [f'"=&v"(nw[{i}])' for i in range(TN)])
 
 
+def next_list_t(TM, TN):
+    return ", ".join([f'"=&v"(nt[{j}])' for j in range(TM)] + [f'"=&v"(nlo[{i}])' for i in range(TN)] +
+                     [f'"=&v"(nhi[{i}])' for i in range(TN)])
+
+
+def wa_list(TN):
+    return ", ".join(f'"v"(wa[{i}])' for i in range(TN))
+
+
 def mfmas(TM, TN, w0, t0):
     return [f"v_mfma_f32_32x32x16_bf16 %{TM*i+j}, %{w0+i}, %{t0+j}, %{TM*i+j}"
             for i in range(TN) for j in range(TM)]
 
 
-def step_body(TM, TN, dma, half=None):
+def step_body(TM, TN, dma, half=None, wt=False):
+    """wt: the weight stage is stored K-major (64 rows of 256 features); each
+    weight fragment comes from two transposing reads (k 0..3 and 4..7 of the
+    lane's 8, 4 rows = 2048 bytes apart) into a low and a high 64-bit half,
+    from one address operand per fragment tile."""
     nacc = TM * TN
     nt0 = nacc
     nw0 = nt0 + TM
-    w0 = nw0 + TN
+    w0 = nw0 + (2 * TN if wt else TN)
     t0 = w0 + TN
     ta = t0 + TM
     wa = ta + 1
     LA, LB = 2 * TM, 2 * TN
-    vo0 = wa + 1
+    vo0 = wa + (TN if wt else 1)
     la = vo0 + LA + LB
     lb, ga, gw = la + 1, la + 2, la + 3
-    reads = ([f"ds_read_b128 %{nt0+j}, %{ta} offset:{4096*j}" for j in range(TM)] +
-             [f"ds_read_b128 %{nw0+i}, %{wa} offset:{4096*i}" for i in range(TN)])
+    reads = [f"ds_read_b128 %{nt0+j}, %{ta} offset:{4096*j}" for j in range(TM)]
+    if wt:
+        reads += [f"ds_read_b64_tr_b16 %{nw0+i+TN*h}, %{wa+i} offset:{2048*h}"
+                  for i in range(TN) for h in range(2)]
+    else:
+        reads += [f"ds_read_b128 %{nw0+i}, %{wa} offset:{4096*i}" for i in range(TN)]
     mf = mfmas(TM, TN, w0, t0)
     loads = []
     if dma:
@@ -84,22 +101,33 @@ def step_body(TM, TN, dma, half=None):
     return "\n".join(q(s) for s in out) + '\n      "s_waitcnt lgkmcnt(0)"'
 
 
-def dma_half(TM, TN, half):
+def dma_half(TM, TN, half, wt=False):
     LA, LB = 2 * TM, 2 * TN
     n = f"{TM}x{TN}"
     vo = ", ".join(f'"v"(vo[{b}])' for b in range(LA + LB))
     sig_cur = f"const bf16x8_t (&w)[{TN}], const bf16x8_t (&t)[{TM}]"
-    sig_next = f"bf16x8_t (&nw)[{TN}], bf16x8_t (&nt)[{TM}]"
+    if wt:
+        name = f"step_dma{half}_t_{n}"
+        sig_next = f"bf16x8_t (&nt)[{TM}], v4i16 (&nlo)[{TN}], v4i16 (&nhi)[{TN}]"
+        addr_sig = f"uint32_t ta, const uint32_t (&wa)[{TN}]"
+        addr = f'"v"(ta), {wa_list(TN)}'
+        nxt = next_list_t(TM, TN)
+    else:
+        name = f"step_dma{half}_{n}"
+        sig_next = f"bf16x8_t (&nw)[{TN}], bf16x8_t (&nt)[{TM}]"
+        addr_sig = "uint32_t ta, uint32_t wa"
+        addr = '"v"(ta), "v"(wa)'
+        nxt = next_list(TM, TN)
     which = "first" if half == 0 else "second"
     return f'''// a K16 step that also issues the {which} half of a stage's LDS-DMA loads
-__device__ __forceinline__ void step_dma{half}_{n}(f32x16_t (&acc)[{TN}][{TM}], {sig_cur},
-    {sig_next}, uint32_t ta, uint32_t wa, const uint32_t (&vo)[{LA+LB}], uint32_t la, uint32_t lb,
+__device__ __forceinline__ void {name}(f32x16_t (&acc)[{TN}][{TM}], {sig_cur},
+    {sig_next}, {addr_sig}, const uint32_t (&vo)[{LA+LB}], uint32_t la, uint32_t lb,
     const char* ga, const char* gw) {{
   asm volatile(
-{step_body(TM, TN, True, half)}
+{step_body(TM, TN, True, half, wt)}
       : {acc_list(TM, TN)},
-        {next_list(TM, TN)}
-      : {cur_list(TM, TN)}, "v"(ta), "v"(wa),
+        {nxt}
+      : {cur_list(TM, TN)}, {addr},
         {vo},
         "s"(la), "s"(lb), "s"(ga), "s"(gw)
       : "memory", "m0", "scc");
@@ -115,6 +143,9 @@ def emit(TM, TN):
     last = "\n".join(q(s) for s in ["s_nop 1"] + mfmas(TM, TN, w0, t0) + ["s_nop 7", "s_nop 7"])
     frag = ([f"ds_read_b128 %{j}, %{TM+TN} offset:{4096*j}" for j in range(TM)] +
             [f"ds_read_b128 %{TM+i}, %{TM+TN+1} offset:{4096*i}" for i in range(TN)])
+    frag_t = ([f"ds_read_b128 %{j}, %{TM+2*TN} offset:{4096*j}" for j in range(TM)] +
+              [f"ds_read_b64_tr_b16 %{TM+i+TN*h}, %{TM+2*TN+1+i} offset:{2048*h}"
+               for i in range(TN) for h in range(2)])
     frag_outs = ", ".join([f'"=&v"(nt[{j}])' for j in range(TM)] + [f'"=&v"(nw[{i}])' for i in range(TN)])
     stg = []
     for b in range(LA):
@@ -157,6 +188,31 @@ __device__ __forceinline__ void frags_{n}({sig_next}, uint32_t ta, uint32_t wa) 
       "s_waitcnt lgkmcnt(0)"
       : {frag_outs}
       : "v"(ta), "v"(wa)
+      : "memory");
+}}
+
+// Variants for a K-major weight stage: the weight fragments come from
+// transposing reads, in 64-bit halves the caller joins.
+__device__ __forceinline__ void step_t_{n}(f32x16_t (&acc)[{TN}][{TM}], {sig_cur},
+    bf16x8_t (&nt)[{TM}], v4i16 (&nlo)[{TN}], v4i16 (&nhi)[{TN}], uint32_t ta, const uint32_t (&wa)[{TN}]) {{
+  asm volatile(
+{step_body(TM, TN, False, None, True)}
+      : {acc_list(TM, TN)},
+        {next_list_t(TM, TN)}
+      : {cur_list(TM, TN)}, "v"(ta), {wa_list(TN)}
+      : "memory");
+}}
+
+{dma_half(TM, TN, 0, True)}
+{dma_half(TM, TN, 1, True)}
+
+__device__ __forceinline__ void frags_t_{n}(bf16x8_t (&nt)[{TM}], v4i16 (&nlo)[{TN}], v4i16 (&nhi)[{TN}],
+    uint32_t ta, const uint32_t (&wa)[{TN}]) {{
+  asm volatile(
+{chr(10).join(q(s) for s in frag_t)}
+      "s_waitcnt lgkmcnt(0)"
+      : {next_list_t(TM, TN)}
+      : "v"(ta), {wa_list(TN)}
       : "memory");
 }}
 

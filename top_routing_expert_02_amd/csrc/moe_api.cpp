@@ -166,8 +166,10 @@ BwdLayout bwd_layout_of(const moe_config& c) {
   const int es = elem_size(c);
   const bool gather = layer_gathers(c);
   L.logits = take(T * E * 4);
-  L.W1t = take(E * d * f * es);
-  L.W2t = take(E * d * f * es);
+  // transposed expert weights (fp32 layers only: the bf16 GEMM reads W1
+  // and W2 as stored for the dgrad products)
+  L.W1t = take(c.dtype == MOE_BF16 ? 0 : E * d * f * es);
+  L.W2t = take(c.dtype == MOE_BF16 ? 0 : E * d * f * es);
   L.x_perm = take(gather ? 0 : R * d * es);
   L.dy_perm = take(gather ? 0 : R * d * es);
   L.u = take(R * f * 4);
@@ -598,9 +600,13 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* x, const void* W_r
   else
     MOE_HIP(launch_logits_f32(static_cast<const float*>(x), static_cast<const float*>(W_r), b_r,
                               logits, c.T, c.d, c.E, s));
-  // transposed expert weights for the dgrad GEMMs: W1t[e] [d, d_ff], W2t[e] [d_ff, d]
-  MOE_HIP(launch_transpose(W1, W1t, c.E, c.d_ff, c.d, bf, s));
-  MOE_HIP(launch_transpose(W2, W2t, c.E, c.d, c.d_ff, bf, s));
+  // fp32 layers: transposed expert weights for the dgrad GEMMs,
+  // W1t[e] [d, d_ff], W2t[e] [d_ff, d] (the bf16 GEMM reads W1 and W2 as
+  // stored, K-major)
+  if (!bf) {
+    MOE_HIP(launch_transpose(W1, W1t, c.E, c.d_ff, c.d, false, s));
+    MOE_HIP(launch_transpose(W2, W2t, c.E, c.d, c.d_ff, false, s));
+  }
   // token rows of x and dy for the kept rows (read through row_token, or copied)
   const bool gather = layer_gathers(c);
   const void* xa = x;
@@ -617,8 +623,8 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* x, const void* W_r
   if (bf) {
     MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(xa), ridx, static_cast<const uint16_t*>(W1), b1,
                              u, nullptr, nullptr, true, kActNone, offsets, c.E, c.d_ff, c.d, R, per_expert, s));
-    MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(dya), ridx, static_cast<const uint16_t*>(W2t),
-                             nullptr, Z, nullptr, nullptr, true, kActNone, offsets, c.E, c.d_ff, c.d, R, per_expert, s));
+    MOE_HIP(launch_gemm_bf16_wt(static_cast<const uint16_t*>(dya), ridx, static_cast<const uint16_t*>(W2),
+                                nullptr, Z, offsets, c.E, c.d_ff, c.d, R, per_expert, s));
   } else {
     MOE_HIP(launch_gemm_f32(static_cast<const float*>(xa), ridx, static_cast<const float*>(W1), b1, u,
                             kActNone, offsets, c.E, c.d_ff, c.d, per_expert, s));
@@ -633,8 +639,8 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* x, const void* W_r
   // dx_perm = du W1_e
   MOE_TRY(mark(MOE_BWD_STAGE_DGRAD));
   if (bf)
-    MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(du), nullptr, static_cast<const uint16_t*>(W1t),
-                             nullptr, dxp, nullptr, nullptr, true, kActNone, offsets, c.E, c.d, c.d_ff, R, per_expert, s));
+    MOE_HIP(launch_gemm_bf16_wt(static_cast<const uint16_t*>(du), nullptr, static_cast<const uint16_t*>(W1),
+                                nullptr, dxp, offsets, c.E, c.d, c.d_ff, R, per_expert, s));
   else
     MOE_HIP(launch_gemm_f32(static_cast<const float*>(du), nullptr, static_cast<const float*>(W1t), nullptr,
                             dxp, kActNone, offsets, c.E, c.d, c.d_ff, per_expert, s));

@@ -182,6 +182,12 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uin
                             const float* bias, void* out, float* out2, int32_t* nsplit,
                             bool out_f32, int act, const int32_t* offsets, int E, int N, int K,
                             int64_t max_rows, int max_rows_per_expert, hipStream_t s);
+// The same product with each W_e stored [K, N] (the transposed layout, so
+// that out = A W_e with W_e as given): fp32 out, no activation, no K split.
+// N and K are multiples of 64.
+hipError_t launch_gemm_bf16_wt(const uint16_t* A, const int32_t* row_idx, const uint16_t* W,
+                               const float* bias, float* out, const int32_t* offsets, int E, int N,
+                               int K, int64_t max_rows, int max_rows_per_expert, hipStream_t s);
 hipError_t launch_gemm_f32(const float* A, const int32_t* row_idx, const float* W, const float* bias,
                            float* out,
                            int act, const int32_t* offsets, int E, int N, int K,
