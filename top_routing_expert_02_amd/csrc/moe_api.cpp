@@ -20,6 +20,13 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int64_t ntiles_of(int64_t T) { return (T + kTileTokens - 1) / kTileTokens; }
 
+// tokens per top-k block: quarter tiles when whole tiles would leave most of
+// the chip idle (bf16 layers; their logits kernel clears the histograms the
+// quarter-tile blocks add into)
+int topk_block_tokens(const moe_config& c) {
+  return (c.dtype == MOE_BF16 && ntiles_of(c.T) < 256) ? 16 : 64;
+}
+
 int64_t max_rows_of(const moe_config& c) {
   const int64_t a = c.T * c.k;
   const int64_t b = static_cast<int64_t>(c.E) * c.capacity;
@@ -81,7 +88,7 @@ Layout layout_of(const moe_config& c) {
   const int64_t T = c.T, E = c.E, k = c.k, R = max_rows_of(c), nt = ntiles_of(c.T);
   const int es = elem_size(c);
   L.logits = take(T * E * 4);
-  L.prob_part = take(nt * E * 4);
+  L.prob_part = take((T + 15) / 16 * E * 4);  // per top-k block (16 or 64 tokens)
   L.hist = take(nt * E * 4);
   L.base = take(nt * E * 4);
   L.ids = take(T * n_cand_of(c) * 4);
@@ -222,16 +229,19 @@ int32_t check_ws(const moe_config& c, void* ws, size_t ws_bytes) {
 int32_t route_stage(const moe_config& c, const void* x, const void* Wr, const float* br,
                     int32_t* ids, float* gates, float* prob_sum, float* logits, float* prob_part,
                     int32_t* hist, hipStream_t s) {
+  const int tb = topk_block_tokens(c);
+  int32_t* zero = (tb < kTileTokens) ? hist : nullptr;  // cleared for the quarter-tile sums
   if (c.dtype == MOE_BF16)
     MOE_HIP(launch_logits_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(Wr), br,
-                               logits, c.T, c.d, c.E, s));
+                               logits, c.T, c.d, c.E, zero, zero != nullptr ? ntiles_of(c.T) * c.E : 0,
+                               s));
   else
     MOE_HIP(launch_logits_f32(static_cast<const float*>(x), static_cast<const float*>(Wr), br, logits,
                               c.T, c.d, c.E, s));
   MOE_HIP(launch_topk(logits, c.T, c.E, c.k, n_cand_of(c), c.renormalize, ids, gates,
-                      prob_sum != nullptr ? prob_part : nullptr, hist, s));
+                      prob_sum != nullptr ? prob_part : nullptr, hist, tb, s));
   if (prob_sum != nullptr)
-    MOE_HIP(launch_prob_reduce(prob_part, static_cast<int>(ntiles_of(c.T)), c.E, prob_sum, s));
+    MOE_HIP(launch_prob_reduce(prob_part, static_cast<int>((c.T + tb - 1) / tb), c.E, prob_sum, s));
   return MOE_OK;
 }
 
@@ -596,7 +606,7 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* x, const void* W_r
   // router logits again (the probabilities of every expert are needed)
   if (bf)
     MOE_HIP(launch_logits_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W_r), b_r,
-                               logits, c.T, c.d, c.E, s));
+                               logits, c.T, c.d, c.E, nullptr, 0, s));
   else
     MOE_HIP(launch_logits_f32(static_cast<const float*>(x), static_cast<const float*>(W_r), b_r,
                               logits, c.T, c.d, c.E, s));

@@ -55,7 +55,8 @@ __device__ __forceinline__ float act_gelu_tanh_fast(float u) {
 
 // logits[t,e] = b_r[e] + sum_m x[t,m] W_r[e,m]  (fp32 result)
 hipError_t launch_logits_bf16(const uint16_t* x, const uint16_t* Wr, const float* br,
-                              float* logits, int64_t T, int d, int E, hipStream_t s);
+                              float* logits, int64_t T, int d, int E, int32_t* zero, int64_t nzero,
+                              hipStream_t s);
 hipError_t launch_logits_f32(const float* x, const float* Wr, const float* br, float* logits,
                              int64_t T, int d, int E, hipStream_t s);
 
@@ -64,7 +65,7 @@ hipError_t launch_logits_f32(const float* x, const float* Wr, const float* br, f
 // ids/gates are [T,nsel] (nsel >= k): the top-k then the next candidates;
 // renormalised gates divide by the sum over the first k only.
 hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int nsel, int renormalize,
-                       int32_t* ids, float* gates, float* prob_part, int32_t* hist,
+                       int32_t* ids, float* gates, float* prob_part, int32_t* hist, int tb,
                        hipStream_t s);
 // out[e] = sum over tiles of part[tile,e], tiles in order.
 hipError_t launch_prob_reduce(const float* part, int ntiles, int E, float* out, hipStream_t s);

@@ -36,12 +36,22 @@ namespace moe {
 // order, so neither P nor the pipelining changes the result. Rows past T
 // and experts past E are clamped on load; their outputs are computed and
 // never stored.
+//
+// zero (nullable): nzero ints the top-k kernel that follows accumulates into
+// (its per-tile expert histograms), cleared here to save a launch.
 template <int MT, int NT, int P>
 __global__ __launch_bounds__(256) void logits_bf16_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ Wr,
                                                           const float* __restrict__ br,
                                                           float* __restrict__ logits, int64_t T,
-                                                          int d, int E) {
+                                                          int d, int E, int32_t* __restrict__ zero,
+                                                          int64_t nzero) {
+  if (zero != nullptr) {
+    const int64_t nthreads = static_cast<int64_t>(gridDim.x) * gridDim.y * 256;
+    for (int64_t i = (static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * 256 + threadIdx.x;
+         i < nzero; i += nthreads)
+      zero[i] = 0;
+  }
   constexpr int NREG = MT * NT * 4;
   constexpr int ROWS = 16 * (MT + NT);  // staged rows per wave and step: x rows, then W_r rows
   constexpr int NLD = ROWS / 8;         // load instructions per step
@@ -214,12 +224,14 @@ __global__ __launch_bounds__(256) void logits_f32_kernel(const float* __restrict
 
 // ------------------------------------------------------------------ top-k, softmax, gates
 //
-// A block owns one tile of 64 tokens. A token is handled by a group of G
-// lanes (G a power of two, 4 <= G <= 64); lane g of the group holds the
-// logits of experts g, g+G, ... (NV of them). A wave holds 64/G tokens at a
-// time, and the block has enough waves (up to 16) that the tile takes as few
-// passes as possible: the rounds below are chains of dependent cross-lane
-// shuffles, so the kernel is latency-bound and wants many waves in flight.
+// A block owns TB tokens: a whole 64-token tile, or a quarter of one when
+// the layer has too few tiles to fill the chip. A token is handled by a
+// group of G lanes (G a power of two, 4 <= G <= 64); lane g of the group
+// holds the logits of experts g, g+G, ... (NV of them). A wave holds 64/G
+// tokens at a time, and the block has enough waves (up to 16) that it takes
+// as few passes as possible: the rounds below are chains of dependent
+// cross-lane shuffles, so the kernel is latency-bound and wants many waves
+// in flight.
 //
 // Round r of k picks the group-wide best (largest logit, then lowest index)
 // among the experts not yet taken, by an xor butterfly over the group; the
@@ -232,9 +244,11 @@ __global__ __launch_bounds__(256) void logits_f32_kernel(const float* __restrict
 // sums add the same two operands on both partner lanes, so every lane holds
 // a bit-identical total and reruns are bit-exact.
 //
-// Side outputs per tile: the expert histogram (integer LDS atomics, order
-// free) and sum_t p_{t,i} (fixed-order sums: lanes, then groups, then waves).
-template <int G, int NV, int WAVES>
+// Side outputs: the expert histogram of each 64-token tile (integer
+// atomics, order free: LDS per block, then, for quarter-tile blocks, added
+// into the tile's row, which the logits kernel cleared) and sum_t p_{t,i}
+// per block (fixed-order sums: lanes, then groups, then waves).
+template <int G, int NV, int WAVES, int TB>
 __global__ __launch_bounds__(64 * WAVES) void topk_kernel(const float* __restrict__ logits, int64_t T,
                                                    int E, int k, int nsel, int renormalize,
                                                    int32_t* __restrict__ ids,
@@ -242,8 +256,9 @@ __global__ __launch_bounds__(64 * WAVES) void topk_kernel(const float* __restric
                                                    float* __restrict__ prob_part,
                                                    int32_t* __restrict__ hist) {
   constexpr int TPW = 64 / G;                 // tokens per wave pass
-  constexpr int PASSES = 64 / (TPW * WAVES);  // passes per wave
-  static_assert(TPW * WAVES * PASSES == 64, "64 tokens per tile");
+  constexpr int PASSES = TB / (TPW * WAVES);  // passes per wave
+  static_assert(TPW * WAVES * PASSES == TB, "TB tokens per block");
+  static_assert(TB == 64 || TB == 16, "whole or quarter tiles");
   constexpr int NT = 64 * WAVES;              // threads
   __shared__ float s_prob[WAVES][1024];
   __shared__ int s_hist[1024];
@@ -265,7 +280,7 @@ __global__ __launch_bounds__(64 * WAVES) void topk_kernel(const float* __restric
   for (int j = 0; j < NV; ++j) psum[j] = 0.f;
 
   for (int pass = 0; pass < PASSES; ++pass) {
-    const int64_t t = tile * 64 + (wave * PASSES + pass) * TPW + grp;
+    const int64_t t = tile * TB + (wave * PASSES + pass) * TPW + grp;
     const bool tv = t < T;
     const float* row = logits + (tv ? t : 0) * E;
     float v[NV];
@@ -364,7 +379,10 @@ __global__ __launch_bounds__(64 * WAVES) void topk_kernel(const float* __restric
       for (int w = 1; w < WAVES; ++w) sum += s_prob[w][e];  // fixed order
       prob_part[tile * E + e] = sum;
     }
-    if (want_hist) hist[tile * E + e] = s_hist[e];
+    if (want_hist) {
+      if constexpr (TB == 64) hist[tile * E + e] = s_hist[e];
+      else if (s_hist[e] != 0) atomicAdd(&hist[(tile * TB / 64) * E + e], s_hist[e]);
+    }
   }
 }
 
@@ -381,25 +399,26 @@ __global__ __launch_bounds__(256) void prob_reduce_kernel(const float* __restric
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_logits_bf16(const uint16_t* x, const uint16_t* Wr, const float* br,
-                              float* logits, int64_t T, int d, int E, hipStream_t s) {
+                              float* logits, int64_t T, int d, int E, int32_t* zero, int64_t nzero,
+                              hipStream_t s) {
   // tiles: 16 tokens x all of E up to 64 experts (32 tokens once that still
   // gives 256 blocks), 64 x 64 beyond; the ring depth P keeps 32-48 KiB of
   // loads in flight per wave
   if (E <= 16) {
     dim3 grid(static_cast<unsigned>((T + 15) / 16), 1);
-    logits_bf16_kernel<1, 1, 4><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E);
+    logits_bf16_kernel<1, 1, 4><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E, zero, nzero);
   } else if (E <= 32) {
     dim3 grid(static_cast<unsigned>((T + 15) / 16), 1);
-    logits_bf16_kernel<1, 2, 4><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E);
+    logits_bf16_kernel<1, 2, 4><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E, zero, nzero);
   } else if (E <= 64 && T >= 32 * 256) {
     dim3 grid(static_cast<unsigned>((T + 31) / 32), 1);
-    logits_bf16_kernel<2, 4, 3><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E);
+    logits_bf16_kernel<2, 4, 3><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E, zero, nzero);
   } else if (E <= 64) {
     dim3 grid(static_cast<unsigned>((T + 15) / 16), 1);
-    logits_bf16_kernel<1, 4, 4><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E);
+    logits_bf16_kernel<1, 4, 4><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E, zero, nzero);
   } else {
     dim3 grid(static_cast<unsigned>((T + 63) / 64), static_cast<unsigned>((E + 63) / 64));
-    logits_bf16_kernel<4, 4, 3><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E);
+    logits_bf16_kernel<4, 4, 3><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E, zero, nzero);
   }
   return hipGetLastError();
 }
@@ -411,12 +430,19 @@ hipError_t launch_logits_f32(const float* x, const float* Wr, const float* br, f
 }
 
 hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int nsel, int renormalize,
-                       int32_t* ids, float* gates, float* prob_part, int32_t* hist,
+                       int32_t* ids, float* gates, float* prob_part, int32_t* hist, int tb,
                        hipStream_t s) {
-  const unsigned grid = static_cast<unsigned>((T + 63) / 64);
-#define MOE_TOPK(G, NV)                                                                          \
-  topk_kernel<G, NV, (G >= 16 ? 16 : G)><<<grid, 64 * (G >= 16 ? 16 : G), 0, s>>>(                \
-      logits, T, E, k, nsel, renormalize, ids, gates, prob_part, hist)
+  const unsigned grid = static_cast<unsigned>((T + tb - 1) / tb);
+  // whole tiles: up to 16 waves; quarter tiles: G/4 waves, one pass
+#define MOE_TOPK(G, NV)                                                                           \
+  do {                                                                                            \
+    if (tb == 64)                                                                                 \
+      topk_kernel<G, NV, (G >= 16 ? 16 : G), 64><<<grid, 64 * (G >= 16 ? 16 : G), 0, s>>>(         \
+          logits, T, E, k, nsel, renormalize, ids, gates, prob_part, hist);                        \
+    else                                                                                          \
+      topk_kernel<G, NV, G / 4, 16><<<grid, 16 * G, 0, s>>>(logits, T, E, k, nsel, renormalize, ids, \
+                                                           gates, prob_part, hist);               \
+  } while (0)
   // groups of at least 16 lanes (k <= 16 results per token) holding up to 16
   // logits per lane: a wave runs 4 tokens' shuffle chains side by side, and
   // each round's butterfly has at most 4 levels below 256 experts
