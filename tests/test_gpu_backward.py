@@ -101,6 +101,10 @@ CASES = {
                                                  act="relu", renormalize=False), 0.0),
     "one_expert_bf16": (WORKLOADS["small_bf16"].scaled(name="one_expert_bwd", T=130, d=64,
                                                        d_ff=128, E=1, k=1, c=1.0), 0.2),
+    # d and d_ff above 256 and not multiples of it: the dgrad GEMMs' K-major
+    # weight stages end in a partial 256-feature tile (clamped columns)
+    "ragged_n_bf16": (WORKLOADS["small_bf16"].scaled(name="ragged_n_bwd", T=500, d=320, d_ff=448,
+                                                     E=4), 0.05),
 }
 
 
