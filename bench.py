@@ -298,9 +298,9 @@ def main():
             "expert_offsets": torch.empty(w.E + 1, dtype=torch.int32, device=dev)}
     stream = torch.cuda.current_stream()
 
-    def step(events=None):
+    def step(events=None, gemm_events=None):
         moe.layer_forward(cfg, inp["x"], inp["W_r"], inp["b_r"], inp["W1"], inp["b1"], inp["W2"],
-                          inp["b2"], y, info=info, ws=ws, stage_events=events)
+                          inp["b2"], y, info=info, ws=ws, stage_events=events, gemm_events=gemm_events)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -344,14 +344,23 @@ def main():
     ms = eager_ms if graph_ms is None else min(eager_ms, graph_ms)
     # stage breakdown: K more eager steps with a HIP event between stages
     # (not part of the timed region)
+    # Then K steps with events that the two expert GEMM kernels' dispatches
+    # record at their own start and end: kernel times without the launch
+    # gaps the stage events include (what a kernel trace reports). Separate
+    # steps, as the kernel events lengthen the stage intervals around them.
     ev = [moe.HipEvents(moe.MOE_NUM_STAGES + 1) for _ in range(K)]
+    gev = [moe.HipEvents(4) for _ in range(K)]
     torch.cuda.synchronize()
     for i in range(K):
         step(ev[i])
+    for i in range(K):
+        step(None, gev[i])
     torch.cuda.synchronize()
     stage_ms = {n: float(np.mean([e.elapsed_ms(s, s + 1) for e in ev]))
                 for s, n in enumerate(moe.STAGE_NAMES)}
-    for e in ev:
+    kernel_ms = {"gemm1": float(np.mean([e.elapsed_ms(0, 1) for e in gev])),
+                 "gemm2": float(np.mean([e.elapsed_ms(2, 3) for e in gev]))}
+    for e in ev + gev:
         e.close()
     log(f"[bench] {K} steps: {ms:.4f} ms/step (eager {eager_ms:.4f}, graph "
         f"{graph_ms if graph_ms is None else round(graph_ms, 4)}); stages {stage_ms}")
@@ -363,11 +372,16 @@ def main():
         st = {"ms": round(stage_ms[n], 5), "bytes": work[n]["bytes"], "flops": work[n]["flops"],
               "GB_s": work[n]["bytes"] / t / 1e9, "hbm_frac": work[n]["bytes"] / t / 1e9 / PEAK_HBM_GBS}
         if work[n]["flops"] and n.startswith("gemm"):
+            # rates over the kernel's own duration
             peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-            st["TFLOP_s"] = work[n]["flops"] / t / 1e12
+            tk = kernel_ms[n] * 1e-3
+            st["kernel_ms"] = round(kernel_ms[n], 5)
+            st["TFLOP_s"] = work[n]["flops"] / tk / 1e12
             st["mfma_frac"] = st["TFLOP_s"] / peak
+            st["GB_s"] = work[n]["bytes"] / tk / 1e9
+            st["hbm_frac"] = st["GB_s"] / PEAK_HBM_GBS
         stages[n] = st
-    dom = max(("gemm1", "gemm2"), key=lambda n: stage_ms[n])
+    dom = max(("gemm1", "gemm2"), key=lambda n: kernel_ms[n])
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     traffic = stored_traffic(w.name, dom)
     roofline = {"bound": "mfma", "kernel": f"grouped_gemm_bf16 ({dom})",

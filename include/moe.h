@@ -258,11 +258,17 @@ int32_t moe_combine(const moe_config *cfg, const float *y_perm, const int32_t *r
  *   ws/ws_bytes: at least moe_workspace_size bytes, 256-byte aligned.
  *   stage_events: NULL, or MOE_NUM_STAGES+1 caller-created hipEvents that
  *   are recorded on `stream` before the first stage and after each stage.
+ *   gemm_events: NULL, or 4 caller-created hipEvents: the start and the end
+ *   of the first expert GEMM's kernel, then of the second's. bf16 layers
+ *   have the kernel dispatches record them (hipExtLaunchKernelGGL), so each
+ *   difference is one kernel's execution time without launch gaps; fp32
+ *   layers record them on `stream` around the launch.
  */
 int32_t moe_layer_forward(const moe_config *cfg, const void *x, const void *W_r,
                           const float *b_r, const void *W1, const float *b1, const void *W2,
                           const float *b2, void *y, const moe_route_info *info, void *ws,
-                          size_t ws_bytes, hipEvent_t *stage_events, hipStream_t stream);
+                          size_t ws_bytes, hipEvent_t *stage_events, hipEvent_t *gemm_events,
+                          hipStream_t stream);
 
 /* Stage boundaries for moe_layer_backward's optional events. */
 enum {

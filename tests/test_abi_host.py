@@ -110,14 +110,18 @@ def test_entry_points_reject_without_launching(m):
     assert L.moe_expert_ffn(ctypes.byref(cfg), fake, fake, fake, None, fake, None, fake, fake, fake, 0, None) == -3
     assert L.moe_combine(ctypes.byref(cfg), fake, fake, fake, odd, None) == -1
     assert L.moe_layer_forward(ctypes.byref(cfg), fake, fake, None, fake, None, fake, None, None,
-                               None, fake, n, None, None) == -1
+                               None, fake, n, None, None, None) == -1
     bad = good_cfg(m, d=96)
     assert L.moe_layer_forward(ctypes.byref(bad), fake, fake, None, fake, None, fake, None, fake,
-                               None, fake, n, None, None) == -2
+                               None, fake, n, None, None, None) == -2
+    # GEMM kernel events: all four or none
+    gev = (ctypes.c_void_p * 4)(fake, fake, None, fake)
+    assert L.moe_layer_forward(ctypes.byref(cfg), fake, fake, None, fake, None, fake, None, fake,
+                               None, fake, n, None, gev, None) == -1
     # T == 0 is a no-op that succeeds without touching any pointer
     empty = good_cfg(m, T=0)
     assert L.moe_layer_forward(ctypes.byref(empty), None, None, None, None, None, None, None, None,
-                               None, None, 0, None, None) == 0
+                               None, None, 0, None, None, None) == 0
     assert L.moe_combine(ctypes.byref(empty), None, None, None, None, None) == 0
 
 

@@ -51,6 +51,8 @@
 //    never stored, so no tile reads outside [0, rows).
 #include "moe_internal.h"
 
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 namespace moe {
@@ -902,8 +904,17 @@ int cu_count() {
 hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uint16_t* W,
                             const float* bias, void* out, float* out2, int32_t* nsplit,
                             bool out_f32, int act, const int32_t* offsets, int E, int N, int K,
-                            int64_t max_rows, int max_rows_per_expert, hipStream_t s) {
-  if (max_rows <= 0) return hipSuccess;
+                            int64_t max_rows, int max_rows_per_expert, hipStream_t s,
+                            hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (max_rows <= 0) {
+    // nothing to launch: the events still mark this (empty) kernel's place
+    for (hipEvent_t ev : {ev_start, ev_stop})
+      if (ev != nullptr) {
+        const hipError_t e = hipEventRecord(ev, s);
+        if (e != hipSuccess) return e;
+      }
+    return hipSuccess;
+  }
   if (!out_f32 || act != kActNone) out2 = nullptr;  // a split needs a linear fp32 output
   const int smax = (out2 != nullptr && (K / BK) % 2 == 0) ? 2 : 1;
   // short tiles when no expert can fill a 256-row tile
@@ -913,14 +924,17 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uin
   const int slots = cu_count();
   const int64_t tiles = mt_bound * ((N + BN - 1) / BN) * smax;
   const unsigned grid = static_cast<unsigned>(tiles < slots ? tiles : slots);
-#define MOE_GEMM(OF, AC)                                                                          \
-  do {                                                                                            \
-    if (shorter)                                                                                  \
-      grouped_gemm_bf16_kernel<OF, AC, true><<<grid, 256, 0, s>>>(A, row_idx, W, bias, out, out2, \
-                                                                  nsplit, offsets, E, N, K);      \
-    else                                                                                          \
-      grouped_gemm_bf16_kernel<OF, AC, false><<<grid, 256, 0, s>>>(A, row_idx, W, bias, out, out2, \
-                                                                   nsplit, offsets, E, N, K);      \
+  // the dispatch records the optional events at the kernel's start and end
+#define MOE_GEMM(OF, AC)                                                                           \
+  do {                                                                                             \
+    if (shorter)                                                                                   \
+      hipExtLaunchKernelGGL(grouped_gemm_bf16_kernel<OF, AC, true>, dim3(grid), dim3(256), 0, s,    \
+                            ev_start, ev_stop, 0, A, row_idx, W, bias, out, static_cast<void*>(out2), \
+                            nsplit, offsets, E, N, K);                                              \
+    else                                                                                           \
+      hipExtLaunchKernelGGL(grouped_gemm_bf16_kernel<OF, AC, false>, dim3(grid), dim3(256), 0, s,   \
+                            ev_start, ev_stop, 0, A, row_idx, W, bias, out, static_cast<void*>(out2), \
+                            nsplit, offsets, E, N, K);                                              \
   } while (0)
   if (out_f32) MOE_GEMM(true, kActNone);
   else if (act == kActRelu) MOE_GEMM(false, kActRelu);

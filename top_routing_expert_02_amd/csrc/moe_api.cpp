@@ -283,32 +283,42 @@ int32_t dispatch_general_stage(const moe_config& c, void* ws, const void* x, con
 }
 
 // A is x_perm (row_idx null) or x with row r of the problem at row_idx[r].
+// e0/e1 (nullable): events for the GEMM kernel's start and end (recorded by
+// the dispatch itself for bf16, around the launch for fp32)
 int32_t gemm1_stage(const moe_config& c, const void* A, const int32_t* row_idx,
                     const int32_t* offsets, const void* W1, const float* b1, void* h,
-                    hipStream_t s) {
+                    hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
   const int64_t R = max_rows_of(c);
   const int per_expert = static_cast<int>(c.T < c.capacity ? c.T : c.capacity);
-  if (c.dtype == MOE_BF16)
+  if (c.dtype == MOE_BF16) {
     MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(A), row_idx, static_cast<const uint16_t*>(W1), b1,
-                             h, nullptr, nullptr, false, c.act, offsets, c.E, c.d_ff, c.d, R, per_expert, s));
-  else
+                             h, nullptr, nullptr, false, c.act, offsets, c.E, c.d_ff, c.d, R, per_expert, s,
+                             e0, e1));
+  } else {
+    if (e0 != nullptr) MOE_HIP(hipEventRecord(e0, s));
     MOE_HIP(launch_gemm_f32(static_cast<const float*>(A), row_idx, static_cast<const float*>(W1), b1,
                             static_cast<float*>(h), c.act, offsets, c.E, c.d_ff, c.d, per_expert, s));
+    if (e1 != nullptr) MOE_HIP(hipEventRecord(e1, s));
+  }
   return MOE_OK;
 }
 
 // y_perm2/nsplit (nullable): let a bf16 GEMM split K (see launch_gemm_bf16)
 int32_t gemm2_stage(const moe_config& c, const void* h, const int32_t* offsets, const void* W2,
                     const float* b2, float* y_perm, float* y_perm2, int32_t* nsplit,
-                    hipStream_t s) {
+                    hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
   const int64_t R = max_rows_of(c);
   const int per_expert = static_cast<int>(c.T < c.capacity ? c.T : c.capacity);
-  if (c.dtype == MOE_BF16)
+  if (c.dtype == MOE_BF16) {
     MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(h), nullptr, static_cast<const uint16_t*>(W2), b2,
-                             y_perm, y_perm2, nsplit, true, kActNone, offsets, c.E, c.d, c.d_ff, R, per_expert, s));
-  else
+                             y_perm, y_perm2, nsplit, true, kActNone, offsets, c.E, c.d, c.d_ff, R, per_expert, s,
+                             e0, e1));
+  } else {
+    if (e0 != nullptr) MOE_HIP(hipEventRecord(e0, s));
     MOE_HIP(launch_gemm_f32(static_cast<const float*>(h), nullptr, static_cast<const float*>(W2), b2, y_perm,
                             kActNone, offsets, c.E, c.d, c.d_ff, per_expert, s));
+    if (e1 != nullptr) MOE_HIP(hipEventRecord(e1, s));
+  }
   return MOE_OK;
 }
 
@@ -471,7 +481,8 @@ int32_t moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* r
 int32_t moe_layer_forward(const moe_config* cfg, const void* x, const void* W_r,
                           const float* b_r, const void* W1, const float* b1, const void* W2,
                           const float* b2, void* y, const moe_route_info* info, void* ws,
-                          size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
+                          size_t ws_bytes, hipEvent_t* stage_events, hipEvent_t* gemm_events,
+                          hipStream_t stream) {
   MOE_TRY(check_cfg(cfg));
   const moe_config& c = *cfg;
   if (c.T == 0) return MOE_OK;
@@ -490,6 +501,9 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* x, const void* W_r,
   if (stage_events != nullptr)
     for (int i = 0; i <= MOE_NUM_STAGES; ++i)
       if (stage_events[i] == nullptr) return MOE_ERR_INVALID_ARG;
+  if (gemm_events != nullptr)
+    for (int i = 0; i < 4; ++i)
+      if (gemm_events[i] == nullptr) return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_ws(c, ws, ws_bytes));
 
   const Layout L = layout_of(c);
@@ -525,12 +539,14 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* x, const void* W_r,
     MOE_TRY(dispatch_stage(c, x, ids, true, hist, at<int32_t>(ws, L.base), counts, offsets, slot,
                            row_of, row_token, x_perm, stream));
   MOE_TRY(mark(2));
+  hipEvent_t* ge = gemm_events;
   MOE_TRY(gemm1_stage(c, gather ? x : x_perm, gather ? row_token : nullptr, offsets, W1, b1, h,
-                      stream));
+                      stream, ge ? ge[0] : nullptr, ge ? ge[1] : nullptr));
   MOE_TRY(mark(3));
   float* y_perm2 = at<float>(ws, L.y_perm2);
   int32_t* nsplit = at<int32_t>(ws, L.nsplit);
-  MOE_TRY(gemm2_stage(c, h, offsets, W2, b2, y_perm, y_perm2, nsplit, stream));
+  MOE_TRY(gemm2_stage(c, h, offsets, W2, b2, y_perm, y_perm2, nsplit, stream, ge ? ge[2] : nullptr,
+                      ge ? ge[3] : nullptr));
   MOE_TRY(mark(4));
   MOE_TRY(combine_stage(c, y_perm, y_perm2, nsplit, row_of, cgates, y, stream));
   return mark(5);

@@ -182,7 +182,8 @@ hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int
 hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uint16_t* W,
                             const float* bias, void* out, float* out2, int32_t* nsplit,
                             bool out_f32, int act, const int32_t* offsets, int E, int N, int K,
-                            int64_t max_rows, int max_rows_per_expert, hipStream_t s);
+                            int64_t max_rows, int max_rows_per_expert, hipStream_t s,
+                            hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 // The same product with each W_e stored [K, N] (the transposed layout, so
 // that out = A W_e with W_e as given): fp32 out, no activation, no K split.
 // N and K are multiples of 64.

@@ -73,7 +73,7 @@ def lib():
         L.moe_expert_ffn.argtypes = [CFG, P, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_combine.argtypes = [CFG, P, P, P, P, P]
         L.moe_layer_forward.argtypes = [CFG, P, P, P, P, P, P, P, P, ctypes.POINTER(MoeRouteInfo),
-                                        P, SZ, P, P]
+                                        P, SZ, P, P, P]
         L.moe_backward_workspace_size.argtypes = [CFG, ctypes.POINTER(SZ)]
         L.moe_layer_backward.argtypes = [CFG, P, P, P, P, P, P, P, ctypes.POINTER(MoeRouteInfo), P,
                                          ctypes.c_float, P, P, P, P, P, P, P, P, SZ, P, P]
@@ -187,17 +187,20 @@ def combine(cfg, y_perm, row_of, topk_gates, y, stream=None):
 
 
 def layer_forward(cfg, x, W_r, b_r, W1, b1, W2, b2, y, info: dict | None = None, ws=None,
-                  stage_events=None, stream=None):
+                  stage_events=None, gemm_events=None, stream=None):
     """info: optional dict of output tensors keyed like moe_route_info's fields.
-    stage_events: optional HipEvents with MOE_NUM_STAGES + 1 events."""
+    stage_events: optional HipEvents with MOE_NUM_STAGES + 1 events.
+    gemm_events: optional HipEvents with 4 events (start and end of each
+    expert GEMM kernel)."""
     ws = alloc_workspace(cfg, x.device) if ws is None else ws
     ri = None
     if info:
         ri = MoeRouteInfo(**{k: _ptr(v) for k, v in info.items()})
     ev = stage_events.array if stage_events is not None else None
+    gev = gemm_events.array if gemm_events is not None else None
     _check("moe_layer_forward", lib().moe_layer_forward(
         ctypes.byref(cfg), _ptr(x), _ptr(W_r), _ptr(b_r), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
-        _ptr(y), ctypes.byref(ri) if ri is not None else None, _ptr(ws), ws.numel(), ev,
+        _ptr(y), ctypes.byref(ri) if ri is not None else None, _ptr(ws), ws.numel(), ev, gev,
         _stream(stream)))
 
 
