@@ -727,9 +727,14 @@ __global__ __launch_bounds__(256) void zero_empty_kernel(const int32_t* __restri
                                                          float* __restrict__ C) {
   const int64_t e = blockIdx.y;
   if (offsets[e + 1] > offsets[e]) return;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < MN;
-       i += static_cast<int64_t>(gridDim.x) * 256)
-    C[e * MN + i] = 0.f;
+  float* Ce = C + e * MN;
+  // 16-byte stores where the matrix starts 16-byte aligned, then the rest
+  const int64_t n4 = (reinterpret_cast<uintptr_t>(Ce) & 15) == 0 ? MN / 4 : 0;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  for (int64_t i = i0; i < n4; i += stride)
+    reinterpret_cast<float4*>(Ce)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t i = 4 * n4 + i0; i < MN; i += stride) Ce[i] = 0.f;
 }
 
 __global__ void range_kernel(int32_t* __restrict__ o, int32_t n) {
@@ -898,8 +903,12 @@ hipError_t launch_seg_colsum(const float* part, const int32_t* poff, int E, int 
 
 
 hipError_t launch_zero_empty(const int32_t* offsets, int E, int64_t MN, float* C, hipStream_t s) {
-  int64_t bx = (MN + 256 * 16 - 1) / (256 * 16);
-  if (bx > 4096) bx = 4096;
+  // blocks of experts with rows exit at once, but each still has to be
+  // dispatched: about 32K blocks in all (a million took 110 us)
+  int64_t bx = (MN + 256 * 64 - 1) / (256 * 64);
+  const int64_t cap = E < 32768 ? 32768 / E : 1;
+  if (bx > cap) bx = cap;
+  if (bx < 1) bx = 1;
   dim3 grid(static_cast<unsigned>(bx), E);
   zero_empty_kernel<<<grid, 256, 0, s>>>(offsets, MN, C);
   return hipGetLastError();
