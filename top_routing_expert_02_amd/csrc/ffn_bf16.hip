@@ -705,8 +705,16 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
   const int eb = tid * per;
   const int b = blockIdx.x;
   // blocks are dealt to the 8 XCDs round-robin: renumber so that consecutive
-  // tiles (which share weight and token panels) run on one XCD
-  const int tile = (Gd % 8 == 0) ? (b % 8) * (Gd / 8) + b / 8 : b;
+  // tiles (which share weight and token panels) run on one XCD. A launch
+  // whose tiles fit in one round spreads them evenly: ceil(tiles / 8) per
+  // XCD (a permutation of the blocks either way, so later rounds, at a
+  // stride of the grid, are unchanged).
+  auto xcd_tile = [&](int total) {
+    if (Gd % 8 != 0) return b;
+    const int per = (min(total, Gd) + 7) / 8;
+    const int kk = b / 8, x = b % 8;
+    return kk < per ? x * per + kk : 8 * per + (kk - per) * 8 + x;
+  };
   const int64_t wes = static_cast<int64_t>(N) * K;
   // K parts allowed: two when out2 is given and K splits into whole stages
   const int smax = (out2 != nullptr && (K / BK) % 2 == 0) ? 2 : 1;
@@ -764,6 +772,7 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
     const int ntiles = s_tiles[E] * NT;
     const int total = ntiles * S;
     const int nkl = K / BK / S;
+    const int tile = xcd_tile(total);
     if (tile >= total) return;
     if (tall)
       tile_loop<4, OUT_F32, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
@@ -821,6 +830,7 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
     const int ntiles = s_tiles[E] * NT;
     const int total = ntiles * S;
     const int nkl = K / BK / S;
+    const int tile = xcd_tile(total);
     if (tile >= total) return;
     if (sel == 0)
       tile_loop<3, OUT_F32, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
@@ -924,23 +934,33 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uin
   const int slots = cu_count();
   const int64_t tiles = mt_bound * ((N + BN - 1) / BN) * smax;
   const unsigned grid = static_cast<unsigned>(tiles < slots ? tiles : slots);
-  // the dispatch records the optional events at the kernel's start and end
-#define MOE_GEMM(OF, AC)                                                                           \
+  // with events, the dispatch records them at the kernel's start and end
+  // (hipExtLaunchKernelGGL); without, a plain launch (the extended launch
+  // measured several microseconds more launch gap per kernel)
+  const bool timed = ev_start != nullptr || ev_stop != nullptr;
+#define MOE_GEMM_ONE(OF, AC, SH)                                                                    \
   do {                                                                                             \
-    if (shorter)                                                                                   \
-      hipExtLaunchKernelGGL(grouped_gemm_bf16_kernel<OF, AC, true>, dim3(grid), dim3(256), 0, s,    \
+    if (timed)                                                                                     \
+      hipExtLaunchKernelGGL(grouped_gemm_bf16_kernel<OF, AC, SH>, dim3(grid), dim3(256), 0, s,      \
                             ev_start, ev_stop, 0, A, row_idx, W, bias, out, static_cast<void*>(out2), \
                             nsplit, offsets, E, N, K);                                              \
     else                                                                                           \
-      hipExtLaunchKernelGGL(grouped_gemm_bf16_kernel<OF, AC, false>, dim3(grid), dim3(256), 0, s,   \
-                            ev_start, ev_stop, 0, A, row_idx, W, bias, out, static_cast<void*>(out2), \
-                            nsplit, offsets, E, N, K);                                              \
+      grouped_gemm_bf16_kernel<OF, AC, SH><<<grid, 256, 0, s>>>(A, row_idx, W, bias, out, out2,    \
+                                                                nsplit, offsets, E, N, K);          \
+  } while (0)
+#define MOE_GEMM(OF, AC)            \
+  do {                              \
+    if (shorter)                    \
+      MOE_GEMM_ONE(OF, AC, true);   \
+    else                            \
+      MOE_GEMM_ONE(OF, AC, false);  \
   } while (0)
   if (out_f32) MOE_GEMM(true, kActNone);
   else if (act == kActRelu) MOE_GEMM(false, kActRelu);
   else if (act == kActGeluTanh) MOE_GEMM(false, kActGeluTanh);
   else MOE_GEMM(false, kActNone);
 #undef MOE_GEMM
+#undef MOE_GEMM_ONE
   return hipGetLastError();
 }
 
