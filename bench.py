@@ -36,24 +36,28 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="small_bf16")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mid_bf16",
+                    help="default: the 16384-token layer, the largest of the single-GPU workloads "
+                         "by expert FLOPs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget-s", type=float, default=30.0,
-                    help="upper bound on the oracle's CPU time for the baseline leg")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0,
+                    help="upper bound on the oracle's expert-FFN CPU time for the baseline leg")
     ap.add_argument("--backward", action="store_true",
                     help="time a training step instead: the layer forward, then its backward "
                          "(gradients of x and every parameter, L_aux coefficient 0.01)")
     ap.add_argument("--graph", action="store_true",
                     help="also time replays of the layer captured once in a HIP graph (on this "
                          "stack they were slower than eager launches; value takes the faster)")
-    ap.add_argument("--cold-steps", type=int, default=5,
+    ap.add_argument("--cold-steps", type=int, default=3,
                     help="after the timed steps, this many extra steps each preceded by a 1 GiB "
                          "write that evicts L2 and the MALL (reported as 'cold', not as value)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run a plain device copy of this many MiB "
                          "three times (calibrates the HBM byte counters of a profiler run)")
+    ap.add_argument("--only-timed", action="store_true",
+                    help="run the warmup and timed steps only (for profiler runs)")
     return ap.parse_args()
 
 
@@ -98,12 +102,14 @@ def copy_probe(mib):
     log(f"[bench] copy probe: 3 x {mib} MiB read + written")
 
 
-def stage_bytes_flops(w, C, counts, offsets):
-    """Algorithmic bytes and flops per stage (one launch each)."""
+def stage_bytes_flops(w, counts, offsets, t_any):
+    """Algorithmic bytes and flops per stage (one layer call), b bytes per
+    element of the layer's dtype everywhere (y_perm included).
+    t_any: tokens with at least one kept assignment."""
     import numpy as np
     b = 2 if w.dtype == "bf16" else 4
     rows = int(offsets[-1])
-    kept_e = np.minimum(counts, C)
+    kept_e = np.diff(np.asarray(offsets))
     T, d, d_ff, E, k = w.T, w.d, w.d_ff, w.E, w.k
     touched = int((kept_e > 0).sum())
     if w.priority != "token" or w.reroute > 0:
@@ -118,19 +124,37 @@ def stage_bytes_flops(w, C, counts, offsets):
         # x read once, W_r once, ids+gates written
         "route": {"bytes": T * d * b + E * d * b + T * k * 8, "flops": 2 * T * d * E},
         "dispatch": disp,
-        # touched experts' W1 read, x_perm read, h written
+        # touched experts' W1 read, token rows read, h written
         "gemm1": {"bytes": touched * d_ff * d * b + rows * d * b + rows * d_ff * b,
                   "flops": 2 * rows * d * d_ff},
-        # touched experts' W2 read, h read, y_perm (fp32) written
-        "gemm2": {"bytes": touched * d * d_ff * b + rows * d_ff * b + rows * d * 4,
+        # touched experts' W2 read, h read, y_perm written
+        "gemm2": {"bytes": touched * d * d_ff * b + rows * d_ff * b + rows * d * b,
                   "flops": 2 * rows * d * d_ff},
-        # y_perm rows read (fp32), ids/gates read, y written
-        "combine": {"bytes": rows * d * 4 + T * k * 8 + T * d * b, "flops": 0},
+        # y_perm rows read, ids/gates read, y written
+        "combine": {"bytes": rows * d * b + T * k * 8 + T * d * b, "flops": 0},
+        # stand-alone dispatch with the permuted copy (moe_dispatch): tokens with
+        # a kept assignment read once, kept rows written, metadata
+        "dispatch_x_perm": {"bytes": t_any * d * b + rows * d * b + T * k * 12 + rows * 4,
+                            "flops": 0},
     }
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, inp, C, budget_s):
-    """The fp64 oracle, as it stands, on the host cores."""
+    """The fp64 oracle, as it stands, on the host cores: route, dispatch and
+    combine on every token; the expert FFN on whole experts, one at a time
+    (weights widened per expert), until the budget is spent, its time
+    scaled to all rows."""
     import numpy as np
     from oracle import moe_oracle as mo
     from tests.parity import host64
@@ -139,36 +163,39 @@ def cpu_baseline(w, inp, C, budget_s):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    h = {k: host64(v, w.dtype) for k, v in inp.items()}
-    # estimate: FFN flops dominate; run the whole layer when it fits the budget,
-    # else a leading slice of the experts' rows (route + dispatch always whole)
+    x64 = host64(inp["x"], w.dtype)
     t0 = time.perf_counter()
-    r = mo.route(h["x"], h["W_r"], h["b_r"], w.k, w.renormalize)
+    r = mo.route(x64, host64(inp["W_r"], w.dtype), host64(inp["b_r"], "f32"), w.k, w.renormalize)
     dsp = mo.dispatch(r["topk_ids"], w.E, C)
+    x_perm = mo.permute(x64, dsp["row_token"])
     t_route = time.perf_counter() - t0
     rows = dsp["rows"]
-    x_perm = mo.permute(h["x"], dsp["row_token"])
     off = dsp["expert_offsets"]
     Y = np.zeros((rows, w.d))
-    t1 = time.perf_counter()
+    t_ffn = 0.0
     done_rows = 0
     for e in range(w.E):
         a, b = int(off[e]), int(off[e + 1])
-        if b > a:
-            _, Y[a:b] = mo.expert_ffn(x_perm[a:b], h["W1"][e], h["b1"][e], h["W2"][e], h["b2"][e], w.act)
-            done_rows += b - a
-        if time.perf_counter() - t1 > budget_s:
+        if b == a:
+            continue
+        W = (host64(inp["W1"][e], w.dtype), host64(inp["b1"][e], "f32"),
+             host64(inp["W2"][e], w.dtype), host64(inp["b2"][e], "f32"))
+        t1 = time.perf_counter()
+        _, Y[a:b] = mo.expert_ffn(x_perm[a:b], *W, w.act)
+        t_ffn += time.perf_counter() - t1
+        done_rows += b - a
+        if t_ffn > budget_s:
             break
-    t_ffn = time.perf_counter() - t1
     t2 = time.perf_counter()
     mo.combine(Y, dsp["row_of"], r["topk_gates"])
     t_comb = time.perf_counter() - t2
     frac = done_rows / max(1, rows)
     est = t_route + t_comb + (t_ffn / frac if frac > 0 else float("inf"))
     sample = ("whole layer" if frac >= 1.0 else
-              f"route+dispatch+combine on all {w.T} tokens, expert FFN on {done_rows}/{rows} rows "
-              f"(time scaled to all rows)")
+              f"route+dispatch+combine on all {w.T} tokens, expert FFN on whole experts holding "
+              f"{done_rows}/{rows} rows (its time scaled to all rows)")
     return {"value": w.T / est, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{w.name}: {sample}; fp64 numpy; {est:.2f} s per layer"}
 
 
@@ -294,36 +321,44 @@ def main():
     R = moe.max_rows(cfg)
     ws = moe.alloc_workspace(cfg, dev)
     y = torch.empty((w.T, w.d), dtype=w.torch_dtype, device=dev)
-    info = {"expert_counts": torch.empty(w.E, dtype=torch.int32, device=dev),
-            "expert_offsets": torch.empty(w.E + 1, dtype=torch.int32, device=dev)}
+    i32 = dict(dtype=torch.int32, device=dev)
+    info = {"expert_counts": torch.empty(w.E, **i32),
+            "expert_offsets": torch.empty(w.E + 1, **i32),
+            "row_of": torch.empty((w.T, w.k), **i32),
+            "prob_sum": torch.empty(w.E, dtype=torch.float32, device=dev)}
     stream = torch.cuda.current_stream()
 
-    def step(events=None, gemm_events=None):
+    def step(events=None, kernel_events=None):
         moe.layer_forward(cfg, inp["x"], inp["W_r"], inp["b_r"], inp["W1"], inp["b1"], inp["W2"],
-                          inp["b2"], y, info=info, ws=ws, stage_events=events, gemm_events=gemm_events)
+                          inp["b2"], y, info=info, ws=ws, stage_events=events,
+                          kernel_events=kernel_events)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    counts = info["expert_counts"].cpu().numpy()
-    offsets = info["expert_offsets"].cpu().numpy()
 
     K = args.steps
 
-    def timed(run):
+    def timed(run, n=K):
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record(stream)
-        for _ in range(K):
+        for _ in range(n):
             run()
         end.record(stream)
         torch.cuda.synchronize()
-        return start.elapsed_time(end) / K
+        return start.elapsed_time(end) / n
 
     # eager launches, no instrumentation
     eager_ms = timed(step)
+    log(f"[bench] {K} steps: {eager_ms:.4f} ms/step")
+    if args.only_timed:
+        print(json.dumps({"metric": METRIC, "value": w.T / (eager_ms * 1e-3), "unit": "tokens/s",
+                          "ms_per_step": eager_ms, "config": {"workload": w.name},
+                          "note": "profiler run: timed steps only"}), flush=True)
+        return
     graph_ms = None
     if args.graph:
         # the same layer call captured once and replayed (launches without
@@ -342,51 +377,99 @@ def main():
             g.replay()
         graph_ms = timed(g.replay)
     ms = eager_ms if graph_ms is None else min(eager_ms, graph_ms)
-    # stage breakdown: K more eager steps with a HIP event between stages
-    # (not part of the timed region)
-    # Then K steps with events that the two expert GEMM kernels' dispatches
-    # record at their own start and end: kernel times without the launch
-    # gaps the stage events include (what a kernel trace reports). Separate
-    # steps, as the kernel events lengthen the stage intervals around them.
-    ev = [moe.HipEvents(moe.MOE_NUM_STAGES + 1) for _ in range(K)]
-    gev = [moe.HipEvents(4) for _ in range(K)]
+    # per-stage kernel times: K more eager steps whose kernel dispatches
+    # record the start of each stage's first kernel and the end of its last
+    # (what a kernel trace reports, without the launch gaps), then K steps
+    # with events between stages on the stream (launch gaps included). Not
+    # part of the timed region.
+    kev = [moe.HipEvents(2 * moe.MOE_NUM_STAGES) for _ in range(K)]
+    sev = [moe.HipEvents(moe.MOE_NUM_STAGES + 1) for _ in range(K)]
     torch.cuda.synchronize()
     for i in range(K):
-        step(ev[i])
+        step(None, kev[i])
     for i in range(K):
-        step(None, gev[i])
+        step(sev[i])
     torch.cuda.synchronize()
-    stage_ms = {n: float(np.mean([e.elapsed_ms(s, s + 1) for e in ev]))
+    kernel_ms = {n: float(np.mean([e.elapsed_ms(2 * s, 2 * s + 1) for e in kev]))
+                 for s, n in enumerate(moe.STAGE_NAMES)}
+    stage_ms = {n: float(np.mean([e.elapsed_ms(s, s + 1) for e in sev]))
                 for s, n in enumerate(moe.STAGE_NAMES)}
-    kernel_ms = {"gemm1": float(np.mean([e.elapsed_ms(0, 1) for e in gev])),
-                 "gemm2": float(np.mean([e.elapsed_ms(2, 3) for e in gev]))}
-    for e in ev + gev:
+    for e in kev + sev:
         e.close()
-    log(f"[bench] {K} steps: {ms:.4f} ms/step (eager {eager_ms:.4f}, graph "
-        f"{graph_ms if graph_ms is None else round(graph_ms, 4)}); stages {stage_ms}")
+    log(f"[bench] stage kernels (ms): {kernel_ms}; stage intervals (ms): {stage_ms}")
 
-    work = stage_bytes_flops(w, C, counts, offsets)
+    counts = info["expert_counts"].cpu().numpy()
+    offsets = info["expert_offsets"].cpu().numpy()
+    row_of = info["row_of"].cpu().numpy()
+    t_any = int((row_of >= 0).any(axis=1).sum())
+    rows = int(offsets[-1])
+    work = stage_bytes_flops(w, counts, offsets, t_any)
+    bf = w.dtype == "bf16"
+    peak_flops = PEAK_BF16_TFLOPS if bf else PEAK_F32_TFLOPS
     stages = {}
     for n in moe.STAGE_NAMES:
-        t = stage_ms[n] * 1e-3
-        st = {"ms": round(stage_ms[n], 5), "bytes": work[n]["bytes"], "flops": work[n]["flops"],
-              "GB_s": work[n]["bytes"] / t / 1e9, "hbm_frac": work[n]["bytes"] / t / 1e9 / PEAK_HBM_GBS}
-        if work[n]["flops"] and n.startswith("gemm"):
-            # rates over the kernel's own duration
-            peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-            tk = kernel_ms[n] * 1e-3
-            st["kernel_ms"] = round(kernel_ms[n], 5)
+        tk = kernel_ms[n] * 1e-3
+        st = {"kernel_ms": round(kernel_ms[n], 5), "interval_ms": round(stage_ms[n], 5),
+              "bytes": work[n]["bytes"], "flops": work[n]["flops"],
+              "GB_s": work[n]["bytes"] / tk / 1e9, "hbm_frac": work[n]["bytes"] / tk / 1e9 / PEAK_HBM_GBS}
+        if work[n]["flops"]:
             st["TFLOP_s"] = work[n]["flops"] / tk / 1e12
-            st["mfma_frac"] = st["TFLOP_s"] / peak
-            st["GB_s"] = work[n]["bytes"] / tk / 1e9
-            st["hbm_frac"] = st["GB_s"] / PEAK_HBM_GBS
+            st["mfma_frac" if bf else "fp32_frac"] = st["TFLOP_s"] / peak_flops
         stages[n] = st
-    dom = max(("gemm1", "gemm2"), key=lambda n: kernel_ms[n])
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    traffic = stored_traffic(w.name, dom)
-    roofline = {"bound": "mfma", "kernel": f"grouped_gemm_bf16 ({dom})",
-                "achieved": stages[dom]["TFLOP_s"], "peak": peak, "unit": "TFLOP/s",
-                "frac": stages[dom]["TFLOP_s"] / peak, "traffic": traffic}
+
+    # the stand-alone dispatch entry point with the permuted copy of x
+    # (the layer path gathers token rows inside its first GEMM instead)
+    disp = None
+    if not (w.priority != "token" or w.reroute > 0):
+        ids = torch.empty((w.T, w.k), **i32)
+        gts = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+        moe.route(cfg, inp["x"], inp["W_r"], inp["b_r"], ids, gts, ws=ws)
+        o_counts, o_offs = torch.empty(w.E, **i32), torch.empty(w.E + 1, **i32)
+        o_slot, o_rof = torch.empty((w.T, w.k), **i32), torch.empty((w.T, w.k), **i32)
+        o_rt = torch.empty(max(R, 1), **i32)
+        x_perm = torch.empty((max(R, 1), w.d), dtype=w.torch_dtype, device=dev)
+
+        def dstep():
+            moe.dispatch(cfg, inp["x"], ids, o_counts, o_offs, o_slot, o_rof, o_rt, x_perm, ws=ws)
+
+        for _ in range(2):
+            dstep()
+        d_ms = timed(dstep)
+        nb = work["dispatch_x_perm"]["bytes"]
+        disp = {"ms": d_ms, "bytes": nb, "GB_s": nb / (d_ms * 1e-3) / 1e9,
+                "hbm_frac": nb / (d_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                "timing": "back-to-back moe_dispatch calls between two events (two kernels each)"}
+        del x_perm
+        log(f"[bench] stand-alone dispatch with x_perm: {d_ms:.4f} ms")
+
+    # load statistics of the step, computed on the device
+    stats_t = torch.empty(len(moe.STAT_NAMES), dtype=torch.float64, device=dev)
+    kept_t = torch.empty(w.E, **i32)
+    drop_t = torch.empty(w.E, **i32)
+    moe.load_stats(cfg, info["expert_counts"], info["expert_offsets"], info["prob_sum"], 0.01,
+                   stats_t, kept=kept_t, dropped=drop_t)
+    torch.cuda.synchronize()
+    load = dict(zip(moe.STAT_NAMES, stats_t.cpu().tolist()))
+    load["aux_alpha"] = 0.01
+    load["tokens_per_expert"] = counts.tolist() if w.E <= 64 else \
+        {"min": int(counts.min()), "median": float(np.median(counts)), "max": int(counts.max())}
+    kept_h, drop_h = kept_t.cpu().numpy(), drop_t.cpu().numpy()
+    load["kept_per_expert"] = kept_h.tolist() if w.E <= 64 else \
+        {"min": int(kept_h.min()), "median": float(np.median(kept_h)), "max": int(kept_h.max())}
+    load["dropped_per_expert"] = drop_h.tolist() if w.E <= 64 else \
+        {"experts_dropping": int((drop_h > 0).sum()), "max": int(drop_h.max())}
+
+    gemms = ("gemm1", "gemm2")
+    dom = max(gemms, key=lambda n: kernel_ms[n])
+    if bf:
+        roofline = {"bound": "mfma", "kernel": f"grouped_gemm_bf16 ({dom})",
+                    "achieved": stages[dom]["TFLOP_s"], "peak": peak_flops, "unit": "TFLOP/s",
+                    "frac": stages[dom]["TFLOP_s"] / peak_flops,
+                    "traffic": stored_traffic(w.name, dom)}
+    else:
+        roofline = {"bound": "alu", "kernel": f"gemm_f32 ({dom})",
+                    "achieved": stages[dom]["TFLOP_s"], "peak": peak_flops, "unit": "TFLOP/s",
+                    "frac": stages[dom]["TFLOP_s"] / peak_flops, "traffic": None}
 
     cold = None
     if args.cold_steps > 0:
@@ -411,7 +494,6 @@ def main():
 
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib)
-    rows = int(offsets[-1])
     out = {"metric": METRIC, "value": w.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
            "steps": K, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
@@ -419,11 +501,13 @@ def main():
                       "c": None if w.dropless else w.c, "C": C, "act": w.act, "rows": rows,
                       "dropped": w.T * w.k - rows, "priority": w.priority, "reroute_rounds": w.reroute,
                       "parallelism": "none"},
-           "roofline": roofline, "stages": stages,
+           "roofline": roofline, "stages": stages, "dispatch_x_perm": disp, "load": load,
            "timing": {"launch": "hip graph replay" if graph_ms is not None and graph_ms < eager_ms
                       else "eager",
                       "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
-                      "stages_from": "HIP events between stages of separate eager steps"}}
+                      "stages_from": "kernel_ms: start of each stage's first kernel to the end of "
+                                     "its last, recorded by the kernel dispatches (separate steps); "
+                                     "interval_ms: HIP events between stages on the stream"}}
     if cold is not None:
         out["cold"] = cold
     if not args.no_cpu_baseline:

@@ -19,9 +19,9 @@
  *    synchronises or prints; all work is enqueued on `stream` in order.
  *  - Row-major, last index contiguous. x [T,d]; W_r [E,d]; b_r [E];
  *    W1 [E,d_ff,d]; b1 [E,d_ff]; W2 [E,d,d_ff]; b2 [E,d]. W1[e] maps d -> d_ff.
- *  - x, W_r, W1, W2, x_perm, h and y have element type cfg->dtype (MOE_F32 or
- *    MOE_BF16, bf16 = the top 16 bits of an IEEE fp32). Biases, logits,
- *    probabilities, gates and y_perm are fp32 for both dtypes.
+ *  - x, W_r, W1, W2, x_perm, h, y_perm and y have element type cfg->dtype
+ *    (MOE_F32 or MOE_BF16, bf16 = the top 16 bits of an IEEE fp32). Biases,
+ *    logits, probabilities and gates are fp32 for both dtypes.
  *  - Top-k returns expert ids in descending score order; equal scores go to
  *    the lower expert index. The choice is made on fp32 logits.
  *  - Capacity is granted first-come in token order (a token's own k choices
@@ -36,8 +36,12 @@
  *    is never read back to the host; buffers indexed by row are sized by
  *    the bound max_rows = min(T*k, E*C) (see moe_max_rows). Entries at and
  *    beyond `rows` are left untouched.
- *  - Return value: MOE_OK (0) or a negative MOE_ERR_* code. On error nothing
- *    has been enqueued. T == 0 is a valid no-op returning MOE_OK.
+ *  - Return value: MOE_OK (0) or a negative MOE_ERR_* code. Every argument is
+ *    checked before the first launch: MOE_ERR_INVALID_ARG, _UNSUPPORTED and
+ *    _WORKSPACE enqueue nothing. MOE_ERR_HIP (a launch or event call the HIP
+ *    runtime refused) may leave the call's earlier kernels enqueued on
+ *    `stream`; its results are then undefined. T == 0 is a valid no-op
+ *    returning MOE_OK.
  *  - Results are deterministic: the same inputs give bit-identical outputs.
  */
 #ifndef MOE_MI355X_H
@@ -118,8 +122,8 @@ typedef struct moe_config {
 } moe_config;
 
 /*
- * Optional routing outputs of moe_layer_forward (device pointers; any may be
- * NULL, in which case that result stays in the workspace).
+ * Optional outputs of moe_layer_forward (device pointers; any may be NULL,
+ * in which case that result stays in the workspace).
  *   topk_ids [T,k] int32, topk_gates [T,k] fp32, prob_sum [E] fp32
  *   (sum over tokens of p_{t,i}, for the load-balance statistics of
  *   [MoE Principles] §3.2), expert_counts [E] int32 (before capacity),
@@ -129,6 +133,9 @@ typedef struct moe_config {
  *   topk_gates are [T,n_cand] candidate lists; served_ids [T,k] int32 and
  *   combine_gates [T,k] fp32 are the serving expert (-1 = dropped) and the
  *   combine weight (0 = dropped) of each assignment. Unused otherwise.
+ *   h [max_rows,d_ff] (dtype): the first expert GEMM's output
+ *   sigma(x W1_e^T + b1_e) per row, kept for the caller (rows >= offsets[E]
+ *   untouched); moe_layer_backward ignores it.
  */
 typedef struct moe_route_info {
   int32_t *topk_ids;
@@ -141,6 +148,7 @@ typedef struct moe_route_info {
   int32_t *row_token;
   int32_t *served_ids;
   float *combine_gates;
+  void *h;
 } moe_route_info;
 
 /*
@@ -232,22 +240,22 @@ int32_t moe_dispatch_reroute(const moe_config *cfg, const void *x, const int32_t
  *   in  x_perm [max_rows,d] (dtype), expert_offsets [E+1] int32 (device).
  *   in  W1 [E,d_ff,d], W2 [E,d,d_ff] (dtype); b1 [E,d_ff], b2 [E,d] fp32 or NULL.
  *   out h [max_rows,d_ff] (dtype): sigma(x_perm W1_e^T + b1_e), rounded once.
- *   out y_perm [max_rows,d] fp32: h W2_e^T + b2_e.
+ *   out y_perm [max_rows,d] (dtype): h W2_e^T + b2_e, rounded once.
  */
 int32_t moe_expert_ffn(const moe_config *cfg, const void *x_perm, const int32_t *expert_offsets,
                        const void *W1, const float *b1, const void *W2, const float *b2,
-                       void *h, float *y_perm, void *ws, size_t ws_bytes, hipStream_t stream);
+                       void *h, void *y_perm, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Combine ([MoE Principles] §2.2 output formula and §5 "send outputs back in
  * token order and weight them"):
  *   y_t = sum_{j<k, row_of[t,j] >= 0} topk_gates[t,j] * y_perm[row_of[t,j]],
  *   summed over j = 0..k-1 in fp32 and rounded once to dtype.
- *   in y_perm [max_rows,d] fp32, row_of [T,k] int32, topk_gates [T,k] fp32
- *   (with re-routing: moe_dispatch_reroute's combine_gates);
+ *   in y_perm [max_rows,d] (dtype), row_of [T,k] int32, topk_gates [T,k]
+ *   fp32 (with re-routing: moe_dispatch_reroute's combine_gates);
  *   out y [T,d] (dtype).
  */
-int32_t moe_combine(const moe_config *cfg, const float *y_perm, const int32_t *row_of,
+int32_t moe_combine(const moe_config *cfg, const void *y_perm, const int32_t *row_of,
                     const float *topk_gates, void *y, hipStream_t stream);
 
 /*
@@ -258,17 +266,53 @@ int32_t moe_combine(const moe_config *cfg, const float *y_perm, const int32_t *r
  *   ws/ws_bytes: at least moe_workspace_size bytes, 256-byte aligned.
  *   stage_events: NULL, or MOE_NUM_STAGES+1 caller-created hipEvents that
  *   are recorded on `stream` before the first stage and after each stage.
- *   gemm_events: NULL, or 4 caller-created hipEvents: the start and the end
- *   of the first expert GEMM's kernel, then of the second's. bf16 layers
- *   have the kernel dispatches record them (hipExtLaunchKernelGGL), so each
- *   difference is one kernel's execution time without launch gaps; fp32
- *   layers record them on `stream` around the launch.
+ *   kernel_events: NULL, or 2*MOE_NUM_STAGES caller-created hipEvents:
+ *   [2s] when stage s's first kernel starts and [2s+1] when its last kernel
+ *   ends, recorded by the kernel dispatches themselves, so each difference
+ *   is the stage's kernel time without the launch gap in front of it (a
+ *   stage without rows records both on `stream`).
+ * The second expert GEMM keeps y_perm in the workspace; when it splits K
+ * (few rows, long K) it keeps two fp32 partial sums there instead, which
+ * the combine adds before weighting.
  */
 int32_t moe_layer_forward(const moe_config *cfg, const void *x, const void *W_r,
                           const float *b_r, const void *W1, const float *b1, const void *W2,
                           const float *b2, void *y, const moe_route_info *info, void *ws,
-                          size_t ws_bytes, hipEvent_t *stage_events, hipEvent_t *gemm_events,
+                          size_t ws_bytes, hipEvent_t *stage_events, hipEvent_t *kernel_events,
                           hipStream_t stream);
+
+/* Figures of moe_load_stats, in this order in its stats array. */
+enum {
+  MOE_STAT_DROPPED = 0,        /* assignments without a row: T k - rows */
+  MOE_STAT_OVERFLOW_RATIO = 1, /* dropped / (T k) */
+  MOE_STAT_MAX_OVER_MEAN = 2,  /* max_e count_e / mean_e count_e (routed load) */
+  MOE_STAT_PADDING_RATIO = 3,  /* E C / rows: a padded [E, C] layout against the rows kept */
+  MOE_STAT_LOAD_ENTROPY = 4,   /* -sum_e f_e ln f_e, f_e = count_e / sum count */
+  MOE_STAT_KEPT_VARIANCE = 5,  /* population variance over experts of the rows each holds */
+  MOE_STAT_AUX_LOSS = 6,       /* aux_alpha E sum_e (count_e / T)(prob_sum_e / T); NaN without prob_sum */
+  MOE_STAT_KEPT_ROWS = 7,      /* rows = expert_offsets[E] */
+  MOE_NUM_STATS = 8
+};
+
+/*
+ * Load statistics of one routing step, computed on the device from the
+ * dispatch's outputs ([MoE Principles] §3.3: tokens received and dropped
+ * per expert, max/mean load; §13: tokens per expert, overflow ratio,
+ * padding ratio; §3.2: L_aux; ai-master.cc EP answer 001, follow-up 2:
+ * entropy of the expert activation distribution, variance of the tokens
+ * each expert processes). One small kernel on `stream`.
+ *   in  expert_counts [E] int32 (routed demand, before capacity),
+ *       expert_offsets [E+1] int32 (rows each expert holds), prob_sum [E]
+ *       fp32 or NULL (moe_route's sum over tokens of p_{t,e}).
+ *   out kept [E] int32 or NULL: offsets[e+1] - offsets[e].
+ *   out dropped [E] int32 or NULL: max(count_e - kept_e, 0) (the plain rule:
+ *       the tokens expert e turned away).
+ *   out stats [MOE_NUM_STATS] fp64 (required): see MOE_STAT_*.
+ * Sums run in a fixed order: the results are bit-reproducible.
+ */
+int32_t moe_load_stats(const moe_config *cfg, const int32_t *expert_counts,
+                       const int32_t *expert_offsets, const float *prob_sum, double aux_alpha,
+                       int32_t *kept, int32_t *dropped, double *stats, hipStream_t stream);
 
 /* Stage boundaries for moe_layer_backward's optional events. */
 enum {

@@ -525,17 +525,26 @@ def aux_loss(counts, prob_sum, T: int, E: int, alpha: float) -> float:
     return alpha * E * float(np.sum(f * pbar))
 
 
-def load_stats(counts, C: int, T: int, k: int) -> dict:
-    """What the pages ask to log per routing step  [MoE Principles §3.3, §13]:
-    tokens per expert, drops per expert, max/mean load, overflow ratio,
-    padding ratio of a padded [E, C] layout, entropy of the load."""
+def load_stats(counts, C: int, T: int, k: int, prob_sum=None, alpha: float = 1.0) -> dict:
+    """What the pages ask to log per routing step  [MoE Principles §3.3: tokens
+    and drops per expert, max/mean load; §13: tokens per expert, overflow
+    ratio, padding ratio; EP 001, follow-up 2: entropy of the expert
+    activation distribution and the variance of the tokens each expert
+    actually processes].
+
+    overflow_ratio = dropped assignments / (T k); max_over_mean_load = max /
+    mean of the routed counts; padding_ratio = E C / kept rows (a padded
+    [E, C] layout against the rows kept); load_entropy = -sum_i f_i ln f_i
+    over the routed shares f_i = count_i / sum(count); kept_variance = the
+    population variance of min(count_i, C). With prob_sum, aux_loss is
+    L_aux of §3.2 (aux_loss below) with the given alpha."""
     counts = np.asarray(counts, dtype=np.int64)
     E = counts.size
     kept = np.minimum(counts, C)
     dropped = counts - kept
     frac = counts / max(1, counts.sum())
     nz = frac[frac > 0]
-    return {
+    out = {
         "tokens_per_expert": counts.tolist(),
         "kept_per_expert": kept.tolist(),
         "dropped_per_expert": dropped.tolist(),
@@ -544,7 +553,11 @@ def load_stats(counts, C: int, T: int, k: int) -> dict:
         "max_over_mean_load": float(counts.max() / max(1e-300, counts.mean())) if E else 0.0,
         "padding_ratio": float(E * C / max(1, kept.sum())),
         "load_entropy": float(-(nz * np.log(nz)).sum()),
+        "kept_variance": float(np.mean((kept - kept.mean()) ** 2)) if E else 0.0,
     }
+    if prob_sum is not None:
+        out["aux_loss"] = aux_loss(counts, prob_sum, T, E, alpha)
+    return out
 
 
 def ffn_flops(rows: int, d: int, d_ff: int) -> int:

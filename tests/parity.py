@@ -153,3 +153,50 @@ def full_parity(w, inp, C, report=None):
     if report is not None:
         report(f"{w.name}: {stats}")
     return y, g, o, stats
+
+
+def expert_of_rows(offsets, rows) -> np.ndarray:
+    """The expert holding each row of the expert-major layout."""
+    return np.searchsorted(np.asarray(offsets), np.asarray(rows), side="right") - 1
+
+
+def covering_rows(offsets, step: int = 64) -> np.ndarray:
+    """Rows of every expert at multiples of `step` from its first row, plus
+    its last row: every M tile of the grouped GEMMs (heights 64, 128, 192
+    and 256 start at multiples of 64 within an expert) holds one of them."""
+    out = []
+    for e in range(len(offsets) - 1):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            out.extend(range(a, b, step))
+            out.append(b - 1)
+    return np.unique(np.asarray(out, dtype=np.int64))
+
+
+def oracle_rows(rows, x64, row_token, offsets, expert_weights, act):
+    """The oracle's expert FFN on the given rows, batched expert by expert:
+    (h [n, d_ff], Y [n, d]) in the order of `rows`. expert_weights(e)
+    returns (W1_e, b1_e, W2_e, b2_e) in fp64."""
+    rows = np.asarray(rows, dtype=np.int64)
+    e_of = expert_of_rows(offsets, rows)
+    h = Y = None
+    for e in np.unique(e_of):
+        idx = np.flatnonzero(e_of == e)
+        W1e, b1e, W2e, b2e = expert_weights(int(e))
+        he, Ye = mo.expert_ffn(x64[np.asarray(row_token)[rows[idx]]], W1e, b1e, W2e, b2e, act)
+        if h is None:
+            h = np.zeros((rows.size, he.shape[1]))
+            Y = np.zeros((rows.size, Ye.shape[1]))
+        h[idx], Y[idx] = he, Ye
+    return h, Y
+
+
+def oracle_tokens_y(tokens, rows, Y_rows, row_of, gates) -> np.ndarray:
+    """y of the given tokens from the expert outputs of `rows` (which must
+    hold every kept row of those tokens), combined by the oracle's rule."""
+    pos = np.full(int(np.max(row_of)) + 2 if row_of.size else 1, -1, dtype=np.int64)
+    pos[np.asarray(rows, dtype=np.int64)] = np.arange(len(rows))
+    ro = np.asarray(row_of)[tokens]
+    sub = np.where(ro >= 0, pos[np.maximum(ro, 0)], -1)
+    assert not ((ro >= 0) & (sub < 0)).any(), "a kept row of a checked token is missing"
+    return mo.combine(Y_rows, sub, np.asarray(gates)[tokens])

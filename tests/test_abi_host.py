@@ -114,10 +114,28 @@ def test_entry_points_reject_without_launching(m):
     bad = good_cfg(m, d=96)
     assert L.moe_layer_forward(ctypes.byref(bad), fake, fake, None, fake, None, fake, None, fake,
                                None, fake, n, None, None, None) == -2
-    # GEMM kernel events: all four or none
-    gev = (ctypes.c_void_p * 4)(fake, fake, None, fake)
+    # stage kernel events: all ten or none
+    kev = (ctypes.c_void_p * 10)(*([fake] * 9 + [None]))
     assert L.moe_layer_forward(ctypes.byref(cfg), fake, fake, None, fake, None, fake, None, fake,
-                               None, fake, n, None, gev, None) == -1
+                               None, fake, n, None, kev, None) == -1
+    # a misaligned optional output
+    info = m.MoeRouteInfo(h=0x100002)
+    assert L.moe_layer_forward(ctypes.byref(cfg), fake, fake, None, fake, None, fake, None, fake,
+                               ctypes.byref(info), fake, n, None, None, None) == -1
+    # every argument right but the workspace, which is checked last: still no
+    # launch (validation ends before the first kernel is enqueued)
+    kev_ok = (ctypes.c_void_p * 10)(*([fake] * 10))
+    sev_ok = (ctypes.c_void_p * 6)(*([fake] * 6))
+    assert L.moe_layer_forward(ctypes.byref(cfg), fake, fake, None, fake, None, fake, None, fake,
+                               None, fake, n - 256, sev_ok, kev_ok, None) == -3
+    # load statistics: stats required, finite alpha
+    f64 = ctypes.c_double
+    assert L.moe_load_stats(ctypes.byref(cfg), fake, fake, None, f64(0.01), None, None, None,
+                            None) == -1
+    assert L.moe_load_stats(ctypes.byref(cfg), fake, fake, None, f64(float("inf")), None, None, fake,
+                            None) == -1
+    assert L.moe_load_stats(ctypes.byref(cfg), fake, fake, odd, f64(0.01), None, None, fake,
+                            None) == -1
     # T == 0 is a no-op that succeeds without touching any pointer
     empty = good_cfg(m, T=0)
     assert L.moe_layer_forward(ctypes.byref(empty), None, None, None, None, None, None, None, None,

@@ -338,15 +338,16 @@ def test_stages_separately(name):
     np.testing.assert_array_equal(synth.to_numpy_bits(x_perm)[:rows], xb[o["row_token"]])
     # expert FFN on the oracle's layout
     hbuf = torch.zeros((R, w.d_ff), dtype=w.torch_dtype, device=dev)
-    yperm = torch.zeros((R, w.d), dtype=torch.float32, device=dev)
+    yperm = torch.zeros((R, w.d), dtype=w.torch_dtype, device=dev)
     m.expert_ffn(cfg, x_perm, offs, inp["W1"], inp["b1"], inp["W2"], inp["b2"], hbuf, yperm, ws=ws)
     torch.cuda.synchronize()
     P.compare_outputs(P.host64(hbuf, w.dtype)[:rows], o["h"], w.dtype)
-    P.compare_outputs(yperm.cpu().numpy().astype(np.float64)[:rows], o["y_perm"], w.dtype)
-    # combine, from the oracle's rows and gates (rounded to fp32 as the ABI takes them)
-    yp = torch.from_numpy(o["y_perm"].astype(np.float32)).to(dev)
+    P.compare_outputs(P.host64(yperm, w.dtype)[:rows], o["y_perm"], w.dtype)
+    # combine, from the oracle's rows (rounded to the layer's dtype as the ABI
+    # takes them) and gates (rounded to fp32)
+    yp = torch.from_numpy(o["y_perm"].astype(np.float32)).to(dev).to(w.torch_dtype)
     if rows == 0:
-        yp = torch.zeros((1, w.d), dtype=torch.float32, device=dev)
+        yp = torch.zeros((1, w.d), dtype=w.torch_dtype, device=dev)
     g32 = torch.from_numpy(o["topk_gates"].astype(np.float32)).to(dev)
     rof = torch.from_numpy(o["row_of"]).to(dev)
     y = torch.empty((w.T, w.d), dtype=w.torch_dtype, device=dev)
@@ -357,20 +358,37 @@ def test_stages_separately(name):
 
 # ------------------------------------------------------------------ full sizes
 
+# Full-size workloads the oracle runs whole in seconds: every token's y and
+# every row's h are compared. The others compare h on rows that cover every
+# (expert, M tile) of both GEMM schedules and y on the tokens of those rows.
+FULL_COMPARE = {"small_bf16", "skewed_bf16"}
+
+
 @pytest.mark.parametrize("name", ["small_bf16", "mid_bf16", "skewed_bf16", "large_e_bf16",
                                   "skewed_dropless_bf16", "decode_bf16", "skewed_reroute_bf16"])
 def test_full_size_workload(name):
     """Full-size workload in the launch configuration the benchmark times:
-    routing and dispatch on every token, x_perm on every row, y on sampled
-    tokens computed by the oracle one token and one expert at a time."""
+    routing and dispatch on every token, x_perm on every row, the first
+    GEMM's h and the layer's y against the oracle's expert FFN on all rows
+    (small and skewed layers) or on rows covering every GEMM tile."""
     w = WORKLOADS[name]
     say(f"[gpu] full size {name}: generating inputs")
     inp = synth.make_inputs(w, "cuda", seed=0)
     C = cap(w)
     m = moe()
     cfg = P.make_cfg(w, C)
+    R = m.max_rows(cfg)
+    dev = "cuda"
     say(f"[gpu] full size {name}: layer forward (C={C})")
-    y, g, _ = P.gpu_layer(w, inp, C)
+    info = P.info_tensors(w, R, dev)
+    info["h"] = torch.empty((max(R, 1), w.d_ff), dtype=w.torch_dtype, device=dev)
+    y = torch.full((w.T, w.d), float("nan"), dtype=w.torch_dtype, device=dev)
+    ws = m.alloc_workspace(cfg, dev)
+    m.layer_forward(cfg, inp["x"], inp["W_r"], inp["b_r"], inp["W1"], inp["b1"], inp["W2"],
+                    inp["b2"], y, info=info, ws=ws)
+    torch.cuda.synchronize()
+    h_gpu = info.pop("h")
+    g = {k: v.cpu().numpy() for k, v in info.items()}
     x64 = P.host64(inp["x"], w.dtype)
     o_route = mo.route(x64, P.host64(inp["W_r"], w.dtype), P.host64(inp["b_r"], "f32"),
                        P.n_cand(w), w.renormalize)
@@ -380,18 +398,13 @@ def test_full_size_workload(name):
     if general:
         o_disp = mo.dispatch_rerouted(g["topk_ids"], w.k, w.E, C, w.priority, w.reroute)
         np.testing.assert_array_equal(g["served_ids"], o_disp["served_ids"])
-        served = o_disp["served_ids"]
         gates_ref = mo.served_gates(mo.candidate_gates(o_route["probs"], g["topk_ids"], w.k,
                                                        w.renormalize), o_disp["served_col"])
     else:
         o_disp = mo.dispatch(g["topk_ids"], w.E, C)
-        served = g["topk_ids"]
         gates_ref = mo.gates(o_route["probs"], g["topk_ids"], w.renormalize)
     P.check_dispatch(g, o_disp)
     # x_perm of the same call, through the dispatch entry point
-    R = m.max_rows(cfg)
-    ws = m.alloc_workspace(cfg, "cuda")
-    dev = "cuda"
     t = {k: torch.empty_like(torch.from_numpy(v)).to(dev) for k, v in g.items()
          if k in ("expert_counts", "expert_offsets", "slot", "row_of")}
     row_token = torch.full((R,), -1, dtype=torch.int32, device=dev)
@@ -410,28 +423,146 @@ def test_full_size_workload(name):
     xb = synth.to_numpy_bits(inp["x"])
     np.testing.assert_array_equal(synth.to_numpy_bits(x_perm[:rows]), xb[o_disp["row_token"]])
     del x_perm, ws
-    # sampled outputs
-    rng = np.random.default_rng(123)
-    dropped_tok = np.flatnonzero(~o_disp["kept"].any(axis=1))
-    part_tok = np.flatnonzero(~o_disp["kept"].all(axis=1) & o_disp["kept"].any(axis=1))
-    tokens = sorted(set(rng.choice(w.T, size=24, replace=False).tolist()
-                        + dropped_tok[:4].tolist() + part_tok[:4].tolist() + [0, w.T - 1]))
+    # checked rows and tokens
+    offsets = o_disp["expert_offsets"]
+    row_of = o_disp["row_of"]
+    if name in FULL_COMPARE:
+        tokens = np.arange(w.T)
+    else:
+        cover = P.covering_rows(offsets)
+        owner = np.zeros(rows, dtype=np.int64)
+        kept = row_of >= 0
+        owner[row_of[kept]] = np.nonzero(kept)[0]
+        dropped_tok = np.flatnonzero(~o_disp["kept"].any(axis=1))
+        tokens = np.unique(np.concatenate([owner[cover], dropped_tok[:4], [0, w.T - 1]]))
+    need = np.unique(row_of[tokens][row_of[tokens] >= 0])
+    if name not in FULL_COMPARE:
+        assert np.isin(P.covering_rows(offsets), need).all()
 
     def expert_weights(e):
         return (P.host64(inp["W1"][e], w.dtype), P.host64(inp["b1"][e], "f32"),
                 P.host64(inp["W2"][e], w.dtype), P.host64(inp["b2"][e], "f32"))
 
-    say(f"[gpu] full size {name}: oracle on {len(tokens)} sampled tokens")
-    y_ref = mo.sampled_outputs(tokens, x64, served, o_disp["row_of"], gates_ref,
-                               expert_weights, w.act)
-    stats.update(P.compare_outputs(P.host64(y[tokens], w.dtype), y_ref, w.dtype))
-    stats.update(rows=rows, dropped=int((~o_disp["kept"]).sum()), C=C)
+    say(f"[gpu] full size {name}: oracle on {need.size} rows of {rows}, {tokens.size} tokens")
+    h_ref, Y_ref = P.oracle_rows(need, x64, o_disp["row_token"], offsets, expert_weights, w.act)
+    h_sel = P.host64(h_gpu[torch.from_numpy(need).to(dev)], w.dtype)
+    hs = P.compare_outputs(h_sel, h_ref, w.dtype)
+    y_ref = P.oracle_tokens_y(tokens, need, Y_ref, row_of, gates_ref)
+    stats.update(P.compare_outputs(P.host64(y[torch.from_numpy(tokens).to(dev)], w.dtype), y_ref,
+                                   w.dtype))
+    stats.update(rows=rows, dropped=int((~o_disp["kept"]).sum()), C=C, checked_rows=int(need.size),
+                 checked_tokens=int(tokens.size), h_max_abs=hs["max_abs"], h_rel_l2=hs["rel_l2"])
     say(f"[gpu] full size {name}: {stats}")
     # fully dropped tokens output exact zeros
+    dropped_tok = np.flatnonzero(~o_disp["kept"].any(axis=1))
     if dropped_tok.size:
         assert torch.all(y[torch.from_numpy(dropped_tok).to(dev)] == 0)
     if w.dropless:
         assert o_disp["kept"].all() and o_disp["rows"] == w.T * w.k
+
+
+# One expert holds every token, in more than 8 M tiles with a partial last
+# group of 4, so both GEMMs run the grouped tile order inside an expert
+# (experts past 8 M tiles: groups of 4 M tiles swept over the N tiles). With
+# 256 CUs the schedule picks 192-row tiles for the first case (14 M tiles,
+# groups 4+4+4+2) and 256-row tiles for the first GEMM of the second (11 M
+# tiles x 23 N tiles fill one round; groups 4+4+3); both split the second
+# GEMM's K. The stage entry point runs the same problem unsplit.
+MANY_MTILES = {
+    "hot_mtiles_192": dict(T=2500, d=512, d_ff=512),
+    "hot_mtiles_256": dict(T=2600, d=512, d_ff=5888),
+}
+
+
+@pytest.mark.parametrize("name", list(MANY_MTILES))
+def test_grouped_order_many_m_tiles(name):
+    w = WORKLOADS["small_bf16"].scaled(name=name, E=2, k=1, dropless=True, **MANY_MTILES[name])
+    dev = "cuda"
+    inp = synth.make_inputs(w, dev, seed=4)
+    inp["b_r"][0] += 40.0  # every token chooses expert 0
+    m = moe()
+    C = cap(w)
+    cfg = P.make_cfg(w, C)
+    R = m.max_rows(cfg)
+    say(f"[gpu] grouped order {name}: one expert with {w.T} rows, d={w.d} d_ff={w.d_ff}")
+    info = P.info_tensors(w, R, dev)
+    info["h"] = torch.full((R, w.d_ff), float("nan"), dtype=w.torch_dtype, device=dev)
+    y = torch.full((w.T, w.d), float("nan"), dtype=w.torch_dtype, device=dev)
+    m.layer_forward(cfg, inp["x"], inp["W_r"], inp["b_r"], inp["W1"], inp["b1"], inp["W2"],
+                    inp["b2"], y, info=info)
+    torch.cuda.synchronize()
+    h = P.host_inputs(inp, w.dtype)
+    o = mo.layer_forward(h["x"], h["W_r"], h["b_r"], h["W1"], h["b1"], h["W2"], h["b2"], k=w.k,
+                         C=C, renormalize=w.renormalize, act=w.act)
+    assert o["expert_counts"].tolist() == [w.T, 0]
+    g = {k: v.cpu().numpy() for k, v in info.items() if k != "h"}
+    P.check_dispatch(g, o)
+    st = {"h": P.compare_outputs(P.host64(info["h"], w.dtype), o["h"], w.dtype),
+          "y": P.compare_outputs(P.host64(y, w.dtype), o["y"], w.dtype)}
+    # the stage entry points on the oracle's permuted rows (no gather, no split)
+    xp = inp["x"][torch.from_numpy(o["row_token"]).to(dev)].contiguous()
+    hb = torch.full((R, w.d_ff), float("nan"), dtype=w.torch_dtype, device=dev)
+    yp = torch.full((R, w.d), float("nan"), dtype=w.torch_dtype, device=dev)
+    m.expert_ffn(cfg, xp, torch.from_numpy(o["expert_offsets"]).to(dev), inp["W1"], inp["b1"],
+                 inp["W2"], inp["b2"], hb, yp)
+    torch.cuda.synchronize()
+    st["stage_h"] = P.compare_outputs(P.host64(hb, w.dtype), o["h"], w.dtype)
+    st["stage_y_perm"] = P.compare_outputs(P.host64(yp, w.dtype), o["y_perm"], w.dtype)
+    say(f"[gpu] grouped order {name}: {st}")
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "f32_mid", "small_bf16_mini", "skewed_bf16_mini",
+                                  "large_e_bf16_mini"])
+def test_load_stats_on_gpu(name):
+    """moe_load_stats on the layer's own counts and probability sums against
+    the oracle's load_stats (pinned by hand-worked examples)."""
+    w = MINI[name]
+    dev = "cuda"
+    inp = synth.make_inputs(w, dev, seed=2)
+    C = cap(w)
+    y, g, cfg = P.gpu_layer(w, inp, C)
+    m = moe()
+    counts = torch.from_numpy(g["expert_counts"]).to(dev)
+    offsets = torch.from_numpy(g["expert_offsets"]).to(dev)
+    psum = torch.from_numpy(g["prob_sum"]).to(dev)
+    stats = torch.full((len(m.STAT_NAMES),), float("nan"), dtype=torch.float64, device=dev)
+    kept = torch.full((w.E,), -7, dtype=torch.int32, device=dev)
+    dropped = torch.full((w.E,), -7, dtype=torch.int32, device=dev)
+    alpha = 0.01
+    m.load_stats(cfg, counts, offsets, psum, alpha, stats, kept=kept, dropped=dropped)
+    torch.cuda.synchronize()
+    got = dict(zip(m.STAT_NAMES, stats.cpu().tolist()))
+    h = P.host_inputs(inp, w.dtype)
+    ref = mo.load_stats(g["expert_counts"], C, w.T, w.k,
+                        prob_sum=mo.route(h["x"], h["W_r"], h["b_r"], w.k, w.renormalize)["prob_sum"],
+                        alpha=alpha)
+    say(f"[gpu] load stats {name}: {got}")
+    assert kept.cpu().tolist() == ref["kept_per_expert"]
+    assert dropped.cpu().tolist() == ref["dropped_per_expert"]
+    assert got["dropped"] == ref["dropped"] and got["kept_rows"] == sum(ref["kept_per_expert"])
+    for key in ("overflow_ratio", "max_over_mean_load", "padding_ratio", "load_entropy",
+                "kept_variance"):
+        assert got[key] == pytest.approx(ref[key], rel=1e-12, abs=1e-12), key
+    assert got["aux_loss"] == pytest.approx(ref["aux_loss"], rel=1e-5)
+
+
+def test_f32_layer_ignores_stale_split_word():
+    """An fp32 layer has no K split: its combine must not read the split
+    word or partial buffer of the workspace, whatever they hold (here int32
+    2 everywhere, the value that means "split")."""
+    w = MINI["f32_mid"]
+    dev = "cuda"
+    inp = synth.make_inputs(w, dev, seed=6)
+    C = cap(w)
+    m = moe()
+    cfg = P.make_cfg(w, C)
+    ws = m.alloc_workspace(cfg, dev)
+    ws.view(torch.int32)[: ws.numel() // 4].fill_(2)
+    y, g, _ = P.gpu_layer(w, inp, C, ws=ws)
+    h = P.host_inputs(inp, w.dtype)
+    o = mo.layer_forward(h["x"], h["W_r"], h["b_r"], h["W1"], h["b1"], h["W2"], h["b2"], k=w.k,
+                         C=C, renormalize=w.renormalize, act=w.act, ids=g["topk_ids"])
+    P.compare_outputs(P.host64(y, w.dtype), o["y"], w.dtype)
 
 
 def test_graph_replay_matches_eager():

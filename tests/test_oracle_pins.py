@@ -426,6 +426,47 @@ def test_load_stats():
     assert s["padding_ratio"] == pytest.approx(2 * 4 / 6)
 
 
+def test_load_stats_worked_example():
+    """The page's §3.3 routing at C = 4 (§4.2), every figure worked by hand
+    (tests/golden/load_stats_example.json)."""
+    g = golden("load_stats_example.json")["worked"]
+    s = mo.load_stats(g["counts"], g["C"], g["T"], g["k"], prob_sum=g["prob_sum"], alpha=1.0)
+    assert s["kept_per_expert"] == [4, 2] and s["dropped_per_expert"] == [2, 0] and s["dropped"] == 2
+    assert s["overflow_ratio"] == pytest.approx(0.25, abs=1e-15)
+    assert s["max_over_mean_load"] == pytest.approx(1.5, abs=1e-15)
+    assert s["padding_ratio"] == pytest.approx(4.0 / 3.0, abs=1e-15)
+    assert s["load_entropy"] == pytest.approx(math.log(4.0) - 0.75 * math.log(3.0), abs=1e-15)
+    assert s["kept_variance"] == pytest.approx(1.0, abs=1e-15)
+    assert s["aux_loss"] == pytest.approx(1.05, abs=1e-12)
+
+
+def test_load_stats_overflow_example():
+    g = golden("load_stats_example.json")["overflow"]
+    s = mo.load_stats(g["counts"], g["C"], g["T"], g["k"])
+    assert s["dropped"] == 659
+    assert s["overflow_ratio"] == pytest.approx(659 / 1024, abs=1e-15)
+    assert s["max_over_mean_load"] == pytest.approx(819 / 128, abs=1e-15)
+    assert s["padding_ratio"] == pytest.approx(1280 / 365, abs=1e-15)
+
+
+@pytest.mark.parametrize("E,n", [(1, 7), (8, 100), (64, 3)])
+def test_load_stats_uniform(E, n):
+    """Equal loads: the entropy is ln E (its maximum), max/mean 1, no spread,
+    and nothing overflows when C holds each expert's share."""
+    s = mo.load_stats([n] * E, n, n * E, 1)
+    assert s["load_entropy"] == pytest.approx(math.log(E), abs=1e-12)
+    assert s["max_over_mean_load"] == 1.0 and s["kept_variance"] == 0.0
+    assert s["overflow_ratio"] == 0.0 and s["padding_ratio"] == 1.0
+
+
+def test_load_stats_one_hot_expert():
+    """Every assignment on one expert: zero entropy, max/mean E, and C caps it."""
+    s = mo.load_stats([0, 0, 40, 0], 10, 40, 1)
+    assert s["load_entropy"] == 0.0 and s["max_over_mean_load"] == 4.0
+    assert s["dropped"] == 30 and s["overflow_ratio"] == 0.75
+    assert s["kept_variance"] == pytest.approx(np.var([0, 0, 10, 0]), abs=1e-15)
+
+
 def test_widen_bf16_exact():
     vals = np.array([1.0, -2.5, 3.140625, 1e-3, 65504.0], dtype=np.float32)
     bits = (vals.view(np.uint32) >> 16).astype(np.uint16)
@@ -855,3 +896,12 @@ def test_planted_missing_aux_grad_is_caught(monkeypatch):
     orig = mo.layer_backward
     monkeypatch.setattr(mo, "layer_backward", lambda *a, **kw: orig(*a, **{**kw, "alpha": 0.0}))
     _expect_fail(check_backward_finite_differences)
+
+
+def test_load_stats_counts_assignments():
+    """Top-2 over 2 experts: every token holds both, so the 4 tokens make 8
+    assignments; C = 3 drops one per expert, 2 of the 8 (a ratio over tokens
+    would read 2 / 4)."""
+    s = mo.load_stats([4, 4], 3, 4, 2)
+    assert s["dropped"] == 2 and s["overflow_ratio"] == 0.25
+    assert s["padding_ratio"] == 1.0 and s["max_over_mean_load"] == 1.0

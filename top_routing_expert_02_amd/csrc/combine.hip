@@ -4,17 +4,62 @@
 // merged by the routing weights).
 //
 // Gather form: a thread owns VEC consecutive columns of one token, reads the
-// token's k rows of y_perm (fp32), accumulates j = 0..k-1 in fp32 in that
-// fixed order and rounds once. No atomics, so the result is deterministic; a
-// token with every assignment dropped writes exact zeros. After a K-split
-// second GEMM, a row is the sum of its two partial rows, formed before the
-// gate multiplies it.
+// token's k rows of y_perm (bf16 for bf16 layers, fp32 for fp32 layers),
+// accumulates j = 0..k-1 in fp32 in that fixed order and rounds once. No
+// atomics, so the result is deterministic; a token with every assignment
+// dropped writes exact zeros. After a K-split second GEMM (the device word
+// nsplit says 2) the rows are fp32 partial sums in two buffers: a row is
+// the sum of its two partial rows, formed before the gate multiplies it.
 #include "moe_internal.h"
 
 namespace moe {
 
+// the VEC columns c.. of row `ro` (element offset) as fp32
+template <int VEC>
+__device__ __forceinline__ void load_row(const void* __restrict__ yp, const float* __restrict__ y2,
+                                         int mode, int64_t ro, float (&q)[VEC]) {
+  if (mode == 1) {  // bf16 rows
+    const uint16_t* src = static_cast<const uint16_t*>(yp) + ro;
+    if constexpr (VEC == 8) {
+      const uint4 u = *reinterpret_cast<const uint4*>(src);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        q[2 * i] = __uint_as_float(w[i] << 16);
+        q[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) q[v] = bf16_to_f32(src[v]);
+    }
+    return;
+  }
+  const float* src = static_cast<const float*>(yp) + ro;
+  if constexpr (VEC % 4 == 0) {
+#pragma unroll
+    for (int v = 0; v < VEC; v += 4) {
+      float4 a = *reinterpret_cast<const float4*>(src + v);
+      if (mode == 2) {  // two fp32 partial sums
+        const float4 b = *reinterpret_cast<const float4*>(y2 + ro + v);
+        a.x += b.x;
+        a.y += b.y;
+        a.z += b.z;
+        a.w += b.w;
+      }
+      q[v] = a.x;
+      q[v + 1] = a.y;
+      q[v + 2] = a.z;
+      q[v + 3] = a.w;
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) q[v] = mode == 2 ? src[v] + y2[ro + v] : src[v];
+  }
+}
+
+// rows: 0 fp32, 1 bf16; with y_perm2 and *nsplit == 2, fp32 pairs (mode 2)
 template <int VEC, bool BF16>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y_perm, int rows_bf16,
                                                       const float* __restrict__ y_perm2,
                                                       const int32_t* __restrict__ nsplit,
                                                       const int32_t* __restrict__ row_of,
@@ -25,7 +70,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (gid >= T * chunks) return;
   const int64_t t = gid / chunks;
   const int c = static_cast<int>(gid - t * chunks) * VEC;
-  const float* y2 = (y_perm2 != nullptr && *nsplit == 2) ? y_perm2 : nullptr;
+  const int mode = (y_perm2 != nullptr && *nsplit == 2) ? 2 : rows_bf16;
   float acc[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
@@ -33,28 +78,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int row = row_of[t * k + j];
     if (row < 0) continue;
     const float g = gates[t * k + j];
-    const int64_t ro = static_cast<int64_t>(row) * d + c;
-    const float* src = y_perm + ro;
-    if constexpr (VEC % 4 == 0) {
+    float q[VEC];
+    load_row<VEC>(y_perm, y_perm2, mode, static_cast<int64_t>(row) * d + c, q);
 #pragma unroll
-      for (int v = 0; v < VEC; v += 4) {
-        float4 q = *reinterpret_cast<const float4*>(src + v);
-        if (y2 != nullptr) {
-          const float4 q2 = *reinterpret_cast<const float4*>(y2 + ro + v);
-          q.x += q2.x;
-          q.y += q2.y;
-          q.z += q2.z;
-          q.w += q2.w;
-        }
-        acc[v + 0] = fmaf(g, q.x, acc[v + 0]);
-        acc[v + 1] = fmaf(g, q.y, acc[v + 1]);
-        acc[v + 2] = fmaf(g, q.z, acc[v + 2]);
-        acc[v + 3] = fmaf(g, q.w, acc[v + 3]);
-      }
-    } else {
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) acc[v] = fmaf(g, y2 != nullptr ? src[v] + y2[ro + v] : src[v], acc[v]);
-    }
+    for (int v = 0; v < VEC; ++v) acc[v] = fmaf(g, q[v], acc[v]);
   }
   if constexpr (BF16) {
     static_assert(VEC == 8, "bf16 output uses 8 columns per thread");
@@ -71,19 +98,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-hipError_t launch_combine(const float* y_perm, const float* y_perm2, const int32_t* nsplit,
-                          const int32_t* row_of, const float* gates, int64_t T, int k, int d,
-                          bool out_bf16, void* y, hipStream_t s) {
+hipError_t launch_combine(const void* y_perm, bool yperm_bf16, const float* y_perm2,
+                          const int32_t* nsplit, const int32_t* row_of, const float* gates, int64_t T,
+                          int k, int d, bool out_bf16, void* y, hipStream_t s) {
   if (nsplit == nullptr) y_perm2 = nullptr;
+  const int rb = yperm_bf16 ? 1 : 0;
   if (out_bf16) {
     const int64_t n = T * (d / 8);
-    combine_kernel<8, true><<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(y_perm, y_perm2, nsplit, row_of, gates, T, k, d, y);
+    klaunch(combine_kernel<8, true>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+            y_perm, rb, y_perm2, nsplit, row_of, gates, T, k, d, y);
   } else if (d % 4 == 0) {
     const int64_t n = T * (d / 4);
-    combine_kernel<4, false><<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(y_perm, y_perm2, nsplit, row_of, gates, T, k, d, y);
+    klaunch(combine_kernel<4, false>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+            y_perm, rb, y_perm2, nsplit, row_of, gates, T, k, d, y);
   } else {
     const int64_t n = T * d;
-    combine_kernel<1, false><<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(y_perm, y_perm2, nsplit, row_of, gates, T, k, d, y);
+    klaunch(combine_kernel<1, false>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+            y_perm, rb, y_perm2, nsplit, row_of, gates, T, k, d, y);
   }
   return hipGetLastError();
 }

@@ -267,13 +267,13 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict
 
 hipError_t launch_hist(const int32_t* ids, int64_t T, int k, int E, int32_t* hist,
                        hipStream_t s) {
-  hist_kernel<<<static_cast<unsigned>((T + kTileTokens - 1) / kTileTokens), 256, 0, s>>>(ids, T, k, E, hist);
+  klaunch(hist_kernel, static_cast<unsigned>((T + kTileTokens - 1) / kTileTokens), 256, 0, s, ids, T, k, E, hist);
   return hipGetLastError();
 }
 
 hipError_t launch_scan(const int32_t* hist, int ntiles, int E, int C, int32_t* base,
                        int32_t* counts, int32_t* offsets, hipStream_t s) {
-  scan_kernel<<<1, 1024, 0, s>>>(hist, ntiles, E, C, base, counts, offsets);
+  klaunch(scan_kernel, 1, 1024, 0, s, hist, ntiles, E, C, base, counts, offsets);
   return hipGetLastError();
 }
 
@@ -286,7 +286,7 @@ hipError_t launch_permute_scan(const void* x, const int32_t* ids, const int32_t*
                                int32_t* offsets, int32_t* slot, int32_t* row_of,
                                int32_t* row_token, void* x_perm, hipStream_t s) {
   const int ntiles = static_cast<int>((T + kTileTokens - 1) / kTileTokens);
-  permute_scan_kernel<<<ntiles, 256, 0, s>>>(ids, hist, ntiles, T, k, E, C, counts, offsets, slot,
+  klaunch(permute_scan_kernel, ntiles, 256, 0, s, ids, hist, ntiles, T, k, E, C, counts, offsets, slot,
                                              row_of, row_token);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || x_perm == nullptr) return err;
@@ -298,7 +298,7 @@ hipError_t launch_permute(const void* x, const int32_t* ids, const int32_t* base
                           int row_bytes, int32_t* slot, int32_t* row_of, int32_t* row_token,
                           void* x_perm, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>((T + kTileTokens - 1) / kTileTokens);
-  permute_kernel<<<grid, 256, 0, s>>>(ids, base, offsets, T, k, E, C, slot, row_of, row_token);
+  klaunch(permute_kernel, grid, 256, 0, s, ids, base, offsets, T, k, E, C, slot, row_of, row_token);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || x_perm == nullptr) return err;
   return launch_gather_rows(x, row_token, offsets, E, T * k, row_bytes, x_perm, s);
@@ -311,10 +311,10 @@ hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int
   const int64_t n = max_rows * (row_bytes / vec);
   const unsigned grid = static_cast<unsigned>(n / 256 + 1 < 8192 ? n / 256 + 1 : 8192);
   if (vec == 16)
-    gather_rows_kernel<16><<<grid, 256, 0, s>>>(static_cast<const char*>(x), row_token, offsets, E,
+    klaunch(gather_rows_kernel<16>, grid, 256, 0, s, static_cast<const char*>(x), row_token, offsets, E,
                                                 row_bytes, static_cast<char*>(x_perm));
   else
-    gather_rows_kernel<4><<<grid, 256, 0, s>>>(static_cast<const char*>(x), row_token, offsets, E,
+    klaunch(gather_rows_kernel<4>, grid, 256, 0, s, static_cast<const char*>(x), row_token, offsets, E,
                                                row_bytes, static_cast<char*>(x_perm));
   return hipGetLastError();
 }

@@ -69,6 +69,12 @@ template <int TM>
 constexpr int stages_for() { return TM <= 2 ? 3 : 2; }  // wait_loads allows at most 3
 constexpr int kLdsBytes = 3 * (128 + BN) * ROWB;  // the largest of NST (BM + BN) rows
 constexpr int TN = 4;         // 32-feature MFMA tiles per wave
+// Output modes of the epilogue: bf16 (after the activation), fp32, or the
+// second expert GEMM's y_perm: bf16 when the launch runs whole tiles, fp32
+// partial sums (one buffer per K half) when it splits K.
+constexpr int kOutBf16 = kGemmOutBf16;
+constexpr int kOutF32 = kGemmOutF32;
+constexpr int kOutYperm = kGemmOutYperm;
 constexpr int WN = BN / 2;    // features per wave
 static_assert(kGemmBM == 256, "the taller of the two tile heights");
 
@@ -251,7 +257,7 @@ struct TileInfo {
 // Epilogue cost of an fp32 output tile in K-equivalents (its stores take
 // about as long as 512 more K per row of MFMA work); weighs a K split, which
 // doubles the stores, against the rounds it saves.
-constexpr int kEpiK = 512;
+[[maybe_unused]] constexpr int kEpiK = 512;
 
 constexpr int kGroupM = 4;  // M tiles per group of the tile order
 
@@ -396,11 +402,14 @@ __device__ __forceinline__ void tile_sources(const TileInfo& t, const uint16_t* 
 
 // Activation, conversion and stores of one wave's (32 TM) x 128 outputs (the
 // accumulators started at the bias). FULL: every row and feature of the tile
-// is in range (no per-lane checks).
-template <int TM, bool OUT_F32, int ACT, bool FULL>
+// is in range (no per-lane checks). split: the launch splits K (kOutYperm
+// then stores fp32 partial sums).
+template <int TM, int OUT, int ACT, bool FULL>
 __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], void* __restrict__ out,
-                                         const TileInfo& t, int N, int wm, int wn, int l5, int hi) {
+                                         const TileInfo& t, int N, int wm, int wn, int l5, int hi,
+                                         bool split) {
   constexpr int WM = 32 * TM;
+  const bool f32 = OUT == kOutF32 || (OUT == kOutYperm && split);
   const int fb = wn * WN + hi * 4;  // this lane's first feature in the tile
   const int nb = t.n0 + fb;
 #pragma unroll
@@ -418,7 +427,7 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], void* __
         const float v2 = activate<ACT>(acc[i][j][4 * q + 2]);
         const float v3 = activate<ACT>(acc[i][j][4 * q + 3]);
         const int64_t o = orow + i * 32 + q * 8;
-        if constexpr (OUT_F32) {
+        if (f32) {
           *reinterpret_cast<float4*>(static_cast<float*>(out) + o) = make_float4(v0, v1, v2, v3);
         } else {
           typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -441,7 +450,7 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], void* __
 // offsets, M the rows of C per expert); else expert-FFN tiles of nkl stages
 // each: ntiles output tiles, and total = ntiles (whole K) or 2 ntiles (two K
 // halves; the second half's partial sums go to out2, without bias).
-template <int TM, bool OUT_F32, int ACT, bool WG, bool WT = false>
+template <int TM, int OUT, int ACT, bool WG, bool WT = false>
 __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const int32_t* __restrict__ row_idx,
                                           const uint16_t* __restrict__ W, const float* __restrict__ bias,
                                           void* __restrict__ out, void* __restrict__ out2,
@@ -662,8 +671,9 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     // features 8q + 4*hi + {0..3} of each 32-feature tile i
     const bool full_tile = done.rv == BM && done.n0 + BN <= N;
     void* dst = done.part ? out2 : out;
-    if (full_tile) epilogue<TM, OUT_F32, ACT, true>(acc, dst, done, N, wm, wn, l5, hi);
-    else epilogue<TM, OUT_F32, ACT, false>(acc, dst, done, N, wm, wn, l5, hi);
+    const bool split = !WG && total != ntiles;
+    if (full_tile) epilogue<TM, OUT, ACT, true>(acc, dst, done, N, wm, wn, l5, hi, split);
+    else epilogue<TM, OUT, ACT, false>(acc, dst, done, N, wm, wn, l5, hi, split);
     if (next >= total) break;
     tile = next;
     par ^= 1;
@@ -676,15 +686,17 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
 // tall tiles), or 192, 128 or 64 rows (every expert holds fewer than 256
 // rows: decode batches, many experts). Two instantiations rather than one
 // kernel with all four: each keeps its own register allocation.
-// out2 (fp32 output without activation only, else null): with it, the
+// OUT: kOutBf16 (after ACT), kOutF32, or kOutYperm (no activation; bf16
+// unless split). out2 (kOutF32 or kOutYperm only, else null): with it, the
 // schedule may split K in two halves when that fills more of the chip (few
 // output tiles, long K); the first half (with bias) goes to out, the second
-// to out2, and the number of parts (1 or 2) to *nsplit (when not null), so
-// out = out + out2 holds the product only when *nsplit is 2.
+// to out2, both as fp32 partial sums, and the number of parts (1 or 2) to
+// *nsplit (when not null). With kOutYperm, out then holds bf16 results when
+// *nsplit is 1 and fp32 partial sums (out + out2 = the product) when it is 2.
 // WT: each W_e is stored [K, N] (K-major, as W^T of the usual [N, K]); the
 // weight stages are loaded row by row of K and read with transposing LDS
 // reads.
-template <bool OUT_F32, int ACT, bool SHORT, bool WT = false>
+template <int OUT, int ACT, bool SHORT, bool WT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ row_idx,
                               const uint16_t* __restrict__ W,
@@ -775,10 +787,10 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
     const int tile = xcd_tile(total);
     if (tile >= total) return;
     if (tall)
-      tile_loop<4, OUT_F32, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
+      tile_loop<4, OUT, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
                                         lds, s_tiles, s_bias, tile, total, ntiles, NT);
     else
-      tile_loop<3, OUT_F32, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
+      tile_loop<3, OUT, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
                                         lds, s_tiles, s_bias, tile, total, ntiles, NT);
   } else {
     // ---- the same with heights 192, 128 and 64, whole or split in K: the
@@ -833,13 +845,13 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
     const int tile = xcd_tile(total);
     if (tile >= total) return;
     if (sel == 0)
-      tile_loop<3, OUT_F32, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
+      tile_loop<3, OUT, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
                                         lds, s_tiles, s_bias, tile, total, ntiles, NT);
     else if (sel == 1)
-      tile_loop<2, OUT_F32, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
+      tile_loop<2, OUT, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
                                         lds, s_tiles, s_bias, tile, total, ntiles, NT);
     else
-      tile_loop<1, OUT_F32, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
+      tile_loop<1, OUT, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
                                         lds, s_tiles, s_bias, tile, total, ntiles, NT);
   }
 #endif
@@ -889,7 +901,7 @@ void grouped_wgrad_bf16_kernel(const uint16_t* __restrict__ At, const uint16_t* 
   const int b = blockIdx.x;
   const int tile = (Gd % 8 == 0) ? (b % 8) * (Gd / 8) + b / 8 : b;
   if (tile >= total) return;
-  tile_loop<4, true, kActNone, true>(At, nullptr, Bt, nullptr, C, nullptr, poff, E, N, 0, lda, 0, M,
+  tile_loop<4, kOutF32, kActNone, true>(At, nullptr, Bt, nullptr, C, nullptr, poff, E, N, 0, lda, 0, M,
                                      lds, s_tiles, s_bias, tile, total, total, NT);
 #endif
 }
@@ -913,19 +925,11 @@ int cu_count() {
 
 hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uint16_t* W,
                             const float* bias, void* out, float* out2, int32_t* nsplit,
-                            bool out_f32, int act, const int32_t* offsets, int E, int N, int K,
-                            int64_t max_rows, int max_rows_per_expert, hipStream_t s,
-                            hipEvent_t ev_start, hipEvent_t ev_stop) {
-  if (max_rows <= 0) {
-    // nothing to launch: the events still mark this (empty) kernel's place
-    for (hipEvent_t ev : {ev_start, ev_stop})
-      if (ev != nullptr) {
-        const hipError_t e = hipEventRecord(ev, s);
-        if (e != hipSuccess) return e;
-      }
-    return hipSuccess;
-  }
-  if (!out_f32 || act != kActNone) out2 = nullptr;  // a split needs a linear fp32 output
+                            int out_mode, int act, const int32_t* offsets, int E, int N, int K,
+                            int64_t max_rows, int max_rows_per_expert, hipStream_t s) {
+  if (max_rows <= 0) return hipSuccess;
+  // a split needs a linear output kept as fp32 partial sums
+  if (out_mode == kGemmOutBf16 || act != kActNone) out2 = nullptr;
   const int smax = (out2 != nullptr && (K / BK) % 2 == 0) ? 2 : 1;
   // short tiles when no expert can fill a 256-row tile
   const bool shorter = max_rows_per_expert < 256;
@@ -934,33 +938,21 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uin
   const int slots = cu_count();
   const int64_t tiles = mt_bound * ((N + BN - 1) / BN) * smax;
   const unsigned grid = static_cast<unsigned>(tiles < slots ? tiles : slots);
-  // with events, the dispatch records them at the kernel's start and end
-  // (hipExtLaunchKernelGGL); without, a plain launch (the extended launch
-  // measured several microseconds more launch gap per kernel)
-  const bool timed = ev_start != nullptr || ev_stop != nullptr;
-#define MOE_GEMM_ONE(OF, AC, SH)                                                                    \
-  do {                                                                                             \
-    if (timed)                                                                                     \
-      hipExtLaunchKernelGGL(grouped_gemm_bf16_kernel<OF, AC, SH>, dim3(grid), dim3(256), 0, s,      \
-                            ev_start, ev_stop, 0, A, row_idx, W, bias, out, static_cast<void*>(out2), \
-                            nsplit, offsets, E, N, K);                                              \
-    else                                                                                           \
-      grouped_gemm_bf16_kernel<OF, AC, SH><<<grid, 256, 0, s>>>(A, row_idx, W, bias, out, out2,    \
-                                                                nsplit, offsets, E, N, K);          \
+#define MOE_GEMM(OM, AC)                                                                              \
+  do {                                                                                               \
+    if (shorter)                                                                                     \
+      klaunch(grouped_gemm_bf16_kernel<OM, AC, true>, dim3(grid), dim3(256), 0, s, A, row_idx, W, bias, \
+              out, static_cast<void*>(out2), nsplit, offsets, E, N, K);                                \
+    else                                                                                             \
+      klaunch(grouped_gemm_bf16_kernel<OM, AC, false>, dim3(grid), dim3(256), 0, s, A, row_idx, W,     \
+              bias, out, static_cast<void*>(out2), nsplit, offsets, E, N, K);                          \
   } while (0)
-#define MOE_GEMM(OF, AC)            \
-  do {                              \
-    if (shorter)                    \
-      MOE_GEMM_ONE(OF, AC, true);   \
-    else                            \
-      MOE_GEMM_ONE(OF, AC, false);  \
-  } while (0)
-  if (out_f32) MOE_GEMM(true, kActNone);
-  else if (act == kActRelu) MOE_GEMM(false, kActRelu);
-  else if (act == kActGeluTanh) MOE_GEMM(false, kActGeluTanh);
-  else MOE_GEMM(false, kActNone);
+  if (out_mode == kGemmOutYperm) MOE_GEMM(kOutYperm, kActNone);
+  else if (out_mode == kGemmOutF32) MOE_GEMM(kOutF32, kActNone);
+  else if (act == kActRelu) MOE_GEMM(kOutBf16, kActRelu);
+  else if (act == kActGeluTanh) MOE_GEMM(kOutBf16, kActGeluTanh);
+  else MOE_GEMM(kOutBf16, kActNone);
 #undef MOE_GEMM
-#undef MOE_GEMM_ONE
   return hipGetLastError();
 }
 
@@ -974,10 +966,10 @@ hipError_t launch_gemm_bf16_wt(const uint16_t* A, const int32_t* row_idx, const 
   const int64_t tiles = mt_bound * ((N + BN - 1) / BN);
   const unsigned grid = static_cast<unsigned>(tiles < slots ? tiles : slots);
   if (shorter)
-    grouped_gemm_bf16_kernel<true, kActNone, true, true><<<grid, 256, 0, s>>>(
+    grouped_gemm_bf16_kernel<kOutF32, kActNone, true, true><<<grid, 256, 0, s>>>(
         A, row_idx, W, bias, out, nullptr, nullptr, offsets, E, N, K);
   else
-    grouped_gemm_bf16_kernel<true, kActNone, false, true><<<grid, 256, 0, s>>>(
+    grouped_gemm_bf16_kernel<kOutF32, kActNone, false, true><<<grid, 256, 0, s>>>(
         A, row_idx, W, bias, out, nullptr, nullptr, offsets, E, N, K);
   return hipGetLastError();
 }

@@ -86,7 +86,7 @@ hipError_t launch_gemm_f32(const float* A, const int32_t* row_idx, const float* 
                            int max_rows_per_expert, hipStream_t s) {
   if (max_rows_per_expert <= 0) return hipSuccess;
   dim3 grid((N + 63) / 64, (max_rows_per_expert + 63) / 64, E);
-  gemm_f32_kernel<<<grid, 256, 0, s>>>(A, row_idx, W, bias, out, offsets, N, K, act);
+  klaunch(gemm_f32_kernel, grid, 256, 0, s, A, row_idx, W, bias, out, offsets, N, K, act);
   return hipGetLastError();
 }
 

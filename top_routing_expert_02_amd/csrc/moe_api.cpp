@@ -8,6 +8,10 @@
 
 #include "moe_internal.h"
 
+namespace moe {
+thread_local StageEvents t_stage_events;
+}
+
 namespace {
 
 using namespace moe;
@@ -101,6 +105,8 @@ Layout layout_of(const moe_config& c) {
   L.row_token = take(R * 4);
   L.x_perm = take(layer_gathers(c) ? 0 : R * c.d * es);
   L.h = take(R * c.d_ff * es);
+  // y_perm in the layer's dtype; bf16 layers size it for fp32, which holds
+  // the first K half's partial sums when the second GEMM splits K
   L.y_perm = take(R * c.d * 4);
   // the second K half's partial sums of a split second GEMM (bf16 layers)
   L.y_perm2 = take(c.dtype == MOE_BF16 ? R * c.d * 4 : 0);
@@ -283,52 +289,54 @@ int32_t dispatch_general_stage(const moe_config& c, void* ws, const void* x, con
 }
 
 // A is x_perm (row_idx null) or x with row r of the problem at row_idx[r].
-// e0/e1 (nullable): events for the GEMM kernel's start and end (recorded by
-// the dispatch itself for bf16, around the launch for fp32)
 int32_t gemm1_stage(const moe_config& c, const void* A, const int32_t* row_idx,
                     const int32_t* offsets, const void* W1, const float* b1, void* h,
-                    hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
+                    hipStream_t s) {
   const int64_t R = max_rows_of(c);
   const int per_expert = static_cast<int>(c.T < c.capacity ? c.T : c.capacity);
-  if (c.dtype == MOE_BF16) {
+  if (c.dtype == MOE_BF16)
     MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(A), row_idx, static_cast<const uint16_t*>(W1), b1,
-                             h, nullptr, nullptr, false, c.act, offsets, c.E, c.d_ff, c.d, R, per_expert, s,
-                             e0, e1));
-  } else {
-    if (e0 != nullptr) MOE_HIP(hipEventRecord(e0, s));
+                             h, nullptr, nullptr, kGemmOutBf16, c.act, offsets, c.E, c.d_ff, c.d, R,
+                             per_expert, s));
+  else
     MOE_HIP(launch_gemm_f32(static_cast<const float*>(A), row_idx, static_cast<const float*>(W1), b1,
                             static_cast<float*>(h), c.act, offsets, c.E, c.d_ff, c.d, per_expert, s));
-    if (e1 != nullptr) MOE_HIP(hipEventRecord(e1, s));
-  }
   return MOE_OK;
 }
 
-// y_perm2/nsplit (nullable): let a bf16 GEMM split K (see launch_gemm_bf16)
+// y_perm in the layer's dtype. y_perm2/nsplit (nullable, bf16 only): let the
+// GEMM split K; y_perm and y_perm2 then hold fp32 partial sums and *nsplit
+// says so (see launch_gemm_bf16).
 int32_t gemm2_stage(const moe_config& c, const void* h, const int32_t* offsets, const void* W2,
-                    const float* b2, float* y_perm, float* y_perm2, int32_t* nsplit,
-                    hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
+                    const float* b2, void* y_perm, float* y_perm2, int32_t* nsplit, hipStream_t s) {
   const int64_t R = max_rows_of(c);
   const int per_expert = static_cast<int>(c.T < c.capacity ? c.T : c.capacity);
-  if (c.dtype == MOE_BF16) {
+  if (c.dtype == MOE_BF16)
     MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(h), nullptr, static_cast<const uint16_t*>(W2), b2,
-                             y_perm, y_perm2, nsplit, true, kActNone, offsets, c.E, c.d, c.d_ff, R, per_expert, s,
-                             e0, e1));
-  } else {
-    if (e0 != nullptr) MOE_HIP(hipEventRecord(e0, s));
-    MOE_HIP(launch_gemm_f32(static_cast<const float*>(h), nullptr, static_cast<const float*>(W2), b2, y_perm,
-                            kActNone, offsets, c.E, c.d, c.d_ff, per_expert, s));
-    if (e1 != nullptr) MOE_HIP(hipEventRecord(e1, s));
-  }
+                             y_perm, y_perm2, nsplit, kGemmOutYperm, kActNone, offsets, c.E, c.d, c.d_ff, R,
+                             per_expert, s));
+  else
+    MOE_HIP(launch_gemm_f32(static_cast<const float*>(h), nullptr, static_cast<const float*>(W2), b2,
+                            static_cast<float*>(y_perm), kActNone, offsets, c.E, c.d, c.d_ff, per_expert, s));
   return MOE_OK;
 }
 
-int32_t combine_stage(const moe_config& c, const float* y_perm, const float* y_perm2,
+// y_perm2/nsplit: as gemm2_stage wrote them (null for fp32 layers and for
+// a caller's y_perm)
+int32_t combine_stage(const moe_config& c, const void* y_perm, const float* y_perm2,
                       const int32_t* nsplit, const int32_t* row_of, const float* gates, void* y,
                       hipStream_t s) {
-  MOE_HIP(launch_combine(y_perm, y_perm2, nsplit, row_of, gates, c.T, c.k, c.d, c.dtype == MOE_BF16,
-                         y, s));
+  const bool bf = c.dtype == MOE_BF16;
+  MOE_HIP(launch_combine(y_perm, bf, bf ? y_perm2 : nullptr, bf ? nsplit : nullptr, row_of, gates, c.T,
+                         c.k, c.d, bf, y, s));
   return MOE_OK;
 }
+
+// Clears the stage kernel events of this thread when a layer call returns
+// (also on an early error return).
+struct StageEventsGuard {
+  ~StageEventsGuard() { t_stage_events = StageEvents{}; }
+};
 
 #define MOE_TRY(expr)              \
   do {                             \
@@ -451,7 +459,7 @@ int32_t moe_dispatch_reroute(const moe_config* cfg, const void* x, const int32_t
 
 int32_t moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
                        const void* W1, const float* b1, const void* W2, const float* b2, void* h,
-                       float* y_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+                       void* y_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
   MOE_TRY(check_cfg(cfg));
   const moe_config& c = *cfg;
   if (c.T == 0) return MOE_OK;
@@ -466,7 +474,7 @@ int32_t moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t*
   return gemm2_stage(c, h, expert_offsets, W2, b2, y_perm, nullptr, nullptr, stream);
 }
 
-int32_t moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* row_of,
+int32_t moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* row_of,
                     const float* topk_gates, void* y, hipStream_t stream) {
   MOE_TRY(check_cfg(cfg));
   const moe_config& c = *cfg;
@@ -481,7 +489,7 @@ int32_t moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* r
 int32_t moe_layer_forward(const moe_config* cfg, const void* x, const void* W_r,
                           const float* b_r, const void* W1, const float* b1, const void* W2,
                           const float* b2, void* y, const moe_route_info* info, void* ws,
-                          size_t ws_bytes, hipEvent_t* stage_events, hipEvent_t* gemm_events,
+                          size_t ws_bytes, hipEvent_t* stage_events, hipEvent_t* kernel_events,
                           hipStream_t stream) {
   MOE_TRY(check_cfg(cfg));
   const moe_config& c = *cfg;
@@ -496,15 +504,17 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* x, const void* W_r,
   if (!aligned(in.topk_ids, 4) || !aligned(in.topk_gates, 4) || !aligned(in.prob_sum, 4) ||
       !aligned(in.expert_counts, 4) || !aligned(in.expert_offsets, 4) || !aligned(in.slot, 4) ||
       !aligned(in.row_of, 4) || !aligned(in.row_token, 4) || !aligned(in.served_ids, 4) ||
-      !aligned(in.combine_gates, 4))
+      !aligned(in.combine_gates, 4) || !aligned(in.h, 16))
     return MOE_ERR_INVALID_ARG;
   if (stage_events != nullptr)
     for (int i = 0; i <= MOE_NUM_STAGES; ++i)
       if (stage_events[i] == nullptr) return MOE_ERR_INVALID_ARG;
-  if (gemm_events != nullptr)
-    for (int i = 0; i < 4; ++i)
-      if (gemm_events[i] == nullptr) return MOE_ERR_INVALID_ARG;
+  if (kernel_events != nullptr)
+    for (int i = 0; i < 2 * MOE_NUM_STAGES; ++i)
+      if (kernel_events[i] == nullptr) return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_ws(c, ws, ws_bytes));
+  // every argument is valid: nothing below returns an error before a HIP call
+  // has failed
 
   const Layout L = layout_of(c);
   int32_t* ids = in.topk_ids != nullptr ? in.topk_ids : at<int32_t>(ws, L.ids);
@@ -516,40 +526,75 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* x, const void* W_r,
   int32_t* row_token = in.row_token != nullptr ? in.row_token : at<int32_t>(ws, L.row_token);
   const bool gather = layer_gathers(c);
   void* x_perm = gather ? nullptr : at<char>(ws, L.x_perm);
-  void* h = at<char>(ws, L.h);
-  float* y_perm = at<float>(ws, L.y_perm);
+  void* h = in.h != nullptr ? in.h : at<char>(ws, L.h);
+  void* y_perm = at<char>(ws, L.y_perm);
+  const bool bf = c.dtype == MOE_BF16;
+  float* y_perm2 = bf ? at<float>(ws, L.y_perm2) : nullptr;
+  int32_t* nsplit = bf ? at<int32_t>(ws, L.nsplit) : nullptr;
   int32_t* hist = at<int32_t>(ws, L.hist);
   const bool gen = general_rule(c);
   float* cgates = gates;  // combine weights
   if (gen) cgates = in.combine_gates != nullptr ? in.combine_gates : at<float>(ws, L.cgates);
 
-  auto mark = [&](int i) -> int32_t {
-    if (stage_events != nullptr && hipEventRecord(stage_events[i], stream) != hipSuccess)
+  StageEventsGuard guard;
+  // stage st begins: its boundary event, and its kernels' start/end events
+  auto begin = [&](int st) -> int32_t {
+    if (stage_events != nullptr && hipEventRecord(stage_events[st], stream) != hipSuccess)
       return MOE_ERR_HIP;
+    if (kernel_events != nullptr) t_stage_events = StageEvents{kernel_events[2 * st], kernel_events[2 * st + 1]};
     return MOE_OK;
   };
-  MOE_TRY(mark(0));
+  // a stage that launched no kernel (no rows) marks its place on the stream
+  auto end = [&](int st) -> int32_t {
+    if (kernel_events != nullptr) {
+      const bool none = t_stage_events.start != nullptr;
+      t_stage_events = StageEvents{};
+      if (none && (hipEventRecord(kernel_events[2 * st], stream) != hipSuccess ||
+                   hipEventRecord(kernel_events[2 * st + 1], stream) != hipSuccess))
+        return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+  };
+  MOE_TRY(begin(MOE_STAGE_ROUTE));
   MOE_TRY(route_stage(c, x, W_r, b_r, ids, gates, in.prob_sum, at<float>(ws, L.logits),
                       at<float>(ws, L.prob_part), gen ? nullptr : hist, stream));
-  MOE_TRY(mark(1));
+  MOE_TRY(end(MOE_STAGE_ROUTE));
+  MOE_TRY(begin(MOE_STAGE_DISPATCH));
   if (gen)
     MOE_TRY(dispatch_general_stage(c, ws, x, ids, gates, counts, offsets, slot, row_of, row_token,
                                    in.served_ids, cgates, x_perm, stream));
   else
     MOE_TRY(dispatch_stage(c, x, ids, true, hist, at<int32_t>(ws, L.base), counts, offsets, slot,
                            row_of, row_token, x_perm, stream));
-  MOE_TRY(mark(2));
-  hipEvent_t* ge = gemm_events;
-  MOE_TRY(gemm1_stage(c, gather ? x : x_perm, gather ? row_token : nullptr, offsets, W1, b1, h,
-                      stream, ge ? ge[0] : nullptr, ge ? ge[1] : nullptr));
-  MOE_TRY(mark(3));
-  float* y_perm2 = at<float>(ws, L.y_perm2);
-  int32_t* nsplit = at<int32_t>(ws, L.nsplit);
-  MOE_TRY(gemm2_stage(c, h, offsets, W2, b2, y_perm, y_perm2, nsplit, stream, ge ? ge[2] : nullptr,
-                      ge ? ge[3] : nullptr));
-  MOE_TRY(mark(4));
+  MOE_TRY(end(MOE_STAGE_DISPATCH));
+  MOE_TRY(begin(MOE_STAGE_GEMM1));
+  MOE_TRY(gemm1_stage(c, gather ? x : x_perm, gather ? row_token : nullptr, offsets, W1, b1, h, stream));
+  MOE_TRY(end(MOE_STAGE_GEMM1));
+  MOE_TRY(begin(MOE_STAGE_GEMM2));
+  MOE_TRY(gemm2_stage(c, h, offsets, W2, b2, y_perm, y_perm2, nsplit, stream));
+  MOE_TRY(end(MOE_STAGE_GEMM2));
+  MOE_TRY(begin(MOE_STAGE_COMBINE));
   MOE_TRY(combine_stage(c, y_perm, y_perm2, nsplit, row_of, cgates, y, stream));
-  return mark(5);
+  MOE_TRY(end(MOE_STAGE_COMBINE));
+  if (stage_events != nullptr && hipEventRecord(stage_events[MOE_NUM_STAGES], stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+int32_t moe_load_stats(const moe_config* cfg, const int32_t* expert_counts,
+                       const int32_t* expert_offsets, const float* prob_sum, double aux_alpha,
+                       int32_t* kept, int32_t* dropped, double* stats, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_config& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  if (expert_counts == nullptr || expert_offsets == nullptr || stats == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(aux_alpha) || !aligned(expert_counts, 4) || !aligned(expert_offsets, 4) ||
+      !aligned(prob_sum, 4) || !aligned(kept, 4) || !aligned(dropped, 4) || !aligned(stats, 8))
+    return MOE_ERR_INVALID_ARG;
+  MOE_HIP(launch_load_stats(expert_counts, expert_offsets, prob_sum, c.E, c.capacity, c.T, c.k, aux_alpha, kept,
+                            dropped, stats, stream));
+  return MOE_OK;
 }
 
 int32_t moe_backward_workspace_size(const moe_config* cfg, size_t* bytes) {
@@ -648,7 +693,8 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* x, const void* W_r
   // u = x W1_e^T + b1_e (pre-activation, fp32); Z = dy W2_e (fp32)
   if (bf) {
     MOE_HIP(launch_gemm_bf16(static_cast<const uint16_t*>(xa), ridx, static_cast<const uint16_t*>(W1), b1,
-                             u, nullptr, nullptr, true, kActNone, offsets, c.E, c.d_ff, c.d, R, per_expert, s));
+                             u, nullptr, nullptr, kGemmOutF32, kActNone, offsets, c.E, c.d_ff, c.d, R,
+                             per_expert, s));
     MOE_HIP(launch_gemm_bf16_wt(static_cast<const uint16_t*>(dya), ridx, static_cast<const uint16_t*>(W2),
                                 nullptr, Z, offsets, c.E, c.d_ff, c.d, R, per_expert, s));
   } else {

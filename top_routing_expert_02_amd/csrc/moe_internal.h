@@ -2,10 +2,37 @@
 // libmoe.so. Not part of the public ABI (that is include/moe.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace moe {
+
+// ---------------------------------------------------------------- kernel timing
+// Optional per-stage kernel timing of the layer forward. While a stage runs
+// with events set, its first kernel dispatch records `start` when the kernel
+// begins and every dispatch records `stop` when its kernel ends (the last
+// one is what remains), so stop - start spans the stage's kernels without
+// the launch gap in front of the first one. Plain launches otherwise (the
+// extended launch adds a few microseconds of launch gap per kernel).
+struct StageEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+extern thread_local StageEvents t_stage_events;
+
+template <typename... KArgs, typename... Args>
+inline void klaunch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s,
+                    Args... args) {
+  StageEvents& ev = t_stage_events;
+  if (ev.start == nullptr && ev.stop == nullptr) {
+    kernel<<<grid, block, shmem, s>>>(static_cast<KArgs>(args)...);
+  } else {
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, ev.start, ev.stop, 0u,
+                          static_cast<KArgs>(args)...);
+    ev.start = nullptr;
+  }
+}
 
 // Tokens per dispatch tile: the unit of the per-tile expert histograms and of
 // the permutation kernel (one 64-bit lane mask per expert and tile).
@@ -173,17 +200,21 @@ hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int
 
 // grouped expert GEMMs
 //   gemm1: h = act(A W1_e^T + b1_e)   A [rows,K=d], W1 [E,N=d_ff,K], h [rows,N]
-//   gemm2: y = A W2_e^T + b2_e        A [rows,K=d_ff], W2 [E,N=d,K], y fp32 [rows,N]
+//   gemm2: y = A W2_e^T + b2_e        A [rows,K=d_ff], W2 [E,N=d,K], y [rows,N]
 // row_idx (nullable): row r of the grouped problem is row row_idx[r] of A.
-// out2 (nullable; used for a linear fp32 output only): a second [rows,N]
-// buffer that lets the kernel split K in two; it then writes the partial sum
-// of the second half there and 2 to *nsplit (1 when it did not split), so the
-// result is out + out2 when *nsplit == 2.
+// out_mode: kGemmOutBf16 (bf16 after act), kGemmOutF32 (fp32, no act), or
+// kGemmOutYperm (no act; bf16 when the launch runs whole tiles).
+// out2 (nullable; fp32 and y_perm modes only): a second fp32 [rows,N]
+// buffer that lets the kernel split K in two; it then writes fp32 partial
+// sums of the two halves to out and out2 and 2 to *nsplit (1 when it did
+// not split), so the result is out + out2 when *nsplit == 2.
+constexpr int kGemmOutBf16 = 0;
+constexpr int kGemmOutF32 = 1;
+constexpr int kGemmOutYperm = 2;
 hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uint16_t* W,
                             const float* bias, void* out, float* out2, int32_t* nsplit,
-                            bool out_f32, int act, const int32_t* offsets, int E, int N, int K,
-                            int64_t max_rows, int max_rows_per_expert, hipStream_t s,
-                            hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+                            int out_mode, int act, const int32_t* offsets, int E, int N, int K,
+                            int64_t max_rows, int max_rows_per_expert, hipStream_t s);
 // The same product with each W_e stored [K, N] (the transposed layout, so
 // that out = A W_e with W_e as given): fp32 out, no activation, no K split.
 // N and K are multiples of 64.
@@ -196,11 +227,28 @@ hipError_t launch_gemm_f32(const float* A, const int32_t* row_idx, const float* 
                            int max_rows_per_expert, hipStream_t s);
 
 // y[t] = sum_j gates[t,j] y_perm[row_of[t,j]] (kept j only), rounded once;
-// with y_perm2 (nullable) and *nsplit == 2 the rows are y_perm + y_perm2
-// (a K-split second GEMM's two partial sums, added first)
-hipError_t launch_combine(const float* y_perm, const float* y_perm2, const int32_t* nsplit,
-                          const int32_t* row_of, const float* gates, int64_t T, int k, int d,
-                          bool out_bf16, void* y, hipStream_t s);
+// y_perm rows are bf16 (yperm_bf16) or fp32; with y_perm2 (nullable) and
+// *nsplit == 2 they are instead the fp32 sums y_perm + y_perm2 (a K-split
+// second GEMM's two partial sums, added first)
+hipError_t launch_combine(const void* y_perm, bool yperm_bf16, const float* y_perm2,
+                          const int32_t* nsplit, const int32_t* row_of, const float* gates,
+                          int64_t T, int k, int d, bool out_bf16, void* y, hipStream_t s);
+
+// load statistics of one routing step (one block): kept [E] = rows per
+// expert from offsets, dropped [E] = max(count - kept, 0) (both nullable);
+// stats [kNumStats] fp64 in the order below (same values as MOE_STAT_*)
+constexpr int kStatDropped = 0;
+constexpr int kStatOverflowRatio = 1;
+constexpr int kStatMaxOverMean = 2;
+constexpr int kStatPaddingRatio = 3;
+constexpr int kStatLoadEntropy = 4;
+constexpr int kStatKeptVariance = 5;
+constexpr int kStatAuxLoss = 6;
+constexpr int kStatKeptRows = 7;
+constexpr int kNumStats = 8;
+hipError_t launch_load_stats(const int32_t* counts, const int32_t* offsets, const float* prob_sum, int E,
+                             int C, int64_t T, int k, double alpha, int32_t* kept, int32_t* dropped,
+                             double* stats, hipStream_t s);
 
 // activation codes (same values as MOE_ACT_*)
 constexpr int kActRelu = 0;

@@ -244,21 +244,21 @@ hipError_t launch_dispatch_reroute(const void* x, const int32_t* cand, const flo
   const int64_t Q = T * k;
   const int64_t ntiles = reroute_tiles(T, k);
   const Order o{T, k, rank_priority};
-  rr_init_kernel<<<blocks_of(T > E ? T : E, 256), 256, 0, s>>>(T, k, E, ws.col, ws.served,
+  klaunch(rr_init_kernel, blocks_of(T > E ? T : E, 256), 256, 0, s, T, k, E, ws.col, ws.served,
                                                                 ws.next_col, ws.fill);
   for (int j = 0; j <= rounds; ++j) {
     if (j > 0)
-      rr_advance_kernel<<<blocks_of(T, 256), 256, 0, s>>>(T, k, n, ws.col, ws.served, ws.next_col);
-    rr_hist_kernel<<<static_cast<unsigned>(ntiles), kRrTile, 0, s>>>(o, Q, cand, n, E, ws.col,
+      klaunch(rr_advance_kernel, blocks_of(T, 256), 256, 0, s, T, k, n, ws.col, ws.served, ws.next_col);
+    klaunch(rr_hist_kernel, static_cast<unsigned>(ntiles), kRrTile, 0, s, o, Q, cand, n, E, ws.col,
                                                                      ws.served, ws.hist);
-    rr_scan_kernel<<<1, 1024, 0, s>>>(ws.hist, static_cast<int>(ntiles), E, C, j, ws.base, ws.fill,
+    klaunch(rr_scan_kernel, 1, 1024, 0, s, ws.hist, static_cast<int>(ntiles), E, C, j, ws.base, ws.fill,
                                       ws.fill0, counts);
-    rr_place_kernel<<<static_cast<unsigned>(ntiles), kRrTile, 0, s>>>(o, Q, cand, n, E, C, ws.col,
+    klaunch(rr_place_kernel, static_cast<unsigned>(ntiles), kRrTile, 0, s, o, Q, cand, n, E, C, ws.col,
                                                                       ws.served, ws.base, ws.fill0,
                                                                       slot);
   }
-  rr_offsets_kernel<<<1, 1024, 0, s>>>(ws.fill, E, offsets);
-  rr_finalize_kernel<<<blocks_of(Q, 256), 256, 0, s>>>(T, k, n, cand, cand_gates, ws.served, slot,
+  klaunch(rr_offsets_kernel, 1, 1024, 0, s, ws.fill, E, offsets);
+  klaunch(rr_finalize_kernel, blocks_of(Q, 256), 256, 0, s, T, k, n, cand, cand_gates, ws.served, slot,
                                                         offsets, row_of, row_token, served_ids,
                                                         combine_gates);
   hipError_t err = hipGetLastError();

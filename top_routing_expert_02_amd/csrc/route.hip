@@ -406,26 +406,26 @@ hipError_t launch_logits_bf16(const uint16_t* x, const uint16_t* Wr, const float
   // loads in flight per wave
   if (E <= 16) {
     dim3 grid(static_cast<unsigned>((T + 15) / 16), 1);
-    logits_bf16_kernel<1, 1, 4><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E, zero, nzero);
+    klaunch(logits_bf16_kernel<1, 1, 4>, grid, 256, 0, s, x, Wr, br, logits, T, d, E, zero, nzero);
   } else if (E <= 32) {
     dim3 grid(static_cast<unsigned>((T + 15) / 16), 1);
-    logits_bf16_kernel<1, 2, 4><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E, zero, nzero);
+    klaunch(logits_bf16_kernel<1, 2, 4>, grid, 256, 0, s, x, Wr, br, logits, T, d, E, zero, nzero);
   } else if (E <= 64 && T >= 32 * 256) {
     dim3 grid(static_cast<unsigned>((T + 31) / 32), 1);
-    logits_bf16_kernel<2, 4, 3><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E, zero, nzero);
+    klaunch(logits_bf16_kernel<2, 4, 3>, grid, 256, 0, s, x, Wr, br, logits, T, d, E, zero, nzero);
   } else if (E <= 64) {
     dim3 grid(static_cast<unsigned>((T + 15) / 16), 1);
-    logits_bf16_kernel<1, 4, 4><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E, zero, nzero);
+    klaunch(logits_bf16_kernel<1, 4, 4>, grid, 256, 0, s, x, Wr, br, logits, T, d, E, zero, nzero);
   } else {
     dim3 grid(static_cast<unsigned>((T + 63) / 64), static_cast<unsigned>((E + 63) / 64));
-    logits_bf16_kernel<4, 4, 3><<<grid, 256, 0, s>>>(x, Wr, br, logits, T, d, E, zero, nzero);
+    klaunch(logits_bf16_kernel<4, 4, 3>, grid, 256, 0, s, x, Wr, br, logits, T, d, E, zero, nzero);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_logits_f32(const float* x, const float* Wr, const float* br, float* logits,
                              int64_t T, int d, int E, hipStream_t s) {
-  logits_f32_kernel<<<static_cast<unsigned>((T + 3) / 4), 256, 0, s>>>(x, Wr, br, logits, T, d, E);
+  klaunch(logits_f32_kernel, static_cast<unsigned>((T + 3) / 4), 256, 0, s, x, Wr, br, logits, T, d, E);
   return hipGetLastError();
 }
 
@@ -437,11 +437,11 @@ hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int nsel, i
 #define MOE_TOPK(G, NV)                                                                           \
   do {                                                                                            \
     if (tb == 64)                                                                                 \
-      topk_kernel<G, NV, (G >= 16 ? 16 : G), 64><<<grid, 64 * (G >= 16 ? 16 : G), 0, s>>>(         \
-          logits, T, E, k, nsel, renormalize, ids, gates, prob_part, hist);                        \
+      klaunch(topk_kernel<G, NV, (G >= 16 ? 16 : G), 64>, grid, 64 * (G >= 16 ? 16 : G), 0, s,    \
+              logits, T, E, k, nsel, renormalize, ids, gates, prob_part, hist);                   \
     else                                                                                          \
-      topk_kernel<G, NV, G / 4, 16><<<grid, 16 * G, 0, s>>>(logits, T, E, k, nsel, renormalize, ids, \
-                                                           gates, prob_part, hist);               \
+      klaunch(topk_kernel<G, NV, G / 4, 16>, grid, 16 * G, 0, s, logits, T, E, k, nsel,          \
+              renormalize, ids, gates, prob_part, hist);                                          \
   } while (0)
   // groups of at least 16 lanes (k <= 16 results per token) holding up to 16
   // logits per lane: a wave runs 4 tokens' shuffle chains side by side, and
@@ -460,7 +460,7 @@ hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int nsel, i
 }
 
 hipError_t launch_prob_reduce(const float* part, int ntiles, int E, float* out, hipStream_t s) {
-  prob_reduce_kernel<<<(E + 255) / 256, 256, 0, s>>>(part, ntiles, E, out);
+  klaunch(prob_reduce_kernel, (E + 255) / 256, 256, 0, s, part, ntiles, E, out);
   return hipGetLastError();
 }
 

@@ -26,8 +26,10 @@ STAGE_NAMES = ["route", "dispatch", "gemm1", "gemm2", "combine"]
 
 EXPORTED = ["moe_capacity", "moe_candidates", "moe_max_rows", "moe_workspace_size", "moe_route",
             "moe_dispatch", "moe_dispatch_reroute", "moe_expert_ffn", "moe_combine",
-            "moe_layer_forward", "moe_backward_workspace_size", "moe_layer_backward",
-            "moe_status_string"]
+            "moe_layer_forward", "moe_load_stats", "moe_backward_workspace_size",
+            "moe_layer_backward", "moe_status_string"]
+STAT_NAMES = ["dropped", "overflow_ratio", "max_over_mean_load", "padding_ratio", "load_entropy",
+              "kept_variance", "aux_loss", "kept_rows"]
 
 
 class MoeError(RuntimeError):
@@ -47,7 +49,7 @@ class MoeConfig(ctypes.Structure):
 class MoeRouteInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("topk_ids", "topk_gates", "prob_sum", "expert_counts", "expert_offsets", "slot",
-                 "row_of", "row_token", "served_ids", "combine_gates")]
+                 "row_of", "row_token", "served_ids", "combine_gates", "h")]
 
 
 _lib = None
@@ -74,6 +76,7 @@ def lib():
         L.moe_combine.argtypes = [CFG, P, P, P, P, P]
         L.moe_layer_forward.argtypes = [CFG, P, P, P, P, P, P, P, P, ctypes.POINTER(MoeRouteInfo),
                                         P, SZ, P, P, P]
+        L.moe_load_stats.argtypes = [CFG, P, P, P, ctypes.c_double, P, P, P, P]
         L.moe_backward_workspace_size.argtypes = [CFG, ctypes.POINTER(SZ)]
         L.moe_layer_backward.argtypes = [CFG, P, P, P, P, P, P, P, ctypes.POINTER(MoeRouteInfo), P,
                                          ctypes.c_float, P, P, P, P, P, P, P, P, SZ, P, P]
@@ -187,21 +190,29 @@ def combine(cfg, y_perm, row_of, topk_gates, y, stream=None):
 
 
 def layer_forward(cfg, x, W_r, b_r, W1, b1, W2, b2, y, info: dict | None = None, ws=None,
-                  stage_events=None, gemm_events=None, stream=None):
+                  stage_events=None, kernel_events=None, stream=None):
     """info: optional dict of output tensors keyed like moe_route_info's fields.
     stage_events: optional HipEvents with MOE_NUM_STAGES + 1 events.
-    gemm_events: optional HipEvents with 4 events (start and end of each
-    expert GEMM kernel)."""
+    kernel_events: optional HipEvents with 2 * MOE_NUM_STAGES events (start of
+    each stage's first kernel, end of its last)."""
     ws = alloc_workspace(cfg, x.device) if ws is None else ws
     ri = None
     if info:
         ri = MoeRouteInfo(**{k: _ptr(v) for k, v in info.items()})
     ev = stage_events.array if stage_events is not None else None
-    gev = gemm_events.array if gemm_events is not None else None
+    gev = kernel_events.array if kernel_events is not None else None
     _check("moe_layer_forward", lib().moe_layer_forward(
         ctypes.byref(cfg), _ptr(x), _ptr(W_r), _ptr(b_r), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
         _ptr(y), ctypes.byref(ri) if ri is not None else None, _ptr(ws), ws.numel(), ev, gev,
         _stream(stream)))
+
+
+def load_stats(cfg, expert_counts, expert_offsets, prob_sum, aux_alpha, stats, kept=None,
+               dropped=None, stream=None):
+    """stats: a float64 tensor of len(STAT_NAMES) (filled on the device)."""
+    _check("moe_load_stats", lib().moe_load_stats(
+        ctypes.byref(cfg), _ptr(expert_counts), _ptr(expert_offsets), _ptr(prob_sum),
+        float(aux_alpha), _ptr(kept), _ptr(dropped), _ptr(stats), _stream(stream)))
 
 
 def backward_workspace_size(cfg: MoeConfig) -> int:
