@@ -295,6 +295,38 @@ def main_backward(args):
     print(json.dumps(out), flush=True)
 
 
+def dispatch_leg(w, cfg, inp, ws, n, timed):
+    """n calls of moe_dispatch with the permuted copy of x (plain rule only),
+    timed with `timed` when given."""
+    import torch
+    from top_routing_expert_02_amd import moe
+    if w.priority != "token" or w.reroute > 0:
+        return None
+    dev = inp["x"].device
+    i32 = dict(dtype=torch.int32, device=dev)
+    R = moe.max_rows(cfg)
+    ids = torch.empty((w.T, w.k), **i32)
+    gts = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+    moe.route(cfg, inp["x"], inp["W_r"], inp["b_r"], ids, gts, ws=ws)
+    counts, offs = torch.empty(w.E, **i32), torch.empty(w.E + 1, **i32)
+    slot, rof = torch.empty((w.T, w.k), **i32), torch.empty((w.T, w.k), **i32)
+    rt = torch.empty(max(R, 1), **i32)
+    x_perm = torch.empty((max(R, 1), w.d), dtype=w.torch_dtype, device=dev)
+
+    def dstep():
+        moe.dispatch(cfg, inp["x"], ids, counts, offs, slot, rof, rt, x_perm, ws=ws)
+
+    if timed is None:
+        for _ in range(n):
+            dstep()
+        torch.cuda.synchronize()
+        return None
+    for _ in range(2):
+        dstep()
+    return {"ms": timed(dstep, n),
+            "timing": "back-to-back moe_dispatch calls between two events (two kernels each)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -355,6 +387,11 @@ def main():
     eager_ms = timed(step)
     log(f"[bench] {K} steps: {eager_ms:.4f} ms/step")
     if args.only_timed:
+        # profiler runs: the timed steps, a few stand-alone dispatch calls
+        # and the copy probe, nothing else
+        dispatch_leg(w, cfg, inp, ws, 3, None)
+        if args.copy_probe_mib > 0:
+            copy_probe(args.copy_probe_mib)
         print(json.dumps({"metric": METRIC, "value": w.T / (eager_ms * 1e-3), "unit": "tokens/s",
                           "ms_per_step": eager_ms, "config": {"workload": w.name},
                           "note": "profiler run: timed steps only"}), flush=True)
@@ -419,28 +456,12 @@ def main():
 
     # the stand-alone dispatch entry point with the permuted copy of x
     # (the layer path gathers token rows inside its first GEMM instead)
-    disp = None
-    if not (w.priority != "token" or w.reroute > 0):
-        ids = torch.empty((w.T, w.k), **i32)
-        gts = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
-        moe.route(cfg, inp["x"], inp["W_r"], inp["b_r"], ids, gts, ws=ws)
-        o_counts, o_offs = torch.empty(w.E, **i32), torch.empty(w.E + 1, **i32)
-        o_slot, o_rof = torch.empty((w.T, w.k), **i32), torch.empty((w.T, w.k), **i32)
-        o_rt = torch.empty(max(R, 1), **i32)
-        x_perm = torch.empty((max(R, 1), w.d), dtype=w.torch_dtype, device=dev)
-
-        def dstep():
-            moe.dispatch(cfg, inp["x"], ids, o_counts, o_offs, o_slot, o_rof, o_rt, x_perm, ws=ws)
-
-        for _ in range(2):
-            dstep()
-        d_ms = timed(dstep)
+    disp = dispatch_leg(w, cfg, inp, ws, K, timed)
+    if disp is not None:
         nb = work["dispatch_x_perm"]["bytes"]
-        disp = {"ms": d_ms, "bytes": nb, "GB_s": nb / (d_ms * 1e-3) / 1e9,
-                "hbm_frac": nb / (d_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                "timing": "back-to-back moe_dispatch calls between two events (two kernels each)"}
-        del x_perm
-        log(f"[bench] stand-alone dispatch with x_perm: {d_ms:.4f} ms")
+        disp.update({"bytes": nb, "GB_s": nb / (disp["ms"] * 1e-3) / 1e9,
+                     "hbm_frac": nb / (disp["ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS})
+        log(f"[bench] stand-alone dispatch with x_perm: {disp['ms']:.4f} ms")
 
     # load statistics of the step, computed on the device
     stats_t = torch.empty(len(moe.STAT_NAMES), dtype=torch.float64, device=dev)

@@ -20,13 +20,18 @@ __device__ __forceinline__ void load_row(const void* __restrict__ yp, const floa
                                          int mode, int64_t ro, float (&q)[VEC]) {
   if (mode == 1) {  // bf16 rows
     const uint16_t* src = static_cast<const uint16_t*>(yp) + ro;
-    if constexpr (VEC == 8) {
-      const uint4 u = *reinterpret_cast<const uint4*>(src);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    if constexpr (VEC % 8 == 0) {
+      uint4 u[VEC / 8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        q[2 * i] = __uint_as_float(w[i] << 16);
-        q[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      for (int h = 0; h < VEC / 8; ++h) u[h] = reinterpret_cast<const uint4*>(src)[h];
+#pragma unroll
+      for (int h = 0; h < VEC / 8; ++h) {
+        const uint32_t w[4] = {u[h].x, u[h].y, u[h].z, u[h].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          q[8 * h + 2 * i] = __uint_as_float(w[i] << 16);
+          q[8 * h + 2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
       }
     } else {
 #pragma unroll
@@ -84,13 +89,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     for (int v = 0; v < VEC; ++v) acc[v] = fmaf(g, q[v], acc[v]);
   }
   if constexpr (BF16) {
-    static_assert(VEC == 8, "bf16 output uses 8 columns per thread");
-    uint4 o;
-    o.x = f32_to_bf16(acc[0]) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
-    o.y = f32_to_bf16(acc[2]) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
-    o.z = f32_to_bf16(acc[4]) | (static_cast<uint32_t>(f32_to_bf16(acc[5])) << 16);
-    o.w = f32_to_bf16(acc[6]) | (static_cast<uint32_t>(f32_to_bf16(acc[7])) << 16);
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + t * d + c) = o;
+    static_assert(VEC % 8 == 0, "bf16 output stores 16-byte groups of 8 columns");
+#pragma unroll
+    for (int h = 0; h < VEC / 8; ++h) {
+      const float* a = acc + 8 * h;
+      uint4 o;
+      o.x = f32_to_bf16(a[0]) | (static_cast<uint32_t>(f32_to_bf16(a[1])) << 16);
+      o.y = f32_to_bf16(a[2]) | (static_cast<uint32_t>(f32_to_bf16(a[3])) << 16);
+      o.z = f32_to_bf16(a[4]) | (static_cast<uint32_t>(f32_to_bf16(a[5])) << 16);
+      o.w = f32_to_bf16(a[6]) | (static_cast<uint32_t>(f32_to_bf16(a[7])) << 16);
+      reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + t * d + c)[h] = o;
+    }
   } else {
     float* dst = static_cast<float*>(y) + t * d + c;
 #pragma unroll
@@ -104,8 +113,10 @@ hipError_t launch_combine(const void* y_perm, bool yperm_bf16, const float* y_pe
   if (nsplit == nullptr) y_perm2 = nullptr;
   const int rb = yperm_bf16 ? 1 : 0;
   if (out_bf16) {
-    const int64_t n = T * (d / 8);
-    klaunch(combine_kernel<8, true>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+    // d is a multiple of 64: 16 columns per thread, two 16-byte loads per
+    // row and k rows in flight
+    const int64_t n = T * (d / 16);
+    klaunch(combine_kernel<16, true>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
             y_perm, rb, y_perm2, nsplit, row_of, gates, T, k, d, y);
   } else if (d % 4 == 0) {
     const int64_t n = T * (d / 4);

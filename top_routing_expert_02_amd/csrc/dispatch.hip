@@ -19,6 +19,8 @@
 // the histograms it needs itself), which saves a launch.
 #include "moe_internal.h"
 
+#include <type_traits>
+
 namespace moe {
 
 __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ ids, int64_t T,
@@ -244,24 +246,76 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(
   }
 }
 
-// x_perm[r] = x[row_token[r]] for every kept row, VEC bytes per thread, rows
-// read from offsets[E] on the device.
+// x_perm[r] = x[row_token[r]] for every kept row (rows read from offsets[E]
+// on the device). One wave copies one row at a time, VEC bytes per lane and
+// up to four loads in flight per lane before their stores.
 template <int VEC>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict__ x,
                                                           const int32_t* __restrict__ row_token,
                                                           const int32_t* __restrict__ offsets, int E,
                                                           int row_bytes, char* __restrict__ x_perm) {
+  typedef typename std::conditional<VEC == 16, uint4, uint32_t>::type V;
   const int64_t rows = offsets[E];
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * 4 + (threadIdx.x >> 6));
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * 4;
   const int chunks = row_bytes / VEC;
-  const int64_t n = rows * chunks;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t r = i / chunks;
-    const int c = static_cast<int>(i - r * chunks) * VEC;
-    const char* src = x + static_cast<int64_t>(row_token[r]) * row_bytes + c;
-    char* dst = x_perm + r * row_bytes + c;
-    if constexpr (VEC == 16) *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-    else *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
+  for (int64_t r = wave; r < rows; r += nwaves) {
+    const V* src = reinterpret_cast<const V*>(x + static_cast<int64_t>(row_token[r]) * row_bytes);
+    V* dst = reinterpret_cast<V*>(x_perm + r * row_bytes);
+    int c = lane;
+    for (; c + 192 < chunks; c += 256) {
+      const V a = src[c], b = src[c + 64], d = src[c + 128], e = src[c + 192];
+      dst[c] = a;
+      dst[c + 64] = b;
+      dst[c + 128] = d;
+      dst[c + 192] = e;
+    }
+    for (; c < chunks; c += 64) dst[c] = src[c];
+  }
+}
+
+// The same copy token by token: x_perm[row_of[t,j]] = x[t] for every kept
+// assignment (t, j). One wave per token reads its row once, up to four
+// VEC-byte loads in flight per lane, and writes it to each of its kept rows
+// (a token kept by k experts is read once, not k times).
+template <int VEC>
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const char* __restrict__ x,
+                                                           const int32_t* __restrict__ row_of,
+                                                           int64_t T, int k, int row_bytes,
+                                                           char* __restrict__ x_perm) {
+  typedef typename std::conditional<VEC == 16, uint4, uint32_t>::type V;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * 4 + (threadIdx.x >> 6));
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * 4;
+  const int chunks = row_bytes / VEC;
+  for (int64_t t = wave; t < T; t += nwaves) {
+    // this token's kept rows (wave-uniform loads)
+    const int32_t* ro = row_of + t * k;
+    bool any = false;
+    for (int j = 0; j < k; ++j) any |= ro[j] >= 0;
+    if (!any) continue;
+    const V* src = reinterpret_cast<const V*>(x + t * row_bytes);
+    int c = lane;
+    for (; c + 192 < chunks; c += 256) {
+      const V a = src[c], b = src[c + 64], d = src[c + 128], e = src[c + 192];
+      for (int j = 0; j < k; ++j) {
+        const int r = ro[j];
+        if (r < 0) continue;
+        V* dst = reinterpret_cast<V*>(x_perm + static_cast<int64_t>(r) * row_bytes);
+        dst[c] = a;
+        dst[c + 64] = b;
+        dst[c + 128] = d;
+        dst[c + 192] = e;
+      }
+    }
+    for (; c < chunks; c += 64) {
+      const V a = src[c];
+      for (int j = 0; j < k; ++j) {
+        const int r = ro[j];
+        if (r >= 0) reinterpret_cast<V*>(x_perm + static_cast<int64_t>(r) * row_bytes)[c] = a;
+      }
+    }
   }
 }
 
@@ -290,7 +344,7 @@ hipError_t launch_permute_scan(const void* x, const int32_t* ids, const int32_t*
                                              row_of, row_token);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || x_perm == nullptr) return err;
-  return launch_gather_rows(x, row_token, offsets, E, T * k, row_bytes, x_perm, s);
+  return launch_scatter_rows(x, row_of, T, k, row_bytes, x_perm, s);
 }
 
 hipError_t launch_permute(const void* x, const int32_t* ids, const int32_t* base,
@@ -301,21 +355,36 @@ hipError_t launch_permute(const void* x, const int32_t* ids, const int32_t* base
   klaunch(permute_kernel, grid, 256, 0, s, ids, base, offsets, T, k, E, C, slot, row_of, row_token);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || x_perm == nullptr) return err;
-  return launch_gather_rows(x, row_token, offsets, E, T * k, row_bytes, x_perm, s);
+  return launch_scatter_rows(x, row_of, T, k, row_bytes, x_perm, s);
+}
+
+hipError_t launch_scatter_rows(const void* x, const int32_t* row_of, int64_t T, int k, int row_bytes,
+                               void* x_perm, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  // one wave per token in flight: enough blocks for every token up to 8 per CU
+  const int64_t blocks = (T + 3) / 4;
+  const unsigned grid = static_cast<unsigned>(blocks < 2048 ? blocks : 2048);
+  if (row_bytes % 16 == 0)
+    klaunch(scatter_rows_kernel<16>, grid, 256, 0, s, static_cast<const char*>(x), row_of, T, k, row_bytes,
+            static_cast<char*>(x_perm));
+  else
+    klaunch(scatter_rows_kernel<4>, grid, 256, 0, s, static_cast<const char*>(x), row_of, T, k, row_bytes,
+            static_cast<char*>(x_perm));
+  return hipGetLastError();
 }
 
 hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int32_t* offsets,
                               int E, int64_t max_rows, int row_bytes, void* x_perm, hipStream_t s) {
   if (max_rows <= 0) return hipSuccess;
-  const int vec = (row_bytes % 16 == 0) ? 16 : 4;
-  const int64_t n = max_rows * (row_bytes / vec);
-  const unsigned grid = static_cast<unsigned>(n / 256 + 1 < 8192 ? n / 256 + 1 : 8192);
-  if (vec == 16)
+  // one wave per row in flight: enough blocks for every row up to 8 per CU
+  const int64_t blocks = (max_rows + 3) / 4;
+  const unsigned grid = static_cast<unsigned>(blocks < 2048 ? blocks : 2048);
+  if (row_bytes % 16 == 0)
     klaunch(gather_rows_kernel<16>, grid, 256, 0, s, static_cast<const char*>(x), row_token, offsets, E,
-                                                row_bytes, static_cast<char*>(x_perm));
+            row_bytes, static_cast<char*>(x_perm));
   else
     klaunch(gather_rows_kernel<4>, grid, 256, 0, s, static_cast<const char*>(x), row_token, offsets, E,
-                                               row_bytes, static_cast<char*>(x_perm));
+            row_bytes, static_cast<char*>(x_perm));
   return hipGetLastError();
 }
 

@@ -194,6 +194,9 @@ hipError_t launch_wgrad_bf16(const uint16_t* At, const uint16_t* Bt, const int32
 // o = {0, n}
 hipError_t launch_range(int32_t* o, int32_t n, hipStream_t s);
 
+// x_perm[row_of[t,j]] = x[t] for every kept assignment (row_of [T,k], -1 = dropped)
+hipError_t launch_scatter_rows(const void* x, const int32_t* row_of, int64_t T, int k, int row_bytes,
+                               void* x_perm, hipStream_t s);
 // x_perm[r] = x[row_token[r]] for r < offsets[E] (rows bounded by max_rows)
 hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int32_t* offsets,
                               int E, int64_t max_rows, int row_bytes, void* x_perm, hipStream_t s);

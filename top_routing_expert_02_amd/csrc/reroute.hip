@@ -263,7 +263,7 @@ hipError_t launch_dispatch_reroute(const void* x, const int32_t* cand, const flo
                                                         combine_gates);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || x_perm == nullptr) return err;
-  return launch_gather_rows(x, row_token, offsets, E, Q, row_bytes, x_perm, s);
+  return launch_scatter_rows(x, row_of, T, k, row_bytes, x_perm, s);
 }
 
 }  // namespace moe

@@ -386,14 +386,23 @@ __global__ __launch_bounds__(64 * WAVES) void topk_kernel(const float* __restric
   }
 }
 
+// One block per expert: thread i adds tiles i, i + 256, ... in order, then a
+// fixed tree over the threads (the result is bit-reproducible).
 __global__ __launch_bounds__(256) void prob_reduce_kernel(const float* __restrict__ part,
                                                           int ntiles, int E,
                                                           float* __restrict__ out) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= E) return;
+  __shared__ float red[256];
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x;
   float s = 0.f;
-  for (int t = 0; t < ntiles; ++t) s += part[static_cast<int64_t>(t) * E + e];
-  out[e] = s;
+  for (int t = tid; t < ntiles; t += 256) s += part[static_cast<int64_t>(t) * E + e];
+  red[tid] = s;
+  __syncthreads();
+  for (int off = 128; off >= 1; off >>= 1) {
+    if (tid < off) red[tid] += red[tid + off];
+    __syncthreads();
+  }
+  if (tid == 0) out[e] = red[0];
 }
 
 // ------------------------------------------------------------------ launchers
@@ -460,7 +469,7 @@ hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int nsel, i
 }
 
 hipError_t launch_prob_reduce(const float* part, int ntiles, int E, float* out, hipStream_t s) {
-  klaunch(prob_reduce_kernel, (E + 255) / 256, 256, 0, s, part, ntiles, E, out);
+  klaunch(prob_reduce_kernel, E, 256, 0, s, part, ntiles, E, out);
   return hipGetLastError();
 }
 
