@@ -281,6 +281,29 @@ int32_t moe_layer_forward(const moe_config *cfg, const void *x, const void *W_r,
                           size_t ws_bytes, hipEvent_t *stage_events, hipEvent_t *kernel_events,
                           hipStream_t stream);
 
+/* Bytes of the fixed device array moe_layer_forward_noalloc works in
+ * (one copy per GPU the library runs on, held until the process ends). */
+#define MOE_NOALLOC_SCRATCH_BYTES 268435456
+
+/*
+ * moe_layer_forward without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). It runs exactly the kernels of
+ * moe_layer_forward, in a fixed array of MOE_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU, and calls no allocator. Arguments and outputs
+ * as moe_layer_forward (no stage or kernel events).
+ *   Errors: those of moe_layer_forward; MOE_ERR_WORKSPACE when the layer's
+ *   moe_workspace_size exceeds MOE_NOALLOC_SCRATCH_BYTES (no device call is
+ *   made then); MOE_ERR_HIP when the array's address cannot be found.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (other streams, other host threads) race and must be ordered by the
+ *   caller. The array keeps the last call's contents; no call relies on them.
+ */
+int32_t moe_layer_forward_noalloc(const moe_config *cfg, const void *x, const void *W_r,
+                                  const float *b_r, const void *W1, const float *b1,
+                                  const void *W2, const float *b2, void *y,
+                                  const moe_route_info *info, hipStream_t stream);
+
 /* Figures of moe_load_stats, in this order in its stats array. */
 enum {
   MOE_STAT_DROPPED = 0,        /* assignments without a row: T k - rows */

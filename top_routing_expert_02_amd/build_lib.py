@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
 SOURCES = ["moe_api.cpp", "route.hip", "dispatch.hip", "reroute.hip", "backward.hip", "ffn_bf16.hip", "ffn_f32.hip",
-           "combine.hip", "stats.hip"]
+           "combine.hip", "stats.hip", "noalloc.hip"]
 
 ARCH = "gfx950"
 

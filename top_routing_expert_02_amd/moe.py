@@ -26,7 +26,7 @@ STAGE_NAMES = ["route", "dispatch", "gemm1", "gemm2", "combine"]
 
 EXPORTED = ["moe_capacity", "moe_candidates", "moe_max_rows", "moe_workspace_size", "moe_route",
             "moe_dispatch", "moe_dispatch_reroute", "moe_expert_ffn", "moe_combine",
-            "moe_layer_forward", "moe_load_stats", "moe_backward_workspace_size",
+            "moe_layer_forward", "moe_layer_forward_noalloc", "moe_load_stats", "moe_backward_workspace_size",
             "moe_layer_backward", "moe_status_string"]
 STAT_NAMES = ["dropped", "overflow_ratio", "max_over_mean_load", "padding_ratio", "load_entropy",
               "kept_variance", "aux_loss", "kept_rows"]
@@ -76,6 +76,8 @@ def lib():
         L.moe_combine.argtypes = [CFG, P, P, P, P, P]
         L.moe_layer_forward.argtypes = [CFG, P, P, P, P, P, P, P, P, ctypes.POINTER(MoeRouteInfo),
                                         P, SZ, P, P, P]
+        L.moe_layer_forward_noalloc.argtypes = [CFG, P, P, P, P, P, P, P, P,
+                                                ctypes.POINTER(MoeRouteInfo), P]
         L.moe_load_stats.argtypes = [CFG, P, P, P, ctypes.c_double, P, P, P, P]
         L.moe_backward_workspace_size.argtypes = [CFG, ctypes.POINTER(SZ)]
         L.moe_layer_backward.argtypes = [CFG, P, P, P, P, P, P, P, ctypes.POINTER(MoeRouteInfo), P,
@@ -213,6 +215,18 @@ def load_stats(cfg, expert_counts, expert_offsets, prob_sum, aux_alpha, stats, k
     _check("moe_load_stats", lib().moe_load_stats(
         ctypes.byref(cfg), _ptr(expert_counts), _ptr(expert_offsets), _ptr(prob_sum),
         float(aux_alpha), _ptr(kept), _ptr(dropped), _ptr(stats), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 268435456
+
+
+def layer_forward_noalloc(cfg, x, W_r, b_r, W1, b1, W2, b2, y, info: dict | None = None,
+                          stream=None):
+    """moe_layer_forward in the library's own fixed device array (no workspace)."""
+    ri = MoeRouteInfo(**{k: _ptr(v) for k, v in info.items()}) if info else None
+    _check("moe_layer_forward_noalloc", lib().moe_layer_forward_noalloc(
+        ctypes.byref(cfg), _ptr(x), _ptr(W_r), _ptr(b_r), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
+        _ptr(y), ctypes.byref(ri) if ri is not None else None, _stream(stream)))
 
 
 def backward_workspace_size(cfg: MoeConfig) -> int:
