@@ -42,6 +42,7 @@ def test_generated_file_is_current(tmp_path):
     parts = []
     for tm, tn in gen.SHAPES:
         parts.append(gen.emit(tm, tn))
+    parts.append(gen.emit_w_stage())
     body = "".join(parts)
     with open(INC) as f:
         current = f.read()

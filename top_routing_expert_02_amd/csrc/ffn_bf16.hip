@@ -54,6 +54,7 @@
 #include <hip/hip_ext.h>
 
 #include <type_traits>
+#include <utility>
 
 namespace moe {
 
@@ -63,11 +64,21 @@ constexpr int BN = 256;       // features per tile
 constexpr int BK = 64;        // K per LDS stage
 constexpr int ROWB = BK * 2;  // bytes per LDS row (128)
 constexpr int kWtRowB = BN * 2;  // bytes per row of a K-major weight stage (512)
-// stage buffers: two for the 256- and 192-row tiles, three for the shorter
-// ones (a tile of few rows streams weights, so more bytes in flight pay)
+// Stage rings. The token (A) and weight (W) tiles of a K stage sit in two
+// rings of their own: NA token buffers and NW weight buffers (NW >= NA). A
+// buffer takes the stage NA (NW) ahead once every wave has read it, so the
+// weight stream, which a tile of few rows is bound by, runs NW - 1 stages
+// ahead: 256-row tiles 2 + 2 buffers (128 KiB), 192 rows 2 + 3 (144 KiB),
+// 128 rows 3 + 3 (144 KiB), 64 rows 3 + 4 (152 KiB).
 template <int TM>
-constexpr int stages_for() { return TM <= 2 ? 3 : 2; }  // wait_loads allows at most 3
-constexpr int kLdsBytes = 3 * (128 + BN) * ROWB;  // the largest of NST (BM + BN) rows
+constexpr int a_stages() { return TM == 1 || TM == 2 ? 3 : 2; }
+template <int TM>
+constexpr int w_stages() { return TM == 4 ? 2 : (TM == 1 ? 4 : 3); }
+template <int TM>
+constexpr int lds_bytes_for() { return a_stages<TM>() * 64 * TM * ROWB + w_stages<TM>() * BN * ROWB; }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+[[maybe_unused]] constexpr int kLdsTall = cmax(lds_bytes_for<4>(), lds_bytes_for<3>());
+[[maybe_unused]] constexpr int kLdsShort = cmax(cmax(lds_bytes_for<3>(), lds_bytes_for<2>()), lds_bytes_for<1>());
 constexpr int TN = 4;         // 32-feature MFMA tiles per wave
 // Output modes of the epilogue: bf16 (after the activation), fp32, or the
 // second expert GEMM's y_perm: bf16 when the launch runs whole tiles, fp32
@@ -335,12 +346,51 @@ __device__ __forceinline__ TileInfo decode_tile_wg(int tile, const int* s_tiles,
   return t;
 }
 
-// Wait until the stage awaited has landed, with n (0 or 1) later stages of
-// G loads each still allowed in flight (at most three stage buffers).
-template <int G>
-__device__ __forceinline__ void wait_loads(int n) {
-  if (n >= 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G) : "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// s_waitcnt vmcnt(n) for a wave-uniform n (a jump over immediate forms).
+template <int N>
+__device__ __forceinline__ bool wait_vm_n() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  return true;
+}
+template <int... N>
+__device__ __forceinline__ void wait_vm_impl(int n, std::integer_sequence<int, N...>) {
+  (void)(((n == N) && wait_vm_n<N>()) || ...);
+}
+__device__ __forceinline__ void wait_vm(int n) {
+  wait_vm_impl(n < 63 ? n : 63, std::make_integer_sequence<int, 64>{});
+}
+
+// This wave's loads issued after the last load of stage t + 1 (token or
+// weight tile), at the wait at the end of stage t of a tile of nk stages.
+// Loads are issued in this order: stage 0 (token, weight); then, after the
+// previous tile's stores, stages p = 1 .. min(NW, nk) - 1 (token p if
+// p < NA, weight p); then after each stage j with j + NA < nk the refill
+// group G_j = (token j + NA, weight min(j + NW, nk - 1)). Loads return in
+// issue order, so vmcnt(this count) means stage t + 1 has landed; older
+// stores may still be in flight (they never make the count pass early, as
+// they are older than the loads waited for).
+template <int NA, int NW, int LA, int LB>
+__device__ __forceinline__ int loads_after(int t, int nk) {
+  const int st = t + 1;
+  int n = 0;
+  if (st < NA) {
+    for (int p = st + 1; p < NW && p < nk; ++p) n += LB + (p < NA ? LA : 0);
+    for (int j = 0; j <= t - 1; ++j)
+      if (j + NA < nk) n += LA + LB;
+  } else {
+    if (NW > NA) n += LB;  // the weight half of the group that holds token stage st
+    for (int j = st - NA + 1; j <= t - 1; ++j)
+      if (j + NA < nk) n += LA + LB;
+  }
+  return n;
+}
+
+// loads of stages 1 .. min(NW, nk) - 1 of a tile's prologue (this wave)
+template <int NA, int NW, int LA, int LB>
+__device__ __forceinline__ int prologue_loads(int nk) {
+  int n = 0;
+  for (int p = 1; p < NW && p < nk; ++p) n += LB + (p < NA ? LA : 0);
+  return n;
 }
 
 // Per-tile DMA sources: byte offsets (from the tile's token and weight bases)
@@ -444,8 +494,8 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], void* __
   }
 }
 
-// The persistent tile loop for tiles of BM = 64 TM rows. lds: NST stage
-// buffers; s_tiles: the M-tile prefix for this height; s_bias: two slices.
+// The persistent tile loop for tiles of BM = 64 TM rows. lds: the two stage
+// rings; s_tiles: the M-tile prefix for this height; s_bias: two slices.
 // WG: weight-gradient tiles (decode_tile_wg; offsets holds the padded K
 // offsets, M the rows of C per expert); else expert-FFN tiles of nkl stages
 // each: ntiles output tiles, and total = ntiles (whole K) or 2 ntiles (two K
@@ -460,13 +510,16 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
                                           int total, int ntiles, int NT) {
   constexpr int BM = 64 * TM;
   constexpr int WM = BM / 2;         // tokens per wave
-  constexpr int A_BYTES = BM * ROWB;
-  constexpr int STAGE = (BM + BN) * ROWB;
+  constexpr int A_BYTES = BM * ROWB;  // one token stage
+  constexpr int W_BYTES = BN * ROWB;  // one weight stage (BK rows of kWtRowB bytes when WT)
+  static_assert(W_BYTES == BK * kWtRowB, "both weight layouts fill the same stage size");
   constexpr int LA = BM / 32;        // 1 KiB (8-row) DMA blocks of the token tile per wave
   constexpr int LB = BN / 32;        // 1 KiB DMA blocks of the weight tile per wave
-  constexpr int G = LA + LB;         // DMA loads per wave per stage
-  constexpr int NST = stages_for<TM>();
-  static_assert(NST * STAGE <= kLdsBytes, "stage buffers exceed the LDS array");
+  static_assert(LB == 8, "stage_w_b8 issues a weight stage");
+  constexpr int NA = a_stages<TM>();
+  constexpr int NW = w_stages<TM>();
+  static_assert(NW >= NA, "the weight ring runs ahead");
+  static_assert(LA <= (LA + LB + 1) / 2, "token loads fall in the first half of a refill");
   const int Gd = gridDim.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -487,8 +540,11 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     else return decode_tile(tl, s_tiles, offsets, E, NT, BM, nkl, ntiles);
   };
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
-  const uint32_t trow = wm * WM * ROWB;            // this wave's token rows in a stage
-  const uint32_t wrow = A_BYTES + wn * WN * ROWB;  // this wave's weight rows in a stage
+  const uint32_t w_base = lds_base + NA * A_BYTES;
+  auto a_slot = [&](int i) { return lds_base + static_cast<uint32_t>(i * A_BYTES); };
+  auto w_slot = [&](int j) { return w_base + static_cast<uint32_t>(j * W_BYTES); };
+  const uint32_t trow = wm * WM * ROWB;  // this wave's token rows in a token stage
+  const uint32_t wrow = wn * WN * ROWB;  // this wave's weight rows in a weight stage
   // WT: the weight stage is K-major, BK rows of BN features (kWtRowB bytes,
   // 64-byte segments at position seg ^ (row & 3)). Weight fragment tile i
   // of lane (l5, hi) in K16 step s: feature 32 i + l5 of this wave's 128,
@@ -501,7 +557,7 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     const int key4 = (lane >> 2) & 3;
     const uint32_t rb = (8 * hi + ((lane & 15) >> 2)) * kWtRowB + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
 #pragma unroll
-    for (int i = 0; i < TN; ++i) wo[i] = A_BYTES + rb + 64 * ((4 * wn + i) ^ key4);
+    for (int i = 0; i < TN; ++i) wo[i] = rb + 64 * ((4 * wn + i) ^ key4);
   }
   // bytes from one K stage of W to the next
   const int64_t wst = WT ? static_cast<int64_t>(BK) * N * 2 : ROWB;
@@ -510,33 +566,43 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     for (int i = 0; i < TN; ++i) wa[i] = sbase + wo[i] + s * 16 * kWtRowB;
   };
 
-  uint32_t aoffs[LA], boffs[LB], vo[G];
+  uint32_t aoffs[LA], boffs[LB], vo[LA + LB];
   const char* Abase;
   const char* Wbase;
-  // a tile's first stages and its bias slice (wave 0, one lane per 4 features)
-  auto prologue = [&](const TileInfo& c, int par) {
-    for (int p = 0; p < NST && p < (WG ? c.nk : nkl); ++p)
-      issue_stage<TM>(aoffs, boffs, lds_base + p * STAGE + wave * LA * 1024,
-                      lds_base + p * STAGE + A_BYTES + wave * LB * 1024, Abase + p * ROWB,
-                      Wbase + p * wst);
+  // a tile's stage 0 and its bias slice (wave 0, one lane per 4 features):
+  // issued before the previous tile's epilogue
+  auto prologue0 = [&](const TileInfo& c, int par) {
+    issue_stage<TM>(aoffs, boffs, a_slot(0) + wave * LA * 1024, w_slot(0) + wave * LB * 1024, Abase, Wbase);
     if (bias != nullptr && c.part == 0 && wave == 0)
       issue_bias(bias + static_cast<int64_t>(c.e) * N + min(c.n0 + 4 * lane, N - 4),
                  static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&s_bias[par][0])));
+  };
+  // its stages 1 .. min(NW, nk) - 1 (token stage p only while p < NA):
+  // issued after the previous tile's epilogue stores
+  auto prologue1 = [&](int nk) {
+    for (int p = 1; p < NW && p < nk; ++p) {
+      if (p < NA)
+        issue_stage<TM>(aoffs, boffs, a_slot(p) + wave * LA * 1024, w_slot(p) + wave * LB * 1024,
+                        Abase + p * ROWB, Wbase + p * wst);
+      else
+        stage_w_b8(boffs, w_slot(p) + wave * LB * 1024, Wbase + p * wst);
+    }
   };
   int par = 0;  // bias slice of the current tile
   TileInfo cur = decode(tile);
   tile_sources<LA, LB, WT>(cur, A, row_idx, W, N, lda, w_estride, wave, drow, dpos, Abase, Wbase, aoffs,
                            boffs);
-  prologue(cur, par);
+  prologue0(cur, par);
+  prologue1(WG ? cur.nk : nkl);
 
   for (;;) {
     // K stages of this tile (cur moves on before its epilogue); the same for
     // every expert-FFN tile
     const int nk = WG ? cur.nk : nkl;
 
-    // the tile's first stages and bias slice (and, after an epilogue, its
-    // stores)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // stage 0 and the bias slice have landed (the later prologue stages may
+    // still be in flight)
+    wait_vm(prologue_loads<NA, NW, LA, LB>(nk));
     __syncthreads();
     // accumulators start at the bias: lane (l5, hi) holds features
     // fb + 32 i + 8 q + {0..3} of tile i (the same for every token tile j)
@@ -563,10 +629,10 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     bf16x8_t wf0[TN], tf0[TM], wf1[TN], tf1[TM];
     if constexpr (WT) {
       uint32_t wa[TN];
-      wadr(lds_base, 0, wa);
-      read_frags_t<TM>(wf0, tf0, lds_base + trow + fo[0], wa);
+      wadr(w_slot(0), 0, wa);
+      read_frags_t<TM>(wf0, tf0, a_slot(0) + trow + fo[0], wa);
     } else {
-      read_frags<TM>(wf0, tf0, lds_base + trow + fo[0], lds_base + wrow + fo[0]);
+      read_frags<TM>(wf0, tf0, a_slot(0) + trow + fo[0], w_slot(0) + wrow + fo[0]);
     }
 
     TileInfo done = cur;
@@ -575,95 +641,98 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     for (int i = 0; i < LA; ++i) vo[i] = aoffs[i];
 #pragma unroll
     for (int i = 0; i < LB; ++i) vo[LA + i] = boffs[i];
-    int sc = 0;              // buffer holding K stage t
-    uint32_t sb = lds_base;  // its LDS address
+    int ai = 0, wi = 0;  // ring slots of stage t
     int t = 0;
     // the second half of the last refill, issued with the next stage's first
     // K16 step: its LDS and global bases
     uint32_t pla = 0, plb = 0;
     const char* pga = nullptr;
     const char* pgw = nullptr;
-    // one K16 step reading the fragments of step s of the stage at sbase
+    // one K16 step reading the fragments of step s of the stage in slots sa, sw
     auto kstep = [&](const bf16x8_t (&w)[TN], const bf16x8_t (&tk)[TM], bf16x8_t (&nw)[TN],
-                     bf16x8_t (&nt)[TM], uint32_t sbase, int s) {
+                     bf16x8_t (&nt)[TM], uint32_t sa, uint32_t sw, int s) {
       if constexpr (WT) {
         uint32_t wa[TN];
-        wadr(sbase, s, wa);
-        step_t<TM>(acc, w, tk, nw, nt, sbase + trow + fo[s], wa);
+        wadr(sw, s, wa);
+        step_t<TM>(acc, w, tk, nw, nt, sa + trow + fo[s], wa);
       } else {
-        step<TM>(acc, w, tk, nw, nt, sbase + trow + fo[s], sbase + wrow + fo[s]);
+        step<TM>(acc, w, tk, nw, nt, sa + trow + fo[s], sw + wrow + fo[s]);
       }
     };
-    // the same with half of a stage's LDS-DMA loads
+    // the same with half of a refill's LDS-DMA loads
     auto kstep_dma = [&](auto half, const bf16x8_t (&w)[TN], const bf16x8_t (&tk)[TM], bf16x8_t (&nw)[TN],
-                         bf16x8_t (&nt)[TM], uint32_t sbase, int s) {
+                         bf16x8_t (&nt)[TM], uint32_t sa, uint32_t sw, int s) {
       constexpr int H = decltype(half)::value;
       if constexpr (WT) {
         uint32_t wa[TN];
-        wadr(sbase, s, wa);
-        step_dma_t<TM, H>(acc, w, tk, nw, nt, sbase + trow + fo[s], wa, vo, pla, plb, pga, pgw);
+        wadr(sw, s, wa);
+        step_dma_t<TM, H>(acc, w, tk, nw, nt, sa + trow + fo[s], wa, vo, pla, plb, pga, pgw);
       } else {
-        step_dma<TM, H>(acc, w, tk, nw, nt, sbase + trow + fo[s], sbase + wrow + fo[s], vo, pla, plb, pga,
-                        pgw);
+        step_dma<TM, H>(acc, w, tk, nw, nt, sa + trow + fo[s], sw + wrow + fo[s], vo, pla, plb, pga, pgw);
       }
     };
-    // One K stage. D1: step 0 issues the second half of the previous stage's
-    // refill; RF: stage t+NST is still to load (this stage's buffer takes it
-    // once every wave has read the stage).
+    // One K stage. D1: step 0 issues the second half of the previous refill;
+    // RF: stage t + NA is still to load (this stage's token buffer takes it,
+    // and its weight buffer the weight stage t + NW, once every wave has
+    // read the stage; past the last weight stage the last one is loaded
+    // again, into a buffer no later stage reads, so every refill has the
+    // same loads).
     auto stage = [&](auto d1, auto rf) {
+      const uint32_t sa = a_slot(ai), sw = w_slot(wi);
       // K16 steps 0..2, each reading the next step's fragments
       if constexpr (decltype(d1)::value)
-        kstep_dma(std::integral_constant<int, 1>{}, wf0, tf0, wf1, tf1, sb, 1);
+        kstep_dma(std::integral_constant<int, 1>{}, wf0, tf0, wf1, tf1, sa, sw, 1);
       else
-        kstep(wf0, tf0, wf1, tf1, sb, 1);
-      kstep(wf1, tf1, wf0, tf0, sb, 2);
-      kstep(wf0, tf0, wf1, tf1, sb, 3);
+        kstep(wf0, tf0, wf1, tf1, sa, sw, 1);
+      kstep(wf1, tf1, wf0, tf0, sa, sw, 2);
+      kstep(wf0, tf0, wf1, tf1, sa, sw, 3);
       // stage t+1 has landed and every wave has read its last fragments of
       // stage t
-      if constexpr (decltype(rf)::value) wait_loads<G>(NST - 2);
-      else wait_loads<G>(nk - 2 - t);
+      wait_vm(loads_after<NA, NW, LA, LB>(t, nk));
       __syncthreads();
-      const int sn_i = (sc + 1 == NST) ? 0 : sc + 1;
-      const uint32_t sn = lds_base + sn_i * STAGE;
+      const int an = (ai + 1 == NA) ? 0 : ai + 1;
+      const int wnx = (wi + 1 == NW) ? 0 : wi + 1;
       // K16 step 3; read step 0 of stage t+1
       if constexpr (decltype(rf)::value) {
-        // the buffer of stage t takes stage t+NST: half of its loads now,
-        // the rest with step 0 of stage t+1
-        pla = sb + wave * LA * 1024;
-        plb = sb + A_BYTES + wave * LB * 1024;
-        pga = Abase + (t + NST) * ROWB;
-        pgw = Wbase + (t + NST) * wst;
-        kstep_dma(std::integral_constant<int, 0>{}, wf1, tf1, wf0, tf0, sn, 0);
+        // half of the refill's loads now, the rest with step 0 of stage t+1
+        pla = sa + wave * LA * 1024;
+        plb = sw + wave * LB * 1024;
+        pga = Abase + (t + NA) * ROWB;
+        pgw = Wbase + min(t + NW, nk - 1) * wst;
+        kstep_dma(std::integral_constant<int, 0>{}, wf1, tf1, wf0, tf0, a_slot(an), w_slot(wnx), 0);
       } else {
-        kstep(wf1, tf1, wf0, tf0, sn, 0);
+        kstep(wf1, tf1, wf0, tf0, a_slot(an), w_slot(wnx), 0);
       }
-      sc = sn_i;
-      sb = sn;
+      ai = an;
+      wi = wnx;
     };
     using yes = std::true_type;
     using no = std::false_type;
-    if (t + NST < nk) {
-      // steady state; the first tail stage (there is one, as NST >= 2)
-      // issues the last refill's second half
+    if (t + NA < nk) {
+      // steady state; the first stage without a refill (there is one, as
+      // NA >= 2) issues the last refill's second half
       stage(no{}, yes{});
-      for (++t; t + NST < nk; ++t) stage(yes{}, yes{});
+      for (++t; t + NA < nk; ++t) stage(yes{}, yes{});
       stage(yes{}, no{});
       ++t;
     }
     // the last stages: nothing more to load
     for (; t + 1 < nk; ++t) stage(no{}, no{});
     // the last stage
-    kstep(wf0, tf0, wf1, tf1, sb, 1);
-    kstep(wf1, tf1, wf0, tf0, sb, 2);
-    kstep(wf0, tf0, wf1, tf1, sb, 3);
+    {
+      const uint32_t sa = a_slot(ai), sw = w_slot(wi);
+      kstep(wf0, tf0, wf1, tf1, sa, sw, 1);
+      kstep(wf1, tf1, wf0, tf0, sa, sw, 2);
+      kstep(wf0, tf0, wf1, tf1, sa, sw, 3);
+    }
     // every wave has read all of its fragments: all buffers are free, and the
-    // next tile's first stages load during this tile's last MFMAs and epilogue
+    // next tile's stage 0 loads during this tile's last MFMAs and epilogue
     __syncthreads();
     if (next < total) {
       cur = decode(next);
       tile_sources<LA, LB, WT>(cur, A, row_idx, W, N, lda, w_estride, wave, drow, dpos, Abase, Wbase,
                                aoffs, boffs);
-      prologue(cur, par ^ 1);
+      prologue0(cur, par ^ 1);
     }
     last_step<TM>(acc, wf1, tf1);
 
@@ -675,6 +744,8 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     if (full_tile) epilogue<TM, OUT, ACT, true>(acc, dst, done, N, wm, wn, l5, hi, split);
     else epilogue<TM, OUT, ACT, false>(acc, dst, done, N, wm, wn, l5, hi, split);
     if (next >= total) break;
+    // the next tile's later prologue stages, after this tile's stores
+    prologue1(WG ? cur.nk : nkl);
     tile = next;
     par ^= 1;
   }
@@ -705,9 +776,11 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
                               const int32_t* __restrict__ offsets, int E, int N, int K) {
   // the body uses gfx950 builtins only: the host pass needs just the signature
 #if defined(__HIP_DEVICE_COMPILE__)
-  __shared__ __attribute__((aligned(1024))) char lds[SHORT ? kLdsBytes : 2 * (256 + BN) * ROWB];
+  __shared__ __attribute__((aligned(1024))) char lds[SHORT ? kLdsShort : kLdsTall];
   __shared__ int s_tiles[1025];  // exclusive prefix of M tiles per expert
-  __shared__ int s_part[SHORT ? 3 : 2][256];
+  // the schedule's partial sums live in the stage rings, which no load
+  // touches before the schedule is done (a barrier follows it)
+  int (*s_part)[256] = reinterpret_cast<int (*)[256]>(lds);
   __shared__ __attribute__((aligned(16))) float s_bias[2][BN];  // bias slices of this and the next tile
 
   const int tid = threadIdx.x;

@@ -230,6 +230,28 @@ __device__ __forceinline__ void stage_{n}(const uint32_t (&ao)[{LA}], const uint
 '''
 
 
+def emit_w_stage(TN=4):
+    """One stage's weight loads alone (the weight ring runs ahead of the
+    token ring, so a tile's first weight stages come without token loads)."""
+    LB = 2 * TN
+    stg = []
+    for b in range(LB):
+        stg += [f"s_add_u32 m0, %{LB}, 0x{b*0x400:x}", "s_nop 0", f"global_load_lds_dwordx4 %{b}, %{LB+1}"]
+    ins = ", ".join(f'"v"(bo[{b}])' for b in range(LB))
+    return f'''
+// one stage's LDS-DMA loads of the weight tile only ({LB} blocks)
+__device__ __forceinline__ void stage_w_b{LB}(const uint32_t (&bo)[{LB}], uint32_t lb, const char* gw) {{
+  asm volatile(
+{chr(10).join(q(s) for s in stg[:-1])}
+      "{stg[-1]}"
+      :
+      : {ins},
+        "s"(lb), "s"(gw)
+      : "memory", "m0", "scc");
+}}
+'''
+
+
 def main():
     here = os.path.dirname(os.path.abspath(__file__))
     parts = ["// Generated by gen_mfma_steps.py; do not edit by hand.\n"
@@ -237,6 +259,7 @@ def main():
              "#pragma clang diagnostic push\n#pragma clang diagnostic ignored \"-Winline-asm\"\n"]
     for TM, TN in SHAPES:
         parts.append(emit(TM, TN))
+    parts.append(emit_w_stage())
     parts.append("#pragma clang diagnostic pop\n")
     with open(os.path.join(here, "mfma_steps.inc"), "w") as f:
         f.write("".join(parts))
