@@ -511,6 +511,24 @@ def test_grouped_order_many_m_tiles(name):
     say(f"[gpu] grouped order {name}: {st}")
 
 
+# K stage counts 1, 2, 3 and 5 in both expert GEMMs, around the depths of the
+# token and weight stage rings (2 to 4 buffers): the short-tile kernel
+# (every expert under 256 rows: 64- and 128-row tiles) and the tall one
+# (256- and 192-row tiles).
+STAGE_EDGES = [(64, 320), (128, 192), (192, 128), (320, 64)]
+
+
+@pytest.mark.parametrize("kernel", ["short", "tall"])
+@pytest.mark.parametrize("d,d_ff", STAGE_EDGES, ids=[f"d{a}_f{b}" for a, b in STAGE_EDGES])
+def test_gemm_stage_counts(kernel, d, d_ff):
+    shape = dict(T=150, E=4, k=2) if kernel == "short" else dict(T=700, E=2, k=1)
+    w = WORKLOADS["small_bf16"].scaled(name=f"stages_{kernel}_d{d}_f{d_ff}", d=d, d_ff=d_ff,
+                                       dropless=True, **shape)
+    inp = synth.make_inputs(w, "cuda", seed=7)
+    say(f"[gpu] stage counts {w.name}")
+    P.full_parity(w, inp, cap(w), report=say)
+
+
 @pytest.mark.parametrize("name", ["tiny_f32", "f32_mid", "small_bf16_mini", "skewed_bf16_mini",
                                   "large_e_bf16_mini"])
 def test_load_stats_on_gpu(name):

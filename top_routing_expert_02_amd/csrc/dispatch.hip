@@ -135,9 +135,10 @@ __global__ __launch_bounds__(256) void permute_kernel(
 // writes counts and offsets.
 constexpr int kFusedScanLimit = 32768;
 
+// hist has hrows rows of 64 / rpt tokens each (rpt rows per 64-token tile).
 __global__ __launch_bounds__(256) void permute_scan_kernel(
-    const int32_t* __restrict__ ids, const int32_t* __restrict__ hist, int ntiles, int64_t T, int k,
-    int E, int C, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ hist, int hrows, int rpt, int64_t T,
+    int k, int E, int C, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ slot, int32_t* __restrict__ row_of, int32_t* __restrict__ row_token) {
   __shared__ unsigned long long mask[1024];
   __shared__ int s_base[1024];
@@ -149,25 +150,26 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(
   const int64_t t0 = tile * kTileTokens;
   const int nt = static_cast<int>(min<int64_t>(kTileTokens, T - t0));
   const int np = nt * k;
-  // s_base[e] = sum of hist[t2][e] over tiles t2 before this one, s_cnt[e] the
-  // sum over all tiles. Tiles first, first + stride, ...: eight loads are
-  // issued before their sums (the loop is bound by load latency; integer
-  // sums do not depend on the order).
+  // s_base[e] = sum of hist[r][e] over the rows r of tiles before this one,
+  // s_cnt[e] the sum over all rows. Rows first, first + stride, ...: eight
+  // loads are issued before their sums (the loop is bound by load latency;
+  // integer sums do not depend on the order).
+  const int before = static_cast<int>(tile) * rpt;
   auto tile_sums = [&](int e, int first, int stride, int& b, int& c) {
     int t2 = first;
-    for (; t2 + 7 * stride < ntiles; t2 += 8 * stride) {
+    for (; t2 + 7 * stride < hrows; t2 += 8 * stride) {
       int h[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) h[u] = hist[static_cast<int64_t>(t2 + u * stride) * E + e];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if (t2 + u * stride < tile) b += h[u];
+        if (t2 + u * stride < before) b += h[u];
         c += h[u];
       }
     }
-    for (; t2 < ntiles; t2 += stride) {
+    for (; t2 < hrows; t2 += stride) {
       const int h = hist[static_cast<int64_t>(t2) * E + e];
-      if (t2 < tile) b += h;
+      if (t2 < before) b += h;
       c += h;
     }
   };
@@ -331,17 +333,18 @@ hipError_t launch_scan(const int32_t* hist, int ntiles, int E, int C, int32_t* b
   return hipGetLastError();
 }
 
-bool fused_scan_fits(int ntiles, int E) {
-  return static_cast<int64_t>(ntiles) * E <= kFusedScanLimit;
+bool fused_scan_fits(int64_t hist_rows, int E) {
+  return hist_rows * E <= kFusedScanLimit;
 }
 
-hipError_t launch_permute_scan(const void* x, const int32_t* ids, const int32_t* hist, int64_t T,
-                               int k, int E, int C, int row_bytes, int32_t* counts,
+hipError_t launch_permute_scan(const void* x, const int32_t* ids, const int32_t* hist, int hist_tokens,
+                               int64_t T, int k, int E, int C, int row_bytes, int32_t* counts,
                                int32_t* offsets, int32_t* slot, int32_t* row_of,
                                int32_t* row_token, void* x_perm, hipStream_t s) {
   const int ntiles = static_cast<int>((T + kTileTokens - 1) / kTileTokens);
-  klaunch(permute_scan_kernel, ntiles, 256, 0, s, ids, hist, ntiles, T, k, E, C, counts, offsets, slot,
-                                             row_of, row_token);
+  const int hrows = static_cast<int>((T + hist_tokens - 1) / hist_tokens);
+  klaunch(permute_scan_kernel, ntiles, 256, 0, s, ids, hist, hrows, kTileTokens / hist_tokens, T, k, E, C,
+          counts, offsets, slot, row_of, row_token);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || x_perm == nullptr) return err;
   return launch_scatter_rows(x, row_of, T, k, row_bytes, x_perm, s);

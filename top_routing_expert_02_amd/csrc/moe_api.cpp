@@ -92,8 +92,8 @@ Layout layout_of(const moe_config& c) {
   const int64_t T = c.T, E = c.E, k = c.k, R = max_rows_of(c), nt = ntiles_of(c.T);
   const int es = elem_size(c);
   L.logits = take(T * E * 4);
-  L.prob_part = take((T + 15) / 16 * E * 4);  // per top-k block (16 or 64 tokens)
-  L.hist = take(nt * E * 4);
+  L.prob_part = take((T + 15) / 16 * E * 4);  // per route block (16, 32 or 64 tokens)
+  L.hist = take((T + 15) / 16 * E * 4);       // per-expert counts in rows of 16, 32 or 64 tokens
   L.base = take(nt * E * 4);
   L.ids = take(T * n_cand_of(c) * 4);
   L.gates = take(T * n_cand_of(c) * 4);
@@ -232,11 +232,29 @@ int32_t check_ws(const moe_config& c, void* ws, size_t ws_bytes) {
 
 // ---- stages (arguments already validated)
 
+// logits_out (nullable): the caller's logits output; logits_ws: workspace
+// for them otherwise. hist (nullable): per-expert counts of the first k
+// choices in rows of *hist_tokens tokens (16 or 32 from the fused route, 64
+// otherwise), as the dispatch takes them.
 int32_t route_stage(const moe_config& c, const void* x, const void* Wr, const float* br,
-                    int32_t* ids, float* gates, float* prob_sum, float* logits, float* prob_part,
-                    int32_t* hist, hipStream_t s) {
+                    int32_t* ids, float* gates, float* prob_sum, float* logits_out, float* logits_ws,
+                    float* prob_part, int32_t* hist, int* hist_tokens, hipStream_t s) {
+  *hist_tokens = kTileTokens;
+  const int fused = c.dtype == MOE_BF16 ? route_fused_tokens(c.T, c.E) : 0;
+  if (fused > 0 && logits_out == nullptr &&
+      (hist == nullptr || fused_scan_fits((c.T + fused - 1) / fused, c.E))) {
+    // logits, softmax, top-k, gates and counts in one launch
+    MOE_HIP(launch_route_fused_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(Wr), br, c.T,
+                                    c.d, c.E, c.k, n_cand_of(c), c.renormalize, ids, gates,
+                                    prob_sum != nullptr ? prob_part : nullptr, hist, s));
+    if (prob_sum != nullptr)
+      MOE_HIP(launch_prob_reduce(prob_part, static_cast<int>((c.T + fused - 1) / fused), c.E, prob_sum, s));
+    *hist_tokens = fused;
+    return MOE_OK;
+  }
+  float* logits = logits_out != nullptr ? logits_out : logits_ws;
   const int tb = topk_block_tokens(c);
-  int32_t* zero = (tb < kTileTokens) ? hist : nullptr;  // cleared for the quarter-tile sums
+  int32_t* zero = (hist != nullptr && tb < kTileTokens) ? hist : nullptr;  // cleared for the quarter-tile sums
   if (c.dtype == MOE_BF16)
     MOE_HIP(launch_logits_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(Wr), br,
                                logits, c.T, c.d, c.E, zero, zero != nullptr ? ntiles_of(c.T) * c.E : 0,
@@ -252,18 +270,24 @@ int32_t route_stage(const moe_config& c, const void* x, const void* Wr, const fl
 }
 
 // x_perm may be null: the row copy is then skipped (the layer gathers rows in
-// its first GEMM instead).
+// its first GEMM instead). hist_ready: hist holds the route's counts in rows
+// of hist_tokens tokens; else they are counted here (64-token rows).
 int32_t dispatch_stage(const moe_config& c, const void* x, const int32_t* ids, bool hist_ready,
-                       int32_t* hist, int32_t* base, int32_t* counts, int32_t* offsets,
-                       int32_t* slot, int32_t* row_of, int32_t* row_token, void* x_perm,
-                       hipStream_t s) {
-  if (!hist_ready) MOE_HIP(launch_hist(ids, c.T, c.k, c.E, hist, s));
+                       int32_t* hist, int hist_tokens, int32_t* base, int32_t* counts,
+                       int32_t* offsets, int32_t* slot, int32_t* row_of, int32_t* row_token,
+                       void* x_perm, hipStream_t s) {
+  if (!hist_ready) {
+    MOE_HIP(launch_hist(ids, c.T, c.k, c.E, hist, s));
+    hist_tokens = kTileTokens;
+  }
   const int nt = static_cast<int>(ntiles_of(c.T));
-  if (fused_scan_fits(nt, c.E)) {
-    MOE_HIP(launch_permute_scan(x, ids, hist, c.T, c.k, c.E, c.capacity, c.d * elem_size(c), counts,
-                                offsets, slot, row_of, row_token, x_perm, s));
+  if (fused_scan_fits((c.T + hist_tokens - 1) / hist_tokens, c.E)) {
+    MOE_HIP(launch_permute_scan(x, ids, hist, hist_tokens, c.T, c.k, c.E, c.capacity, c.d * elem_size(c),
+                                counts, offsets, slot, row_of, row_token, x_perm, s));
     return MOE_OK;
   }
+  // the separate scan takes 64-token rows (the fused route is used only when
+  // its rows fit the one-launch path)
   MOE_HIP(launch_scan(hist, nt, c.E, c.capacity, base, counts, offsets, s));
   MOE_HIP(launch_permute(x, ids, base, offsets, c.T, c.k, c.E, c.capacity, c.d * elem_size(c), slot,
                          row_of, row_token, x_perm, s));
@@ -404,9 +428,9 @@ int32_t moe_route(const moe_config* cfg, const void* x, const void* W_r, const f
     return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_ws(c, ws, ws_bytes));
   const Layout L = layout_of(c);
-  return route_stage(c, x, W_r, b_r, topk_ids, topk_gates, prob_sum,
-                     logits != nullptr ? logits : at<float>(ws, L.logits), at<float>(ws, L.prob_part),
-                     nullptr, stream);
+  int hist_tokens = 0;
+  return route_stage(c, x, W_r, b_r, topk_ids, topk_gates, prob_sum, logits, at<float>(ws, L.logits),
+                     at<float>(ws, L.prob_part), nullptr, &hist_tokens, stream);
 }
 
 int32_t moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_ids,
@@ -430,7 +454,7 @@ int32_t moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_i
   if (general_rule(c))
     return dispatch_general_stage(c, ws, x, topk_ids, nullptr, expert_counts, expert_offsets, slot,
                                   row_of, row_token, nullptr, nullptr, x_perm, stream);
-  return dispatch_stage(c, x, topk_ids, false, at<int32_t>(ws, L.hist), at<int32_t>(ws, L.base),
+  return dispatch_stage(c, x, topk_ids, false, at<int32_t>(ws, L.hist), kTileTokens, at<int32_t>(ws, L.base),
                         expert_counts, expert_offsets, slot, row_of, row_token, x_perm, stream);
 }
 
@@ -556,16 +580,17 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* x, const void* W_r,
     return MOE_OK;
   };
   MOE_TRY(begin(MOE_STAGE_ROUTE));
-  MOE_TRY(route_stage(c, x, W_r, b_r, ids, gates, in.prob_sum, at<float>(ws, L.logits),
-                      at<float>(ws, L.prob_part), gen ? nullptr : hist, stream));
+  int hist_tokens = kTileTokens;
+  MOE_TRY(route_stage(c, x, W_r, b_r, ids, gates, in.prob_sum, nullptr, at<float>(ws, L.logits),
+                      at<float>(ws, L.prob_part), gen ? nullptr : hist, &hist_tokens, stream));
   MOE_TRY(end(MOE_STAGE_ROUTE));
   MOE_TRY(begin(MOE_STAGE_DISPATCH));
   if (gen)
     MOE_TRY(dispatch_general_stage(c, ws, x, ids, gates, counts, offsets, slot, row_of, row_token,
                                    in.served_ids, cgates, x_perm, stream));
   else
-    MOE_TRY(dispatch_stage(c, x, ids, true, hist, at<int32_t>(ws, L.base), counts, offsets, slot,
-                           row_of, row_token, x_perm, stream));
+    MOE_TRY(dispatch_stage(c, x, ids, true, hist, hist_tokens, at<int32_t>(ws, L.base), counts, offsets,
+                           slot, row_of, row_token, x_perm, stream));
   MOE_TRY(end(MOE_STAGE_DISPATCH));
   MOE_TRY(begin(MOE_STAGE_GEMM1));
   MOE_TRY(gemm1_stage(c, gather ? x : x_perm, gather ? row_token : nullptr, offsets, W1, b1, h, stream));

@@ -94,6 +94,14 @@ hipError_t launch_logits_f32(const float* x, const float* Wr, const float* br, f
 hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int nsel, int renormalize,
                        int32_t* ids, float* gates, float* prob_part, int32_t* hist, int tb,
                        hipStream_t s);
+// Router logits, softmax, top-nsel and gates in one launch for E <= 64
+// (route_fused_tokens(T, E) > 0): blocks of route_fused_tokens tokens; per
+// block one row of prob_part [blocks,E] (nullable) and of hist [blocks,E]
+// (nullable): the counts of the first k choices of its tokens.
+int route_fused_tokens(int64_t T, int E);
+hipError_t launch_route_fused_bf16(const uint16_t* x, const uint16_t* Wr, const float* br, int64_t T, int d,
+                                   int E, int k, int nsel, int renormalize, int32_t* ids, float* gates,
+                                   float* prob_part, int32_t* hist, hipStream_t s);
 // out[e] = sum over tiles of part[tile,e], tiles in order.
 hipError_t launch_prob_reduce(const float* part, int ntiles, int E, float* out, hipStream_t s);
 
@@ -110,10 +118,11 @@ hipError_t launch_permute(const void* x, const int32_t* ids, const int32_t* base
                           int row_bytes, int32_t* slot, int32_t* row_of, int32_t* row_token,
                           void* x_perm, hipStream_t s);
 
-// scan and permute in one launch; valid when fused_scan_fits(ntiles, E)
-bool fused_scan_fits(int ntiles, int E);
-hipError_t launch_permute_scan(const void* x, const int32_t* ids, const int32_t* hist, int64_t T,
-                               int k, int E, int C, int row_bytes, int32_t* counts,
+// scan and permute in one launch, from histograms of hist_tokens (16, 32 or
+// 64) tokens per row; valid when fused_scan_fits(rows of hist, E)
+bool fused_scan_fits(int64_t hist_rows, int E);
+hipError_t launch_permute_scan(const void* x, const int32_t* ids, const int32_t* hist, int hist_tokens,
+                               int64_t T, int k, int E, int C, int row_bytes, int32_t* counts,
                                int32_t* offsets, int32_t* slot, int32_t* row_of,
                                int32_t* row_token, void* x_perm, hipStream_t s);
 

@@ -39,28 +39,25 @@ namespace moe {
 //
 // zero (nullable): nzero ints the top-k kernel that follows accumulates into
 // (its per-tile expert histograms), cleared here to save a launch.
-template <int MT, int NT, int P>
-__global__ __launch_bounds__(256) void logits_bf16_kernel(const uint16_t* __restrict__ x,
-                                                          const uint16_t* __restrict__ Wr,
-                                                          const float* __restrict__ br,
-                                                          float* __restrict__ logits, int64_t T,
-                                                          int d, int E, int32_t* __restrict__ zero,
-                                                          int64_t nzero) {
-  if (zero != nullptr) {
-    const int64_t nthreads = static_cast<int64_t>(gridDim.x) * gridDim.y * 256;
-    for (int64_t i = (static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * 256 + threadIdx.x;
-         i < nzero; i += nthreads)
-      zero[i] = 0;
-  }
-  constexpr int NREG = MT * NT * 4;
-  constexpr int ROWS = 16 * (MT + NT);  // staged rows per wave and step: x rows, then W_r rows
-  constexpr int NLD = ROWS / 8;         // load instructions per step
+template <int MT, int NT>
+struct LogitsShape {
+  static constexpr int NREG = MT * NT * 4;
+  static constexpr int ROWS = 16 * (MT + NT);  // staged rows per wave and step: x rows, then W_r rows
+  static constexpr int NLD = ROWS / 8;         // load instructions per step
   static_assert(4 * ROWS * 8 * 16 >= 3 * NREG * 64 * 4, "the partial sums reuse the tiles");
-  __shared__ u32x4_t tile[4][ROWS][8];
+};
+
+// This wave's partial sums of the block tile (tokens t0.., experts e0..)
+// over its K steps, in acc; my is its staging tile.
+template <int MT, int NT, int P>
+__device__ __forceinline__ void logits_accumulate(const uint16_t* __restrict__ x,
+                                                  const uint16_t* __restrict__ Wr, int64_t T, int d, int E,
+                                                  int64_t t0, int e0,
+                                                  u32x4_t (&my)[LogitsShape<MT, NT>::ROWS][8],
+                                                  f32x4_t (&acc)[MT][NT]) {
+  constexpr int NLD = LogitsShape<MT, NT>::NLD;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * (16 * MT);
-  const int e0 = blockIdx.y * (16 * NT);
 
   // whole-line loads: instruction j, lane l -> staged row 8j + l/8, chunk l%8
   const uint16_t* src[NLD];
@@ -77,9 +74,7 @@ __global__ __launch_bounds__(256) void logits_bf16_kernel(const uint16_t* __rest
       src[j] = Wr + static_cast<int64_t>(e) * d + 8 * (lane & 7);
     }
   }
-  u32x4_t(&my)[ROWS][8] = tile[wave];
 
-  f32x4_t acc[MT][NT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -163,9 +158,18 @@ __global__ __launch_bounds__(256) void logits_bf16_kernel(const uint16_t* __rest
       }
     }
   }
+}
 
+// Adds the four waves' partial sums in a fixed order: afterwards wave 0's acc
+// holds the block tile (the other waves' acc are left as they were). tiles:
+// the staging tiles of all waves, reused for the partials.
+template <int MT, int NT>
+__device__ __forceinline__ void logits_reduce(f32x4_t (&acc)[MT][NT], void* tiles) {
+  constexpr int NREG = LogitsShape<MT, NT>::NREG;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   __syncthreads();  // every wave is done with its tile: the partial sums reuse them
-  float(&red)[3][NREG][64] = *reinterpret_cast<float(*)[3][NREG][64]>(&tile[0][0][0]);
+  float(&red)[3][NREG][64] = *reinterpret_cast<float(*)[3][NREG][64]>(tiles);
   if (wave > 0) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -175,6 +179,44 @@ __global__ __launch_bounds__(256) void logits_bf16_kernel(const uint16_t* __rest
         for (int i = 0; i < 4; ++i) red[wave - 1][(mt * NT + nt) * 4 + i][lane] = acc[mt][nt][i];
   }
   __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = (mt * NT + nt) * 4 + i;
+          float v = acc[mt][nt][i];
+          v += red[0][r][lane];
+          v += red[1][r][lane];
+          v += red[2][r][lane];
+          acc[mt][nt][i] = v;
+        }
+  }
+}
+
+template <int MT, int NT, int P>
+__global__ __launch_bounds__(256) void logits_bf16_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ Wr,
+                                                          const float* __restrict__ br,
+                                                          float* __restrict__ logits, int64_t T,
+                                                          int d, int E, int32_t* __restrict__ zero,
+                                                          int64_t nzero) {
+  if (zero != nullptr) {
+    const int64_t nthreads = static_cast<int64_t>(gridDim.x) * gridDim.y * 256;
+    for (int64_t i = (static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * 256 + threadIdx.x;
+         i < nzero; i += nthreads)
+      zero[i] = 0;
+  }
+  __shared__ u32x4_t tile[4][LogitsShape<MT, NT>::ROWS][8];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * (16 * MT);
+  const int e0 = blockIdx.y * (16 * NT);
+  f32x4_t acc[MT][NT];
+  logits_accumulate<MT, NT, P>(x, Wr, T, d, E, t0, e0, tile[wave], acc);
+  logits_reduce<MT, NT>(acc, &tile[0][0][0]);
   if (wave != 0) return;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -184,14 +226,9 @@ __global__ __launch_bounds__(256) void logits_bf16_kernel(const uint16_t* __rest
       const float bias = (br != nullptr && e < E) ? br[e] : 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = (mt * NT + nt) * 4 + i;
-        float v = acc[mt][nt][i];
-        v += red[0][r][lane];
-        v += red[1][r][lane];
-        v += red[2][r][lane];
         // output layout of the 16x16 MFMA: lane holds rows 4*(lane/16)+i, column lane%16
         const int64_t t = t0 + mt * 16 + (lane >> 4) * 4 + i;
-        if (t < T && e < E) logits[t * E + e] = v + bias;
+        if (t < T && e < E) logits[t * E + e] = acc[mt][nt][i] + bias;
       }
     }
 }
@@ -248,6 +285,64 @@ __global__ __launch_bounds__(256) void logits_f32_kernel(const float* __restrict
 // atomics, order free: LDS per block, then, for quarter-tile blocks, added
 // into the tile's row, which the logits kernel cleared) and sum_t p_{t,i}
 // per block (fixed-order sums: lanes, then groups, then waves).
+// One token's selection by its group of G lanes: v holds lane gl's logits
+// of experts gl, gl + G, ... (bit j of `invalid` set where there is no
+// expert or no token). Returns the lane's pick (round gl < nsel) and its
+// gate, and each logit's exp(s - m) with their group-wide sum se (for the
+// probabilities).
+template <int G, int NV>
+__device__ __forceinline__ void token_topk(const float (&v)[NV], uint32_t invalid, int gl, int E, int k,
+                                           int nsel, int renormalize, int& my_id, float& my_gate,
+                                           float (&ex)[NV], float& se) {
+  uint32_t taken = invalid;
+  float my_v = 0.f, top = 0.f;
+  my_id = -1;
+  for (int r = 0; r < nsel; ++r) {
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int e = gl + j * G;
+      if (!((taken >> j) & 1u) && (v[j] > bv || (v[j] == bv && e < bi))) {
+        bv = v[j];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int off = G / 2; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oi = __shfl_xor(bi, off, 64);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (r == 0) top = bv;
+    if ((bi & (G - 1)) == gl && bi < E) taken |= 1u << (bi / G);
+    if (gl == r) {
+      my_v = bv;
+      my_id = bi;
+    }
+  }
+  // softmax denominator
+  se = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    ex[j] = ((invalid >> j) & 1u) ? 0.f : __expf(v[j] - top);
+    se += ex[j];
+  }
+#pragma unroll
+  for (int off = G / 2; off >= 1; off >>= 1) se += __shfl_xor(se, off, 64);
+  const float mine = (gl < nsel) ? __expf(my_v - top) : 0.f;
+  float den = se;
+  if (renormalize) {
+    den = (gl < k) ? mine : 0.f;  // the top-k sum, also for later candidates
+#pragma unroll
+    for (int off = G / 2; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
+  }
+  my_gate = mine / den;
+}
+
 template <int G, int NV, int WAVES, int TB>
 __global__ __launch_bounds__(64 * WAVES) void topk_kernel(const float* __restrict__ logits, int64_t T,
                                                    int E, int k, int nsel, int renormalize,
@@ -284,7 +379,7 @@ __global__ __launch_bounds__(64 * WAVES) void topk_kernel(const float* __restric
     const bool tv = t < T;
     const float* row = logits + (tv ? t : 0) * E;
     float v[NV];
-    uint32_t taken = 0;
+    uint32_t invalid = 0;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int e = gl + j * G;
@@ -292,62 +387,15 @@ __global__ __launch_bounds__(64 * WAVES) void topk_kernel(const float* __restric
         v[j] = row[e];
       } else {
         v[j] = 0.f;
-        taken |= 1u << j;  // not an expert: never chosen, not summed
+        invalid |= 1u << j;  // not an expert: never chosen, not summed
       }
     }
-    const uint32_t invalid = taken;
-
-    float my_v = 0.f, top = 0.f;
-    int my_id = -1;
-    for (int r = 0; r < nsel; ++r) {
-      float bv = -__builtin_inff();
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const int e = gl + j * G;
-        if (!((taken >> j) & 1u) && (v[j] > bv || (v[j] == bv && e < bi))) {
-          bv = v[j];
-          bi = e;
-        }
-      }
-#pragma unroll
-      for (int off = G / 2; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oi = __shfl_xor(bi, off, 64);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if (r == 0) top = bv;
-      if ((bi & (G - 1)) == gl && bi < E) taken |= 1u << (bi / G);
-      if (gl == r) {
-        my_v = bv;
-        my_id = bi;
-      }
-    }
-
-    // softmax denominator
-    float ex[NV];
-    float se = 0.f;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      ex[j] = ((invalid >> j) & 1u) ? 0.f : __expf(v[j] - top);
-      se += ex[j];
-    }
-#pragma unroll
-    for (int off = G / 2; off >= 1; off >>= 1) se += __shfl_xor(se, off, 64);
-
-    const float mine = (gl < nsel) ? __expf(my_v - top) : 0.f;
-    float den = se;
-    if (renormalize) {
-      den = (gl < k) ? mine : 0.f;  // the top-k sum, also for later candidates
-#pragma unroll
-      for (int off = G / 2; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
-    }
+    int my_id;
+    float my_gate, ex[NV], se;
+    token_topk<G, NV>(v, invalid, gl, E, k, nsel, renormalize, my_id, my_gate, ex, se);
     if (tv && gl < nsel) {
       ids[t * nsel + gl] = my_id;
-      gates[t * nsel + gl] = mine / den;
+      gates[t * nsel + gl] = my_gate;
       if (want_hist && gl < k) atomicAdd(&s_hist[my_id], 1);
     }
     if (want_prob && tv) {
@@ -383,6 +431,108 @@ __global__ __launch_bounds__(64 * WAVES) void topk_kernel(const float* __restric
       if constexpr (TB == 64) hist[tile * E + e] = s_hist[e];
       else if (s_hist[e] != 0) atomicAdd(&hist[(tile * TB / 64) * E + e], s_hist[e]);
     }
+  }
+}
+
+// ------------------------------------------------------------------ fused route (E <= 64)
+//
+// Router logits, softmax, top-k, gates and the block's expert histogram in
+// one launch, for layers whose experts fit one logits tile (E <= 16 NT). A
+// block computes its 16 MT tokens x all experts with the MFMA K loop above;
+// the sums go to LDS instead of HBM, and the 256 threads then select per
+// token as topk_kernel does (G lanes per token). Side outputs per block:
+// the histogram row of its tokens' first k choices (rows of 16 MT tokens,
+// plain stores) and its probability sums (fixed order: lanes, groups,
+// waves), which prob_reduce adds in block order.
+template <int MT, int NT, int P, int G, int NV>
+__global__ __launch_bounds__(256) void route_fused_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wr, const float* __restrict__ br,
+    int64_t T, int d, int E, int k, int nsel, int renormalize, int32_t* __restrict__ ids,
+    float* __restrict__ gates, float* __restrict__ prob_part, int32_t* __restrict__ hist) {
+  constexpr int TB = 16 * MT;       // tokens per block
+  constexpr int NE = 16 * NT;       // experts of the tile (E <= NE)
+  constexpr int TPW = 64 / G;       // tokens per wave pass
+  constexpr int PASSES = TB / (TPW * 4) > 0 ? TB / (TPW * 4) : 1;
+  __shared__ u32x4_t tile[4][LogitsShape<MT, NT>::ROWS][8];
+  __shared__ float s_log[TB][NE + 1];
+  __shared__ float s_prob[4][NE];
+  __shared__ int s_hist[NE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TB;
+
+  f32x4_t acc[MT][NT];
+  logits_accumulate<MT, NT, P>(x, Wr, T, d, E, t0, 0, tile[wave], acc);
+  logits_reduce<MT, NT>(acc, &tile[0][0][0]);
+  if (wave == 0) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int e = nt * 16 + (lane & 15);
+        const float bias = (br != nullptr && e < E) ? br[e] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_log[mt * 16 + (lane >> 4) * 4 + i][e] = acc[mt][nt][i] + bias;
+      }
+  }
+  if (tid < NE) s_hist[tid] = 0;
+  __syncthreads();
+
+  const int gl = lane & (G - 1);
+  const int grp = lane / G;
+  float psum[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) psum[j] = 0.f;
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int tl = (wave * PASSES + pass) * TPW + grp;  // token within the block
+    const int64_t t = t0 + tl;
+    const bool tv = tl < TB && t < T;
+    float v[NV];
+    uint32_t invalid = 0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int e = gl + j * G;
+      if (e < E && tv) {
+        v[j] = s_log[tl][e];
+      } else {
+        v[j] = 0.f;
+        invalid |= 1u << j;
+      }
+    }
+    int my_id;
+    float my_gate, ex[NV], se;
+    token_topk<G, NV>(v, invalid, gl, E, k, nsel, renormalize, my_id, my_gate, ex, se);
+    if (tv && gl < nsel) {
+      ids[t * nsel + gl] = my_id;
+      gates[t * nsel + gl] = my_gate;
+      if (hist != nullptr && gl < k) atomicAdd(&s_hist[my_id], 1);
+    }
+    if (prob_part != nullptr && tv) {
+      const float inv = 1.0f / se;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) psum[j] += ex[j] * inv;
+    }
+  }
+  if (prob_part != nullptr) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int off = G; off < 64; off <<= 1) psum[j] += __shfl_xor(psum[j], off, 64);
+    if (grp == 0) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int e = gl + j * G;
+        if (e < NE) s_prob[wave][e] = psum[j];
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < E) {
+    if (prob_part != nullptr)
+      prob_part[static_cast<int64_t>(blockIdx.x) * E + tid] =
+          ((s_prob[0][tid] + s_prob[1][tid]) + s_prob[2][tid]) + s_prob[3][tid];
+    if (hist != nullptr) hist[static_cast<int64_t>(blockIdx.x) * E + tid] = s_hist[tid];
   }
 }
 
@@ -429,6 +579,35 @@ hipError_t launch_logits_bf16(const uint16_t* x, const uint16_t* Wr, const float
     dim3 grid(static_cast<unsigned>((T + 63) / 64), static_cast<unsigned>((E + 63) / 64));
     klaunch(logits_bf16_kernel<4, 4, 3>, grid, 256, 0, s, x, Wr, br, logits, T, d, E, zero, nzero);
   }
+  return hipGetLastError();
+}
+
+int route_fused_tokens(int64_t T, int E) {
+  if (E > 64) return 0;
+  return (E > 32 && T >= 32 * 256) ? 32 : 16;
+}
+
+hipError_t launch_route_fused_bf16(const uint16_t* x, const uint16_t* Wr, const float* br, int64_t T, int d,
+                                   int E, int k, int nsel, int renormalize, int32_t* ids, float* gates,
+                                   float* prob_part, int32_t* hist, hipStream_t s) {
+  const int tb = route_fused_tokens(T, E);
+  const dim3 grid(static_cast<unsigned>((T + tb - 1) / tb));
+  // tile shapes and ring depths as the logits kernel; G lanes per token
+  if (E <= 8)
+    klaunch(route_fused_bf16_kernel<1, 1, 4, 8, 1>, grid, 256, 0, s, x, Wr, br, T, d, E, k, nsel, renormalize,
+            ids, gates, prob_part, hist);
+  else if (E <= 16)
+    klaunch(route_fused_bf16_kernel<1, 1, 4, 16, 1>, grid, 256, 0, s, x, Wr, br, T, d, E, k, nsel,
+            renormalize, ids, gates, prob_part, hist);
+  else if (E <= 32)
+    klaunch(route_fused_bf16_kernel<1, 2, 4, 16, 2>, grid, 256, 0, s, x, Wr, br, T, d, E, k, nsel,
+            renormalize, ids, gates, prob_part, hist);
+  else if (tb == 32)
+    klaunch(route_fused_bf16_kernel<2, 4, 3, 16, 4>, grid, 256, 0, s, x, Wr, br, T, d, E, k, nsel,
+            renormalize, ids, gates, prob_part, hist);
+  else
+    klaunch(route_fused_bf16_kernel<1, 4, 4, 16, 4>, grid, 256, 0, s, x, Wr, br, T, d, E, k, nsel,
+            renormalize, ids, gates, prob_part, hist);
   return hipGetLastError();
 }
 
