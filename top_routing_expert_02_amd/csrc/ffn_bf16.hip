@@ -51,6 +51,8 @@
 //    never stored, so no tile reads outside [0, rows).
 #include "moe_internal.h"
 
+#include "gemm_schedule.h"
+
 #include <hip/hip_ext.h>
 
 #include <type_traits>
@@ -234,6 +236,14 @@ __device__ __forceinline__ void issue_stage(const uint32_t (&ao)[2 * TM], const 
   else stage_1x4(ao, bo, la, lb, ga, gw);
 }
 
+template <int TM>
+__device__ __forceinline__ void stage_a(const uint32_t (&ao)[2 * TM], uint32_t la, const char* ga) {
+  if constexpr (TM == 4) stage_a_4x4(ao, la, ga);
+  else if constexpr (TM == 3) stage_a_3x4(ao, la, ga);
+  else if constexpr (TM == 2) stage_a_2x4(ao, la, ga);
+  else stage_a_1x4(ao, la, ga);
+}
+
 // The tile's bias slice (BN fp32 values, 1 KiB) goes to LDS with the tile's
 // first stage: lane L loads features n0 + 4L .. n0 + 4L + 3 (clamped into
 // [0, N); a clamped slot duplicates a value that is never stored).
@@ -360,37 +370,15 @@ __device__ __forceinline__ void wait_vm(int n) {
   wait_vm_impl(n < 63 ? n : 63, std::make_integer_sequence<int, 64>{});
 }
 
-// This wave's loads issued after the last load of stage t + 1 (token or
-// weight tile), at the wait at the end of stage t of a tile of nk stages.
-// Loads are issued in this order: stage 0 (token, weight); then, after the
-// previous tile's stores, stages p = 1 .. min(NW, nk) - 1 (token p if
-// p < NA, weight p); then after each stage j with j + NA < nk the refill
-// group G_j = (token j + NA, weight min(j + NW, nk - 1)). Loads return in
-// issue order, so vmcnt(this count) means stage t + 1 has landed; older
-// stores may still be in flight (they never make the count pass early, as
-// they are older than the loads waited for).
+// The loads a wave may leave in flight at each wait: gemm_schedule.h counts
+// them from the issue order of the stage rings.
 template <int NA, int NW, int LA, int LB>
 __device__ __forceinline__ int loads_after(int t, int nk) {
-  const int st = t + 1;
-  int n = 0;
-  if (st < NA) {
-    for (int p = st + 1; p < NW && p < nk; ++p) n += LB + (p < NA ? LA : 0);
-    for (int j = 0; j <= t - 1; ++j)
-      if (j + NA < nk) n += LA + LB;
-  } else {
-    if (NW > NA) n += LB;  // the weight half of the group that holds token stage st
-    for (int j = st - NA + 1; j <= t - 1; ++j)
-      if (j + NA < nk) n += LA + LB;
-  }
-  return n;
+  return sched_loads_after(t, nk, NA, NW, LA, LB);
 }
-
-// loads of stages 1 .. min(NW, nk) - 1 of a tile's prologue (this wave)
 template <int NA, int NW, int LA, int LB>
 __device__ __forceinline__ int prologue_loads(int nk) {
-  int n = 0;
-  for (int p = 1; p < NW && p < nk; ++p) n += LB + (p < NA ? LA : 0);
-  return n;
+  return sched_prologue_loads(nk, NA, NW, LA, LB);
 }
 
 // Per-tile DMA sources: byte offsets (from the tile's token and weight bases)
@@ -518,8 +506,8 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
   static_assert(LB == 8, "stage_w_b8 issues a weight stage");
   constexpr int NA = a_stages<TM>();
   constexpr int NW = w_stages<TM>();
-  static_assert(NW >= NA, "the weight ring runs ahead");
-  static_assert(LA <= (LA + LB + 1) / 2, "token loads fall in the first half of a refill");
+  constexpr int NMIN = NA < NW ? NA : NW;  // refills run while stage t + NMIN exists
+  constexpr int NMAX = NA > NW ? NA : NW;
   const int Gd = gridDim.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -580,12 +568,14 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
   // its stages 1 .. min(NW, nk) - 1 (token stage p only while p < NA):
   // issued after the previous tile's epilogue stores
   auto prologue1 = [&](int nk) {
-    for (int p = 1; p < NW && p < nk; ++p) {
-      if (p < NA)
+    for (int p = 1; p < NMAX && p < nk; ++p) {
+      if (p < NA && p < NW)
         issue_stage<TM>(aoffs, boffs, a_slot(p) + wave * LA * 1024, w_slot(p) + wave * LB * 1024,
                         Abase + p * ROWB, Wbase + p * wst);
-      else
+      else if (p < NW)
         stage_w_b8(boffs, w_slot(p) + wave * LB * 1024, Wbase + p * wst);
+      else
+        stage_a<TM>(aoffs, a_slot(p) + wave * LA * 1024, Abase + p * ROWB);
     }
   };
   int par = 0;  // bias slice of the current tile
@@ -672,11 +662,10 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
       }
     };
     // One K stage. D1: step 0 issues the second half of the previous refill;
-    // RF: stage t + NA is still to load (this stage's token buffer takes it,
-    // and its weight buffer the weight stage t + NW, once every wave has
-    // read the stage; past the last weight stage the last one is loaded
-    // again, into a buffer no later stage reads, so every refill has the
-    // same loads).
+    // RF: refill this stage's buffers (token stage t + NA, weight stage
+    // t + NW) once every wave has read the stage; a stage past the last one
+    // loads the last one again, into a buffer no later stage reads, so every
+    // refill has the same loads.
     auto stage = [&](auto d1, auto rf) {
       const uint32_t sa = a_slot(ai), sw = w_slot(wi);
       // K16 steps 0..2, each reading the next step's fragments
@@ -697,7 +686,7 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
         // half of the refill's loads now, the rest with step 0 of stage t+1
         pla = sa + wave * LA * 1024;
         plb = sw + wave * LB * 1024;
-        pga = Abase + (t + NA) * ROWB;
+        pga = Abase + min(t + NA, nk - 1) * ROWB;
         pgw = Wbase + min(t + NW, nk - 1) * wst;
         kstep_dma(std::integral_constant<int, 0>{}, wf1, tf1, wf0, tf0, a_slot(an), w_slot(wnx), 0);
       } else {
@@ -708,11 +697,11 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     };
     using yes = std::true_type;
     using no = std::false_type;
-    if (t + NA < nk) {
+    if (t + NMIN < nk) {
       // steady state; the first stage without a refill (there is one, as
-      // NA >= 2) issues the last refill's second half
+      // NMIN >= 2) issues the last refill's second half
       stage(no{}, yes{});
-      for (++t; t + NA < nk; ++t) stage(yes{}, yes{});
+      for (++t; t + NMIN < nk; ++t) stage(yes{}, yes{});
       stage(yes{}, no{});
       ++t;
     }

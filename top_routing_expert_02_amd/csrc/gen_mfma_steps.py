@@ -154,6 +154,10 @@ def emit(TM, TN):
         stg += [f"s_add_u32 m0, %{LA+LB+1}, 0x{b*0x400:x}", "s_nop 0",
                 f"global_load_lds_dwordx4 %{LA+b}, %{LA+LB+3}"]
     stg_ins = ", ".join([f'"v"(ao[{b}])' for b in range(LA)] + [f'"v"(bo[{b}])' for b in range(LB)])
+    stg_a = []
+    for b in range(LA):
+        stg_a += [f"s_add_u32 m0, %{LA}, 0x{b*0x400:x}", "s_nop 0", f"global_load_lds_dwordx4 %{b}, %{LA+1}"]
+    ao_ins = ", ".join(f'"v"(ao[{b}])' for b in range(LA))
     sig_cur = f"const bf16x8_t (&w)[{TN}], const bf16x8_t (&t)[{TM}]"
     sig_next = f"bf16x8_t (&nw)[{TN}], bf16x8_t (&nt)[{TM}]"
     return f'''
@@ -214,6 +218,17 @@ __device__ __forceinline__ void frags_t_{n}(bf16x8_t (&nt)[{TM}], v4i16 (&nlo)[{
       : {next_list_t(TM, TN)}
       : "v"(ta), {wa_list(TN)}
       : "memory");
+}}
+
+// one stage's LDS-DMA loads of the token tile only ({LA} blocks)
+__device__ __forceinline__ void stage_a_{n}(const uint32_t (&ao)[{LA}], uint32_t la, const char* ga) {{
+  asm volatile(
+{chr(10).join(q(x) for x in stg_a[:-1])}
+      "{stg_a[-1]}"
+      :
+      : {ao_ins},
+        "s"(la), "s"(ga)
+      : "memory", "m0", "scc");
 }}
 
 // one stage's LDS-DMA loads: {LA} token blocks, then {LB} weight blocks
