@@ -48,14 +48,20 @@ def brute(nk, NA, NW, LA, LB, t):
 def closed_forms(tmp_path_factory):
     d = tmp_path_factory.mktemp("sched")
     src = d / "check.cpp"
-    lines = ['#include "gemm_schedule.h"', "#include <cstdio>", "int main() {"]
-    for na, nw, la, lb in CASES:
-        for nk in NK:
-            lines.append(f'  std::printf("P {na} {nw} {la} {lb} {nk} %d\\n", '
-                         f'moe::sched_prologue_loads({nk}, {na}, {nw}, {la}, {lb}));')
-            for t in range(0, nk - 1):
-                lines.append(f'  std::printf("W {na} {nw} {la} {lb} {nk} {t} %d\\n", '
-                             f'moe::sched_loads_after({t}, {nk}, {na}, {nw}, {la}, {lb}));')
+    cases = ", ".join("{%d, %d, %d, %d}" % c for c in CASES)
+    nks = ", ".join(str(n) for n in NK)
+    # one loop over the cases (an unrolled call per case takes minutes to compile)
+    lines = ['#include "gemm_schedule.h"', "#include <cstdio>", "int main() {",
+             f"  const int cases[][4] = {{{cases}}};",
+             f"  const int nks[] = {{{nks}}};",
+             "  for (const auto& c : cases)",
+             "    for (int nk : nks) {",
+             '      std::printf("P %d %d %d %d %d %d\\n", c[0], c[1], c[2], c[3], nk,',
+             "                  moe::sched_prologue_loads(nk, c[0], c[1], c[2], c[3]));",
+             "      for (int t = 0; t < nk - 1; ++t)",
+             '        std::printf("W %d %d %d %d %d %d %d\\n", c[0], c[1], c[2], c[3], nk, t,',
+             "                    moe::sched_loads_after(t, nk, c[0], c[1], c[2], c[3]));",
+             "    }"]
     lines.append("  return 0;\n}")
     src.write_text("\n".join(lines))
     exe = d / "check"
