@@ -90,3 +90,48 @@ def test_prologue_wait_matches_the_issue_order(closed_forms):
         # stage 0 is the first entry: everything of the prologue after it
         seq = issue_order(nk, na, nw, la, lb, 0)
         assert got == len(seq) - (la + lb), (na, nw, la, lb, nk)
+
+
+def test_xcd_plan_covers_every_tile_once(tmp_path):
+    """sched_xcd_plan: every tile of a launch goes to exactly one block, each
+    block takes slot b // 8 of its windows of G // 8 consecutive tiles, one
+    window per round (interleaved: XCD b % 8 takes window 8 r + b % 8 in
+    round r; otherwise a contiguous range of windows per XCD), and no block
+    runs more rounds than ceil(total / G)."""
+    src = tmp_path / "plan.cpp"
+    src.write_text("\n".join([
+        '#include "gemm_schedule.h"', "#include <cstdio>", "int main() {",
+        "  const int grids[] = {256, 248, 64, 8, 7};",
+        "  const int totals[] = {0, 1, 5, 8, 9, 63, 255, 256, 257, 511, 512, 513, 2800, 2816, 2992, 7488, 9856};",
+        "  for (int rr = 0; rr < 2; ++rr)",
+        "    for (int G : grids)",
+        "      for (int total : totals)",
+        "        for (int b = 0; b < G; ++b) {",
+        "          int first, stride, end;",
+        "          moe::sched_xcd_plan(b, G, total, rr != 0, first, stride, end);",
+        '          std::printf("%d %d %d %d %d %d %d\\n", rr, G, total, b, first, stride, end);',
+        "        }",
+        "  return 0;\n}"]))
+    exe = tmp_path / "plan"
+    subprocess.run(["g++", "-std=c++17", "-O1", f"-I{CSRC}", str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    runs = {}
+    for line in out.splitlines():
+        rr, G, total, b, first, stride, end = map(int, line.split())
+        assert stride > 0 and end <= total
+        runs.setdefault((rr, G, total), []).append((b, list(range(first, end, stride))))
+    assert len(runs) == 2 * 5 * 17
+    for (rr, G, total), blocks in runs.items():
+        seen = [t for _, ts in blocks for t in ts]
+        assert sorted(seen) == list(range(total)), (rr, G, total)
+        rounds = -(-total // G)
+        assert max(len(ts) for _, ts in blocks) <= max(rounds, 1), (rr, G, total)
+        if G % 8 == 0 and total > G:
+            S = G // 8
+            for b, ts in blocks:
+                assert all(t % S == b // 8 for t in ts), (rr, G, total, b)
+                windows = [t // S for t in ts]
+                if rr:
+                    assert windows == [8 * r + b % 8 for r in range(len(ts))], (G, total, b)
+                else:
+                    assert all(w2 - w1 == 1 for w1, w2 in zip(windows, windows[1:])), (G, total, b)

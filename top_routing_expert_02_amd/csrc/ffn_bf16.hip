@@ -482,8 +482,9 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], void* __
   }
 }
 
-// The persistent tile loop for tiles of BM = 64 TM rows. lds: the two stage
-// rings; s_tiles: the M-tile prefix for this height; s_bias: two slices.
+// The persistent tile loop for tiles of BM = 64 TM rows: tiles tile,
+// tile + stride, ... below end. lds: the two stage rings; s_tiles: the M-tile
+// prefix for this height; s_bias: two slices.
 // WG: weight-gradient tiles (decode_tile_wg; offsets holds the padded K
 // offsets, M the rows of C per expert); else expert-FFN tiles of nkl stages
 // each: ntiles output tiles, and total = ntiles (whole K) or 2 ntiles (two K
@@ -495,7 +496,7 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
                                           const int32_t* __restrict__ offsets,
                                           int E, int N, int nkl, int lda, int64_t w_estride, int M,
                                           char* lds, const int* s_tiles, float (*s_bias)[BN], int tile,
-                                          int total, int ntiles, int NT) {
+                                          int stride, int end, int total, int ntiles, int NT) {
   constexpr int BM = 64 * TM;
   constexpr int WM = BM / 2;         // tokens per wave
   constexpr int A_BYTES = BM * ROWB;  // one token stage
@@ -508,7 +509,6 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
   constexpr int NW = w_stages<TM>();
   constexpr int NMIN = NA < NW ? NA : NW;  // refills run while stage t + NMIN exists
   constexpr int NMAX = NA > NW ? NA : NW;
-  const int Gd = gridDim.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -626,7 +626,7 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     }
 
     TileInfo done = cur;
-    const int next = tile + Gd;
+    const int next = tile + stride;
 #pragma unroll
     for (int i = 0; i < LA; ++i) vo[i] = aoffs[i];
 #pragma unroll
@@ -717,7 +717,7 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     // every wave has read all of its fragments: all buffers are free, and the
     // next tile's stage 0 loads during this tile's last MFMAs and epilogue
     __syncthreads();
-    if (next < total) {
+    if (next < end) {
       cur = decode(next);
       tile_sources<LA, LB, WT>(cur, A, row_idx, W, N, lda, w_estride, wave, drow, dpos, Abase, Wbase,
                                aoffs, boffs);
@@ -732,7 +732,7 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     const bool split = !WG && total != ntiles;
     if (full_tile) epilogue<TM, OUT, ACT, true>(acc, dst, done, N, wm, wn, l5, hi, split);
     else epilogue<TM, OUT, ACT, false>(acc, dst, done, N, wm, wn, l5, hi, split);
-    if (next >= total) break;
+    if (next >= end) break;
     // the next tile's later prologue stages, after this tile's stores
     prologue1(WG ? cur.nk : nkl);
     tile = next;
@@ -778,16 +778,12 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
   const int per = (E + 255) / 256;
   const int eb = tid * per;
   const int b = blockIdx.x;
-  // blocks are dealt to the 8 XCDs round-robin: renumber so that consecutive
-  // tiles (which share weight and token panels) run on one XCD. A launch
-  // whose tiles fit in one round spreads them evenly: ceil(tiles / 8) per
-  // XCD (a permutation of the blocks either way, so later rounds, at a
-  // stride of the grid, are unchanged).
-  auto xcd_tile = [&](int total) {
-    if (Gd % 8 != 0) return b;
-    const int per = (min(total, Gd) + 7) / 8;
-    const int kk = b / 8, x = b % 8;
-    return kk < per ? x * per + kk : 8 * per + (kk - per) * 8 + x;
+  // this block's tiles: first, first + stride, ... below end (see
+  // sched_xcd_plan; reread: some expert has more M tiles than one group of
+  // the tile order holds, so its weight panels are read more than once)
+  int first = b, stride = Gd, end = 0;
+  auto xcd_plan = [&](int total, bool reread) {
+    sched_xcd_plan(b, Gd, total, reread, first, stride, end);
   };
   const int64_t wes = static_cast<int64_t>(N) * K;
   // K parts allowed: two when out2 is given and K splits into whole stages
@@ -832,28 +828,32 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
         }
       }
     const int BMs = tall ? 256 : 192;
+    int many = 0;  // an expert of this thread has more than 2 kGroupM M tiles
     {
       const int sel = tall ? 0 : 1;
       int run = s_part[sel][tid] - (tall ? c256 : c192);
       for (int e = eb; e < min(E, eb + per); ++e) {
         s_tiles[e] = run;
-        run += (offsets[e + 1] - offsets[e] + BMs - 1) / BMs;
+        const int mt = (offsets[e + 1] - offsets[e] + BMs - 1) / BMs;
+        many |= mt > 2 * kGroupM;
+        run += mt;
       }
       if (tid == 255) s_tiles[E] = s_part[sel][255];
     }
-    __syncthreads();
+    const bool reread = __syncthreads_or(many) != 0;
     if (nsplit != nullptr && b == 0 && tid == 0) *nsplit = S;
     const int ntiles = s_tiles[E] * NT;
     const int total = ntiles * S;
     const int nkl = K / BK / S;
-    const int tile = xcd_tile(total);
-    if (tile >= total) return;
+    xcd_plan(total, reread);
+    if (first >= end) return;
+    const int tile = first;
     if (tall)
       tile_loop<4, OUT, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
-                                        lds, s_tiles, s_bias, tile, total, ntiles, NT);
+                                        lds, s_tiles, s_bias, tile, stride, end, total, ntiles, NT);
     else
       tile_loop<3, OUT, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
-                                        lds, s_tiles, s_bias, tile, total, ntiles, NT);
+                                        lds, s_tiles, s_bias, tile, stride, end, total, ntiles, NT);
   } else {
     // ---- the same with heights 192, 128 and 64, whole or split in K: the
     // least cost with h + 64 rows per tile of height h (its MFMA rows plus a
@@ -891,30 +891,34 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
         }
       }
     const int BMs = sel == 0 ? 192 : (sel == 1 ? 128 : 64);
+    int many = 0;  // an expert of this thread has more than 2 kGroupM M tiles
     {
       int run = s_part[sel][tid] - c[sel];
       for (int e = eb; e < min(E, eb + per); ++e) {
         s_tiles[e] = run;
-        run += (offsets[e + 1] - offsets[e] + BMs - 1) / BMs;
+        const int mt = (offsets[e + 1] - offsets[e] + BMs - 1) / BMs;
+        many |= mt > 2 * kGroupM;
+        run += mt;
       }
       if (tid == 255) s_tiles[E] = s_part[sel][255];
     }
-    __syncthreads();
+    const bool reread = __syncthreads_or(many) != 0;
     if (nsplit != nullptr && b == 0 && tid == 0) *nsplit = S;
     const int ntiles = s_tiles[E] * NT;
     const int total = ntiles * S;
     const int nkl = K / BK / S;
-    const int tile = xcd_tile(total);
-    if (tile >= total) return;
+    xcd_plan(total, reread);
+    if (first >= end) return;
+    const int tile = first;
     if (sel == 0)
       tile_loop<3, OUT, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
-                                        lds, s_tiles, s_bias, tile, total, ntiles, NT);
+                                        lds, s_tiles, s_bias, tile, stride, end, total, ntiles, NT);
     else if (sel == 1)
       tile_loop<2, OUT, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
-                                        lds, s_tiles, s_bias, tile, total, ntiles, NT);
+                                        lds, s_tiles, s_bias, tile, stride, end, total, ntiles, NT);
     else
       tile_loop<1, OUT, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
-                                        lds, s_tiles, s_bias, tile, total, ntiles, NT);
+                                        lds, s_tiles, s_bias, tile, stride, end, total, ntiles, NT);
   }
 #endif
 }
@@ -964,7 +968,7 @@ void grouped_wgrad_bf16_kernel(const uint16_t* __restrict__ At, const uint16_t* 
   const int tile = (Gd % 8 == 0) ? (b % 8) * (Gd / 8) + b / 8 : b;
   if (tile >= total) return;
   tile_loop<4, kOutF32, kActNone, true>(At, nullptr, Bt, nullptr, C, nullptr, poff, E, N, 0, lda, 0, M,
-                                     lds, s_tiles, s_bias, tile, total, total, NT);
+                                     lds, s_tiles, s_bias, tile, Gd, total, total, total, NT);
 #endif
 }
 
