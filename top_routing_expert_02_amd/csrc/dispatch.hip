@@ -136,10 +136,15 @@ __global__ __launch_bounds__(256) void permute_kernel(
 constexpr int kFusedScanLimit = 32768;
 
 // hist has hrows rows of 64 / rpt tokens each (rpt rows per 64-token tile).
+// prob_sum (nullable): also the route's mean-probability sums, prob_sum[e] =
+// sum over the prows rows of prob_part [prows, E] (one row per route block),
+// expert e in block e mod gridDim.x, in the order of prob_reduce_kernel (so
+// the same bits): a layer call then needs no launch of its own for them.
 __global__ __launch_bounds__(256) void permute_scan_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ hist, int hrows, int rpt, int64_t T,
     int k, int E, int C, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ slot, int32_t* __restrict__ row_of, int32_t* __restrict__ row_token) {
+    int32_t* __restrict__ slot, int32_t* __restrict__ row_of, int32_t* __restrict__ row_token,
+    const float* __restrict__ prob_part, int prows, float* __restrict__ prob_sum) {
   __shared__ unsigned long long mask[1024];
   __shared__ int s_base[1024];
   __shared__ int s_cnt[1024];
@@ -246,6 +251,21 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(
     row_of[t0 * k + p] = row;
     if (row >= 0) row_token[row] = static_cast<int32_t>(t0 + t);
   }
+  if (prob_sum != nullptr) {
+    float* red = reinterpret_cast<float*>(s_part);  // 256 floats, free after the scan
+    for (int e = static_cast<int>(blockIdx.x); e < E; e += gridDim.x) {
+      float acc = 0.f;
+      for (int r = tid; r < prows; r += 256) acc += prob_part[static_cast<int64_t>(r) * E + e];
+      __syncthreads();
+      red[tid] = acc;
+      __syncthreads();
+      for (int off = 128; off >= 1; off >>= 1) {
+        if (tid < off) red[tid] += red[tid + off];
+        __syncthreads();
+      }
+      if (tid == 0) prob_sum[e] = red[0];
+    }
+  }
 }
 
 // x_perm[r] = x[row_token[r]] for every kept row (rows read from offsets[E]
@@ -340,11 +360,12 @@ bool fused_scan_fits(int64_t hist_rows, int E) {
 hipError_t launch_permute_scan(const void* x, const int32_t* ids, const int32_t* hist, int hist_tokens,
                                int64_t T, int k, int E, int C, int row_bytes, int32_t* counts,
                                int32_t* offsets, int32_t* slot, int32_t* row_of,
-                               int32_t* row_token, void* x_perm, hipStream_t s) {
+                               int32_t* row_token, void* x_perm, const float* prob_part, int prows,
+                               float* prob_sum, hipStream_t s) {
   const int ntiles = static_cast<int>((T + kTileTokens - 1) / kTileTokens);
   const int hrows = static_cast<int>((T + hist_tokens - 1) / hist_tokens);
   klaunch(permute_scan_kernel, ntiles, 256, 0, s, ids, hist, hrows, kTileTokens / hist_tokens, T, k, E, C,
-          counts, offsets, slot, row_of, row_token);
+          counts, offsets, slot, row_of, row_token, prob_part, prows, prob_sum);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || x_perm == nullptr) return err;
   return launch_scatter_rows(x, row_of, T, k, row_bytes, x_perm, s);

@@ -280,7 +280,7 @@ struct TileInfo {
 // doubles the stores, against the rounds it saves.
 [[maybe_unused]] constexpr int kEpiK = 512;
 
-constexpr int kGroupM = 4;  // M tiles per group of the tile order
+constexpr int kGroupM = 5;  // M tiles per group of the tile order
 
 // s_tiles[e]: exclusive prefix over experts of their M tiles of height BM;
 // ntiles output tiles, each in K parts of nk stages (unit u covers tile
@@ -302,10 +302,13 @@ __device__ __forceinline__ TileInfo decode_tile(int u, const int* s_tiles, const
   const int mte = s_tiles[lo + 1] - s_tiles[lo];
   const int v = tile - s_tiles[lo] * NT;
   // grouped order inside an expert with many M tiles: groups of kGroupM M
-  // tiles, each swept over all N tiles with its M tiles innermost, so the 32
-  // consecutive tiles one XCD runs at a time share 4 token panels and 8
-  // weight panels; up to 8 M tiles form one group (every weight panel is
-  // then read once per expert)
+  // tiles, each swept over all N tiles with its M tiles innermost, so the
+  // tiles one XCD runs at a time share a few token and weight panels; up to
+  // 2 kGroupM M tiles form one group (every weight panel is then read once
+  // per expert). Groups of 5: a group of N-tile sweeps then ends inside a
+  // window of G / 8 tiles whenever there are 16 N tiles; on the 16384-token
+  // layer's second GEMM (16 N tiles) groups of 3, 5 and 7 ran 2-4% faster
+  // than groups of 4, 6, 8 and 10, which line up with the windows
   const int GM = mte <= 2 * kGroupM ? mte : kGroupM;
   const int g = v / (GM * NT);
   const int r = v - g * GM * NT;

@@ -236,10 +236,14 @@ int32_t check_ws(const moe_config& c, void* ws, size_t ws_bytes) {
 // for them otherwise. hist (nullable): per-expert counts of the first k
 // choices in rows of *hist_tokens tokens (16 or 32 from the fused route, 64
 // otherwise), as the dispatch takes them.
+// defer_rows (nullable): the caller's dispatch can sum the probability
+// partials (a plain-rule dispatch whose scan runs in one launch); when the
+// route leaves them to it, *defer_rows is the number of partial rows, else 0.
 int32_t route_stage(const moe_config& c, const void* x, const void* Wr, const float* br,
                     int32_t* ids, float* gates, float* prob_sum, float* logits_out, float* logits_ws,
-                    float* prob_part, int32_t* hist, int* hist_tokens, hipStream_t s) {
+                    float* prob_part, int32_t* hist, int* hist_tokens, int* defer_rows, hipStream_t s) {
   *hist_tokens = kTileTokens;
+  if (defer_rows != nullptr) *defer_rows = 0;
   const int fused = c.dtype == MOE_BF16 ? route_fused_tokens(c.T, c.E) : 0;
   if (fused > 0 && logits_out == nullptr &&
       (hist == nullptr || fused_scan_fits((c.T + fused - 1) / fused, c.E))) {
@@ -247,9 +251,12 @@ int32_t route_stage(const moe_config& c, const void* x, const void* Wr, const fl
     MOE_HIP(launch_route_fused_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(Wr), br, c.T,
                                     c.d, c.E, c.k, n_cand_of(c), c.renormalize, ids, gates,
                                     prob_sum != nullptr ? prob_part : nullptr, hist, s));
-    if (prob_sum != nullptr)
-      MOE_HIP(launch_prob_reduce(prob_part, static_cast<int>((c.T + fused - 1) / fused), c.E, prob_sum, s));
+    const int prows = static_cast<int>((c.T + fused - 1) / fused);
     *hist_tokens = fused;
+    if (prob_sum != nullptr) {
+      if (defer_rows != nullptr && hist != nullptr) *defer_rows = prows;
+      else MOE_HIP(launch_prob_reduce(prob_part, prows, c.E, prob_sum, s));
+    }
     return MOE_OK;
   }
   float* logits = logits_out != nullptr ? logits_out : logits_ws;
@@ -264,18 +271,27 @@ int32_t route_stage(const moe_config& c, const void* x, const void* Wr, const fl
                               c.T, c.d, c.E, s));
   MOE_HIP(launch_topk(logits, c.T, c.E, c.k, n_cand_of(c), c.renormalize, ids, gates,
                       prob_sum != nullptr ? prob_part : nullptr, hist, tb, s));
-  if (prob_sum != nullptr)
-    MOE_HIP(launch_prob_reduce(prob_part, static_cast<int>((c.T + tb - 1) / tb), c.E, prob_sum, s));
+  if (prob_sum != nullptr) {
+    const int prows = static_cast<int>((c.T + tb - 1) / tb);
+    if (defer_rows != nullptr && hist != nullptr && fused_scan_fits(ntiles_of(c.T), c.E))
+      *defer_rows = prows;
+    else
+      MOE_HIP(launch_prob_reduce(prob_part, prows, c.E, prob_sum, s));
+  }
   return MOE_OK;
 }
 
 // x_perm may be null: the row copy is then skipped (the layer gathers rows in
 // its first GEMM instead). hist_ready: hist holds the route's counts in rows
 // of hist_tokens tokens; else they are counted here (64-token rows).
+// prob_rows > 0: also sum the route's probability partials (prob_part
+// [prob_rows, E]) into prob_sum; only with the one-launch scan, which the
+// route checked before leaving them here.
 int32_t dispatch_stage(const moe_config& c, const void* x, const int32_t* ids, bool hist_ready,
                        int32_t* hist, int hist_tokens, int32_t* base, int32_t* counts,
                        int32_t* offsets, int32_t* slot, int32_t* row_of, int32_t* row_token,
-                       void* x_perm, hipStream_t s) {
+                       void* x_perm, const float* prob_part, int prob_rows, float* prob_sum,
+                       hipStream_t s) {
   if (!hist_ready) {
     MOE_HIP(launch_hist(ids, c.T, c.k, c.E, hist, s));
     hist_tokens = kTileTokens;
@@ -283,7 +299,8 @@ int32_t dispatch_stage(const moe_config& c, const void* x, const int32_t* ids, b
   const int nt = static_cast<int>(ntiles_of(c.T));
   if (fused_scan_fits((c.T + hist_tokens - 1) / hist_tokens, c.E)) {
     MOE_HIP(launch_permute_scan(x, ids, hist, hist_tokens, c.T, c.k, c.E, c.capacity, c.d * elem_size(c),
-                                counts, offsets, slot, row_of, row_token, x_perm, s));
+                                counts, offsets, slot, row_of, row_token, x_perm, prob_part, prob_rows,
+                                prob_rows > 0 ? prob_sum : nullptr, s));
     return MOE_OK;
   }
   // the separate scan takes 64-token rows (the fused route is used only when
@@ -430,7 +447,7 @@ int32_t moe_route(const moe_config* cfg, const void* x, const void* W_r, const f
   const Layout L = layout_of(c);
   int hist_tokens = 0;
   return route_stage(c, x, W_r, b_r, topk_ids, topk_gates, prob_sum, logits, at<float>(ws, L.logits),
-                     at<float>(ws, L.prob_part), nullptr, &hist_tokens, stream);
+                     at<float>(ws, L.prob_part), nullptr, &hist_tokens, nullptr, stream);
 }
 
 int32_t moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_ids,
@@ -455,7 +472,8 @@ int32_t moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_i
     return dispatch_general_stage(c, ws, x, topk_ids, nullptr, expert_counts, expert_offsets, slot,
                                   row_of, row_token, nullptr, nullptr, x_perm, stream);
   return dispatch_stage(c, x, topk_ids, false, at<int32_t>(ws, L.hist), kTileTokens, at<int32_t>(ws, L.base),
-                        expert_counts, expert_offsets, slot, row_of, row_token, x_perm, stream);
+                        expert_counts, expert_offsets, slot, row_of, row_token, x_perm, nullptr, 0, nullptr,
+                        stream);
 }
 
 int32_t moe_dispatch_reroute(const moe_config* cfg, const void* x, const int32_t* cand_ids,
@@ -581,8 +599,9 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* x, const void* W_r,
   };
   MOE_TRY(begin(MOE_STAGE_ROUTE));
   int hist_tokens = kTileTokens;
+  int prob_rows = 0;  // > 0: the dispatch sums the route's probability partials
   MOE_TRY(route_stage(c, x, W_r, b_r, ids, gates, in.prob_sum, nullptr, at<float>(ws, L.logits),
-                      at<float>(ws, L.prob_part), gen ? nullptr : hist, &hist_tokens, stream));
+                      at<float>(ws, L.prob_part), gen ? nullptr : hist, &hist_tokens, &prob_rows, stream));
   MOE_TRY(end(MOE_STAGE_ROUTE));
   MOE_TRY(begin(MOE_STAGE_DISPATCH));
   if (gen)
@@ -590,7 +609,8 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* x, const void* W_r,
                                    in.served_ids, cgates, x_perm, stream));
   else
     MOE_TRY(dispatch_stage(c, x, ids, true, hist, hist_tokens, at<int32_t>(ws, L.base), counts, offsets,
-                           slot, row_of, row_token, x_perm, stream));
+                           slot, row_of, row_token, x_perm, at<float>(ws, L.prob_part), prob_rows,
+                           in.prob_sum, stream));
   MOE_TRY(end(MOE_STAGE_DISPATCH));
   MOE_TRY(begin(MOE_STAGE_GEMM1));
   MOE_TRY(gemm1_stage(c, gather ? x : x_perm, gather ? row_token : nullptr, offsets, W1, b1, h, stream));

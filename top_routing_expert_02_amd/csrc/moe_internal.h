@@ -119,12 +119,15 @@ hipError_t launch_permute(const void* x, const int32_t* ids, const int32_t* base
                           void* x_perm, hipStream_t s);
 
 // scan and permute in one launch, from histograms of hist_tokens (16, 32 or
-// 64) tokens per row; valid when fused_scan_fits(rows of hist, E)
+// 64) tokens per row; valid when fused_scan_fits(rows of hist, E). With
+// prob_sum (nullable) it also sums the route's probability partials
+// (prob_part [prows, E]) as launch_prob_reduce would.
 bool fused_scan_fits(int64_t hist_rows, int E);
 hipError_t launch_permute_scan(const void* x, const int32_t* ids, const int32_t* hist, int hist_tokens,
                                int64_t T, int k, int E, int C, int row_bytes, int32_t* counts,
                                int32_t* offsets, int32_t* slot, int32_t* row_of,
-                               int32_t* row_token, void* x_perm, hipStream_t s);
+                               int32_t* row_token, void* x_perm, const float* prob_part, int prows,
+                               float* prob_sum, hipStream_t s);
 
 // Dispatch with a priority order and overflow re-routing rounds. The plan's
 // buffers live in the workspace: col/served [T*k], next_col [T], fill/fill0
