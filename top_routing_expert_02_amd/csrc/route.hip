@@ -7,6 +7,8 @@
 // equal scores to the lower expert index.
 #include "moe_internal.h"
 
+#include <type_traits>
+
 namespace moe {
 
 // ------------------------------------------------------------------ logits (bf16, MFMA)
@@ -285,6 +287,36 @@ __global__ __launch_bounds__(256) void logits_f32_kernel(const float* __restrict
 // atomics, order free: LDS per block, then, for quarter-tile blocks, added
 // into the tile's row, which the logits kernel cleared) and sum_t p_{t,i}
 // per block (fixed-order sums: lanes, then groups, then waves).
+// Exchange with a partner lane inside a group of up to 16 lanes (one DPP
+// row) without the LDS: the partner of lane i is i ^ 1 and i ^ 2 (quad
+// permutes), i ^ 7 (mirror inside 8 lanes) and i ^ 15 (mirror inside 16)
+// for OFF = 1, 2, 4, 8; larger OFF go through ds_bpermute as i ^ OFF. The
+// masks 1, 2, 7, 15 are linearly independent over GF(2), so the four steps,
+// in any order, combine every lane of a 16-lane group exactly once, as the
+// xor butterfly 1, 2, 4, 8 does. Every lane of the wave must be active.
+template <int OFF>
+__device__ __forceinline__ int grp_xchg(int v) {
+  if constexpr (OFF == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);       // quad_perm 1,0,3,2
+  else if constexpr (OFF == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);  // quad_perm 2,3,0,1
+  else if constexpr (OFF == 4) return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true); // row_half_mirror
+  else if constexpr (OFF == 8) return __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, true); // row_mirror
+  else return __shfl_xor(v, OFF, 64);
+}
+template <int OFF>
+__device__ __forceinline__ float grp_xchg(float v) {
+  return __builtin_bit_cast(float, grp_xchg<OFF>(__builtin_bit_cast(int, v)));
+}
+// step(integral_constant<OFF>) for OFF = G/2, G/4, ..., 1
+template <int G, typename F>
+__device__ __forceinline__ void grp_steps(F&& step) {
+  if constexpr (G >= 64) step(std::integral_constant<int, 32>{});
+  if constexpr (G >= 32) step(std::integral_constant<int, 16>{});
+  if constexpr (G >= 16) step(std::integral_constant<int, 8>{});
+  if constexpr (G >= 8) step(std::integral_constant<int, 4>{});
+  if constexpr (G >= 4) step(std::integral_constant<int, 2>{});
+  if constexpr (G >= 2) step(std::integral_constant<int, 1>{});
+}
+
 // One token's selection by its group of G lanes: v holds lane gl's logits
 // of experts gl, gl + G, ... (bit j of `invalid` set where there is no
 // expert or no token). Returns the lane's pick (round gl < nsel) and its
@@ -308,15 +340,15 @@ __device__ __forceinline__ void token_topk(const float (&v)[NV], uint32_t invali
         bi = e;
       }
     }
-#pragma unroll
-    for (int off = G / 2; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
+    grp_steps<G>([&](auto o) {
+      constexpr int OFF = decltype(o)::value;
+      const float ov = grp_xchg<OFF>(bv);
+      const int oi = grp_xchg<OFF>(bi);
       if (ov > bv || (ov == bv && oi < bi)) {
         bv = ov;
         bi = oi;
       }
-    }
+    });
     if (r == 0) top = bv;
     if ((bi & (G - 1)) == gl && bi < E) taken |= 1u << (bi / G);
     if (gl == r) {
@@ -331,14 +363,12 @@ __device__ __forceinline__ void token_topk(const float (&v)[NV], uint32_t invali
     ex[j] = ((invalid >> j) & 1u) ? 0.f : __expf(v[j] - top);
     se += ex[j];
   }
-#pragma unroll
-  for (int off = G / 2; off >= 1; off >>= 1) se += __shfl_xor(se, off, 64);
+  grp_steps<G>([&](auto o) { se += grp_xchg<decltype(o)::value>(se); });
   const float mine = (gl < nsel) ? __expf(my_v - top) : 0.f;
   float den = se;
   if (renormalize) {
     den = (gl < k) ? mine : 0.f;  // the top-k sum, also for later candidates
-#pragma unroll
-    for (int off = G / 2; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
+    grp_steps<G>([&](auto o) { den += grp_xchg<decltype(o)::value>(den); });
   }
   my_gate = mine / den;
 }
