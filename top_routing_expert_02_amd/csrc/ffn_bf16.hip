@@ -280,6 +280,16 @@ struct TileInfo {
 // doubles the stores, against the rounds it saves.
 [[maybe_unused]] constexpr int kEpiK = 512;
 
+// The tall schedule's share of a tile for its weight panel, in rows of the
+// K loop: 256-row and 192-row tiles stream the same 256 weight rows per K
+// stage. With it the 16384-token layer takes 256-row tiles (30 and 9 rounds
+// against 39 and 11 of 192 rows); its GEMMs ran 3336 and 3280 µs that way
+// against 3522 and 3398 µs with 192-row tiles, which the bare row count
+// preferred. Layers with a short K (1024: the skewed layers' second GEMM)
+// keep 192-row tiles, whose epilogues are shorter (256-row tiles ran 216
+// µs there against 181).
+[[maybe_unused]] constexpr int kTallShare = 128;
+
 constexpr int kGroupM = 5;  // M tiles per group of the tile order
 
 // s_tiles[e]: exclusive prefix over experts of their M tiles of height BM;
@@ -789,12 +799,24 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
     sched_xcd_plan(b, Gd, total, reread, first, stride, end);
   };
   const int64_t wes = static_cast<int64_t>(N) * K;
-  // K parts allowed: two when out2 is given and K splits into whole stages
+  // K parts allowed: two when out2 is given and K splits into whole stages,
+  // and only for a schedule whose whole tiles fill fewer than two rounds
+  // (few rows, long K: decode batches). With more tiles a split only evens
+  // out the last round, and its fp32 partial sums (twice the stores, and
+  // twice the combine's reads in fp32) cost more than that.
   const int smax = (out2 != nullptr && (K / BK) % 2 == 0) ? 2 : 1;
-  // work of one block: rounds of units x (rows x (K per part + epilogue))
+  // work of one block: rounds of units x (rows x (K per part + epilogue)),
+  // rows = the tile's MFMA rows plus a share for its weight panel
   auto cost = [&](int64_t tiles, int rows, int S) {
     const int64_t rounds = (tiles * S + Gd - 1) / Gd;
     return rounds * rows * static_cast<int64_t>(K / S + kEpiK);
+  };
+  auto may_split = [&](int64_t tiles, int S) { return S == 1 || tiles < 2 * static_cast<int64_t>(Gd); };
+  // the same for the tall heights h, the weight panel's share charged to the
+  // K loop only (the epilogue stores h rows)
+  auto cost_tall = [&](int64_t tiles, int h, int S) {
+    const int64_t rounds = (tiles * S + Gd - 1) / Gd;
+    return rounds * ((h + kTallShare) * static_cast<int64_t>(K / S) + static_cast<int64_t>(h) * kEpiK);
   };
   if constexpr (!SHORT) {
     // ---- device-side schedule. Both tile heights are counted, each whole
@@ -823,7 +845,9 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
     int64_t best = -1;
     for (int sp = 1; sp <= smax; ++sp)
       for (int q = 0; q < 2; ++q) {
-        const int64_t c = cost(static_cast<int64_t>(s_part[q][255]) * NT, q == 0 ? 256 : 192, sp);
+        const int64_t tiles = static_cast<int64_t>(s_part[q][255]) * NT;
+        if (!may_split(tiles, sp)) continue;
+        const int64_t c = cost_tall(tiles, q == 0 ? 256 : 192, sp);
         if (best < 0 || c < best) {
           best = c;
           tall = q == 0;
@@ -886,7 +910,9 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
     for (int sp = 1; sp <= smax; ++sp)
 #pragma unroll
       for (int q = 0; q < 3; ++q) {
-        const int64_t c = cost(static_cast<int64_t>(s_part[q][255]) * NT, kH[q] + 64, sp);
+        const int64_t tiles = static_cast<int64_t>(s_part[q][255]) * NT;
+        if (!may_split(tiles, sp)) continue;
+        const int64_t c = cost(tiles, kH[q] + 64, sp);
         if (best < 0 || c < best) {
           best = c;
           sel = q;
