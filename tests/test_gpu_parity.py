@@ -461,16 +461,16 @@ def test_full_size_workload(name):
         assert o_disp["kept"].all() and o_disp["rows"] == w.T * w.k
 
 
-# One expert holds every token, in more than 10 M tiles with a partial last
-# group of 5, so both GEMMs run the grouped tile order inside an expert
-# (experts past 10 M tiles: groups of 5 M tiles swept over the N tiles).
-# With 256 CUs the schedule picks 192-row tiles for the first case (14 M
-# tiles, groups 5+5+4) and 256-row tiles for the first GEMM of the second
-# (11 M tiles x 23 N tiles fill one round; groups 5+5+1); both split the
+# One expert holds every token, in more than 12 M tiles with a partial last
+# group of 6, so both GEMMs run the grouped tile order inside an expert
+# (experts past 12 M tiles: groups of 6 M tiles swept over the N tiles).
+# With 256 CUs the schedule picks 192-row tiles for the first case (16 M
+# tiles, groups 6+6+4) and 256-row tiles for the first GEMM of the second
+# (14 M tiles x 18 N tiles fill one round; groups 6+6+2); both split the
 # second GEMM's K. The stage entry point runs the same problem unsplit.
 MANY_MTILES = {
-    "hot_mtiles_192": dict(T=2500, d=512, d_ff=512),
-    "hot_mtiles_256": dict(T=2600, d=512, d_ff=5888),
+    "hot_mtiles_192": dict(T=3000, d=512, d_ff=512),
+    "hot_mtiles_256": dict(T=3400, d=512, d_ff=4608),
 }
 
 

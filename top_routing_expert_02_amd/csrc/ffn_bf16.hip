@@ -290,7 +290,7 @@ struct TileInfo {
 // µs there against 181).
 [[maybe_unused]] constexpr int kTallShare = 128;
 
-constexpr int kGroupM = 5;  // M tiles per group of the tile order
+constexpr int kGroupM = 6;  // M tiles per group of the tile order
 
 // s_tiles[e]: exclusive prefix over experts of their M tiles of height BM;
 // ntiles output tiles, each in K parts of nk stages (unit u covers tile
@@ -315,10 +315,10 @@ __device__ __forceinline__ TileInfo decode_tile(int u, const int* s_tiles, const
   // tiles, each swept over all N tiles with its M tiles innermost, so the
   // tiles one XCD runs at a time share a few token and weight panels; up to
   // 2 kGroupM M tiles form one group (every weight panel is then read once
-  // per expert). Groups of 5: a group of N-tile sweeps then ends inside a
-  // window of G / 8 tiles whenever there are 16 N tiles; on the 16384-token
-  // layer's second GEMM (16 N tiles) groups of 3, 5 and 7 ran 2-4% faster
-  // than groups of 4, 6, 8 and 10, which line up with the windows
+  // per expert). The group size was picked by measurement on the
+  // 16384-token layer (17 M tiles of 256 rows per expert): groups of 6 ran
+  // its GEMMs 0.5% and 2.4% faster than groups of 5, and groups of 3, 4 and
+  // 7 no better than 5
   const int GM = mte <= 2 * kGroupM ? mte : kGroupM;
   const int g = v / (GM * NT);
   const int r = v - g * GM * NT;
@@ -800,10 +800,12 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
   };
   const int64_t wes = static_cast<int64_t>(N) * K;
   // K parts allowed: two when out2 is given and K splits into whole stages,
-  // and only for a schedule whose whole tiles fill fewer than two rounds
-  // (few rows, long K: decode batches). With more tiles a split only evens
-  // out the last round, and its fp32 partial sums (twice the stores, and
-  // twice the combine's reads in fp32) cost more than that.
+  // and only for a schedule whose whole tiles fit in one round (few rows,
+  // long K: decode batches). With more tiles a split only evens out the
+  // last round, and its fp32 partial sums (twice the stores, and twice the
+  // combine's reads in fp32) cost more than that: the skewed layer's second
+  // GEMM (352 tiles) split ran no faster and its combine took 25.8 µs
+  // instead of 12.7.
   const int smax = (out2 != nullptr && (K / BK) % 2 == 0) ? 2 : 1;
   // work of one block: rounds of units x (rows x (K per part + epilogue)),
   // rows = the tile's MFMA rows plus a share for its weight panel
@@ -811,7 +813,7 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
     const int64_t rounds = (tiles * S + Gd - 1) / Gd;
     return rounds * rows * static_cast<int64_t>(K / S + kEpiK);
   };
-  auto may_split = [&](int64_t tiles, int S) { return S == 1 || tiles < 2 * static_cast<int64_t>(Gd); };
+  auto may_split = [&](int64_t tiles, int S) { return S == 1 || tiles <= static_cast<int64_t>(Gd); };
   // the same for the tall heights h, the weight panel's share charged to the
   // K loop only (the epilogue stores h rows)
   auto cost_tall = [&](int64_t tiles, int h, int S) {
