@@ -306,6 +306,17 @@ template <int OFF>
 __device__ __forceinline__ float grp_xchg(float v) {
   return __builtin_bit_cast(float, grp_xchg<OFF>(__builtin_bit_cast(int, v)));
 }
+// (v, i) replaces (bv, bi) when ok and it ranks higher: the larger value,
+// the lower index on a tie. Bitwise tests and selects, no branches: the
+// exec-mask code the compiler makes for short-circuit tests cost several
+// times the comparisons themselves (the skewed layer's selection ran about
+// 1300 cycles per round that way).
+__device__ __forceinline__ void keep_better(float v, int i, bool ok, float& bv, int& bi) {
+  const bool take = ok & ((v > bv) | ((v == bv) & (i < bi)));
+  bv = take ? v : bv;
+  bi = take ? i : bi;
+}
+
 // step(integral_constant<OFF>) for OFF = G/2, G/4, ..., 1
 template <int G, typename F>
 __device__ __forceinline__ void grp_steps(F&& step) {
@@ -333,28 +344,16 @@ __device__ __forceinline__ void token_topk(const float (&v)[NV], uint32_t invali
     float bv = -__builtin_inff();
     int bi = 0x7fffffff;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int e = gl + j * G;
-      if (!((taken >> j) & 1u) && (v[j] > bv || (v[j] == bv && e < bi))) {
-        bv = v[j];
-        bi = e;
-      }
-    }
+    for (int j = 0; j < NV; ++j) keep_better(v[j], gl + j * G, !((taken >> j) & 1u), bv, bi);
     grp_steps<G>([&](auto o) {
       constexpr int OFF = decltype(o)::value;
-      const float ov = grp_xchg<OFF>(bv);
-      const int oi = grp_xchg<OFF>(bi);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
+      keep_better(grp_xchg<OFF>(bv), grp_xchg<OFF>(bi), true, bv, bi);
     });
     if (r == 0) top = bv;
-    if ((bi & (G - 1)) == gl && bi < E) taken |= 1u << (bi / G);
-    if (gl == r) {
-      my_v = bv;
-      my_id = bi;
-    }
+    taken |= (((bi & (G - 1)) == gl) & (bi < E)) ? (1u << (bi / G)) : 0u;
+    const bool mine_r = gl == r;
+    my_v = mine_r ? bv : my_v;
+    my_id = mine_r ? bi : my_id;
   }
   // softmax denominator
   se = 0.f;
