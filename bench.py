@@ -61,14 +61,23 @@ def parse():
     return ap.parse_args()
 
 
-def gemm_source_digest():
-    """sha256 of the grouped-GEMM kernel source; stored HBM counter figures
-    count only while it is unchanged."""
+def code_text(src):
+    """C++/HIP source without comments and with runs of blank space folded,
+    so that a change of comments alone keeps a source's digest."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
+def gemm_source_digest(root=None):
+    """sha256 of the grouped-GEMM kernel code (comments left out); stored
+    HBM counter figures count only while it is unchanged."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("ffn_bf16.hip", "mfma_steps.inc", "moe_internal.h"):
-        with open(os.path.join(ROOT, "top_routing_expert_02_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in ("ffn_bf16.hip", "gemm_schedule.h", "mfma_steps.inc", "moe_internal.h"):
+        with open(os.path.join(root or ROOT, "top_routing_expert_02_amd", "csrc", f)) as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -20,11 +20,13 @@
 //    lane's accumulators hold 4 consecutive features of one token: the
 //    epilogue stores 8-byte (bf16) or 16-byte (fp32) vectors.
 //  * The tile height is chosen on the device, per launch, from the actual
-//    expert row counts (the cost model is at the schedule below): a group
-//    count that leaves a mostly idle last round of 256-row tiles runs as
-//    192-row tiles, and experts with a few dozen rows (decode batches) run
-//    64-row tiles, which stream the same weights with a quarter of the
-//    MFMAs. The host never learns the row counts.
+//    expert row counts (the cost model is at the schedule below: rounds of
+//    the persistent blocks times the K-loop work of a tile, its rows plus a
+//    share for the weight panel every tile streams whole, plus its
+//    epilogue): long-K layers with thousands of rows per expert run 256-row
+//    tiles, ragged ones 192-row tiles, and experts with a few dozen rows
+//    (decode batches) 64-row tiles, which stream the same weights with a
+//    quarter of the MFMAs. The host never learns the row counts.
 //  * K advances in stages of BK=64: every LDS row is 128 bytes, one full
 //    cache line of the source row, so each L1->L2 request moves a whole line.
 //    The 16-byte chunks of a row are XOR-swizzled by (row/2)&7, which keeps
@@ -33,20 +35,24 @@
 //    (global_load_lds_dwordx4: no staging registers, no ds_write); one
 //    instruction fills 8 rows (1 KiB); each lane fetches the chunk that the
 //    swizzle places at its LDS slot.
-//  * Two stage buffers (three for tiles of 128 or 64 rows). A stage is four K16 steps; each step's MFMAs run with
-//    the next step's fragment reads in flight, and the buffer a stage occupied
-//    is refilled (with the stage after next) right after the barrier that
-//    shows every wave has read it: half of the loads between the MFMAs of
-//    that stage's last step, the other half between those of the next
-//    stage's first step (a whole stage's loads at once back up the load
-//    queue, and the wave stalls at an MFMA issue slot). The next tile's first
-//    stages, and its bias slice, load during the current tile's last step and
-//    epilogue.
+//  * Token and weight stages sit in rings of their own (2 + 2 buffers for
+//    256-row tiles, 2 + 3 for 192, 3 + 3 for 128, 3 + 4 for 64). A stage is
+//    four K16 steps; each step's MFMAs run with the next step's fragment
+//    reads in flight, and a buffer is refilled (with the stage NA or NW
+//    ahead) right after the barrier that shows every wave has read it: half
+//    of the loads between the MFMAs of that stage's last step, the other
+//    half between those of the next stage's first step (a whole stage's
+//    loads at once back up the load queue, and the wave stalls at an MFMA
+//    issue slot). The next tile's first stage, and its bias slice, load
+//    during the current tile's last step and epilogue; its later stages
+//    after the epilogue's stores.
 //  * Persistent blocks, one per CU. The schedule is computed on the device
-//    from expert_offsets (no host read-back): expert-major tiles, M tiles of
-//    an expert innermost, so concurrent tiles share weight panels. Blocks are
-//    renumbered so that consecutive tiles run on one XCD (blocks are dealt to
-//    the 8 XCDs round-robin) and share its L2.
+//    from expert_offsets (no host read-back): expert-major tiles, and inside
+//    an expert with many M tiles groups of kGroupM M tiles swept over the N
+//    tiles, so concurrent tiles share token and weight panels. The tiles one
+//    XCD runs at a time are consecutive (blocks are dealt to the 8 XCDs
+//    round-robin) and share its L2 (sched_xcd_plan: interleaved rounds when
+//    an expert's weights are re-read, else a contiguous range per XCD).
 //  * Ragged M: rows past an expert's end read that expert's last row and are
 //    never stored, so no tile reads outside [0, rows).
 #include "moe_internal.h"
