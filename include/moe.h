@@ -171,6 +171,18 @@ int32_t moe_max_rows(const moe_config *cfg, int64_t *rows);
  * more than this (host only). */
 int32_t moe_workspace_size(const moe_config *cfg, size_t *bytes);
 
+/* Caps the grid of the persistent expert GEMMs (forward and backward) at
+ * `blocks` workgroups per launch, on every device; 0 (the default) runs one
+ * per CU. For callers that keep CUs free for other work beside the layer,
+ * such as an expert-parallel all-to-all pipelined with the expert
+ * computation (ai-master.cc EP engineering answer 001, §二, compute-
+ * communication overlap). The GEMMs lay out their tiles on the device for
+ * whatever grid they get, so results stay within the layer's tolerance at
+ * any cap (sums may round differently). Process-wide; applies to launches
+ * issued after it returns (host only, no device call).
+ * Errors: MOE_ERR_INVALID_ARG if blocks < 0. */
+int32_t moe_set_gemm_max_blocks(int32_t blocks);
+
 /*
  * Route ([MoE Principles] §2.1-§2.2; page "MiniMax 面试: MoE gate 与分布式通信",
  * mianshidashi.cn, 深入解析 01: the gate emits scores, top-k ids and weights).

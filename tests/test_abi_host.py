@@ -204,3 +204,9 @@ def test_status_strings(m):
     L = m.lib()
     for s in (0, -1, -2, -3, -4, 99):
         assert isinstance(L.moe_status_string(s), bytes)
+
+
+def test_gemm_block_cap_rejects_negative(m):
+    L = m.lib()
+    assert m.STATUS[L.moe_set_gemm_max_blocks(-1)] == "MOE_ERR_INVALID_ARG"
+    assert L.moe_set_gemm_max_blocks(0) == m.MOE_OK

@@ -61,6 +61,8 @@ def closed_forms(tmp_path_factory):
              "      for (int t = 0; t < nk - 1; ++t)",
              '        std::printf("W %d %d %d %d %d %d %d\\n", c[0], c[1], c[2], c[3], nk, t,',
              "                    moe::sched_loads_after(t, nk, c[0], c[1], c[2], c[3]));",
+             '      std::printf("S %d %d %d %d %d\\n", c[0], c[1], c[2], c[3],',
+             "                  moe::sched_steady_loads(c[0], c[1], c[2], c[3]));",
              "    }"]
     lines.append("  return 0;\n}")
     src.write_text("\n".join(lines))
@@ -135,3 +137,24 @@ def test_xcd_plan_covers_every_tile_once(tmp_path):
                     assert windows == [8 * r + b % 8 for r in range(len(ts))], (G, total, b)
                 else:
                     assert all(w2 - w1 == 1 for w1, w2 in zip(windows, windows[1:])), (G, total, b)
+
+
+def test_refilling_stages_wait_the_steady_count(closed_forms):
+    """A stage t that refills (t + min(NA, NW) < nk) waits with the rings'
+    fixed count sched_steady_loads, an immediate in the kernel's steady
+    state: for rings with NA <= NW <= NA + 1 (the kernel's) it
+    must equal the closed form (itself checked against the brute-force walk)
+    at every such stage."""
+    steady = {tuple(map(int, r[1:5])): int(r[5]) for r in closed_forms if r[0] == "S"}
+    n = 0
+    for rec in closed_forms:
+        if rec[0] != "W":
+            continue
+        na, nw, la, lb, nk, t, got = map(int, rec[1:])
+        if t + min(na, nw) < nk and na <= nw <= na + 1:
+            assert got == steady[(na, nw, la, lb)], (na, nw, la, lb, nk, t)
+            n += 1
+    assert n > 500
+    # the kernel's rings: 2+2, 2+3, 3+3, 3+4 buffers
+    for na, nw in ((2, 2), (2, 3), (3, 3), (3, 4)):
+        assert na <= nw <= na + 1

@@ -511,6 +511,48 @@ def test_grouped_order_many_m_tiles(name):
     say(f"[gpu] grouped order {name}: {st}")
 
 
+# The second GEMM's tail parts (the M tiles of a last, partly filled round
+# of whole tiles run as K parts, which the combine adds) at sizes the oracle
+# finishes in seconds: the GEMMs' grid is capped at 16 blocks, so two full
+# rounds take 32 tiles. d_ff = 1024 (16 K stages):
+#  * d = 512 (two feature panels), one expert of 4200 rows: 17 M tiles of
+#    256 rows, 34 tiles; two rounds and the last M tile's 2 tiles (104 rows)
+#    left, run as 8 K parts each;
+#  * d = 256 (one panel), experts of 8400, 0 and 100 rows: 34 tiles, 2 left:
+#    expert 0's last M tile (208 rows) and, past the empty expert 1, expert
+#    2's only one, run as 8 K parts each.
+TAIL_CASES = {
+    "tail_one_expert": dict(T=4200, E=2, d=512, last=None, counts=[4200, 0]),
+    "tail_across_experts": dict(T=8500, E=3, d=256, last=100, counts=[8400, 0, 100]),
+}
+
+
+@pytest.mark.parametrize("name", list(TAIL_CASES))
+def test_gemm2_tail_parts(name):
+    spec = TAIL_CASES[name]
+    w = WORKLOADS["small_bf16"].scaled(name=name, T=spec["T"], E=spec["E"], k=1, d=spec["d"],
+                                       d_ff=1024, dropless=True)
+    inp = synth.make_inputs(w, "cuda", seed=5)
+    if spec["last"] is None:
+        inp["b_r"][0] += 40.0  # every token chooses expert 0
+    else:
+        inp["b_r"][1] -= 40.0  # expert 1 is never chosen
+        # exactly `last` tokens prefer expert 2: expert 0's bias moves to the
+        # middle of the gap between the last-th and next largest margins
+        h = P.host_inputs(inp, w.dtype)
+        s = mo.router_logits(h["x"], h["W_r"], h["b_r"])
+        gap = np.sort(s[:, 2] - s[:, 0])[::-1]
+        inp["b_r"][0] += float((gap[spec["last"] - 1] + gap[spec["last"]]) / 2)
+    m = moe()
+    say(f"[gpu] tail parts {name}: GEMM grid capped at 16 blocks")
+    m.set_gemm_max_blocks(16)
+    try:
+        _, _, o, _ = P.full_parity(w, inp, cap(w), report=say)
+    finally:
+        m.set_gemm_max_blocks(0)
+    assert o["expert_counts"].tolist() == spec["counts"]
+
+
 # K stage counts 1, 2, 3 and 5 in both expert GEMMs, around the depths of the
 # token and weight stage rings (2 to 4 buffers): the short-tile kernel
 # (every expert under 256 rows: 64- and 128-row tiles) and the tall one

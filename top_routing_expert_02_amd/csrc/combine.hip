@@ -7,18 +7,19 @@
 // token's k rows of y_perm (bf16 for bf16 layers, fp32 for fp32 layers),
 // accumulates j = 0..k-1 in fp32 in that fixed order and rounds once. No
 // atomics, so the result is deterministic; a token with every assignment
-// dropped writes exact zeros. After a K-split second GEMM (the device word
-// nsplit says 2) the rows are fp32 partial sums in two buffers: a row is
-// the sum of its two partial rows, formed before the gate multiplies it.
+// dropped writes exact zeros. When the second GEMM ran some tiles as K parts
+// (device words nsplit: parts p, first split row, split row count), each
+// row from the first split row on is the sum of its p fp32 partial rows,
+// in part order, formed before the gate multiplies it.
 #include "moe_internal.h"
 
 namespace moe {
 
-// the VEC columns c.. of row `ro` (element offset) as fp32
+// the VEC columns c.. of row `ro` (element offset) as fp32; rows bf16 or fp32
 template <int VEC>
-__device__ __forceinline__ void load_row(const void* __restrict__ yp, const float* __restrict__ y2,
-                                         int mode, int64_t ro, float (&q)[VEC]) {
-  if (mode == 1) {  // bf16 rows
+__device__ __forceinline__ void load_row(const void* __restrict__ yp, bool bf16, int64_t ro,
+                                         float (&q)[VEC]) {
+  if (bf16) {
     const uint16_t* src = static_cast<const uint16_t*>(yp) + ro;
     if constexpr (VEC % 8 == 0) {
       uint4 u[VEC / 8];
@@ -43,14 +44,7 @@ __device__ __forceinline__ void load_row(const void* __restrict__ yp, const floa
   if constexpr (VEC % 4 == 0) {
 #pragma unroll
     for (int v = 0; v < VEC; v += 4) {
-      float4 a = *reinterpret_cast<const float4*>(src + v);
-      if (mode == 2) {  // two fp32 partial sums
-        const float4 b = *reinterpret_cast<const float4*>(y2 + ro + v);
-        a.x += b.x;
-        a.y += b.y;
-        a.z += b.z;
-        a.w += b.w;
-      }
+      const float4 a = *reinterpret_cast<const float4*>(src + v);
       q[v] = a.x;
       q[v + 1] = a.y;
       q[v + 2] = a.z;
@@ -58,11 +52,28 @@ __device__ __forceinline__ void load_row(const void* __restrict__ yp, const floa
     }
   } else {
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) q[v] = mode == 2 ? src[v] + y2[ro + v] : src[v];
+    for (int v = 0; v < VEC; ++v) q[v] = src[v];
   }
 }
 
-// rows: 0 fp32, 1 bf16; with y_perm2 and *nsplit == 2, fp32 pairs (mode 2)
+// the same columns of a row split in K: part 0 from y_perm (fp32 view, row
+// r), part j >= 1 from y_perm2 row (j - 1) trows + r - r_tail, added in
+// order j = 0, 1, ..
+template <int VEC>
+__device__ __forceinline__ void load_parts(const void* __restrict__ yp, const float* __restrict__ y2,
+                                           int p, int64_t r, int64_t r_tail, int64_t trows, int d, int c,
+                                           float (&q)[VEC]) {
+  load_row<VEC>(yp, false, r * d + c, q);
+  for (int j = 1; j < p; ++j) {
+    float b[VEC];
+    load_row<VEC>(y2, false, ((j - 1) * trows + r - r_tail) * d + c, b);
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) q[v] += b[v];
+  }
+}
+
+// y_perm rows bf16 (rows_bf16) or fp32; with y_perm2, nsplit = {p, r_tail,
+// trows}: rows r >= r_tail are sums of p fp32 parts when p > 1
 template <int VEC, bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y_perm, int rows_bf16,
                                                       const float* __restrict__ y_perm2,
@@ -75,7 +86,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   if (gid >= T * chunks) return;
   const int64_t t = gid / chunks;
   const int c = static_cast<int>(gid - t * chunks) * VEC;
-  const int mode = (y_perm2 != nullptr && *nsplit == 2) ? 2 : rows_bf16;
+  int p = 1, r_tail = 0, trows = 0;
+  if (y_perm2 != nullptr) {
+    p = nsplit[0];
+    r_tail = nsplit[1];
+    trows = nsplit[2];
+  }
   float acc[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
@@ -84,7 +100,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     if (row < 0) continue;
     const float g = gates[t * k + j];
     float q[VEC];
-    load_row<VEC>(y_perm, y_perm2, mode, static_cast<int64_t>(row) * d + c, q);
+    if (p > 1 && row >= r_tail)
+      load_parts<VEC>(y_perm, y_perm2, p, row, r_tail, trows, d, c, q);
+    else
+      load_row<VEC>(y_perm, rows_bf16 != 0, static_cast<int64_t>(row) * d + c, q);
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] = fmaf(g, q[v], acc[v]);
   }

@@ -55,12 +55,18 @@
 //    an expert's weights are re-read, else a contiguous range per XCD).
 //  * Ragged M: rows past an expert's end read that expert's last row and are
 //    never stored, so no tile reads outside [0, rows).
+//  * With a second output buffer (the second expert GEMM), tiles may run as
+//    K parts whose fp32 partial sums the combine adds: all tiles in two
+//    halves when the whole tiles fit in one round, or, after two or more
+//    full rounds, only the tiles of a last, partly filled round, split so
+//    that their parts fill it.
 #include "moe_internal.h"
 
 #include "gemm_schedule.h"
 
 #include <hip/hip_ext.h>
 
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -273,12 +279,27 @@ __device__ __forceinline__ float activate(float v) {
   else return v;
 }
 
-// One output tile: expert e, output rows [row0, row0 + rv) (rv valid of the
-// tile's height), features from n0; operand A's first row arow and K range
-// [k0, k0 + 64 nk); part: which K half (split launches write the second half's
-// partial sums to their own buffer).
+// One output tile: expert e, rows [row0, row0 + rv) of the grouped problem
+// (rv valid of the tile's height), features from n0; operand A's first row
+// arow and K range [k0, k0 + 64 nk); part: which K part (part 0 carries the
+// bias; parts 1.. go to the second output buffer); split: the tile is one K
+// part of several (fp32 partial sums); orow: the output row of row0 in its
+// buffer.
 struct TileInfo {
-  int e, row0, rv, n0, arow, k0, nk, part;
+  int e, row0, rv, n0, arow, k0, nk, part, orow;
+  bool split;
+};
+
+// The tiles of one launch: the first mcap M tiles (in expert-major order)
+// run whole, as units [0, dp = mcap NT) in the grouped order below; the last
+// mt M tiles (rows r_tail onward, tail_rows of them) run as p K parts of nkp
+// stages each: part j of tail M tile m (0..mt-1) and feature panel n is
+// unit dp + (j NT + n) mt + m, so the parts that share a weight panel slice
+// are neighbours. Part 0 writes fp32 sums (with the bias) at the rows' own
+// places in out (viewed as fp32); part j >= 1 writes rows
+// (j - 1) tail_rows + (row - r_tail) of out2. p = 1: no parts (mt = 0).
+struct TilePlan {
+  int mcap, nk, p, nkp, mt, r_tail, tail_rows;
 };
 
 // Epilogue cost of an fp32 output tile in K-equivalents (its stores take
@@ -298,25 +319,55 @@ struct TileInfo {
 
 constexpr int kGroupM = 6;  // M tiles per group of the tile order
 
-// s_tiles[e]: exclusive prefix over experts of their M tiles of height BM;
-// ntiles output tiles, each in K parts of nk stages (unit u covers tile
-// u mod ntiles, part u / ntiles; at most two parts).
+// s_tiles[e]: exclusive prefix over experts of their M tiles of height BM.
+// PARTS: the kernel may run K parts (else every unit is a whole tile and
+// pl.mcap is the M-tile count).
+template <bool PARTS>
 __device__ __forceinline__ TileInfo decode_tile(int u, const int* s_tiles, const int32_t* offsets,
-                                                int E, int NT, int BM, int nk, int ntiles) {
-  const int part = u >= ntiles ? 1 : 0;
-  const int tile = u - part * ntiles;
-  // expert: the largest e with s_tiles[e] * NT <= tile (experts with no
-  // rows share their successor's prefix and are skipped)
+                                                int E, int NT, int BM, const TilePlan& pl) {
+  TileInfo t;
+  const int dp = pl.mcap * NT;
+  if (PARTS && u >= dp) {
+    // a K part of a tail tile: parts outermost, then feature panels, M tiles
+    // innermost
+    const int tt = pl.mt * NT;
+    const int v = u - dp;
+    const int j = v / tt;
+    const int r = v - j * tt;
+    const int n = r / pl.mt;
+    const int gm = pl.mcap + (r - n * pl.mt);
+    // expert: the largest e with s_tiles[e] <= gm (experts with no rows
+    // share their successor's prefix and are skipped)
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_tiles[mid] <= gm) lo = mid;
+      else hi = mid - 1;
+    }
+    t.e = lo;
+    t.row0 = offsets[lo] + (gm - s_tiles[lo]) * BM;
+    t.rv = min(BM, offsets[lo + 1] - t.row0);
+    t.n0 = n * BN;
+    t.arow = t.row0;
+    t.k0 = j * pl.nkp * BK;
+    t.nk = pl.nkp;
+    t.part = j;
+    t.split = true;
+    t.orow = j == 0 ? t.row0 : (j - 1) * pl.tail_rows + (t.row0 - pl.r_tail);
+    return t;
+  }
+  // a whole tile. Expert: the largest e with min(s_tiles[e], mcap) NT <= u
+  // (experts with no rows, or all rows in the tail, are skipped)
+  auto pre = [&](int e) { return PARTS ? min(s_tiles[e], pl.mcap) : s_tiles[e]; };
   int lo = 0, hi = E - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (s_tiles[mid] * NT <= tile) lo = mid;
+    if (pre(mid) * NT <= u) lo = mid;
     else hi = mid - 1;
   }
-  TileInfo t;
   t.e = lo;
-  const int mte = s_tiles[lo + 1] - s_tiles[lo];
-  const int v = tile - s_tiles[lo] * NT;
+  const int mte = pre(lo + 1) - s_tiles[lo];
+  const int v = u - s_tiles[lo] * NT;
   // grouped order inside an expert with many M tiles: groups of kGroupM M
   // tiles, each swept over all N tiles with its M tiles innermost, so the
   // tiles one XCD runs at a time share a few token and weight panels; up to
@@ -335,9 +386,11 @@ __device__ __forceinline__ TileInfo decode_tile(int u, const int* s_tiles, const
   t.rv = min(BM, offsets[lo + 1] - t.row0);
   t.n0 = nt * BN;
   t.arow = t.row0;
-  t.k0 = part * nk * BK;
-  t.nk = nk;
-  t.part = part;
+  t.k0 = 0;
+  t.nk = pl.nk;
+  t.part = 0;
+  t.split = false;
+  t.orow = t.row0;
   return t;
 }
 
@@ -372,6 +425,8 @@ __device__ __forceinline__ TileInfo decode_tile_wg(int tile, const int* s_tiles,
   t.k0 = poff[lo];
   t.nk = (poff[lo + 1] - poff[lo]) / BK;
   t.part = 0;
+  t.split = false;
+  t.orow = t.row0;
   return t;
 }
 
@@ -459,21 +514,20 @@ __device__ __forceinline__ void tile_sources(const TileInfo& t, const uint16_t* 
 
 // Activation, conversion and stores of one wave's (32 TM) x 128 outputs (the
 // accumulators started at the bias). FULL: every row and feature of the tile
-// is in range (no per-lane checks). split: the launch splits K (kOutYperm
-// then stores fp32 partial sums).
+// is in range (no per-lane checks). A K part of a tile (t.split) stores
+// fp32 partial sums (kOutYperm); rows go to t.orow onward.
 template <int TM, int OUT, int ACT, bool FULL>
 __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], void* __restrict__ out,
-                                         const TileInfo& t, int N, int wm, int wn, int l5, int hi,
-                                         bool split) {
+                                         const TileInfo& t, int N, int wm, int wn, int l5, int hi) {
   constexpr int WM = 32 * TM;
-  const bool f32 = OUT == kOutF32 || (OUT == kOutYperm && split);
+  const bool f32 = OUT == kOutF32 || (OUT == kOutYperm && t.split);
   const int fb = wn * WN + hi * 4;  // this lane's first feature in the tile
   const int nb = t.n0 + fb;
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
     const int m = wm * WM + j * 32 + l5;
     if (!FULL && m >= t.rv) continue;
-    const int64_t orow = static_cast<int64_t>(t.row0 + m) * N + nb;
+    const int64_t orow = static_cast<int64_t>(t.orow + m) * N + nb;
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
 #pragma unroll
@@ -501,21 +555,22 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], void* __
   }
 }
 
-// The persistent tile loop for tiles of BM = 64 TM rows: tiles tile,
-// tile + stride, ... below end. lds: the two stage rings; s_tiles: the M-tile
-// prefix for this height; s_bias: two slices.
+// The persistent tile loop for tiles of BM = 64 TM rows: units tile,
+// tile + stride, ... below end, then tile2, tile2 + stride2, ... below end2.
+// lds: the two stage rings; s_tiles: the M-tile prefix for this height;
+// s_bias: two slices.
 // WG: weight-gradient tiles (decode_tile_wg; offsets holds the padded K
-// offsets, M the rows of C per expert); else expert-FFN tiles of nkl stages
-// each: ntiles output tiles, and total = ntiles (whole K) or 2 ntiles (two K
-// halves; the second half's partial sums go to out2, without bias).
+// offsets, M the rows of C per expert); else expert-FFN units as the plan
+// pl numbers them (decode_tile: whole tiles, then K parts of tail tiles,
+// whose parts 1.. go to out2 without bias).
 template <int TM, int OUT, int ACT, bool WG, bool WT = false>
 __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const int32_t* __restrict__ row_idx,
                                           const uint16_t* __restrict__ W, const float* __restrict__ bias,
                                           void* __restrict__ out, void* __restrict__ out2,
                                           const int32_t* __restrict__ offsets,
-                                          int E, int N, int nkl, int lda, int64_t w_estride, int M,
+                                          int E, int N, const TilePlan& pl, int lda, int64_t w_estride, int M,
                                           char* lds, const int* s_tiles, float (*s_bias)[BN], int tile,
-                                          int stride, int end, int total, int ntiles, int NT) {
+                                          int stride, int end, int tile2, int stride2, int end2, int NT) {
   constexpr int BM = 64 * TM;
   constexpr int WM = BM / 2;         // tokens per wave
   constexpr int A_BYTES = BM * ROWB;  // one token stage
@@ -526,8 +581,12 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
   static_assert(LB == 8, "stage_w_b8 issues a weight stage");
   constexpr int NA = a_stages<TM>();
   constexpr int NW = w_stages<TM>();
+  // K parts only for y_perm outputs (the second expert GEMM): other kernels
+  // keep the plain unit sequence and decode (fewer live registers)
+  constexpr bool PARTS = !WG && OUT == kOutYperm;
   constexpr int NMIN = NA < NW ? NA : NW;  // refills run while stage t + NMIN exists
   constexpr int NMAX = NA > NW ? NA : NW;
+  static_assert(NA <= NW && NW <= NA + 1, "sched_steady_loads holds for rings with NA <= NW <= NA + 1");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -542,9 +601,24 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
 #pragma unroll
   for (int s = 0; s < 4; ++s) fo[s] = l5 * ROWB + 16 * ((2 * s + hi) ^ key);
   const int drow = lane >> 3, dpos = lane & 7;
+  // a unit's tile is the same for the whole wave: its fields go to scalar
+  // registers (the DMA asm takes its base addresses as SGPRs)
   auto decode = [&](int tl) {
-    if constexpr (WG) return decode_tile_wg(tl, s_tiles, offsets, E, NT, BM, M);
-    else return decode_tile(tl, s_tiles, offsets, E, NT, BM, nkl, ntiles);
+    TileInfo t;
+    if constexpr (WG) t = decode_tile_wg(tl, s_tiles, offsets, E, NT, BM, M);
+    else t = decode_tile<PARTS>(tl, s_tiles, offsets, E, NT, BM, pl);
+    if constexpr (PARTS) {
+    t.e = __builtin_amdgcn_readfirstlane(t.e);
+    t.row0 = __builtin_amdgcn_readfirstlane(t.row0);
+    t.rv = __builtin_amdgcn_readfirstlane(t.rv);
+    t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
+    t.arow = __builtin_amdgcn_readfirstlane(t.arow);
+    t.k0 = __builtin_amdgcn_readfirstlane(t.k0);
+    t.nk = __builtin_amdgcn_readfirstlane(t.nk);
+    t.part = __builtin_amdgcn_readfirstlane(t.part);
+    t.orow = __builtin_amdgcn_readfirstlane(t.orow);
+    }
+    return t;
   };
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
   const uint32_t w_base = lds_base + NA * A_BYTES;
@@ -602,12 +676,11 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
   tile_sources<LA, LB, WT>(cur, A, row_idx, W, N, lda, w_estride, wave, drow, dpos, Abase, Wbase, aoffs,
                            boffs);
   prologue0(cur, par);
-  prologue1(WG ? cur.nk : nkl);
+  prologue1((WG || PARTS) ? cur.nk : pl.nk);
 
   for (;;) {
-    // K stages of this tile (cur moves on before its epilogue); the same for
-    // every expert-FFN tile
-    const int nk = WG ? cur.nk : nkl;
+    // K stages of this tile (cur moves on before its epilogue)
+    const int nk = (WG || PARTS) ? cur.nk : pl.nk;
 
     // stage 0 and the bias slice have landed (the later prologue stages may
     // still be in flight)
@@ -645,7 +718,11 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     }
 
     TileInfo done = cur;
-    const int next = tile + stride;
+    // the next unit: on in this sequence, else the first of the second
+    int next = tile + stride;
+    const bool second = PARTS && next >= end;
+    if (second) next = tile2;
+    const bool more = second ? tile2 < end2 : next < end;
 #pragma unroll
     for (int i = 0; i < LA; ++i) vo[i] = aoffs[i];
 #pragma unroll
@@ -695,8 +772,11 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
       kstep(wf1, tf1, wf0, tf0, sa, sw, 2);
       kstep(wf0, tf0, wf1, tf1, sa, sw, 3);
       // stage t+1 has landed and every wave has read its last fragments of
-      // stage t
-      wait_vm(loads_after<NA, NW, LA, LB>(t, nk));
+      // stage t (a refilling stage waits for the rings' fixed count)
+      if constexpr (decltype(rf)::value)
+        wait_vm_n<sched_steady_loads(NA, NW, LA, LB)>();
+      else
+        wait_vm(loads_after<NA, NW, LA, LB>(t, nk));
       __syncthreads();
       const int an = (ai + 1 == NA) ? 0 : ai + 1;
       const int wnx = (wi + 1 == NW) ? 0 : wi + 1;
@@ -736,7 +816,7 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     // every wave has read all of its fragments: all buffers are free, and the
     // next tile's stage 0 loads during this tile's last MFMAs and epilogue
     __syncthreads();
-    if (next < end) {
+    if (more) {
       cur = decode(next);
       tile_sources<LA, LB, WT>(cur, A, row_idx, W, N, lda, w_estride, wave, drow, dpos, Abase, Wbase,
                                aoffs, boffs);
@@ -748,13 +828,17 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     // features 8q + 4*hi + {0..3} of each 32-feature tile i
     const bool full_tile = done.rv == BM && done.n0 + BN <= N;
     void* dst = done.part ? out2 : out;
-    const bool split = !WG && total != ntiles;
-    if (full_tile) epilogue<TM, OUT, ACT, true>(acc, dst, done, N, wm, wn, l5, hi, split);
-    else epilogue<TM, OUT, ACT, false>(acc, dst, done, N, wm, wn, l5, hi, split);
-    if (next >= end) break;
+    if (full_tile) epilogue<TM, OUT, ACT, true>(acc, dst, done, N, wm, wn, l5, hi);
+    else epilogue<TM, OUT, ACT, false>(acc, dst, done, N, wm, wn, l5, hi);
+    if (!more) break;
     // the next tile's later prologue stages, after this tile's stores
-    prologue1(WG ? cur.nk : nkl);
+    prologue1((WG || PARTS) ? cur.nk : pl.nk);
     tile = next;
+    if (second) {
+      stride = stride2;
+      end = end2;
+      tile2 = end2;
+    }
     par ^= 1;
   }
 }
@@ -766,12 +850,15 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
 // rows: decode batches, many experts). Two instantiations rather than one
 // kernel with all four: each keeps its own register allocation.
 // OUT: kOutBf16 (after ACT), kOutF32, or kOutYperm (no activation; bf16
-// unless split). out2 (kOutF32 or kOutYperm only, else null): with it, the
-// schedule may split K in two halves when that fills more of the chip (few
-// output tiles, long K); the first half (with bias) goes to out, the second
-// to out2, both as fp32 partial sums, and the number of parts (1 or 2) to
-// *nsplit (when not null). With kOutYperm, out then holds bf16 results when
-// *nsplit is 1 and fp32 partial sums (out + out2 = the product) when it is 2.
+// for whole tiles). out2 (kOutYperm only, else null; cap_rows
+// rows of N fp32): with it, the schedule may run tiles as K parts (TilePlan:
+// all tiles in two halves, or the last M tiles in p parts). nsplit (when
+// not null) receives p (1: no parts), the first row of the split tiles,
+// r_tail, and their row count, tail_rows. With kOutYperm, a row r < r_tail
+// of out is then a bf16 result, and a row r >= r_tail is the sum, in order,
+// of out's fp32 row r (out viewed as fp32: its byte range lies past every
+// bf16 row below r_tail) and out2's rows (j - 1) tail_rows + r - r_tail,
+// j = 1 .. p - 1.
 // WT: each W_e is stored [K, N] (K-major, as W^T of the usual [N, K]); the
 // weight stages are loaded row by row of K and read with transposing LDS
 // reads.
@@ -781,7 +868,7 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
                               const uint16_t* __restrict__ W,
                               const float* __restrict__ bias, void* __restrict__ out,
                               void* __restrict__ out2, int32_t* __restrict__ nsplit,
-                              const int32_t* __restrict__ offsets, int E, int N, int K) {
+                              const int32_t* __restrict__ offsets, int E, int N, int K, int cap_rows) {
   // the body uses gfx950 builtins only: the host pass needs just the signature
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __attribute__((aligned(1024))) char lds[SHORT ? kLdsShort : kLdsTall];
@@ -797,166 +884,169 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
   const int per = (E + 255) / 256;
   const int eb = tid * per;
   const int b = blockIdx.x;
-  // this block's tiles: first, first + stride, ... below end (see
-  // sched_xcd_plan; reread: some expert has more M tiles than one group of
-  // the tile order holds, so its weight panels are read more than once)
-  int first = b, stride = Gd, end = 0;
-  auto xcd_plan = [&](int total, bool reread) {
-    sched_xcd_plan(b, Gd, total, reread, first, stride, end);
-  };
   const int64_t wes = static_cast<int64_t>(N) * K;
-  // K parts allowed: two when out2 is given and K splits into whole stages,
-  // and only for a schedule whose whole tiles fit in one round (few rows,
-  // long K: decode batches). With more tiles a split only evens out the
-  // last round, and its fp32 partial sums (twice the stores, and twice the
-  // combine's reads in fp32) cost more than that: the skewed layer's second
-  // GEMM (352 tiles) split ran no faster and its combine took 25.8 µs
-  // instead of 12.7.
-  const int smax = (out2 != nullptr && (K / BK) % 2 == 0) ? 2 : 1;
-  // work of one block: rounds of units x (rows x (K per part + epilogue)),
-  // rows = the tile's MFMA rows plus a share for its weight panel
-  auto cost = [&](int64_t tiles, int rows, int S) {
-    const int64_t rounds = (tiles * S + Gd - 1) / Gd;
-    return rounds * rows * static_cast<int64_t>(K / S + kEpiK);
-  };
-  auto may_split = [&](int64_t tiles, int S) { return S == 1 || tiles <= static_cast<int64_t>(Gd); };
-  // the same for the tall heights h, the weight panel's share charged to the
-  // K loop only (the epilogue stores h rows)
-  auto cost_tall = [&](int64_t tiles, int h, int S) {
-    const int64_t rounds = (tiles * S + Gd - 1) / Gd;
-    return rounds * ((h + kTallShare) * static_cast<int64_t>(K / S) + static_cast<int64_t>(h) * kEpiK);
-  };
-  if constexpr (!SHORT) {
-    // ---- device-side schedule. Both tile heights are counted, each whole
-    // and (when allowed) split in K; the choice whose units need the least
-    // block work (cost above) runs: the taller height, then the unsplit one,
-    // on a tie.
-    int c256 = 0, c192 = 0;
-    for (int e = eb; e < min(E, eb + per); ++e) {
-      const int n = offsets[e + 1] - offsets[e];
-      c256 += (n + 255) / 256;
-      c192 += (n + 191) / 192;
-    }
-    s_part[0][tid] = c256;
-    s_part[1][tid] = c192;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const int a0 = (tid >= off) ? s_part[0][tid - off] : 0;
-      const int a1 = (tid >= off) ? s_part[1][tid - off] : 0;
-      __syncthreads();
-      s_part[0][tid] += a0;
-      s_part[1][tid] += a1;
-      __syncthreads();
-    }
-    bool tall = true;
-    int S = 1;
-    int64_t best = -1;
-    for (int sp = 1; sp <= smax; ++sp)
-      for (int q = 0; q < 2; ++q) {
-        const int64_t tiles = static_cast<int64_t>(s_part[q][255]) * NT;
-        if (!may_split(tiles, sp)) continue;
-        const int64_t c = cost_tall(tiles, q == 0 ? 256 : 192, sp);
-        if (best < 0 || c < best) {
-          best = c;
-          tall = q == 0;
-          S = sp;
-        }
-      }
-    const int BMs = tall ? 256 : 192;
-    int many = 0;  // an expert of this thread has more than 2 kGroupM M tiles
-    {
-      const int sel = tall ? 0 : 1;
-      int run = s_part[sel][tid] - (tall ? c256 : c192);
-      for (int e = eb; e < min(E, eb + per); ++e) {
-        s_tiles[e] = run;
-        const int mt = (offsets[e + 1] - offsets[e] + BMs - 1) / BMs;
-        many |= mt > 2 * kGroupM;
-        run += mt;
-      }
-      if (tid == 255) s_tiles[E] = s_part[sel][255];
-    }
-    const bool reread = __syncthreads_or(many) != 0;
-    if (nsplit != nullptr && b == 0 && tid == 0) *nsplit = S;
-    const int ntiles = s_tiles[E] * NT;
-    const int total = ntiles * S;
-    const int nkl = K / BK / S;
-    xcd_plan(total, reread);
-    if (first >= end) return;
-    const int tile = first;
-    if (tall)
-      tile_loop<4, OUT, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
-                                        lds, s_tiles, s_bias, tile, stride, end, total, ntiles, NT);
+  const int nks = K / BK;
+  // ---- device-side schedule. Tile heights: 256 or 192 (tall), 192, 128 or
+  // 64 (short). For each height the M tiles per expert are counted and
+  // prefix-summed; then every plan is costed as the work of the busiest
+  // block, in row-K units: rounds x (rows x K + rows x kEpiK), where rows
+  // are the tile's MFMA rows plus a share for the weight panel it streams
+  // whole (kTallShare, charged to the K loop only, in the tall kernel; 64
+  // rows in the short one).
+  constexpr int NQ = SHORT ? 3 : 2;
+  constexpr int kH[3] = {SHORT ? 192 : 256, SHORT ? 128 : 192, 64};
+  auto unit_cost = [&](int h, int p) {  // one tile of height h, K split in p parts
+    if constexpr (SHORT)
+      return static_cast<int64_t>(h + 64) * (nks / p * BK + kEpiK);
     else
-      tile_loop<3, OUT, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
-                                        lds, s_tiles, s_bias, tile, stride, end, total, ntiles, NT);
-  } else {
-    // ---- the same with heights 192, 128 and 64, whole or split in K: the
-    // least cost with h + 64 rows per tile of height h (its MFMA rows plus a
-    // fixed share for its weight panel, which short tiles stream with fewer
-    // MFMAs); the taller height, then the unsplit one, on a tie
-    constexpr int kH[3] = {192, 128, 64};
-    int c[3] = {0, 0, 0};
-    for (int e = eb; e < min(E, eb + per); ++e) {
-      const int n = offsets[e + 1] - offsets[e];
+      return static_cast<int64_t>(h + kTallShare) * (nks / p * BK) + static_cast<int64_t>(h) * kEpiK;
+  };
+  int c[NQ];
 #pragma unroll
-      for (int q = 0; q < 3; ++q) c[q] += (n + kH[q] - 1) / kH[q];
-    }
+  for (int q = 0; q < NQ; ++q) c[q] = 0;
+  for (int e = eb; e < min(E, eb + per); ++e) {
+    const int n = offsets[e + 1] - offsets[e];
 #pragma unroll
-    for (int q = 0; q < 3; ++q) s_part[q][tid] = c[q];
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      int a[3];
-#pragma unroll
-      for (int q = 0; q < 3; ++q) a[q] = (tid >= off) ? s_part[q][tid - off] : 0;
-      __syncthreads();
-#pragma unroll
-      for (int q = 0; q < 3; ++q) s_part[q][tid] += a[q];
-      __syncthreads();
-    }
-    int sel = 0, S = 1;
-    int64_t best = -1;
-    for (int sp = 1; sp <= smax; ++sp)
-#pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        const int64_t tiles = static_cast<int64_t>(s_part[q][255]) * NT;
-        if (!may_split(tiles, sp)) continue;
-        const int64_t c = cost(tiles, kH[q] + 64, sp);
-        if (best < 0 || c < best) {
-          best = c;
-          sel = q;
-          S = sp;
-        }
-      }
-    const int BMs = sel == 0 ? 192 : (sel == 1 ? 128 : 64);
-    int many = 0;  // an expert of this thread has more than 2 kGroupM M tiles
-    {
-      int run = s_part[sel][tid] - c[sel];
-      for (int e = eb; e < min(E, eb + per); ++e) {
-        s_tiles[e] = run;
-        const int mt = (offsets[e + 1] - offsets[e] + BMs - 1) / BMs;
-        many |= mt > 2 * kGroupM;
-        run += mt;
-      }
-      if (tid == 255) s_tiles[E] = s_part[sel][255];
-    }
-    const bool reread = __syncthreads_or(many) != 0;
-    if (nsplit != nullptr && b == 0 && tid == 0) *nsplit = S;
-    const int ntiles = s_tiles[E] * NT;
-    const int total = ntiles * S;
-    const int nkl = K / BK / S;
-    xcd_plan(total, reread);
-    if (first >= end) return;
-    const int tile = first;
-    if (sel == 0)
-      tile_loop<3, OUT, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
-                                        lds, s_tiles, s_bias, tile, stride, end, total, ntiles, NT);
-    else if (sel == 1)
-      tile_loop<2, OUT, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
-                                        lds, s_tiles, s_bias, tile, stride, end, total, ntiles, NT);
-    else
-      tile_loop<1, OUT, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, nkl, K, wes, 0,
-                                        lds, s_tiles, s_bias, tile, stride, end, total, ntiles, NT);
+    for (int q = 0; q < NQ; ++q) c[q] += (n + kH[q] - 1) / kH[q];
   }
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) s_part[q][tid] = c[q];
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    int a[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) a[q] = (tid >= off) ? s_part[q][tid - off] : 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) s_part[q][tid] += a[q];
+    __syncthreads();
+  }
+  // Plans: whole tiles of one height (the taller first, so it wins a tie),
+  // then, with out2, K parts:
+  //  * every tile in two K halves, when the whole tiles fit in one round
+  //    (few rows, long K: decode batches);
+  //  * after at least two rounds of whole tiles, the last M tiles (enough
+  //    of them, with all their feature panels, to hold the tiles that would
+  //    run in a last, partly filled round) in p K parts, as many as still
+  //    fit in one round: the last round then runs short parts on every
+  //    block instead of whole tiles on a few. On the 16384-token layer's
+  //    second GEMM: 8 rounds of 256 whole tiles and 64 tiles left, which
+  //    run as 256 quarter tiles.
+  //  A split only to even out one round after a single round of whole
+  //  tiles is not offered: on the skewed layer's second GEMM (352 tiles,
+  //  K = 1024) the parts ran no faster and the combine, which adds their
+  //  fp32 rows, took 25.8 µs instead of 12.7.
+  int sel = 0, P = 1, MT = 0;
+  int64_t best = -1;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int64_t tiles = static_cast<int64_t>(s_part[q][255]) * NT;
+    const int64_t cq = (tiles + Gd - 1) / Gd * unit_cost(kH[q], 1);
+    if (best < 0 || cq < best) {
+      best = cq;
+      sel = q;
+    }
+  }
+  if (OUT == kOutYperm && out2 != nullptr) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int mtq = s_part[q][255];
+      const int64_t tiles = static_cast<int64_t>(mtq) * NT;
+      int p = 1, mt = 0;
+      int64_t cq = -1;
+      if (tiles > 0 && tiles <= Gd) {
+        if (nks % 2 == 0) {
+          p = 2;
+          mt = mtq;
+          cq = (2 * tiles + Gd - 1) / Gd * unit_cost(kH[q], 2);
+        }
+      } else if (tiles > Gd) {
+        const int64_t full = tiles / Gd, rest = tiles % Gd;
+        if (full >= 2 && rest > 0) {
+          mt = static_cast<int>((rest + NT - 1) / NT);
+          for (int pp = Gd / (mt * NT); pp >= 2; --pp)
+            if (nks % pp == 0 && static_cast<int64_t>(pp - 1) * mt * kH[q] <= cap_rows) {
+              p = pp;
+              break;
+            }
+          if (p > 1) cq = full * unit_cost(kH[q], 1) + unit_cost(kH[q], p);
+        }
+      }
+      if (cq >= 0 && cq < best) {
+        best = cq;
+        sel = q;
+        P = p;
+        MT = mt;
+      }
+    }
+  }
+  const int BMs = kH[sel];
+  int many = 0;  // an expert of this thread has more than 2 kGroupM M tiles
+  {
+    int run = s_part[sel][tid] - c[sel];
+    for (int e = eb; e < min(E, eb + per); ++e) {
+      s_tiles[e] = run;
+      const int mt = (offsets[e + 1] - offsets[e] + BMs - 1) / BMs;
+      many |= mt > 2 * kGroupM;
+      run += mt;
+    }
+    if (tid == 255) s_tiles[E] = s_part[sel][255];
+  }
+  // (also the barrier after s_tiles)
+  const bool reread = __syncthreads_or(many) != 0;
+  TilePlan pl;
+  pl.mcap = s_tiles[E] - MT;
+  pl.nk = nks;
+  pl.p = P;
+  pl.nkp = nks / P;
+  pl.mt = MT;
+  pl.r_tail = offsets[E];
+  if (MT > 0) {
+    int lo = 0, hi = E - 1;  // the expert of M tile mcap
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_tiles[mid] <= pl.mcap) lo = mid;
+      else hi = mid - 1;
+    }
+    pl.r_tail = offsets[lo] + (pl.mcap - s_tiles[lo]) * BMs;
+  }
+  pl.tail_rows = offsets[E] - pl.r_tail;
+  if (nsplit != nullptr && b == 0 && tid == 0) {
+    nsplit[0] = P;
+    nsplit[1] = pl.r_tail;
+    nsplit[2] = pl.tail_rows;
+  }
+  // this block's units (sched_xcd_plan; reread: some expert has more M
+  // tiles than one group of the tile order holds, so its weight panels are
+  // read more than once): whole tiles first, then tail parts
+  const int dp = pl.mcap * NT;
+  const int nparts = P > 1 ? P * MT * NT : 0;
+  int first, stride, end, first2, stride2, end2;
+  sched_xcd_plan(b, Gd, dp, reread, first, stride, end);
+  sched_xcd_plan(b, Gd, nparts, reread, first2, stride2, end2);
+  first2 += dp;
+  end2 += dp;
+  if (first >= end) {
+    if (first2 >= end2) return;
+    first = first2;
+    stride = stride2;
+    end = end2;
+    first2 = end2;
+  }
+#define MOE_TILE_LOOP(TMV)                                                                                \
+  tile_loop<TMV, OUT, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, pl, K, wes, 0, lds, \
+                                      s_tiles, s_bias, first, stride, end, first2, stride2, end2, NT)
+  // each kernel instantiates only its own heights (separate register
+  // allocations)
+  if constexpr (!SHORT) {
+    if (BMs == 256) MOE_TILE_LOOP(4);
+    else MOE_TILE_LOOP(3);
+  } else {
+    if (BMs == 192) MOE_TILE_LOOP(3);
+    else if (BMs == 128) MOE_TILE_LOOP(2);
+    else MOE_TILE_LOOP(1);
+  }
+#undef MOE_TILE_LOOP
 #endif
 }
 
@@ -1004,35 +1094,45 @@ void grouped_wgrad_bf16_kernel(const uint16_t* __restrict__ At, const uint16_t* 
   const int b = blockIdx.x;
   const int tile = (Gd % 8 == 0) ? (b % 8) * (Gd / 8) + b / 8 : b;
   if (tile >= total) return;
-  tile_loop<4, kOutF32, kActNone, true>(At, nullptr, Bt, nullptr, C, nullptr, poff, E, N, 0, lda, 0, M,
-                                     lds, s_tiles, s_bias, tile, Gd, total, total, total, NT);
+  const TilePlan pl{};  // unused by weight-gradient tiles
+  tile_loop<4, kOutF32, kActNone, true>(At, nullptr, Bt, nullptr, C, nullptr, poff, E, N, pl, lda, 0, M,
+                                     lds, s_tiles, s_bias, tile, Gd, total, total, 1, total, NT);
 #endif
 }
 
 namespace {
 
+std::atomic<int> g_max_blocks{0};  // 0: no cap
+
+// persistent blocks for one GEMM launch: one per CU, at most the cap
 int cu_count() {
   static int cached[64] = {0};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cached[dev] = n;
+  int n = 256;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    if (cached[dev] == 0) {
+      int c = 0;
+      if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+        c = 256;
+      cached[dev] = c;
+    }
+    n = cached[dev];
   }
-  return cached[dev];
+  const int cap = g_max_blocks.load(std::memory_order_relaxed);
+  return cap > 0 && cap < n ? cap : n;
 }
 
 }  // namespace
+
+void set_gemm_max_blocks(int blocks) { g_max_blocks.store(blocks, std::memory_order_relaxed); }
 
 hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uint16_t* W,
                             const float* bias, void* out, float* out2, int32_t* nsplit,
                             int out_mode, int act, const int32_t* offsets, int E, int N, int K,
                             int64_t max_rows, int max_rows_per_expert, hipStream_t s) {
   if (max_rows <= 0) return hipSuccess;
-  // a split needs a linear output kept as fp32 partial sums
-  if (out_mode == kGemmOutBf16 || act != kActNone) out2 = nullptr;
+  // K parts: y_perm outputs only (the combine adds the parts)
+  if (out_mode != kGemmOutYperm) out2 = nullptr;
   const int smax = (out2 != nullptr && (K / BK) % 2 == 0) ? 2 : 1;
   // short tiles when no expert can fill a 256-row tile
   const bool shorter = max_rows_per_expert < 256;
@@ -1041,14 +1141,15 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uin
   const int slots = cu_count();
   const int64_t tiles = mt_bound * ((N + BN - 1) / BN) * smax;
   const unsigned grid = static_cast<unsigned>(tiles < slots ? tiles : slots);
+  const int cap = static_cast<int>(max_rows < INT32_MAX ? max_rows : INT32_MAX);  // rows of out2
 #define MOE_GEMM(OM, AC)                                                                              \
   do {                                                                                               \
     if (shorter)                                                                                     \
       klaunch(grouped_gemm_bf16_kernel<OM, AC, true>, dim3(grid), dim3(256), 0, s, A, row_idx, W, bias, \
-              out, static_cast<void*>(out2), nsplit, offsets, E, N, K);                                \
+              out, static_cast<void*>(out2), nsplit, offsets, E, N, K, cap);                           \
     else                                                                                             \
       klaunch(grouped_gemm_bf16_kernel<OM, AC, false>, dim3(grid), dim3(256), 0, s, A, row_idx, W,     \
-              bias, out, static_cast<void*>(out2), nsplit, offsets, E, N, K);                          \
+              bias, out, static_cast<void*>(out2), nsplit, offsets, E, N, K, cap);                     \
   } while (0)
   if (out_mode == kGemmOutYperm) MOE_GEMM(kOutYperm, kActNone);
   else if (out_mode == kGemmOutF32) MOE_GEMM(kOutF32, kActNone);
@@ -1070,10 +1171,10 @@ hipError_t launch_gemm_bf16_wt(const uint16_t* A, const int32_t* row_idx, const 
   const unsigned grid = static_cast<unsigned>(tiles < slots ? tiles : slots);
   if (shorter)
     grouped_gemm_bf16_kernel<kOutF32, kActNone, true, true><<<grid, 256, 0, s>>>(
-        A, row_idx, W, bias, out, nullptr, nullptr, offsets, E, N, K);
+        A, row_idx, W, bias, out, nullptr, nullptr, offsets, E, N, K, 0);
   else
     grouped_gemm_bf16_kernel<kOutF32, kActNone, false, true><<<grid, 256, 0, s>>>(
-        A, row_idx, W, bias, out, nullptr, nullptr, offsets, E, N, K);
+        A, row_idx, W, bias, out, nullptr, nullptr, offsets, E, N, K, 0);
   return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@
 namespace moe {
 
 // loads of prologue entries 0 .. p - 1
-MOE_HD inline int sched_prefix(int p, int NA, int NW, int LA, int LB) {
+MOE_HD constexpr int sched_prefix(int p, int NA, int NW, int LA, int LB) {
   int n = 0;
   for (int q = 0; q < p; ++q) n += (q < NA ? LA : 0) + (q < NW ? LB : 0);
   return n;
@@ -37,7 +37,7 @@ MOE_HD inline int sched_prefix(int p, int NA, int NW, int LA, int LB) {
 
 // issue position (1-based count of loads up to and including it) of the
 // last load of token stage s (weight = false) or weight stage s
-MOE_HD inline int sched_pos(bool weight, int s, int nk, int NA, int NW, int LA, int LB) {
+MOE_HD constexpr int sched_pos(bool weight, int s, int nk, int NA, int NW, int LA, int LB) {
   const int nmax = NA > NW ? NA : NW;
   const int entries = nmax < nk ? nmax : nk;
   const int N = weight ? NW : NA;
@@ -50,7 +50,7 @@ MOE_HD inline int sched_pos(bool weight, int s, int nk, int NA, int NW, int LA, 
 }
 
 // loads issued after stage t + 1's last load, at the wait at the end of stage t
-MOE_HD inline int sched_loads_after(int t, int nk, int NA, int NW, int LA, int LB) {
+MOE_HD constexpr int sched_loads_after(int t, int nk, int NA, int NW, int LA, int LB) {
   const int nmax = NA > NW ? NA : NW;
   const int nmin = NA < NW ? NA : NW;
   const int entries = nmax < nk ? nmax : nk;
@@ -60,6 +60,16 @@ MOE_HD inline int sched_loads_after(int t, int nk, int NA, int NW, int LA, int L
   const int a = sched_pos(false, t + 1, nk, NA, NW, LA, LB);
   const int w = sched_pos(true, t + 1, nk, NA, NW, LA, LB);
   return issued - (a > w ? a : w);
+}
+
+// The same wait at any stage t that refills (t + min(NA, NW) < nk), for
+// rings with NA <= NW <= NA + 1 (the kernel's): every refill
+// group issues the same loads, so the count depends on the rings alone (a
+// host test checks it against sched_loads_after at every such t). The
+// kernel uses it as an immediate in its steady state. (With other depths
+// the count changes over the first stages.)
+MOE_HD constexpr int sched_steady_loads(int NA, int NW, int LA, int LB) {
+  return sched_loads_after(0, 2 * (NA + NW) + 2, NA, NW, LA, LB);
 }
 
 // loads of prologue entries 1 .. (issued after the previous tile's stores)

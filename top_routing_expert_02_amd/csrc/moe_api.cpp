@@ -110,7 +110,7 @@ Layout layout_of(const moe_config& c) {
   L.y_perm = take(R * c.d * 4);
   // the second K half's partial sums of a split second GEMM (bf16 layers)
   L.y_perm2 = take(c.dtype == MOE_BF16 ? R * c.d * 4 : 0);
-  L.nsplit = take(4);
+  L.nsplit = take(3 * 4);  // parts, first split row, split rows (second GEMM)
   // state of the general dispatch (priority order, re-routing rounds); small
   // next to h, so every layout has it and moe_dispatch_reroute works for any
   // config
@@ -429,6 +429,12 @@ int32_t moe_workspace_size(const moe_config* cfg, size_t* bytes) {
   MOE_TRY(check_cfg(cfg));
   if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
   *bytes = layout_of(*cfg).total;
+  return MOE_OK;
+}
+
+int32_t moe_set_gemm_max_blocks(int32_t blocks) {
+  if (blocks < 0) return MOE_ERR_INVALID_ARG;
+  set_gemm_max_blocks(blocks);
   return MOE_OK;
 }
 

@@ -219,10 +219,15 @@ hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int
 // row_idx (nullable): row r of the grouped problem is row row_idx[r] of A.
 // out_mode: kGemmOutBf16 (bf16 after act), kGemmOutF32 (fp32, no act), or
 // kGemmOutYperm (no act; bf16 when the launch runs whole tiles).
-// out2 (nullable; fp32 and y_perm modes only): a second fp32 [rows,N]
-// buffer that lets the kernel split K in two; it then writes fp32 partial
-// sums of the two halves to out and out2 and 2 to *nsplit (1 when it did
-// not split), so the result is out + out2 when *nsplit == 2.
+// out2 (nullable; y_perm mode only): a second fp32 [max_rows,N]
+// buffer that lets the kernel run tiles as K parts; nsplit (3 words) then
+// receives p, r_tail and tail_rows: with p > 1, rows r >= r_tail of the
+// result are the sum, in order j = 0 .. p-1, of part 0 = out's fp32 row r
+// (out viewed as fp32 [max_rows, N]; in y_perm mode rows below r_tail stay
+// bf16, which end below that byte range) and part j = out2's row
+// (j-1) tail_rows + r - r_tail.
+// cap on the persistent GEMMs' grid (0: one block per CU)
+void set_gemm_max_blocks(int blocks);
 constexpr int kGemmOutBf16 = 0;
 constexpr int kGemmOutF32 = 1;
 constexpr int kGemmOutYperm = 2;
@@ -243,8 +248,8 @@ hipError_t launch_gemm_f32(const float* A, const int32_t* row_idx, const float* 
 
 // y[t] = sum_j gates[t,j] y_perm[row_of[t,j]] (kept j only), rounded once;
 // y_perm rows are bf16 (yperm_bf16) or fp32; with y_perm2 (nullable) and
-// *nsplit == 2 they are instead the fp32 sums y_perm + y_perm2 (a K-split
-// second GEMM's two partial sums, added first)
+// nsplit[0] = p > 1, rows r >= nsplit[1] are instead the sums of the second
+// GEMM's p fp32 partial rows (launch_gemm_bf16), added first
 hipError_t launch_combine(const void* y_perm, bool yperm_bf16, const float* y_perm2,
                           const int32_t* nsplit, const int32_t* row_of, const float* gates,
                           int64_t T, int k, int d, bool out_bf16, void* y, hipStream_t s);

@@ -27,7 +27,7 @@ STAGE_NAMES = ["route", "dispatch", "gemm1", "gemm2", "combine"]
 EXPORTED = ["moe_capacity", "moe_candidates", "moe_max_rows", "moe_workspace_size", "moe_route",
             "moe_dispatch", "moe_dispatch_reroute", "moe_expert_ffn", "moe_combine",
             "moe_layer_forward", "moe_layer_forward_noalloc", "moe_load_stats", "moe_backward_workspace_size",
-            "moe_layer_backward", "moe_status_string"]
+            "moe_layer_backward", "moe_set_gemm_max_blocks", "moe_status_string"]
 STAT_NAMES = ["dropped", "overflow_ratio", "max_over_mean_load", "padding_ratio", "load_entropy",
               "kept_variance", "aux_loss", "kept_rows"]
 
@@ -82,6 +82,7 @@ def lib():
         L.moe_backward_workspace_size.argtypes = [CFG, ctypes.POINTER(SZ)]
         L.moe_layer_backward.argtypes = [CFG, P, P, P, P, P, P, P, ctypes.POINTER(MoeRouteInfo), P,
                                          ctypes.c_float, P, P, P, P, P, P, P, P, SZ, P, P]
+        L.moe_set_gemm_max_blocks.argtypes = [I32]
         L.moe_status_string.argtypes = [I32]
         L.moe_status_string.restype = ctypes.c_char_p
         for n in EXPORTED[:-1]:
@@ -143,6 +144,11 @@ def workspace_size(cfg: MoeConfig) -> int:
     out = ctypes.c_size_t(0)
     _check("moe_workspace_size", lib().moe_workspace_size(ctypes.byref(cfg), ctypes.byref(out)))
     return out.value
+
+
+def set_gemm_max_blocks(blocks: int) -> None:
+    """Cap the persistent expert GEMMs' grid (0: one block per CU)."""
+    _check("moe_set_gemm_max_blocks", lib().moe_set_gemm_max_blocks(int(blocks)))
 
 
 def alloc_workspace(cfg: MoeConfig, device="cuda") -> torch.Tensor:
