@@ -845,8 +845,8 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
 
 }  // namespace
 
-// SHORT selects the tile heights: 256 or 192 rows (experts that can fill
-// tall tiles), or 192, 128 or 64 rows (every expert holds fewer than 256
+// SHORT selects the tile heights: 256 or 192 rows (experts that can hold
+// many tall tiles), or 192, 128 or 64 rows (every expert holds at most 512
 // rows: decode batches, many experts). Two instantiations rather than one
 // kernel with all four: each keeps its own register allocation.
 // OUT: kOutBf16 (after ACT), kOutF32, or kOutYperm (no activation; bf16
@@ -1134,8 +1134,12 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uin
   // K parts: y_perm outputs only (the combine adds the parts)
   if (out_mode != kGemmOutYperm) out2 = nullptr;
   const int smax = (out2 != nullptr && (K / BK) % 2 == 0) ? 2 : 1;
-  // short tiles when no expert can fill a 256-row tile
-  const bool shorter = max_rows_per_expert < 256;
+  // short tiles (192, 128, 64 rows) when no expert can hold more than two
+  // 256-row tiles: ragged experts of a few hundred rows pad less with the
+  // finer heights. The skewed layer (64 experts, capacity 512) ran its GEMMs
+  // 44 / 54 µs that way against 50 / 60 µs with the tall heights; the small
+  // layer (capacity 1280) did not gain.
+  const bool shorter = max_rows_per_expert <= 512;
   // upper bound on tiles: sum_e ceil(n_e/h) <= max_rows/h + E for the shortest h
   const int64_t mt_bound = max_rows / (shorter ? 64 : 192) + E;
   const int slots = cu_count();
