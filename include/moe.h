@@ -42,7 +42,10 @@
  *    runtime refused) may leave the call's earlier kernels enqueued on
  *    `stream`; its results are then undefined. T == 0 is a valid no-op
  *    returning MOE_OK.
- *  - Results are deterministic: the same inputs give bit-identical outputs.
+ *  - Results are deterministic: the same inputs give bit-identical outputs
+ *    on the same device (CU count) with the same GEMM block cap (see
+ *    moe_set_gemm_max_blocks): the expert GEMMs' tile plan, and with it the
+ *    order of some sums, follows the number of persistent blocks.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
