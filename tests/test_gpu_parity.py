@@ -514,24 +514,25 @@ def test_grouped_order_many_m_tiles(name):
 # The second GEMM's tail parts (the M tiles of a last, partly filled round
 # of whole tiles run as K parts, which the combine adds) at sizes the oracle
 # finishes in seconds: the GEMMs' grid is capped at 16 blocks, so two full
-# rounds take 32 tiles. d_ff = 1024 (16 K stages):
-#  * d = 512 (two feature panels), one expert of 4200 rows: 17 M tiles of
-#    256 rows, 34 tiles; two rounds and the last M tile's 2 tiles (104 rows)
-#    left, run as 8 K parts each;
-#  * d = 256 (one panel), experts of 8400, 0 and 100 rows: 34 tiles, 2 left:
-#    expert 0's last M tile (208 rows) and, past the empty expert 1, expert
-#    2's only one, run as 8 K parts each.
+# rounds take 32 tiles. d = 512 (two feature panels), d_ff = 1024 (16 K
+# stages); the schedule's costs pick (by its arithmetic, which the sizes
+# were chosen with):
+#  * one expert of 3100 rows: 17 M tiles of 192 rows, 34 tiles; two rounds
+#    and the last M tile's 2 tiles (28 rows) left, run as 4 K parts each;
+#  * experts of 6200, 0 and 40 rows: 26 M tiles of 256 rows, 52 tiles;
+#    three rounds and 4 tiles left: expert 0's last M tile (56 rows) and,
+#    past the empty expert 1, expert 2's only one, run as 4 K parts each.
 TAIL_CASES = {
-    "tail_one_expert": dict(T=4200, E=2, d=512, last=None, counts=[4200, 0]),
-    "tail_across_experts": dict(T=8500, E=3, d=256, last=100, counts=[8400, 0, 100]),
+    "tail_one_expert": dict(T=3100, E=2, last=None, counts=[3100, 0]),
+    "tail_across_experts": dict(T=6240, E=3, last=40, counts=[6200, 0, 40]),
 }
 
 
 @pytest.mark.parametrize("name", list(TAIL_CASES))
 def test_gemm2_tail_parts(name):
     spec = TAIL_CASES[name]
-    w = WORKLOADS["small_bf16"].scaled(name=name, T=spec["T"], E=spec["E"], k=1, d=spec["d"],
-                                       d_ff=1024, dropless=True)
+    w = WORKLOADS["small_bf16"].scaled(name=name, T=spec["T"], E=spec["E"], k=1, d=512, d_ff=1024,
+                                       dropless=True)
     inp = synth.make_inputs(w, "cuda", seed=5)
     if spec["last"] is None:
         inp["b_r"][0] += 40.0  # every token chooses expert 0

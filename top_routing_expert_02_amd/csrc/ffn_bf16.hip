@@ -319,6 +319,11 @@ struct TilePlan {
 
 constexpr int kGroupM = 6;  // M tiles per group of the tile order
 
+// At most this many K parts per tail tile: the combine reads one fp32
+// partial row per part for each of the tail's rows, which the cost model
+// does not see.
+constexpr int kMaxParts = 4;
+
 // s_tiles[e]: exclusive prefix over experts of their M tiles of height BM.
 // PARTS: the kernel may run K parts (else every unit is a whole tile and
 // pl.mcap is the M-tile count).
@@ -928,10 +933,10 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
   //  * after at least two rounds of whole tiles, the last M tiles (enough
   //    of them, with all their feature panels, to hold the tiles that would
   //    run in a last, partly filled round) in p K parts, as many as still
-  //    fit in one round: the last round then runs short parts on every
-  //    block instead of whole tiles on a few. On the 16384-token layer's
-  //    second GEMM: 8 rounds of 256 whole tiles and 64 tiles left, which
-  //    run as 256 quarter tiles.
+  //    fit in one round, at most kMaxParts: the last round then runs short
+  //    parts on most blocks instead of whole tiles on a few. On the
+  //    16384-token layer's second GEMM (2144 tiles): 8 rounds of 256 whole
+  //    tiles, and the 96 tiles left (6 M tiles) run as 192 half tiles.
   //  A split only to even out one round after a single round of whole
   //  tiles is not offered: on the skewed layer's second GEMM (352 tiles,
   //  K = 1024) the parts ran no faster and the combine, which adds their
@@ -964,7 +969,7 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
         const int64_t full = tiles / Gd, rest = tiles % Gd;
         if (full >= 2 && rest > 0) {
           mt = static_cast<int>((rest + NT - 1) / NT);
-          for (int pp = Gd / (mt * NT); pp >= 2; --pp)
+          for (int pp = min(Gd / (mt * NT), kMaxParts); pp >= 2; --pp)
             if (nks % pp == 0 && static_cast<int64_t>(pp - 1) * mt * kH[q] <= cap_rows) {
               p = pp;
               break;
