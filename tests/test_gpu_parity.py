@@ -57,6 +57,11 @@ MINI = {
     # an expert count that does not divide 256 (the per-expert histogram sums
     # take the strided path)
     "e12_bf16": WORKLOADS["skewed_bf16"].scaled(name="e12_bf16", T=900, d=64, d_ff=128, E=12, k=3),
+    # capacity 400: at most 512 rows per expert, so the short-tile kernel
+    # (192-, 128- and 64-row tiles) runs, with several M tiles per expert
+    "mid_cap400_bf16": WORKLOADS["mid_bf16"].scaled(name="mid_cap400_bf16", T=1280, d=512, d_ff=1024),
+    "skewed_cap400_bf16": WORKLOADS["skewed_bf16"].scaled(name="skewed_cap400_bf16", T=6400, d=256,
+                                                          d_ff=256),
     # 33 tiles x 1024 experts: above the single-launch scan limit, so the
     # separate scan kernel runs
     "scan_split_bf16": WORKLOADS["large_e_bf16"].scaled(name="scan_split_bf16", T=2100, d=64, d_ff=64,
