@@ -95,8 +95,8 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 [[maybe_unused]] constexpr int kLdsShort = cmax(cmax(lds_bytes_for<3>(), lds_bytes_for<2>()), lds_bytes_for<1>());
 constexpr int TN = 4;         // 32-feature MFMA tiles per wave
 // Output modes of the epilogue: bf16 (after the activation), fp32, or the
-// second expert GEMM's y_perm: bf16 when the launch runs whole tiles, fp32
-// partial sums (one buffer per K half) when it splits K.
+// second expert GEMM's y_perm: bf16 for whole tiles, fp32 partial sums for
+// the K parts of a split tile (see TilePlan).
 constexpr int kOutBf16 = kGemmOutBf16;
 constexpr int kOutF32 = kGemmOutF32;
 constexpr int kOutYperm = kGemmOutYperm;

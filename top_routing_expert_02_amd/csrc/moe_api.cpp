@@ -106,9 +106,9 @@ Layout layout_of(const moe_config& c) {
   L.x_perm = take(layer_gathers(c) ? 0 : R * c.d * es);
   L.h = take(R * c.d_ff * es);
   // y_perm in the layer's dtype; bf16 layers size it for fp32, which holds
-  // the first K half's partial sums when the second GEMM splits K
+  // the part-0 partial sums of the rows the second GEMM splits in K
   L.y_perm = take(R * c.d * 4);
-  // the second K half's partial sums of a split second GEMM (bf16 layers)
+  // the other K parts' partial sums of those rows (bf16 layers)
   L.y_perm2 = take(c.dtype == MOE_BF16 ? R * c.d * 4 : 0);
   L.nsplit = take(3 * 4);  // parts, first split row, split rows (second GEMM)
   // state of the general dispatch (priority order, re-routing rounds); small
@@ -346,8 +346,8 @@ int32_t gemm1_stage(const moe_config& c, const void* A, const int32_t* row_idx,
 }
 
 // y_perm in the layer's dtype. y_perm2/nsplit (nullable, bf16 only): let the
-// GEMM split K; y_perm and y_perm2 then hold fp32 partial sums and *nsplit
-// says so (see launch_gemm_bf16).
+// GEMM run some tiles as K parts; their rows in y_perm and y_perm2 then hold
+// fp32 partial sums, and nsplit says which (see launch_gemm_bf16).
 int32_t gemm2_stage(const moe_config& c, const void* h, const int32_t* offsets, const void* W2,
                     const float* b2, void* y_perm, float* y_perm2, int32_t* nsplit, hipStream_t s) {
   const int64_t R = max_rows_of(c);
