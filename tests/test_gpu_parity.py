@@ -559,6 +559,23 @@ def test_gemm2_tail_parts(name):
     assert o["expert_counts"].tolist() == spec["counts"]
 
 
+# The same layers on other grids: the tile plan (heights, K parts of a last
+# partial round, XCD windows; a grid that is not a multiple of 8 takes the
+# plain order) follows the grid the GEMMs get.
+@pytest.mark.parametrize("blocks", [8, 60, 248])
+@pytest.mark.parametrize("name", ["small_bf16_mini", "mid_bf16_mini", "mid_cap400_bf16"])
+def test_layer_parity_capped_grid(name, blocks):
+    w = MINI[name]
+    inp = synth.make_inputs(w, "cuda", seed=3)
+    m = moe()
+    say(f"[gpu] capped grid {name}: {blocks} blocks")
+    m.set_gemm_max_blocks(blocks)
+    try:
+        P.full_parity(w, inp, cap(w), report=say)
+    finally:
+        m.set_gemm_max_blocks(0)
+
+
 # K stage counts 1, 2, 3 and 5 in both expert GEMMs, around the depths of the
 # token and weight stage rings (2 to 4 buffers): the short-tile kernel
 # (every expert under 256 rows: 64- and 128-row tiles) and the tall one
