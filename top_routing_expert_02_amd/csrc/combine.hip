@@ -9,7 +9,7 @@
 // atomics, so the result is deterministic; a token with every assignment
 // dropped writes exact zeros. When the second GEMM ran some tiles as K parts
 // (device words nsplit: parts p, first split row, split row count), each
-// row from the first split row on is the sum of its p fp32 partial rows,
+// row from the first split row on is the sum of its p partial rows (bf16),
 // in part order, formed before the gate multiplies it.
 #include "moe_internal.h"
 
@@ -56,27 +56,27 @@ __device__ __forceinline__ void load_row(const void* __restrict__ yp, bool bf16,
   }
 }
 
-// the same columns of a row split in K: part 0 from y_perm (fp32 view, row
-// r), part j >= 1 from y_perm2 row (j - 1) trows + r - r_tail, added in
-// order j = 0, 1, ..
+// the same columns of a row split in K: part 0 from y_perm row r, part
+// j >= 1 from y_perm2 row (j - 1) trows + r - r_tail (bf16 rows), added in
+// fp32 in order j = 0, 1, ..
 template <int VEC>
-__device__ __forceinline__ void load_parts(const void* __restrict__ yp, const float* __restrict__ y2,
+__device__ __forceinline__ void load_parts(const void* __restrict__ yp, const void* __restrict__ y2,
                                            int p, int64_t r, int64_t r_tail, int64_t trows, int d, int c,
                                            float (&q)[VEC]) {
-  load_row<VEC>(yp, false, r * d + c, q);
+  load_row<VEC>(yp, true, r * d + c, q);
   for (int j = 1; j < p; ++j) {
     float b[VEC];
-    load_row<VEC>(y2, false, ((j - 1) * trows + r - r_tail) * d + c, b);
+    load_row<VEC>(y2, true, ((j - 1) * trows + r - r_tail) * d + c, b);
 #pragma unroll
     for (int v = 0; v < VEC; ++v) q[v] += b[v];
   }
 }
 
 // y_perm rows bf16 (rows_bf16) or fp32; with y_perm2, nsplit = {p, r_tail,
-// trows}: rows r >= r_tail are sums of p fp32 parts when p > 1
+// trows}: rows r >= r_tail are sums of p bf16 parts when p > 1
 template <int VEC, bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y_perm, int rows_bf16,
-                                                      const float* __restrict__ y_perm2,
+                                                      const void* __restrict__ y_perm2,
                                                       const int32_t* __restrict__ nsplit,
                                                       const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ gates, int64_t T,
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   }
 }
 
-hipError_t launch_combine(const void* y_perm, bool yperm_bf16, const float* y_perm2,
+hipError_t launch_combine(const void* y_perm, bool yperm_bf16, const void* y_perm2,
                           const int32_t* nsplit, const int32_t* row_of, const float* gates, int64_t T,
                           int k, int d, bool out_bf16, void* y, hipStream_t s) {
   if (nsplit == nullptr) y_perm2 = nullptr;

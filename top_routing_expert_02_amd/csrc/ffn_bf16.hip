@@ -56,7 +56,7 @@
 //  * Ragged M: rows past an expert's end read that expert's last row and are
 //    never stored, so no tile reads outside [0, rows).
 //  * With a second output buffer (the second expert GEMM), tiles may run as
-//    K parts whose fp32 partial sums the combine adds: all tiles in two
+//    K parts whose partial sums (bf16) the combine adds: all tiles in two
 //    halves when the whole tiles fit in one round, or, after two or more
 //    full rounds, only the tiles of a last, partly filled round, split so
 //    that their parts fill it.
@@ -95,8 +95,8 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 [[maybe_unused]] constexpr int kLdsShort = cmax(cmax(lds_bytes_for<3>(), lds_bytes_for<2>()), lds_bytes_for<1>());
 constexpr int TN = 4;         // 32-feature MFMA tiles per wave
 // Output modes of the epilogue: bf16 (after the activation), fp32, or the
-// second expert GEMM's y_perm: bf16 for whole tiles, fp32 partial sums for
-// the K parts of a split tile (see TilePlan).
+// second expert GEMM's y_perm: bf16, for whole tiles and for the partial
+// sums of the K parts of a split tile alike (see TilePlan).
 constexpr int kOutBf16 = kGemmOutBf16;
 constexpr int kOutF32 = kGemmOutF32;
 constexpr int kOutYperm = kGemmOutYperm;
@@ -283,7 +283,7 @@ __device__ __forceinline__ float activate(float v) {
 // (rv valid of the tile's height), features from n0; operand A's first row
 // arow and K range [k0, k0 + 64 nk); part: which K part (part 0 carries the
 // bias; parts 1.. go to the second output buffer); split: the tile is one K
-// part of several (fp32 partial sums); orow: the output row of row0 in its
+// part of several (a partial sum); orow: the output row of row0 in its
 // buffer.
 struct TileInfo {
   int e, row0, rv, n0, arow, k0, nk, part, orow;
@@ -295,8 +295,8 @@ struct TileInfo {
 // mt M tiles (rows r_tail onward, tail_rows of them) run as p K parts of nkp
 // stages each: part j of tail M tile m (0..mt-1) and feature panel n is
 // unit dp + (j NT + n) mt + m, so the parts that share a weight panel slice
-// are neighbours. Part 0 writes fp32 sums (with the bias) at the rows' own
-// places in out (viewed as fp32); part j >= 1 writes rows
+// are neighbours. Part 0 writes its partial sums (with the bias) at the
+// rows' own places in out; part j >= 1 writes rows
 // (j - 1) tail_rows + (row - r_tail) of out2. p = 1: no parts (mt = 0).
 struct TilePlan {
   int mcap, nk, p, nkp, mt, r_tail, tail_rows;
@@ -319,9 +319,9 @@ struct TilePlan {
 
 constexpr int kGroupM = 6;  // M tiles per group of the tile order
 
-// At most this many K parts per tail tile: the combine reads one fp32
-// partial row per part for each of the tail's rows, which the cost model
-// does not see.
+// At most this many K parts per tail tile: the combine reads one partial
+// row per part for each of the tail's rows, which the cost model does not
+// see.
 constexpr int kMaxParts = 4;
 
 // s_tiles[e]: exclusive prefix over experts of their M tiles of height BM.
@@ -520,12 +520,12 @@ __device__ __forceinline__ void tile_sources(const TileInfo& t, const uint16_t* 
 // Activation, conversion and stores of one wave's (32 TM) x 128 outputs (the
 // accumulators started at the bias). FULL: every row and feature of the tile
 // is in range (no per-lane checks). A K part of a tile (t.split) stores
-// fp32 partial sums (kOutYperm); rows go to t.orow onward.
+// partial sums; rows go to t.orow onward.
 template <int TM, int OUT, int ACT, bool FULL>
 __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], void* __restrict__ out,
                                          const TileInfo& t, int N, int wm, int wn, int l5, int hi) {
   constexpr int WM = 32 * TM;
-  const bool f32 = OUT == kOutF32 || (OUT == kOutYperm && t.split);
+  const bool f32 = OUT == kOutF32;
   const int fb = wn * WN + hi * 4;  // this lane's first feature in the tile
   const int nb = t.n0 + fb;
 #pragma unroll
@@ -854,16 +854,15 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
 // many tall tiles), or 192, 128 or 64 rows (every expert holds at most 512
 // rows: decode batches, many experts). Two instantiations rather than one
 // kernel with all four: each keeps its own register allocation.
-// OUT: kOutBf16 (after ACT), kOutF32, or kOutYperm (no activation; bf16
-// for whole tiles). out2 (kOutYperm only, else null; cap_rows
-// rows of N fp32): with it, the schedule may run tiles as K parts (TilePlan:
-// all tiles in two halves, or the last M tiles in p parts). nsplit (when
-// not null) receives p (1: no parts), the first row of the split tiles,
-// r_tail, and their row count, tail_rows. With kOutYperm, a row r < r_tail
-// of out is then a bf16 result, and a row r >= r_tail is the sum, in order,
-// of out's fp32 row r (out viewed as fp32: its byte range lies past every
-// bf16 row below r_tail) and out2's rows (j - 1) tail_rows + r - r_tail,
-// j = 1 .. p - 1.
+// OUT: kOutBf16 (after ACT), kOutF32, or kOutYperm (no activation, bf16).
+// out2 (kOutYperm only, else null; cap_rows bf16 rows of N): with it, the
+// schedule may run tiles as K parts (TilePlan: all tiles in two halves, or
+// the last M tiles in p parts). nsplit (when not null) receives p (1: no
+// parts), the first row of the split tiles, r_tail, and their row count,
+// tail_rows. A row r < r_tail of out is then a result, and a row
+// r >= r_tail the sum, in order, of out's row r and out2's rows
+// (j - 1) tail_rows + r - r_tail, j = 1 .. p - 1 (each part rounded to
+// bf16).
 // WT: each W_e is stored [K, N] (K-major, as W^T of the usual [N, K]); the
 // weight stages are loaded row by row of K and read with transposing LDS
 // reads.
@@ -1132,7 +1131,7 @@ int cu_count() {
 void set_gemm_max_blocks(int blocks) { g_max_blocks.store(blocks, std::memory_order_relaxed); }
 
 hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uint16_t* W,
-                            const float* bias, void* out, float* out2, int32_t* nsplit,
+                            const float* bias, void* out, void* out2, int32_t* nsplit,
                             int out_mode, int act, const int32_t* offsets, int E, int N, int K,
                             int64_t max_rows, int max_rows_per_expert, hipStream_t s) {
   if (max_rows <= 0) return hipSuccess;
@@ -1155,10 +1154,10 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uin
   do {                                                                                               \
     if (shorter)                                                                                     \
       klaunch(grouped_gemm_bf16_kernel<OM, AC, true>, dim3(grid), dim3(256), 0, s, A, row_idx, W, bias, \
-              out, static_cast<void*>(out2), nsplit, offsets, E, N, K, cap);                           \
+              out, out2, nsplit, offsets, E, N, K, cap);                           \
     else                                                                                             \
       klaunch(grouped_gemm_bf16_kernel<OM, AC, false>, dim3(grid), dim3(256), 0, s, A, row_idx, W,     \
-              bias, out, static_cast<void*>(out2), nsplit, offsets, E, N, K, cap);                     \
+              bias, out, out2, nsplit, offsets, E, N, K, cap);                     \
   } while (0)
   if (out_mode == kGemmOutYperm) MOE_GEMM(kOutYperm, kActNone);
   else if (out_mode == kGemmOutF32) MOE_GEMM(kOutF32, kActNone);

@@ -105,11 +105,11 @@ Layout layout_of(const moe_config& c) {
   L.row_token = take(R * 4);
   L.x_perm = take(layer_gathers(c) ? 0 : R * c.d * es);
   L.h = take(R * c.d_ff * es);
-  // y_perm in the layer's dtype; bf16 layers size it for fp32, which holds
-  // the part-0 partial sums of the rows the second GEMM splits in K
-  L.y_perm = take(R * c.d * 4);
-  // the other K parts' partial sums of those rows (bf16 layers)
-  L.y_perm2 = take(c.dtype == MOE_BF16 ? R * c.d * 4 : 0);
+  // y_perm in the layer's dtype (it holds the part-0 partial sums of the
+  // rows the second GEMM splits in K, in place)
+  L.y_perm = take(R * c.d * es);
+  // the other K parts' partial sums of those rows (bf16 layers; bf16 rows)
+  L.y_perm2 = take(c.dtype == MOE_BF16 ? R * c.d * 2 : 0);
   L.nsplit = take(3 * 4);  // parts, first split row, split rows (second GEMM)
   // state of the general dispatch (priority order, re-routing rounds); small
   // next to h, so every layout has it and moe_dispatch_reroute works for any
@@ -347,9 +347,9 @@ int32_t gemm1_stage(const moe_config& c, const void* A, const int32_t* row_idx,
 
 // y_perm in the layer's dtype. y_perm2/nsplit (nullable, bf16 only): let the
 // GEMM run some tiles as K parts; their rows in y_perm and y_perm2 then hold
-// fp32 partial sums, and nsplit says which (see launch_gemm_bf16).
+// bf16 partial sums, and nsplit says which (see launch_gemm_bf16).
 int32_t gemm2_stage(const moe_config& c, const void* h, const int32_t* offsets, const void* W2,
-                    const float* b2, void* y_perm, float* y_perm2, int32_t* nsplit, hipStream_t s) {
+                    const float* b2, void* y_perm, void* y_perm2, int32_t* nsplit, hipStream_t s) {
   const int64_t R = max_rows_of(c);
   const int per_expert = static_cast<int>(c.T < c.capacity ? c.T : c.capacity);
   if (c.dtype == MOE_BF16)
@@ -364,7 +364,7 @@ int32_t gemm2_stage(const moe_config& c, const void* h, const int32_t* offsets, 
 
 // y_perm2/nsplit: as gemm2_stage wrote them (null for fp32 layers and for
 // a caller's y_perm)
-int32_t combine_stage(const moe_config& c, const void* y_perm, const float* y_perm2,
+int32_t combine_stage(const moe_config& c, const void* y_perm, const void* y_perm2,
                       const int32_t* nsplit, const int32_t* row_of, const float* gates, void* y,
                       hipStream_t s) {
   const bool bf = c.dtype == MOE_BF16;
@@ -577,7 +577,7 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* x, const void* W_r,
   void* h = in.h != nullptr ? in.h : at<char>(ws, L.h);
   void* y_perm = at<char>(ws, L.y_perm);
   const bool bf = c.dtype == MOE_BF16;
-  float* y_perm2 = bf ? at<float>(ws, L.y_perm2) : nullptr;
+  void* y_perm2 = bf ? at<char>(ws, L.y_perm2) : nullptr;
   int32_t* nsplit = bf ? at<int32_t>(ws, L.nsplit) : nullptr;
   int32_t* hist = at<int32_t>(ws, L.hist);
   const bool gen = general_rule(c);

@@ -219,20 +219,18 @@ hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int
 // row_idx (nullable): row r of the grouped problem is row row_idx[r] of A.
 // out_mode: kGemmOutBf16 (bf16 after act), kGemmOutF32 (fp32, no act), or
 // kGemmOutYperm (no act; bf16 when the launch runs whole tiles).
-// out2 (nullable; y_perm mode only): a second fp32 [max_rows,N]
-// buffer that lets the kernel run tiles as K parts; nsplit (3 words) then
-// receives p, r_tail and tail_rows: with p > 1, rows r >= r_tail of the
-// result are the sum, in order j = 0 .. p-1, of part 0 = out's fp32 row r
-// (out viewed as fp32 [max_rows, N]; in y_perm mode rows below r_tail stay
-// bf16, which end below that byte range) and part j = out2's row
-// (j-1) tail_rows + r - r_tail.
+// out2 (nullable; y_perm mode only): a second bf16 [max_rows,N] buffer
+// that lets the kernel run tiles as K parts; nsplit (3 words) then receives
+// p, r_tail and tail_rows: with p > 1, rows r >= r_tail of the result are
+// the sum, in order j = 0 .. p-1, of part 0 = out's row r and part j =
+// out2's row (j-1) tail_rows + r - r_tail, each part rounded to bf16.
 // cap on the persistent GEMMs' grid (0: one block per CU)
 void set_gemm_max_blocks(int blocks);
 constexpr int kGemmOutBf16 = 0;
 constexpr int kGemmOutF32 = 1;
 constexpr int kGemmOutYperm = 2;
 hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* row_idx, const uint16_t* W,
-                            const float* bias, void* out, float* out2, int32_t* nsplit,
+                            const float* bias, void* out, void* out2, int32_t* nsplit,
                             int out_mode, int act, const int32_t* offsets, int E, int N, int K,
                             int64_t max_rows, int max_rows_per_expert, hipStream_t s);
 // The same product with each W_e stored [K, N] (the transposed layout, so
@@ -249,8 +247,8 @@ hipError_t launch_gemm_f32(const float* A, const int32_t* row_idx, const float* 
 // y[t] = sum_j gates[t,j] y_perm[row_of[t,j]] (kept j only), rounded once;
 // y_perm rows are bf16 (yperm_bf16) or fp32; with y_perm2 (nullable) and
 // nsplit[0] = p > 1, rows r >= nsplit[1] are instead the sums of the second
-// GEMM's p fp32 partial rows (launch_gemm_bf16), added first
-hipError_t launch_combine(const void* y_perm, bool yperm_bf16, const float* y_perm2,
+// GEMM's p bf16 partial rows (launch_gemm_bf16), added first in fp32
+hipError_t launch_combine(const void* y_perm, bool yperm_bf16, const void* y_perm2,
                           const int32_t* nsplit, const int32_t* row_of, const float* gates,
                           int64_t T, int k, int d, bool out_bf16, void* y, hipStream_t s);
 
