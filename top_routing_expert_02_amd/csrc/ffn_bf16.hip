@@ -460,6 +460,18 @@ __device__ __forceinline__ int prologue_loads(int nk) {
   return sched_prologue_loads(nk, NA, NW, LA, LB);
 }
 
+// The lane id, read afresh. Per-lane values derived from it are then
+// computed where they are used: derived from a lane id kept since the
+// kernel's start, the compiler hoists them out of the tile loop and, with
+// every register taken, spills them, and reloading a spilled value waits
+// for every vector-memory operation issued before it (the next tile's
+// stage loads included).
+__device__ __forceinline__ int fresh_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // Per-tile DMA sources: byte offsets (from the tile's token and weight bases)
 // of the chunk each lane loads for every 1 KiB block it fills (lane L lands
 // at row L/8, position L%8 of its block). Token rows past the expert's end
@@ -472,9 +484,11 @@ __device__ __forceinline__ int prologue_loads(int nk) {
 template <int LA, int LB, bool WT>
 __device__ __forceinline__ void tile_sources(const TileInfo& t, const uint16_t* A,
                                              const int32_t* __restrict__ row_idx, const uint16_t* W,
-                                             int N, int lda, int64_t w_estride, int wave, int drow,
-                                             int dpos, const char*& Abase, const char*& Wbase,
+                                             int N, int lda, int64_t w_estride, int wave,
+                                             const char*& Abase, const char*& Wbase,
                                              uint32_t (&aoffs)[LA], uint32_t (&boffs)[LB]) {
+  const int lane = fresh_lane();
+  const int drow = lane >> 3, dpos = lane & 7;
   if constexpr (WT)  // W_e stored [K, N]: the tile's columns from its first K row
     Wbase = reinterpret_cast<const char*>(W + t.e * w_estride + static_cast<int64_t>(t.k0) * N + t.n0);
   else
@@ -500,7 +514,6 @@ __device__ __forceinline__ void tile_sources(const TileInfo& t, const uint16_t* 
     // each); lane L lands at byte 16 (L % 32) of row kr + L / 32, in 64-byte
     // segment p = (L % 32) / 4, which holds the row's segment p ^ (kr & 3).
     // Columns past N read column N - 8 onward (never stored).
-    const int lane = drow * 8 + dpos;
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
       const int kr = (wave * LB + i) * 2 + (lane >> 5);
@@ -560,6 +573,97 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TN][TM], void* __
   }
 }
 
+// Per-lane words parked in LDS while a tile's epilogue runs: word i of
+// lane L at byte addr + 256 i + 4 L, written and read in pairs. Kept in
+// registers, the next tile's DMA offsets were spilled to scratch around
+// the epilogue, and each spill and reload waited for every vector-memory
+// operation in flight (the next tile's stage 0, the epilogue's stores).
+// N is even; unpark waits for its reads before it returns.
+template <int N>
+__device__ __forceinline__ void park_words(const uint32_t (&v)[N], uint32_t addr) {
+  static_assert(N % 2 == 0 && N <= 8, "pairs, at most 8 words");
+#pragma unroll
+  for (int i = 0; i < N; i += 2)
+    asm volatile("ds_write2st64_b32 %0, %1, %2 offset0:%3 offset1:%4"
+                 :
+                 : "v"(addr), "v"(v[i]), "v"(v[i + 1]), "i"(i), "i"(i + 1)
+                 : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void unpark_words(uint32_t (&v)[N], uint32_t addr) {
+  static_assert(N % 2 == 0 && N <= 8, "pairs, at most 8 words");
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  u32x2_t w[4];
+  if constexpr (N == 2) {
+    asm volatile("ds_read2st64_b32 %0, %1 offset0:0 offset1:1\n\ts_waitcnt lgkmcnt(0)"
+                 : "=v"(w[0]) : "v"(addr) : "memory");
+  } else if constexpr (N == 4) {
+    asm volatile(
+        "ds_read2st64_b32 %0, %2 offset0:0 offset1:1\n\tds_read2st64_b32 %1, %2 offset0:2 offset1:3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0]), "=&v"(w[1]) : "v"(addr) : "memory");
+  } else if constexpr (N == 6) {
+    asm volatile(
+        "ds_read2st64_b32 %0, %3 offset0:0 offset1:1\n\tds_read2st64_b32 %1, %3 offset0:2 offset1:3\n\t"
+        "ds_read2st64_b32 %2, %3 offset0:4 offset1:5\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]) : "v"(addr) : "memory");
+  } else {
+    asm volatile(
+        "ds_read2st64_b32 %0, %4 offset0:0 offset1:1\n\tds_read2st64_b32 %1, %4 offset0:2 offset1:3\n\t"
+        "ds_read2st64_b32 %2, %4 offset0:4 offset1:5\n\tds_read2st64_b32 %3, %4 offset0:6 offset1:7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]) : "v"(addr) : "memory");
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = w[i / 2][i % 2];
+}
+
+// The same for a full tile with bf16 outputs, through LDS: the accumulator
+// layout gives a store instruction 32 rows x 16 bytes (32 partial cache
+// lines), so each 32-token slab of the wave's outputs (32 rows x 128
+// features, 8 KiB) is written to the wave's staging area stg, 16-byte chunk
+// c of row r at position c ^ (r & 15), and read back as whole rows: a store
+// then writes 4 rows x 256 bytes (8 whole lines). Same values as epilogue().
+// One wave's LDS operations run in order, so the slabs reuse stg without a
+// wait, and the stores consume the reads before any later write to stg.
+template <int TM, int ACT>
+__device__ __forceinline__ void epilogue_staged(const f32x16_t (&acc)[TN][TM], uint16_t* __restrict__ out,
+                                                const TileInfo& t, int N, int wm, int wn,
+                                                char* __restrict__ stg) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  constexpr int WM = 32 * TM;
+  const int lane = fresh_lane();
+  const int l5 = lane & 31, hi = lane >> 5;
+  const int orow = __builtin_amdgcn_readfirstlane(t.orow);
+  const int n0 = __builtin_amdgcn_readfirstlane(t.n0);
+  const int rq = lane >> 4, rc = lane & 15;  // read-back: row 4g + rq, chunk rc
+  char* wp = stg + l5 * 256 + 8 * hi;
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x4_t h = {static_cast<__bf16>(activate<ACT>(acc[i][j][4 * q + 0])),
+                            static_cast<__bf16>(activate<ACT>(acc[i][j][4 * q + 1])),
+                            static_cast<__bf16>(activate<ACT>(acc[i][j][4 * q + 2])),
+                            static_cast<__bf16>(activate<ACT>(acc[i][j][4 * q + 3]))};
+        *reinterpret_cast<bf16x4_t*>(wp + (((4 * i + q) ^ (l5 & 15)) << 4)) = h;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    uint16_t* o = out + static_cast<int64_t>(orow + wm * WM + j * 32 + rq) * N + n0 + wn * WN + 8 * rc;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int r = 4 * g + rq;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + r * 256 + ((rc ^ (r & 15)) << 4));
+      *reinterpret_cast<u32x4_t*>(o + static_cast<int64_t>(4 * g) * N) = v;
+      if (g % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // The persistent tile loop for tiles of BM = 64 TM rows: units tile,
 // tile + stride, ... below end, then tile2, tile2 + stride2, ... below end2.
 // lds: the two stage rings; s_tiles: the M-tile prefix for this height;
@@ -605,7 +709,6 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
   uint32_t fo[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) fo[s] = l5 * ROWB + 16 * ((2 * s + hi) ^ key);
-  const int drow = lane >> 3, dpos = lane & 7;
   // a unit's tile is the same for the whole wave: its fields go to scalar
   // registers (the DMA asm takes its base addresses as SGPRs)
   auto decode = [&](int tl) {
@@ -660,11 +763,31 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
   auto prologue0 = [&](const TileInfo& c, int par) {
     issue_stage<TM>(aoffs, boffs, a_slot(0) + wave * LA * 1024, w_slot(0) + wave * LB * 1024, Abase, Wbase);
     if (bias != nullptr && c.part == 0 && wave == 0)
-      issue_bias(bias + static_cast<int64_t>(c.e) * N + min(c.n0 + 4 * lane, N - 4),
+      issue_bias(bias + static_cast<int64_t>(c.e) * N + min(c.n0 + 4 * fresh_lane(), N - 4),
                  static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&s_bias[par][0])));
   };
   // its stages 1 .. min(NW, nk) - 1 (token stage p only while p < NA):
   // issued after the previous tile's epilogue stores
+  // Parking place of the next tile's DMA offsets during the epilogue: this
+  // wave's own part of token slot 1 (of slots 2 and 1 for 64-row tiles,
+  // whose part of a slot holds 8 words), free from the last stage's barrier
+  // until prologue1 below refills it, after reading them back.
+  static_assert(TM > 1 || NA >= 3, "64-row tiles park their token offsets in token slot 2");
+  auto park_base = [&]() {
+    return a_slot(1) + static_cast<uint32_t>(wave * LA * 1024 + 4 * fresh_lane());
+  };
+  auto park = [&]() {
+    const uint32_t pb = park_base();
+    park_words<LB>(boffs, pb);
+    if constexpr (TM > 1) park_words<LA>(aoffs, pb + LB * 256);
+    else park_words<LA>(aoffs, pb + A_BYTES);
+  };
+  auto unpark = [&]() {
+    const uint32_t pb = park_base();
+    unpark_words<LB>(boffs, pb);
+    if constexpr (TM > 1) unpark_words<LA>(aoffs, pb + LB * 256);
+    else unpark_words<LA>(aoffs, pb + A_BYTES);
+  };
   auto prologue1 = [&](int nk) {
     for (int p = 1; p < NMAX && p < nk; ++p) {
       if (p < NA && p < NW)
@@ -678,7 +801,7 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
   };
   int par = 0;  // bias slice of the current tile
   TileInfo cur = decode(tile);
-  tile_sources<LA, LB, WT>(cur, A, row_idx, W, N, lda, w_estride, wave, drow, dpos, Abase, Wbase, aoffs,
+  tile_sources<LA, LB, WT>(cur, A, row_idx, W, N, lda, w_estride, wave, Abase, Wbase, aoffs,
                            boffs);
   prologue0(cur, par);
   prologue1((WG || PARTS) ? cur.nk : pl.nk);
@@ -696,7 +819,7 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     f32x16_t acc[TN][TM];
     {
       const bool with_bias = bias != nullptr && cur.part == 0;
-      const int fb = wn * WN + hi * 4;
+      const int fb = wn * WN + (fresh_lane() >> 5) * 4;
 #pragma unroll
       for (int i = 0; i < TN; ++i)
 #pragma unroll
@@ -823,9 +946,10 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     __syncthreads();
     if (more) {
       cur = decode(next);
-      tile_sources<LA, LB, WT>(cur, A, row_idx, W, N, lda, w_estride, wave, drow, dpos, Abase, Wbase,
+      tile_sources<LA, LB, WT>(cur, A, row_idx, W, N, lda, w_estride, wave, Abase, Wbase,
                                aoffs, boffs);
       prologue0(cur, par ^ 1);
+      park();
     }
     last_step<TM>(acc, wf1, tf1);
 
@@ -833,10 +957,28 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
     // features 8q + 4*hi + {0..3} of each 32-feature tile i
     const bool full_tile = done.rv == BM && done.n0 + BN <= N;
     void* dst = done.part ? out2 : out;
-    if (full_tile) epilogue<TM, OUT, ACT, true>(acc, dst, done, N, wm, wn, l5, hi);
-    else epilogue<TM, OUT, ACT, false>(acc, dst, done, N, wm, wn, l5, hi);
+    if constexpr (OUT != kOutF32) {
+      // Staging area: this wave's own 8 KiB of a weight slot other than 0
+      // (the next tile's stage 0). The wave itself refills that region in
+      // prologue1, after these reads. With NW = NA + 1 the last refill of
+      // the K loop loaded a stage past the last one into weight slot
+      // nk % NW and nothing has waited for it, so that slot is avoided.
+      const int ws = (NW > NA && nk % NW == 1) ? 2 : 1;
+      char* stg = lds + NA * A_BYTES + ws * W_BYTES + wave * LB * 1024;
+      if (full_tile) {
+        epilogue_staged<TM, ACT>(acc, static_cast<uint16_t*>(dst), done, N, wm, wn, stg);
+      } else {
+        const int fl = fresh_lane();
+        epilogue<TM, OUT, ACT, false>(acc, dst, done, N, wm, wn, fl & 31, fl >> 5);
+      }
+    } else {
+      const int fl = fresh_lane();
+      if (full_tile) epilogue<TM, OUT, ACT, true>(acc, dst, done, N, wm, wn, fl & 31, fl >> 5);
+      else epilogue<TM, OUT, ACT, false>(acc, dst, done, N, wm, wn, fl & 31, fl >> 5);
+    }
     if (!more) break;
     // the next tile's later prologue stages, after this tile's stores
+    unpark();
     prologue1((WG || PARTS) ? cur.nk : pl.nk);
     tile = next;
     if (second) {
