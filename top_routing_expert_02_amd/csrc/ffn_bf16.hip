@@ -941,8 +941,11 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
       kstep(wf1, tf1, wf0, tf0, sa, sw, 2);
       kstep(wf0, tf0, wf1, tf1, sa, sw, 3);
     }
+    // the last K16 step's MFMAs (fragments already in registers) run while
+    // the wave meets the others and sets up the next tile
+    last_step<TM>(acc, wf1, tf1);
     // every wave has read all of its fragments: all buffers are free, and the
-    // next tile's stage 0 loads during this tile's last MFMAs and epilogue
+    // next tile's stage 0 loads during this tile's epilogue
     __syncthreads();
     if (more) {
       cur = decode(next);
@@ -951,7 +954,6 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
       prologue0(cur, par ^ 1);
       park();
     }
-    last_step<TM>(acc, wf1, tf1);
 
     // ---- epilogue: lane holds token l5 of each 32-token tile j and
     // features 8q + 4*hi + {0..3} of each 32-feature tile i
