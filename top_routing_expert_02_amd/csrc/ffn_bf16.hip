@@ -627,7 +627,11 @@ __device__ __forceinline__ void unpark_words(uint32_t (&v)[N], uint32_t addr) {
 // then writes 4 rows x 256 bytes (8 whole lines). Same values as epilogue().
 // One wave's LDS operations run in order, so the slabs reuse stg without a
 // wait, and the stores consume the reads before any later write to stg.
-template <int TM, int ACT>
+// FULL: every row and feature of the tile is in range; else slabs past the
+// tile's rv rows are skipped and each lane stores only rows below rv and
+// features below N (N and the tile's first feature are multiples of 64, so
+// a lane's 8 features are all in range or all out).
+template <int TM, int ACT, bool FULL>
 __device__ __forceinline__ void epilogue_staged(const f32x16_t (&acc)[TN][TM], uint16_t* __restrict__ out,
                                                 const TileInfo& t, int N, int wm, int wn,
                                                 char* __restrict__ stg) {
@@ -639,8 +643,12 @@ __device__ __forceinline__ void epilogue_staged(const f32x16_t (&acc)[TN][TM], u
   const int n0 = __builtin_amdgcn_readfirstlane(t.n0);
   const int rq = lane >> 4, rc = lane & 15;  // read-back: row 4g + rq, chunk rc
   char* wp = stg + l5 * 256 + 8 * hi;
+  // rows of the wave's first slab still in range; features in range
+  const int rleft = FULL ? WM : __builtin_amdgcn_readfirstlane(t.rv) - wm * WM;
+  const bool col_ok = FULL || n0 + wn * WN + 8 * rc < N;
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
+    if (!FULL && j * 32 >= rleft) break;
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
 #pragma unroll
@@ -658,7 +666,8 @@ __device__ __forceinline__ void epilogue_staged(const f32x16_t (&acc)[TN][TM], u
     for (int g = 0; g < 8; ++g) {
       const int r = 4 * g + rq;
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + r * 256 + ((rc ^ (r & 15)) << 4));
-      *reinterpret_cast<u32x4_t*>(o + static_cast<int64_t>(4 * g) * N) = v;
+      if (FULL || (j * 32 + r < rleft && col_ok))
+        *reinterpret_cast<u32x4_t*>(o + static_cast<int64_t>(4 * g) * N) = v;
       if (g % 2 == 1) __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -672,7 +681,12 @@ __device__ __forceinline__ void epilogue_staged(const f32x16_t (&acc)[TN][TM], u
 // offsets, M the rows of C per expert); else expert-FFN units as the plan
 // pl numbers them (decode_tile: whole tiles, then K parts of tail tiles,
 // whose parts 1.. go to out2 without bias).
-template <int TM, int OUT, int ACT, bool WG, bool WT = false>
+// SP: partly filled bf16 tiles also store through LDS (the short-tile
+// kernel, where most tiles are partly filled: the large-E layer's second
+// GEMM 900 -> 867 us); the tall-tile kernels keep the direct stores there,
+// which need fewer registers (the staged path for partial tiles cost them
+// 2-3 more spilled VGPRs and 0.5% on the 16384-token layer).
+template <int TM, int OUT, int ACT, bool WG, bool WT = false, bool SP = false>
 __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const int32_t* __restrict__ row_idx,
                                           const uint16_t* __restrict__ W, const float* __restrict__ bias,
                                           void* __restrict__ out, void* __restrict__ out2,
@@ -968,7 +982,9 @@ __device__ __forceinline__ void tile_loop(const uint16_t* __restrict__ A, const 
       const int ws = (NW > NA && nk % NW == 1) ? 2 : 1;
       char* stg = lds + NA * A_BYTES + ws * W_BYTES + wave * LB * 1024;
       if (full_tile) {
-        epilogue_staged<TM, ACT>(acc, static_cast<uint16_t*>(dst), done, N, wm, wn, stg);
+        epilogue_staged<TM, ACT, true>(acc, static_cast<uint16_t*>(dst), done, N, wm, wn, stg);
+      } else if constexpr (SP) {
+        epilogue_staged<TM, ACT, false>(acc, static_cast<uint16_t*>(dst), done, N, wm, wn, stg);
       } else {
         const int fl = fresh_lane();
         epilogue<TM, OUT, ACT, false>(acc, dst, done, N, wm, wn, fl & 31, fl >> 5);
@@ -1182,7 +1198,7 @@ void grouped_gemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __r
     first2 = end2;
   }
 #define MOE_TILE_LOOP(TMV)                                                                                \
-  tile_loop<TMV, OUT, ACT, false, WT>(A, row_idx, W, bias, out, out2, offsets, E, N, pl, K, wes, 0, lds, \
+  tile_loop<TMV, OUT, ACT, false, WT, SHORT>(A, row_idx, W, bias, out, out2, offsets, E, N, pl, K, wes, 0, lds, \
                                       s_tiles, s_bias, first, stride, end, first2, stride2, end2, NT)
   // each kernel instantiates only its own heights (separate register
   // allocations)
