@@ -62,6 +62,17 @@ MINI = {
     "mid_cap400_bf16": WORKLOADS["mid_bf16"].scaled(name="mid_cap400_bf16", T=1280, d=512, d_ff=1024),
     "skewed_cap400_bf16": WORKLOADS["skewed_bf16"].scaled(name="skewed_cap400_bf16", T=6400, d=256,
                                                           d_ff=256),
+    # K stage counts one past a multiple of the weight ring (3 buffers for
+    # 192-row tiles, 4 for 64-row tiles) in the short-tile kernel: the K
+    # loop's last refill then loads a stage past the last one into weight
+    # slot 1, and the epilogue's LDS staging must take slot 2 (d = 320, 448,
+    # 832: 5, 7, 13 stages; d_ff = 576, 256, 320: 9, 4, 5 stages)
+    "ring_wrap_decode_bf16": WORKLOADS["small_bf16"].scaled(name="ring_wrap_decode_bf16", T=40, d=320,
+                                                            d_ff=576, dropless=True),
+    "ring_wrap_c1_bf16": WORKLOADS["small_bf16"].scaled(name="ring_wrap_c1_bf16", T=900, d=448, d_ff=256,
+                                                        c=1.0),
+    "ring_wrap_k13_bf16": WORKLOADS["small_bf16"].scaled(name="ring_wrap_k13_bf16", T=1100, d=832,
+                                                         d_ff=320, c=1.0),
     # 33 tiles x 1024 experts: above the single-launch scan limit, so the
     # separate scan kernel runs
     "scan_split_bf16": WORKLOADS["large_e_bf16"].scaled(name="scan_split_bf16", T=2100, d=64, d_ff=64,
