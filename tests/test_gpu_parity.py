@@ -73,6 +73,12 @@ MINI = {
                                                         c=1.0),
     "ring_wrap_k13_bf16": WORKLOADS["small_bf16"].scaled(name="ring_wrap_k13_bf16", T=1100, d=832,
                                                          d_ff=320, c=1.0),
+    # more than 16384 tokens with at most 8 experts (over a thousand route
+    # blocks, a ragged last one; with 5 experts the logits tile has columns
+    # past E)
+    "many_tokens_bf16": WORKLOADS["small_bf16"].scaled(name="many_tokens_bf16", T=16500, d=256, d_ff=256),
+    "many_tokens_e5_bf16": WORKLOADS["small_bf16"].scaled(name="many_tokens_e5_bf16", T=16421, d=512,
+                                                         d_ff=128, E=5, k=2),
     # 33 tiles x 1024 experts: above the single-launch scan limit, so the
     # separate scan kernel runs
     "scan_split_bf16": WORKLOADS["large_e_bf16"].scaled(name="scan_split_bf16", T=2100, d=64, d_ff=64,
