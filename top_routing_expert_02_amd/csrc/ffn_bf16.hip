@@ -17,8 +17,15 @@
 //    four waves in a 2x2 grid; each wave owns BM/2 tokens x 128 features as 32x32
 //    v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulators in AGPRs. The
 //    weight tile is the MFMA A operand and the token tile the B operand, so a
-//    lane's accumulators hold 4 consecutive features of one token: the
-//    epilogue stores 8-byte (bf16) or 16-byte (fp32) vectors.
+//    lane's accumulators hold 4 consecutive features of one token. bf16
+//    outputs go through LDS in 32-token slabs so that the stores write whole
+//    cache lines (4 rows x 256 bytes per instruction); fp32 outputs store
+//    16-byte vectors from the accumulators.
+//  * Registers: the 256-row kernels use all 512 (256 of them accumulators).
+//    Per-lane terms are recomputed from a fresh lane id where they are used
+//    and the next tile's DMA offsets wait in LDS across the epilogue, so
+//    that little is spilled: a scratch reload waits for every vector-memory
+//    operation issued before it, the next tile's stage loads included.
 //  * The tile height is chosen on the device, per launch, from the actual
 //    expert row counts (the cost model is at the schedule below: rounds of
 //    the persistent blocks times the K-loop work of a tile, its rows plus a
