@@ -204,7 +204,7 @@ def cpu_baseline(w, inp, C, budget_s):
               f"route+dispatch+combine on all {w.T} tokens, expert FFN on whole experts holding "
               f"{done_rows}/{rows} rows (its time scaled to all rows)")
     return {"value": w.T / est, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "cpu": cpu_model(),
+            "cpu": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{w.name}: {sample}; fp64 numpy; {est:.2f} s per layer"}
 
 
