@@ -160,19 +160,6 @@ def expert_of_rows(offsets, rows) -> np.ndarray:
     return np.searchsorted(np.asarray(offsets), np.asarray(rows), side="right") - 1
 
 
-def covering_rows(offsets, step: int = 64) -> np.ndarray:
-    """Rows of every expert at multiples of `step` from its first row, plus
-    its last row: every M tile of the grouped GEMMs (heights 64, 128, 192
-    and 256 start at multiples of 64 within an expert) holds one of them."""
-    out = []
-    for e in range(len(offsets) - 1):
-        a, b = int(offsets[e]), int(offsets[e + 1])
-        if b > a:
-            out.extend(range(a, b, step))
-            out.append(b - 1)
-    return np.unique(np.asarray(out, dtype=np.int64))
-
-
 def oracle_rows(rows, x64, row_token, offsets, expert_weights, act):
     """The oracle's expert FFN on the given rows, batched expert by expert:
     (h [n, d_ff], Y [n, d]) in the order of `rows`. expert_weights(e)

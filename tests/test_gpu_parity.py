@@ -380,19 +380,14 @@ def test_stages_separately(name):
 
 # ------------------------------------------------------------------ full sizes
 
-# Full-size workloads the oracle runs whole in seconds: every token's y and
-# every row's h are compared. The others compare h on rows that cover every
-# (expert, M tile) of both GEMM schedules and y on the tokens of those rows.
-FULL_COMPARE = {"small_bf16", "skewed_bf16"}
-
-
 @pytest.mark.parametrize("name", ["small_bf16", "mid_bf16", "skewed_bf16", "large_e_bf16",
                                   "skewed_dropless_bf16", "decode_bf16", "skewed_reroute_bf16"])
 def test_full_size_workload(name):
     """Full-size workload in the launch configuration the benchmark times:
     routing and dispatch on every token, x_perm on every row, the first
-    GEMM's h and the layer's y against the oracle's expert FFN on all rows
-    (small and skewed layers) or on rows covering every GEMM tile."""
+    GEMM's h on every kept row and the layer's y on every token against the
+    oracle (its expert FFN batched expert by expert; under a minute on 16
+    host cores for the largest layer)."""
     w = WORKLOADS[name]
     say(f"[gpu] full size {name}: generating inputs")
     inp = synth.make_inputs(w, "cuda", seed=0)
@@ -445,21 +440,12 @@ def test_full_size_workload(name):
     xb = synth.to_numpy_bits(inp["x"])
     np.testing.assert_array_equal(synth.to_numpy_bits(x_perm[:rows]), xb[o_disp["row_token"]])
     del x_perm, ws
-    # checked rows and tokens
+    # every token and every kept row
     offsets = o_disp["expert_offsets"]
     row_of = o_disp["row_of"]
-    if name in FULL_COMPARE:
-        tokens = np.arange(w.T)
-    else:
-        cover = P.covering_rows(offsets)
-        owner = np.zeros(rows, dtype=np.int64)
-        kept = row_of >= 0
-        owner[row_of[kept]] = np.nonzero(kept)[0]
-        dropped_tok = np.flatnonzero(~o_disp["kept"].any(axis=1))
-        tokens = np.unique(np.concatenate([owner[cover], dropped_tok[:4], [0, w.T - 1]]))
-    need = np.unique(row_of[tokens][row_of[tokens] >= 0])
-    if name not in FULL_COMPARE:
-        assert np.isin(P.covering_rows(offsets), need).all()
+    tokens = np.arange(w.T)
+    need = np.unique(row_of[row_of >= 0])
+    assert need.size == rows
 
     def expert_weights(e):
         return (P.host64(inp["W1"][e], w.dtype), P.host64(inp["b1"][e], "f32"),
