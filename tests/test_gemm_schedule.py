@@ -158,3 +158,44 @@ def test_refilling_stages_wait_the_steady_count(closed_forms):
     # the kernel's rings: 2+2, 2+3, 3+3, 3+4 buffers
     for na, nw in ((2, 2), (2, 3), (3, 3), (3, 4)):
         assert na <= nw <= na + 1
+
+
+def refill_slots(nk, NA, NW, LA, LB):
+    """(kind, stage, slot) of every refill load of a tile's K loop: the
+    refill at stage j loads token stage j + NA into token slot j % NA and
+    weight stage j + NW into weight slot j % NW (a stage past the last loads
+    the last one again, marked stage -1)."""
+    out = []
+    for j in range(0, max(0, nk - min(NA, NW))):
+        a, w = j + NA, j + NW
+        out += [("A", a if a < nk else -1, j % NA)] * LA
+        out += [("W", w if w < nk else -1, j % NW)] * LB
+    return out
+
+
+@pytest.mark.parametrize("na,nw,la,lb", [c for c in CASES if c[0] <= c[1] <= c[0] + 1])
+def test_epilogue_lds_is_free(na, nw, la, lb):
+    """After a tile's last stage, the loads issued after the last stage's own
+    loads have not been waited for. None of them may land in the LDS the
+    epilogue uses: the weight slot its outputs are staged in (slot 1, or 2
+    when the K loop's last refill reloaded the last stage into slot 1, as
+    the tile loop picks it) or the token slots the next tile's offsets park
+    in (slot 1, and slot 2 for 64-row tiles, whose token offsets go there).
+    Slot 0 is the next tile's stage 0."""
+    tm = la // 2
+    for nk in NK:
+        seq = []
+        for p in range(min(max(na, nw), nk)):  # the prologue: stage 0, then 1 ..
+            seq += ([("A", p, p)] * la if p < na else []) + ([("W", p, p)] * lb if p < nw else [])
+        seq += refill_slots(nk, na, nw, la, lb)
+        last = max(i for i, x in enumerate(seq) if x[1] == nk - 1)
+        pending = seq[last + 1:]
+        ws = 2 if (nw > na and nk % nw == 1) else 1
+        parked = {1, 2} if tm == 1 else {1}
+        assert ws < nw
+        for kind, stage, slot in pending:
+            assert stage == -1, (nk, kind, stage)
+            if kind == "W":
+                assert slot != ws, (na, nw, nk)
+            else:
+                assert slot not in parked, (na, nw, nk)
